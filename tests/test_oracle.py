@@ -1,0 +1,368 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: hand-worked
+values (tests/golden), closed forms, textbook routines (torch CPU float64),
+an independent dense brute force (oracle.brute), or invariants.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from oracle import brute, tie_filter
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sb_array(vals, kind):
+    if kind == "bf16":
+        return np.array([[int(v, 16) for v in vals]], dtype=np.uint16)
+    return np.array([vals], dtype=np.float32)
+
+
+def small_cfg(T=8, H=128, E=6, k=2, I=64, Is=64, bf16=True, seed=11):
+    return moe_synth.Config("custom", moe_synth.Shape(T=T, H=H, E=E, top_k=k, I=I, I_shared=Is,
+                                                      sb_bf16=bf16), seed=seed)
+
+
+def _zero_sb(w, prefix):
+    for m in ("gate", "up", "down"):
+        for p in ("_s", "_b"):
+            w[prefix + m + p] = np.zeros_like(w[prefix + m + p])
+
+
+# ---------------------------------------------------------------- dequant
+
+
+@pytest.mark.parametrize("ex", _load("dequant_examples.json")["examples"], ids=lambda e: e["name"])
+def test_dequant_hand_examples(ex):
+    if "words_repeat" in ex:
+        word, n = ex["words_repeat"]
+        words = np.array([[int(word, 16)] * n], dtype=np.uint32)
+    else:
+        words = np.array([[int(w, 16) for w in ex["words"]]], dtype=np.uint32)
+    s = _sb_array(ex["scale"], ex["sb"])
+    b = _sb_array(ex["bias"], ex["sb"])
+    W = oracle.dequant(words, s, b, group=ex["group"])[0]
+    if "values_runs" in ex:
+        expect = np.concatenate([np.full(n, v) for v, n in ex["values_runs"]])
+    else:
+        expect = np.array(ex["values"])
+        codes = [oracle.code(words, s, b, 0, k, group=ex["group"]) for k in range(8)]
+        assert codes == ex["codes"]
+    np.testing.assert_array_equal(W, expect)
+
+
+def test_code_position_single_nibble():
+    """A lone non-zero nibble at bit position 4p of word w is element 8w+p."""
+    K = 128
+    for w in range(K // 8):
+        for p in range(8):
+            q = np.zeros((1, K // 8), dtype=np.uint32)
+            q[0, w] = np.uint32(9 << (4 * p))
+            W = oracle.dequant(q, np.ones((1, 2), np.float32), np.zeros((1, 2), np.float32))
+            nz = np.nonzero(W[0])[0]
+            assert list(nz) == [8 * w + p] and W[0, 8 * w + p] == 9.0
+
+
+# ---------------------------------------------------------------- routing
+
+
+@pytest.mark.parametrize("ex", _load("routing_examples.json")["examples"], ids=str)
+def test_routing_hand_examples(ex):
+    idx, w = oracle.select(np.array([ex["logits"]]), ex["k"])
+    assert list(idx[0]) == ex["idx"]
+    np.testing.assert_allclose(w[0], ex["w"], rtol=0, atol=1e-15)
+
+
+def test_routing_invariants_random():
+    rng = np.random.default_rng(5)
+    for E, k in ((16, 2), (256, 8), (64, 7), (5, 5)):
+        logits = rng.standard_normal((200, E))
+        idx, w = oracle.select(logits, k)
+        assert np.all(np.abs(w.sum(axis=1) - 1.0) <= k * 2.0 ** -52)
+        for t in range(len(idx)):
+            sel = idx[t]
+            assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < E
+            rest = np.setdiff1d(np.arange(E), sel)
+            if len(rest):
+                assert logits[t, sel].min() >= logits[t, rest].max()
+            assert np.all(np.diff(w[t]) <= 0)
+            assert np.all(np.diff(logits[t, sel]) <= 0)
+
+
+def test_routing_k1_weight_is_one():
+    logits = np.random.default_rng(1).standard_normal((50, 16))
+    idx, w = oracle.select(logits, 1)
+    assert np.all(w == 1.0)
+    np.testing.assert_array_equal(idx[:, 0], np.argmax(logits, axis=1))
+
+
+def test_routing_k_equals_E_is_full_softmax():
+    logits = np.random.default_rng(2).standard_normal((20, 9)) * 3
+    idx, w = oracle.select(logits, 9)
+    sm = torch.softmax(torch.from_numpy(logits), dim=1).numpy()
+    for t in range(20):
+        np.testing.assert_allclose(w[t], sm[t, idx[t]], rtol=1e-13)
+        np.testing.assert_array_equal(np.sort(idx[t]), np.arange(9))
+
+
+def test_router_logits_against_matmul():
+    cfg = small_cfg(T=5, H=256, E=7)
+    x = moe_synth.token_rows(cfg)
+    R = moe_synth.router_weights(cfg)
+    bias = np.linspace(-1, 1, 7).astype(np.float32)
+    got = oracle.router_logits(x, R, bias)
+    X = torch.from_numpy(moe_synth.bf16_bits_to_f32(x).astype(np.float64))
+    Wr = torch.from_numpy(moe_synth.bf16_bits_to_f32(R).astype(np.float64))
+    ref = (X @ Wr.T).numpy() + bias.astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- permute
+
+
+def test_permute_hand_example():
+    ex = _load("permute_example.json")
+    counts, offsets, ss = oracle.permute(np.array(ex["idx"]), ex["E"])
+    assert counts.tolist() == ex["counts"]
+    assert offsets.tolist() == ex["offsets"]
+    assert ss.tolist() == ex["sorted_slot"]
+
+
+def test_permute_invariants():
+    rng = np.random.default_rng(3)
+    T, k, E = 300, 8, 256
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, offsets, ss = oracle.permute(idx, E)
+    assert counts.sum() == T * k and offsets[-1] == T * k
+    np.testing.assert_array_equal(np.sort(ss), np.arange(T * k))
+    flat = idx.ravel()
+    for e in range(E):
+        seg = ss[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+# ---------------------------------------------------------------- expert FFN
+
+
+def _expert(w, e, prefix=""):
+    return tuple((w[prefix + m + "_q"][e], w[prefix + m + "_s"][e], w[prefix + m + "_b"][e])
+                 for m in ("gate", "up", "down"))
+
+
+def test_ffn_one_hot_input_reads_one_column():
+    """x = unit vector e_i (bf16 1.0 at i): g[n] = W_gate[n][i] exactly."""
+    cfg = small_cfg(H=256, I=64)
+    w = moe_synth.layer_weights(cfg)
+    gate, up, down = _expert(w, 1)
+    Wg = oracle.dequant(*gate)
+    Wu = oracle.dequant(*up)
+    for i in (0, 7, 8, 63, 64, 200, 255):
+        x = np.zeros((1, 256), dtype=np.uint16)
+        x[0, i] = 0x3F80  # 1.0
+        y, g, u = oracle.expert_ffn(gate, up, down, x, want_gu=True)
+        np.testing.assert_array_equal(g[0], Wg[:, i])
+        np.testing.assert_array_equal(u[0], Wu[:, i])
+
+
+def test_ffn_all_codes_zero_closed_form():
+    """All codes 0: W = bias per group, so g[n] = sum_g b[n][g] * sum_{h in g} x[h]."""
+    cfg = small_cfg(H=256, I=64, bf16=False)
+    w = moe_synth.layer_weights(cfg)
+    gate, up, down = _expert(w, 0)
+    gate = (np.zeros_like(gate[0]),) + gate[1:]
+    x = moe_synth.token_rows(cfg)[:3]
+    _, g, _ = oracle.expert_ffn(gate, up, down, x, want_gu=True)
+    xs = moe_synth.bf16_bits_to_f32(x).astype(np.float64).reshape(3, 4, 64).sum(axis=2)
+    expect = xs @ gate[2].astype(np.float64).T
+    np.testing.assert_allclose(g, expect, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_textbook_swiglu_mlp():
+    """E=1, k=1: routing weight 1, so out = SwiGLU(x; expert 0) + SwiGLU(x; shared)."""
+    cfg = small_cfg(T=6, H=128, E=1, k=1, I=64, Is=128)
+    w = moe_synth.layer_weights(cfg)
+    x = moe_synth.token_rows(cfg)
+    res = oracle.moe_layer(w, x, 1)
+    X = torch.from_numpy(moe_synth.bf16_bits_to_f32(x).astype(np.float64))
+
+    def mlp(prefix, e):
+        Wg, Wu, Wd = (torch.from_numpy(oracle.dequant(*m)) for m in _expert(w, e, prefix))
+        return torch.nn.functional.linear(torch.nn.functional.silu(X @ Wg.T) * (X @ Wu.T), Wd)
+
+    ref = (mlp("", 0) + mlp("shared_", 0)).numpy()
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-11, atol=1e-11)
+    assert np.all(res["w"] == 1.0) and np.all(res["idx"] == 0)
+
+
+def test_k_equals_E_is_dense_softmax_mixture():
+    cfg = small_cfg(T=4, H=128, E=5, k=5, I=64)
+    w = moe_synth.layer_weights(cfg)
+    x = moe_synth.token_rows(cfg)
+    res = oracle.moe_layer(w, x, 5, want_logits=True)
+    X = torch.from_numpy(moe_synth.bf16_bits_to_f32(x).astype(np.float64))
+    p = torch.softmax(torch.from_numpy(res["logits"]), dim=1)
+
+    def mlp(prefix, e):
+        Wg, Wu, Wd = (torch.from_numpy(oracle.dequant(*m)) for m in _expert(w, e, prefix))
+        return (torch.nn.functional.silu(X @ Wg.T) * (X @ Wu.T)) @ Wd.T
+
+    ref = sum(p[:, e:e + 1] * mlp("", e) for e in range(5)) + mlp("shared_", 0)
+    np.testing.assert_allclose(res["out"], ref.numpy(), rtol=1e-11, atol=1e-11)
+
+
+def test_zeroed_routed_experts_leave_shared_only_and_vice_versa():
+    cfg = small_cfg(T=5, E=6, k=2)
+    w = moe_synth.layer_weights(cfg)
+    x = moe_synth.token_rows(cfg)
+    full = oracle.moe_layer(w, x, 2)["out"]
+    w_r0 = dict(w)
+    _zero_sb(w_r0, "")
+    shared_only = oracle.moe_layer(w_r0, x, 2)["out"]
+    w_s0 = dict(w)
+    _zero_sb(w_s0, "shared_")
+    routed_only = oracle.moe_layer(w_s0, x, 2)["out"]
+    ys = oracle.expert_ffn(*_expert(w, 0, "shared_"), x)
+    np.testing.assert_allclose(shared_only, ys, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(routed_only + shared_only, full, rtol=1e-12, atol=1e-12)
+    assert np.abs(routed_only).max() > 0.1 and np.abs(shared_only).max() > 0.1
+
+
+# ---------------------------------------------------------------- whole layer vs brute force
+
+
+def _rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def test_tiny_config_against_brute_force():
+    cfg = moe_synth.CONFIGS["tiny"]
+    w = moe_synth.layer_weights(cfg)
+    x = tie_filter.tokens("tiny")
+    res = oracle.moe_layer(w, x, cfg.shape.top_k)
+    bf = brute.layer(w, x, cfg.shape.top_k)
+    assert np.abs(res["out"] - bf["out"]).max() <= 1e-12 * _rms(bf["out"]) * 1e3
+    M = np.zeros_like(bf["mask"])
+    np.put_along_axis(M, res["idx"].astype(np.int64), True, axis=1)
+    np.testing.assert_array_equal(M, bf["mask"])
+    np.testing.assert_allclose(np.take_along_axis(bf["r"], res["idx"].astype(np.int64), 1), res["w"], rtol=1e-13)
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23, 24])
+def test_random_tiny_shapes_against_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 12))
+    k = int(rng.integers(1, E + 1))
+    cfg = small_cfg(T=int(rng.integers(1, 9)), H=64 * int(rng.integers(1, 4)), E=E, k=k,
+                    I=64 * int(rng.integers(1, 3)), Is=64 * int(rng.integers(1, 3)),
+                    bf16=bool(seed % 2), seed=seed)
+    w = moe_synth.layer_weights(cfg)
+    x = moe_synth.token_rows(cfg)
+    res = oracle.moe_layer(w, x, k)
+    bf = brute.layer(w, x, k)
+    assert np.abs(res["out"] - bf["out"]).max() <= 1e-9 * _rms(bf["out"])
+    M = np.zeros_like(bf["mask"])
+    np.put_along_axis(M, res["idx"].astype(np.int64), True, axis=1)
+    np.testing.assert_array_equal(M, bf["mask"])
+
+
+def test_logit_bias_enters_selection_and_softmax():
+    cfg = small_cfg(T=6, E=8, k=3)
+    w = moe_synth.layer_weights(cfg)
+    w["logit_bias"] = np.linspace(2.0, -2.0, 8).astype(np.float32)
+    x = moe_synth.token_rows(cfg)
+    res = oracle.moe_layer(w, x, 3)
+    bf = brute.layer(w, x, 3)
+    assert np.abs(res["out"] - bf["out"]).max() <= 1e-9 * _rms(bf["out"])
+
+
+# ---------------------------------------------------------------- invariances
+
+
+def test_token_subset_equals_full_batch():
+    cfg = small_cfg(T=8, E=6, k=2)
+    w = moe_synth.layer_weights(cfg)
+    x = moe_synth.token_rows(cfg)
+    full = oracle.moe_layer(w, x, 2)
+    sub = oracle.moe_layer(w, x, 2, tokens=[6, 1, 3])
+    np.testing.assert_array_equal(sub["out"], full["out"][[6, 1, 3]])
+    alone = oracle.moe_layer(w, x[3:4], 2)
+    np.testing.assert_allclose(alone["out"][0], full["out"][3], rtol=1e-14, atol=1e-14)
+
+
+def test_expert_relabelling_invariance():
+    cfg = small_cfg(T=8, E=6, k=2)
+    w = moe_synth.layer_weights(cfg)
+    x = moe_synth.token_rows(cfg)
+    perm = np.array([3, 5, 0, 1, 4, 2])
+    w2 = dict(w)
+    for key in ("router", "gate_q", "gate_s", "gate_b", "up_q", "up_s", "up_b", "down_q", "down_s", "down_b"):
+        w2[key] = w[key][perm]
+    a = oracle.moe_layer(w, x, 2)
+    b = oracle.moe_layer(w2, x, 2)
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(np.sort(a["idx"], 1), np.sort(perm[b["idx"]], 1))
+
+
+# ---------------------------------------------------------------- inputs
+
+
+def test_near_ties_removed():
+    for name in ("tiny", "decode", "decode64"):
+        cfg = moe_synth.CONFIGS[name]
+        x = tie_filter.tokens(name)
+        l = tie_filter.router_logits_f64(x, moe_synth.router_weights(cfg))
+        assert np.all(tie_filter.kth_gap(l, cfg.shape.top_k) >= tie_filter.TAU)
+
+
+def test_oracle_float32_logit_error_is_far_below_tie_margin():
+    """fp32 sums of the router products (pairwise and sequential) stay within TAU/10 of float64."""
+    cfg = moe_synth.CONFIGS["decode64"]
+    x = tie_filter.tokens("decode64")
+    R = moe_synth.router_weights(cfg)
+    l64 = tie_filter.router_logits_f64(x, R)
+    X = moe_synth.bf16_bits_to_f32(x)
+    W = moe_synth.bf16_bits_to_f32(R)
+    l32 = X @ W.T
+    seq = np.zeros_like(l32)
+    for h in range(0, X.shape[1], 16):
+        seq += X[:, h:h + 16] @ W[:, h:h + 16].T
+    assert np.abs(l32 - l64).max() < tie_filter.TAU / 10
+    assert np.abs(seq - l64).max() < tie_filter.TAU / 10
+
+
+def test_zipf_offset_reaches_half_of_assignments_on_sampled_layers():
+    cfg = moe_synth.CONFIGS["stack40"]
+    x = moe_synth.token_rows(cfg, 1024)
+    shares = []
+    for layer in (0, 13, 39):
+        l = tie_filter.router_logits_f64(x, moe_synth.router_weights(cfg, layer), moe_synth.zipf_bias(cfg, layer))
+        idx, _ = oracle.select(l, cfg.shape.top_k)
+        c = np.sort(np.bincount(idx.ravel(), minlength=cfg.shape.E))[::-1]
+        shares.append(c[:16].sum() / idx.size)
+    assert abs(np.mean(shares) - 0.5) < 0.05
+
+
+def test_generator_formats():
+    cfg = moe_synth.CONFIGS["tiny"]
+    w = moe_synth.layer_weights(cfg)
+    sh = cfg.shape
+    assert w["gate_q"].shape == (sh.E, sh.I, sh.H // 8) and w["gate_q"].dtype == np.uint32
+    assert w["down_q"].shape == (sh.E, sh.H, sh.I // 8)
+    assert w["gate_s"].shape == (sh.E, sh.I, sh.H // 64) and w["gate_s"].dtype == np.float32
+    assert w["shared_down_b"].shape == (1, sh.H, sh.I_shared // 64)
+    assert 0.005 <= w["gate_s"].min() and w["gate_s"].max() <= 0.02
+    w1 = moe_synth.layer_weights(moe_synth.CONFIGS["tiny"])
+    np.testing.assert_array_equal(w1["up_q"], w["up_q"])
+    assert math.isclose(moe_synth.bf16_bits_to_f32(np.array([0x3F80], np.uint16))[0], 1.0)
