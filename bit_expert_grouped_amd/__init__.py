@@ -1,0 +1,250 @@
+"""Python binding of libbitmoe (include/moe.h): the gfx950 4-bit grouped-expert MoE layer.
+
+Argument marshalling only: torch tensors in device memory are turned into
+pointers and the current torch stream into a ``hipStream_t``; every step of
+the layer runs in the HIP kernels of ``libbitmoe.so``.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+
+Names follow the C ABI: ``moe_workspace_size``, ``moe_route``,
+``moe_permute``, ``moe_expert_ffn``, ``moe_combine``, ``moe_layer``,
+``moe_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbitmoe.so")
+
+MOE_BF16, MOE_F32 = 0, 1
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
+          -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
+           "moe_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__("%s failed: %s (%s)" % (call, STATUS.get(status, status), status_string(status)))
+        self.status = status
+
+
+class Dims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("T", "H", "E", "top_k", "I", "I_shared", "group", "sb_dtype",
+                                          "out_dtype")]
+
+
+class QMat(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("scale", C.c_void_p), ("bias", C.c_void_p)]
+
+
+class Ffn(C.Structure):
+    _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+class Weights(C.Structure):
+    _fields_ = [("router", C.c_void_p), ("logit_bias", C.c_void_p), ("experts", Ffn), ("shared", Ffn)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libbitmoe.so (built in-tree by ``python -m bit_expert_grouped_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libbitmoe.so is not built; run `python -m bit_expert_grouped_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, D = C.c_void_p, C.POINTER(Dims)
+        L.moe_workspace_size.argtypes = [D]
+        L.moe_workspace_size.restype = C.c_size_t
+        L.moe_status_string.argtypes = [C.c_int]
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_route.argtypes = [D, P, P, P, P, P, P]
+        L.moe_permute.argtypes = [D, P, P, P, P, P, C.c_size_t, P]
+        L.moe_expert_ffn.argtypes = [D, P, P, P, C.POINTER(Ffn), C.POINTER(Ffn), P, P, P, C.c_size_t, P]
+        L.moe_combine.argtypes = [D, P, P, P, P, P]
+        L.moe_layer.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P]
+        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer"):
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+moe_status_string = status_string
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise MoeError(status, call)
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dims(T, H, E, top_k, I, I_shared, sb_bf16=True, group=64, out_dtype=MOE_F32) -> Dims:
+    return Dims(T, H, E, top_k, I, I_shared, group, MOE_BF16 if sb_bf16 else MOE_F32, out_dtype)
+
+
+def moe_workspace_size(d: Dims) -> int:
+    return lib().moe_workspace_size(C.byref(d))
+
+
+def workspace(d: Dims, device="cuda"):
+    """A workspace tensor of moe_workspace_size(d) bytes (torch allocations are 256-byte aligned)."""
+    import torch
+
+    n = moe_workspace_size(d)
+    if n == 0:
+        raise MoeError(-2, "moe_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- weights
+
+
+class LayerWeights:
+    """Device tensors of one layer (router, stacked experts, shared expert) plus the C structs."""
+
+    def __init__(self, tensors: dict):
+        self.t = tensors
+        self.sb_bf16 = tensors["gate_s"].element_size() == 2
+        self.E, self.I, hw = tensors["gate_q"].shape
+        self.H = hw * 8
+        self.I_shared = tensors["shared_gate_q"].shape[1] if tensors.get("shared_gate_q") is not None else 0
+
+        def qm(prefix, name):
+            return QMat(_p(tensors[prefix + name + "_q"]), _p(tensors[prefix + name + "_s"]),
+                        _p(tensors[prefix + name + "_b"]))
+
+        self.experts = Ffn(qm("", "gate"), qm("", "up"), qm("", "down"))
+        self.shared = (Ffn(qm("shared_", "gate"), qm("shared_", "up"), qm("shared_", "down"))
+                       if self.I_shared else Ffn())
+        self.struct = Weights(_p(tensors["router"]), _p(tensors.get("logit_bias")), self.experts, self.shared)
+
+    def dims(self, T, top_k) -> Dims:
+        return dims(T, self.H, self.E, top_k, self.I, self.I_shared, self.sb_bf16)
+
+
+def upload_weights(w: dict, device="cuda") -> LayerWeights:
+    """numpy weights (moe_synth layout: uint32 codes, bf16 bits as uint16 or float32) -> device tensors."""
+    import numpy as np
+    import torch
+
+    t = {}
+    for k, v in w.items():
+        if v is None:
+            t[k] = None
+            continue
+        a = np.ascontiguousarray(v)
+        if a.dtype == np.uint32:
+            t[k] = torch.from_numpy(a.view(np.int32)).to(device)
+        elif a.dtype == np.uint16:
+            t[k] = torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        else:
+            t[k] = torch.from_numpy(a).to(device)
+    return LayerWeights(t)
+
+
+def bf16_tensor(x_bits, device="cuda"):
+    """bf16 bit patterns (numpy uint16) -> torch.bfloat16 tensor on device."""
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- calls
+
+
+def moe_route(x, router, top_k, logit_bias=None, topk_idx=None, topk_w=None):
+    import torch
+
+    T, H = x.shape
+    E = router.shape[0]
+    d = dims(T, H, E, top_k, 64, 0)
+    if topk_idx is None:
+        topk_idx = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+    _check(lib().moe_route(C.byref(d), _p(x), _p(router), _p(logit_bias), _p(topk_idx), _p(topk_w), _stream()),
+           "moe_route")
+    return topk_idx, topk_w
+
+
+def moe_permute(topk_idx, E, ws=None, d=None):
+    import torch
+
+    T, k = topk_idx.shape
+    if d is None:
+        d = dims(T, 64, E, k, 64, 0)
+    if ws is None:
+        ws = workspace(d, topk_idx.device)
+    counts = torch.empty(E, dtype=torch.int32, device=topk_idx.device)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=topk_idx.device)
+    sorted_slot = torch.empty(max(T * k, 1), dtype=torch.int32, device=topk_idx.device)
+    _check(lib().moe_permute(C.byref(d), _p(topk_idx), _p(counts), _p(offsets), _p(sorted_slot), _p(ws),
+                             ws.numel(), _stream()), "moe_permute")
+    return counts, offsets, sorted_slot
+
+
+def moe_expert_ffn(x, offsets, sorted_slot, weights: LayerWeights, top_k, with_shared=True, ws=None):
+    import torch
+
+    T, H = x.shape
+    d = weights.dims(T, top_k)
+    if ws is None:
+        ws = workspace(d, x.device)
+    y_slot = torch.empty(max(T * top_k, 1), H, dtype=torch.float32, device=x.device)
+    y_shared = torch.empty(T, H, dtype=torch.float32, device=x.device) if (with_shared and weights.I_shared) else None
+    shared = C.byref(weights.shared) if y_shared is not None else None
+    _check(lib().moe_expert_ffn(C.byref(d), _p(x), _p(offsets), _p(sorted_slot), C.byref(weights.experts), shared,
+                                _p(y_slot), _p(y_shared), _p(ws), ws.numel(), _stream()), "moe_expert_ffn")
+    return y_slot, y_shared
+
+
+def moe_combine(y_slot, topk_w, y_shared=None, out=None):
+    import torch
+
+    T, k = topk_w.shape
+    H = y_slot.shape[1]
+    d = dims(T, H, max(k, 1), k, 64, 0)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.float32, device=y_slot.device)
+    _check(lib().moe_combine(C.byref(d), _p(y_slot), _p(topk_w), _p(y_shared), _p(out), _stream()), "moe_combine")
+    return out
+
+
+def moe_layer(x, weights: LayerWeights, top_k, out=None, ws=None, want_routing=False):
+    """out [T][H] float32 = the whole MoE layer on bf16 activations x [T][H]."""
+    import torch
+
+    T, H = x.shape
+    d = weights.dims(T, top_k)
+    if ws is None:
+        ws = workspace(d, x.device)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.float32, device=x.device)
+    idx = w = counts = None
+    if want_routing:
+        idx = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+        w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+        counts = torch.empty(weights.E, dtype=torch.int32, device=x.device)
+    _check(lib().moe_layer(C.byref(d), C.byref(weights.struct), _p(x), _p(out), _p(idx), _p(w), _p(counts), _p(ws),
+                           ws.numel(), _stream()), "moe_layer")
+    if want_routing:
+        return out, idx, w, counts
+    return out

@@ -1,0 +1,78 @@
+// Launchers of the gfx950 MoE kernels (internal to libbitmoe; the public ABI is
+// include/moe.h).  Every launcher only enqueues on `stream` and returns the
+// launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitmoe {
+
+// One stack of affine 4-bit matrices [n][N][K]: q [n][N][K/8] words,
+// scale/bias [n][N][K/64].
+struct QMatPtr {
+    const uint32_t* q;
+    const void* s;
+    const void* b;
+};
+
+struct FfnPtr {
+    QMatPtr gate, up, down;
+};
+
+// A row tile of one expert group: group g (0..E-1 routed, E shared), the first
+// row in the grouped row space, the number of rows (1..kTileRows).
+// Grouped row space: rows [0, T*k) are the routed slots in expert order
+// (row p holds slot sorted_slot[p]); rows [T*k, T*k+T) are the shared expert's
+// tokens in order.
+struct Tile {
+    int32_t group, row0, rows, pad;
+};
+
+constexpr int kTileRows = 128;  // rows of the grouped products handled by one workgroup
+
+// Upper bound of the number of tiles for T tokens (host side).
+inline int64_t max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
+    return (T * k + (shared ? T : 0)) / kTileRows + E + (shared ? 1 : 0) + 1;
+}
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H,
+                         int E, int top_k, int32_t* topk_idx, float* topk_w, _Float16* x16,
+                         float* out_clear, hipStream_t stream);
+
+hipError_t launch_convert_x(const uint16_t* x, int T, int H, _Float16* x16, hipStream_t stream);
+
+// Histogram, exclusive scan, scatter and tile map (one workgroup).
+hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E, bool shared, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_slot, Tile* tiles, int32_t* n_tiles,
+                          hipStream_t stream);
+
+// Tile map only, from caller-provided offsets [E+1].
+hipError_t launch_tiles(const int32_t* offsets, int T, int k, int E, bool shared, Tile* tiles,
+                        int32_t* n_tiles, hipStream_t stream);
+
+struct GemmProblem {
+    int T, H, E, k, I;
+    bool shared;
+    bool sb_bf16;
+    const Tile* tiles;
+    const int32_t* n_tiles;
+    int64_t max_tiles;
+    const int32_t* sorted_slot;  // [T*k]
+    FfnPtr experts, shared_w;
+};
+
+// gate/up products with SwiGLU: h [T*k + T][I] float16 in grouped row order,
+// 8-column blocks in dequantisation order.
+hipError_t launch_gateup(const GemmProblem& p, const _Float16* x16, _Float16* h, hipStream_t stream);
+
+// down products.  combine == true: out[t] += w * y (float32 atomics, out cleared
+// beforehand; routed rows weighted by topk_w, shared rows by 1).  combine ==
+// false: y_slot[slot] = y for routed rows, y_shared[t] = y for shared rows.
+hipError_t launch_down(const GemmProblem& p, const _Float16* h, const float* topk_w, bool combine,
+                       float* out, float* y_slot, float* y_shared, hipStream_t stream);
+
+hipError_t launch_combine(const float* y_slot, const float* topk_w, const float* y_shared, int T, int H,
+                          int k, float* out, hipStream_t stream);
+
+}  // namespace bitmoe

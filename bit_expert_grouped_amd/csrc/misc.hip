@@ -1,0 +1,71 @@
+// Small elementwise kernels for gfx950: the float16 activation copy used by the
+// expert products of the step-by-step API, and the stand-alone weighted combine.
+#include "common.h"
+#include "kernels.h"
+
+namespace bitmoe {
+
+namespace {
+
+// x [T][H] bf16 -> x16 [T][H] float16 with 8-column blocks in dequantisation order.
+__global__ __launch_bounds__(256) void convert_x_kernel(const uint16_t* __restrict__ x, int64_t nblk,
+                                                        _Float16* __restrict__ x16) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nblk; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 raw = reinterpret_cast<const uint4*>(x)[i];
+        const uint16_t* hb = reinterpret_cast<const uint16_t*>(&raw);
+        half8_t o;
+#pragma unroll
+        for (int e = 0; e < 8; e++) o[e] = (_Float16)bf16_to_f32(hb[nibble_of(e)]);
+        reinterpret_cast<half8_t*>(x16)[i] = o;
+    }
+}
+
+// Pages: one shared expert is added to the routed experts' output (aimanavo.com
+// page, section "Qwen3.6's 256 experts and two layer types make the MLX-Lily gap").
+// out[t][h] = sum_j w[t][j] * y_slot[t*k+j][h] + y_shared[t][h]; 4 columns per thread.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_slot,
+                                                      const float* __restrict__ topk_w,
+                                                      const float* __restrict__ y_shared, int T, int H, int k,
+                                                      float* __restrict__ out) {
+    const int h4 = H / 4;
+    const int64_t n = (int64_t)T * h4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int t = (int)(i / h4), c = (int)(i % h4);
+        float4 acc = y_shared ? reinterpret_cast<const float4*>(y_shared + (size_t)t * H)[c]
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < k; j++) {
+            const float w = topk_w[(size_t)t * k + j];
+            const float4 y = reinterpret_cast<const float4*>(y_slot + ((size_t)t * k + j) * H)[c];
+            acc.x += w * y.x;
+            acc.y += w * y.y;
+            acc.z += w * y.z;
+            acc.w += w * y.w;
+        }
+        reinterpret_cast<float4*>(out + (size_t)t * H)[c] = acc;
+    }
+}
+
+int grid_for(int64_t n) {
+    int64_t g = (n + 255) / 256;
+    return (int)(g < 1 ? 1 : (g > 8192 ? 8192 : g));
+}
+
+}  // namespace
+
+hipError_t launch_convert_x(const uint16_t* x, int T, int H, _Float16* x16, hipStream_t stream) {
+    const int64_t nblk = (int64_t)T * H / 8;
+    if (nblk <= 0) return hipSuccess;
+    hipLaunchKernelGGL(convert_x_kernel, dim3(grid_for(nblk)), dim3(256), 0, stream, x, nblk, x16);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* y_slot, const float* topk_w, const float* y_shared, int T, int H, int k,
+                          float* out, hipStream_t stream) {
+    const int64_t n = (int64_t)T * (H / 4);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n)), dim3(256), 0, stream, y_slot, topk_w, y_shared, T, H, k,
+                       out);
+    return hipGetLastError();
+}
+
+}  // namespace bitmoe

@@ -1,0 +1,272 @@
+// C ABI of the gfx950 MoE layer (include/moe.h): host-side validation,
+// workspace layout and kernel dispatch on the caller's stream.  Nothing here
+// allocates, frees or synchronises; every check runs before the first launch.
+#include "../../include/moe.h"
+
+#include <stdint.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace bitmoe;
+
+namespace {
+
+constexpr int kMaxH = 16384;
+constexpr int kMaxI = 4096;
+constexpr int64_t kMaxT = int64_t(1) << 22;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_dims(const moe_dims* d) {
+    if (!d) return MOE_ERR_NULL;
+    if (d->T < 0 || d->H <= 0 || d->E <= 0 || d->top_k <= 0 || d->I <= 0 || d->I_shared < 0 || d->group <= 0)
+        return MOE_ERR_SHAPE;
+    if (d->top_k > d->E) return MOE_ERR_SHAPE;
+    if (d->H % d->group != 0 || d->I % d->group != 0 || d->I_shared % d->group != 0) return MOE_ERR_SHAPE;
+    if (d->sb_dtype != MOE_BF16 && d->sb_dtype != MOE_F32) return MOE_ERR_SHAPE;
+    if (d->out_dtype != MOE_BF16 && d->out_dtype != MOE_F32) return MOE_ERR_SHAPE;
+    if (d->group != kGroup) return MOE_ERR_UNSUPPORTED;
+    if (d->E > kMaxE || d->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+    if (d->H > kMaxH || d->I > kMaxI) return MOE_ERR_UNSUPPORTED;
+    if (d->I_shared != 0 && d->I_shared != d->I) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)d->T > kMaxT) return MOE_ERR_UNSUPPORTED;
+    if (d->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// Workspace layout; every region starts on a 256-byte boundary.
+struct Layout {
+    size_t x16, h, idx, w, counts, offsets, sorted, tiles, n_tiles, total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Layout layout_of(const moe_dims* d) {
+    const size_t T = (size_t)d->T, H = (size_t)d->H, k = (size_t)d->top_k, E = (size_t)d->E, I = (size_t)d->I;
+    const bool shared = d->I_shared > 0;
+    Layout L;
+    size_t o = 0;
+    L.x16 = o;
+    o = up256(o + T * H * 2);
+    L.h = o;
+    o = up256(o + (T * k + (shared ? T : 0)) * I * 2);
+    L.idx = o;
+    o = up256(o + T * k * 4);
+    L.w = o;
+    o = up256(o + T * k * 4);
+    L.counts = o;
+    o = up256(o + E * 4);
+    L.offsets = o;
+    o = up256(o + (E + 1) * 4);
+    L.sorted = o;
+    o = up256(o + T * k * 4);
+    L.tiles = o;
+    o = up256(o + (size_t)max_tiles(d->T, d->top_k, d->E, shared) * sizeof(Tile));
+    L.n_tiles = o;
+    o = up256(o + 4);
+    L.total = o;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
+}
+
+moe_status check_ws(const moe_dims* d, const void* ws, size_t ws_bytes) {
+    if (!ws) return MOE_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_ALIGN;
+    if (ws_bytes < layout_of(d).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+moe_status check_qmat(const moe_qmat& m) {
+    if (!m.q || !m.scale || !m.bias) return MOE_ERR_NULL;
+    if (!aligned16(m.q) || !aligned16(m.scale) || !aligned16(m.bias)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+moe_status check_ffn(const moe_ffn* f) {
+    if (!f) return MOE_ERR_NULL;
+    moe_status s;
+    if ((s = check_qmat(f->gate)) != MOE_OK) return s;
+    if ((s = check_qmat(f->up)) != MOE_OK) return s;
+    return check_qmat(f->down);
+}
+
+moe_status check_ptrs(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (!p) return MOE_ERR_NULL;
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+moe_status check_opt(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+QMatPtr to_ptr(const moe_qmat& m) { return QMatPtr{m.q, m.scale, m.bias}; }
+
+FfnPtr to_ptr(const moe_ffn* f) {
+    if (!f) return FfnPtr{};
+    return FfnPtr{to_ptr(f->gate), to_ptr(f->up), to_ptr(f->down)};
+}
+
+#define MOE_TRY(expr)                          \
+    do {                                       \
+        moe_status _s = (expr);                \
+        if (_s != MOE_OK) return _s;           \
+    } while (0)
+
+#define HIP_TRY(expr)                          \
+    do {                                       \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_dims* dims) {
+    if (check_dims(dims) != MOE_OK) return 0;
+    return layout_of(dims).total;
+}
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "inconsistent or non-positive sizes";
+        case MOE_ERR_UNSUPPORTED: return "sizes outside the supported limits";
+        case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
+        case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
+        case MOE_ERR_HIP: return "a kernel launch failed";
+    }
+    return "unknown status";
+}
+
+moe_status moe_route(const moe_dims* d, const uint16_t* x, const uint16_t* router, const float* logit_bias,
+                     int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, router, topk_idx, topk_w}));
+    MOE_TRY(check_opt({logit_bias}));
+    HIP_TRY(launch_router(x, router, logit_bias, d->T, d->H, d->E, d->top_k, topk_idx, topk_w, nullptr, nullptr,
+                          stream));
+    return MOE_OK;
+}
+
+moe_status moe_permute(const moe_dims* d, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_slot, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({topk_idx, counts, offsets, sorted_slot}));
+    MOE_TRY(check_ws(d, ws, ws_bytes));
+    const Layout L = layout_of(d);
+    HIP_TRY(launch_permute(topk_idx, d->T, d->top_k, d->E, d->I_shared > 0, counts, offsets, sorted_slot,
+                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.n_tiles), stream));
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_dims* d, const uint16_t* x, const int32_t* offsets, const int32_t* sorted_slot,
+                          const moe_ffn* experts, const moe_ffn* shared, float* y_slot, float* y_shared, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, offsets, sorted_slot, y_slot}));
+    MOE_TRY(check_ffn(experts));
+    const bool use_shared = shared != nullptr && y_shared != nullptr;
+    if (use_shared) {
+        if (d->I_shared == 0) return MOE_ERR_SHAPE;
+        MOE_TRY(check_ffn(shared));
+        MOE_TRY(check_ptrs({y_shared}));
+    }
+    MOE_TRY(check_ws(d, ws, ws_bytes));
+    const Layout L = layout_of(d);
+    GemmProblem p;
+    p.T = d->T;
+    p.H = d->H;
+    p.E = d->E;
+    p.k = d->top_k;
+    p.I = d->I;
+    p.shared = use_shared;
+    p.sb_bf16 = d->sb_dtype == MOE_BF16;
+    p.tiles = at<Tile>(ws, L.tiles);
+    p.n_tiles = at<int32_t>(ws, L.n_tiles);
+    p.max_tiles = max_tiles(d->T, d->top_k, d->E, use_shared);
+    p.sorted_slot = sorted_slot;
+    p.experts = to_ptr(experts);
+    p.shared_w = use_shared ? to_ptr(shared) : FfnPtr{};
+    _Float16* x16 = at<_Float16>(ws, L.x16);
+    _Float16* h = at<_Float16>(ws, L.h);
+    HIP_TRY(launch_tiles(offsets, d->T, d->top_k, d->E, use_shared, at<Tile>(ws, L.tiles),
+                         at<int32_t>(ws, L.n_tiles), stream));
+    HIP_TRY(launch_convert_x(x, d->T, d->H, x16, stream));
+    HIP_TRY(launch_gateup(p, x16, h, stream));
+    HIP_TRY(launch_down(p, h, nullptr, false, nullptr, y_slot, use_shared ? y_shared : nullptr, stream));
+    return MOE_OK;
+}
+
+moe_status moe_combine(const moe_dims* d, const float* y_slot, const float* topk_w, const float* y_shared, void* out,
+                       hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({y_slot, topk_w, out}));
+    MOE_TRY(check_opt({y_shared}));
+    HIP_TRY(launch_combine(y_slot, topk_w, y_shared, d->T, d->H, d->top_k, static_cast<float*>(out), stream));
+    return MOE_OK;
+}
+
+moe_status moe_layer(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out, int32_t* topk_idx_out,
+                     float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->T == 0) return MOE_OK;
+    if (!wts) return MOE_ERR_NULL;
+    MOE_TRY(check_ptrs({x, out, wts->router}));
+    MOE_TRY(check_opt({wts->logit_bias, topk_idx_out, topk_w_out, counts_out}));
+    MOE_TRY(check_ffn(&wts->experts));
+    const bool shared = d->I_shared > 0;
+    if (shared) {
+        MOE_TRY(check_ffn(&wts->shared));
+    } else if (wts->shared.gate.q) {
+        return MOE_ERR_SHAPE;
+    }
+    MOE_TRY(check_ws(d, ws, ws_bytes));
+    const Layout L = layout_of(d);
+    int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+    float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+    int32_t* counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* sorted = at<int32_t>(ws, L.sorted);
+    _Float16* x16 = at<_Float16>(ws, L.x16);
+    _Float16* h = at<_Float16>(ws, L.h);
+    float* o = static_cast<float*>(out);
+
+    GemmProblem p;
+    p.T = d->T;
+    p.H = d->H;
+    p.E = d->E;
+    p.k = d->top_k;
+    p.I = d->I;
+    p.shared = shared;
+    p.sb_bf16 = d->sb_dtype == MOE_BF16;
+    p.tiles = at<Tile>(ws, L.tiles);
+    p.n_tiles = at<int32_t>(ws, L.n_tiles);
+    p.max_tiles = max_tiles(d->T, d->top_k, d->E, shared);
+    p.sorted_slot = sorted;
+    p.experts = to_ptr(&wts->experts);
+    p.shared_w = shared ? to_ptr(&wts->shared) : FfnPtr{};
+
+    HIP_TRY(launch_router(x, wts->router, wts->logit_bias, d->T, d->H, d->E, d->top_k, idx, w, x16, o, stream));
+    HIP_TRY(launch_permute(idx, d->T, d->top_k, d->E, shared, counts, offsets, sorted, at<Tile>(ws, L.tiles),
+                           at<int32_t>(ws, L.n_tiles), stream));
+    HIP_TRY(launch_gateup(p, x16, h, stream));
+    HIP_TRY(launch_down(p, h, w, true, o, nullptr, nullptr, stream));
+    return MOE_OK;
+}
+
+}  // extern "C"

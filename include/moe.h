@@ -1,0 +1,159 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) grouped-expert MoE layer with affine
+ * 4-bit expert weights.
+ *
+ * The layer is the mixture-of-experts block of Qwen3.6-35B-A3B as the pages on
+ * Lily (Perplexity's inference engine) describe it:
+ *   - every token scores all E routed experts, keeps top_k of them and adds
+ *     one always-on shared expert (aimanavo.com page, section "Qwen3.6's 256
+ *     experts and two layer types make the MLX-Lily gap");
+ *   - routing stays on the GPU with no host synchronisation inside the layer
+ *     (same page, section "Lily does not treat prefill and decode as the same
+ *     job"; dzen.guru page, section "Where does the speed-up come from?");
+ *   - expert weights are MLX affine 4-bit with group size 64 and are restored
+ *     inside the grouped matrix product, never written out dequantised (same
+ *     sections; aimanavo.com page, section on the single 4-bit checkpoint;
+ *     news.mantis.guru page, section "Rust drives the model, Metal does the
+ *     compute").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
+ *     every buffer (weights, activations, outputs, workspace); the library
+ *     allocates nothing, frees nothing, keeps no pointer after returning and
+ *     holds no mutable global state.  Calls only ENQUEUE work on `stream`
+ *     (stream-ordered: buffers must stay valid until that work completes);
+ *     none synchronises the host.
+ *   - Every check runs on the host before anything is enqueued.  A status other
+ *     than MOE_OK means nothing was enqueued, except MOE_ERR_HIP, which reports
+ *     a failed launch (the stream may then hold part of the work).
+ *   - Device-side preconditions that are documented but not checked: weights
+ *     and activations are finite; |x| and |silu(gate)*up| stay below 65504
+ *     (the expert products run in float16 with float32 accumulation); every
+ *     topk_idx entry handed to moe_permute lies in [0, E) with top_k distinct
+ *     entries per token; offsets/sorted_slot handed to moe_expert_ffn are a
+ *     valid permutation such as moe_permute produces.
+ *   - Alignment: every pointer must be 16-byte aligned (MOE_ERR_ALIGN).
+ *
+ * Layouts (row-major; "bf16" = bfloat16 bit patterns in uint16_t)
+ *   x          [T][H] bf16 activations
+ *   router     [E][H] bf16
+ *   logit_bias [E] float32, nullable: added to the router logits before
+ *              selection and softmax
+ *   moe_qmat   one stack of n matrices of shape [N][K]:
+ *                q     [n][N][K/8] uint32, the code of column k in bits
+ *                      [4*(k%8), 4*(k%8)+4) of word k/8 (MLX packing);
+ *                scale [n][N][K/64], bias [n][N][K/64] (bf16 or float32,
+ *                      moe_dims.sb_dtype); weight = scale*code + bias.
+ *   experts    gate, up: N=I, K=H; down: N=H, K=I; n=E
+ *   shared     gate, up: N=I_shared, K=H; down: N=H, K=I_shared; n=1
+ *   slot       s = t*top_k + j for token t and its j-th ranked expert
+ */
+#ifndef BITMOE_MOE_H
+#define BITMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,       /* inconsistent or non-positive sizes */
+    MOE_ERR_UNSUPPORTED = -3, /* valid in principle, outside this library's limits */
+    MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE = -5,   /* workspace smaller than moe_workspace_size() */
+    MOE_ERR_HIP = -6          /* a kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+/* Host struct.  Limits (MOE_ERR_UNSUPPORTED beyond them):
+ *   group == 64; H % 64 == 0, 64 <= H <= 16384; I % 64 == 0, 64 <= I <= 4096;
+ *   I_shared == 0 (no shared expert) or as I; 1 <= top_k <= 8; top_k <= E <= 256;
+ *   0 <= T <= 2^22 (T == 0 is a valid empty call that enqueues nothing);
+ *   sb_dtype MOE_BF16 or MOE_F32; out_dtype MOE_F32 (MOE_BF16 is unsupported). */
+typedef struct {
+    int32_t T, H, E, top_k, I, I_shared, group;
+    int32_t sb_dtype;  /* moe_dtype of expert scales and biases */
+    int32_t out_dtype; /* moe_dtype of the layer output */
+} moe_dims;
+
+typedef struct {
+    const uint32_t *q;
+    const void *scale;
+    const void *bias;
+} moe_qmat;
+
+typedef struct {
+    moe_qmat gate, up, down;
+} moe_ffn;
+
+typedef struct {
+    const uint16_t *router;   /* [E][H] bf16 */
+    const float *logit_bias;  /* [E] or NULL */
+    moe_ffn experts;          /* E routed experts */
+    moe_ffn shared;           /* the shared expert; shared.gate.q == NULL iff I_shared == 0 */
+} moe_weights;
+
+/* Bytes of device workspace the calls below need for these dims (host-only,
+ * pure; 0 when the dims are invalid).  One workspace serves every entry point.
+ * Contents need no initialisation and are scratch between calls. */
+size_t moe_workspace_size(const moe_dims *dims /* host */);
+
+/* Router and top-k (pages: score every expert, keep top_k, on the GPU).
+ * logits l[t][e] = sum_h x[t][h]*router[e][h] (+ logit_bias[e]), float32
+ * accumulation of exact bf16 products; the top_k largest logits in rank order
+ * (equal logits: lower expert index first); topk_w[t][j] = softmax of the
+ * selected logits, i.e. the softmax over all E renormalised over the kept ones.
+ * Outputs: topk_idx [T][top_k] int32, topk_w [T][top_k] float32. */
+moe_status moe_route(const moe_dims *dims, const uint16_t *x, const uint16_t *router,
+                     const float *logit_bias, int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+/* Permute (pages: routing closed on the GPU, no per-layer host sync): counting
+ * sort of the T*top_k slots by expert.  counts [E], offsets [E+1] (exclusive
+ * prefix sum of counts), sorted_slot [T*top_k]: the slots of expert e occupy
+ * sorted_slot[offsets[e] .. offsets[e+1]), in unspecified order within e.
+ * Uses the workspace.  Requires T*top_k <= 2^22 for this call. */
+moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, int32_t *counts,
+                       int32_t *offsets, int32_t *sorted_slot, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Grouped expert FFN with dequantisation inside the products (pages: 4-bit
+ * weights restored inside the grouped GEMM).  For every slot s of expert e,
+ * with t = s / top_k:  y_slot[s] = W_down,e (silu(W_gate,e x[t]) * (W_up,e x[t])).
+ * y_shared[t] = the shared expert applied to x[t] (skipped when shared or
+ * y_shared is NULL).  offsets/sorted_slot as produced by moe_permute.
+ * Outputs: y_slot [T*top_k][H] float32 (row = slot), y_shared [T][H] float32. */
+moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x, const int32_t *offsets,
+                          const int32_t *sorted_slot, const moe_ffn *experts /* host */,
+                          const moe_ffn *shared /* host, nullable */, float *y_slot,
+                          float *y_shared /* nullable */, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Weighted combine plus shared expert (pages: add one shared expert):
+ * out[t] = sum_j topk_w[t][j] * y_slot[t*top_k+j] + y_shared[t] (y_shared nullable).
+ * out [T][H] float32. */
+moe_status moe_combine(const moe_dims *dims, const float *y_slot, const float *topk_w,
+                       const float *y_shared, void *out, hipStream_t stream);
+
+/* The whole layer as one device-side pipeline: route, permute, gate/up with
+ * SwiGLU, down with the weighted combine fused into its epilogue, shared expert
+ * included.  out [T][H] float32.  Optional copies of the routing:
+ * topk_idx_out [T][top_k], topk_w_out [T][top_k], counts_out [E] (each nullable). */
+moe_status moe_layer(const moe_dims *dims, const moe_weights *weights /* host */,
+                     const uint16_t *x, void *out, int32_t *topk_idx_out, float *topk_w_out,
+                     int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static English text for a status code (host). */
+const char *moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITMOE_MOE_H */

@@ -45,14 +45,11 @@ def kth_gap(logits, k):
     return part[:, 1] - part[:, 0]
 
 
-@functools.lru_cache(maxsize=None)
-def attempts_for(cfg_name: str, T: int | None = None, tau: float = TAU):
-    """Re-draw counts (token -> attempt) that leave no near-tie in any layer."""
-    cfg = moe_synth.CONFIGS[cfg_name]
+def attempts(cfg, routers, T: int | None = None, tau: float = TAU) -> dict:
+    """Re-draw counts (token -> attempt) that leave no near-tie under any of the
+    given (router bits, logit bias) pairs."""
     k = cfg.shape.top_k
-    routers = [(moe_synth.router_weights(cfg, l),
-                moe_synth.zipf_bias(cfg, l) if cfg.zipf else None) for l in range(cfg.layers)]
-    attempts: dict[int, int] = {}
+    att: dict[int, int] = {}
     x = moe_synth.token_rows(cfg, T)
     todo = np.arange(x.shape[0])
     for _ in range(64):
@@ -61,12 +58,26 @@ def attempts_for(cfg_name: str, T: int | None = None, tau: float = TAU):
             bad |= kth_gap(router_logits_f64(x[todo], R, b), k) < tau
         todo = todo[bad]
         if len(todo) == 0:
-            return tuple(sorted(attempts.items()))
+            return att
         for t in todo:
-            attempts[int(t)] = attempts.get(int(t), 0) + 1
-        xr = moe_synth.token_rows(cfg, x.shape[0], attempts)
+            att[int(t)] = att.get(int(t), 0) + 1
+        xr = moe_synth.token_rows(cfg, x.shape[0], att)
         x[todo] = xr[todo]
     raise RuntimeError("near-tie rejection did not converge")
+
+
+@functools.lru_cache(maxsize=None)
+def attempts_for(cfg_name: str, T: int | None = None, tau: float = TAU):
+    """Re-draw counts for a named config (every layer's router and offset)."""
+    cfg = moe_synth.CONFIGS[cfg_name]
+    routers = [(moe_synth.router_weights(cfg, l),
+                moe_synth.zipf_bias(cfg, l) if cfg.zipf else None) for l in range(cfg.layers)]
+    return tuple(sorted(attempts(cfg, routers, T, tau).items()))
+
+
+def tokens_for(cfg, router, logit_bias=None, T: int | None = None) -> np.ndarray:
+    """Activations of an ad-hoc config with near-ties re-drawn."""
+    return moe_synth.token_rows(cfg, T, attempts(cfg, [(router, logit_bias)], T))
 
 
 def tokens(cfg_name: str, T: int | None = None) -> np.ndarray:

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/moe.h declares, sizes its workspace, and rejects bad arguments on the
+host before anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import bit_expert_grouped_amd as bem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = 0x10000  # a 256-byte aligned non-NULL address; never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bem.LIB_PATH):
+        from bit_expert_grouped_amd import build
+
+        build.build()
+    return bem.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_ ]*?\**\s*\b(moe_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(bem.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def qwen_dims(tokens=512, **kw):
+    d = bem.dims(tokens, 2048, 256, 8, 512, 512)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_workspace_size(lib):
+    d = qwen_dims(4096)
+    n = bem.moe_workspace_size(d)
+    # float16 activations + float16 h rows (routed + shared) dominate
+    assert n >= 4096 * 2048 * 2 + (4096 * 8 + 4096) * 512 * 2
+    assert n < 64 << 20
+    assert bem.moe_workspace_size(qwen_dims(1)) > 0
+    assert bem.moe_workspace_size(qwen_dims(0)) > 0
+    assert bem.moe_workspace_size(qwen_dims(4096)) > bem.moe_workspace_size(qwen_dims(512))
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("H", 100, -2), ("I", 96, -2), ("top_k", 0, -2), ("top_k", 300, -2), ("T", -1, -2), ("E", 0, -2),
+    ("group", 32, -3), ("E", 512, -3), ("top_k", 9, -3), ("H", 32768, -3), ("I_shared", 1024, -3),
+    ("out_dtype", 0, -3), ("sb_dtype", 7, -2),
+])
+def test_invalid_dims(lib, field, value, status):
+    d = qwen_dims(8, **{field: value})
+    assert bem.moe_workspace_size(d) == 0
+    ws = FAKE
+    st = lib.moe_permute(C.byref(d), FAKE, FAKE, FAKE, FAKE, ws, 1 << 30, None)
+    assert st == status
+    st = lib.moe_route(C.byref(d), FAKE, FAKE, None, FAKE, FAKE, None)
+    assert st == status
+
+
+def _weights(ptr=FAKE, shared=True):
+    q = bem.QMat(ptr, ptr, ptr)
+    f = bem.Ffn(q, q, q)
+    return bem.Weights(ptr, None, f, f if shared else bem.Ffn())
+
+
+def test_layer_argument_checks(lib):
+    d = qwen_dims(8)
+    need = bem.moe_workspace_size(d)
+    w = _weights()
+    assert lib.moe_layer(C.byref(d), None, FAKE, FAKE, None, None, None, FAKE, need, None) == -1
+    assert lib.moe_layer(C.byref(d), C.byref(w), None, FAKE, None, None, None, FAKE, need, None) == -1
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE + 2, FAKE, None, None, None, FAKE, need, None) == -4
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, None, None, None, FAKE + 16, need, None) == -4
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, None, None, None, FAKE, need - 1, None) == -5
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, None, None, None, None, need, None) == -1
+    bad = _weights()
+    bad.experts.down.scale = None
+    assert lib.moe_layer(C.byref(d), C.byref(bad), FAKE, FAKE, None, None, None, FAKE, need, None) == -1
+    bad = _weights()
+    bad.experts.up.q = FAKE + 4
+    assert lib.moe_layer(C.byref(d), C.byref(bad), FAKE, FAKE, None, None, None, FAKE, need, None) == -4
+    noshared = _weights(shared=False)
+    assert lib.moe_layer(C.byref(d), C.byref(noshared), FAKE, FAKE, None, None, None, FAKE, need, None) == -1
+    d0 = qwen_dims(8, I_shared=0)
+    assert lib.moe_layer(C.byref(d0), C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -2
+    assert lib.moe_layer(None, C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -1
+
+
+def test_empty_call_enqueues_nothing(lib):
+    d = qwen_dims(0)
+    assert lib.moe_layer(C.byref(d), None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.moe_route(C.byref(d), None, None, None, None, None, None) == 0
+    assert lib.moe_combine(C.byref(d), None, None, None, None, None) == 0
+
+
+def test_other_calls_check_arguments(lib):
+    d = qwen_dims(8)
+    need = bem.moe_workspace_size(d)
+    f = bem.Ffn(bem.QMat(FAKE, FAKE, FAKE), bem.QMat(FAKE, FAKE, FAKE), bem.QMat(FAKE, FAKE, FAKE))
+    assert lib.moe_route(C.byref(d), FAKE, FAKE, FAKE + 8, FAKE, FAKE, None) == -4
+    assert lib.moe_route(C.byref(d), FAKE, None, None, FAKE, FAKE, None) == -1
+    assert lib.moe_permute(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, need - 256, None) == -5
+    assert lib.moe_expert_ffn(C.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, need, None) == -1
+    assert lib.moe_expert_ffn(C.byref(d), FAKE, FAKE, FAKE, C.byref(f), None, None, None, FAKE, need, None) == -1
+    assert lib.moe_combine(C.byref(d), FAKE, FAKE, FAKE + 4, FAKE, None) == -4
+    assert lib.moe_combine(C.byref(d), FAKE, None, None, FAKE, None) == -1
+
+
+def test_status_strings(lib):
+    for code in bem.STATUS:
+        assert len(bem.status_string(code)) >= 2
+    assert "workspace" in bem.status_string(-5)

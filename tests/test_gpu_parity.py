@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (per the layer's contract): expert indices as per-token sets and
+per-expert counts bit-exact; routing weights matched by expert index within
+1e-5; outputs within max|err| <= 2e-2 * RMS(oracle output).  Several results are
+correct for the slot order inside a token and the row order inside an expert
+bucket, so those are compared as sets.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import moe_synth
+import oracle
+from oracle import tie_filter
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def bem():
+    import bit_expert_grouped_amd as m
+
+    m.lib()
+    return m
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(np.asarray(a, dtype=np.float64)))))
+
+
+def assert_close(gpu, ref, what):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    err = np.abs(gpu - ref).max()
+    bound = TOL * rms(ref)
+    print("%s: max|err| = %.3e, 2e-2*RMS = %.3e, ratio %.4f" % (what, err, bound, err / bound))
+    assert np.all(np.isfinite(gpu)), what + ": non-finite output"
+    assert err <= bound, what
+
+
+def assert_same_routing(idx_gpu, w_gpu, idx_ref, w_ref):
+    idx_gpu = np.asarray(idx_gpu)
+    w_gpu = np.asarray(w_gpu, dtype=np.float64)
+    assert idx_gpu.shape == idx_ref.shape
+    np.testing.assert_array_equal(np.sort(idx_gpu, axis=1), np.sort(idx_ref, axis=1))
+    og = np.argsort(idx_gpu, axis=1)
+    orf = np.argsort(idx_ref, axis=1)
+    wg = np.take_along_axis(w_gpu, og, 1)
+    wr = np.take_along_axis(w_ref, orf, 1)
+    assert np.abs(wg - wr).max() <= 1e-5
+    assert np.abs(w_gpu.sum(axis=1) - 1).max() <= 1e-5
+
+
+@functools.lru_cache(maxsize=None)
+def case(name, layer=0, n_sample=None):
+    """Seeded inputs of a config plus the oracle's result (on a token sample when given)."""
+    cfg = moe_synth.CONFIGS[name]
+    w = moe_synth.layer_weights(cfg, layer)
+    x = tie_filter.tokens(name)
+    T = x.shape[0]
+    tokens = None
+    if n_sample is not None and n_sample < T:
+        rng = np.random.default_rng(1234 + layer)
+        tokens = np.sort(rng.choice(T, n_sample, replace=False)).astype(np.int32)
+        tokens[0] = 0
+        tokens[-1] = T - 1
+    ref = oracle.moe_layer(w, x, cfg.shape.top_k, tokens=tokens)
+    return cfg, w, x, tokens, ref
+
+
+def run_layer(w, x, top_k):
+    m = bem()
+    lw = m.upload_weights(w)
+    xt = m.bf16_tensor(x)
+    out, idx, wt, counts = m.moe_layer(xt, lw, top_k, want_routing=True)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy(), counts.cpu().numpy()
+
+
+# ------------------------------------------------------------------ whole layer on the configs
+
+
+@pytest.mark.parametrize("name,n_sample", [("tiny", None), ("decode", None), ("decode64", None),
+                                           ("prefill512", 48), ("prefill4096", 32)])
+def test_layer_config(name, n_sample):
+    cfg, w, x, tokens, ref = case(name, 0, n_sample)
+    print("case", name, "T", x.shape[0], flush=True)
+    out, idx, wt, counts = run_layer(w, x, cfg.shape.top_k)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    sel = out if tokens is None else out[tokens]
+    assert_close(sel, ref["out"], name)
+
+
+@pytest.mark.parametrize("layer", [0, 23])
+def test_layer_stack40_sampled_layers(layer):
+    cfg, w, x, tokens, ref = case("stack40", layer, 16)
+    print("case stack40 layer", layer, flush=True)
+    out, idx, wt, counts = run_layer(w, x, cfg.shape.top_k)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert counts.max() > 1000  # skewed: the hottest expert spans many row tiles
+    assert_close(out[tokens], ref["out"], "stack40 layer %d" % layer)
+
+
+# ------------------------------------------------------------------ step-by-step ABI
+
+
+def test_route_step():
+    cfg, w, x, _, ref = case("decode64")
+    m = bem()
+    idx, wt = m.moe_route(m.bf16_tensor(x), m.bf16_tensor(w["router"]), cfg.shape.top_k)
+    torch.cuda.synchronize()
+    assert_same_routing(idx.cpu().numpy(), wt.cpu().numpy(), ref["idx"], ref["w"])
+
+
+def test_route_step_with_logit_bias():
+    cfg = moe_synth.CONFIGS["stack40"]
+    x = tie_filter.tokens("stack40")[:256]
+    R = moe_synth.router_weights(cfg, 5)
+    b = moe_synth.zipf_bias(cfg, 5)
+    l = oracle.router_logits(x, R, b)
+    ref_idx, ref_w = oracle.select(l, cfg.shape.top_k)
+    m = bem()
+    idx, wt = m.moe_route(m.bf16_tensor(x), m.bf16_tensor(R), cfg.shape.top_k,
+                          logit_bias=torch.from_numpy(b).cuda())
+    torch.cuda.synchronize()
+    assert_same_routing(idx.cpu().numpy(), wt.cpu().numpy(), ref_idx, ref_w)
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (37, 8, 256), (4096, 8, 256), (16, 2, 16), (50, 3, 40), (9, 1, 1)])
+def test_permute_step(T, k, E):
+    rng = np.random.default_rng(T * 1000 + E)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts_r, offsets_r, ss_r = oracle.permute(idx, E)
+    m = bem()
+    counts, offsets, ss = m.moe_permute(torch.from_numpy(idx).cuda(), E)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(counts.cpu().numpy(), counts_r)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), offsets_r)
+    ss = ss.cpu().numpy()[: T * k]
+    for e in range(E):
+        a, b = offsets_r[e], offsets_r[e + 1]
+        np.testing.assert_array_equal(np.sort(ss[a:b]), ss_r[a:b])
+
+
+def _slot_reference(w, x, idx, slots, k):
+    """oracle expert outputs for the given slots (t*k+j)."""
+    out = {}
+    by_e = {}
+    for s in slots:
+        by_e.setdefault(int(idx.ravel()[s]), []).append(int(s))
+    for e, ss in by_e.items():
+        ex = tuple((w[m + "_q"][e], w[m + "_s"][e], w[m + "_b"][e]) for m in ("gate", "up", "down"))
+        y = oracle.expert_ffn(*ex, x[[s // k for s in ss]])
+        for s, row in zip(ss, y):
+            out[s] = row
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode64", "prefill512"])
+def test_expert_ffn_and_combine_steps(name):
+    cfg, w, x, _, ref = case(name, 0, 48 if name == "prefill512" else None)
+    k = cfg.shape.top_k
+    m = bem()
+    lw = m.upload_weights(w)
+    xt = m.bf16_tensor(x)
+    offsets = torch.from_numpy(ref["offsets"]).cuda()
+    ss = torch.from_numpy(ref["sorted_slot"]).cuda()
+    y_slot, y_shared = m.moe_expert_ffn(xt, offsets, ss, lw, k)
+    torch.cuda.synchronize()
+    y_slot = y_slot.cpu().numpy()
+    y_shared = y_shared.cpu().numpy()
+    rng = np.random.default_rng(7)
+    slots = rng.choice(x.shape[0] * k, min(64, x.shape[0] * k), replace=False)
+    yr = _slot_reference(w, x, ref["idx"], slots, k)
+    assert_close(y_slot[slots], np.stack([yr[s] for s in slots]), name + " y_slot")
+    toks = np.unique(slots // k)[:16]
+    ex = tuple((w["shared_" + mm + "_q"][0], w["shared_" + mm + "_s"][0], w["shared_" + mm + "_b"][0])
+               for mm in ("gate", "up", "down"))
+    assert_close(y_shared[toks], oracle.expert_ffn(*ex, x[toks]), name + " y_shared")
+
+
+def test_combine_step():
+    rng = np.random.default_rng(3)
+    T, k, H = 37, 8, 2048
+    y_slot = rng.standard_normal((T * k, H)).astype(np.float32)
+    y_sh = rng.standard_normal((T, H)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    ref = oracle.combine(y_slot.reshape(T, k, H), w, y_sh)
+    m = bem()
+    out = m.moe_combine(torch.from_numpy(y_slot).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(y_sh).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+    out2 = m.moe_combine(torch.from_numpy(y_slot).cuda(), torch.from_numpy(w).cuda(), None)
+    ref2 = oracle.combine(y_slot.reshape(T, k, H), w, None)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out2.cpu().numpy(), ref2, rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------------------ edge cases
+
+
+def _custom(T, H, E, k, I, Is, bf16=True, seed=77, bias=None):
+    cfg = moe_synth.Config("custom", moe_synth.Shape(T=T, H=H, E=E, top_k=k, I=I, I_shared=Is, sb_bf16=bf16),
+                           seed=seed)
+    w = moe_synth.layer_weights(cfg)
+    if bias is not None:
+        w["logit_bias"] = bias
+    x = tie_filter.tokens_for(cfg, w["router"], bias)
+    return cfg, w, x
+
+
+@pytest.mark.parametrize("T,H,E,k,I,bf16", [
+    (37, 2048, 256, 8, 512, True),     # ragged token count, real shapes
+    (129, 512, 64, 4, 128, False),     # ragged, several row tiles per expert
+    (5, 256, 40, 3, 64, True),         # E not a multiple of 32
+    (6, 128, 8, 8, 64, True),          # k == E
+    (7, 192, 1, 1, 192, False),        # single expert
+])
+def test_edge_shapes(T, H, E, k, I, bf16):
+    cfg, w, x = _custom(T, H, E, k, I, I, bf16)
+    ref = oracle.moe_layer(w, x, k)
+    out, idx, wt, counts = run_layer(w, x, k)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out, ref["out"], "edge T%d H%d E%d k%d I%d" % (T, H, E, k, I))
+
+
+def test_hot_expert_spans_many_tiles():
+    bias = np.zeros(32, dtype=np.float32)
+    bias[5] = 50.0
+    cfg, w, x = _custom(300, 256, 32, 2, 128, 128, True, bias=bias)
+    ref = oracle.moe_layer(w, x, 2)
+    out, idx, wt, counts = run_layer(w, x, 2)
+    assert counts[5] == 300
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out, ref["out"], "hot expert")
+
+
+def test_no_shared_expert():
+    cfg, w, x = _custom(20, 256, 16, 2, 64, 64, True)
+    w = {key: v for key, v in w.items() if not key.startswith("shared_")}
+    ref = oracle.moe_layer(w, x, 2)
+    m = bem()
+    lw = m.upload_weights(w)
+    assert lw.I_shared == 0
+    out = m.moe_layer(m.bf16_tensor(x), lw, 2)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref["out"], "no shared expert")
+
+
+def test_empty_batch_is_a_noop():
+    import ctypes
+
+    cfg, w, x = _custom(4, 256, 16, 2, 64, 64)
+    m = bem()
+    lw = m.upload_weights(w)
+    out = torch.full((1, 256), 7.0, device="cuda")
+    d = lw.dims(0, 2)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    st = m.lib().moe_layer(ctypes.byref(d), ctypes.byref(lw.struct), None, out.data_ptr(), None, None, None,
+                           ws.data_ptr(), ws.numel(), m._stream())
+    torch.cuda.synchronize()
+    assert st == 0
+    assert float(out[0, 0]) == 7.0
+
+
+# ------------------------------------------------------------------ invariances
+
+
+def test_batch_invariance_and_repeatability():
+    cfg, w, x, _, ref = case("decode64")
+    k = cfg.shape.top_k
+    out, idx, wt, counts = run_layer(w, x, k)
+    out2, idx2, _, counts2 = run_layer(w, x, k)
+    np.testing.assert_array_equal(idx, idx2)
+    np.testing.assert_array_equal(counts, counts2)
+    for t in (0, 17, 63):
+        o1, i1, _, _ = run_layer(w, x[t:t + 1], k)
+        np.testing.assert_array_equal(np.sort(i1[0]), np.sort(idx[t]))
+        assert np.abs(o1[0] - out[t]).max() <= 1e-3 * rms(out[t])
