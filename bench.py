@@ -1,0 +1,249 @@
+"""Benchmark of the 4-bit grouped-expert MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|decode64|prefill512|prefill4096|stack40]
+
+A step is one pass of the whole layer (router, permute, gate/up + SwiGLU, down +
+weighted combine + shared expert) over one batch of synthetic tokens, through the
+C ABI entry point ``moe_layer_events`` (``moe_layer`` plus a HIP event after each
+kernel, which gives the per-kernel durations inside the timed region).  Inputs
+are resident in HBM before timing starts.  Successive steps cycle through
+distinct weight sets drawn in device memory, so a step does not find the
+previous steps' weights in the 256 MB last-level cache, and use fresh
+activations.  The default workload is one decode step (T=1) of the
+Qwen3.6-35B-A3B layer shape (H=2048, 256 experts, top-8, shared expert, I=512).
+
+Prints one JSON line.  ``cpu_baseline`` times the CPU oracle (single-threaded
+C) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (prefill T=512/4096), decode µs/layer; % HBM / MFMA peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA, TFLOP/s
+
+WORKLOADS = {
+    # name: (config name, layers per step, bound of the dominant kernel, default weight sets)
+    "decode": ("decode", 1, "hbm", 40),
+    "decode64": ("decode64", 1, "hbm", 8),
+    "prefill512": ("prefill512", 1, "hbm", 4),
+    "prefill4096": ("prefill4096", 1, "mfma", 4),
+    "stack40": ("stack40", 40, "mfma", 40),
+}
+
+
+def expert_bytes(H, I, sb_bytes, group=64):
+    """Packed codes + scales + biases of one expert's gate, up and down matrices."""
+    mat = lambda N, K: N * K // 2 + 2 * N * (K // group) * sb_bytes  # noqa: E731
+    return {"gate_up": 2 * mat(I, H), "down": mat(H, I)}
+
+
+def stage_work(name, sh, T, touched, shared):
+    """Algorithmic bytes and flops of one launch of a stage.
+
+    touched: number of routed experts with at least one token (plus the shared
+    expert when present).  Bytes count what the step must move: the touched
+    experts' packed weights, scales and biases, the router, the activations read
+    and the results written; no padding, no re-reads."""
+    H, I, E, k = sh.H, sh.I, sh.E, sh.top_k
+    sb = 2 if sh.sb_bf16 else 4
+    eb = expert_bytes(H, I, sb)
+    rows = T * k + (T if shared else 0)
+    n_exp = touched + (1 if shared else 0)
+    if name == "router":
+        return E * H * 2 + T * H * 2 + T * k * 8 + T * H * 2 + T * H * 4, 2.0 * T * H * E
+    if name == "permute":
+        return T * k * 4 * 2 + E * 8, 0.0
+    if name == "gate_up":
+        return n_exp * eb["gate_up"] + T * H * 2 + rows * I * 2, 2.0 * rows * H * 2 * I
+    if name == "down_combine":
+        return n_exp * eb["down"] + rows * I * 2 + T * H * 4, 2.0 * rows * I * H
+    return 0, 0.0
+
+
+def cpu_baseline(cfg, T, seconds):
+    """Time the CPU oracle on a bounded sample of the workload (tokens/s)."""
+    import numpy as np
+
+    import moe_synth
+    import oracle
+
+    w = moe_synth.layer_weights(cfg)
+    n = T if T <= 4 else 4  # tokens per oracle call
+    x_all = moe_synth.token_rows(cfg, 64)
+    done_tokens, calls = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        x = x_all[(calls * n) % 64:(calls * n) % 64 + n]
+        oracle.moe_layer(w, x, cfg.shape.top_k)
+        done_tokens += x.shape[0]
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(done_tokens / el, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d oracle calls of %d token(s) each on one %s layer (H=%d, E=%d, top-%d, I=%d), "
+                      "%.1f s single-threaded; per-token cost includes routing all experts and dequantising "
+                      "every touched expert" % (calls, n, cfg.name, cfg.shape.H, cfg.shape.E, cfg.shape.top_k,
+                                                cfg.shape.I, el),
+            "seconds": round(el, 2), "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--weight-sets", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard by tokens or by experts; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_expert_grouped_amd as bem
+    import moe_synth
+
+    cfg_name, layers_per_step, bound, default_sets = WORKLOADS[args.workload]
+    cfg = moe_synth.CONFIGS[cfg_name]
+    sh = cfg.shape
+    T = sh.T
+    big = T >= 512
+    steps = args.steps if args.steps is not None else (20 if big else 200)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 20)
+    n_sets = args.weight_sets or default_sets
+    if layers_per_step > 1:
+        n_sets = layers_per_step
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bem.lib()
+    alpha = moe_synth.zipf_alpha() if cfg.zipf else None
+    sets = [bem.LayerWeights(moe_synth.device_layer(sh, cfg.seed, l, dev, alpha)) for l in range(n_sets)]
+    n_x = min(steps + warmup, 64) if not big else 4
+    xs = [moe_synth.device_tokens(sh, T, cfg.seed, i, dev) for i in range(n_x)]
+    d = sets[0].dims(T, sh.top_k)
+    ws = bem.workspace(d, dev)
+    out = torch.empty(T, sh.H, dtype=torch.float32, device=dev)
+    stages = bem.moe_layer_stages(d)
+    n_calls = steps * layers_per_step
+    counts = torch.zeros(n_calls, sh.E, dtype=torch.int32, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_calls)]
+    torch.cuda.synchronize()
+
+    def one_call(i, li, record):
+        w = sets[li % n_sets]
+        x = xs[i % n_x]
+        if record:
+            bem.moe_layer(x, w, sh.top_k, out=out, ws=ws, events=evs[i * layers_per_step + li],
+                          counts_out=counts[i * layers_per_step + li])
+        else:
+            bem.moe_layer(x, w, sh.top_k, out=out, ws=ws)
+
+    for i in range(warmup):
+        for li in range(layers_per_step):
+            one_call(i + 1000, li, False)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        for li in range(layers_per_step):
+            one_call(i, li, True)
+    stop.record()
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - t_host0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / steps
+
+    # per-stage durations inside the timed region
+    stage_us = {s: 0.0 for s in stages}
+    for e in evs:
+        for j, s in enumerate(stages):
+            stage_us[s] += e[j].elapsed_time(e[j + 1]) * 1000.0
+    for s in stages:
+        stage_us[s] /= n_calls
+    c = counts.cpu()
+    touched = float((c > 0).sum(dim=1).double().mean())
+    shared = sh.I_shared > 0
+    dominant = max(stages, key=lambda s: stage_us[s])
+    nbytes, flops = stage_work(dominant, sh, T, touched, shared)
+    dur_s = stage_us[dominant] * 1e-6
+    if bound == "hbm":
+        achieved = nbytes / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": dominant, "kernel_us": round(stage_us[dominant], 2),
+                 "algorithmic_bytes_per_launch": int(nbytes), "algorithmic_flops_per_launch": flops})
+
+    tokens = T * steps * layers_per_step
+    value = tokens / (total_ms / 1000.0)
+    layer_bytes = sum(stage_work(s, sh, T, touched, shared)[0] for s in stages)
+    layer_flops = sum(stage_work(s, sh, T, touched, shared)[1] for s in stages)
+    us_layer = total_ms * 1000.0 / n_calls
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "H": sh.H, "E": sh.E, "top_k": sh.top_k, "I": sh.I,
+                   "I_shared": sh.I_shared, "layers_per_step": layers_per_step, "weight_sets": n_sets,
+                   "weights": "affine 4-bit g64, bf16 scales/biases", "activations": "bf16",
+                   "products": "f16 MFMA, fp32 accumulation; router bf16 MFMA; fp32 output"},
+        "us_per_layer": round(us_layer, 3),
+        "layer_hbm_frac": round(layer_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_mfma_frac": round(layer_flops / (us_layer * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "touched_experts": round(touched, 2),
+        "stages_us": {s: round(v, 2) for s, v in stage_us.items()},
+        "host_wall_s": round(host_s, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, T, args.cpu_seconds)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ MOE_BF16, MOE_F32 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
-           "moe_status_string")
+           "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -67,7 +67,12 @@ def lib():
         L.moe_expert_ffn.argtypes = [D, P, P, P, C.POINTER(Ffn), C.POINTER(Ffn), P, P, P, C.c_size_t, P]
         L.moe_combine.argtypes = [D, P, P, P, P, P]
         L.moe_layer.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P]
-        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer"):
+        L.moe_layer_events.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P, P, C.c_int32]
+        L.moe_layer_stage_count.argtypes = [D]
+        L.moe_layer_stage_count.restype = C.c_int32
+        L.moe_layer_stage_name.argtypes = [D, C.c_int32]
+        L.moe_layer_stage_name.restype = C.c_char_p
+        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer", "moe_layer_events"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -228,8 +233,20 @@ def moe_combine(y_slot, topk_w, y_shared=None, out=None):
     return out
 
 
-def moe_layer(x, weights: LayerWeights, top_k, out=None, ws=None, want_routing=False):
-    """out [T][H] float32 = the whole MoE layer on bf16 activations x [T][H]."""
+def moe_layer_stages(d: Dims):
+    """Names of the kernels moe_layer launches for these dims."""
+    n = lib().moe_layer_stage_count(C.byref(d))
+    return [lib().moe_layer_stage_name(C.byref(d), i).decode() for i in range(n)]
+
+
+def moe_layer(x, weights: LayerWeights, top_k, out=None, ws=None, want_routing=False, events=None,
+              topk_idx_out=None, topk_w_out=None, counts_out=None):
+    """out [T][H] float32 = the whole MoE layer on bf16 activations x [T][H].
+
+    want_routing: also return (topk_idx, topk_w, counts), allocated here unless
+    given.  events: optional list of torch.cuda.Event (enable_timing=True), one
+    more than the number of stages; recorded around each kernel by
+    moe_layer_events."""
     import torch
 
     T, H = x.shape
@@ -238,13 +255,25 @@ def moe_layer(x, weights: LayerWeights, top_k, out=None, ws=None, want_routing=F
         ws = workspace(d, x.device)
     if out is None:
         out = torch.empty(T, H, dtype=torch.float32, device=x.device)
-    idx = w = counts = None
+    idx, w, counts = topk_idx_out, topk_w_out, counts_out
     if want_routing:
-        idx = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
-        w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
-        counts = torch.empty(weights.E, dtype=torch.int32, device=x.device)
-    _check(lib().moe_layer(C.byref(d), C.byref(weights.struct), _p(x), _p(out), _p(idx), _p(w), _p(counts), _p(ws),
-                           ws.numel(), _stream()), "moe_layer")
+        if idx is None:
+            idx = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+        if w is None:
+            w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+        if counts is None:
+            counts = torch.empty(weights.E, dtype=torch.int32, device=x.device)
+    if events is None:
+        _check(lib().moe_layer(C.byref(d), C.byref(weights.struct), _p(x), _p(out), _p(idx), _p(w), _p(counts),
+                               _p(ws), ws.numel(), _stream()), "moe_layer")
+    else:
+        for e in events:
+            if not e.cuda_event:  # torch creates the HIP event lazily, on first record
+                e.record()
+        arr = (C.c_void_p * len(events))(*[e.cuda_event for e in events])
+        _check(lib().moe_layer_events(C.byref(d), C.byref(weights.struct), _p(x), _p(out), _p(idx), _p(w),
+                                      _p(counts), _p(ws), ws.numel(), _stream(), C.cast(arr, C.c_void_p),
+                                      len(events)), "moe_layer_events")
     if want_routing:
         return out, idx, w, counts
     return out

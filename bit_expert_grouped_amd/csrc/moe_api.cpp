@@ -221,8 +221,14 @@ moe_status moe_combine(const moe_dims* d, const float* y_slot, const float* topk
     return MOE_OK;
 }
 
-moe_status moe_layer(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out, int32_t* topk_idx_out,
-                     float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+const char* const kPrefillStages[] = {"router", "permute", "gate_up", "down_combine"};
+constexpr int kPrefillStageCount = 4;
+
+moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out,
+                      int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream, hipEvent_t* events, int32_t n_events) {
     MOE_TRY(check_dims(d));
     if (d->T == 0) return MOE_OK;
     if (!wts) return MOE_ERR_NULL;
@@ -236,6 +242,11 @@ moe_status moe_layer(const moe_dims* d, const moe_weights* wts, const uint16_t* 
         return MOE_ERR_SHAPE;
     }
     MOE_TRY(check_ws(d, ws, ws_bytes));
+    if (events) {
+        if (n_events < kPrefillStageCount + 1) return MOE_ERR_SHAPE;
+        for (int i = 0; i <= kPrefillStageCount; i++)
+            if (!events[i]) return MOE_ERR_NULL;
+    }
     const Layout L = layout_of(d);
     int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
     float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
@@ -261,12 +272,44 @@ moe_status moe_layer(const moe_dims* d, const moe_weights* wts, const uint16_t* 
     p.experts = to_ptr(&wts->experts);
     p.shared_w = shared ? to_ptr(&wts->shared) : FfnPtr{};
 
+    auto mark = [&](int i) -> bool { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
+    if (!mark(0)) return MOE_ERR_HIP;
     HIP_TRY(launch_router(x, wts->router, wts->logit_bias, d->T, d->H, d->E, d->top_k, idx, w, x16, o, stream));
+    if (!mark(1)) return MOE_ERR_HIP;
     HIP_TRY(launch_permute(idx, d->T, d->top_k, d->E, shared, counts, offsets, sorted, at<Tile>(ws, L.tiles),
                            at<int32_t>(ws, L.n_tiles), stream));
+    if (!mark(2)) return MOE_ERR_HIP;
     HIP_TRY(launch_gateup(p, x16, h, stream));
+    if (!mark(3)) return MOE_ERR_HIP;
     HIP_TRY(launch_down(p, h, w, true, o, nullptr, nullptr, stream));
+    if (!mark(4)) return MOE_ERR_HIP;
     return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_layer(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out, int32_t* topk_idx_out,
+                     float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return layer_impl(d, wts, x, out, topk_idx_out, topk_w_out, counts_out, ws, ws_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_layer_events(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out,
+                            int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream, hipEvent_t* events, int32_t n_events) {
+    if (!events) return MOE_ERR_NULL;
+    return layer_impl(d, wts, x, out, topk_idx_out, topk_w_out, counts_out, ws, ws_bytes, stream, events,
+                      n_events);
+}
+
+int32_t moe_layer_stage_count(const moe_dims* d) {
+    if (check_dims(d) != MOE_OK || d->T == 0) return 0;
+    return kPrefillStageCount;
+}
+
+const char* moe_layer_stage_name(const moe_dims* d, int32_t i) {
+    const int32_t n = moe_layer_stage_count(d);
+    if (i < 0 || i >= n) return nullptr;
+    return kPrefillStages[i];
 }
 
 }  // extern "C"

@@ -149,6 +149,23 @@ moe_status moe_layer(const moe_dims *dims, const moe_weights *weights /* host */
                      const uint16_t *x, void *out, int32_t *topk_idx_out, float *topk_w_out,
                      int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Instrumentation variant of moe_layer: the same work, plus HIP events recorded
+ * on `stream` around its kernels.  events (host array) holds
+ * moe_layer_stage_count(dims) + 1 caller-created events: events[0] is recorded
+ * before the first kernel and events[i] right after kernel i (i >= 1).  Fewer
+ * events than that: MOE_ERR_SHAPE.  Adds one event record per kernel. */
+moe_status moe_layer_events(const moe_dims *dims, const moe_weights *weights /* host */,
+                            const uint16_t *x, void *out, int32_t *topk_idx_out, float *topk_w_out,
+                            int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t *events /* host */, int32_t n_events);
+
+/* Number of kernels moe_layer launches for these dims (host-only, pure; 0 when
+ * the dims are invalid or T == 0). */
+int32_t moe_layer_stage_count(const moe_dims *dims /* host */);
+
+/* Static name of kernel i (0-based) of moe_layer for these dims, or NULL. */
+const char *moe_layer_stage_name(const moe_dims *dims /* host */, int32_t i);
+
 /* Static English text for a status code (host). */
 const char *moe_status_string(moe_status status);
 
