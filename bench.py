@@ -2,15 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|decode64|prefill512|prefill4096|stack40]
 
-A step is one pass of the whole layer (router, permute, gate/up + SwiGLU, down +
-weighted combine + shared expert) over one batch of synthetic tokens, through the
-C ABI entry point ``moe_layer_events`` (``moe_layer`` plus a HIP event after each
-kernel, which gives the per-kernel durations inside the timed region).  Inputs
-are resident in HBM before timing starts.  Successive steps cycle through
-distinct weight sets drawn in device memory, so a step does not find the
-previous steps' weights in the 256 MB last-level cache, and use fresh
-activations.  The default workload is one decode step (T=1) of the
-Qwen3.6-35B-A3B layer shape (H=2048, 256 experts, top-8, shared expert, I=512).
+A step is one pass of the whole layer (routing, permute, gate/up + SwiGLU,
+down + weighted combine + shared expert) over one batch of synthetic tokens,
+through the C ABI entry point ``moe_layer``.  Inputs are resident in HBM before
+timing starts.  Successive steps cycle through distinct weight sets drawn in
+device memory, so a step does not find the previous steps' weights in the
+256 MB last-level cache, and use fresh activations.  The default workload is
+one decode step (T=1) of the Qwen3.6-35B-A3B layer shape (H=2048, 256 experts,
+top-8, shared expert, I=512).
+
+Launch: for T <= 64 the K timed steps are captured once into a HIP graph and
+replayed (how a decode loop issues a launch-bound layer); larger T launches
+eagerly.  The timed region carries no instrumentation.  Per-kernel durations
+for the roofline come from an instrumented replay of the same K steps through
+``moe_layer_events`` (HIP events around every kernel, on the launch stream).
 
 Prints one JSON line.  ``cpu_baseline`` times the CPU oracle (single-threaded
 C) on a bounded sample of the same workload.
@@ -18,6 +23,7 @@ C) on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -50,8 +56,8 @@ def expert_bytes(H, I, sb_bytes, group=64):
 def stage_work(name, sh, T, touched, shared):
     """Algorithmic bytes and flops of one launch of a stage.
 
-    touched: number of routed experts with at least one token (plus the shared
-    expert when present).  Bytes count what the step must move: the touched
+    touched: number of routed experts with at least one token; the shared expert
+    is added when present.  Bytes count what the step must move: the touched
     experts' packed weights, scales and biases, the router, the activations read
     and the results written; no padding, no re-reads."""
     H, I, E, k = sh.H, sh.I, sh.E, sh.top_k
@@ -59,14 +65,20 @@ def stage_work(name, sh, T, touched, shared):
     eb = expert_bytes(H, I, sb)
     rows = T * k + (T if shared else 0)
     n_exp = touched + (1 if shared else 0)
+    router = (E * H * 2 + T * H * 2, 2.0 * T * H * E)
+    gate_up = (n_exp * eb["gate_up"] + T * H * 2 + rows * I * 2, 2.0 * rows * H * 2 * I)
+    down = (n_exp * eb["down"] + rows * I * 2 + T * H * 4, 2.0 * rows * I * H)
     if name == "router":
-        return E * H * 2 + T * H * 2 + T * k * 8 + T * H * 2 + T * H * 4, 2.0 * T * H * E
+        return router[0] + T * k * 8 + T * H * 2 + T * H * 4, router[1]
     if name == "permute":
         return T * k * 4 * 2 + E * 8, 0.0
     if name == "gate_up":
-        return n_exp * eb["gate_up"] + T * H * 2 + rows * I * 2, 2.0 * rows * H * 2 * I
+        return gate_up
     if name == "down_combine":
-        return n_exp * eb["down"] + rows * I * 2 + T * H * 4, 2.0 * rows * I * H
+        return down
+    if name == "decode_layer":  # the whole layer in one kernel: router + all touched experts + output
+        return (router[0] + n_exp * (eb["gate_up"] + eb["down"]) + T * H * 4,
+                router[1] + gate_up[1] + down[1])
     return 0, 0.0
 
 
@@ -117,6 +129,9 @@ def main():
     ap.add_argument("--weight-sets", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("eager", "graph"), default=None,
+                    help="graph: replay one HIP graph holding the K timed steps (default for T <= 64); "
+                         "eager: one foreign call per layer call")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -156,35 +171,100 @@ def main():
     n_calls = steps * layers_per_step
     counts = torch.zeros(n_calls, sh.E, dtype=torch.int32, device=dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_calls)]
+    mode = args.mode or ("graph" if T <= 64 else "eager")
     torch.cuda.synchronize()
 
-    def one_call(i, li, record):
-        w = sets[li % n_sets]
-        x = xs[i % n_x]
-        if record:
-            bem.moe_layer(x, w, sh.top_k, out=out, ws=ws, events=evs[i * layers_per_step + li],
-                          counts_out=counts[i * layers_per_step + li])
-        else:
-            bem.moe_layer(x, w, sh.top_k, out=out, ws=ws)
+    # Pre-built argument tuples of the C entry points: the timed loop is one
+    # foreign call per layer call.
+    stream = torch.cuda.current_stream()
+    lib = bem.lib()
+    dref = ctypes.byref(d)
+    for e in evs:
+        for ev in e:
+            ev.record()
+    torch.cuda.synchronize()
 
+    def call_args(i, li, s_handle, with_events):
+        w = sets[li % n_sets] if layers_per_step > 1 else sets[i % n_sets]
+        x = xs[i % n_x]
+        c = i * layers_per_step + li
+        base = (dref, ctypes.byref(w.struct), x.data_ptr(), out.data_ptr(), None, None, None, ws.data_ptr(),
+                ws.numel(), s_handle)
+        if not with_events:
+            return base
+        arr = (ctypes.c_void_p * len(evs[c]))(*[ev.cuda_event for ev in evs[c]])
+        return base + (ctypes.cast(arr, ctypes.c_void_p), len(evs[c])), arr
+
+    def run_eager(i_offset, record):
+        keep = []
+        for i in range(steps):
+            for li in range(layers_per_step):
+                if record:
+                    a, arr = call_args(i, li, stream.cuda_stream, True)
+                    keep.append(arr)
+                    st = lib.moe_layer_events(*a)
+                else:
+                    st = lib.moe_layer(*call_args(i + i_offset, li, stream.cuda_stream, False))
+                if st != 0:
+                    raise bem.MoeError(st, "moe_layer")
+        return keep
+
+    # warm-up (eager)
     for i in range(warmup):
         for li in range(layers_per_step):
-            one_call(i + 1000, li, False)
+            st = lib.moe_layer(*call_args(i + 1000, li, stream.cuda_stream, False))
+            if st != 0:
+                raise bem.MoeError(st, "moe_layer")
     torch.cuda.synchronize()
 
+    def capture(with_events):
+        """One HIP graph holding all K steps (and, instrumented, the per-kernel events)."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            prepared = [call_args(i, li, side.cuda_stream, with_events)
+                        for i in range(steps) for li in range(layers_per_step)]
+            with torch.cuda.graph(g, stream=side):
+                for a in prepared:
+                    st = lib.moe_layer_events(*a[0]) if with_events else lib.moe_layer(*a)
+                    if st != 0:
+                        raise bem.MoeError(st, "moe_layer (capture)")
+        torch.cuda.synchronize()
+        g.replay()  # one untimed replay
+        torch.cuda.synchronize()
+        return g, prepared
+
+    plain = capture(False)[0] if mode == "graph" else None
+
+    # ---- timed region: exactly K steps, no instrumentation ----
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_host0 = time.perf_counter()
     start.record()
-    for i in range(steps):
-        for li in range(layers_per_step):
-            one_call(i, li, True)
+    if plain is not None:
+        plain.replay()
+    else:
+        for i in range(steps):
+            for li in range(layers_per_step):
+                st = lib.moe_layer(*call_args(i, li, stream.cuda_stream, False))
+                if st != 0:
+                    raise bem.MoeError(st, "moe_layer")
     stop.record()
     torch.cuda.synchronize()
     host_s = time.perf_counter() - t_host0
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / steps
+
+    # ---- instrumented replay of the same K steps: HIP events around every kernel ----
+    if mode == "graph":
+        inst, _keep = capture(True)
+        torch.cuda.synchronize()
+        inst.replay()
+    else:
+        _keep = run_eager(0, True)
+    torch.cuda.synchronize()
 
     # per-stage durations inside the timed region
     stage_us = {s: 0.0 for s in stages}
@@ -193,7 +273,17 @@ def main():
             stage_us[s] += e[j].elapsed_time(e[j + 1]) * 1000.0
     for s in stages:
         stage_us[s] /= n_calls
+    # experts touched per call (outside the timed region: the same calls again,
+    # with the per-expert counts requested)
+    for i in range(min(steps, 16)):
+        for li in range(layers_per_step if layers_per_step <= 4 else 4):
+            a = call_args(i, li, stream.cuda_stream, False)
+            st = lib.moe_layer(*(a[:6] + (counts[i * layers_per_step + li].data_ptr(),) + a[7:]))
+            if st != 0:
+                raise bem.MoeError(st, "moe_layer")
+    torch.cuda.synchronize()
     c = counts.cpu()
+    c = c[(c.sum(dim=1) > 0)]
     touched = float((c > 0).sum(dim=1).double().mean())
     shared = sh.I_shared > 0
     dominant = max(stages, key=lambda s: stage_us[s])
@@ -237,7 +327,10 @@ def main():
         "layer_mfma_frac": round(layer_flops / (us_layer * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
         "touched_experts": round(touched, 2),
         "stages_us": {s: round(v, 2) for s, v in stage_us.items()},
+        "stages_note": "per-kernel durations from HIP events around each kernel in an instrumented replay of "
+                       "the same K steps (the timed region itself carries no per-kernel events)",
         "host_wall_s": round(host_s, 4),
+        "launch": mode,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

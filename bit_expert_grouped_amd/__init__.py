@@ -109,13 +109,14 @@ def moe_workspace_size(d: Dims) -> int:
 
 
 def workspace(d: Dims, device="cuda"):
-    """A workspace tensor of moe_workspace_size(d) bytes (torch allocations are 256-byte aligned)."""
+    """A zeroed workspace tensor of moe_workspace_size(d) bytes (torch allocations are 256-byte aligned)."""
     import torch
 
     n = moe_workspace_size(d)
     if n == 0:
         raise MoeError(-2, "moe_workspace_size")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    # the library requires a zero-filled workspace before its first use
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------- weights

@@ -64,4 +64,93 @@ __device__ __forceinline__ half2_t splat_half2(float v) {
     return r;
 }
 
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ void argmax_dpp_step(float& bv, int& bi) {
+    const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), kCtrl, 0xF, 0xF, false));
+    const int oi = __builtin_amdgcn_mov_dpp(bi, kCtrl, 0xF, 0xF, false);
+    if (ranks_before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
+// Wave-wide arg-max of (value desc, index asc): DPP butterflies inside each row
+// of 16 lanes (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four
+// row winners through readlane.  Every lane receives the winner.
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+    argmax_dpp_step<0xB1>(bv, bi);   // quad_perm 1,0,3,2
+    argmax_dpp_step<0x4E>(bv, bi);   // quad_perm 2,3,0,1
+    argmax_dpp_step<0x141>(bv, bi);  // row_half_mirror
+    argmax_dpp_step<0x140>(bv, bi);  // row_mirror
+    float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    int i = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+    for (int r = 1; r < 4; r++) {
+        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+        const int ri = __builtin_amdgcn_readlane(bi, 16 * r);
+        if (ranks_before(rv, ri, v, i)) {
+            v = rv;
+            i = ri;
+        }
+    }
+    bv = v;
+    bi = i;
+}
+
+// Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max on
+// (logit desc, expert index asc), then the softmax of the kept logits (equal to
+// the softmax over all E renormalised over the kept ones).  `logit(e)` returns
+// the logit of expert e < E.  Lane j < k receives rank j: idx_j and w_j.
+template <typename LogitFn>
+__device__ __forceinline__ void wave_topk(LogitFn logit, int E, int top_k, int lane, int* idx_j, float* w_j) {
+    float v[kMaxE / kWave];
+    int id[kMaxE / kWave];
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; i++) {
+        id[i] = lane + kWave * i;
+        v[i] = id[i] < E ? logit(id[i]) : -INFINITY;
+        if (id[i] >= E) id[i] = 0x7fffffff;
+    }
+    float kept_v[kMaxTopK];
+    int kept_i[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; j++) {
+        if (j >= top_k) break;
+        float bv = v[0];
+        int bi = id[0];
+#pragma unroll
+        for (int i = 1; i < kMaxE / kWave; i++) {
+            if (ranks_before(v[i], id[i], bv, bi)) {
+                bv = v[i];
+                bi = id[i];
+            }
+        }
+        wave_argmax(bv, bi);
+        kept_v[j] = bv;
+        kept_i[j] = bi;
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) {
+            if (id[i] == bi) v[i] = -INFINITY, id[i] = 0x7fffffff;
+        }
+    }
+    float z = 0.0f, wj = 0.0f;
+    int ij = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; j++) {
+        if (j >= top_k) break;
+        const float p = expf(kept_v[j] - kept_v[0]);
+        z += p;
+        if (j == lane) {
+            wj = p;
+            ij = kept_i[j];
+        }
+    }
+    *idx_j = ij;
+    *w_j = wj / z;
+}
+
 }  // namespace bitmoe

@@ -1,0 +1,556 @@
+// Decode path (a handful of tokens) for gfx950: ONE kernel per layer call, no
+// host sync.
+//
+// Pages: decode reads the weights every step, so it is bound by memory
+// bandwidth, not arithmetic; the engine treats it as a different workload from
+// prefill and overlaps the dependent stages of a decode step (aimanavo.com page,
+// section "Lily does not treat prefill and decode as the same job"); routing
+// stays on the GPU (same section; dzen.guru page, section "Where does the
+// speed-up come from?").
+//
+// At T <= kDecodeMaxT only ~9 of 257 experts are touched and every product is a
+// matrix-vector product, so there is no MFMA here.  Two facts of the hardware
+// shape the kernel: a compute unit sustains only a few tens of GB/s on its own
+// (its outstanding misses times the ~1-2 us memory latency), so the ~17 MB of a
+// step must be spread over every compute unit; and every hop between
+// workgroups costs a memory round trip, so the chain router -> gate/up -> down
+// has as few hops as possible and no arrival counters on it.
+//
+// Workgroup roles, in grid order (the grid is dispatched in order and every
+// role waits only on roles before it, so waits always terminate):
+//   router  [0, R)     R = E/4: one expert per wave, its logit for every token.
+//                      Also clears the output rows.
+//   gate/up [R, R+G)   one per (slot, 16-row block of the intermediate dim);
+//                      the shared expert is one more slot per token.  Waits for
+//                      its token's logits, ranks them itself (wave top-k), then
+//                      computes 16 values of h = silu(gate x) * (up x).
+//   down    [R+G, ...) one per (slot, 128 output rows).  Ranks like gate/up, has
+//                      its 32 KB of whole down rows land in LDS (direct loads,
+//                      issued before it waits for h), waits for the slot's h,
+//                      then adds w * (W_down h) for its rows to the float32
+//                      output with atomics (the fused combine: k+1 adds per
+//                      output element).
+// Values crossing workgroups (logits, h) are published as 64-bit words {epoch,
+// value} with L2-bypassing (agent-scope) stores and polled with L2-bypassing
+// loads: a consumer waits for the data itself, not for a counter.  The epoch is
+// one more than the control word the previous call left; the last workgroup to
+// finish stores it.  Waits are bounded: after kSpinLimit polls a workgroup sets
+// the error control word and carries on (that call's output is then invalid).
+//
+// Dot products run v_dot2_f32_f16 directly on exponent-trick codes: a word's low
+// nibbles become 1024+q and its high nibbles 64+q as float16, so
+//   sum_k q_k a_k = (sum over low of (1024+q) a) - 1024 * (sum over low of a)
+//                 + (sum over high of (64+q) a) -   64 * (sum over high of a)
+// and a group contributes scale * sum q a + bias * sum a: 9 VALU ops per word.
+#include "common.h"
+#include "kernels.h"
+
+namespace bitmoe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kRouterExperts = kWaves;  // one expert per wave
+constexpr int kGURows = 16;             // gate and up rows per gate/up workgroup
+constexpr int kDRows = 128;             // output rows per down workgroup
+constexpr long kSpinLimit = 1l << 20;
+
+// control words (uint32 indices into the workspace control block)
+constexpr int kCtlEpoch = 0;    // epoch of the last completed call
+constexpr int kCtlDone = 1;     // workgroups finished in this call
+constexpr int kCtlError = 255;  // nonzero: a wait timed out
+
+// float16 pairs of 8 activations in the order the exponent trick produces codes
+struct Pairs8 {
+    half2_t a04, a15, a26, a37;
+};
+
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+    // (w & mask) | magic in one VALU op; gfx950 allows one scalar operand, so the
+    // magic constant sits in a VGPR
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+    return r;
+}
+
+// accumulate one packed word (8 codes) against its 8 activations
+__device__ __forceinline__ void dot_word(uint32_t w, const Pairs8& p, float& acc_lo, float& acc_hi) {
+    const uint32_t w8 = w >> 8;
+    acc_lo = __builtin_amdgcn_fdot2(as_half2(and_or(w, 0x000F000Fu, 0x64006400u)), p.a04, acc_lo, false);
+    acc_hi = __builtin_amdgcn_fdot2(as_half2(and_or(w, 0x00F000F0u, 0x54005400u)), p.a15, acc_hi, false);
+    acc_lo = __builtin_amdgcn_fdot2(as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)), p.a26, acc_lo, false);
+    acc_hi = __builtin_amdgcn_fdot2(as_half2(and_or(w8, 0x00F000F0u, 0x54005400u)), p.a37, acc_hi, false);
+}
+
+__device__ __forceinline__ Pairs8 pairs_of(const uint4& v) {
+    Pairs8 p;
+    p.a04 = as_half2(v.x);
+    p.a15 = as_half2(v.y);
+    p.a26 = as_half2(v.z);
+    p.a37 = as_half2(v.w);
+    return p;
+}
+
+// 8 bf16 activations -> float16 pairs in nibble order; adds the low/high sums
+__device__ __forceinline__ Pairs8 pairs_from_bf16(const uint4& raw, float& lo, float& hi) {
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(&raw);
+    _Float16 h[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) h[i] = (_Float16)bf16_to_f32(b[i]);
+    lo += (float)h[0] + (float)h[4] + (float)h[2] + (float)h[6];
+    hi += (float)h[1] + (float)h[5] + (float)h[3] + (float)h[7];
+    Pairs8 p;
+    p.a04 = half2_t{h[0], h[4]};
+    p.a15 = half2_t{h[1], h[5]};
+    p.a26 = half2_t{h[2], h[6]};
+    p.a37 = half2_t{h[3], h[7]};
+    return p;
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// sum over aligned groups of n consecutive lanes (n a power of two <= 64); every
+// lane of a group receives the group's total
+__device__ __forceinline__ float group_sum(float v, int n) {
+    if (n >= 2) v += dpp<0xB1>(v);    // quad_perm 1,0,3,2
+    if (n >= 4) v += dpp<0x4E>(v);    // quad_perm 2,3,0,1
+    if (n >= 8) v += dpp<0x141>(v);   // row_half_mirror
+    if (n >= 16) v += dpp<0x140>(v);  // row_mirror
+    if (n >= 32) v += __shfl_xor(v, 16);
+    if (n >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Sum each of 8 per-lane values over the 64 lanes of a wave through an LDS
+// transpose (red: 64*9 floats of this wave).  Lane 8v receives the total of value v.
+__device__ __forceinline__ float wave_sum8(const float (&v)[8], float* red, int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) red[lane * 9 + i] = v[i];
+    const int which = lane / 8, part = lane % 8;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) s += red[(part * 8 + j) * 9 + which];
+    return group_sum(s, 8);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// {epoch, value} words crossing workgroups: agent-scope accesses bypass the
+// per-XCD L2, so no write-back or invalidate is needed
+__device__ __forceinline__ void publish(unsigned long long* p, unsigned epoch, float v) {
+    __hip_atomic_store(p, ((unsigned long long)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long peek(unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct RoleShared {
+    union {
+        float red[kWaves][kWave * 9];  // gate/up role: cross-lane sums
+        struct {
+            uint4 drows[kDRows * 16];  // 128 whole rows of up to 512 columns, landed by direct loads
+            uint4 dsb[2][256];         // scale and bias of those rows (when they fit)
+            _Float16 hh[kMaxDecodeI];  // the slot's h, each 8-column block in nibble order
+            float2 hsum[kMaxDecodeI / 8];  // low/high sums of h per 8 columns
+        } down;
+    };
+    float logits[kMaxE];  // this workgroup's token, once published
+    int ex;
+    float wgt;
+    int ok;
+};
+
+// Poll n published words until every one carries `epoch`; each thread handles
+// indices tid, tid + kThreads, ...; value i goes to keep(i, value).  Returns
+// false on timeout.
+template <typename Keep>
+__device__ bool await_published(unsigned long long* src, int n, unsigned epoch, Keep keep, unsigned* err) {
+    long spins = 0;
+    for (;;) {
+        int missing = 0;
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+            const unsigned long long w = peek(src + i);
+            if ((unsigned)(w >> 32) == epoch) {
+                keep(i, __uint_as_float((uint32_t)w));
+            } else {
+                missing = 1;
+            }
+        }
+        if (__syncthreads_or(missing) == 0) return true;
+        if (++spins > kSpinLimit) {
+            if (threadIdx.x == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// Wait for token t's published logits; for a routed slot, rank them and keep
+// the expert and weight of the slot's rank (slot % top_k).  The shared expert's
+// slots take expert 0 of the shared stack with weight 1.
+__device__ void route_slot(const DecodeArgs& p, int slot, int t, bool routed, unsigned epoch, RoleShared& sh) {
+    const bool ok = await_published(p.logits64 + (size_t)t * p.E, p.E, epoch,
+                                    [&](int i, float v) { sh.logits[i] = v; }, p.ctl + kCtlError);
+    if (!routed) {
+        if (threadIdx.x == 0) {
+            sh.ex = 0;
+            sh.wgt = 1.0f;
+            sh.ok = ok;
+        }
+    } else if (threadIdx.x < kWave) {
+        int ij;
+        float wj;
+        wave_topk([&](int e) { return sh.logits[e]; }, p.E, p.top_k, threadIdx.x, &ij, &wj);
+        if (threadIdx.x == slot % p.top_k) {
+            sh.ex = min(max(ij, 0), p.E - 1);  // in range even for non-finite logits
+            sh.wgt = wj;
+            sh.ok = ok;
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------ router role
+
+__device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShared& sh) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int H = p.H, T = p.T;
+    const int e = b * kRouterExperts + wave;
+    const int nblk = H / 8;  // 16-byte chunks of a row
+    // clear the output rows (write-through), then wait for those stores before
+    // the logits go out: a consumer that sees every logit sees cleared rows
+    for (int i = b * kThreads + tid; i < T * H; i += p.router_wgs * kThreads)
+        __hip_atomic_store(p.out + i, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    float acc[kDecodeMaxT];
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxT; t++) acc[t] = 0.0f;
+    const uint4* wr = reinterpret_cast<const uint4*>(p.router + (size_t)min(e, p.E - 1) * H);
+    for (int c0 = 0; c0 < nblk; c0 += 4 * kWave) {
+        uint4 a[4], xv[kDecodeMaxT][4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int c = min(c0 + lane + kWave * j, nblk - 1);
+            a[j] = wr[c];
+#pragma unroll
+            for (int t = 0; t < kDecodeMaxT; t++)
+                xv[t][j] = reinterpret_cast<const uint4*>(p.x + (size_t)min(t, T - 1) * H)[c];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if (c0 + lane + kWave * j >= nblk) continue;
+            const uint16_t* ab = reinterpret_cast<const uint16_t*>(&a[j]);
+#pragma unroll
+            for (int t = 0; t < kDecodeMaxT; t++) {
+                const uint16_t* xb = reinterpret_cast<const uint16_t*>(&xv[t][j]);
+#pragma unroll
+                for (int i = 0; i < 8; i++) acc[t] += bf16_to_f32(xb[i]) * bf16_to_f32(ab[i]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxT; t++) acc[t] = group_sum(acc[t], kWave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (lane == 0 && e < p.E) {
+        const float bias = p.logit_bias ? p.logit_bias[e] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < kDecodeMaxT; t++)
+            if (t < T) publish(p.logits64 + (size_t)t * p.E + e, epoch, acc[t] + bias);
+    }
+}
+
+// ------------------------------------------------------------------ gate/up role
+
+// kRouted: the slot belongs to a routed expert (else to the shared expert); a
+// template parameter so that each instantiation reads one weight set directly
+template <typename SB, bool kRouted>
+__device__ void gateup_role(const DecodeArgs& p, int slot, int blk, unsigned epoch, RoleShared& sh) {
+    const int H = p.H, I = p.I;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int TK = p.T * p.top_k;
+    constexpr bool routed = kRouted;
+    const int t = routed ? slot / p.top_k : slot - TK;
+    const int i0 = blk * kGURows;
+
+    // the shared expert does not depend on the routing and starts at once
+    if (routed) {
+        route_slot(p, slot, t, true, epoch, sh);
+    } else if (tid == 0) {
+        sh.ex = 0;
+        sh.ok = 1;
+    }
+    __syncthreads();
+    const size_t ex = (size_t)sh.ex;
+
+    const FfnPtr& f = kRouted ? p.experts : p.shared;
+    const uint32_t* g_q = f.gate.q;
+    const void* g_s = f.gate.s;
+    const void* g_b = f.gate.b;
+    const uint32_t* u_q = f.up.q;
+    const void* u_s = f.up.s;
+    const void* u_b = f.up.b;
+
+    // wave w owns rows i0+4w .. i0+4w+3 of gate and of up; lane l covers the
+    // input columns [32 l, 32 l + 32) (+2048 per further chunk pass)
+    constexpr int kRowsPerWave = kGURows / kWaves;  // 4
+    const int n_chunks = H / 32;
+    const int ng = H / kGroup;
+    const size_t row0 = ex * I + i0 + wave * kRowsPerWave;
+    const uint32_t* gq = g_q + row0 * (size_t)(H / 8);
+    const uint32_t* uq = u_q + row0 * (size_t)(H / 8);
+    const SB* gs = reinterpret_cast<const SB*>(g_s) + row0 * ng;
+    const SB* gb = reinterpret_cast<const SB*>(g_b) + row0 * ng;
+    const SB* us = reinterpret_cast<const SB*>(u_s) + row0 * ng;
+    const SB* ub = reinterpret_cast<const SB*>(u_b) + row0 * ng;
+    const uint4* xrow = reinterpret_cast<const uint4*>(p.x + (size_t)t * H);
+
+    float acc[8];  // gate rows 0..3, up rows 0..3
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = 0.0f;
+    for (int c0 = 0; c0 < n_chunks; c0 += kWave) {
+        const bool valid = c0 + lane < n_chunks;
+        const int c = min(c0 + lane, n_chunks - 1);
+        uint4 gv[kRowsPerWave], uv[kRowsPerWave], xr[4];
+        SB gsr[kRowsPerWave], gbr[kRowsPerWave], usr[kRowsPerWave], ubr[kRowsPerWave];
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; r++) {
+            gsr[r] = gs[(size_t)r * ng + c / 2];
+            gbr[r] = gb[(size_t)r * ng + c / 2];
+            usr[r] = us[(size_t)r * ng + c / 2];
+            ubr[r] = ub[(size_t)r * ng + c / 2];
+        }
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; r++) {
+            gv[r] = reinterpret_cast<const uint4*>(gq + (size_t)r * (H / 8))[c];
+            uv[r] = reinterpret_cast<const uint4*>(uq + (size_t)r * (H / 8))[c];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++) xr[m] = xrow[c * 4 + m];
+        __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the math
+
+        Pairs8 pr[4];
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; m++) pr[m] = pairs_from_bf16(xr[m], lo, hi);
+        const float vmask = valid ? 1.0f : 0.0f;
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; r++) {
+            float glo = 0.0f, ghi = 0.0f, ulo = 0.0f, uhi = 0.0f;
+            dot_word(gv[r].x, pr[0], glo, ghi);
+            dot_word(gv[r].y, pr[1], glo, ghi);
+            dot_word(gv[r].z, pr[2], glo, ghi);
+            dot_word(gv[r].w, pr[3], glo, ghi);
+            dot_word(uv[r].x, pr[0], ulo, uhi);
+            dot_word(uv[r].y, pr[1], ulo, uhi);
+            dot_word(uv[r].z, pr[2], ulo, uhi);
+            dot_word(uv[r].w, pr[3], ulo, uhi);
+            const float gqx = (glo - 1024.0f * lo) + (ghi - 64.0f * hi);
+            const float uqx = (ulo - 1024.0f * lo) + (uhi - 64.0f * hi);
+            acc[r] += vmask * (sb_to_f32<SB>(gsr[r]) * gqx + sb_to_f32<SB>(gbr[r]) * (lo + hi));
+            acc[4 + r] += vmask * (sb_to_f32<SB>(usr[r]) * uqx + sb_to_f32<SB>(ubr[r]) * (lo + hi));
+        }
+    }
+    const float total = wave_sum8(acc, sh.red[wave], lane);
+    // lane 8v holds value v: v < 4 gate row v, v >= 4 up row v-4
+    const float upv = __shfl(total, (lane + 32) & 63);
+    if (lane < 32 && lane % 8 == 0)
+        publish(p.h64 + (size_t)slot * I + i0 + wave * kRowsPerWave + lane / 8, epoch, silu(total) * upv);
+}
+
+// ------------------------------------------------------------------ down role
+
+template <typename SB, bool kRouted>
+__device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch, RoleShared& sh) {
+    const int H = p.H, I = p.I;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int TK = p.T * p.top_k;
+    constexpr bool routed = kRouted;
+    const int t = routed ? slot / p.top_k : slot - TK;
+    const int n0 = blk * kDRows;
+
+    // every down workgroup waits for its token's logits, shared ones too: the
+    // router clears the output rows before it publishes them
+    route_slot(p, slot, t, routed, epoch, sh);
+    const size_t ex = (size_t)sh.ex;
+    const float wgt = sh.wgt;
+    const FfnPtr& f = kRouted ? p.experts : p.shared;
+    const uint32_t* d_q = f.down.q;
+    const void* d_s = f.down.s;
+    const void* d_b = f.down.b;
+
+    // rows [n0, n0+128) land in LDS through direct loads: instruction j of wave w
+    // fills 64 consecutive 16-byte units of the row-major [row][I/32] block
+    const int gd = I / kGroup;
+    const int u_per_row = I / 32;  // 16-byte units per row
+    const int n_rows = min(kDRows, H - n0);
+    const int n_units = n_rows * u_per_row;
+    const uint4* dq = reinterpret_cast<const uint4*>(d_q + (ex * (size_t)H + n0) * (I / 8));
+    const bool rows_in_lds = u_per_row <= 16;  // I <= 512
+    if (rows_in_lds) {
+        for (int f0 = wave * kWave; f0 < n_units; f0 += kThreads)
+            __builtin_amdgcn_global_load_lds(dq + min(f0 + lane, n_units - 1), &sh.down.drows[f0], 16, 0, 0);
+    }
+    const SB* ds = reinterpret_cast<const SB*>(d_s) + (ex * (size_t)H + n0) * gd;
+    const SB* db = reinterpret_cast<const SB*>(d_b) + (ex * (size_t)H + n0) * gd;
+    // scale and bias of the rows are contiguous too: land them beside the rows
+    const int sb_units = n_rows * gd * (int)sizeof(SB) / 16;
+    const bool sb_in_lds = sb_units <= 256;
+    if (sb_in_lds && wave < 2) {
+        const uint4* src = reinterpret_cast<const uint4*>(wave == 0 ? ds : db);
+        for (int f0 = 0; f0 < sb_units; f0 += kWave)
+            __builtin_amdgcn_global_load_lds(src + min(f0 + lane, sb_units - 1), &sh.down.dsb[wave][f0], 16, 0, 0);
+    }
+    const SB* lds_s = reinterpret_cast<const SB*>(sh.down.dsb[0]);
+    const SB* lds_b = reinterpret_cast<const SB*>(sh.down.dsb[1]);
+
+    // wait for the slot's h; keep it as float16 in nibble order, then the
+    // low/high sums of every 8 columns
+    _Float16* hh = sh.down.hh;
+    const bool ok = await_published(p.h64 + (size_t)slot * I, I, epoch,
+                                    [&](int i, float v) { hh[(i & ~7) + slot_of_column(i & 7)] = (_Float16)v; },
+                                    p.ctl + kCtlError) &&
+                    sh.ok;
+    for (int b8 = tid; b8 < I / 8; b8 += kThreads) {
+        const _Float16* hv = hh + b8 * 8;  // 0,4,1,5,2,6,3,7
+        sh.down.hsum[b8] = make_float2((float)hv[0] + (float)hv[1] + (float)hv[4] + (float)hv[5],
+                                       (float)hv[2] + (float)hv[3] + (float)hv[6] + (float)hv[7]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
+    __syncthreads();
+
+    // thread (row r, group g): tpr threads per row, rows-per-pass = 256 / tpr
+    int tpr = 1;
+    while (tpr < gd) tpr <<= 1;
+    const int rpp = kThreads / tpr;
+    const int g = tid % tpr, r_in = tid / tpr;
+    float* orow = p.out + (size_t)t * H + n0;
+    for (int r0 = 0; r0 < n_rows; r0 += rpp) {
+        const int r = r0 + r_in;
+        float y = 0.0f;
+        if (g < gd && r < n_rows) {
+            uint4 v0, v1;
+            if (rows_in_lds) {
+                v0 = sh.down.drows[r * u_per_row + 2 * g];
+                v1 = sh.down.drows[r * u_per_row + 2 * g + 1];
+            } else {
+                v0 = dq[(size_t)r * u_per_row + 2 * g];
+                v1 = dq[(size_t)r * u_per_row + 2 * g + 1];
+            }
+            const uint4* hp4 = reinterpret_cast<const uint4*>(hh) + g * 8;
+            float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
+            const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                dot_word(wv[m], pairs_of(hp4[m]), alo, ahi);
+                const float2 sm = sh.down.hsum[g * 8 + m];
+                lo += sm.x;
+                hi += sm.y;
+            }
+            const SB sv = sb_in_lds ? lds_s[r * gd + g] : ds[(size_t)r * gd + g];
+            const SB bv = sb_in_lds ? lds_b[r * gd + g] : db[(size_t)r * gd + g];
+            y = sb_to_f32<SB>(sv) * ((alo - 1024.0f * lo) + (ahi - 64.0f * hi)) + sb_to_f32<SB>(bv) * (lo + hi);
+        }
+        y = group_sum(y, tpr);
+        if (g == 0 && r < n_rows && ok) atomicAdd(orow + r, wgt * y);
+    }
+}
+
+template <typename SB>
+__global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
+    __shared__ RoleShared sh;
+    unsigned epoch = __hip_atomic_load(p.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    if (epoch == 0) epoch = 1;  // words of a zero-filled workspace carry epoch 0
+    const int b = blockIdx.x;
+    if (b < p.router_wgs) {
+        router_role(p, b, epoch, sh);
+    } else if (b < p.router_wgs + p.gateup_wgs) {
+        const int unit = b - p.router_wgs, nblk = p.I / kGURows;
+        const int slot = unit / nblk, blk = unit % nblk;
+        if (slot < p.T * p.top_k)
+            gateup_role<SB, true>(p, slot, blk, epoch, sh);
+        else
+            gateup_role<SB, false>(p, slot, blk, epoch, sh);
+    } else {
+        const int unit = b - p.router_wgs - p.gateup_wgs, nblk = (p.H + kDRows - 1) / kDRows;
+        const int slot = unit / nblk, blk = unit % nblk;
+        if (slot < p.T * p.top_k)
+            down_role<SB, true>(p, slot, blk, epoch, sh);
+        else
+            down_role<SB, false>(p, slot, blk, epoch, sh);
+    }
+    // the last workgroup to finish advances the epoch for the next call
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = __hip_atomic_fetch_add(p.ctl + kCtlDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == gridDim.x - 1) {
+            __hip_atomic_store(p.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.ctl + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// routing outputs requested by the caller: a tiny second kernel (only when asked)
+__global__ __launch_bounds__(kThreads) void decode_routing_out_kernel(DecodeArgs p) {
+    __shared__ float lg[kMaxE];
+    __shared__ int ids[kDecodeMaxT * kMaxTopK];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const unsigned epoch = __hip_atomic_load(p.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = 0; t < p.T; t++) {
+        for (int e = tid; e < p.E; e += kThreads) {
+            const unsigned long long w = peek(p.logits64 + (size_t)t * p.E + e);
+            lg[e] = (unsigned)(w >> 32) == epoch ? __uint_as_float((uint32_t)w) : -INFINITY;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int ij;
+            float wj;
+            wave_topk([&](int e) { return lg[e]; }, p.E, p.top_k, lane, &ij, &wj);
+            if (lane < p.top_k) {
+                if (p.idx_out) p.idx_out[t * p.top_k + lane] = ij;
+                if (p.w_out) p.w_out[t * p.top_k + lane] = wj;
+                ids[t * p.top_k + lane] = ij;
+            }
+        }
+        __syncthreads();
+    }
+    if (p.counts_out) {
+        for (int e = tid; e < p.E; e += kThreads) {
+            int c = 0;
+            for (int s = 0; s < p.T * p.top_k; s++) c += ids[s] == e;
+            p.counts_out[e] = c;
+        }
+    }
+}
+
+}  // namespace
+
+int decode_router_wgs(int E) { return (E + kRouterExperts - 1) / kRouterExperts; }
+int decode_gateup_wgs(int T, int k, bool shared, int I) { return (T * k + (shared ? T : 0)) * (I / kGURows); }
+int decode_down_wgs(int T, int k, bool shared, int H) {
+    return (T * k + (shared ? T : 0)) * ((H + kDRows - 1) / kDRows);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, bool sb_bf16, hipStream_t stream) {
+    const dim3 grid(a.router_wgs + a.gateup_wgs + a.down_wgs);
+    if (sb_bf16)
+        hipLaunchKernelGGL(decode_layer_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(decode_layer_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (a.idx_out || a.w_out || a.counts_out) {
+        hipLaunchKernelGGL(decode_routing_out_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+        err = hipGetLastError();
+    }
+    return err;
+}
+
+}  // namespace bitmoe

@@ -72,6 +72,40 @@ hipError_t launch_gateup(const GemmProblem& p, const _Float16* x16, _Float16* h,
 hipError_t launch_down(const GemmProblem& p, const _Float16* h, const float* topk_w, bool combine,
                        float* out, float* y_slot, float* y_shared, hipStream_t stream);
 
+// Decode path (T <= kDecodeMaxT, I <= kMaxDecodeI): one kernel per call whose
+// router workgroups publish the logits, whose gate/up workgroups rank them and
+// publish h, and whose down workgroups combine into `out` with float32 atomics.
+// Values cross workgroups as {epoch, value} words in the decode region at the
+// start of the workspace (kDecodeRegionBytes, fixed for every dims, zero-filled
+// before first use); the control word kept there advances by one per call.
+constexpr int kDecodeMaxT = 4;
+constexpr int kMaxDecodeI = 4096;
+constexpr int kDecodeControlBytes = 1024;
+constexpr size_t kDecodeLogitBytes = (size_t)kDecodeMaxT * 256 * 8;
+constexpr size_t kDecodeHBytes = (size_t)kDecodeMaxT * (8 + 1) * kMaxDecodeI * 8;
+constexpr size_t kDecodeRegionBytes = kDecodeControlBytes + kDecodeLogitBytes + kDecodeHBytes;
+
+struct DecodeArgs {
+    int T, H, E, top_k, I;
+    int router_wgs, gateup_wgs, down_wgs;  // workgroups per role (decode_*_wgs)
+    const uint16_t* x;
+    const uint16_t* router;
+    const float* logit_bias;
+    unsigned* ctl;                  // control words
+    unsigned long long* logits64;   // [T][E] {epoch, logit}
+    unsigned long long* h64;        // [slots][I] {epoch, h}; slots = T*k routed, then T shared
+    int32_t* idx_out;               // optional copies of the routing
+    float* w_out;
+    int32_t* counts_out;
+    float* out;                     // [T][H]
+    FfnPtr experts, shared;         // shared.gate.q == nullptr: no shared expert
+};
+
+int decode_router_wgs(int E);
+int decode_gateup_wgs(int T, int k, bool shared, int I);
+int decode_down_wgs(int T, int k, bool shared, int H);
+hipError_t launch_decode(const DecodeArgs& a, bool sb_bf16, hipStream_t stream);
+
 hipError_t launch_combine(const float* y_slot, const float* topk_w, const float* y_shared, int T, int H,
                           int k, float* out, hipStream_t stream);
 

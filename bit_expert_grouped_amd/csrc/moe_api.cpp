@@ -37,7 +37,7 @@ moe_status check_dims(const moe_dims* d) {
 
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
-    size_t x16, h, idx, w, counts, offsets, sorted, tiles, n_tiles, total;
+    size_t ctl, logits64, h64, x16, h, idx, w, counts, offsets, sorted, tiles, n_tiles, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -47,6 +47,14 @@ Layout layout_of(const moe_dims* d) {
     const bool shared = d->I_shared > 0;
     Layout L;
     size_t o = 0;
+    // decode region: the same offsets and size for every dims, so that words
+    // another call left there are always {epoch, value} words
+    L.ctl = o;
+    o += kDecodeControlBytes;
+    L.logits64 = o;
+    o += kDecodeLogitBytes;
+    L.h64 = o;
+    o = up256(o + kDecodeHBytes);
     L.x16 = o;
     o = up256(o + T * H * 2);
     L.h = o;
@@ -225,6 +233,12 @@ namespace {
 
 const char* const kPrefillStages[] = {"router", "permute", "gate_up", "down_combine"};
 constexpr int kPrefillStageCount = 4;
+const char* const kDecodeStages[] = {"decode_layer"};
+constexpr int kDecodeStageCount = 1;
+
+bool use_decode_path(const moe_dims* d) { return d->T <= kDecodeMaxT && d->I <= kMaxDecodeI; }
+
+int stage_count(const moe_dims* d) { return use_decode_path(d) ? kDecodeStageCount : kPrefillStageCount; }
 
 moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out,
                       int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
@@ -242,12 +256,43 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         return MOE_ERR_SHAPE;
     }
     MOE_TRY(check_ws(d, ws, ws_bytes));
+    const int n_stages = stage_count(d);
     if (events) {
-        if (n_events < kPrefillStageCount + 1) return MOE_ERR_SHAPE;
-        for (int i = 0; i <= kPrefillStageCount; i++)
+        if (n_events < n_stages + 1) return MOE_ERR_SHAPE;
+        for (int i = 0; i <= n_stages; i++)
             if (!events[i]) return MOE_ERR_NULL;
     }
     const Layout L = layout_of(d);
+    auto mark = [&](int i) -> bool { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
+
+    if (use_decode_path(d)) {
+        DecodeArgs a;
+        a.T = d->T;
+        a.H = d->H;
+        a.E = d->E;
+        a.top_k = d->top_k;
+        a.I = d->I;
+        a.router_wgs = decode_router_wgs(d->E);
+        a.gateup_wgs = decode_gateup_wgs(d->T, d->top_k, shared, d->I);
+        a.down_wgs = decode_down_wgs(d->T, d->top_k, shared, d->H);
+        a.x = x;
+        a.router = wts->router;
+        a.logit_bias = wts->logit_bias;
+        a.ctl = at<unsigned>(ws, L.ctl);
+        a.logits64 = at<unsigned long long>(ws, L.logits64);
+        a.h64 = at<unsigned long long>(ws, L.h64);
+        a.idx_out = topk_idx_out;
+        a.w_out = topk_w_out;
+        a.counts_out = counts_out;
+        a.out = static_cast<float*>(out);
+        a.experts = to_ptr(&wts->experts);
+        a.shared = shared ? to_ptr(&wts->shared) : FfnPtr{};
+        if (!mark(0)) return MOE_ERR_HIP;
+        HIP_TRY(launch_decode(a, d->sb_dtype == MOE_BF16, stream));
+        if (!mark(1)) return MOE_ERR_HIP;
+        return MOE_OK;
+    }
+
     int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
     float* w = topk_w_out ? topk_w_out : at<float>(ws, L.w);
     int32_t* counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
@@ -272,7 +317,6 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     p.experts = to_ptr(&wts->experts);
     p.shared_w = shared ? to_ptr(&wts->shared) : FfnPtr{};
 
-    auto mark = [&](int i) -> bool { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
     if (!mark(0)) return MOE_ERR_HIP;
     HIP_TRY(launch_router(x, wts->router, wts->logit_bias, d->T, d->H, d->E, d->top_k, idx, w, x16, o, stream));
     if (!mark(1)) return MOE_ERR_HIP;
@@ -303,13 +347,13 @@ moe_status moe_layer_events(const moe_dims* d, const moe_weights* wts, const uin
 
 int32_t moe_layer_stage_count(const moe_dims* d) {
     if (check_dims(d) != MOE_OK || d->T == 0) return 0;
-    return kPrefillStageCount;
+    return stage_count(d);
 }
 
 const char* moe_layer_stage_name(const moe_dims* d, int32_t i) {
     const int32_t n = moe_layer_stage_count(d);
     if (i < 0 || i >= n) return nullptr;
-    return kPrefillStages[i];
+    return use_decode_path(d) ? kDecodeStages[i] : kPrefillStages[i];
 }
 
 }  // extern "C"

@@ -26,10 +26,6 @@ namespace {
 
 constexpr int kRouterTokens = 32;
 
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
-}
-
 template <bool kFused>
 __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ wr,
@@ -93,61 +89,10 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
     for (int r = wave * 8; r < wave * 8 + 8; r++) {
         const int t = t0 + r;
         if (t >= T) break;
-        float v[4];
-        int id[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            id[i] = lane + 64 * i;
-            v[i] = logits[r][id[i]];
-        }
-        float kept_v[kMaxTopK];
-        int kept_i[kMaxTopK];
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; j++) {
-            if (j >= top_k) break;
-            // best candidate of this lane
-            float bv = v[0];
-            int bi = id[0];
-#pragma unroll
-            for (int i = 1; i < 4; i++) {
-                if (ranks_before(v[i], id[i], bv, bi)) {
-                    bv = v[i];
-                    bi = id[i];
-                }
-            }
-            // wave-wide arg-max
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                float ov = __shfl_xor(bv, off);
-                int oi = __shfl_xor(bi, off);
-                if (ranks_before(ov, oi, bv, bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            kept_v[j] = bv;
-            kept_i[j] = bi;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (id[i] == bi) v[i] = -INFINITY, id[i] = 0x7fffffff;
-            }
-        }
-        // softmax of the kept logits (= softmax over all E, renormalised)
-        float z = 0.0f;
-        float wj = 0.0f;
-        int ij = 0;
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; j++) {
-            if (j >= top_k) break;
-            const float p = expf(kept_v[j] - kept_v[0]);
-            z += p;
-            if (j == lane) {
-                wj = p;
-                ij = kept_i[j];
-            }
-        }
+        int ij;
+        float wj;
+        wave_topk([&](int e) { return logits[r][e]; }, E, top_k, lane, &ij, &wj);
         if (lane < top_k) {
-            wj = wj / z;
             topk_idx[(size_t)t * top_k + lane] = ij;
             topk_w[(size_t)t * top_k + lane] = wj;
         }

@@ -102,7 +102,12 @@ typedef struct {
 
 /* Bytes of device workspace the calls below need for these dims (host-only,
  * pure; 0 when the dims are invalid).  One workspace serves every entry point.
- * Contents need no initialisation and are scratch between calls. */
+ * Zero-fill the whole workspace once after allocating it; after that, every
+ * call leaves it ready for the next one, whatever the dims of either.  The
+ * first 1024 bytes are control words: word 0 counts decode calls and word 255
+ * (bytes 1020..1023) is set to nonzero, and stays so, if a device-side wait of
+ * a decode call timed out (that call's output is then invalid).  Calls that
+ * share a workspace must not overlap in time (use one workspace per stream). */
 size_t moe_workspace_size(const moe_dims *dims /* host */);
 
 /* Router and top-k (pages: score every expert, keep top_k, on the GPU).
@@ -141,10 +146,15 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x, const int32_t
 moe_status moe_combine(const moe_dims *dims, const float *y_slot, const float *topk_w,
                        const float *y_shared, void *out, hipStream_t stream);
 
-/* The whole layer as one device-side pipeline: route, permute, gate/up with
- * SwiGLU, down with the weighted combine fused into its epilogue, shared expert
- * included.  out [T][H] float32.  Optional copies of the routing:
- * topk_idx_out [T][top_k], topk_w_out [T][top_k], counts_out [E] (each nullable). */
+/* The whole layer as one device-side pipeline, shared expert included;
+ * out [T][H] float32.  Optional copies of the routing: topk_idx_out [T][top_k],
+ * topk_w_out [T][top_k], counts_out [E] (each nullable).
+ * Prefill (T > 4): route, permute, gate/up with SwiGLU, down with the weighted
+ * combine fused into its epilogue.  Decode (T <= 4; pages: decode is a
+ * bandwidth-bound workload of its own): a single kernel whose router workgroups
+ * rank the experts on the device and whose expert workgroups run the SwiGLU
+ * experts and combine into out with atomics.  Uses the workspace's decode region
+ * and control words (see moe_workspace_size). */
 moe_status moe_layer(const moe_dims *dims, const moe_weights *weights /* host */,
                      const uint16_t *x, void *out, int32_t *topk_idx_out, float *topk_w_out,
                      int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream);

@@ -291,3 +291,113 @@ def test_batch_invariance_and_repeatability():
         o1, i1, _, _ = run_layer(w, x[t:t + 1], k)
         np.testing.assert_array_equal(np.sort(i1[0]), np.sort(idx[t]))
         assert np.abs(o1[0] - out[t]).max() <= 1e-3 * rms(out[t])
+
+
+# ------------------------------------------------------------------ decode path (T <= 4)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_decode_path_real_shapes(T):
+    cfg, w, x = _custom(T, 2048, 256, 8, 512, 512, True, seed=500 + T)
+    ref = oracle.moe_layer(w, x, 8)
+    out, idx, wt, counts = run_layer(w, x, 8)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out, ref["out"], "decode T=%d" % T)
+
+
+@pytest.mark.parametrize("T,H,E,k,I,bf16,shared", [
+    (3, 256, 16, 2, 64, False, True),
+    (2, 512, 40, 3, 128, True, True),
+    (1, 128, 8, 8, 64, True, False),
+    (4, 2560, 64, 4, 192, True, True),
+])
+def test_decode_path_other_shapes(T, H, E, k, I, bf16, shared):
+    cfg, w, x = _custom(T, H, E, k, I, I, bf16, seed=600 + T + E)
+    if not shared:
+        w = {key: v for key, v in w.items() if not key.startswith("shared_")}
+    ref = oracle.moe_layer(w, x, k)
+    out, idx, wt, counts = run_layer(w, x, k)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out, ref["out"], "decode T%d H%d E%d k%d I%d" % (T, H, E, k, I))
+
+
+def control_words(ws):
+    """(decode call counter, timeout flag) of a workspace."""
+    words = ws[:1024].view(torch.int32).cpu().numpy()
+    return int(words[0]), int(words[255])
+
+
+def test_decode_repeated_calls_and_control_words():
+    """Successive decode calls on one workspace each match the oracle; the call
+    counter advances by one per call and no wait times out."""
+    cfg, w, x = _custom(4, 2048, 256, 8, 512, 512, True, seed=700)
+    m = bem()
+    lw = m.upload_weights(w)
+    d = lw.dims(1, 8)
+    ws = m.workspace(d)
+    for t in range(4):
+        ref = oracle.moe_layer(w, x[t:t + 1], 8)
+        out = m.moe_layer(m.bf16_tensor(x[t:t + 1]), lw, 8, ws=ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref["out"], "decode call %d" % t)
+        assert control_words(ws) == (t + 1, 0)
+
+
+def test_workspace_shared_by_prefill_and_decode():
+    """One workspace serves prefill and decode calls of different dims in any
+    order: the decode region sits at fixed offsets, so what a prefill call wrote
+    can never pass for a published decode value."""
+    cfg, w, x = _custom(64, 2048, 256, 8, 512, 512, True, seed=710)
+    m = bem()
+    lw = m.upload_weights(w)
+    ws = m.workspace(lw.dims(64, 8))
+    calls = [64, 1, 3, 48, 4, 2, 64, 1]
+    for n, T in enumerate(calls):
+        xs = x[n % 3:n % 3 + T]
+        ref = oracle.moe_layer(w, xs, 8)
+        out = m.moe_layer(m.bf16_tensor(xs), lw, 8, ws=ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref["out"], "call %d T%d" % (n, T))
+    assert control_words(ws) == (sum(1 for T in calls if T <= 4), 0)
+
+
+# ------------------------------------------------------------------ HIP graph capture
+
+
+@pytest.mark.parametrize("T", [1, 37])
+def test_graph_replays_match_eager(T):
+    """moe_layer captured in a HIP graph: several replays, with new inputs copied in
+    eagerly between them, each match an eager call on the same inputs."""
+    cfg, w, x = _custom(3 * T, 2048, 256, 8, 512, 512, True, seed=800 + T)
+    m = bem()
+    lw = m.upload_weights(w)
+    d = lw.dims(T, 8)
+    ws = m.workspace(d)
+    xin = m.bf16_tensor(x[:T])
+    out = torch.empty(T, 2048, device="cuda")
+    idx = torch.empty(T, 8, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T, 8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        m.moe_layer(xin, lw, 8, out=out, ws=ws, want_routing=True, topk_idx_out=idx, topk_w_out=wt)  # warm-up
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            m.moe_layer(xin, lw, 8, out=out, ws=ws, want_routing=True, topk_idx_out=idx, topk_w_out=wt)
+    torch.cuda.synchronize()
+    ws_eager = m.workspace(d)
+    for rep in range(3):
+        xr = m.bf16_tensor(x[rep * T:(rep + 1) * T])
+        xin.copy_(xr)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_e, i_e, w_e, _ = m.moe_layer(xr, lw, 8, ws=ws_eager, want_routing=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(np.sort(idx.cpu().numpy(), 1), np.sort(i_e.cpu().numpy(), 1))
+        ref = o_e.cpu().numpy().astype(np.float64)
+        assert np.abs(out.cpu().numpy() - ref).max() <= 1e-3 * rms(ref)
+        assert control_words(ws)[1] == 0
