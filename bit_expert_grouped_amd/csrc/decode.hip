@@ -18,24 +18,39 @@
 //
 // Workgroup roles, in grid order (the grid is dispatched in order and every
 // role waits only on roles before it, so waits always terminate):
-//   router  [0, R)     R = E/4: one expert per wave, its logit for every token.
-//                      Also clears the output rows.
+//   router  [0, R)     R = E/4: one expert per wave, its logit for every token;
+//                      also clears the output rows.  Once every logit is out,
+//                      each router workgroup ranks its own experts against all
+//                      of them (one ballot per 64 logits) and publishes, for
+//                      each expert that made the top k, its logit and index
+//                      at its rank.
 //   gate/up [R, R+G)   one per (slot, 16-row block of the intermediate dim);
-//                      the shared expert is one more slot per token.  Waits for
-//                      its token's logits, ranks them itself (wave top-k), then
-//                      computes 16 values of h = silu(gate x) * (up x).
-//   down    [R+G, ...) one per (slot, 128 output rows).  Ranks like gate/up, has
-//                      its 32 KB of whole down rows land in LDS (direct loads,
-//                      issued before it waits for h), waits for the slot's h,
-//                      then adds w * (W_down h) for its rows to the float32
-//                      output with atomics (the fused combine: k+1 adds per
-//                      output element).
-// Values crossing workgroups (logits, h) are published as 64-bit words {epoch,
-// value} with L2-bypassing (agent-scope) stores and polled with L2-bypassing
-// loads: a consumer waits for the data itself, not for a counter.  The epoch is
-// one more than the control word the previous call left; the last workgroup to
-// finish stores it.  Waits are bounded: after kSpinLimit polls a workgroup sets
-// the error control word and carries on (that call's output is then invalid).
+//                      the shared expert is one more slot per token.  Reads
+//                      the k words of its token's top k, then computes 16
+//                      values of h = silu(gate x) * (up x).
+//   down    [R+G, ...) one per (slot, 128 output rows).  Reads the top k like
+//                      gate/up, has its 32 KB of whole down rows land in LDS
+//                      (direct loads, issued before it waits for h), waits for
+//                      the slot's h, then adds w * (W_down h) for its rows to
+//                      the float32 output with atomics (the fused combine: k+1
+//                      adds per output element).
+// Hand-over between workgroups.  Polling is what costs here: a poll waits
+// behind every load its compute unit has in flight, and hundreds of
+// workgroups polling many words flood the memory system that the weights are
+// streaming through.  So every poll is a few lanes on a few words:
+//   - logits and top-k entries are 64-bit words {epoch, value} written with
+//     L2-bypassing (agent-scope) stores; a reader waits for the words
+//     themselves.  The router workgroups read one of kXchReplicas copies of the
+//     logits, the expert workgroups one of kSelReplicas copies of the top k
+//     (lanes 0..k-1 of one wave poll them).  The epoch is one more than the
+//     control word the previous call left; the last workgroup to finish stores
+//     it.
+//   - h goes out as plain float32 (agent-scope stores); each gate/up workgroup
+//     then bumps its slot's counter, which one thread of each down workgroup
+//     polls before it reads the slot's h.  The last workgroup to finish resets
+//     the counters.
+// Waits are bounded: after kSpinLimit polls a workgroup sets the error control
+// word and carries on (that call's output is then invalid).
 //
 // Dot products run v_dot2_f32_f16 directly on exponent-trick codes: a word's low
 // nibbles become 1024+q and its high nibbles 64+q as float16, so
@@ -52,14 +67,23 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kRouterExperts = kWaves;  // one expert per wave
-constexpr int kGURows = 16;             // gate and up rows per gate/up workgroup
-constexpr int kDRows = 128;             // output rows per down workgroup
+constexpr int kXchReplicas = kDecodeXchReplicas;
+constexpr int kSelReplicas = kDecodeSelReplicas;
+constexpr size_t kXchWords = (size_t)kDecodeMaxT * kMaxE;     // one copy of the logits: [T][E]
+constexpr size_t kSelWords = (size_t)kDecodeMaxT * kMaxTopK;  // one copy of the top k: [T][k]
+constexpr int kGURows = 16;  // gate and up rows per gate/up workgroup
+constexpr int kDRows = 128;  // output rows per down workgroup
 constexpr long kSpinLimit = 1l << 20;
 
-// control words (uint32 indices into the workspace control block)
-constexpr int kCtlEpoch = 0;    // epoch of the last completed call
-constexpr int kCtlDone = 1;     // workgroups finished in this call
-constexpr int kCtlError = 255;  // nonzero: a wait timed out
+// control words (uint32 indices into the workspace control block); words that
+// many workgroups touch sit on lines of their own
+constexpr int kCtlEpoch = 0;      // epoch of the last completed call
+constexpr int kCtlDone = 64;      // workgroups finished in this call
+constexpr int kCtlError = 255;    // nonzero: a wait timed out
+constexpr int kCtlSlot0 = 512;    // gate/up workgroups of slot s whose h is out: word kCtlSlot0 + 64 s
+constexpr int kCtlSlotStride = 64;
+constexpr int kMaxSlots = kDecodeMaxT * (kMaxTopK + 1);
+static_assert(kCtlSlot0 + kCtlSlotStride * kMaxSlots <= kDecodeControlBytes / 4, "control block too small");
 
 // float16 pairs of 8 activations in the order the exponent trick produces codes
 struct Pairs8 {
@@ -139,14 +163,22 @@ __device__ __forceinline__ float wave_sum8(const float (&v)[8], float* red, int 
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// {epoch, value} words crossing workgroups: agent-scope accesses bypass the
-// per-XCD L2, so no write-back or invalidate is needed
-__device__ __forceinline__ void publish(unsigned long long* p, unsigned epoch, float v) {
-    __hip_atomic_store(p, ((unsigned long long)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+// {epoch, value} words and plain values crossing workgroups: agent-scope
+// accesses bypass the per-XCD L2, so no write-back or invalidate is needed
+__device__ __forceinline__ void publish(unsigned long long* p, unsigned epoch, uint32_t bits) {
+    __hip_atomic_store(p, ((unsigned long long)epoch << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned long long peek(unsigned long long* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ unsigned long long peek(const unsigned long long* p) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_error(unsigned* ctl) {
+    __hip_atomic_store(ctl + kCtlError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct RoleShared {
@@ -158,57 +190,124 @@ struct RoleShared {
             _Float16 hh[kMaxDecodeI];  // the slot's h, each 8-column block in nibble order
             float2 hsum[kMaxDecodeI / 8];  // low/high sums of h per 8 columns
         } down;
+        unsigned long long keys[kDecodeMaxT * kMaxE];  // router role: ranking keys [t][e]
     };
-    float logits[kMaxE];  // this workgroup's token, once published
     int ex;
     float wgt;
-    int ok;
+    int ok;       // routing read in time
+    int wait_ok;  // result of the last wait_count
+    int last;     // this workgroup finished last
 };
 
 // Poll n published words until every one carries `epoch`; each thread handles
-// indices tid, tid + kThreads, ...; value i goes to keep(i, value).  Returns
-// false on timeout.
+// indices tid, tid + kThreads, ...; value i goes to keep(i, bits).  Returns
+// false (and sets the error word) on timeout.
 template <typename Keep>
-__device__ bool await_published(unsigned long long* src, int n, unsigned epoch, Keep keep, unsigned* err) {
+__device__ bool await_published(const unsigned long long* src, int n, unsigned epoch, Keep keep, unsigned* ctl) {
     long spins = 0;
     for (;;) {
         int missing = 0;
         for (int i = threadIdx.x; i < n; i += kThreads) {
             const unsigned long long w = peek(src + i);
             if ((unsigned)(w >> 32) == epoch) {
-                keep(i, __uint_as_float((uint32_t)w));
+                keep(i, (uint32_t)w);
             } else {
                 missing = 1;
             }
         }
         if (__syncthreads_or(missing) == 0) return true;
         if (++spins > kSpinLimit) {
-            if (threadIdx.x == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (threadIdx.x == 0) flag_error(ctl);
             return false;
         }
         __builtin_amdgcn_s_sleep(2);
     }
 }
 
-// Wait for token t's published logits; for a routed slot, rank them and keep
-// the expert and weight of the slot's rank (slot % top_k).  The shared expert's
-// slots take expert 0 of the shared stack with weight 1.
-__device__ void route_slot(const DecodeArgs& p, int slot, int t, bool routed, unsigned epoch, RoleShared& sh) {
-    const bool ok = await_published(p.logits64 + (size_t)t * p.E, p.E, epoch,
-                                    [&](int i, float v) { sh.logits[i] = v; }, p.ctl + kCtlError);
-    if (!routed) {
-        if (threadIdx.x == 0) {
-            sh.ex = 0;
-            sh.wgt = 1.0f;
-            sh.ok = ok;
+// One thread polls *ctr until it reaches `target`; the workgroup then proceeds.
+// Returns false (and sets the error word) on timeout.
+__device__ bool wait_count(unsigned* ctr, unsigned target, unsigned* ctl, RoleShared& sh) {
+    if (threadIdx.x == 0) {
+        long spins = 0;
+        int ok = 1;
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (++spins > kSpinLimit) {
+                flag_error(ctl);
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
         }
-    } else if (threadIdx.x < kWave) {
-        int ij;
-        float wj;
-        wave_topk([&](int e) { return sh.logits[e]; }, p.E, p.top_k, threadIdx.x, &ij, &wj);
-        if (threadIdx.x == slot % p.top_k) {
-            sh.ex = min(max(ij, 0), p.E - 1);  // in range even for non-finite logits
-            sh.wgt = wj;
+        sh.wait_ok = ok;
+    }
+    __syncthreads();
+    return sh.wait_ok;
+}
+
+// Ranking key of logit v of expert e: a larger key ranks first, i.e. the larger
+// logit, and on equal logits the lower expert index.  The float maps to an
+// order-preserving unsigned integer (flip all bits of negatives, the sign bit of
+// the rest; -0 is taken as +0, which it equals); the low word holds ~e.
+__device__ __forceinline__ unsigned long long rank_key(float v, int e) {
+    const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)o << 32) | (uint32_t)~e;
+}
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Read token t's top k from copy `rep` of the published entries: on return lane
+// j < k of the calling wave holds the logit and expert of rank j.  Polls until
+// all k entries carry `epoch`; returns false on timeout.
+__device__ bool read_topk(const DecodeArgs& p, int t, int rep, unsigned epoch, float& l, int& ex) {
+    const int lane = threadIdx.x % kWave, k = p.top_k;
+    const unsigned long long* wl = p.sel64 + rep * kSelWords + t * kMaxTopK + lane;
+    const unsigned long long* we = wl + kSelReplicas * kSelWords;
+    l = 0.0f;
+    ex = 0;
+    for (long spins = 0;; spins++) {
+        bool have = true;
+        if (lane < k) {
+            const unsigned long long a = peek(wl), c = peek(we);
+            have = (unsigned)(a >> 32) == epoch && (unsigned)(c >> 32) == epoch;
+            l = __uint_as_float((uint32_t)a);
+            ex = (int)(uint32_t)c;
+        }
+        if (__ballot(!have) == 0) return true;
+        if (spins > kSpinLimit) {
+            if (lane == 0) flag_error(p.ctl);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Routing weight of rank j: softmax over the k kept logits (lane r holds the
+// logit of rank r), summed in rank order.  Wave-uniform result.
+__device__ __forceinline__ float topk_weight(float l, int k, int j) {
+    const float pr = expf(l - lane_f(l, 0));
+    float z = 0.0f;
+    for (int r = 0; r < k; r++) z += lane_f(pr, r);
+    return lane_f(pr, j) / z;
+}
+
+// The expert and weight of `slot`: wave 0 reads its token's top k (copy
+// blockIdx % kSelReplicas) and keeps rank slot % top_k.  The shared expert's
+// slots read it too (so that they never add into rows not yet cleared) and take
+// expert 0 of the shared stack with weight 1.
+__device__ void route_slot(const DecodeArgs& p, int slot, int t, bool routed, unsigned epoch, RoleShared& sh) {
+    if (threadIdx.x < kWave) {
+        float l;
+        int ex;
+        const bool ok = read_topk(p, t, blockIdx.x % kSelReplicas, epoch, l, ex);
+        const int j = slot % p.top_k;
+        const float w = topk_weight(l, p.top_k, j);
+        const int e = __builtin_amdgcn_readlane(ex, j);
+        if (threadIdx.x == 0) {
+            sh.ex = routed ? min(max(e, 0), p.E - 1) : 0;  // in range whatever was read
+            sh.wgt = routed ? w : 1.0f;
             sh.ok = ok;
         }
     }
@@ -219,18 +318,18 @@ __device__ void route_slot(const DecodeArgs& p, int slot, int t, bool routed, un
 
 __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShared& sh) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int H = p.H, T = p.T;
+    const int H = p.H, T = p.T, E = p.E;
     const int e = b * kRouterExperts + wave;
     const int nblk = H / 8;  // 16-byte chunks of a row
-    // clear the output rows (write-through), then wait for those stores before
-    // the logits go out: a consumer that sees every logit sees cleared rows
-    for (int i = b * kThreads + tid; i < T * H; i += p.router_wgs * kThreads)
-        __hip_atomic_store(p.out + i, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // clear the output rows (write-through); they are complete before any logit
+    // goes out, hence before any top-k entry, which every down workgroup reads
+    // before it adds into them
+    for (int i = b * kThreads + tid; i < T * H; i += p.router_wgs * kThreads) put(p.out + i, 0.0f);
 
     float acc[kDecodeMaxT];
 #pragma unroll
     for (int t = 0; t < kDecodeMaxT; t++) acc[t] = 0.0f;
-    const uint4* wr = reinterpret_cast<const uint4*>(p.router + (size_t)min(e, p.E - 1) * H);
+    const uint4* wr = reinterpret_cast<const uint4*>(p.router + (size_t)min(e, E - 1) * H);
     for (int c0 = 0; c0 < nblk; c0 += 4 * kWave) {
         uint4 a[4], xv[kDecodeMaxT][4];
 #pragma unroll
@@ -254,15 +353,40 @@ __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShar
             }
         }
     }
+    const float bias = (p.logit_bias && e < E) ? p.logit_bias[e] : 0.0f;
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxT; t++) acc[t] = group_sum(acc[t], kWave);
-    __builtin_amdgcn_s_waitcnt(0);
+    for (int t = 0; t < kDecodeMaxT; t++) acc[t] = group_sum(acc[t], kWave) + bias;  // every lane: the logit
+    for (int i = tid; i < kDecodeMaxT * kMaxE; i += kThreads) sh.keys[i] = 0;  // below every real key
+    __builtin_amdgcn_s_waitcnt(0);  // the clearing stores are out
     __syncthreads();
-    if (lane == 0 && e < p.E) {
-        const float bias = p.logit_bias ? p.logit_bias[e] : 0.0f;
+    if (lane < kXchReplicas && e < E) {  // lane r writes copy r
 #pragma unroll
         for (int t = 0; t < kDecodeMaxT; t++)
-            if (t < T) publish(p.logits64 + (size_t)t * p.E + e, epoch, acc[t] + bias);
+            if (t < T) publish(p.xch64 + lane * kXchWords + (size_t)t * E + e, epoch, __float_as_uint(acc[t]));
+    }
+
+    // rank this workgroup's experts against every logit: the rank of a key is
+    // the number of larger keys (keys are distinct), one ballot per 64 of them
+    const bool ok = await_published(p.xch64 + (b % kXchReplicas) * kXchWords, T * E, epoch,
+                                    [&](int i, uint32_t bits) { sh.keys[i] = rank_key(__uint_as_float(bits), i % E); },
+                                    p.ctl);
+    if (e >= E || !ok) return;
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxT; t++) {
+        if (t >= T) break;
+        const unsigned long long* kt = sh.keys + t * E;
+        const unsigned long long mine = kt[e];
+        int r = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) {
+            const int j = lane + kWave * i;
+            r += __popcll(__ballot(j < E && kt[min(j, E - 1)] > mine));
+        }
+        if (r < p.top_k && lane < kSelReplicas) {  // lane r writes copy r
+            unsigned long long* w = p.sel64 + lane * kSelWords + t * kMaxTopK + r;
+            publish(w, epoch, __float_as_uint(acc[t]));
+            publish(w + kSelReplicas * kSelWords, epoch, (uint32_t)e);
+        }
     }
 }
 
@@ -361,7 +485,12 @@ __device__ void gateup_role(const DecodeArgs& p, int slot, int blk, unsigned epo
     // lane 8v holds value v: v < 4 gate row v, v >= 4 up row v-4
     const float upv = __shfl(total, (lane + 32) & 63);
     if (lane < 32 && lane % 8 == 0)
-        publish(p.h64 + (size_t)slot * I + i0 + wave * kRowsPerWave + lane / 8, epoch, silu(total) * upv);
+        put(p.hbuf + (size_t)slot * I + i0 + wave * kRowsPerWave + lane / 8, silu(total) * upv);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's h is out
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_fetch_add(p.ctl + kCtlSlot0 + kCtlSlotStride * slot, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ down role
@@ -413,10 +542,9 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     // wait for the slot's h; keep it as float16 in nibble order, then the
     // low/high sums of every 8 columns
     _Float16* hh = sh.down.hh;
-    const bool ok = await_published(p.h64 + (size_t)slot * I, I, epoch,
-                                    [&](int i, float v) { hh[(i & ~7) + slot_of_column(i & 7)] = (_Float16)v; },
-                                    p.ctl + kCtlError) &&
-                    sh.ok;
+    const bool ok = wait_count(p.ctl + kCtlSlot0 + kCtlSlotStride * slot, (unsigned)(I / kGURows), p.ctl, sh) && sh.ok;
+    for (int i = tid; i < I; i += kThreads) hh[(i & ~7) + slot_of_column(i & 7)] = (_Float16)get(p.hbuf + (size_t)slot * I + i);
+    __syncthreads();
     for (int b8 = tid; b8 < I / 8; b8 += kThreads) {
         const _Float16* hv = hh + b8 * 8;  // 0,4,1,5,2,6,3,7
         sh.down.hsum[b8] = make_float2((float)hv[0] + (float)hv[1] + (float)hv[4] + (float)hv[5],
@@ -485,49 +613,56 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
         else
             down_role<SB, false>(p, slot, blk, epoch, sh);
     }
-    // the last workgroup to finish advances the epoch for the next call
+    // the last workgroup to finish (every other one is past its waits) resets
+    // the counters and advances the epoch for the next call
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned old = __hip_atomic_fetch_add(p.ctl + kCtlDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == gridDim.x - 1) {
+        sh.last = old == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (sh.last) {
+        const int i = threadIdx.x;
+        if (i < kMaxSlots)
+            __hip_atomic_store(p.ctl + kCtlSlot0 + kCtlSlotStride * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (i == 0) {
             __hip_atomic_store(p.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(p.ctl + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-// routing outputs requested by the caller: a tiny second kernel (only when asked)
-__global__ __launch_bounds__(kThreads) void decode_routing_out_kernel(DecodeArgs p) {
-    __shared__ float lg[kMaxE];
-    __shared__ int ids[kDecodeMaxT * kMaxTopK];
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+// Routing outputs requested by the caller, from the top-k entries the layer
+// kernel used (copy 0), with the same weight arithmetic: a tiny second kernel,
+// only when asked.
+__global__ __launch_bounds__(kWave) void decode_routing_out_kernel(DecodeArgs p) {
+    __shared__ int counts[kMaxE];
+    const int lane = threadIdx.x;
     const unsigned epoch = __hip_atomic_load(p.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int t = 0; t < p.T; t++) {
-        for (int e = tid; e < p.E; e += kThreads) {
-            const unsigned long long w = peek(p.logits64 + (size_t)t * p.E + e);
-            lg[e] = (unsigned)(w >> 32) == epoch ? __uint_as_float((uint32_t)w) : -INFINITY;
+    const int k = p.top_k;
+    for (int e = lane; e < kMaxE; e += kWave) counts[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxT; t++) {
+        if (t >= p.T) break;
+        float l;
+        int ex;
+        read_topk(p, t, 0, epoch, l, ex);
+        float w = 0.0f;
+        for (int j = 0; j < k; j++) {
+            const float wj = topk_weight(l, k, j);
+            if (lane == j) w = wj;
         }
-        __syncthreads();
-        if (wave == 0) {
-            int ij;
-            float wj;
-            wave_topk([&](int e) { return lg[e]; }, p.E, p.top_k, lane, &ij, &wj);
-            if (lane < p.top_k) {
-                if (p.idx_out) p.idx_out[t * p.top_k + lane] = ij;
-                if (p.w_out) p.w_out[t * p.top_k + lane] = wj;
-                ids[t * p.top_k + lane] = ij;
-            }
-        }
-        __syncthreads();
-    }
-    if (p.counts_out) {
-        for (int e = tid; e < p.E; e += kThreads) {
-            int c = 0;
-            for (int s = 0; s < p.T * p.top_k; s++) c += ids[s] == e;
-            p.counts_out[e] = c;
+        if (lane < k) {
+            if (p.idx_out) p.idx_out[t * k + lane] = ex;
+            if (p.w_out) p.w_out[t * k + lane] = w;
+            if (ex >= 0 && ex < p.E) atomicAdd(&counts[ex], 1);
         }
     }
+    __syncthreads();
+    if (p.counts_out)
+        for (int e = lane; e < p.E; e += kWave) p.counts_out[e] = counts[e];
 }
 
 }  // namespace
@@ -547,7 +682,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool sb_bf16, hipStream_t stream) 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (a.idx_out || a.w_out || a.counts_out) {
-        hipLaunchKernelGGL(decode_routing_out_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(decode_routing_out_kernel, dim3(1), dim3(kWave), 0, stream, a);
         err = hipGetLastError();
     }
     return err;

@@ -73,17 +73,20 @@ hipError_t launch_down(const GemmProblem& p, const _Float16* h, const float* top
                        float* out, float* y_slot, float* y_shared, hipStream_t stream);
 
 // Decode path (T <= kDecodeMaxT, I <= kMaxDecodeI): one kernel per call whose
-// router workgroups publish the logits, whose gate/up workgroups rank them and
-// publish h, and whose down workgroups combine into `out` with float32 atomics.
-// Values cross workgroups as {epoch, value} words in the decode region at the
-// start of the workspace (kDecodeRegionBytes, fixed for every dims, zero-filled
-// before first use); the control word kept there advances by one per call.
+// router workgroups publish the logits and rank them, whose gate/up workgroups
+// publish h, and whose down workgroups combine into `out` with float32
+// atomics.  It uses the decode region at the start of the workspace
+// (kDecodeRegionBytes, the same offsets for every dims, zero before the first
+// call): control words, then the values handed between workgroups.
 constexpr int kDecodeMaxT = 4;
 constexpr int kMaxDecodeI = 4096;
-constexpr int kDecodeControlBytes = 1024;
-constexpr size_t kDecodeLogitBytes = (size_t)kDecodeMaxT * 256 * 8;
-constexpr size_t kDecodeHBytes = (size_t)kDecodeMaxT * (8 + 1) * kMaxDecodeI * 8;
-constexpr size_t kDecodeRegionBytes = kDecodeControlBytes + kDecodeLogitBytes + kDecodeHBytes;
+constexpr int kDecodeXchReplicas = 4;   // copies of the logits, each read by a share of the router workgroups
+constexpr int kDecodeSelReplicas = 16;  // copies of the top k, each read by a share of the expert workgroups
+constexpr int kDecodeControlBytes = 16384;
+constexpr size_t kDecodeXchBytes = (size_t)kDecodeXchReplicas * kDecodeMaxT * 256 * 8;
+constexpr size_t kDecodeSelBytes = (size_t)2 * kDecodeSelReplicas * kDecodeMaxT * 8 * 8;
+constexpr size_t kDecodeHBytes = (size_t)kDecodeMaxT * (8 + 1) * kMaxDecodeI * 4;
+constexpr size_t kDecodeRegionBytes = kDecodeControlBytes + kDecodeXchBytes + kDecodeSelBytes + kDecodeHBytes;
 
 struct DecodeArgs {
     int T, H, E, top_k, I;
@@ -91,14 +94,15 @@ struct DecodeArgs {
     const uint16_t* x;
     const uint16_t* router;
     const float* logit_bias;
-    unsigned* ctl;                  // control words
-    unsigned long long* logits64;   // [T][E] {epoch, logit}
-    unsigned long long* h64;        // [slots][I] {epoch, h}; slots = T*k routed, then T shared
-    int32_t* idx_out;               // optional copies of the routing
+    unsigned* ctl;               // control words and counters
+    unsigned long long* xch64;   // kDecodeXchReplicas copies of [kDecodeMaxT][256] {epoch, logit}
+    unsigned long long* sel64;   // logits, then experts: each kDecodeSelReplicas copies of [kDecodeMaxT][8] {epoch, value}
+    float* hbuf;                 // [slots][I]; slots = T*k routed, then T shared
+    int32_t* idx_out;            // optional copies of the routing
     float* w_out;
     int32_t* counts_out;
-    float* out;                     // [T][H]
-    FfnPtr experts, shared;         // shared.gate.q == nullptr: no shared expert
+    float* out;                  // [T][H]
+    FfnPtr experts, shared;      // shared.gate.q == nullptr: no shared expert
 };
 
 int decode_router_wgs(int E);

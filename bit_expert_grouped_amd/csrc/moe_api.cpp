@@ -37,7 +37,7 @@ moe_status check_dims(const moe_dims* d) {
 
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
-    size_t ctl, logits64, h64, x16, h, idx, w, counts, offsets, sorted, tiles, n_tiles, total;
+    size_t ctl, xch, sel, hbuf, x16, h, idx, w, counts, offsets, sorted, tiles, n_tiles, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -47,13 +47,15 @@ Layout layout_of(const moe_dims* d) {
     const bool shared = d->I_shared > 0;
     Layout L;
     size_t o = 0;
-    // decode region: the same offsets and size for every dims, so that words
-    // another call left there are always {epoch, value} words
+    // decode region: the same offsets for every dims, so that what one call
+    // leaves there is what the next call expects, whatever the dims of either
     L.ctl = o;
     o += kDecodeControlBytes;
-    L.logits64 = o;
-    o += kDecodeLogitBytes;
-    L.h64 = o;
+    L.xch = o;
+    o += kDecodeXchBytes;
+    L.sel = o;
+    o += kDecodeSelBytes;
+    L.hbuf = o;
     o = up256(o + kDecodeHBytes);
     L.x16 = o;
     o = up256(o + T * H * 2);
@@ -279,8 +281,9 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.router = wts->router;
         a.logit_bias = wts->logit_bias;
         a.ctl = at<unsigned>(ws, L.ctl);
-        a.logits64 = at<unsigned long long>(ws, L.logits64);
-        a.h64 = at<unsigned long long>(ws, L.h64);
+        a.xch64 = at<unsigned long long>(ws, L.xch);
+        a.sel64 = at<unsigned long long>(ws, L.sel);
+        a.hbuf = at<float>(ws, L.hbuf);
         a.idx_out = topk_idx_out;
         a.w_out = topk_w_out;
         a.counts_out = counts_out;

@@ -104,10 +104,11 @@ typedef struct {
  * pure; 0 when the dims are invalid).  One workspace serves every entry point.
  * Zero-fill the whole workspace once after allocating it; after that, every
  * call leaves it ready for the next one, whatever the dims of either.  The
- * first 1024 bytes are control words: word 0 counts decode calls and word 255
- * (bytes 1020..1023) is set to nonzero, and stays so, if a device-side wait of
- * a decode call timed out (that call's output is then invalid).  Calls that
- * share a workspace must not overlap in time (use one workspace per stream). */
+ * first 16384 bytes are control words of the decode path: word 0 counts its
+ * calls, and word 255 (bytes 1020..1023) is set to nonzero, and stays so, if a
+ * device-side wait of a decode call timed out (that call's output is then
+ * invalid).  Calls that share a workspace must not overlap in time (use one
+ * workspace per stream). */
 size_t moe_workspace_size(const moe_dims *dims /* host */);
 
 /* Router and top-k (pages: score every expert, keep top_k, on the GPU).
