@@ -14,8 +14,16 @@ top-8, shared expert, I=512).
 Launch: for T <= 64 the K timed steps are captured once into a HIP graph and
 replayed (how a decode loop issues a launch-bound layer); larger T launches
 eagerly.  The timed region carries no instrumentation.  Per-kernel durations
-for the roofline come from an instrumented replay of the same K steps through
-``moe_layer_events`` (HIP events around every kernel, on the launch stream).
+for the roofline come from an eager, instrumented run of the same K steps
+through ``moe_layer_events`` (HIP events recorded on the launch stream around
+every kernel; events inside a captured graph do not time kernels).
+
+``roofline.traffic`` is the dominant kernel's HBM bytes per launch measured by
+rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
+reads for a plain copy of known size; ``--copy-calibration`` runs that copy).
+The figures live in ``profiles/<kernel>_<workload>_pmc.txt`` together with the
+SHA-256 of the kernel's source file; when the source has changed since, the
+field is null.
 
 Prints one JSON line.  ``cpu_baseline`` times the CPU oracle (single-threaded
 C) on a bounded sample of the same workload.
@@ -24,6 +32,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -82,6 +91,57 @@ def stage_work(name, sh, T, touched, shared):
     return 0, 0.0
 
 
+# kernel name -> source file that holds it (for the counter figures' freshness)
+KERNEL_SOURCES = {
+    "decode_layer": "bit_expert_grouped_amd/csrc/decode.hip",
+    "router": "bit_expert_grouped_amd/csrc/router.hip",
+    "permute": "bit_expert_grouped_amd/csrc/permute.hip",
+    "gate_up": "bit_expert_grouped_amd/csrc/expert_gemm.hip",
+    "down_combine": "bit_expert_grouped_amd/csrc/expert_gemm.hip",
+}
+
+
+def source_sha(kernel):
+    path = os.path.join(ROOT, KERNEL_SOURCES.get(kernel, ""))
+    if not os.path.isfile(path):
+        return None
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it is for the
+    current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_pmc.txt" % (kernel, workload))
+    if not os.path.isfile(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "$")):
+            key, v = line.split(":", 1)
+            vals[key.strip()] = v.strip()
+    if vals.get("source_sha256") != source_sha(kernel):
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+
+
 def cpu_baseline(cfg, T, seconds):
     """Time the CPU oracle on a bounded sample of the workload (tokens/s)."""
     import numpy as np
@@ -129,10 +189,15 @@ def main():
     ap.add_argument("--weight-sets", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (three times) for counter calibration")
     ap.add_argument("--mode", choices=("eager", "graph"), default=None,
                     help="graph: replay one HIP graph holding the K timed steps (default for T <= 64); "
                          "eager: one foreign call per layer call")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -217,25 +282,25 @@ def main():
                 raise bem.MoeError(st, "moe_layer")
     torch.cuda.synchronize()
 
-    def capture(with_events):
-        """One HIP graph holding all K steps (and, instrumented, the per-kernel events)."""
+    def capture():
+        """One HIP graph holding all K steps."""
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            prepared = [call_args(i, li, side.cuda_stream, with_events)
+            prepared = [call_args(i, li, side.cuda_stream, False)
                         for i in range(steps) for li in range(layers_per_step)]
             with torch.cuda.graph(g, stream=side):
                 for a in prepared:
-                    st = lib.moe_layer_events(*a[0]) if with_events else lib.moe_layer(*a)
+                    st = lib.moe_layer(*a)
                     if st != 0:
                         raise bem.MoeError(st, "moe_layer (capture)")
         torch.cuda.synchronize()
         g.replay()  # one untimed replay
         torch.cuda.synchronize()
-        return g, prepared
+        return g
 
-    plain = capture(False)[0] if mode == "graph" else None
+    plain = capture() if mode == "graph" else None
 
     # ---- timed region: exactly K steps, no instrumentation ----
     start = torch.cuda.Event(enable_timing=True)
@@ -257,13 +322,8 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / steps
 
-    # ---- instrumented replay of the same K steps: HIP events around every kernel ----
-    if mode == "graph":
-        inst, _keep = capture(True)
-        torch.cuda.synchronize()
-        inst.replay()
-    else:
-        _keep = run_eager(0, True)
+    # ---- instrumented eager run of the same K steps: HIP events around every kernel ----
+    _keep = run_eager(0, True)
     torch.cuda.synchronize()
 
     # per-stage durations inside the timed region
@@ -288,7 +348,11 @@ def main():
     shared = sh.I_shared > 0
     dominant = max(stages, key=lambda s: stage_us[s])
     nbytes, flops = stage_work(dominant, sh, T, touched, shared)
-    dur_s = stage_us[dominant] * 1e-6
+    us_layer = total_ms * 1000.0 / n_calls
+    # A layer that is one kernel: its duration is the timed region's per-call
+    # time (back-to-back launches); else the instrumented per-kernel events.
+    kernel_us = us_layer if len(stages) == 1 else stage_us[dominant]
+    dur_s = kernel_us * 1e-6
     if bound == "hbm":
         achieved = nbytes / dur_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -297,14 +361,16 @@ def main():
         achieved = flops / dur_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    roof.update({"kernel": dominant, "kernel_us": round(stage_us[dominant], 2),
+    traffic = measured_traffic(dominant, args.workload)
+    roof["traffic"] = traffic
+    roof.update({"kernel": dominant, "kernel_us": round(kernel_us, 2),
+                 "kernel_us_source": "timed region per call" if len(stages) == 1 else "instrumented events",
                  "algorithmic_bytes_per_launch": int(nbytes), "algorithmic_flops_per_launch": flops})
 
     tokens = T * steps * layers_per_step
     value = tokens / (total_ms / 1000.0)
     layer_bytes = sum(stage_work(s, sh, T, touched, shared)[0] for s in stages)
     layer_flops = sum(stage_work(s, sh, T, touched, shared)[1] for s in stages)
-    us_layer = total_ms * 1000.0 / n_calls
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -327,7 +393,7 @@ def main():
         "layer_mfma_frac": round(layer_flops / (us_layer * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
         "touched_experts": round(touched, 2),
         "stages_us": {s: round(v, 2) for s, v in stage_us.items()},
-        "stages_note": "per-kernel durations from HIP events around each kernel in an instrumented replay of "
+        "stages_note": "per-kernel durations from HIP events around each kernel in an eager instrumented run of "
                        "the same K steps (the timed region itself carries no per-kernel events)",
         "host_wall_s": round(host_s, 4),
         "launch": mode,
