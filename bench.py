@@ -83,8 +83,10 @@ def stage_work(name, sh, T, touched, shared):
         return T * k * 4 * 2 + E * 8, 0.0
     if name == "gate_up":
         return gate_up
-    if name == "down_combine":
-        return down
+    if name == "down":  # rows written as float16 slot rows
+        return (n_exp * eb["down"] + rows * I * 2 + rows * H * 2, 2.0 * rows * I * H)
+    if name == "combine":
+        return (rows * H * 2 + T * k * 4 + T * H * 4, 2.0 * T * k * H)
     if name == "decode_layer":  # the whole layer in one kernel: router + all touched experts + output
         return (router[0] + n_exp * (eb["gate_up"] + eb["down"]) + T * H * 4,
                 router[1] + gate_up[1] + down[1])
@@ -97,7 +99,8 @@ KERNEL_SOURCES = {
     "router": "bit_expert_grouped_amd/csrc/router.hip",
     "permute": "bit_expert_grouped_amd/csrc/permute.hip",
     "gate_up": "bit_expert_grouped_amd/csrc/expert_gemm.hip",
-    "down_combine": "bit_expert_grouped_amd/csrc/expert_gemm.hip",
+    "down": "bit_expert_grouped_amd/csrc/expert_gemm.hip",
+    "combine": "bit_expert_grouped_amd/csrc/misc.hip",
 }
 
 

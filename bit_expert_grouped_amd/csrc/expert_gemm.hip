@@ -15,21 +15,26 @@
 //     kernel and leave when there is no work.  Work ids are handed out in
 //     contiguous ranges per XCD (workgroups are dispatched round-robin over the
 //     8 XCDs), so the slabs of one tile and the tiles of one expert share an L2.
-//   - Activations (float16) are staged through LDS, one 64-column group per
-//     stage, double-buffered, rows XOR-swizzled so the 32-row MFMA operand reads
-//     are bank-conflict free.  Gate/up gathers token rows through the slot
-//     permutation (the permuted activation matrix is never materialised).
-//   - Weights never touch LDS: every lane of the 32x32x16 MFMA B operand needs 8
-//     consecutive K values of one output row, which is exactly one packed word.
-//     A lane loads 4 words (16 bytes) per group, dequantises them in registers
-//     (dequant_word: 13 VALU ops per 8 weights) and feeds four MFMAs.  Weight
-//     loads run two groups ahead of the math.
+//   - Operands stream through a ring of LDS stages, one 64-column group of K
+//     per stage, filled by direct-to-LDS loads (global_load_lds_dwordx4): the
+//     activation rows (float16, XOR-swizzled so the 32-row MFMA operand reads
+//     are conflict free; gate/up gathers token rows through the slot
+//     permutation, so the permuted matrix is never materialised) and each
+//     lane's 16 bytes of packed weights.  The ring is deeper for shorter tiles
+//     (less arithmetic per stage), so HBM stays busy at every batch size.  The
+//     waits are counted by hand (s_waitcnt vmcnt(stages ahead x loads per
+//     stage)) and the ring reads are inline-asm ds_reads, so the compiler's
+//     conservative waits for LDS DMA never drain the ring.
+//   - A lane's 8 consecutive K values of one output column are exactly one
+//     packed word: it is dequantised in registers (dequant_word: 13 VALU ops
+//     per 8 weights) straight into the B operand of v_mfma_f32_32x32x16_f16.
 //   - gate/up: a wave computes a 32-column stripe of gate and the same stripe of
 //     up, so SwiGLU is elementwise on the accumulators; h goes to global memory
-//     as float16 through an LDS transpose (16-byte stores).
-//   - down: a wave computes two 32-column stripes; the epilogue either scales by
-//     the routing weight and adds into the float32 output with atomics (the
-//     fused combine) or stores the slot rows.
+//     as float16 through an LDS transpose (16-byte stores), 8-column blocks in
+//     dequantisation order, which is the K order the down product reads.
+//   - down: a wave computes two 32-column stripes; the epilogue stores each
+//     row to its slot's row (un-permute on store): float16 rows for the
+//     layer's combine kernel, or float32 rows for the step-by-step API.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,11 +43,35 @@ namespace bitmoe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMT = kTileRows / 32;          // 32-row MFMA tiles per row tile
-constexpr int kStageRowBytes = kGroup * 2;   // one group of float16 per row
-constexpr int kStageBytes = kTileRows * kStageRowBytes;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMT = kTileRows / 32;              // 32-row MFMA tiles per full row tile
+constexpr int kStageRowBytes = kGroup * 2;       // one group of float16 per row
+constexpr int kBStageBytes = kWaves * 2 * kWave * 16;  // 4 waves x 2 stripes x 64 lanes x 16 B
+constexpr int kLdsBytes = 120 * 1024;                  // the ring (and the epilogue tiles)
+// Scales and biases of a wave's 2 x 32 weight rows for a block of groups, in
+// LDS for the whole K loop: per (stripe, array), 32 rows x kSBRowDwords dwords
+// (a row's 64-byte block plus one dword, so that a block starting at a 2-byte
+// offset fits), loaded with dword direct loads.
+constexpr int kSBRowDwords = 17;
+constexpr int kSBArrayDwords = 9 * kWave;              // >= 32 x 17, whole load instructions
+constexpr int kSBWaveBytes = 4 * kSBArrayDwords * 4;   // (stripe 0, 1) x (scale, bias)
+constexpr int kSBBytes = kWaves * kSBWaveBytes;
+static_assert(32 * kSBRowDwords <= kSBArrayDwords, "scale block layout");
 
-enum Mode { kGateUp = 0, kDownCombine = 1, kDownStore = 2 };
+enum Mode { kGateUp = 0, kDownY16 = 1, kDownStore = 2 };
+
+// Ring of stages for a row tile of MT 32-row MFMA tiles.  Loads per stage and
+// wave, all direct-to-LDS: MT activation chunks and 2 weight chunks.
+template <int MT>
+struct Ring {
+    static constexpr int D = MT == 1 ? 10 : (MT == 2 ? 7 : (MT == 3 ? 6 : 5));
+    static constexpr int kABytes = MT * 32 * kStageRowBytes;
+    static constexpr int kStage = kABytes + kBStageBytes;
+    static constexpr int kLoads = MT + 2;
+    static_assert(D * kStage <= kLdsBytes, "ring exceeds LDS");
+    static_assert((D - 2) * kLoads <= 63, "vmcnt holds 6 bits");
+    static_assert(D - 2 <= 8, "wait_stages covers up to 8 stages ahead");
+};
 
 struct GemmArgs {
     const Tile* tiles;
@@ -52,16 +81,15 @@ struct GemmArgs {
     int lda;
     int K;              // contraction length
     int N;              // output columns of each group's matrices
-    int k, TK, H;
+    int k, TK, T, H;
     const int32_t* sorted_slot;
     QMatPtr m0, m1;     // routed stacks used by stripe 0 / stripe 1
     QMatPtr s0, s1;     // shared-expert matrices used by stripe 0 / stripe 1
     int E;
     _Float16* h;        // gate/up output [rows][N]
-    const float* topk_w;
-    float* out;
-    float* y_slot;
-    float* y_shared;
+    _Float16* y16;      // down output [T*k + T][H] float16: slot rows, then shared rows
+    float* y_slot;      // down output [T*k][H] float32 (step-by-step API)
+    float* y_shared;    // [T][H] float32, nullable
 };
 
 template <typename SB>
@@ -84,190 +112,352 @@ __device__ __forceinline__ Stripe<SB> stripe_of(const QMatPtr& routed, const QMa
     return st;
 }
 
-template <typename SB>
-struct BRegs {
-    uint4 q0, q1;
-    SB s0, b0, s1, b1;
-};
-
-template <typename SB>
-__device__ __forceinline__ void load_b(BRegs<SB>& r, const Stripe<SB>& st0, const Stripe<SB>& st1, int kg,
-                                       int half) {
-    r.q0 = st0.q[kg * 2 + half];
-    r.q1 = st1.q[kg * 2 + half];
-    r.s0 = st0.s[kg];
-    r.b0 = st0.b[kg];
-    r.s1 = st1.s[kg];
-    r.b1 = st1.b[kg];
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int s) {
-    return s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
+__device__ __forceinline__ uint32_t word_of(const uint32_t __attribute__((ext_vector_type(4))) & v, int s) {
+    return v[s];
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-template <typename SB, int kMode>
-__global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)reinterpret_cast<uintptr_t>(p);
+}
+
+// this wave's loads of every stage but the `ahead` newest ones have landed
+template <int L>
+__device__ __forceinline__ void wait_stages(int ahead) {
+    switch (ahead) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * L > 63 ? 63 : 1 * L) : "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L > 63 ? 63 : 2 * L) : "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L > 63 ? 63 : 3 * L) : "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * L > 63 ? 63 : 4 * L) : "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * L > 63 ? 63 : 5 * L) : "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * L > 63 ? 63 : 6 * L) : "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(7 * L > 63 ? 63 : 7 * L) : "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * L > 63 ? 63 : 8 * L) : "memory"); break;
+    }
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ half8_t ds_read16(unsigned addr) {
+    half8_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 ds_read16u(unsigned addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+template <int N>
+__device__ __forceinline__ void wait_lds() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N > 15 ? 15 : N) : "memory");
+}
+// the same for a count known after unrolling
+__device__ __forceinline__ void wait_lds_n(int n) {
+    switch (n) {
+        case 0: wait_lds<0>(); break;
+        case 1: wait_lds<1>(); break;
+        case 2: wait_lds<2>(); break;
+        case 3: wait_lds<3>(); break;
+        case 4: wait_lds<4>(); break;
+        case 5: wait_lds<5>(); break;
+        case 6: wait_lds<6>(); break;
+        case 7: wait_lds<7>(); break;
+        default: wait_lds<8>(); break;
+    }
+}
+// make a value produced by an inline-asm LDS read depend on the wait above
+template <typename V>
+__device__ __forceinline__ void landed(V& v) {
+    asm volatile("" : "+v"(v));
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+    // (w & mask) | magic in one VALU op; one scalar operand is allowed, so the
+    // magic constant sits in a VGPR
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+    return r;
+}
+
+// dequant_word (common.h) with the code extraction in v_and_or_b32: 13 VALU ops
+__device__ __forceinline__ half8_t dequant_fast(uint32_t w, half2_t s, half2_t b, uint32_t m1024, uint32_t m64) {
+    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const half2_t k64 = {(_Float16)64.0f, (_Float16)64.0f};
+    const uint32_t w8 = w >> 8;
+    const half2_t q04 = as_half2(and_or(w, 0x000F000Fu, m1024)) - k1024;
+    const half2_t q15 = as_half2(and_or(w, 0x00F000F0u, m64)) - k64;
+    const half2_t q26 = as_half2(and_or(w8, 0x000F000Fu, m1024)) - k1024;
+    const half2_t q37 = as_half2(and_or(w8, 0x00F000F0u, m64)) - k64;
+    const half2_t r0 = __builtin_elementwise_fma(q04, s, b);
+    const half2_t r1 = __builtin_elementwise_fma(q15, s, b);
+    const half2_t r2 = __builtin_elementwise_fma(q26, s, b);
+    const half2_t r3 = __builtin_elementwise_fma(q37, s, b);
+    return half8_t{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+}
+
+template <typename SB>
+__device__ __forceinline__ float sb_bits_to_f32(uint32_t v);
+template <>
+__device__ __forceinline__ float sb_bits_to_f32<uint16_t>(uint32_t v) {
+    return __uint_as_float(v << 16);
+}
+template <>
+__device__ __forceinline__ float sb_bits_to_f32<float>(uint32_t v) {
+    return __uint_as_float(v);
+}
+template <typename SB>
+__device__ __forceinline__ uint32_t ds_read_sb(unsigned addr) {
+    uint32_t v;
+    if constexpr (sizeof(SB) == 2)
+        asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(addr));
+    else
+        asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// One row tile x column slab, MT 32-row MFMA tiles.
+template <typename SB, int kMode, int MT>
+__device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned char* smem, const int* row_src,
+                          const int* row_dst) {
+    using R = Ring<MT>;
+    constexpr int D = R::D;
     constexpr int kWaveCols = kMode == kGateUp ? 32 : 64;  // output columns per wave
     constexpr int kStripeStep = kMode == kGateUp ? 0 : 32;  // row offset of stripe 1
     constexpr int kSlabCols = 4 * kWaveCols;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
-    __shared__ int row_src[kTileRows];
-    __shared__ int row_t[kTileRows];
-    __shared__ int row_slot[kTileRows];
-    __shared__ float row_w[kTileRows];
-
-    // ---- work id -> (tile, slab), contiguous ranges per XCD ----
-    const int n_work = *p.n_tiles * p.slabs;
-    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-    const int per = (n_work + 7) / 8;
-    const int work = xcd * per + local;
-    if (local >= per || work >= n_work) return;
-    const int slab = work % p.slabs;
-    const Tile tl = p.tiles[work / p.slabs];
-    const int mt_count = (tl.rows + 31) / 32;
-    const int rows_pad = mt_count * 32;
-
     const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int col = lane % 32, half = lane / 32;
-
-    if (tid < kTileRows) {
-        const int r = tid;
-        int src = -1, t = 0, slot = -1;
-        float w = 1.0f;
-        if (r < tl.rows) {
-            const int gp = tl.row0 + r;
-            if (gp < p.TK) {
-                slot = p.sorted_slot[gp];
-                t = slot / p.k;
-                if (kMode == kDownCombine) w = p.topk_w[slot];
-            } else {
-                t = gp - p.TK;
-            }
-            src = kMode == kGateUp ? t : gp;
-        }
-        row_src[r] = src;
-        row_t[r] = t;
-        row_slot[r] = slot;
-        row_w[r] = w;
-    }
-    __syncthreads();
-
-    // ---- operands of this wave ----
-    const int c0 = slab * kSlabCols + wave * kWaveCols;
-    const bool active = c0 < p.N;
-    const int brow = active ? c0 + col : 0;
-    const Stripe<SB> st0 = stripe_of<SB>(p.m0, p.s0, tl.group, p.E, p.N, p.K, brow);
-    const Stripe<SB> st1 = stripe_of<SB>(p.m1, p.s1, tl.group, p.E, p.N, p.K, brow + (active ? kStripeStep : 0));
     const int n_groups = p.K / kGroup;
 
-    // A staging: thread -> 16-byte chunk (tid % 8) of rows tid/8 + 32j
-    const int a_chunk = tid % 8;
-    const int a_row0 = tid / 8;
-    const _Float16* a_ptr[kMT];
+    // ---- weight rows of this wave: inactive waves read a valid row and drop it ----
+    const int c0 = slab * kSlabCols + wave * kWaveCols;
+    const bool active = c0 < p.N;
+    const int brow = active ? c0 + col : col;
+    const Stripe<SB> st0 = stripe_of<SB>(p.m0, p.s0, tl.group, p.E, p.N, p.K, brow);
+    const Stripe<SB> st1 = stripe_of<SB>(p.m1, p.s1, tl.group, p.E, p.N, p.K, brow + (active ? kStripeStep : 0));
+
+    // ---- activation chunk of each of this lane's MT direct loads per stage ----
+    // load i of wave w fills LDS chunks u = (4 i + w) * 64 + lane: row u / 8,
+    // stored position u % 8, which holds the row's chunk (u % 8) ^ (row % 8)
+    const char* a_src[MT];
 #pragma unroll
-    for (int j = 0; j < kMT; j++) {
-        const int r = a_row0 + 32 * j;
-        const int src = row_src[r];
-        a_ptr[j] = src >= 0 ? p.a + (size_t)src * p.lda + a_chunk * 8 : nullptr;
+    for (int i = 0; i < MT; i++) {
+        const int u = (i * kWaves + wave) * kWave + lane;
+        const int r = u >> 3, c = (u & 7) ^ (r & 7);
+        const int src = row_src[r] >= 0 ? row_src[r] : row_src[0];
+        a_src[i] = reinterpret_cast<const char*>(p.a + (size_t)src * p.lda) + c * 16;
     }
-    uint4 a_regs[kMT];
-    auto load_a = [&](int kg) {
+
+    auto issue = [&](int kg, int slot) {
+        unsigned char* base = smem + slot * R::kStage;
 #pragma unroll
-        for (int j = 0; j < kMT; j++) {
-            const int r = a_row0 + 32 * j;
-            if (r < rows_pad && a_ptr[j]) {
-                a_regs[j] = *reinterpret_cast<const uint4*>(a_ptr[j] + kg * kGroup);
-            } else {
-                a_regs[j] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < kMT; j++) {
-            const int r = a_row0 + 32 * j;
-            if (r < rows_pad) {
-                unsigned char* dst = smem + buf * kStageBytes + r * kStageRowBytes + ((a_chunk ^ (r & 7)) * 16);
-                *reinterpret_cast<uint4*>(dst) = a_regs[j];
-            }
-        }
+        for (int i = 0; i < MT; i++)
+            __builtin_amdgcn_global_load_lds(a_src[i] + kg * kStageRowBytes, base + (i * kWaves + wave) * kWave * 16,
+                                             16, 0, 0);
+        __builtin_amdgcn_global_load_lds(st0.q + kg * 2 + half, base + R::kABytes + (wave * 2 + 0) * kWave * 16, 16,
+                                         0, 0);
+        __builtin_amdgcn_global_load_lds(st1.q + kg * 2 + half, base + R::kABytes + (wave * 2 + 1) * kWave * 16, 16,
+                                         0, 0);
     };
 
-    floatx16 acc0[kMT], acc1[kMT];
+    // ---- scales and biases of this wave's rows, one block of groups at a time ----
+    // array i of the wave: (stripe i / 2, scale or bias); rows of a stripe are
+    // consecutive, so array i of group block g0 is the dword range covering
+    // elements [row0 * ng + g0, (row0 + 32) * ng) (row0 = the stripe's first row),
+    // read dword by dword from where each row's block starts
+    constexpr int kBlk = 64 / (int)sizeof(SB);  // groups per block
+    const int ng = n_groups;
+    const SB* arr_base[4] = {st0.s - (size_t)col * ng, st0.b - (size_t)col * ng, st1.s - (size_t)col * ng,
+                             st1.b - (size_t)col * ng};  // row `col` back to the stripe's first row
+    const SB* arr_start[4];  // the group's rows of each array (loads are clamped to them)
+    {
+        const bool sh = tl.group >= p.E;
+        const size_t off0 = (size_t)(sh ? 0 : tl.group) * p.N * ng;
+        arr_start[0] = reinterpret_cast<const SB*>(sh ? p.s0.s : p.m0.s) + off0;
+        arr_start[1] = reinterpret_cast<const SB*>(sh ? p.s0.b : p.m0.b) + off0;
+        arr_start[2] = reinterpret_cast<const SB*>(sh ? p.s1.s : p.m1.s) + off0;
+        arr_start[3] = reinterpret_cast<const SB*>(sh ? p.s1.b : p.m1.b) + off0;
+    }
+    const size_t group_elems = (size_t)p.N * ng;
+    unsigned char* sb_lds = smem + kLdsBytes + wave * kSBWaveBytes;
+    auto load_scales = [&](int g0) {
 #pragma unroll
-    for (int m = 0; m < kMT; m++) {
+        for (int i = 0; i < 4; i++) {
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(arr_start[i]) & ~uintptr_t(3);
+            const uintptr_t hi = (reinterpret_cast<uintptr_t>(arr_start[i] + group_elems) - 4) & ~uintptr_t(3);
+#pragma unroll
+            for (int j = 0; j < kSBArrayDwords / kWave; j++) {
+                const int u = j * kWave + lane;
+                const int r = min(u / kSBRowDwords, 31), dw = u - r * kSBRowDwords;
+                const uintptr_t row_blk = reinterpret_cast<uintptr_t>(arr_base[i] + (size_t)r * ng + g0) & ~uintptr_t(3);
+                uintptr_t a = row_blk + (uintptr_t)dw * 4;
+                a = a < lo ? lo : (a > hi ? hi : a);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a),
+                                                 sb_lds + i * kSBArrayDwords * 4 + j * kWave * 4, 4, 0, 0);
+            }
+        }
+    };
+    // LDS byte offset of this lane's element g of block g0, array i
+    auto sb_off = [&](int i, int g0, int g) -> unsigned {
+        const uintptr_t e = reinterpret_cast<uintptr_t>(arr_base[i] + (size_t)col * ng + g0);
+        return lds_addr(sb_lds) + i * kSBArrayDwords * 4 + col * kSBRowDwords * 4 + (unsigned)(e & 3) +
+               (unsigned)(g - g0) * (unsigned)sizeof(SB);
+    };
+
+    floatx16 acc0[MT], acc1[MT];
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
         acc0[m] = floatx16{0};
         acc1[m] = floatx16{0};
     }
 
-    BRegs<SB> bc = {}, bn = {}, bnn = {};
-    if (active) {
-        load_b(bc, st0, st1, 0, half);
-        if (n_groups > 1) load_b(bn, st0, st1, 1, half);
-    }
-    load_a(0);
-    store_a(0);
-    if (n_groups > 1) load_a(1);
+    // LDS offsets of this lane's operand reads inside a stage
+    const unsigned b_off = R::kABytes + wave * 2 * kWave * 16 + lane * 16;
+    unsigned a_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) a_off[s] = col * kStageRowBytes + (((4 * half + s) ^ (col & 7)) * 16);
 
-    for (int kg = 0; kg < n_groups; kg++) {
-        __syncthreads();
-        const int buf = kg & 1;
-        if (kg + 1 < n_groups) store_a(buf ^ 1);
-        if (kg + 2 < n_groups) {
-            load_a(kg + 2);
-            if (active) load_b(bnn, st0, st1, kg + 2, half);
-        }
-        if (active) {
-            const half2_t sc0 = splat_half2(sb_to_f32<SB>(bc.s0));
-            const half2_t bi0 = splat_half2(sb_to_f32<SB>(bc.b0));
-            const half2_t sc1 = splat_half2(sb_to_f32<SB>(bc.s1));
-            const half2_t bi1 = splat_half2(sb_to_f32<SB>(bc.b1));
-            const unsigned char* abase = smem + buf * kStageBytes;
+    // exponent-trick constants held in VGPRs (v_and_or_b32 takes one scalar)
+    uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;
+    asm volatile("" : "+v"(m1024), "+v"(m64));
+
+    auto compute = [&](int slot, int kg, int g0) {
+        const unsigned base = lds_addr(smem) + slot * R::kStage;
+        u32x4 bq0 = ds_read16u(base + b_off);
+        u32x4 bq1 = ds_read16u(base + b_off + kWave * 16);
+        uint32_t sv0 = ds_read_sb<SB>(sb_off(0, g0, kg));
+        uint32_t bv0 = ds_read_sb<SB>(sb_off(1, g0, kg));
+        uint32_t sv1 = ds_read_sb<SB>(sb_off(2, g0, kg));
+        uint32_t bv1 = ds_read_sb<SB>(sb_off(3, g0, kg));
+        if constexpr (MT <= 2) {
+            // short tiles: every LDS read of the stage goes out at once; the
+            // weights are dequantised while the activation reads land
+            half8_t a[4][MT];
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+#pragma unroll
+                for (int m = 0; m < MT; m++) a[s][m] = ds_read16(base + a_off[s] + m * 32 * kStageRowBytes);
+            wait_lds<4 * MT>();  // the weights and scales (the six oldest reads)
+            landed(bq0);
+            landed(bq1);
+            landed(sv0);
+            landed(bv0);
+            landed(sv1);
+            landed(bv1);
+            const half2_t sc0 = splat_half2(sb_bits_to_f32<SB>(sv0));
+            const half2_t bi0 = splat_half2(sb_bits_to_f32<SB>(bv0));
+            const half2_t sc1 = splat_half2(sb_bits_to_f32<SB>(sv1));
+            const half2_t bi1 = splat_half2(sb_bits_to_f32<SB>(bv1));
+            half8_t w0[4], w1[4];
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                const half8_t w0 = dequant_word(word_of(bc.q0, s), sc0, bi0);
-                const half8_t w1 = dequant_word(word_of(bc.q1, s), sc1, bi1);
-                const int chunk = 4 * half + s;
+                w0[s] = dequant_fast(word_of(bq0, s), sc0, bi0, m1024, m64);
+                w1[s] = dequant_fast(word_of(bq1, s), sc1, bi1, m1024, m64);
+            }
 #pragma unroll
-                for (int m = 0; m < kMT; m++) {
-                    if (m < mt_count) {
-                        const int r = m * 32 + col;
-                        const half8_t av = *reinterpret_cast<const half8_t*>(
-                            abase + r * kStageRowBytes + ((chunk ^ (r & 7)) * 16));
-                        acc0[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, w0, acc0[m], 0, 0, 0);
-                        acc1[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, w1, acc1[m], 0, 0, 0);
-                    }
+            for (int s = 0; s < 4; s++) {
+                wait_lds_n((3 - s) * MT);
+#pragma unroll
+                for (int m = 0; m < MT; m++) {
+                    landed(a[s][m]);
+                    acc0[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][m], w0[s], acc0[m], 0, 0, 0);
+                    acc1[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][m], w1[s], acc1[m], 0, 0, 0);
+                }
+            }
+        } else {
+            // tall tiles: activation reads one K step ahead of the MFMAs
+            half8_t a_cur[MT], a_nxt[MT];
+#pragma unroll
+            for (int m = 0; m < MT; m++) a_cur[m] = ds_read16(base + a_off[0] + m * 32 * kStageRowBytes);
+            half2_t sc0, bi0, sc1, bi1;
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                if (s < 3) {
+#pragma unroll
+                    for (int m = 0; m < MT; m++) a_nxt[m] = ds_read16(base + a_off[s + 1] + m * 32 * kStageRowBytes);
+                    wait_lds<MT>();
+                } else {
+                    wait_lds<0>();
+                }
+                if (s == 0) {
+                    landed(bq0);
+                    landed(bq1);
+                    landed(sv0);
+                    landed(bv0);
+                    landed(sv1);
+                    landed(bv1);
+                    sc0 = splat_half2(sb_bits_to_f32<SB>(sv0));
+                    bi0 = splat_half2(sb_bits_to_f32<SB>(bv0));
+                    sc1 = splat_half2(sb_bits_to_f32<SB>(sv1));
+                    bi1 = splat_half2(sb_bits_to_f32<SB>(bv1));
+                }
+#pragma unroll
+                for (int m = 0; m < MT; m++) landed(a_cur[m]);
+                const half8_t w0 = dequant_fast(word_of(bq0, s), sc0, bi0, m1024, m64);
+                const half8_t w1 = dequant_fast(word_of(bq1, s), sc1, bi1, m1024, m64);
+#pragma unroll
+                for (int m = 0; m < MT; m++) {
+                    acc0[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[m], w0, acc0[m], 0, 0, 0);
+                    acc1[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[m], w1, acc1[m], 0, 0, 0);
+                }
+                if (s < 3) {
+#pragma unroll
+                    for (int m = 0; m < MT; m++) a_cur[m] = a_nxt[m];
                 }
             }
         }
-        bc = bn;
-        bn = bnn;
+    };
+
+    // ---- main loop: stage kg in slot kg % D; D - 1 stages in flight ----
+    // the first scale block goes out before the ring, so waiting for stage 0
+    // also waits for it (loads of a wave complete in order)
+    load_scales(0);
+#pragma unroll
+    for (int j = 0; j < D - 1; j++)
+        if (j < n_groups) issue(j, j);
+    int g0 = 0;
+    int slot = 0, fill = D - 1;  // slot of stage kg; slot that stage kg + D - 1 goes to
+#pragma unroll 1
+    for (int kg = 0; kg < n_groups; kg++) {
+        if (kg == g0 + kBlk) {
+            // next scale block (K beyond one block): drain, reload, go on
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            barrier();
+            g0 = kg;
+            load_scales(g0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            barrier();
+        }
+        wait_stages<R::kLoads>(min(D - 2, n_groups - 1 - kg));
+        barrier();  // every wave's stage kg has landed; every wave is done with stage kg - 1
+        if (kg + D - 1 < n_groups) issue(kg + D - 1, fill);
+        compute(slot, kg, g0);
+        slot = slot == D - 1 ? 0 : slot + 1;
+        fill = fill == D - 1 ? 0 : fill + 1;
     }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    barrier();  // the ring is free for the epilogue
 
     // ---- epilogues.  Accumulator element 4i+j of a lane: row 8i + 4*half + j, column `col` ----
     if constexpr (kMode == kGateUp) {
-        __syncthreads();  // every wave is done reading the activation stages
         // LDS tile [128 rows][kSlabCols columns] float16, columns in dequantisation order
         _Float16* ht = reinterpret_cast<_Float16*>(smem);
         if (active) {
             const int cl = wave * kWaveCols + col;  // column within the slab
             const int pos = (cl & ~7) + slot_of_column(cl & 7);
 #pragma unroll
-            for (int m = 0; m < kMT; m++) {
-                if (m < mt_count) {
+            for (int m = 0; m < MT; m++) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
+                for (int i = 0; i < 4; i++) {
 #pragma unroll
-                        for (int j = 0; j < 4; j++) {
-                            const int r = m * 32 + 8 * i + 4 * half + j;
-                            const float g = acc0[m][4 * i + j];
-                            const float u = acc1[m][4 * i + j];
-                            ht[r * kSlabCols + pos] = (_Float16)(silu(g) * u);
-                        }
+                    for (int j = 0; j < 4; j++) {
+                        const int r = m * 32 + 8 * i + 4 * half + j;
+                        ht[r * kSlabCols + pos] = (_Float16)(silu(acc0[m][4 * i + j]) * acc1[m][4 * i + j]);
                     }
                 }
             }
@@ -282,33 +472,50 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
                 *reinterpret_cast<uint4*>(p.h + (size_t)(tl.row0 + r) * p.N + slab * kSlabCols + c * 8) = v;
             }
         }
+    } else if constexpr (kMode == kDownY16) {
+        // LDS tile [128 rows][kSlabCols columns] float16 in natural column order
+        _Float16* yt = reinterpret_cast<_Float16*>(smem);
+        if (active) {
+            const int cl = wave * kWaveCols + col;
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int r = m * 32 + 8 * i + 4 * half + j;
+                        yt[r * kSlabCols + cl] = (_Float16)acc0[m][4 * i + j];
+                        yt[r * kSlabCols + cl + kStripeStep] = (_Float16)acc1[m][4 * i + j];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        constexpr int kChunks = kSlabCols / 8;
+        const int col_chunks = min(kChunks, (p.N - slab * kSlabCols) / 8);
+        for (int idx = tid; idx < tl.rows * kChunks; idx += kThreads) {
+            const int r = idx / kChunks, c = idx % kChunks;
+            if (c < col_chunks) {
+                const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kSlabCols + c * 8);
+                *reinterpret_cast<uint4*>(p.y16 + (size_t)row_dst[r] * p.H + slab * kSlabCols + c * 8) = v;
+            }
+        }
     } else {
         if (active) {
 #pragma unroll
-            for (int m = 0; m < kMT; m++) {
-                if (m < mt_count) {
+            for (int m = 0; m < MT; m++) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
+                for (int i = 0; i < 4; i++) {
 #pragma unroll
-                        for (int j = 0; j < 4; j++) {
-                            const int r = m * 32 + 8 * i + 4 * half + j;
-                            if (r < tl.rows) {
-                                const int n0 = c0 + col;
-                                const int n1 = c0 + kStripeStep + col;
-                                if constexpr (kMode == kDownCombine) {
-                                    float* o = p.out + (size_t)row_t[r] * p.H;
-                                    const float w = row_w[r];
-                                    atomicAdd(o + n0, w * acc0[m][4 * i + j]);
-                                    atomicAdd(o + n1, w * acc1[m][4 * i + j]);
-                                } else {
-                                    const int slot = row_slot[r];
-                                    float* o = slot >= 0 ? p.y_slot + (size_t)slot * p.H
-                                                         : p.y_shared + (size_t)row_t[r] * p.H;
-                                    if (slot >= 0 || p.y_shared) {
-                                        o[n0] = acc0[m][4 * i + j];
-                                        o[n1] = acc1[m][4 * i + j];
-                                    }
-                                }
+                    for (int j = 0; j < 4; j++) {
+                        const int r = m * 32 + 8 * i + 4 * half + j;
+                        if (r < tl.rows) {
+                            const int d = row_dst[r];
+                            float* o = d < p.TK ? p.y_slot + (size_t)d * p.H
+                                                : (p.y_shared ? p.y_shared + (size_t)(d - p.TK) * p.H : nullptr);
+                            if (o) {
+                                o[c0 + col] = acc0[m][4 * i + j];
+                                o[c0 + kStripeStep + col] = acc1[m][4 * i + j];
                             }
                         }
                     }
@@ -318,10 +525,82 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
     }
 }
 
+template <typename SB, int kMode>
+__global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes + kSBBytes];
+    __shared__ int row_src[kTileRows];
+    __shared__ int row_dst[kTileRows];
+
+    // ---- work id -> (tile, slab), contiguous ranges per XCD ----
+    const int n_work = *p.n_tiles * p.slabs;
+    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    const int per = (n_work + 7) / 8;
+    const int work = xcd * per + local;
+    if (local >= per || work >= n_work) return;
+    const int slab = work % p.slabs;
+    const Tile tl = p.tiles[work / p.slabs];
+    const int mt_count = (tl.rows + 31) / 32;
+
+    // row r of the tile: where its activations come from and where its output goes
+    // (-1: padding).  Grouped row gp < T*k is slot sorted_slot[gp] of token slot / k;
+    // rows from T*k on are the shared expert's tokens.
+    const int tid = threadIdx.x;
+    if (tid < kTileRows) {
+        const int r = tid;
+        int src = -1, dst = -1;
+        if (r < tl.rows) {
+            const int gp = tl.row0 + r;
+            int slot, t;
+            if (gp < p.TK) {
+                slot = p.sorted_slot[gp];
+                t = slot / p.k;
+            } else {
+                t = gp - p.TK;
+                slot = p.TK + t;
+            }
+            src = kMode == kGateUp ? t : gp;
+            dst = slot;
+        }
+        row_src[r] = src;
+        row_dst[r] = dst;
+    }
+    __syncthreads();
+
+    switch (mt_count) {
+        case 1: gemm_tile<SB, kMode, 1>(p, tl, slab, smem, row_src, row_dst); break;
+        case 2: gemm_tile<SB, kMode, 2>(p, tl, slab, smem, row_src, row_dst); break;
+        case 3: gemm_tile<SB, kMode, 3>(p, tl, slab, smem, row_src, row_dst); break;
+        default: gemm_tile<SB, kMode, kMT>(p, tl, slab, smem, row_src, row_dst); break;
+    }
+}
+
+template <int kMode>
+hipError_t launch_mode(const GemmArgs& a, bool sb_bf16, int64_t grid, hipStream_t stream) {
+    if (sb_bf16)
+        hipLaunchKernelGGL((expert_gemm_kernel<uint16_t, kMode>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((expert_gemm_kernel<float, kMode>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+GemmArgs common_args(const GemmProblem& pr) {
+    GemmArgs a = {};
+    a.tiles = pr.tiles;
+    a.n_tiles = pr.n_tiles;
+    a.k = pr.k;
+    a.TK = pr.T * pr.k;
+    a.T = pr.T;
+    a.H = pr.H;
+    a.E = pr.E;
+    a.sorted_slot = pr.sorted_slot;
+    return a;
+}
+
 }  // namespace
 
 hipError_t launch_gateup(const GemmProblem& pr, const _Float16* x16, _Float16* h, hipStream_t stream) {
-    GemmArgs a = {};
+    GemmArgs a = common_args(pr);
     a.a = x16;
     a.lda = pr.H;
     a.K = pr.H;
@@ -331,28 +610,14 @@ hipError_t launch_gateup(const GemmProblem& pr, const _Float16* x16, _Float16* h
     a.s0 = pr.shared_w.gate;
     a.s1 = pr.shared_w.up;
     a.h = h;
-    a.tiles = pr.tiles;
-    a.n_tiles = pr.n_tiles;
     a.slabs = (pr.I + 127) / 128;
-    a.k = pr.k;
-    a.TK = pr.T * pr.k;
-    a.H = pr.H;
-    a.E = pr.E;
-    a.sorted_slot = pr.sorted_slot;
     const int64_t grid = (pr.max_tiles * a.slabs + 7) / 8 * 8;
-    if (pr.sb_bf16) {
-        hipLaunchKernelGGL((expert_gemm_kernel<uint16_t, kGateUp>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, a);
-    } else {
-        hipLaunchKernelGGL((expert_gemm_kernel<float, kGateUp>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, a);
-    }
-    return hipGetLastError();
+    return launch_mode<kGateUp>(a, pr.sb_bf16, grid, stream);
 }
 
-hipError_t launch_down(const GemmProblem& pr, const _Float16* h, const float* topk_w, bool combine, float* out,
-                       float* y_slot, float* y_shared, hipStream_t stream) {
-    GemmArgs a = {};
+hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, float* y_slot, float* y_shared,
+                       hipStream_t stream) {
+    GemmArgs a = common_args(pr);
     a.a = h;
     a.lda = pr.I;
     a.K = pr.I;
@@ -361,35 +626,13 @@ hipError_t launch_down(const GemmProblem& pr, const _Float16* h, const float* to
     a.m1 = pr.experts.down;
     a.s0 = pr.shared_w.down;
     a.s1 = pr.shared_w.down;
-    a.topk_w = topk_w;
-    a.out = out;
+    a.y16 = y16;
     a.y_slot = y_slot;
     a.y_shared = y_shared;
-    a.tiles = pr.tiles;
-    a.n_tiles = pr.n_tiles;
     a.slabs = (pr.H + 255) / 256;
-    a.k = pr.k;
-    a.TK = pr.T * pr.k;
-    a.H = pr.H;
-    a.E = pr.E;
-    a.sorted_slot = pr.sorted_slot;
     const int64_t grid = (pr.max_tiles * a.slabs + 7) / 8 * 8;
-    if (combine) {
-        if (pr.sb_bf16)
-            hipLaunchKernelGGL((expert_gemm_kernel<uint16_t, kDownCombine>), dim3((unsigned)grid), dim3(kThreads),
-                               0, stream, a);
-        else
-            hipLaunchKernelGGL((expert_gemm_kernel<float, kDownCombine>), dim3((unsigned)grid), dim3(kThreads), 0,
-                               stream, a);
-    } else {
-        if (pr.sb_bf16)
-            hipLaunchKernelGGL((expert_gemm_kernel<uint16_t, kDownStore>), dim3((unsigned)grid), dim3(kThreads), 0,
-                               stream, a);
-        else
-            hipLaunchKernelGGL((expert_gemm_kernel<float, kDownStore>), dim3((unsigned)grid), dim3(kThreads), 0,
-                               stream, a);
-    }
-    return hipGetLastError();
+    return y16 ? launch_mode<kDownY16>(a, pr.sb_bf16, grid, stream)
+               : launch_mode<kDownStore>(a, pr.sb_bf16, grid, stream);
 }
 
 }  // namespace bitmoe

@@ -66,11 +66,12 @@ struct GemmProblem {
 // 8-column blocks in dequantisation order.
 hipError_t launch_gateup(const GemmProblem& p, const _Float16* x16, _Float16* h, hipStream_t stream);
 
-// down products.  combine == true: out[t] += w * y (float32 atomics, out cleared
-// beforehand; routed rows weighted by topk_w, shared rows by 1).  combine ==
-// false: y_slot[slot] = y for routed rows, y_shared[t] = y for shared rows.
-hipError_t launch_down(const GemmProblem& p, const _Float16* h, const float* topk_w, bool combine,
-                       float* out, float* y_slot, float* y_shared, hipStream_t stream);
+// down products; each row goes to its slot's row (un-permute on store).
+// y16 != nullptr: y16 [T*k + T][H] float16, routed slots then the shared
+// expert's tokens (the layer path; launch_combine16 finishes it).  Else
+// y_slot [T*k][H] float32 and, when not null, y_shared [T][H] float32.
+hipError_t launch_down(const GemmProblem& p, const _Float16* h, _Float16* y16, float* y_slot, float* y_shared,
+                       hipStream_t stream);
 
 // Decode path (T <= kDecodeMaxT, I <= kMaxDecodeI): one kernel per call whose
 // router workgroups publish the logits and rank them, whose gate/up workgroups
@@ -112,5 +113,9 @@ hipError_t launch_decode(const DecodeArgs& a, bool sb_bf16, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_slot, const float* topk_w, const float* y_shared, int T, int H,
                           int k, float* out, hipStream_t stream);
+
+// out[t] = sum_j topk_w[t][j] * y16[t*k+j] (+ y16[T*k+t] when shared), float32.
+hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool shared, int T, int H, int k, float* out,
+                            hipStream_t stream);
 
 }  // namespace bitmoe

@@ -1,5 +1,6 @@
 // Small elementwise kernels for gfx950: the float16 activation copy used by the
-// expert products of the step-by-step API, and the stand-alone weighted combine.
+// expert products of the step-by-step API, the stand-alone weighted combine,
+// and the layer's combine over float16 expert rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -45,12 +46,48 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
 }
 
+// The layer's combine over float16 expert rows: 8 columns per thread, float32
+// accumulation in slot order, then the shared expert's row.
+__global__ __launch_bounds__(256) void combine16_kernel(const _Float16* __restrict__ y16,
+                                                        const float* __restrict__ topk_w, int shared, int T, int H,
+                                                        int k, float* __restrict__ out) {
+    const int h8 = H / 8;
+    const int64_t n = (int64_t)T * h8;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int t = (int)(i / h8), c = (int)(i % h8);
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int j = 0; j < k; j++) {
+            const float w = topk_w[(size_t)t * k + j];
+            const half8_t y = reinterpret_cast<const half8_t*>(y16 + ((size_t)t * k + j) * H)[c];
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[e] += w * (float)y[e];
+        }
+        if (shared) {
+            const half8_t y = reinterpret_cast<const half8_t*>(y16 + ((size_t)T * k + t) * H)[c];
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[e] += (float)y[e];
+        }
+        float4* o = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * c;
+        o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+}
+
 int grid_for(int64_t n) {
     int64_t g = (n + 255) / 256;
     return (int)(g < 1 ? 1 : (g > 8192 ? 8192 : g));
 }
 
 }  // namespace
+
+hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool shared, int T, int H, int k, float* out,
+                            hipStream_t stream) {
+    const int64_t n = (int64_t)T * (H / 8);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(combine16_kernel, dim3(grid_for(n)), dim3(256), 0, stream, y16, topk_w, shared ? 1 : 0, T, H,
+                       k, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_convert_x(const uint16_t* x, int T, int H, _Float16* x16, hipStream_t stream) {
     const int64_t nblk = (int64_t)T * H / 8;

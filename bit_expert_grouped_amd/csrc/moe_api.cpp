@@ -37,7 +37,7 @@ moe_status check_dims(const moe_dims* d) {
 
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
-    size_t ctl, xch, sel, hbuf, x16, h, idx, w, counts, offsets, sorted, tiles, n_tiles, total;
+    size_t ctl, xch, sel, hbuf, x16, h, y16, idx, w, counts, offsets, sorted, tiles, n_tiles, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -61,6 +61,8 @@ Layout layout_of(const moe_dims* d) {
     o = up256(o + T * H * 2);
     L.h = o;
     o = up256(o + (T * k + (shared ? T : 0)) * I * 2);
+    L.y16 = o;
+    o = up256(o + (T * k + (shared ? T : 0)) * H * 2);
     L.idx = o;
     o = up256(o + T * k * 4);
     L.w = o;
@@ -217,7 +219,7 @@ moe_status moe_expert_ffn(const moe_dims* d, const uint16_t* x, const int32_t* o
                          at<int32_t>(ws, L.n_tiles), stream));
     HIP_TRY(launch_convert_x(x, d->T, d->H, x16, stream));
     HIP_TRY(launch_gateup(p, x16, h, stream));
-    HIP_TRY(launch_down(p, h, nullptr, false, nullptr, y_slot, use_shared ? y_shared : nullptr, stream));
+    HIP_TRY(launch_down(p, h, nullptr, y_slot, use_shared ? y_shared : nullptr, stream));
     return MOE_OK;
 }
 
@@ -233,8 +235,8 @@ moe_status moe_combine(const moe_dims* d, const float* y_slot, const float* topk
 
 namespace {
 
-const char* const kPrefillStages[] = {"router", "permute", "gate_up", "down_combine"};
-constexpr int kPrefillStageCount = 4;
+const char* const kPrefillStages[] = {"router", "permute", "gate_up", "down", "combine"};
+constexpr int kPrefillStageCount = 5;
 const char* const kDecodeStages[] = {"decode_layer"};
 constexpr int kDecodeStageCount = 1;
 
@@ -303,6 +305,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     int32_t* sorted = at<int32_t>(ws, L.sorted);
     _Float16* x16 = at<_Float16>(ws, L.x16);
     _Float16* h = at<_Float16>(ws, L.h);
+    _Float16* y16 = at<_Float16>(ws, L.y16);
     float* o = static_cast<float*>(out);
 
     GemmProblem p;
@@ -321,15 +324,18 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     p.shared_w = shared ? to_ptr(&wts->shared) : FfnPtr{};
 
     if (!mark(0)) return MOE_ERR_HIP;
-    HIP_TRY(launch_router(x, wts->router, wts->logit_bias, d->T, d->H, d->E, d->top_k, idx, w, x16, o, stream));
+    HIP_TRY(launch_router(x, wts->router, wts->logit_bias, d->T, d->H, d->E, d->top_k, idx, w, x16, nullptr,
+                          stream));
     if (!mark(1)) return MOE_ERR_HIP;
     HIP_TRY(launch_permute(idx, d->T, d->top_k, d->E, shared, counts, offsets, sorted, at<Tile>(ws, L.tiles),
                            at<int32_t>(ws, L.n_tiles), stream));
     if (!mark(2)) return MOE_ERR_HIP;
     HIP_TRY(launch_gateup(p, x16, h, stream));
     if (!mark(3)) return MOE_ERR_HIP;
-    HIP_TRY(launch_down(p, h, w, true, o, nullptr, nullptr, stream));
+    HIP_TRY(launch_down(p, h, y16, nullptr, nullptr, stream));
     if (!mark(4)) return MOE_ERR_HIP;
+    HIP_TRY(launch_combine16(y16, w, shared, d->T, d->H, d->top_k, o, stream));
+    if (!mark(5)) return MOE_ERR_HIP;
     return MOE_OK;
 }
 

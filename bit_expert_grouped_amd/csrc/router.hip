@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
         }
         const int n4 = H / 4;
         const float4 zero = {0.f, 0.f, 0.f, 0.f};
-        for (int i = threadIdx.x; i < kRouterTokens * n4; i += blockDim.x) {
+        for (int i = threadIdx.x; out_clear && i < kRouterTokens * n4; i += blockDim.x) {
             const int r = i / n4, c = i % n4;
             const int t = t0 + r;
             if (t >= T) break;

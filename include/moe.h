@@ -150,8 +150,8 @@ moe_status moe_combine(const moe_dims *dims, const float *y_slot, const float *t
 /* The whole layer as one device-side pipeline, shared expert included;
  * out [T][H] float32.  Optional copies of the routing: topk_idx_out [T][top_k],
  * topk_w_out [T][top_k], counts_out [E] (each nullable).
- * Prefill (T > 4): route, permute, gate/up with SwiGLU, down with the weighted
- * combine fused into its epilogue.  Decode (T <= 4; pages: decode is a
+ * Prefill (T > 4): route, permute, gate/up with SwiGLU, down storing float16
+ * rows per slot, then the weighted combine with the shared expert.  Decode (T <= 4; pages: decode is a
  * bandwidth-bound workload of its own): a single kernel whose router workgroups
  * rank the experts on the device and whose expert workgroups run the SwiGLU
  * experts and combine into out with atomics.  Uses the workspace's decode region

@@ -48,9 +48,9 @@ def qwen_dims(tokens=512, **kw):
 def test_workspace_size(lib):
     d = qwen_dims(4096)
     n = bem.moe_workspace_size(d)
-    # float16 activations + float16 h rows (routed + shared) dominate
-    assert n >= 4096 * 2048 * 2 + (4096 * 8 + 4096) * 512 * 2
-    assert n < 64 << 20
+    # float16 activations, h rows and expert output rows (routed + shared) dominate
+    big = 4096 * 2048 * 2 + (4096 * 8 + 4096) * 512 * 2 + (4096 * 8 + 4096) * 2048 * 2
+    assert big <= n < big + (8 << 20)
     assert bem.moe_workspace_size(qwen_dims(1)) > 0
     assert bem.moe_workspace_size(qwen_dims(0)) > 0
     assert bem.moe_workspace_size(qwen_dims(4096)) > bem.moe_workspace_size(qwen_dims(512))
