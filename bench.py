@@ -77,8 +77,10 @@ def stage_work(name, sh, T, touched, shared):
     router = (E * H * 2 + T * H * 2, 2.0 * T * H * E)
     gate_up = (n_exp * eb["gate_up"] + T * H * 2 + rows * I * 2, 2.0 * rows * H * 2 * I)
     down = (n_exp * eb["down"] + rows * I * 2 + T * H * 4, 2.0 * rows * I * H)
-    if name == "router":
-        return router[0] + T * k * 8 + T * H * 2 + T * H * 4, router[1]
+    if name == "router":  # logits to the workspace
+        return router[0] + T * E * 4, router[1]
+    if name == "topk":  # logits in, routing out, float16 copy of x
+        return T * E * 4 + T * k * 8 + T * H * 2 + T * H * 2, 0.0
     if name == "permute":
         return T * k * 4 * 2 + E * 8, 0.0
     if name == "gate_up":
@@ -97,6 +99,7 @@ def stage_work(name, sh, T, touched, shared):
 KERNEL_SOURCES = {
     "decode_layer": "bit_expert_grouped_amd/csrc/decode.hip",
     "router": "bit_expert_grouped_amd/csrc/router.hip",
+    "topk": "bit_expert_grouped_amd/csrc/router.hip",
     "permute": "bit_expert_grouped_amd/csrc/permute.hip",
     "gate_up": "bit_expert_grouped_amd/csrc/expert_gemm.hip",
     "down": "bit_expert_grouped_amd/csrc/expert_gemm.hip",

@@ -36,9 +36,20 @@ inline int64_t max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
     return (T * k + (shared ? T : 0)) / kTileRows + E + (shared ? 1 : 0) + 1;
 }
 
+// Router + top-k in one kernel (32 tokens x all experts per workgroup).
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H,
-                         int E, int top_k, int32_t* topk_idx, float* topk_w, _Float16* x16,
-                         float* out_clear, hipStream_t stream);
+                         int E, int top_k, int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+// The layer's spread router: logits [T][E] float32 (workspace), then one wave
+// per token for the top-k, the expert histogram and the float16 copy of x.
+// Counters that thousands of atomics hit are padded to one per 128-byte line
+// (kCounterStride ints apart); launch_logits zeroes zero0[e * kCounterStride]
+// and zero1[e * kCounterStride].
+constexpr int kCounterStride = 32;
+hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H, int E,
+                         float* logits, int32_t* zero0, int32_t* zero1, hipStream_t stream);
+hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int top_k, int32_t* topk_idx,
+                       float* topk_w, int32_t* hist, _Float16* x16, hipStream_t stream);
 
 hipError_t launch_convert_x(const uint16_t* x, int T, int H, _Float16* x16, hipStream_t stream);
 
@@ -46,6 +57,13 @@ hipError_t launch_convert_x(const uint16_t* x, int T, int H, _Float16* x16, hipS
 hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E, bool shared, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_slot, Tile* tiles, int32_t* n_tiles,
                           hipStream_t stream);
+
+// Scan, tile map and scatter from the padded histogram of launch_topk; also
+// writes counts [E] (nullable).  cursor: padded like the histogram, zeroed
+// beforehand (launch_logits' zero1).
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* hist, int T, int k, int E, bool shared,
+                          int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* sorted_slot, Tile* tiles,
+                          int32_t* n_tiles, hipStream_t stream);
 
 // Tile map only, from caller-provided offsets [E+1].
 hipError_t launch_tiles(const int32_t* offsets, int T, int k, int E, bool shared, Tile* tiles,

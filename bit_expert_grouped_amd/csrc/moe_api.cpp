@@ -37,7 +37,9 @@ moe_status check_dims(const moe_dims* d) {
 
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
-    size_t ctl, xch, sel, hbuf, x16, h, y16, idx, w, counts, offsets, sorted, tiles, n_tiles, total;
+    size_t ctl, xch, sel, hbuf;                          // decode region
+    size_t x16, h, y16, logits, hist, cursor;            // prefill buffers
+    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -63,6 +65,12 @@ Layout layout_of(const moe_dims* d) {
     o = up256(o + (T * k + (shared ? T : 0)) * I * 2);
     L.y16 = o;
     o = up256(o + (T * k + (shared ? T : 0)) * H * 2);
+    L.logits = o;
+    o = up256(o + T * E * 4);
+    L.hist = o;
+    o = up256(o + E * kCounterStride * 4);
+    L.cursor = o;
+    o = up256(o + E * kCounterStride * 4);
     L.idx = o;
     o = up256(o + T * k * 4);
     L.w = o;
@@ -167,8 +175,7 @@ moe_status moe_route(const moe_dims* d, const uint16_t* x, const uint16_t* route
     if (d->T == 0) return MOE_OK;
     MOE_TRY(check_ptrs({x, router, topk_idx, topk_w}));
     MOE_TRY(check_opt({logit_bias}));
-    HIP_TRY(launch_router(x, router, logit_bias, d->T, d->H, d->E, d->top_k, topk_idx, topk_w, nullptr, nullptr,
-                          stream));
+    HIP_TRY(launch_router(x, router, logit_bias, d->T, d->H, d->E, d->top_k, topk_idx, topk_w, stream));
     return MOE_OK;
 }
 
@@ -235,8 +242,8 @@ moe_status moe_combine(const moe_dims* d, const float* y_slot, const float* topk
 
 namespace {
 
-const char* const kPrefillStages[] = {"router", "permute", "gate_up", "down", "combine"};
-constexpr int kPrefillStageCount = 5;
+const char* const kPrefillStages[] = {"router", "topk", "permute", "gate_up", "down", "combine"};
+constexpr int kPrefillStageCount = 6;
 const char* const kDecodeStages[] = {"decode_layer"};
 constexpr int kDecodeStageCount = 1;
 
@@ -324,18 +331,22 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     p.shared_w = shared ? to_ptr(&wts->shared) : FfnPtr{};
 
     if (!mark(0)) return MOE_ERR_HIP;
-    HIP_TRY(launch_router(x, wts->router, wts->logit_bias, d->T, d->H, d->E, d->top_k, idx, w, x16, nullptr,
+    int32_t* hist = at<int32_t>(ws, L.hist);
+    int32_t* cursor = at<int32_t>(ws, L.cursor);
+    HIP_TRY(launch_logits(x, wts->router, wts->logit_bias, d->T, d->H, d->E, at<float>(ws, L.logits), hist, cursor,
                           stream));
     if (!mark(1)) return MOE_ERR_HIP;
-    HIP_TRY(launch_permute(idx, d->T, d->top_k, d->E, shared, counts, offsets, sorted, at<Tile>(ws, L.tiles),
-                           at<int32_t>(ws, L.n_tiles), stream));
+    HIP_TRY(launch_topk(at<float>(ws, L.logits), x, d->T, d->H, d->E, d->top_k, idx, w, hist, x16, stream));
     if (!mark(2)) return MOE_ERR_HIP;
-    HIP_TRY(launch_gateup(p, x16, h, stream));
+    HIP_TRY(launch_scatter(idx, hist, d->T, d->top_k, d->E, shared, counts, offsets, cursor, sorted,
+                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.n_tiles), stream));
     if (!mark(3)) return MOE_ERR_HIP;
-    HIP_TRY(launch_down(p, h, y16, nullptr, nullptr, stream));
+    HIP_TRY(launch_gateup(p, x16, h, stream));
     if (!mark(4)) return MOE_ERR_HIP;
-    HIP_TRY(launch_combine16(y16, w, shared, d->T, d->H, d->top_k, o, stream));
+    HIP_TRY(launch_down(p, h, y16, nullptr, nullptr, stream));
     if (!mark(5)) return MOE_ERR_HIP;
+    HIP_TRY(launch_combine16(y16, w, shared, d->T, d->H, d->top_k, o, stream));
+    if (!mark(6)) return MOE_ERR_HIP;
     return MOE_OK;
 }
 

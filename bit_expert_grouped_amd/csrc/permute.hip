@@ -7,9 +7,11 @@
 // grouped products are therefore launched with a grid sized from T alone and
 // read the tile map written here.
 //
-// One workgroup of 1024 threads does everything in LDS: histogram with LDS
-// atomics, block scans, scatter with LDS cursors.  Rows of one expert come out in
-// an unspecified order (LDS atomic order); counts and offsets are exact.
+// Step-by-step call: one workgroup of 1024 threads does everything in LDS
+// (histogram with LDS atomics, block scans, scatter with LDS cursors).  Layer
+// call: scatter_kernel after the top-k kernel's histogram.  Rows of one expert
+// come out in an unspecified order (atomic order); counts and offsets are
+// exact.  Expert indices outside [0, E) are skipped.
 #include "common.h"
 #include "kernels.h"
 
@@ -92,7 +94,10 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     const int n = T * k;
     if (tid < kMaxE) hist[tid] = 0;
     __syncthreads();
-    for (int s = tid; s < n; s += kThreads) atomicAdd(&hist[topk_idx[s]], 1);
+    for (int s = tid; s < n; s += kThreads) {
+        const int e = topk_idx[s];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
     __syncthreads();
     const int c = tid < E ? hist[tid] : 0;
     const int incl = block_inclusive_scan(c, tmp);
@@ -109,8 +114,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     __syncthreads();
     for (int s = tid; s < n; s += kThreads) {
         const int e = topk_idx[s];
-        const int pos = atomicAdd(&cursor[e], 1);
-        sorted_slot[pos] = s;
+        if (e >= 0 && e < E) sorted_slot[atomicAdd(&cursor[e], 1)] = s;
     }
 }
 
@@ -129,6 +133,46 @@ __global__ __launch_bounds__(kThreads) void tiles_kernel(const int32_t* __restri
     write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap);
 }
 
+// The layer's permute after topk_kernel has counted the histogram: every
+// workgroup scans the counts itself (E <= 256 values), workgroup 0 also writes
+// the offsets and the tile map, and each thread places one slot through a
+// global per-expert cursor (zeroed before the top-k), so the scatter spreads
+// over ceil(T k / 1024) workgroups instead of one.
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                           const int32_t* __restrict__ hist, int T, int k,
+                                                           int E, int shared, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ cursor,
+                                                           int32_t* __restrict__ sorted_slot,
+                                                           Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+                                                           int cap) {
+    __shared__ int off[kMaxE];
+    __shared__ int tmp[kThreads / kWave];
+    const int tid = threadIdx.x;
+    const int n = T * k;
+    const int c =
+        tid < E ? __hip_atomic_load(hist + tid * kCounterStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    const int incl = block_inclusive_scan(c, tmp);
+    const int excl = incl - c;
+    if (tid < E) off[tid] = excl;
+    if (blockIdx.x == 0) {
+        if (tid < E) {
+            offsets[tid] = excl;
+            if (counts) counts[tid] = c;
+        }
+        if (tid == E - 1) offsets[E] = incl;
+        const int g_rows = tid < E ? c : ((tid == E && shared) ? T : 0);
+        const int row_base = tid < E ? excl : n;
+        write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap);
+    }
+    __syncthreads();
+    const int s = blockIdx.x * kThreads + tid;
+    if (s < n) {
+        const int e = topk_idx[s];
+        if (e >= 0 && e < E) sorted_slot[off[e] + atomicAdd(cursor + e * kCounterStride, 1)] = s;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E, bool shared, int32_t* counts,
@@ -136,6 +180,17 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E, bool sha
                           hipStream_t stream) {
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kThreads), 0, stream, topk_idx, T, k, E, shared ? 1 : 0,
                        counts, offsets, sorted_slot, tiles, n_tiles, (int)max_tiles(T, k, E, shared));
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* hist, int T, int k, int E, bool shared,
+                          int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* sorted_slot, Tile* tiles,
+                          int32_t* n_tiles, hipStream_t stream) {
+    const int n = T * k;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(scatter_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, topk_idx,
+                       hist, T, k, E, shared ? 1 : 0, counts, offsets, cursor, sorted_slot, tiles, n_tiles,
+                       (int)max_tiles(T, k, E, shared));
     return hipGetLastError();
 }
 

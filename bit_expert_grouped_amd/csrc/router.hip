@@ -13,10 +13,15 @@
 // ranks 8 of the tokens: k rounds of a wave-wide arg-max (ties -> lower index),
 // then the softmax of the kept logits.
 //
-// The fused variant used by the whole-layer call also
-//   - writes the float16 copy of x (8-column blocks in dequantisation order)
-//     that the expert kernels read, and
-//   - clears the float32 output rows that the down kernel accumulates into.
+// That single kernel serves the step-by-step moe_route call.  The whole-layer
+// call spreads the router over the chip instead (a workgroup reading the whole
+// 1 MiB router on its own is bound by one compute unit's bandwidth):
+//   - logits_kernel: one workgroup per (32 tokens, 32 experts); its four waves
+//     split K and sum through LDS; logits go to the workspace;
+//   - topk_kernel: one wave per token ranks its logits, writes the routing,
+//     counts the expert histogram with atomics and writes the float16 copy of
+//     the token's row (8-column blocks in dequantisation order) that the expert
+//     products read.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,16 +30,14 @@ namespace bitmoe {
 namespace {
 
 constexpr int kRouterTokens = 32;
+constexpr int kWaves4 = 4;  // waves per workgroup of the spread router kernels
 
-template <bool kFused>
 __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ wr,
                                                      const float* __restrict__ logit_bias, int T,
                                                      int H, int E, int top_k,
                                                      int32_t* __restrict__ topk_idx,
-                                                     float* __restrict__ topk_w,
-                                                     _Float16* __restrict__ x16,
-                                                     float* __restrict__ out_clear) {
+                                                     float* __restrict__ topk_w) {
     __shared__ float logits[kRouterTokens][kMaxE + 1];
 
     const int wave = threadIdx.x / kWave;
@@ -97,28 +100,104 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
             topk_w[(size_t)t * top_k + lane] = wj;
         }
     }
+}
 
-    if constexpr (kFused) {
-        // float16 copy of x, 8-column blocks in dequantisation order
+constexpr int kLT = 32;  // tokens per logits workgroup
+constexpr int kLE = 32;  // experts per logits workgroup
+constexpr int kLSteps = 8;  // K steps (16 columns each) per load batch
+
+__global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                     const float* __restrict__ logit_bias, int T, int H, int E,
+                                                     float* __restrict__ logits, int32_t* __restrict__ zero0,
+                                                     int32_t* __restrict__ zero1) {
+    __shared__ float part[kWaves4][kLT][kLE + 1];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int row = lane % 32, half = lane / 32;
+    const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+        for (int i = tid; i < E; i += blockDim.x) {
+            if (zero0) __hip_atomic_store(zero0 + i * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (zero1) __hip_atomic_store(zero1 + i * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // wave w takes K columns [w H/4, (w+1) H/4): 16-byte chunk 2 kk + half of its range
+    const int kq = H / 4;
+    const int nk = kq / 16;
+    const uint4* arow = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + row, T - 1) * H + wave * kq);
+    const uint4* brow = reinterpret_cast<const uint4*>(wr + (size_t)min(e0 + row, E - 1) * H + wave * kq);
+    floatx16 acc = {0};
+    uint4 a[kLSteps], b[kLSteps], an[kLSteps], bn[kLSteps];
+#pragma unroll
+    for (int j = 0; j < kLSteps; j++) {
+        const int c = 2 * min(j, nk - 1) + half;
+        a[j] = arow[c];
+        b[j] = brow[c];
+    }
+    for (int kb = 0; kb < nk; kb += kLSteps) {
+        const bool more = kb + kLSteps < nk;
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < kLSteps; j++) {
+                const int c = 2 * min(kb + kLSteps + j, nk - 1) + half;
+                an[j] = arow[c];
+                bn[j] = brow[c];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kLSteps; j++)
+            if (kb + j < nk)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
+                                                              __builtin_bit_cast(bf16x8_t, b[j]), acc, 0, 0, 0);
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < kLSteps; j++) {
+                a[j] = an[j];
+                b[j] = bn[j];
+            }
+        }
+    }
+    // C layout of 32x32 MFMA: lane holds column (lane%32) = expert, rows 8i + 4*(lane/32) + j = tokens
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) part[wave][8 * i + 4 * half + j][row] = acc[4 * i + j];
+    __syncthreads();
+    for (int i = tid; i < kLT * kLE; i += blockDim.x) {
+        const int r = i / kLE, c = i % kLE;
+        const int t = t0 + r, e = e0 + c;
+        if (t < T && e < E) {
+            float v = part[0][r][c] + part[1][r][c] + part[2][r][c] + part[3][r][c];
+            if (logit_bias) v += logit_bias[e];
+            logits[(size_t)t * E + e] = v;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, const uint16_t* __restrict__ x,
+                                                   int T, int H, int E, int top_k, int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w, int32_t* __restrict__ hist,
+                                                   _Float16* __restrict__ x16) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * kWaves4 + wave;
+    if (t >= T) return;  // no workgroup barrier below
+    const float* lt = logits + (size_t)t * E;
+    int ij;
+    float wj;
+    wave_topk([&](int e) { return lt[e]; }, E, top_k, lane, &ij, &wj);
+    if (lane < top_k) {
+        topk_idx[(size_t)t * top_k + lane] = ij;
+        topk_w[(size_t)t * top_k + lane] = wj;
+        if (hist && ij >= 0 && ij < E) atomicAdd(hist + ij * kCounterStride, 1);
+    }
+    if (x16) {
         const int nblk = H / 8;
-        for (int i = threadIdx.x; i < kRouterTokens * nblk; i += blockDim.x) {
-            const int r = i / nblk, blk = i % nblk;
-            const int t = t0 + r;
-            if (t >= T) break;
-            uint4 raw = reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk];
+        for (int blk = lane; blk < nblk; blk += kWave) {
+            const uint4 raw = reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk];
             const uint16_t* hb = reinterpret_cast<const uint16_t*>(&raw);
             half8_t o;
 #pragma unroll
             for (int e = 0; e < 8; e++) o[e] = (_Float16)bf16_to_f32(hb[nibble_of(e)]);
             reinterpret_cast<half8_t*>(x16 + (size_t)t * H)[blk] = o;
-        }
-        const int n4 = H / 4;
-        const float4 zero = {0.f, 0.f, 0.f, 0.f};
-        for (int i = threadIdx.x; out_clear && i < kRouterTokens * n4; i += blockDim.x) {
-            const int r = i / n4, c = i % n4;
-            const int t = t0 + r;
-            if (t >= T) break;
-            reinterpret_cast<float4*>(out_clear + (size_t)t * H)[c] = zero;
         }
     }
 }
@@ -126,17 +205,27 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
 }  // namespace
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H,
-                         int E, int top_k, int32_t* topk_idx, float* topk_w, _Float16* x16,
-                         float* out_clear, hipStream_t stream) {
+                         int E, int top_k, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     dim3 grid((T + kRouterTokens - 1) / kRouterTokens);
-    if (x16) {
-        hipLaunchKernelGGL(router_kernel<true>, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E,
-                           top_k, topk_idx, topk_w, x16, out_clear);
-    } else {
-        hipLaunchKernelGGL(router_kernel<false>, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E,
-                           top_k, topk_idx, topk_w, x16, out_clear);
-    }
+    hipLaunchKernelGGL(router_kernel, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E, top_k, topk_idx,
+                       topk_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H, int E,
+                         float* logits, int32_t* zero0, int32_t* zero1, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    const dim3 grid((T + kLT - 1) / kLT, (E + kLE - 1) / kLE);
+    hipLaunchKernelGGL(logits_kernel, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E, logits, zero0, zero1);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int top_k, int32_t* topk_idx,
+                       float* topk_w, int32_t* hist, _Float16* x16, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_kernel, dim3((T + kWaves4 - 1) / kWaves4), dim3(256), 0, stream, logits, x, T, H, E,
+                       top_k, topk_idx, topk_w, hist, x16);
     return hipGetLastError();
 }
 
