@@ -28,8 +28,8 @@
 //                      the shared expert is one more slot per token.  Reads
 //                      the k words of its token's top k, then computes 16
 //                      values of h = silu(gate x) * (up x).
-//   down    [R+G, ...) one per (slot, 128 output rows).  Reads the top k like
-//                      gate/up, has its 32 KB of whole down rows land in LDS
+//   down    [R+G, ...) one per (slot, 64 output rows).  Reads the top k like
+//                      gate/up, has its 16 KB of whole down rows land in LDS
 //                      (direct loads, issued before it waits for h), waits for
 //                      the slot's h, then adds w * (W_down h) for its rows to
 //                      the float32 output with atomics (the fused combine: k+1
@@ -38,17 +38,17 @@
 // behind every load its compute unit has in flight, and hundreds of
 // workgroups polling many words flood the memory system that the weights are
 // streaming through.  So every poll is a few lanes on a few words:
-//   - logits and top-k entries are 64-bit words {epoch, value} written with
-//     L2-bypassing (agent-scope) stores; a reader waits for the words
-//     themselves.  The router workgroups read one of kXchReplicas copies of the
-//     logits, the expert workgroups one of kSelReplicas copies of the top k
-//     (lanes 0..k-1 of one wave poll them).  The epoch is one more than the
-//     control word the previous call left; the last workgroup to finish stores
-//     it.
-//   - h goes out as plain float32 (agent-scope stores); each gate/up workgroup
-//     then bumps its slot's counter, which one thread of each down workgroup
-//     polls before it reads the slot's h.  The last workgroup to finish resets
-//     the counters.
+//   - values go out as 64-bit words {epoch, value} written with L2-bypassing
+//     (agent-scope) stores; a reader waits for the words themselves.  The
+//     epoch is one more than the control word the previous call left; the last
+//     workgroup to finish stores it.
+//   - the router workgroups read one of kXchReplicas copies of the logits, the
+//     expert workgroups one of kSelReplicas copies of the top k (lanes 0..k-1
+//     of one wave poll them).
+//   - h goes out as float16 pairs, one pair per {epoch, pair} word; a gate/up
+//     workgroup's 16 values are 8 words stored by 8 lanes of one wave.  The
+//     first wave of a down workgroup polls the slot's I/2 words itself (the
+//     poll is the read), sleeping between rounds.
 // Waits are bounded: after kSpinLimit polls a workgroup sets the error control
 // word and carries on (that call's output is then invalid).
 //
@@ -72,7 +72,7 @@ constexpr int kSelReplicas = kDecodeSelReplicas;
 constexpr size_t kXchWords = (size_t)kDecodeMaxT * kMaxE;     // one copy of the logits: [T][E]
 constexpr size_t kSelWords = (size_t)kDecodeMaxT * kMaxTopK;  // one copy of the top k: [T][k]
 constexpr int kGURows = 16;  // gate and up rows per gate/up workgroup
-constexpr int kDRows = 128;  // output rows per down workgroup
+constexpr int kDRows = 64;   // output rows per down workgroup
 constexpr long kSpinLimit = 1l << 20;
 
 // control words (uint32 indices into the workspace control block); words that
@@ -80,10 +80,6 @@ constexpr long kSpinLimit = 1l << 20;
 constexpr int kCtlEpoch = 0;      // epoch of the last completed call
 constexpr int kCtlDone = 64;      // workgroups finished in this call
 constexpr int kCtlError = 255;    // nonzero: a wait timed out
-constexpr int kCtlSlot0 = 512;    // gate/up workgroups of slot s whose h is out: word kCtlSlot0 + 64 s
-constexpr int kCtlSlotStride = 64;
-constexpr int kMaxSlots = kDecodeMaxT * (kMaxTopK + 1);
-static_assert(kCtlSlot0 + kCtlSlotStride * kMaxSlots <= kDecodeControlBytes / 4, "control block too small");
 
 // float16 pairs of 8 activations in the order the exponent trick produces codes
 struct Pairs8 {
@@ -174,9 +170,6 @@ __device__ __forceinline__ unsigned long long peek(const unsigned long long* p) 
 __device__ __forceinline__ void put(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float get(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void flag_error(unsigned* ctl) {
     __hip_atomic_store(ctl + kCtlError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -185,17 +178,18 @@ struct RoleShared {
     union {
         float red[kWaves][kWave * 9];  // gate/up role: cross-lane sums
         struct {
-            uint4 drows[kDRows * 16];  // 128 whole rows of up to 512 columns, landed by direct loads
+            uint4 drows[kDRows * 16];  // 64 whole rows of up to 512 columns, landed by direct loads
             uint4 dsb[2][256];         // scale and bias of those rows (when they fit)
-            _Float16 hh[kMaxDecodeI];  // the slot's h, each 8-column block in nibble order
+            _Float16 hh[kMaxDecodeI];  // the slot's h, 8-column blocks in nibble order, blocks rotated per group
             float2 hsum[kMaxDecodeI / 8];  // low/high sums of h per 8 columns
         } down;
         unsigned long long keys[kDecodeMaxT * kMaxE];  // router role: ranking keys [t][e]
     };
+    float hrow[kGURows];  // gate/up role: this workgroup's h
     int ex;
     float wgt;
     int ok;       // routing read in time
-    int wait_ok;  // result of the last wait_count
+    int wait_ok;  // result of the last wait on published values
     int last;     // this workgroup finished last
 };
 
@@ -222,26 +216,6 @@ __device__ bool await_published(const unsigned long long* src, int n, unsigned e
         }
         __builtin_amdgcn_s_sleep(2);
     }
-}
-
-// One thread polls *ctr until it reaches `target`; the workgroup then proceeds.
-// Returns false (and sets the error word) on timeout.
-__device__ bool wait_count(unsigned* ctr, unsigned target, unsigned* ctl, RoleShared& sh) {
-    if (threadIdx.x == 0) {
-        long spins = 0;
-        int ok = 1;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (++spins > kSpinLimit) {
-                flag_error(ctl);
-                ok = 0;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        sh.wait_ok = ok;
-    }
-    __syncthreads();
-    return sh.wait_ok;
 }
 
 // Ranking key of logit v of expert e: a larger key ranks first, i.e. the larger
@@ -484,13 +458,13 @@ __device__ void gateup_role(const DecodeArgs& p, int slot, int blk, unsigned epo
     const float total = wave_sum8(acc, sh.red[wave], lane);
     // lane 8v holds value v: v < 4 gate row v, v >= 4 up row v-4
     const float upv = __shfl(total, (lane + 32) & 63);
-    if (lane < 32 && lane % 8 == 0)
-        put(p.hbuf + (size_t)slot * I + i0 + wave * kRowsPerWave + lane / 8, silu(total) * upv);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's h is out
+    if (lane < 32 && lane % 8 == 0) sh.hrow[wave * kRowsPerWave + lane / 8] = silu(total) * upv;
     __syncthreads();
-    if (tid == 0)
-        __hip_atomic_fetch_add(p.ctl + kCtlSlot0 + kCtlSlotStride * slot, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    // the 16 values as 8 words {epoch, float16 pair}, one 64-byte store of one wave
+    if (tid < kGURows / 2) {
+        const half2_t pr = {(_Float16)sh.hrow[2 * tid], (_Float16)sh.hrow[2 * tid + 1]};
+        publish(p.h64 + ((size_t)slot * I + i0) / 2 + tid, epoch, as_u32(pr));
+    }
 }
 
 // ------------------------------------------------------------------ down role
@@ -522,9 +496,15 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     const int n_units = n_rows * u_per_row;
     const uint4* dq = reinterpret_cast<const uint4*>(d_q + (ex * (size_t)H + n0) * (I / 8));
     const bool rows_in_lds = u_per_row <= 16;  // I <= 512
+    // 16-unit rows are stored rotated (unit u of row r at u ^ (r % 16)) so that
+    // the 8 rows a wave reads at once hit different LDS banks
+    const int swz_mask = u_per_row == 16 ? 15 : 0;
     if (rows_in_lds) {
-        for (int f0 = wave * kWave; f0 < n_units; f0 += kThreads)
-            __builtin_amdgcn_global_load_lds(dq + min(f0 + lane, n_units - 1), &sh.down.drows[f0], 16, 0, 0);
+        for (int f0 = wave * kWave; f0 < n_units; f0 += kThreads) {
+            const int f = min(f0 + lane, n_units - 1);
+            const int r = f / u_per_row, u = f % u_per_row;
+            __builtin_amdgcn_global_load_lds(dq + r * u_per_row + (u ^ (r & swz_mask)), &sh.down.drows[f0], 16, 0, 0);
+        }
     }
     const SB* ds = reinterpret_cast<const SB*>(d_s) + (ex * (size_t)H + n0) * gd;
     const SB* db = reinterpret_cast<const SB*>(d_b) + (ex * (size_t)H + n0) * gd;
@@ -539,14 +519,45 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     const SB* lds_s = reinterpret_cast<const SB*>(sh.down.dsb[0]);
     const SB* lds_b = reinterpret_cast<const SB*>(sh.down.dsb[1]);
 
-    // wait for the slot's h; keep it as float16 in nibble order, then the
-    // low/high sums of every 8 columns
+    // wait for the slot's h: wave 0 polls the I/2 words {epoch, float16 pair}
+    // until every one carries this call's epoch.  h is kept as float16 in
+    // nibble order; 8-column block m of group g sits at block g * 8 + (m + g) % 8,
+    // so the 8 groups a wave reads at once hit different banks.
+    const unsigned long long* hsrc = p.h64 + (size_t)slot * I / 2;
     _Float16* hh = sh.down.hh;
-    const bool ok = wait_count(p.ctl + kCtlSlot0 + kCtlSlotStride * slot, (unsigned)(I / kGURows), p.ctl, sh) && sh.ok;
-    for (int i = tid; i < I; i += kThreads) hh[(i & ~7) + slot_of_column(i & 7)] = (_Float16)get(p.hbuf + (size_t)slot * I + i);
+    auto h_pos = [](int i) {
+        const int b = i >> 3, g = b >> 3, m = b & 7;
+        return ((g << 3) + ((m + g) & 7)) * 8 + slot_of_column(i & 7);
+    };
+    if (wave == 0) {
+        int ok_h = 1;
+        for (long spins = 0;; spins++) {
+            bool have = true;
+            for (int w = lane; w < I / 2; w += kWave) {
+                const unsigned long long v = peek(hsrc + w);
+                if ((unsigned)(v >> 32) == epoch) {
+                    const half2_t pr = as_half2((uint32_t)v);
+                    hh[h_pos(2 * w)] = pr.x;
+                    hh[h_pos(2 * w + 1)] = pr.y;
+                } else {
+                    have = false;
+                }
+            }
+            if (__ballot(!have) == 0) break;
+            if (spins > kSpinLimit) {
+                if (lane == 0) flag_error(p.ctl);
+                ok_h = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+        }
+        if (lane == 0) sh.wait_ok = ok_h;
+    }
     __syncthreads();
+    const bool ok = sh.wait_ok && sh.ok;
     for (int b8 = tid; b8 < I / 8; b8 += kThreads) {
-        const _Float16* hv = hh + b8 * 8;  // 0,4,1,5,2,6,3,7
+        const int g = b8 >> 3, m = b8 & 7;
+        const _Float16* hv = hh + ((g << 3) + ((m + g) & 7)) * 8;  // 0,4,1,5,2,6,3,7
         sh.down.hsum[b8] = make_float2((float)hv[0] + (float)hv[1] + (float)hv[4] + (float)hv[5],
                                        (float)hv[2] + (float)hv[3] + (float)hv[6] + (float)hv[7]);
     }
@@ -565,18 +576,18 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
         if (g < gd && r < n_rows) {
             uint4 v0, v1;
             if (rows_in_lds) {
-                v0 = sh.down.drows[r * u_per_row + 2 * g];
-                v1 = sh.down.drows[r * u_per_row + 2 * g + 1];
+                v0 = sh.down.drows[r * u_per_row + ((2 * g) ^ (r & swz_mask))];
+                v1 = sh.down.drows[r * u_per_row + ((2 * g + 1) ^ (r & swz_mask))];
             } else {
                 v0 = dq[(size_t)r * u_per_row + 2 * g];
                 v1 = dq[(size_t)r * u_per_row + 2 * g + 1];
             }
-            const uint4* hp4 = reinterpret_cast<const uint4*>(hh) + g * 8;
+            const uint4* hp4 = reinterpret_cast<const uint4*>(hh) + g * 8;  // blocks rotated by g
             float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
             const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
             for (int m = 0; m < 8; m++) {
-                dot_word(wv[m], pairs_of(hp4[m]), alo, ahi);
+                dot_word(wv[m], pairs_of(hp4[(m + g) & 7]), alo, ahi);
                 const float2 sm = sh.down.hsum[g * 8 + m];
                 lo += sm.x;
                 hi += sm.y;
@@ -613,8 +624,8 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
         else
             down_role<SB, false>(p, slot, blk, epoch, sh);
     }
-    // the last workgroup to finish (every other one is past its waits) resets
-    // the counters and advances the epoch for the next call
+    // the last workgroup to finish resets the done counter and advances the
+    // epoch for the next call
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -622,14 +633,9 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
         sh.last = old == gridDim.x - 1;
     }
     __syncthreads();
-    if (sh.last) {
-        const int i = threadIdx.x;
-        if (i < kMaxSlots)
-            __hip_atomic_store(p.ctl + kCtlSlot0 + kCtlSlotStride * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (i == 0) {
-            __hip_atomic_store(p.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(p.ctl + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    if (sh.last && threadIdx.x == 0) {
+        __hip_atomic_store(p.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ctl + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

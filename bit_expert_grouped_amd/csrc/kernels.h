@@ -104,7 +104,7 @@ constexpr int kDecodeSelReplicas = 16;  // copies of the top k, each read by a s
 constexpr int kDecodeControlBytes = 16384;
 constexpr size_t kDecodeXchBytes = (size_t)kDecodeXchReplicas * kDecodeMaxT * 256 * 8;
 constexpr size_t kDecodeSelBytes = (size_t)2 * kDecodeSelReplicas * kDecodeMaxT * 8 * 8;
-constexpr size_t kDecodeHBytes = (size_t)kDecodeMaxT * (8 + 1) * kMaxDecodeI * 4;
+constexpr size_t kDecodeHBytes = (size_t)kDecodeMaxT * (8 + 1) * kMaxDecodeI * 8;
 constexpr size_t kDecodeRegionBytes = kDecodeControlBytes + kDecodeXchBytes + kDecodeSelBytes + kDecodeHBytes;
 
 struct DecodeArgs {
@@ -116,7 +116,7 @@ struct DecodeArgs {
     unsigned* ctl;               // control words and counters
     unsigned long long* xch64;   // kDecodeXchReplicas copies of [kDecodeMaxT][256] {epoch, logit}
     unsigned long long* sel64;   // logits, then experts: each kDecodeSelReplicas copies of [kDecodeMaxT][8] {epoch, value}
-    float* hbuf;                 // [slots][I]; slots = T*k routed, then T shared
+    unsigned long long* h64;     // [slots][I] {epoch, h}; slots = T*k routed, then T shared
     int32_t* idx_out;            // optional copies of the routing
     float* w_out;
     int32_t* counts_out;

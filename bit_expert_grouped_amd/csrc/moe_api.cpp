@@ -292,7 +292,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.ctl = at<unsigned>(ws, L.ctl);
         a.xch64 = at<unsigned long long>(ws, L.xch);
         a.sel64 = at<unsigned long long>(ws, L.sel);
-        a.hbuf = at<float>(ws, L.hbuf);
+        a.h64 = at<unsigned long long>(ws, L.hbuf);
         a.idx_out = topk_idx_out;
         a.w_out = topk_w_out;
         a.counts_out = counts_out;
