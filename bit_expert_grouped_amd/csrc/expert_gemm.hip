@@ -32,9 +32,11 @@
 //     up, so SwiGLU is elementwise on the accumulators; h goes to global memory
 //     as float16 through an LDS transpose (16-byte stores), 8-column blocks in
 //     dequantisation order, which is the K order the down product reads.
-//   - down: a wave computes two 32-column stripes; the epilogue stores each
-//     row to its slot's row (un-permute on store): float16 rows for the
-//     layer's combine kernel, or float32 rows for the step-by-step API.
+//   - down: a wave computes four 32-column stripes (512 output columns per
+//     workgroup, so the activations staged once feed four times the MFMAs of
+//     one stripe pair); the epilogue stores each row to its slot's row
+//     (un-permute on store): float16 rows for the layer's combine kernel, or
+//     float32 rows for the step-by-step API.
 #include "common.h"
 #include "kernels.h"
 
@@ -46,29 +48,43 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMT = kTileRows / 32;              // 32-row MFMA tiles per full row tile
 constexpr int kStageRowBytes = kGroup * 2;       // one group of float16 per row
-constexpr int kBStageBytes = kWaves * 2 * kWave * 16;  // 4 waves x 2 stripes x 64 lanes x 16 B
-constexpr int kLdsBytes = 120 * 1024;                  // the ring (and the epilogue tiles)
-// Scales and biases of a wave's 2 x 32 weight rows for a block of groups, in
-// LDS for the whole K loop: per (stripe, array), 32 rows x kSBRowDwords dwords
-// (a row's 64-byte block plus one dword, so that a block starting at a 2-byte
-// offset fits), loaded with dword direct loads.
-constexpr int kSBRowDwords = 17;
-constexpr int kSBArrayDwords = 9 * kWave;              // >= 32 x 17, whole load instructions
-constexpr int kSBWaveBytes = 4 * kSBArrayDwords * 4;   // (stripe 0, 1) x (scale, bias)
-constexpr int kSBBytes = kWaves * kSBWaveBytes;
-static_assert(32 * kSBRowDwords <= kSBArrayDwords, "scale block layout");
 
 enum Mode { kGateUp = 0, kDownY16 = 1, kDownStore = 2 };
 
+// Geometry of a mode: a wave owns NS stripes of 32 weight rows.  gate/up: the
+// same 32 rows of gate and of up (SwiGLU pairs them); down: consecutive
+// stripes, 4 for the layer's float16 rows (the activations staged once feed
+// 512 output columns), 2 for the float32 rows of the step-by-step call.
+// Scales and biases of a wave's rows stay in LDS for a block of groups: per
+// (stripe, array), 32 rows x kSBRowDwords dwords (a row's block plus one
+// dword, so that a block starting at a 2-byte offset fits), loaded with dword
+// direct loads.
+template <int kMode>
+struct Geo {
+    static constexpr int NS = kMode == kDownY16 ? 4 : 2;
+    static constexpr int kWaveCols = kMode == kGateUp ? 32 : 32 * NS;  // output columns per wave
+    static constexpr int kSlabCols = kWaves * kWaveCols;
+    static constexpr int kBStageBytes = kWaves * NS * kWave * 16;  // each lane's 16 bytes per stripe
+    static constexpr int kSBRowDwords = kMode == kGateUp ? 17 : 5;
+    static constexpr int kSBArrayDwords = (32 * kSBRowDwords + kWave - 1) / kWave * kWave;
+    static constexpr int kSBWaveBytes = NS * 2 * kSBArrayDwords * 4;
+    static constexpr int kSBBytes = kWaves * kSBWaveBytes;
+    // the ring (and the epilogue tiles): what the 160 KB of LDS leaves beside
+    // the scale block and the row tables, in whole KB
+    static constexpr int kRingBytes = kMode == kDownY16 ? 128 * 1024 : 120 * 1024;
+    static_assert(kRingBytes + kSBBytes + 2 * kTileRows * 4 <= 160 * 1024, "LDS");
+};
+
 // Ring of stages for a row tile of MT 32-row MFMA tiles.  Loads per stage and
-// wave, all direct-to-LDS: MT activation chunks and 2 weight chunks.
-template <int MT>
+// wave, all direct-to-LDS: MT activation chunks and NS weight chunks.
+template <int kMode, int MT>
 struct Ring {
-    static constexpr int D = MT == 1 ? 10 : (MT == 2 ? 7 : (MT == 3 ? 6 : 5));
+    using G = Geo<kMode>;
     static constexpr int kABytes = MT * 32 * kStageRowBytes;
-    static constexpr int kStage = kABytes + kBStageBytes;
-    static constexpr int kLoads = MT + 2;
-    static_assert(D * kStage <= kLdsBytes, "ring exceeds LDS");
+    static constexpr int kStage = kABytes + G::kBStageBytes;
+    static constexpr int D = G::kRingBytes / kStage > 10 ? 10 : G::kRingBytes / kStage;
+    static constexpr int kLoads = MT + G::NS;
+    static_assert(D >= 3, "ring too shallow");
     static_assert((D - 2) * kLoads <= 63, "vmcnt holds 6 bits");
     static_assert(D - 2 <= 8, "wait_stages covers up to 8 stages ahead");
 };
@@ -223,23 +239,38 @@ __device__ __forceinline__ uint32_t ds_read_sb(unsigned addr) {
 template <typename SB, int kMode, int MT>
 __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned char* smem, const int* row_src,
                           const int* row_dst) {
-    using R = Ring<MT>;
+    using G = Geo<kMode>;
+    using R = Ring<kMode, MT>;
+    constexpr int NS = G::NS;
     constexpr int D = R::D;
-    constexpr int kWaveCols = kMode == kGateUp ? 32 : 64;  // output columns per wave
-    constexpr int kStripeStep = kMode == kGateUp ? 0 : 32;  // row offset of stripe 1
-    constexpr int kSlabCols = 4 * kWaveCols;
+    constexpr int kWaveCols = G::kWaveCols;
+    constexpr int kSlabCols = G::kSlabCols;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int col = lane % 32, half = lane / 32;
     const int n_groups = p.K / kGroup;
+    const bool sh = tl.group >= p.E;
 
-    // ---- weight rows of this wave: inactive waves read a valid row and drop it ----
+    // ---- weight rows of this wave's stripes; a stripe past N reads a valid row and drops it ----
+    // gate/up: stripe 0 = gate rows [c0, c0+32), stripe 1 = up rows [c0, c0+32);
+    // down: stripe i = rows [c0 + 32 i, c0 + 32 i + 32)
     const int c0 = slab * kSlabCols + wave * kWaveCols;
-    const bool active = c0 < p.N;
-    const int brow = active ? c0 + col : col;
-    const Stripe<SB> st0 = stripe_of<SB>(p.m0, p.s0, tl.group, p.E, p.N, p.K, brow);
-    const Stripe<SB> st1 = stripe_of<SB>(p.m1, p.s1, tl.group, p.E, p.N, p.K, brow + (active ? kStripeStep : 0));
+    bool s_active[NS];
+    Stripe<SB> st[NS];
+    const SB* arr_start[2 * NS];  // the group's rows of each scale/bias array (loads are clamped to them)
+#pragma unroll
+    for (int i = 0; i < NS; i++) {
+        const int r0 = kMode == kGateUp ? c0 : c0 + 32 * i;
+        s_active[i] = r0 < p.N;
+        const QMatPtr& routed = (kMode == kGateUp && i == 1) ? p.m1 : p.m0;
+        const QMatPtr& shared = (kMode == kGateUp && i == 1) ? p.s1 : p.s0;
+        st[i] = stripe_of<SB>(routed, shared, tl.group, p.E, p.N, p.K, s_active[i] ? r0 + col : col);
+        const QMatPtr& m = sh ? shared : routed;
+        const size_t off0 = (size_t)(sh ? 0 : tl.group) * p.N * n_groups;
+        arr_start[2 * i] = reinterpret_cast<const SB*>(m.s) + off0;
+        arr_start[2 * i + 1] = reinterpret_cast<const SB*>(m.b) + off0;
+    }
 
     // ---- activation chunk of each of this lane's MT direct loads per stage ----
     // load i of wave w fills LDS chunks u = (4 i + w) * 64 + lane: row u / 8,
@@ -259,65 +290,55 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
         for (int i = 0; i < MT; i++)
             __builtin_amdgcn_global_load_lds(a_src[i] + kg * kStageRowBytes, base + (i * kWaves + wave) * kWave * 16,
                                              16, 0, 0);
-        __builtin_amdgcn_global_load_lds(st0.q + kg * 2 + half, base + R::kABytes + (wave * 2 + 0) * kWave * 16, 16,
-                                         0, 0);
-        __builtin_amdgcn_global_load_lds(st1.q + kg * 2 + half, base + R::kABytes + (wave * 2 + 1) * kWave * 16, 16,
-                                         0, 0);
+#pragma unroll
+        for (int i = 0; i < NS; i++)
+            __builtin_amdgcn_global_load_lds(st[i].q + kg * 2 + half,
+                                             base + R::kABytes + (wave * NS + i) * kWave * 16, 16, 0, 0);
     };
 
     // ---- scales and biases of this wave's rows, one block of groups at a time ----
-    // array i of the wave: (stripe i / 2, scale or bias); rows of a stripe are
-    // consecutive, so array i of group block g0 is the dword range covering
-    // elements [row0 * ng + g0, (row0 + 32) * ng) (row0 = the stripe's first row),
-    // read dword by dword from where each row's block starts
-    constexpr int kBlk = 64 / (int)sizeof(SB);  // groups per block
+    // array i: (stripe i / 2, scale or bias); rows of a stripe are consecutive,
+    // so array i of group block g0 is read dword by dword from where each of
+    // the 32 rows' blocks starts
+    constexpr int kBlk = (G::kSBRowDwords - 1) * 4 / (int)sizeof(SB);  // groups per block
     const int ng = n_groups;
-    const SB* arr_base[4] = {st0.s - (size_t)col * ng, st0.b - (size_t)col * ng, st1.s - (size_t)col * ng,
-                             st1.b - (size_t)col * ng};  // row `col` back to the stripe's first row
-    const SB* arr_start[4];  // the group's rows of each array (loads are clamped to them)
-    {
-        const bool sh = tl.group >= p.E;
-        const size_t off0 = (size_t)(sh ? 0 : tl.group) * p.N * ng;
-        arr_start[0] = reinterpret_cast<const SB*>(sh ? p.s0.s : p.m0.s) + off0;
-        arr_start[1] = reinterpret_cast<const SB*>(sh ? p.s0.b : p.m0.b) + off0;
-        arr_start[2] = reinterpret_cast<const SB*>(sh ? p.s1.s : p.m1.s) + off0;
-        arr_start[3] = reinterpret_cast<const SB*>(sh ? p.s1.b : p.m1.b) + off0;
-    }
     const size_t group_elems = (size_t)p.N * ng;
-    unsigned char* sb_lds = smem + kLdsBytes + wave * kSBWaveBytes;
+    unsigned char* sb_lds = smem + G::kRingBytes + wave * G::kSBWaveBytes;
+    auto arr_row = [&](int i, int r) {  // first element of row r of the stripe, array i
+        return (i & 1 ? st[i / 2].b : st[i / 2].s) + ((size_t)r - (size_t)col) * ng;
+    };
     auto load_scales = [&](int g0) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 2 * NS; i++) {
             const uintptr_t lo = reinterpret_cast<uintptr_t>(arr_start[i]) & ~uintptr_t(3);
             const uintptr_t hi = (reinterpret_cast<uintptr_t>(arr_start[i] + group_elems) - 4) & ~uintptr_t(3);
 #pragma unroll
-            for (int j = 0; j < kSBArrayDwords / kWave; j++) {
+            for (int j = 0; j < G::kSBArrayDwords / kWave; j++) {
                 const int u = j * kWave + lane;
-                const int r = min(u / kSBRowDwords, 31), dw = u - r * kSBRowDwords;
-                const uintptr_t row_blk = reinterpret_cast<uintptr_t>(arr_base[i] + (size_t)r * ng + g0) & ~uintptr_t(3);
+                const int r = min(u / G::kSBRowDwords, 31), dw = u - r * G::kSBRowDwords;
+                const uintptr_t row_blk = reinterpret_cast<uintptr_t>(arr_row(i, r) + g0) & ~uintptr_t(3);
                 uintptr_t a = row_blk + (uintptr_t)dw * 4;
                 a = a < lo ? lo : (a > hi ? hi : a);
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a),
-                                                 sb_lds + i * kSBArrayDwords * 4 + j * kWave * 4, 4, 0, 0);
+                                                 sb_lds + i * G::kSBArrayDwords * 4 + j * kWave * 4, 4, 0, 0);
             }
         }
     };
     // LDS byte offset of this lane's element g of block g0, array i
     auto sb_off = [&](int i, int g0, int g) -> unsigned {
-        const uintptr_t e = reinterpret_cast<uintptr_t>(arr_base[i] + (size_t)col * ng + g0);
-        return lds_addr(sb_lds) + i * kSBArrayDwords * 4 + col * kSBRowDwords * 4 + (unsigned)(e & 3) +
+        const uintptr_t e = reinterpret_cast<uintptr_t>(arr_row(i, col) + g0);
+        return lds_addr(sb_lds) + i * G::kSBArrayDwords * 4 + col * G::kSBRowDwords * 4 + (unsigned)(e & 3) +
                (unsigned)(g - g0) * (unsigned)sizeof(SB);
     };
 
-    floatx16 acc0[MT], acc1[MT];
+    floatx16 acc[NS][MT];
 #pragma unroll
-    for (int m = 0; m < MT; m++) {
-        acc0[m] = floatx16{0};
-        acc1[m] = floatx16{0};
-    }
+    for (int i = 0; i < NS; i++)
+#pragma unroll
+        for (int m = 0; m < MT; m++) acc[i][m] = floatx16{0};
 
     // LDS offsets of this lane's operand reads inside a stage
-    const unsigned b_off = R::kABytes + wave * 2 * kWave * 16 + lane * 16;
+    const unsigned b_off = R::kABytes + wave * NS * kWave * 16 + lane * 16;
     unsigned a_off[4];
 #pragma unroll
     for (int s = 0; s < 4; s++) a_off[s] = col * kStageRowBytes + (((4 * half + s) ^ (col & 7)) * 16);
@@ -328,12 +349,26 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
 
     auto compute = [&](int slot, int kg, int g0) {
         const unsigned base = lds_addr(smem) + slot * R::kStage;
-        u32x4 bq0 = ds_read16u(base + b_off);
-        u32x4 bq1 = ds_read16u(base + b_off + kWave * 16);
-        uint32_t sv0 = ds_read_sb<SB>(sb_off(0, g0, kg));
-        uint32_t bv0 = ds_read_sb<SB>(sb_off(1, g0, kg));
-        uint32_t sv1 = ds_read_sb<SB>(sb_off(2, g0, kg));
-        uint32_t bv1 = ds_read_sb<SB>(sb_off(3, g0, kg));
+        u32x4 bq[NS];
+        uint32_t sv[NS], bv[NS];
+#pragma unroll
+        for (int i = 0; i < NS; i++) bq[i] = ds_read16u(base + b_off + i * kWave * 16);
+#pragma unroll
+        for (int i = 0; i < NS; i++) {
+            sv[i] = ds_read_sb<SB>(sb_off(2 * i, g0, kg));
+            bv[i] = ds_read_sb<SB>(sb_off(2 * i + 1, g0, kg));
+        }
+        half2_t sc[NS], bi[NS];
+        auto scales_landed = [&]() {
+#pragma unroll
+            for (int i = 0; i < NS; i++) {
+                landed(bq[i]);
+                landed(sv[i]);
+                landed(bv[i]);
+                sc[i] = splat_half2(sb_bits_to_f32<SB>(sv[i]));
+                bi[i] = splat_half2(sb_bits_to_f32<SB>(bv[i]));
+            }
+        };
         if constexpr (MT <= 2) {
             // short tiles: every LDS read of the stage goes out at once; the
             // weights are dequantised while the activation reads land
@@ -342,31 +377,22 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
             for (int s = 0; s < 4; s++)
 #pragma unroll
                 for (int m = 0; m < MT; m++) a[s][m] = ds_read16(base + a_off[s] + m * 32 * kStageRowBytes);
-            wait_lds<4 * MT>();  // the weights and scales (the six oldest reads)
-            landed(bq0);
-            landed(bq1);
-            landed(sv0);
-            landed(bv0);
-            landed(sv1);
-            landed(bv1);
-            const half2_t sc0 = splat_half2(sb_bits_to_f32<SB>(sv0));
-            const half2_t bi0 = splat_half2(sb_bits_to_f32<SB>(bv0));
-            const half2_t sc1 = splat_half2(sb_bits_to_f32<SB>(sv1));
-            const half2_t bi1 = splat_half2(sb_bits_to_f32<SB>(bv1));
-            half8_t w0[4], w1[4];
+            wait_lds<4 * MT>();  // the weights and scales (the 3 NS oldest reads)
+            scales_landed();
+            half8_t w[NS][4];
 #pragma unroll
-            for (int s = 0; s < 4; s++) {
-                w0[s] = dequant_fast(word_of(bq0, s), sc0, bi0, m1024, m64);
-                w1[s] = dequant_fast(word_of(bq1, s), sc1, bi1, m1024, m64);
-            }
+            for (int s = 0; s < 4; s++)
+#pragma unroll
+                for (int i = 0; i < NS; i++) w[i][s] = dequant_fast(word_of(bq[i], s), sc[i], bi[i], m1024, m64);
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 wait_lds_n((3 - s) * MT);
 #pragma unroll
                 for (int m = 0; m < MT; m++) {
                     landed(a[s][m]);
-                    acc0[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][m], w0[s], acc0[m], 0, 0, 0);
-                    acc1[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][m], w1[s], acc1[m], 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < NS; i++)
+                        acc[i][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][m], w[i][s], acc[i][m], 0, 0, 0);
                 }
             }
         } else {
@@ -374,7 +400,6 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
             half8_t a_cur[MT], a_nxt[MT];
 #pragma unroll
             for (int m = 0; m < MT; m++) a_cur[m] = ds_read16(base + a_off[0] + m * 32 * kStageRowBytes);
-            half2_t sc0, bi0, sc1, bi1;
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 if (s < 3) {
@@ -384,27 +409,17 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
                 } else {
                     wait_lds<0>();
                 }
-                if (s == 0) {
-                    landed(bq0);
-                    landed(bq1);
-                    landed(sv0);
-                    landed(bv0);
-                    landed(sv1);
-                    landed(bv1);
-                    sc0 = splat_half2(sb_bits_to_f32<SB>(sv0));
-                    bi0 = splat_half2(sb_bits_to_f32<SB>(bv0));
-                    sc1 = splat_half2(sb_bits_to_f32<SB>(sv1));
-                    bi1 = splat_half2(sb_bits_to_f32<SB>(bv1));
-                }
+                if (s == 0) scales_landed();
 #pragma unroll
                 for (int m = 0; m < MT; m++) landed(a_cur[m]);
-                const half8_t w0 = dequant_fast(word_of(bq0, s), sc0, bi0, m1024, m64);
-                const half8_t w1 = dequant_fast(word_of(bq1, s), sc1, bi1, m1024, m64);
+                half8_t w[NS];
 #pragma unroll
-                for (int m = 0; m < MT; m++) {
-                    acc0[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[m], w0, acc0[m], 0, 0, 0);
-                    acc1[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[m], w1, acc1[m], 0, 0, 0);
-                }
+                for (int i = 0; i < NS; i++) w[i] = dequant_fast(word_of(bq[i], s), sc[i], bi[i], m1024, m64);
+#pragma unroll
+                for (int m = 0; m < MT; m++)
+#pragma unroll
+                    for (int i = 0; i < NS; i++)
+                        acc[i][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[m], w[i], acc[i][m], 0, 0, 0);
                 if (s < 3) {
 #pragma unroll
                     for (int m = 0; m < MT; m++) a_cur[m] = a_nxt[m];
@@ -447,7 +462,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     if constexpr (kMode == kGateUp) {
         // LDS tile [128 rows][kSlabCols columns] float16, columns in dequantisation order
         _Float16* ht = reinterpret_cast<_Float16*>(smem);
-        if (active) {
+        if (s_active[0]) {
             const int cl = wave * kWaveCols + col;  // column within the slab
             const int pos = (cl & ~7) + slot_of_column(cl & 7);
 #pragma unroll
@@ -457,7 +472,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
                         const int r = m * 32 + 8 * i + 4 * half + j;
-                        ht[r * kSlabCols + pos] = (_Float16)(silu(acc0[m][4 * i + j]) * acc1[m][4 * i + j]);
+                        ht[r * kSlabCols + pos] = (_Float16)(silu(acc[0][m][4 * i + j]) * acc[1][m][4 * i + j]);
                     }
                 }
             }
@@ -473,50 +488,56 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
             }
         }
     } else if constexpr (kMode == kDownY16) {
-        // LDS tile [128 rows][kSlabCols columns] float16 in natural column order
+        // LDS tile [64 rows][kSlabCols columns] float16 in natural column order,
+        // one half of the row tile at a time
         _Float16* yt = reinterpret_cast<_Float16*>(smem);
-        if (active) {
-            const int cl = wave * kWaveCols + col;
+        constexpr int kChunks = kSlabCols / 8;
+        const int col_chunks = min(kChunks, (p.N - slab * kSlabCols) / 8);
 #pragma unroll
-            for (int m = 0; m < MT; m++) {
+        for (int hh = 0; hh < (MT + 1) / 2; hh++) {
+            if (hh > 0) __syncthreads();  // the previous half is stored
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
+            for (int m = 2 * hh; m < 2 * hh + 2 && m < MT; m++) {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const int r = m * 32 + 8 * i + 4 * half + j;
-                        yt[r * kSlabCols + cl] = (_Float16)acc0[m][4 * i + j];
-                        yt[r * kSlabCols + cl + kStripeStep] = (_Float16)acc1[m][4 * i + j];
+                for (int si = 0; si < NS; si++) {
+                    if (!s_active[si]) continue;
+                    const int cl = wave * kWaveCols + 32 * si + col;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+#pragma unroll
+                        for (int j = 0; j < 4; j++) {
+                            const int r = (m - 2 * hh) * 32 + 8 * i + 4 * half + j;
+                            yt[r * kSlabCols + cl] = (_Float16)acc[si][m][4 * i + j];
+                        }
                     }
                 }
             }
-        }
-        __syncthreads();
-        constexpr int kChunks = kSlabCols / 8;
-        const int col_chunks = min(kChunks, (p.N - slab * kSlabCols) / 8);
-        for (int idx = tid; idx < tl.rows * kChunks; idx += kThreads) {
-            const int r = idx / kChunks, c = idx % kChunks;
-            if (c < col_chunks) {
-                const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kSlabCols + c * 8);
-                *reinterpret_cast<uint4*>(p.y16 + (size_t)row_dst[r] * p.H + slab * kSlabCols + c * 8) = v;
+            __syncthreads();
+            const int r_lo = 64 * hh, r_hi = min(tl.rows, 64 * hh + 64);
+            for (int idx = tid; idx < (r_hi - r_lo) * kChunks; idx += kThreads) {
+                const int r = idx / kChunks, c = idx % kChunks;
+                if (c < col_chunks) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kSlabCols + c * 8);
+                    *reinterpret_cast<uint4*>(p.y16 + (size_t)row_dst[r_lo + r] * p.H + slab * kSlabCols + c * 8) = v;
+                }
             }
         }
     } else {
-        if (active) {
 #pragma unroll
-            for (int m = 0; m < MT; m++) {
+        for (int m = 0; m < MT; m++) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < 4; i++) {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const int r = m * 32 + 8 * i + 4 * half + j;
-                        if (r < tl.rows) {
-                            const int d = row_dst[r];
-                            float* o = d < p.TK ? p.y_slot + (size_t)d * p.H
-                                                : (p.y_shared ? p.y_shared + (size_t)(d - p.TK) * p.H : nullptr);
-                            if (o) {
-                                o[c0 + col] = acc0[m][4 * i + j];
-                                o[c0 + kStripeStep + col] = acc1[m][4 * i + j];
-                            }
+                for (int j = 0; j < 4; j++) {
+                    const int r = m * 32 + 8 * i + 4 * half + j;
+                    if (r < tl.rows) {
+                        const int d = row_dst[r];
+                        float* o = d < p.TK ? p.y_slot + (size_t)d * p.H
+                                            : (p.y_shared ? p.y_shared + (size_t)(d - p.TK) * p.H : nullptr);
+                        if (o) {
+#pragma unroll
+                            for (int si = 0; si < NS; si++)
+                                if (s_active[si]) o[c0 + 32 * si + col] = acc[si][m][4 * i + j];
                         }
                     }
                 }
@@ -527,7 +548,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
 
 template <typename SB, int kMode>
 __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes + kSBBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Geo<kMode>::kRingBytes + Geo<kMode>::kSBBytes];
     __shared__ int row_src[kTileRows];
     __shared__ int row_dst[kTileRows];
 
@@ -610,7 +631,7 @@ hipError_t launch_gateup(const GemmProblem& pr, const _Float16* x16, _Float16* h
     a.s0 = pr.shared_w.gate;
     a.s1 = pr.shared_w.up;
     a.h = h;
-    a.slabs = (pr.I + 127) / 128;
+    a.slabs = (pr.I + Geo<kGateUp>::kSlabCols - 1) / Geo<kGateUp>::kSlabCols;
     const int64_t grid = (pr.max_tiles * a.slabs + 7) / 8 * 8;
     return launch_mode<kGateUp>(a, pr.sb_bf16, grid, stream);
 }
@@ -629,7 +650,8 @@ hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, 
     a.y16 = y16;
     a.y_slot = y_slot;
     a.y_shared = y_shared;
-    a.slabs = (pr.H + 255) / 256;
+    const int cols = y16 ? Geo<kDownY16>::kSlabCols : Geo<kDownStore>::kSlabCols;
+    a.slabs = (pr.H + cols - 1) / cols;
     const int64_t grid = (pr.max_tiles * a.slabs + 7) / 8 * 8;
     return y16 ? launch_mode<kDownY16>(a, pr.sb_bf16, grid, stream)
                : launch_mode<kDownStore>(a, pr.sb_bf16, grid, stream);
