@@ -48,31 +48,34 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMT = kTileRows / 32;              // 32-row MFMA tiles per full row tile
 constexpr int kStageRowBytes = kGroup * 2;       // one group of float16 per row
+#ifndef GEMM_SB_ROW_DWORDS
+#define GEMM_SB_ROW_DWORDS 5
+#endif
 
 enum Mode { kGateUp = 0, kDownY16 = 1, kDownStore = 2 };
 
-// Geometry of a mode: a wave owns NS stripes of 32 weight rows.  gate/up: the
-// same 32 rows of gate and of up (SwiGLU pairs them); down: consecutive
-// stripes, 4 for the layer's float16 rows (the activations staged once feed
-// 512 output columns), 2 for the float32 rows of the step-by-step call.
+// Geometry of a mode: a wave owns NS stripes of 32 weight rows.  gate/up:
+// stripes 0 .. NS/2-1 of gate and the same rows of up (SwiGLU pairs them), so
+// a wave owns 32 NS/2 columns of h; down: NS consecutive stripes, 4 for the
+// layer's float16 rows (the activations staged once feed 512 output columns),
+// 2 for the float32 rows of the step-by-step call.
 // Scales and biases of a wave's rows stay in LDS for a block of groups: per
 // (stripe, array), 32 rows x kSBRowDwords dwords (a row's block plus one
 // dword, so that a block starting at a 2-byte offset fits), loaded with dword
 // direct loads.
 template <int kMode>
 struct Geo {
-    static constexpr int NS = kMode == kDownY16 ? 4 : 2;
-    static constexpr int kWaveCols = kMode == kGateUp ? 32 : 32 * NS;  // output columns per wave
+    static constexpr int NS = kMode == kDownStore ? 2 : 4;
+    static constexpr int kWaveCols = kMode == kGateUp ? 32 * NS / 2 : 32 * NS;  // output columns per wave
     static constexpr int kSlabCols = kWaves * kWaveCols;
     static constexpr int kBStageBytes = kWaves * NS * kWave * 16;  // each lane's 16 bytes per stripe
-    static constexpr int kSBRowDwords = kMode == kGateUp ? 17 : 5;
+    static constexpr int kSBRowDwords = GEMM_SB_ROW_DWORDS;
     static constexpr int kSBArrayDwords = (32 * kSBRowDwords + kWave - 1) / kWave * kWave;
     static constexpr int kSBWaveBytes = NS * 2 * kSBArrayDwords * 4;
     static constexpr int kSBBytes = kWaves * kSBWaveBytes;
     // the ring (and the epilogue tiles): what the 160 KB of LDS leaves beside
     // the scale block and the row tables, in whole KB
-    static constexpr int kRingBytes = kMode == kDownY16 ? 128 * 1024 : 120 * 1024;
-    static_assert(kRingBytes + kSBBytes + 2 * kTileRows * 4 <= 160 * 1024, "LDS");
+    static constexpr int kRingBytes = (160 * 1024 - kSBBytes - 2 * kTileRows * 4) / 1024 * 1024;
 };
 
 // Ring of stages for a row tile of MT 32-row MFMA tiles.  Loads per stage and
@@ -253,23 +256,24 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     const bool sh = tl.group >= p.E;
 
     // ---- weight rows of this wave's stripes; a stripe past N reads a valid row and drops it ----
-    // gate/up: stripe 0 = gate rows [c0, c0+32), stripe 1 = up rows [c0, c0+32);
-    // down: stripe i = rows [c0 + 32 i, c0 + 32 i + 32)
+    // gate/up: stripe i < NS/2 = gate rows [c0 + 32 i, c0 + 32 i + 32), stripe
+    // NS/2 + i = the same rows of up; down: stripe i = rows [c0 + 32 i, c0 + 32 i + 32)
     const int c0 = slab * kSlabCols + wave * kWaveCols;
     bool s_active[NS];
-    Stripe<SB> st[NS];
+    int row0[NS];                 // first weight row of each stripe (0 for a dropped stripe)
+    const uint4* q_row[NS];       // this lane's row of packed words, 16-byte units
     const SB* arr_start[2 * NS];  // the group's rows of each scale/bias array (loads are clamped to them)
+    const size_t grp = (size_t)(sh ? 0 : tl.group) * p.N;
 #pragma unroll
     for (int i = 0; i < NS; i++) {
-        const int r0 = kMode == kGateUp ? c0 : c0 + 32 * i;
+        const bool up = kMode == kGateUp && i >= NS / 2;
+        const int r0 = c0 + 32 * (up ? i - NS / 2 : i);
         s_active[i] = r0 < p.N;
-        const QMatPtr& routed = (kMode == kGateUp && i == 1) ? p.m1 : p.m0;
-        const QMatPtr& shared = (kMode == kGateUp && i == 1) ? p.s1 : p.s0;
-        st[i] = stripe_of<SB>(routed, shared, tl.group, p.E, p.N, p.K, s_active[i] ? r0 + col : col);
-        const QMatPtr& m = sh ? shared : routed;
-        const size_t off0 = (size_t)(sh ? 0 : tl.group) * p.N * n_groups;
-        arr_start[2 * i] = reinterpret_cast<const SB*>(m.s) + off0;
-        arr_start[2 * i + 1] = reinterpret_cast<const SB*>(m.b) + off0;
+        row0[i] = s_active[i] ? r0 : 0;
+        const QMatPtr& m = sh ? (up ? p.s1 : p.s0) : (up ? p.m1 : p.m0);
+        q_row[i] = reinterpret_cast<const uint4*>(m.q + (grp + row0[i] + col) * (p.K / 8));
+        arr_start[2 * i] = reinterpret_cast<const SB*>(m.s) + grp * n_groups;
+        arr_start[2 * i + 1] = reinterpret_cast<const SB*>(m.b) + grp * n_groups;
     }
 
     // ---- activation chunk of each of this lane's MT direct loads per stage ----
@@ -292,7 +296,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
                                              16, 0, 0);
 #pragma unroll
         for (int i = 0; i < NS; i++)
-            __builtin_amdgcn_global_load_lds(st[i].q + kg * 2 + half,
+            __builtin_amdgcn_global_load_lds(q_row[i] + kg * 2 + half,
                                              base + R::kABytes + (wave * NS + i) * kWave * 16, 16, 0, 0);
     };
 
@@ -305,7 +309,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     const size_t group_elems = (size_t)p.N * ng;
     unsigned char* sb_lds = smem + G::kRingBytes + wave * G::kSBWaveBytes;
     auto arr_row = [&](int i, int r) {  // first element of row r of the stripe, array i
-        return (i & 1 ? st[i / 2].b : st[i / 2].s) + ((size_t)r - (size_t)col) * ng;
+        return arr_start[i] + (size_t)(row0[i / 2] + r) * ng;
     };
     auto load_scales = [&](int g0) {
 #pragma unroll
@@ -460,10 +464,12 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
 
     // ---- epilogues.  Accumulator element 4i+j of a lane: row 8i + 4*half + j, column `col` ----
     if constexpr (kMode == kGateUp) {
-        // LDS tile [128 rows][kSlabCols columns] float16, columns in dequantisation order
+        // LDS tile [128 rows][kSlabCols columns] float16 (64 KB), columns in dequantisation order
         _Float16* ht = reinterpret_cast<_Float16*>(smem);
-        if (s_active[0]) {
-            const int cl = wave * kWaveCols + col;  // column within the slab
+#pragma unroll
+        for (int si = 0; si < NS / 2; si++) {
+            if (!s_active[si]) continue;
+            const int cl = wave * kWaveCols + 32 * si + col;  // column within the slab
             const int pos = (cl & ~7) + slot_of_column(cl & 7);
 #pragma unroll
             for (int m = 0; m < MT; m++) {
@@ -472,7 +478,8 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
                         const int r = m * 32 + 8 * i + 4 * half + j;
-                        ht[r * kSlabCols + pos] = (_Float16)(silu(acc[0][m][4 * i + j]) * acc[1][m][4 * i + j]);
+                        ht[r * kSlabCols + pos] =
+                            (_Float16)(silu(acc[si][m][4 * i + j]) * acc[si + NS / 2][m][4 * i + j]);
                     }
                 }
             }
