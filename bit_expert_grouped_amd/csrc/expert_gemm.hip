@@ -12,19 +12,24 @@
 //   - A workgroup (4 waves) owns one row tile of one expert group (<= 128 rows,
 //     from the device tile map) and one slab of output columns.  The grid is
 //     sized from T alone; workgroups read the tile count written by the permute
-//     kernel and leave when there is no work.  Work ids are handed out in
-//     contiguous ranges per XCD (workgroups are dispatched round-robin over the
-//     8 XCDs), so the slabs of one tile and the tiles of one expert share an L2.
+//     kernel and leave when there is no work.  Workgroups are dispatched
+//     round-robin over the 8 XCDs; tiles are dealt to XCDs the same way in map
+//     order (the map lists long tiles first, so the grid ends on short work and
+//     every XCD gets an equal share), and the slabs of a tile stay on one XCD,
+//     so they share its activation rows in that XCD's L2.
 //   - Operands stream through a ring of LDS stages, one 64-column group of K
 //     per stage, filled by direct-to-LDS loads (global_load_lds_dwordx4): the
 //     activation rows (float16, XOR-swizzled so the 32-row MFMA operand reads
 //     are conflict free; gate/up gathers token rows through the slot
-//     permutation, so the permuted matrix is never materialised) and each
-//     lane's 16 bytes of packed weights.  The ring is deeper for shorter tiles
-//     (less arithmetic per stage), so HBM stays busy at every batch size.  The
-//     waits are counted by hand (s_waitcnt vmcnt(stages ahead x loads per
-//     stage)) and the ring reads are inline-asm ds_reads, so the compiler's
-//     conservative waits for LDS DMA never drain the ring.
+//     permutation, so the permuted matrix is never materialised) and, every
+//     second stage, 64 bytes of each weight row (two groups; requests of 64
+//     bytes stream ~1.4x faster than 32-byte row slices), also XOR-swizzled.
+//     The loads of a later stage go out between the MFMAs of the current one.
+//     The ring is deeper for shorter tiles (less arithmetic per stage), so HBM
+//     stays busy at every batch size.  The waits are counted by hand
+//     (s_waitcnt vmcnt(loads of the stages issued since)) and the ring reads
+//     are inline-asm ds_reads, so the compiler's conservative waits for LDS
+//     DMA never drain the ring.
 //   - A lane's 8 consecutive K values of one output column are exactly one
 //     packed word: it is dequantised in registers (dequant_word: 13 VALU ops
 //     per 8 weights) straight into the B operand of v_mfma_f32_32x32x16_f16.
@@ -78,18 +83,25 @@ struct Geo {
     static constexpr int kRingBytes = (160 * 1024 - kSBBytes - 2 * kTileRows * 4) / 1024 * 1024;
 };
 
-// Ring of stages for a row tile of MT 32-row MFMA tiles.  Loads per stage and
-// wave, all direct-to-LDS: MT activation chunks and NS weight chunks.
+// Ring of stages for a row tile of MT 32-row MFMA tiles, one 64-column group
+// of K per stage.  Loads per wave, all direct-to-LDS: every stage brings MT
+// activation chunks; every even stage also brings the weights of its group and
+// the next one (64 bytes of each weight row in one request, 2 per stripe), so
+// a pair of slots holds [A | B of two groups] [A].
 template <int kMode, int MT>
 struct Ring {
     using G = Geo<kMode>;
     static constexpr int kABytes = MT * 32 * kStageRowBytes;
-    static constexpr int kStage = kABytes + G::kBStageBytes;
-    static constexpr int D = G::kRingBytes / kStage > 10 ? 10 : G::kRingBytes / kStage;
-    static constexpr int kLoads = MT + G::NS;
-    static_assert(D >= 3, "ring too shallow");
-    static_assert((D - 2) * kLoads <= 63, "vmcnt holds 6 bits");
-    static_assert(D - 2 <= 8, "wait_stages covers up to 8 stages ahead");
+    static constexpr int kEven = kABytes + 2 * G::kBStageBytes;
+    static constexpr int kPair = kEven + kABytes;
+    static constexpr int DP = G::kRingBytes / kPair > 5 ? 5 : G::kRingBytes / kPair;
+    static constexpr int D = 2 * DP;  // slots; stage j goes to slot j % D
+    static constexpr int kLoadsEven = MT + 2 * G::NS;
+    static constexpr int kLoadsOdd = MT;
+    static_assert(DP >= 2, "ring too shallow");
+    static_assert((D - 2) / 2 * kLoadsEven + (D - 2) / 2 * kLoadsOdd <= 48, "wait_vm covers 48 loads");
+    static __device__ __forceinline__ int slot_offset(int slot) { return (slot >> 1) * kPair + (slot & 1) * kEven; }
+    static __device__ __forceinline__ int loads(int j) { return (j & 1) ? kLoadsOdd : kLoadsEven; }
 };
 
 struct GemmArgs {
@@ -141,21 +153,23 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)reinterpret_cast<uintptr_t>(p);
 }
 
-// this wave's loads of every stage but the `ahead` newest ones have landed
-template <int L>
-__device__ __forceinline__ void wait_stages(int ahead) {
-    switch (ahead) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(1 * L > 63 ? 63 : 1 * L) : "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L > 63 ? 63 : 2 * L) : "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * L > 63 ? 63 : 3 * L) : "memory"); break;
-        case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * L > 63 ? 63 : 4 * L) : "memory"); break;
-        case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * L > 63 ? 63 : 5 * L) : "memory"); break;
-        case 6: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * L > 63 ? 63 : 6 * L) : "memory"); break;
-        case 7: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(7 * L > 63 ? 63 : 7 * L) : "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * L > 63 ? 63 : 8 * L) : "memory"); break;
+// all but this wave's n newest loads have landed (a smaller n is always safe)
+#define GEMM_VM_CASE(N) \
+    case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+        GEMM_VM_CASE(1) GEMM_VM_CASE(2) GEMM_VM_CASE(3) GEMM_VM_CASE(4) GEMM_VM_CASE(5) GEMM_VM_CASE(6)
+        GEMM_VM_CASE(7) GEMM_VM_CASE(8) GEMM_VM_CASE(9) GEMM_VM_CASE(10) GEMM_VM_CASE(11) GEMM_VM_CASE(12)
+        GEMM_VM_CASE(13) GEMM_VM_CASE(14) GEMM_VM_CASE(15) GEMM_VM_CASE(16) GEMM_VM_CASE(17) GEMM_VM_CASE(18)
+        GEMM_VM_CASE(19) GEMM_VM_CASE(20) GEMM_VM_CASE(21) GEMM_VM_CASE(22) GEMM_VM_CASE(23) GEMM_VM_CASE(24)
+        GEMM_VM_CASE(25) GEMM_VM_CASE(26) GEMM_VM_CASE(27) GEMM_VM_CASE(28) GEMM_VM_CASE(29) GEMM_VM_CASE(30)
+        GEMM_VM_CASE(31) GEMM_VM_CASE(32) GEMM_VM_CASE(33) GEMM_VM_CASE(34) GEMM_VM_CASE(35) GEMM_VM_CASE(36)
+        GEMM_VM_CASE(37) GEMM_VM_CASE(38) GEMM_VM_CASE(39) GEMM_VM_CASE(40) GEMM_VM_CASE(41) GEMM_VM_CASE(42)
+        GEMM_VM_CASE(43) GEMM_VM_CASE(44) GEMM_VM_CASE(45) GEMM_VM_CASE(46) GEMM_VM_CASE(47) GEMM_VM_CASE(48)
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
 }
+#undef GEMM_VM_CASE
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -261,7 +275,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     const int c0 = slab * kSlabCols + wave * kWaveCols;
     bool s_active[NS];
     int row0[NS];                 // first weight row of each stripe (0 for a dropped stripe)
-    const uint4* q_row[NS];       // this lane's row of packed words, 16-byte units
+    const char* q_row[NS];        // first packed row of each stripe
     const SB* arr_start[2 * NS];  // the group's rows of each scale/bias array (loads are clamped to them)
     const size_t grp = (size_t)(sh ? 0 : tl.group) * p.N;
 #pragma unroll
@@ -271,7 +285,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
         s_active[i] = r0 < p.N;
         row0[i] = s_active[i] ? r0 : 0;
         const QMatPtr& m = sh ? (up ? p.s1 : p.s0) : (up ? p.m1 : p.m0);
-        q_row[i] = reinterpret_cast<const uint4*>(m.q + (grp + row0[i] + col) * (p.K / 8));
+        q_row[i] = reinterpret_cast<const char*>(m.q + (grp + row0[i]) * (p.K / 8));
         arr_start[2 * i] = reinterpret_cast<const SB*>(m.s) + grp * n_groups;
         arr_start[2 * i + 1] = reinterpret_cast<const SB*>(m.b) + grp * n_groups;
     }
@@ -288,16 +302,31 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
         a_src[i] = reinterpret_cast<const char*>(p.a + (size_t)src * p.lda) + c * 16;
     }
 
-    auto issue = [&](int kg, int slot) {
-        unsigned char* base = smem + slot * R::kStage;
-#pragma unroll
-        for (int i = 0; i < MT; i++)
-            __builtin_amdgcn_global_load_lds(a_src[i] + kg * kStageRowBytes, base + (i * kWaves + wave) * kWave * 16,
+    // weights: load h of stripe i, lane L -> row 16 h + L / 4 of the stripe,
+    // LDS position L % 4 of that row's 64 bytes, which holds the row's 16-byte
+    // chunk c = (L % 4) ^ ((L / 16) % 4) (group kg + c / 2, half c % 2): the
+    // XOR keeps the 16 rows that one LDS read cycle serves on distinct banks
+    const int row_bytes = p.K / 2;
+    const int b_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const int b_lane = (lane >> 2) * row_bytes + (b_chunk & 1) * 16;
+    const int b_grp = b_chunk >> 1;
+
+    // load q of stage kg (q < MT: activations; then 2 per stripe on even stages)
+    auto issue_one = [&](int kg, int slot, int q) {
+        unsigned char* base = smem + R::slot_offset(slot);
+        if (q < MT) {
+            __builtin_amdgcn_global_load_lds(a_src[q] + kg * kStageRowBytes, base + (q * kWaves + wave) * kWave * 16,
                                              16, 0, 0);
+        } else if (q < MT + 2 * NS && (kg & 1) == 0) {
+            const int i = (q - MT) >> 1, h = (q - MT) & 1;
+            const int g = min(kg + b_grp, n_groups - 1);
+            __builtin_amdgcn_global_load_lds(q_row[i] + 16 * h * row_bytes + b_lane + g * 32,
+                                             base + R::kABytes + ((wave * NS + i) * 2 + h) * kWave * 16, 16, 0, 0);
+        }
+    };
+    auto issue = [&](int kg, int slot) {
 #pragma unroll
-        for (int i = 0; i < NS; i++)
-            __builtin_amdgcn_global_load_lds(q_row[i] + kg * 2 + half,
-                                             base + R::kABytes + (wave * NS + i) * kWave * 16, 16, 0, 0);
+        for (int q = 0; q < MT + 2 * NS; q++) issue_one(kg, slot, q);
     };
 
     // ---- scales and biases of this wave's rows, one block of groups at a time ----
@@ -341,8 +370,11 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
 #pragma unroll
         for (int m = 0; m < MT; m++) acc[i][m] = floatx16{0};
 
-    // LDS offsets of this lane's operand reads inside a stage
-    const unsigned b_off = R::kABytes + wave * NS * kWave * 16 + lane * 16;
+    // LDS offsets of this lane's operand reads: weights of row `col`, chunk
+    // 2 (kg % 2) + half, in the even slot of the pair
+    const int b_row = R::kABytes + wave * NS * 2 * kWave * 16 + (col >> 4) * kWave * 16 + (col & 15) * 64;
+    const unsigned b_off[2] = {(unsigned)(b_row + ((half ^ ((col >> 2) & 3)) * 16)),
+                               (unsigned)(b_row + (((2 + half) ^ ((col >> 2) & 3)) * 16))};
     unsigned a_off[4];
 #pragma unroll
     for (int s = 0; s < 4; s++) a_off[s] = col * kStageRowBytes + (((4 * half + s) ^ (col & 7)) * 16);
@@ -351,12 +383,21 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;
     asm volatile("" : "+v"(m1024), "+v"(m64));
 
-    auto compute = [&](int slot, int kg, int g0) {
-        const unsigned base = lds_addr(smem) + slot * R::kStage;
+    // compute stage kg; the loads of stage nk (< 0: none) into slot nslot go
+    // out one after each MFMA, so their issue hides under the matrix cores
+    auto compute = [&](int slot, int kg, int g0, int nk, int nslot) {
+        int q = 0;
+        auto mfma_then_load = [&](const half8_t& a, const half8_t& w, floatx16& c) {
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w, c, 0, 0, 0);
+            if (q < MT + 2 * NS && nk >= 0) issue_one(nk, nslot, q);
+            q++;
+        };
+        const unsigned base = lds_addr(smem) + R::slot_offset(slot);
+        const unsigned b_base = lds_addr(smem) + R::slot_offset(slot & ~1) + b_off[kg & 1];
         u32x4 bq[NS];
         uint32_t sv[NS], bv[NS];
 #pragma unroll
-        for (int i = 0; i < NS; i++) bq[i] = ds_read16u(base + b_off + i * kWave * 16);
+        for (int i = 0; i < NS; i++) bq[i] = ds_read16u(b_base + i * 2 * kWave * 16);
 #pragma unroll
         for (int i = 0; i < NS; i++) {
             sv[i] = ds_read_sb<SB>(sb_off(2 * i, g0, kg));
@@ -395,8 +436,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
                 for (int m = 0; m < MT; m++) {
                     landed(a[s][m]);
 #pragma unroll
-                    for (int i = 0; i < NS; i++)
-                        acc[i][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][m], w[i][s], acc[i][m], 0, 0, 0);
+                    for (int i = 0; i < NS; i++) mfma_then_load(a[s][m], w[i][s], acc[i][m]);
                 }
             }
         } else {
@@ -422,8 +462,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
 #pragma unroll
                 for (int m = 0; m < MT; m++)
 #pragma unroll
-                    for (int i = 0; i < NS; i++)
-                        acc[i][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[m], w[i], acc[i][m], 0, 0, 0);
+                    for (int i = 0; i < NS; i++) mfma_then_load(a_cur[m], w[i], acc[i][m]);
                 if (s < 3) {
 #pragma unroll
                     for (int m = 0; m < MT; m++) a_cur[m] = a_nxt[m];
@@ -432,15 +471,17 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
         }
     };
 
-    // ---- main loop: stage kg in slot kg % D; D - 1 stages in flight ----
-    // the first scale block goes out before the ring, so waiting for stage 0
-    // also waits for it (loads of a wave complete in order)
+    // ---- main loop: stage kg in slot kg % D; D - 2 stages in flight ----
+    // A slot is refilled two iterations after its stage was computed, so the
+    // weights of an even stage stay for the odd stage after it.  The first
+    // scale block goes out before the ring, so waiting for stage 0 also waits
+    // for it (loads of a wave complete in order).
     load_scales(0);
 #pragma unroll
-    for (int j = 0; j < D - 1; j++)
+    for (int j = 0; j < D - 2; j++)
         if (j < n_groups) issue(j, j);
     int g0 = 0;
-    int slot = 0, fill = D - 1;  // slot of stage kg; slot that stage kg + D - 1 goes to
+    int slot = 0, fill = D - 2;  // slot of stage kg; slot that stage kg + D - 2 goes to
 #pragma unroll 1
     for (int kg = 0; kg < n_groups; kg++) {
         if (kg == g0 + kBlk) {
@@ -452,10 +493,15 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             barrier();
         }
-        wait_stages<R::kLoads>(min(D - 2, n_groups - 1 - kg));
+        // stage kg has landed once only the loads of the stages issued after
+        // it (kg + 1 .. kg + D - 3, those that exist) may be outstanding
+        int younger = 0;
+#pragma unroll
+        for (int j = 1; j <= D - 3; j++)
+            if (kg + j < n_groups) younger += R::loads(kg + j);
+        wait_vm(younger);
         barrier();  // every wave's stage kg has landed; every wave is done with stage kg - 1
-        if (kg + D - 1 < n_groups) issue(kg + D - 1, fill);
-        compute(slot, kg, g0);
+        compute(slot, kg, g0, kg + D - 2 < n_groups ? kg + D - 2 : -1, fill);
         slot = slot == D - 1 ? 0 : slot + 1;
         fill = fill == D - 1 ? 0 : fill + 1;
     }
@@ -559,14 +605,13 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
     __shared__ int row_src[kTileRows];
     __shared__ int row_dst[kTileRows];
 
-    // ---- work id -> (tile, slab), contiguous ranges per XCD ----
-    const int n_work = *p.n_tiles * p.slabs;
+    // ---- workgroup -> (tile, slab): tiles dealt round-robin to the 8 XCDs in
+    // map order (longest first), the slabs of a tile on one XCD ----
     const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-    const int per = (n_work + 7) / 8;
-    const int work = xcd * per + local;
-    if (local >= per || work >= n_work) return;
-    const int slab = work % p.slabs;
-    const Tile tl = p.tiles[work / p.slabs];
+    const int tile = (local / p.slabs) * 8 + xcd;
+    const int slab = local % p.slabs;
+    if (tile >= *p.n_tiles) return;
+    const Tile tl = p.tiles[tile];
     const int mt_count = (tl.rows + 31) / 32;
 
     // row r of the tile: where its activations come from and where its output goes
@@ -639,7 +684,7 @@ hipError_t launch_gateup(const GemmProblem& pr, const _Float16* x16, _Float16* h
     a.s1 = pr.shared_w.up;
     a.h = h;
     a.slabs = (pr.I + Geo<kGateUp>::kSlabCols - 1) / Geo<kGateUp>::kSlabCols;
-    const int64_t grid = (pr.max_tiles * a.slabs + 7) / 8 * 8;
+    const int64_t grid = (pr.max_tiles + 7) / 8 * 8 * a.slabs;
     return launch_mode<kGateUp>(a, pr.sb_bf16, grid, stream);
 }
 
@@ -659,7 +704,7 @@ hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, 
     a.y_shared = y_shared;
     const int cols = y16 ? Geo<kDownY16>::kSlabCols : Geo<kDownStore>::kSlabCols;
     a.slabs = (pr.H + cols - 1) / cols;
-    const int64_t grid = (pr.max_tiles * a.slabs + 7) / 8 * 8;
+    const int64_t grid = (pr.max_tiles + 7) / 8 * 8 * a.slabs;
     return y16 ? launch_mode<kDownY16>(a, pr.sb_bf16, grid, stream)
                : launch_mode<kDownStore>(a, pr.sb_bf16, grid, stream);
 }

@@ -21,8 +21,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 
-// Inclusive scan over the block; `tmp` holds kThreads/64 ints.
-__device__ int block_inclusive_scan(int v, int* tmp) {
+// Inclusive scan over the block; `tmp` holds kThreads/64 ints.  `total`
+// (optional) receives the sum over the block.
+__device__ int block_inclusive_scan(int v, int* tmp, int* total = nullptr) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -42,42 +43,41 @@ __device__ int block_inclusive_scan(int v, int* tmp) {
     }
     __syncthreads();
     int r = v + (wave > 0 ? tmp[wave - 1] : 0);
+    if (total) *total = tmp[kThreads / kWave - 1];
     __syncthreads();
     return r;
 }
 
-// Rows per tile for a group of n rows: split into ceil(n / kTileRows) near-equal
-// chunks rounded up to the 32-row MFMA tile.
-__device__ void chunking(int n, int* rows_per_tile, int* ntiles) {
-    if (n <= 0) {
-        *rows_per_tile = kTileRows;
-        *ntiles = 0;
-        return;
-    }
-    int nch = (n + kTileRows - 1) / kTileRows;
-    int cs = (n + nch - 1) / nch;
-    cs = (cs + 31) / 32 * 32;
-    *rows_per_tile = cs;
-    *ntiles = (n + cs - 1) / cs;
-}
-
-// Thread g (< E, or == E for the shared expert) writes the tiles of group g.
-// Tiles beyond `cap` (the workspace capacity) are dropped, so inconsistent
-// caller offsets cannot write outside the tile array.
+// Tiles of a group of n rows: n / kTileRows full tiles and one tile of the
+// remainder, so at most 31 rows of a group are MFMA padding.  Thread g (< E, or
+// == E for the shared expert) writes the tiles of group g.  The map lists the
+// tiles longest first (full tiles, then remainders of 96, 64 and 32 rows or
+// fewer), so the grouped products start the long work first and end on short
+// tiles.  Tiles beyond `cap` (the workspace capacity) are dropped, so
+// inconsistent caller offsets cannot write outside the tile array.
 __device__ void write_tiles(int g_rows, int row_base, int* tmp, Tile* tiles, int32_t* n_tiles, int cap) {
-    int cs, nt;
-    chunking(g_rows, &cs, &nt);
-    const int incl = block_inclusive_scan(nt, tmp);
-    const int first = incl - nt;
-    for (int c = 0; c < nt && first + c < cap; c++) {
-        Tile t;
-        t.group = threadIdx.x;
-        t.row0 = row_base + c * cs;
-        t.rows = min(cs, g_rows - c * cs);
-        t.pad = 0;
-        tiles[first + c] = t;
+    const int n = max(g_rows, 0);
+    const int full = n / kTileRows, rem = n % kTileRows;
+    const int mt_rem = (rem + 31) / 32;  // 0 .. kTileRows / 32
+    int first_of_class = 0;
+    // classes: kTileRows/32 (full tiles and remainders of that height), then shorter remainders
+    for (int c = kTileRows / 32; c >= 1; c--) {
+        const int cnt = (c == kTileRows / 32 ? full : 0) + (mt_rem == c ? 1 : 0);
+        int total;
+        const int incl = block_inclusive_scan(cnt, tmp, &total);
+        int pos = first_of_class + incl - cnt;
+        for (int j = 0; j < cnt && pos < cap; j++, pos++) {
+            const bool is_rem = j == cnt - 1 && mt_rem == c;
+            Tile t;
+            t.group = threadIdx.x;
+            t.row0 = row_base + (is_rem ? full : j) * kTileRows;
+            t.rows = is_rem ? rem : kTileRows;
+            t.pad = 0;
+            tiles[pos] = t;
+        }
+        first_of_class += total;
     }
-    if (threadIdx.x == kThreads - 1) *n_tiles = min(incl, cap);
+    if (threadIdx.x == 0) *n_tiles = min(first_of_class, cap);
 }
 
 __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ topk_idx, int T,
