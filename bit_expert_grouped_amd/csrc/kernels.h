@@ -36,6 +36,20 @@ inline int64_t max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
     return (T * k + (shared ? T : 0)) / kTileRows + E + (shared ? 1 : 0) + 1;
 }
 
+// Tokens (and experts) per workgroup of the layer's logits kernel, and the
+// number of K slices it splits the router product into (a power of two with
+// H / (64 S) whole; more slices for small batches, so that a few hundred
+// workgroups share the router's rows).  The logits workspace holds S x T x E
+// floats.
+inline int logits_tile(int64_t T) { return T >= 2048 ? 64 : 32; }
+inline int logits_splits(int64_t T, int64_t H, int64_t E) {
+    const int64_t tm = logits_tile(T);
+    const int64_t blocks = ((T + tm - 1) / tm) * ((E + tm - 1) / tm);
+    int S = 1;
+    while (blocks * S < 256 && H % (64 * 2 * S) == 0) S *= 2;
+    return S;
+}
+
 // Router + top-k in one kernel (32 tokens x all experts per workgroup).
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H,
                          int E, int top_k, int32_t* topk_idx, float* topk_w, hipStream_t stream);

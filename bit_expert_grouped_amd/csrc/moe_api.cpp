@@ -66,7 +66,7 @@ Layout layout_of(const moe_dims* d) {
     L.y16 = o;
     o = up256(o + (T * k + (shared ? T : 0)) * H * 2);
     L.logits = o;
-    o = up256(o + T * E * 4);
+    o = up256(o + (size_t)logits_splits(d->T, d->H, d->E) * T * E * 4);
     L.hist = o;
     o = up256(o + E * kCounterStride * 4);
     L.cursor = o;

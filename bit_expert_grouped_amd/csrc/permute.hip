@@ -135,9 +135,11 @@ __global__ __launch_bounds__(kThreads) void tiles_kernel(const int32_t* __restri
 
 // The layer's permute after topk_kernel has counted the histogram: every
 // workgroup scans the counts itself (E <= 256 values), workgroup 0 also writes
-// the offsets and the tile map, and each thread places one slot through a
-// global per-expert cursor (zeroed before the top-k), so the scatter spreads
-// over ceil(T k / 1024) workgroups instead of one.
+// the offsets and the tile map, and each workgroup places its 1024 slots: ranks
+// within the workgroup from LDS atomics, one global atomic per (workgroup,
+// expert) on a per-expert cursor (zeroed before the top-k) to reserve the run,
+// so the scatter spreads over ceil(T k / 1024) workgroups with little
+// contention on the cursors.
 __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __restrict__ topk_idx,
                                                            const int32_t* __restrict__ hist, int T, int k,
                                                            int E, int shared, int32_t* __restrict__ counts,
@@ -147,9 +149,11 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
                                                            Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                            int cap) {
     __shared__ int off[kMaxE];
+    __shared__ int local[kMaxE];  // this workgroup's slots per expert, then their global base
     __shared__ int tmp[kThreads / kWave];
     const int tid = threadIdx.x;
     const int n = T * k;
+    if (tid < kMaxE) local[tid] = 0;
     const int c =
         tid < E ? __hip_atomic_load(hist + tid * kCounterStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
     const int incl = block_inclusive_scan(c, tmp);
@@ -166,11 +170,16 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
         write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap);
     }
     __syncthreads();
+    // rank each slot among this workgroup's slots of its expert (LDS atomics),
+    // then reserve the workgroup's run of each expert with one global atomic
     const int s = blockIdx.x * kThreads + tid;
-    if (s < n) {
-        const int e = topk_idx[s];
-        if (e >= 0 && e < E) sorted_slot[off[e] + atomicAdd(cursor + e * kCounterStride, 1)] = s;
-    }
+    const int e = s < n ? topk_idx[s] : -1;
+    const bool valid = e >= 0 && e < E;
+    const int rank = valid ? atomicAdd(&local[e], 1) : 0;
+    __syncthreads();
+    if (tid < E && local[tid] > 0) local[tid] = off[tid] + atomicAdd(cursor + tid * kCounterStride, local[tid]);
+    __syncthreads();
+    if (valid) sorted_slot[local[e] + rank] = s;
 }
 
 }  // namespace

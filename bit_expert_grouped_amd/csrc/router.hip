@@ -18,7 +18,7 @@
 // 1 MiB router on its own is bound by one compute unit's bandwidth):
 //   - logits_kernel: one workgroup per (32 tokens, 32 experts); its four waves
 //     split K and sum through LDS; logits go to the workspace;
-//   - topk_kernel: one wave per token ranks its logits, writes the routing,
+//   - topk_kernel: one wave per token sums and ranks its logits, writes the routing,
 //     counts the expert histogram with atomics and writes the float16 copy of
 //     the token's row (8-column blocks in dequantisation order) that the expert
 //     products read.
@@ -102,88 +102,143 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
     }
 }
 
-constexpr int kLT = 32;  // tokens per logits workgroup
-constexpr int kLE = 32;  // experts per logits workgroup
-constexpr int kLSteps = 8;  // K steps (16 columns each) per load batch
-
+// logits_kernel: one workgroup per (TM tokens, TM experts, 1/S of K).  Its four
+// waves split the workgroup's K range and sum through LDS; split z writes its
+// partial logits to partial[z][T][E] (split 0 adds the bias) and topk_kernel
+// sums the S splits in order.  TM = 64 for large batches (each x row and router
+// row is read by half as many workgroups), 32 with K split S ways for small
+// ones, so that the router's 1 MiB is spread over a few hundred workgroups.
+template <int TM>
 __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-                                                     const float* __restrict__ logit_bias, int T, int H, int E,
-                                                     float* __restrict__ logits, int32_t* __restrict__ zero0,
+                                                     const float* __restrict__ logit_bias, int T, int H, int E, int S,
+                                                     float* __restrict__ partial, int32_t* __restrict__ zero0,
                                                      int32_t* __restrict__ zero1) {
-    __shared__ float part[kWaves4][kLT][kLE + 1];
+    constexpr int MB = TM / 32;               // 32-row MFMA blocks per side
+    constexpr int kSteps = TM == 32 ? 8 : 4;  // K steps (16 columns each) per load batch
+    __shared__ float part[kWaves4][TM][TM + 1];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int row = lane % 32, half = lane / 32;
-    const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
-    if (blockIdx.x == 0 && blockIdx.y == 0) {
+    const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TM, z = blockIdx.z;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && z == 0) {
         for (int i = tid; i < E; i += blockDim.x) {
             if (zero0) __hip_atomic_store(zero0 + i * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (zero1) __hip_atomic_store(zero1 + i * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // wave w takes K columns [w H/4, (w+1) H/4): 16-byte chunk 2 kk + half of its range
-    const int kq = H / 4;
+    // wave w takes K columns [kb, kb + kq) of this split: 16-byte chunk 2 kk + half of its range
+    const int kq = H / (kWaves4 * S);
     const int nk = kq / 16;
-    const uint4* arow = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + row, T - 1) * H + wave * kq);
-    const uint4* brow = reinterpret_cast<const uint4*>(wr + (size_t)min(e0 + row, E - 1) * H + wave * kq);
-    floatx16 acc = {0};
-    uint4 a[kLSteps], b[kLSteps], an[kLSteps], bn[kLSteps];
+    const int kb = z * (H / S) + wave * kq;
+    const uint4* arow[MB];
+    const uint4* brow[MB];
 #pragma unroll
-    for (int j = 0; j < kLSteps; j++) {
-        const int c = 2 * min(j, nk - 1) + half;
-        a[j] = arow[c];
-        b[j] = brow[c];
+    for (int m = 0; m < MB; m++) {
+        arow[m] = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + 32 * m + row, T - 1) * H + kb);
+        brow[m] = reinterpret_cast<const uint4*>(wr + (size_t)min(e0 + 32 * m + row, E - 1) * H + kb);
     }
-    for (int kb = 0; kb < nk; kb += kLSteps) {
-        const bool more = kb + kLSteps < nk;
+    floatx16 acc[MB][MB];
+#pragma unroll
+    for (int m = 0; m < MB; m++)
+#pragma unroll
+        for (int n = 0; n < MB; n++) acc[m][n] = floatx16{0};
+    uint4 a[kSteps][MB], b[kSteps][MB], an[kSteps][MB], bn[kSteps][MB];
+#pragma unroll
+    for (int j = 0; j < kSteps; j++) {
+        const int c = 2 * min(j, nk - 1) + half;
+#pragma unroll
+        for (int m = 0; m < MB; m++) {
+            a[j][m] = arow[m][c];
+            b[j][m] = brow[m][c];
+        }
+    }
+    for (int kk = 0; kk < nk; kk += kSteps) {
+        const bool more = kk + kSteps < nk;
         if (more) {
 #pragma unroll
-            for (int j = 0; j < kLSteps; j++) {
-                const int c = 2 * min(kb + kLSteps + j, nk - 1) + half;
-                an[j] = arow[c];
-                bn[j] = brow[c];
+            for (int j = 0; j < kSteps; j++) {
+                const int c = 2 * min(kk + kSteps + j, nk - 1) + half;
+#pragma unroll
+                for (int m = 0; m < MB; m++) {
+                    an[j][m] = arow[m][c];
+                    bn[j][m] = brow[m][c];
+                }
             }
         }
 #pragma unroll
-        for (int j = 0; j < kLSteps; j++)
-            if (kb + j < nk)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
-                                                              __builtin_bit_cast(bf16x8_t, b[j]), acc, 0, 0, 0);
+        for (int j = 0; j < kSteps; j++)
+            if (kk + j < nk) {
+#pragma unroll
+                for (int m = 0; m < MB; m++)
+#pragma unroll
+                    for (int n = 0; n < MB; n++)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[j][m]),
+                                                                            __builtin_bit_cast(bf16x8_t, b[j][n]),
+                                                                            acc[m][n], 0, 0, 0);
+            }
         if (more) {
 #pragma unroll
-            for (int j = 0; j < kLSteps; j++) {
-                a[j] = an[j];
-                b[j] = bn[j];
-            }
+            for (int j = 0; j < kSteps; j++)
+#pragma unroll
+                for (int m = 0; m < MB; m++) {
+                    a[j][m] = an[j][m];
+                    b[j][m] = bn[j][m];
+                }
         }
     }
     // C layout of 32x32 MFMA: lane holds column (lane%32) = expert, rows 8i + 4*(lane/32) + j = tokens
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int m = 0; m < MB; m++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) part[wave][8 * i + 4 * half + j][row] = acc[4 * i + j];
+        for (int n = 0; n < MB; n++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) part[wave][32 * m + 8 * i + 4 * half + j][32 * n + row] = acc[m][n][4 * i + j];
     __syncthreads();
-    for (int i = tid; i < kLT * kLE; i += blockDim.x) {
-        const int r = i / kLE, c = i % kLE;
+    for (int i = tid; i < TM * TM; i += blockDim.x) {
+        const int r = i / TM, c = i % TM;
         const int t = t0 + r, e = e0 + c;
         if (t < T && e < E) {
             float v = part[0][r][c] + part[1][r][c] + part[2][r][c] + part[3][r][c];
-            if (logit_bias) v += logit_bias[e];
-            logits[(size_t)t * E + e] = v;
+            if (z == 0 && logit_bias) v += logit_bias[e];
+            partial[((size_t)z * T + t) * E + e] = v;
         }
     }
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, const uint16_t* __restrict__ x,
-                                                   int T, int H, int E, int top_k, int32_t* __restrict__ topk_idx,
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int S,
+                                                   const uint16_t* __restrict__ x, int T, int H, int E, int top_k,
+                                                   int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w, int32_t* __restrict__ hist,
                                                    _Float16* __restrict__ x16) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int t = blockIdx.x * kWaves4 + wave;
     if (t >= T) return;  // no workgroup barrier below
     const float* lt = logits + (size_t)t * E;
+    const size_t split = (size_t)T * E;
+    // this lane's experts lane + 64 i: sum of the S partial logits, in split
+    // order; the loads of 8 splits go out before their adds
+    constexpr int kPer = kMaxE / kWave;
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; i++) v[i] = lane + kWave * i < E ? lt[lane + kWave * i] : 0.0f;
+    for (int z0 = 1; z0 < S; z0 += 8) {
+        float p[8][kPer];
+#pragma unroll
+        for (int dz = 0; dz < 8; dz++)
+#pragma unroll
+            for (int i = 0; i < kPer; i++) {
+                const int e = lane + kWave * i;
+                p[dz][i] = (z0 + dz < S && e < E) ? lt[(size_t)(z0 + dz) * split + e] : 0.0f;
+            }
+#pragma unroll
+        for (int dz = 0; dz < 8; dz++)
+#pragma unroll
+            for (int i = 0; i < kPer; i++) v[i] += p[dz][i];
+    }
     int ij;
     float wj;
-    wave_topk([&](int e) { return lt[e]; }, E, top_k, lane, &ij, &wj);
+    wave_topk([&](int e) { return v[e / kWave]; }, E, top_k, lane, &ij, &wj);
     if (lane < top_k) {
         topk_idx[(size_t)t * top_k + lane] = ij;
         topk_w[(size_t)t * top_k + lane] = wj;
@@ -216,16 +271,23 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* log
 hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H, int E,
                          float* logits, int32_t* zero0, int32_t* zero1, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    const dim3 grid((T + kLT - 1) / kLT, (E + kLE - 1) / kLE);
-    hipLaunchKernelGGL(logits_kernel, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E, logits, zero0, zero1);
+    const int tm = logits_tile(T);
+    const int S = logits_splits(T, H, E);
+    const dim3 grid((T + tm - 1) / tm, (E + tm - 1) / tm, S);
+    if (tm == 64)
+        hipLaunchKernelGGL(logits_kernel<64>, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E, S, logits, zero0,
+                           zero1);
+    else
+        hipLaunchKernelGGL(logits_kernel<32>, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E, S, logits, zero0,
+                           zero1);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int top_k, int32_t* topk_idx,
                        float* topk_w, int32_t* hist, _Float16* x16, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3((T + kWaves4 - 1) / kWaves4), dim3(256), 0, stream, logits, x, T, H, E,
-                       top_k, topk_idx, topk_w, hist, x16);
+    hipLaunchKernelGGL(topk_kernel, dim3((T + kWaves4 - 1) / kWaves4), dim3(256), 0, stream, logits,
+                       logits_splits(T, H, E), x, T, H, E, top_k, topk_idx, topk_w, hist, x16);
     return hipGetLastError();
 }
 
