@@ -384,8 +384,11 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     asm volatile("" : "+v"(m1024), "+v"(m64));
 
     // compute stage kg; the loads of stage nk (< 0: none) into slot nslot go
-    // out one after each MFMA, so their issue hides under the matrix cores
-    auto compute = [&](int slot, int kg, int g0, int nk, int nslot) {
+    // out one after each MFMA, so their issue hides under the matrix cores.
+    // g_next >= 0: once this stage's scales are read, this wave's scale block
+    // is refilled with the block starting at group g_next (each wave owns its
+    // block, so no barrier is needed).
+    auto compute = [&](int slot, int kg, int g0, int nk, int nslot, int g_next) {
         int q = 0;
         auto mfma_then_load = [&](const half8_t& a, const half8_t& w, floatx16& c) {
             c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w, c, 0, 0, 0);
@@ -424,6 +427,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
                 for (int m = 0; m < MT; m++) a[s][m] = ds_read16(base + a_off[s] + m * 32 * kStageRowBytes);
             wait_lds<4 * MT>();  // the weights and scales (the 3 NS oldest reads)
             scales_landed();
+            if (g_next >= 0) load_scales(g_next);
             half8_t w[NS][4];
 #pragma unroll
             for (int s = 0; s < 4; s++)
@@ -453,7 +457,10 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
                 } else {
                     wait_lds<0>();
                 }
-                if (s == 0) scales_landed();
+                if (s == 0) {
+                    scales_landed();
+                    if (g_next >= 0) load_scales(g_next);
+                }
 #pragma unroll
                 for (int m = 0; m < MT; m++) landed(a_cur[m]);
                 half8_t w[NS];
@@ -475,7 +482,8 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     // A slot is refilled two iterations after its stage was computed, so the
     // weights of an even stage stay for the odd stage after it.  The first
     // scale block goes out before the ring, so waiting for stage 0 also waits
-    // for it (loads of a wave complete in order).
+    // for it (loads of a wave complete in order); later blocks go out during
+    // the last stage of the block before, so the ring never drains.
     load_scales(0);
 #pragma unroll
     for (int j = 0; j < D - 2; j++)
@@ -484,24 +492,25 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     int slot = 0, fill = D - 2;  // slot of stage kg; slot that stage kg + D - 2 goes to
 #pragma unroll 1
     for (int kg = 0; kg < n_groups; kg++) {
-        if (kg == g0 + kBlk) {
-            // next scale block (K beyond one block): drain, reload, go on
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            barrier();
-            g0 = kg;
-            load_scales(g0);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            barrier();
-        }
-        // stage kg has landed once only the loads of the stages issued after
-        // it (kg + 1 .. kg + D - 3, those that exist) may be outstanding
         int younger = 0;
+        if (kg == g0 + kBlk) {
+            // first stage of the next scale block: the block went out in the
+            // previous iteration, after the loads of stages up to kg + D - 4
+            // and before those of stage kg + D - 3, so all but stage
+            // kg + D - 3's loads must have landed
+            g0 = kg;
+            if (kg + D - 3 < n_groups) younger = R::loads(kg + D - 3);
+        } else {
+            // stage kg has landed once only the loads of the stages issued
+            // after it (kg + 1 .. kg + D - 3, those that exist) may be outstanding
 #pragma unroll
-        for (int j = 1; j <= D - 3; j++)
-            if (kg + j < n_groups) younger += R::loads(kg + j);
+            for (int j = 1; j <= D - 3; j++)
+                if (kg + j < n_groups) younger += R::loads(kg + j);
+        }
         wait_vm(younger);
         barrier();  // every wave's stage kg has landed; every wave is done with stage kg - 1
-        compute(slot, kg, g0, kg + D - 2 < n_groups ? kg + D - 2 : -1, fill);
+        const int g_next = kg + 1 == g0 + kBlk && kg + 1 < n_groups ? kg + 1 : -1;
+        compute(slot, kg, g0, kg + D - 2 < n_groups ? kg + D - 2 : -1, fill, g_next);
         slot = slot == D - 1 ? 0 : slot + 1;
         fill = fill == D - 1 ? 0 : fill + 1;
     }
