@@ -444,8 +444,10 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
                 }
             }
         } else {
-            // tall tiles: activation reads one K step ahead of the MFMAs
+            // tall tiles: activation reads one K step ahead of the MFMAs, and
+            // the next K step's weights dequantised between this step's MFMAs
             half8_t a_cur[MT], a_nxt[MT];
+            half8_t w_cur[NS], w_nxt[NS];
 #pragma unroll
             for (int m = 0; m < MT; m++) a_cur[m] = ds_read16(base + a_off[0] + m * 32 * kStageRowBytes);
 #pragma unroll
@@ -460,19 +462,24 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
                 if (s == 0) {
                     scales_landed();
                     if (g_next >= 0) load_scales(g_next);
+#pragma unroll
+                    for (int i = 0; i < NS; i++) w_cur[i] = dequant_fast(word_of(bq[i], 0), sc[i], bi[i], m1024, m64);
                 }
 #pragma unroll
                 for (int m = 0; m < MT; m++) landed(a_cur[m]);
-                half8_t w[NS];
-#pragma unroll
-                for (int i = 0; i < NS; i++) w[i] = dequant_fast(word_of(bq[i], s), sc[i], bi[i], m1024, m64);
 #pragma unroll
                 for (int m = 0; m < MT; m++)
 #pragma unroll
-                    for (int i = 0; i < NS; i++) mfma_then_load(a_cur[m], w[i], acc[i][m]);
+                    for (int i = 0; i < NS; i++) {
+                        mfma_then_load(a_cur[m], w_cur[i], acc[i][m]);
+                        if (m == 0 && s < 3)
+                            w_nxt[i] = dequant_fast(word_of(bq[i], s + 1), sc[i], bi[i], m1024, m64);
+                    }
                 if (s < 3) {
 #pragma unroll
                     for (int m = 0; m < MT; m++) a_cur[m] = a_nxt[m];
+#pragma unroll
+                    for (int i = 0; i < NS; i++) w_cur[i] = w_nxt[i];
                 }
             }
         }
