@@ -625,8 +625,9 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
             down_role<SB, false>(p, slot, blk, epoch, sh);
     }
     // the last workgroup to finish resets the done counter and advances the
-    // epoch for the next call
-    __builtin_amdgcn_s_waitcnt(0);
+    // epoch for the next call.  Its own stores and atomics need not have
+    // landed: the next call starts after this kernel has ended, and every
+    // workgroup read the epoch when it started, before it counted itself done.
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned old = __hip_atomic_fetch_add(p.ctl + kCtlDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
