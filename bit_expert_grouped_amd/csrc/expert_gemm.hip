@@ -634,7 +634,18 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
     // (-1: padding).  Grouped row gp < T*k is slot sorted_slot[gp] of token slot / k;
     // rows from T*k on are the shared expert's tokens.
     const int tid = threadIdx.x;
-    if (tid < kTileRows) {
+    if (kMode != kGateUp) {
+        // down reads grouped row gp itself; only its epilogue needs the slot,
+        // which lands by a direct load that the main loop's final wait covers
+        if (tid < kTileRows) {
+            const int r = tid, gp = tl.row0 + r;
+            row_src[r] = r < tl.rows ? gp : -1;
+            if (r < tl.rows && gp < p.TK)
+                __builtin_amdgcn_global_load_lds(p.sorted_slot + gp, &row_dst[tid / kWave * kWave], 4, 0, 0);
+            else
+                row_dst[r] = r < tl.rows ? gp : -1;  // shared rows: slot T*k + t = gp
+        }
+    } else if (tid < kTileRows) {
         const int r = tid;
         int src = -1, dst = -1;
         if (r < tl.rows) {
