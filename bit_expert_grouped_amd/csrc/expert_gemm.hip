@@ -68,9 +68,12 @@ enum Mode { kGateUp = 0, kDownY16 = 1, kDownStore = 2 };
 // (stripe, array), 32 rows x kSBRowDwords dwords (a row's block plus one
 // dword, so that a block starting at a 2-byte offset fits), loaded with dword
 // direct loads.
-template <int kMode>
+// kS (small batches, tiles of at most 64 rows): 2 stripes per wave and at most
+// 80 KB of LDS, so that two workgroups share a compute unit and twice the
+// loads are in flight per unit where the weights stream for few rows.
+template <int kMode, bool kS = false>
 struct Geo {
-    static constexpr int NS = kMode == kDownStore ? 2 : 4;
+    static constexpr int NS = kS || kMode == kDownStore ? 2 : 4;
     static constexpr int kWaveCols = kMode == kGateUp ? 32 * NS / 2 : 32 * NS;  // output columns per wave
     static constexpr int kSlabCols = kWaves * kWaveCols;
     static constexpr int kBStageBytes = kWaves * NS * kWave * 16;  // each lane's 16 bytes per stripe
@@ -80,7 +83,9 @@ struct Geo {
     static constexpr int kSBBytes = kWaves * kSBWaveBytes;
     // the ring (and the epilogue tiles): what the 160 KB of LDS leaves beside
     // the scale block and the row tables, in whole KB
-    static constexpr int kRingBytes = (160 * 1024 - kSBBytes - 2 * kTileRows * 4) / 1024 * 1024;
+    static constexpr int kLdsBytes = kS ? 80 * 1024 : 160 * 1024;
+    static constexpr int kRingBytes = (kLdsBytes - kSBBytes - 2 * kTileRows * 4) / 1024 * 1024;
+    static constexpr int kMaxMT = kS ? 2 : kMT;  // tallest tile
 };
 
 // Ring of stages for a row tile of MT 32-row MFMA tiles, one 64-column group
@@ -88,9 +93,9 @@ struct Geo {
 // activation chunks; every even stage also brings the weights of its group and
 // the next one (64 bytes of each weight row in one request, 2 per stripe), so
 // a pair of slots holds [A | B of two groups] [A].
-template <int kMode, int MT>
+template <int kMode, int MT, bool kS = false>
 struct Ring {
-    using G = Geo<kMode>;
+    using G = Geo<kMode, kS>;
     static constexpr int kABytes = MT * 32 * kStageRowBytes;
     static constexpr int kEven = kABytes + 2 * G::kBStageBytes;
     static constexpr int kPair = kEven + kABytes;
@@ -253,11 +258,11 @@ __device__ __forceinline__ uint32_t ds_read_sb(unsigned addr) {
 }
 
 // One row tile x column slab, MT 32-row MFMA tiles.
-template <typename SB, int kMode, int MT>
+template <typename SB, int kMode, int MT, bool kS>
 __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned char* smem, const int* row_src,
                           const int* row_dst) {
-    using G = Geo<kMode>;
-    using R = Ring<kMode, MT>;
+    using G = Geo<kMode, kS>;
+    using R = Ring<kMode, MT, kS>;
     constexpr int NS = G::NS;
     constexpr int D = R::D;
     constexpr int kWaveCols = G::kWaveCols;
@@ -615,9 +620,10 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     }
 }
 
-template <typename SB, int kMode>
-__global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Geo<kMode>::kRingBytes + Geo<kMode>::kSBBytes];
+template <typename SB, int kMode, bool kS>
+__global__ __launch_bounds__(kThreads, kS ? 2 : 1) void expert_gemm_kernel(GemmArgs p) {
+    using G = Geo<kMode, kS>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G::kRingBytes + G::kSBBytes];
     __shared__ int row_src[kTileRows];
     __shared__ int row_dst[kTileRows];
 
@@ -628,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
     const int slab = local % p.slabs;
     if (tile >= *p.n_tiles) return;
     const Tile tl = p.tiles[tile];
-    const int mt_count = (tl.rows + 31) / 32;
+    const int mt_count = min((tl.rows + 31) / 32, G::kMaxMT);
 
     // row r of the tile: where its activations come from and where its output goes
     // (-1: padding).  Grouped row gp < T*k is slot sorted_slot[gp] of token slot / k;
@@ -666,21 +672,32 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(GemmArgs p) {
     }
     __syncthreads();
 
-    switch (mt_count) {
-        case 1: gemm_tile<SB, kMode, 1>(p, tl, slab, smem, row_src, row_dst); break;
-        case 2: gemm_tile<SB, kMode, 2>(p, tl, slab, smem, row_src, row_dst); break;
-        case 3: gemm_tile<SB, kMode, 3>(p, tl, slab, smem, row_src, row_dst); break;
-        default: gemm_tile<SB, kMode, kMT>(p, tl, slab, smem, row_src, row_dst); break;
+    if constexpr (kS) {
+        if (mt_count == 1)
+            gemm_tile<SB, kMode, 1, kS>(p, tl, slab, smem, row_src, row_dst);
+        else
+            gemm_tile<SB, kMode, 2, kS>(p, tl, slab, smem, row_src, row_dst);
+    } else {
+        switch (mt_count) {
+            case 1: gemm_tile<SB, kMode, 1, kS>(p, tl, slab, smem, row_src, row_dst); break;
+            case 2: gemm_tile<SB, kMode, 2, kS>(p, tl, slab, smem, row_src, row_dst); break;
+            case 3: gemm_tile<SB, kMode, 3, kS>(p, tl, slab, smem, row_src, row_dst); break;
+            default: gemm_tile<SB, kMode, kMT, kS>(p, tl, slab, smem, row_src, row_dst); break;
+        }
     }
 }
 
-template <int kMode>
-hipError_t launch_mode(const GemmArgs& a, bool sb_bf16, int64_t grid, hipStream_t stream) {
+template <int kMode, bool kS>
+hipError_t launch_mode(GemmArgs a, int64_t max_tiles, int cols, bool sb_bf16, hipStream_t stream) {
+    a.slabs = (a.N + Geo<kMode, kS>::kSlabCols - 1) / Geo<kMode, kS>::kSlabCols;
+    const int64_t grid = (max_tiles + 7) / 8 * 8 * a.slabs;
+    (void)cols;
     if (sb_bf16)
-        hipLaunchKernelGGL((expert_gemm_kernel<uint16_t, kMode>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((expert_gemm_kernel<uint16_t, kMode, kS>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            a);
     else
-        hipLaunchKernelGGL((expert_gemm_kernel<float, kMode>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((expert_gemm_kernel<float, kMode, kS>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           a);
     return hipGetLastError();
 }
 
@@ -710,9 +727,8 @@ hipError_t launch_gateup(const GemmProblem& pr, const _Float16* x16, _Float16* h
     a.s0 = pr.shared_w.gate;
     a.s1 = pr.shared_w.up;
     a.h = h;
-    a.slabs = (pr.I + Geo<kGateUp>::kSlabCols - 1) / Geo<kGateUp>::kSlabCols;
-    const int64_t grid = (pr.max_tiles + 7) / 8 * 8 * a.slabs;
-    return launch_mode<kGateUp>(a, pr.sb_bf16, grid, stream);
+    return pr.small_tiles ? launch_mode<kGateUp, true>(a, pr.max_tiles, 0, pr.sb_bf16, stream)
+                          : launch_mode<kGateUp, false>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
 }
 
 hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, float* y_slot, float* y_shared,
@@ -729,11 +745,9 @@ hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, 
     a.y16 = y16;
     a.y_slot = y_slot;
     a.y_shared = y_shared;
-    const int cols = y16 ? Geo<kDownY16>::kSlabCols : Geo<kDownStore>::kSlabCols;
-    a.slabs = (pr.H + cols - 1) / cols;
-    const int64_t grid = (pr.max_tiles + 7) / 8 * 8 * a.slabs;
-    return y16 ? launch_mode<kDownY16>(a, pr.sb_bf16, grid, stream)
-               : launch_mode<kDownStore>(a, pr.sb_bf16, grid, stream);
+    if (!y16) return launch_mode<kDownStore, false>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
+    return pr.small_tiles ? launch_mode<kDownY16, true>(a, pr.max_tiles, 0, pr.sb_bf16, stream)
+                          : launch_mode<kDownY16, false>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
 }
 
 }  // namespace bitmoe

@@ -32,8 +32,17 @@ struct Tile {
 constexpr int kTileRows = 128;  // rows of the grouped products handled by one workgroup
 
 // Upper bound of the number of tiles for T tokens (host side).
+// Tiles of the grouped rows at most: one partial tile per group plus full
+// tiles of tile_rows rows.
+inline int64_t max_tiles(int64_t T, int64_t k, int64_t E, bool shared, int tile_rows) {
+    return (T * k + (shared ? T : 0)) / tile_rows + E + (shared ? 1 : 0) + 1;
+}
+// The layer's tile height: 64 rows when groups average at most 32 rows (small
+// batches; the grouped products then run two workgroups per compute unit),
+// else kTileRows.
+inline bool layer_small_tiles(int64_t T, int64_t k, int64_t E) { return T * k <= 32 * E; }
 inline int64_t max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
-    return (T * k + (shared ? T : 0)) / kTileRows + E + (shared ? 1 : 0) + 1;
+    return max_tiles(T, k, E, shared, kTileRows);
 }
 
 // Tokens (and experts) per workgroup of the layer's logits kernel, and the
@@ -77,7 +86,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E, bool sha
 // beforehand (launch_logits' zero1).
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* hist, int T, int k, int E, bool shared,
                           int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* sorted_slot, Tile* tiles,
-                          int32_t* n_tiles, hipStream_t stream);
+                          int32_t* n_tiles, int tile_rows, hipStream_t stream);
 
 // Tile map only, from caller-provided offsets [E+1].
 hipError_t launch_tiles(const int32_t* offsets, int T, int k, int E, bool shared, Tile* tiles,
@@ -92,6 +101,7 @@ struct GemmProblem {
     int64_t max_tiles;
     const int32_t* sorted_slot;  // [T*k]
     FfnPtr experts, shared_w;
+    bool small_tiles;  // every tile has at most 64 rows: two workgroups per compute unit
 };
 
 // gate/up products with SwiGLU: h [T*k + T][I] float16 in grouped row order,

@@ -82,7 +82,7 @@ Layout layout_of(const moe_dims* d) {
     L.sorted = o;
     o = up256(o + T * k * 4);
     L.tiles = o;
-    o = up256(o + (size_t)max_tiles(d->T, d->top_k, d->E, shared) * sizeof(Tile));
+    o = up256(o + (size_t)max_tiles(d->T, d->top_k, d->E, shared, 64) * sizeof(Tile));  // room for either height
     L.n_tiles = o;
     o = up256(o + 4);
     L.total = o;
@@ -218,6 +218,7 @@ moe_status moe_expert_ffn(const moe_dims* d, const uint16_t* x, const int32_t* o
     p.n_tiles = at<int32_t>(ws, L.n_tiles);
     p.max_tiles = max_tiles(d->T, d->top_k, d->E, use_shared);
     p.sorted_slot = sorted_slot;
+    p.small_tiles = false;  // caller-provided offsets: no bound on rows per expert
     p.experts = to_ptr(experts);
     p.shared_w = use_shared ? to_ptr(shared) : FfnPtr{};
     _Float16* x16 = at<_Float16>(ws, L.x16);
@@ -325,8 +326,12 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     p.sb_bf16 = d->sb_dtype == MOE_BF16;
     p.tiles = at<Tile>(ws, L.tiles);
     p.n_tiles = at<int32_t>(ws, L.n_tiles);
-    p.max_tiles = max_tiles(d->T, d->top_k, d->E, shared);
+    // small batches: 64-row tiles, two workgroups per compute unit
+    const bool small = layer_small_tiles(d->T, d->top_k, d->E);
+    const int tile_rows = small ? 64 : kTileRows;
+    p.max_tiles = max_tiles(d->T, d->top_k, d->E, shared, tile_rows);
     p.sorted_slot = sorted;
+    p.small_tiles = small;
     p.experts = to_ptr(&wts->experts);
     p.shared_w = shared ? to_ptr(&wts->shared) : FfnPtr{};
 
@@ -339,7 +344,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     HIP_TRY(launch_topk(at<float>(ws, L.logits), x, d->T, d->H, d->E, d->top_k, idx, w, hist, x16, stream));
     if (!mark(2)) return MOE_ERR_HIP;
     HIP_TRY(launch_scatter(idx, hist, d->T, d->top_k, d->E, shared, counts, offsets, cursor, sorted,
-                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.n_tiles), stream));
+                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.n_tiles), tile_rows, stream));
     if (!mark(3)) return MOE_ERR_HIP;
     HIP_TRY(launch_gateup(p, x16, h, stream));
     if (!mark(4)) return MOE_ERR_HIP;

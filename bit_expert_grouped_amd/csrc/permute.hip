@@ -48,21 +48,21 @@ __device__ int block_inclusive_scan(int v, int* tmp, int* total = nullptr) {
     return r;
 }
 
-// Tiles of a group of n rows: n / kTileRows full tiles and one tile of the
-// remainder, so at most 31 rows of a group are MFMA padding.  Thread g (< E, or
+// Tiles of a group of n rows: n / tr full tiles of tr (kTileRows or 64) rows
+// and one tile of the remainder, so at most 31 rows of a group are MFMA padding.  Thread g (< E, or
 // == E for the shared expert) writes the tiles of group g.  The map lists the
 // tiles longest first (full tiles, then remainders of 96, 64 and 32 rows or
 // fewer), so the grouped products start the long work first and end on short
 // tiles.  Tiles beyond `cap` (the workspace capacity) are dropped, so
 // inconsistent caller offsets cannot write outside the tile array.
-__device__ void write_tiles(int g_rows, int row_base, int* tmp, Tile* tiles, int32_t* n_tiles, int cap) {
+__device__ void write_tiles(int g_rows, int row_base, int* tmp, Tile* tiles, int32_t* n_tiles, int cap, int tr) {
     const int n = max(g_rows, 0);
-    const int full = n / kTileRows, rem = n % kTileRows;
-    const int mt_rem = (rem + 31) / 32;  // 0 .. kTileRows / 32
+    const int full = n / tr, rem = n % tr;
+    const int mt_rem = (rem + 31) / 32;  // 0 .. tr / 32
     int first_of_class = 0;
-    // classes: kTileRows/32 (full tiles and remainders of that height), then shorter remainders
-    for (int c = kTileRows / 32; c >= 1; c--) {
-        const int cnt = (c == kTileRows / 32 ? full : 0) + (mt_rem == c ? 1 : 0);
+    // classes: tr/32 (full tiles and remainders of that height), then shorter remainders
+    for (int c = tr / 32; c >= 1; c--) {
+        const int cnt = (c == tr / 32 ? full : 0) + (mt_rem == c ? 1 : 0);
         int total;
         const int incl = block_inclusive_scan(cnt, tmp, &total);
         int pos = first_of_class + incl - cnt;
@@ -70,8 +70,8 @@ __device__ void write_tiles(int g_rows, int row_base, int* tmp, Tile* tiles, int
             const bool is_rem = j == cnt - 1 && mt_rem == c;
             Tile t;
             t.group = threadIdx.x;
-            t.row0 = row_base + (is_rem ? full : j) * kTileRows;
-            t.rows = is_rem ? rem : kTileRows;
+            t.row0 = row_base + (is_rem ? full : j) * tr;
+            t.rows = is_rem ? rem : tr;
             t.pad = 0;
             tiles[pos] = t;
         }
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     if (tid == E - 1) offsets[E] = incl;
     const int g_rows = tid < E ? c : ((tid == E && shared) ? T : 0);
     const int row_base = tid < E ? excl : n;
-    write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap);
+    write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap, kTileRows);
     __syncthreads();
     for (int s = tid; s < n; s += kThreads) {
         const int e = topk_idx[s];
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void tiles_kernel(const int32_t* __restri
     } else if (tid == E && shared) {
         g_rows = T;
     }
-    write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap);
+    write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap, kTileRows);
 }
 
 // The layer's permute after topk_kernel has counted the histogram: every
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ cursor,
                                                            int32_t* __restrict__ sorted_slot,
                                                            Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-                                                           int cap) {
+                                                           int cap, int tr) {
     __shared__ int off[kMaxE];
     __shared__ int local[kMaxE];  // this workgroup's slots per expert, then their global base
     __shared__ int tmp[kThreads / kWave];
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
         if (tid == E - 1) offsets[E] = incl;
         const int g_rows = tid < E ? c : ((tid == E && shared) ? T : 0);
         const int row_base = tid < E ? excl : n;
-        write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap);
+        write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap, tr);
     }
     __syncthreads();
     // rank each slot among this workgroup's slots of its expert (LDS atomics),
@@ -194,12 +194,13 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E, bool sha
 
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* hist, int T, int k, int E, bool shared,
                           int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* sorted_slot, Tile* tiles,
-                          int32_t* n_tiles, hipStream_t stream) {
+                          int32_t* n_tiles, int tile_rows, hipStream_t stream) {
+    if (tile_rows != kTileRows && tile_rows != 64) return hipErrorInvalidValue;
     const int n = T * k;
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(scatter_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, topk_idx,
                        hist, T, k, E, shared ? 1 : 0, counts, offsets, cursor, sorted_slot, tiles, n_tiles,
-                       (int)max_tiles(T, k, E, shared));
+                       (int)max_tiles(T, k, E, shared, tile_rows), tile_rows);
     return hipGetLastError();
 }
 
