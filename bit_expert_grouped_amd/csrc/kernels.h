@@ -83,10 +83,12 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E, bool sha
 
 // Scan, tile map and scatter from the padded histogram of launch_topk; also
 // writes counts [E] (nullable).  cursor: padded like the histogram, zeroed
-// beforehand (launch_logits' zero1).
+// beforehand (launch_logits' zero1).  tiles64 (nullable): a second tile map of
+// 64-row tiles over the same groups.
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* hist, int T, int k, int E, bool shared,
                           int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* sorted_slot, Tile* tiles,
-                          int32_t* n_tiles, int tile_rows, hipStream_t stream);
+                          int32_t* n_tiles, int tile_rows, Tile* tiles64, int32_t* n_tiles64,
+                          hipStream_t stream);
 
 // Tile map only, from caller-provided offsets [E+1].
 hipError_t launch_tiles(const int32_t* offsets, int T, int k, int E, bool shared, Tile* tiles,

@@ -39,7 +39,7 @@ moe_status check_dims(const moe_dims* d) {
 struct Layout {
     size_t ctl, xch, sel, hbuf;                          // decode region
     size_t x16, h, y16, logits, hist, cursor;            // prefill buffers
-    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, total;
+    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -84,6 +84,10 @@ Layout layout_of(const moe_dims* d) {
     L.tiles = o;
     o = up256(o + (size_t)max_tiles(d->T, d->top_k, d->E, shared, 64) * sizeof(Tile));  // room for either height
     L.n_tiles = o;
+    o = up256(o + 4);
+    L.tiles64 = o;
+    o = up256(o + (size_t)max_tiles(d->T, d->top_k, d->E, shared, 64) * sizeof(Tile));
+    L.n_tiles64 = o;
     o = up256(o + 4);
     L.total = o;
     return L;
@@ -343,12 +347,23 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     if (!mark(1)) return MOE_ERR_HIP;
     HIP_TRY(launch_topk(at<float>(ws, L.logits), x, d->T, d->H, d->E, d->top_k, idx, w, hist, x16, stream));
     if (!mark(2)) return MOE_ERR_HIP;
+    // large batches: down (short K, so per-tile overheads weigh more) runs on
+    // a second map of 64-row tiles with two workgroups per compute unit
     HIP_TRY(launch_scatter(idx, hist, d->T, d->top_k, d->E, shared, counts, offsets, cursor, sorted,
-                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.n_tiles), tile_rows, stream));
+                           at<Tile>(ws, L.tiles), at<int32_t>(ws, L.n_tiles), tile_rows,
+                           small ? nullptr : at<Tile>(ws, L.tiles64), small ? nullptr : at<int32_t>(ws, L.n_tiles64),
+                           stream));
     if (!mark(3)) return MOE_ERR_HIP;
     HIP_TRY(launch_gateup(p, x16, h, stream));
     if (!mark(4)) return MOE_ERR_HIP;
-    HIP_TRY(launch_down(p, h, y16, nullptr, nullptr, stream));
+    GemmProblem pd = p;
+    if (!small) {
+        pd.tiles = at<Tile>(ws, L.tiles64);
+        pd.n_tiles = at<int32_t>(ws, L.n_tiles64);
+        pd.max_tiles = max_tiles(d->T, d->top_k, d->E, shared, 64);
+        pd.small_tiles = true;
+    }
+    HIP_TRY(launch_down(pd, h, y16, nullptr, nullptr, stream));
     if (!mark(5)) return MOE_ERR_HIP;
     HIP_TRY(launch_combine16(y16, w, shared, d->T, d->H, d->top_k, o, stream));
     if (!mark(6)) return MOE_ERR_HIP;

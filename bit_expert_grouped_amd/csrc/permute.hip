@@ -147,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ cursor,
                                                            int32_t* __restrict__ sorted_slot,
                                                            Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-                                                           int cap, int tr) {
+                                                           int cap, int tr, Tile* __restrict__ tiles2,
+                                                           int32_t* __restrict__ n_tiles2, int cap2) {
     __shared__ int off[kMaxE];
     __shared__ int local[kMaxE];  // this workgroup's slots per expert, then their global base
     __shared__ int tmp[kThreads / kWave];
@@ -168,6 +169,12 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
         const int g_rows = tid < E ? c : ((tid == E && shared) ? T : 0);
         const int row_base = tid < E ? excl : n;
         write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap, tr);
+    }
+    // the second map from workgroup 1 (0 if alone), beside workgroup 0's
+    if (tiles2 && blockIdx.x == (gridDim.x > 1 ? 1u : 0u)) {
+        const int g_rows = tid < E ? c : ((tid == E && shared) ? T : 0);
+        const int row_base = tid < E ? excl : n;
+        write_tiles(g_rows, row_base, tmp, tiles2, n_tiles2, cap2, 64);
     }
     __syncthreads();
     // rank each slot among this workgroup's slots of its expert (LDS atomics),
@@ -194,13 +201,15 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E, bool sha
 
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* hist, int T, int k, int E, bool shared,
                           int32_t* counts, int32_t* offsets, int32_t* cursor, int32_t* sorted_slot, Tile* tiles,
-                          int32_t* n_tiles, int tile_rows, hipStream_t stream) {
+                          int32_t* n_tiles, int tile_rows, Tile* tiles64, int32_t* n_tiles64,
+                          hipStream_t stream) {
     if (tile_rows != kTileRows && tile_rows != 64) return hipErrorInvalidValue;
     const int n = T * k;
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(scatter_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, topk_idx,
                        hist, T, k, E, shared ? 1 : 0, counts, offsets, cursor, sorted_slot, tiles, n_tiles,
-                       (int)max_tiles(T, k, E, shared, tile_rows), tile_rows);
+                       (int)max_tiles(T, k, E, shared, tile_rows), tile_rows, tiles64, n_tiles64,
+                       (int)max_tiles(T, k, E, shared, 64));
     return hipGetLastError();
 }
 
