@@ -53,6 +53,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMT = kTileRows / 32;              // 32-row MFMA tiles per full row tile
 constexpr int kStageRowBytes = kGroup * 2;       // one group of float16 per row
+#ifndef GEMM_GATEUP_LARGE
+#define GEMM_GATEUP_LARGE kWide
+#endif
 #ifndef GEMM_SB_ROW_DWORDS
 #define GEMM_SB_ROW_DWORDS 5
 #endif
@@ -68,24 +71,29 @@ enum Mode { kGateUp = 0, kDownY16 = 1, kDownStore = 2 };
 // (stripe, array), 32 rows x kSBRowDwords dwords (a row's block plus one
 // dword, so that a block starting at a 2-byte offset fits), loaded with dword
 // direct loads.
-// kS (small batches, tiles of at most 64 rows): 2 stripes per wave and at most
-// 80 KB of LDS, so that two workgroups share a compute unit and twice the
-// loads are in flight per unit where the weights stream for few rows.
-template <int kMode, bool kS = false>
+// Variants: kBig (4 waves), kSmall (tiles of at most 64 rows: 2 stripes per
+// wave and at most 80 KB of LDS, so that two workgroups share a compute unit
+// and twice the loads are in flight per unit where the weights stream for few
+// rows), kWide (8 waves of 2 stripes: the same tile and LDS as kBig with two
+// waves per SIMD, so one wave's waits are covered by the other's MFMAs).
+enum Variant { kBig = 0, kSmall = 1, kWide = 2 };
+template <int kMode, int kV = kBig>
 struct Geo {
-    static constexpr int NS = kS || kMode == kDownStore ? 2 : 4;
+    static constexpr int kWavesV = kV == kWide ? 8 : kWaves;
+    static constexpr int kThreadsV = kWavesV * kWave;
+    static constexpr int NS = kV != kBig || kMode == kDownStore ? 2 : 4;
     static constexpr int kWaveCols = kMode == kGateUp ? 32 * NS / 2 : 32 * NS;  // output columns per wave
-    static constexpr int kSlabCols = kWaves * kWaveCols;
-    static constexpr int kBStageBytes = kWaves * NS * kWave * 16;  // each lane's 16 bytes per stripe
+    static constexpr int kSlabCols = kWavesV * kWaveCols;
+    static constexpr int kBStageBytes = kWavesV * NS * kWave * 16;  // each lane's 16 bytes per stripe
     static constexpr int kSBRowDwords = GEMM_SB_ROW_DWORDS;
     static constexpr int kSBArrayDwords = (32 * kSBRowDwords + kWave - 1) / kWave * kWave;
     static constexpr int kSBWaveBytes = NS * 2 * kSBArrayDwords * 4;
-    static constexpr int kSBBytes = kWaves * kSBWaveBytes;
+    static constexpr int kSBBytes = kWavesV * kSBWaveBytes;
     // the ring (and the epilogue tiles): what the 160 KB of LDS leaves beside
     // the scale block and the row tables, in whole KB
-    static constexpr int kLdsBytes = kS ? 80 * 1024 : 160 * 1024;
+    static constexpr int kLdsBytes = kV == kSmall ? 80 * 1024 : 160 * 1024;
     static constexpr int kRingBytes = (kLdsBytes - kSBBytes - 2 * kTileRows * 4) / 1024 * 1024;
-    static constexpr int kMaxMT = kS ? 2 : kMT;  // tallest tile
+    static constexpr int kMaxMT = kV == kSmall ? 2 : kMT;  // tallest tile
 };
 
 // Ring of stages for a row tile of MT 32-row MFMA tiles, one 64-column group
@@ -93,16 +101,21 @@ struct Geo {
 // activation chunks; every even stage also brings the weights of its group and
 // the next one (64 bytes of each weight row in one request, 2 per stripe), so
 // a pair of slots holds [A | B of two groups] [A].
-template <int kMode, int MT, bool kS = false>
+template <int kMode, int MT, int kV = kBig>
 struct Ring {
-    using G = Geo<kMode, kS>;
+    using G = Geo<kMode, kV>;
+    // the 4 MT 1-KB activation loads of a stage, dealt round-robin to the
+    // waves: at most kALoadsMax per wave, at least kALoads (what the counted
+    // waits assume, so a wave with one more only waits longer)
+    static constexpr int kALoadsMax = (4 * MT + G::kWavesV - 1) / G::kWavesV;
+    static constexpr int kALoads = 4 * MT / G::kWavesV;
     static constexpr int kABytes = MT * 32 * kStageRowBytes;
     static constexpr int kEven = kABytes + 2 * G::kBStageBytes;
     static constexpr int kPair = kEven + kABytes;
     static constexpr int DP = G::kRingBytes / kPair > 5 ? 5 : G::kRingBytes / kPair;
     static constexpr int D = 2 * DP;  // slots; stage j goes to slot j % D
-    static constexpr int kLoadsEven = MT + 2 * G::NS;
-    static constexpr int kLoadsOdd = MT;
+    static constexpr int kLoadsEven = kALoads + 2 * G::NS;
+    static constexpr int kLoadsOdd = kALoads;
     static_assert(DP >= 2, "ring too shallow");
     static_assert((D - 2) / 2 * kLoadsEven + (D - 2) / 2 * kLoadsOdd <= 48, "wait_vm covers 48 loads");
     static __device__ __forceinline__ int slot_offset(int slot) { return (slot >> 1) * kPair + (slot & 1) * kEven; }
@@ -258,11 +271,13 @@ __device__ __forceinline__ uint32_t ds_read_sb(unsigned addr) {
 }
 
 // One row tile x column slab, MT 32-row MFMA tiles.
-template <typename SB, int kMode, int MT, bool kS>
+template <typename SB, int kMode, int MT, int kV>
 __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned char* smem, const int* row_src,
                           const int* row_dst) {
-    using G = Geo<kMode, kS>;
-    using R = Ring<kMode, MT, kS>;
+    using G = Geo<kMode, kV>;
+    using R = Ring<kMode, MT, kV>;
+    constexpr int kW = G::kWavesV;
+    constexpr int kNT = G::kThreadsV;
     constexpr int NS = G::NS;
     constexpr int D = R::D;
     constexpr int kWaveCols = G::kWaveCols;
@@ -295,13 +310,16 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
         arr_start[2 * i + 1] = reinterpret_cast<const SB*>(m.b) + grp * n_groups;
     }
 
-    // ---- activation chunk of each of this lane's MT direct loads per stage ----
-    // load i of wave w fills LDS chunks u = (4 i + w) * 64 + lane: row u / 8,
-    // stored position u % 8, which holds the row's chunk (u % 8) ^ (row % 8)
-    const char* a_src[MT];
+    // ---- activation chunk of each of this lane's direct loads per stage ----
+    // load i of wave w is the stage's load j = i kW + w (if j < 4 MT); it fills
+    // LDS chunks u = j * 64 + lane: row u / 8, stored position u % 8, which
+    // holds the row's chunk (u % 8) ^ (row % 8)
+    constexpr int kAL = R::kALoadsMax;
+    const char* a_src[kAL];
 #pragma unroll
-    for (int i = 0; i < MT; i++) {
-        const int u = (i * kWaves + wave) * kWave + lane;
+    for (int i = 0; i < kAL; i++) {
+        const int j = min(i * kW + wave, 4 * MT - 1);
+        const int u = j * kWave + lane;
         const int r = u >> 3, c = (u & 7) ^ (r & 7);
         const int src = row_src[r] >= 0 ? row_src[r] : row_src[0];
         a_src[i] = reinterpret_cast<const char*>(p.a + (size_t)src * p.lda) + c * 16;
@@ -316,14 +334,15 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     const int b_lane = (lane >> 2) * row_bytes + (b_chunk & 1) * 16;
     const int b_grp = b_chunk >> 1;
 
-    // load q of stage kg (q < MT: activations; then 2 per stripe on even stages)
+    // load q of stage kg (q < kAL: activations; then 2 per stripe on even stages)
     auto issue_one = [&](int kg, int slot, int q) {
         unsigned char* base = smem + R::slot_offset(slot);
-        if (q < MT) {
-            __builtin_amdgcn_global_load_lds(a_src[q] + kg * kStageRowBytes, base + (q * kWaves + wave) * kWave * 16,
-                                             16, 0, 0);
-        } else if (q < MT + 2 * NS && (kg & 1) == 0) {
-            const int i = (q - MT) >> 1, h = (q - MT) & 1;
+        if (q < kAL) {
+            const int j = q * kW + wave;
+            if (j < 4 * MT)
+                __builtin_amdgcn_global_load_lds(a_src[q] + kg * kStageRowBytes, base + j * kWave * 16, 16, 0, 0);
+        } else if (q < kAL + 2 * NS && (kg & 1) == 0) {
+            const int i = (q - kAL) >> 1, h = (q - kAL) & 1;
             const int g = min(kg + b_grp, n_groups - 1);
             __builtin_amdgcn_global_load_lds(q_row[i] + 16 * h * row_bytes + b_lane + g * 32,
                                              base + R::kABytes + ((wave * NS + i) * 2 + h) * kWave * 16, 16, 0, 0);
@@ -331,7 +350,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     };
     auto issue = [&](int kg, int slot) {
 #pragma unroll
-        for (int q = 0; q < MT + 2 * NS; q++) issue_one(kg, slot, q);
+        for (int q = 0; q < kAL + 2 * NS; q++) issue_one(kg, slot, q);
     };
 
     // ---- scales and biases of this wave's rows, one block of groups at a time ----
@@ -397,7 +416,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
         int q = 0;
         auto mfma_then_load = [&](const half8_t& a, const half8_t& w, floatx16& c) {
             c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w, c, 0, 0, 0);
-            if (q < MT + 2 * NS && nk >= 0) issue_one(nk, nslot, q);
+            if (q < kAL + 2 * NS && nk >= 0) issue_one(nk, nslot, q);
             q++;
         };
         const unsigned base = lds_addr(smem) + R::slot_offset(slot);
@@ -554,7 +573,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
         __syncthreads();
         constexpr int kChunks = kSlabCols / 8;  // 16-byte chunks per row
         const int col_chunks = min(kChunks, (p.N - slab * kSlabCols) / 8);
-        for (int idx = tid; idx < tl.rows * kChunks; idx += kThreads) {
+        for (int idx = tid; idx < tl.rows * kChunks; idx += kNT) {
             const int r = idx / kChunks, c = idx % kChunks;
             if (c < col_chunks) {
                 const uint4 v = *reinterpret_cast<const uint4*>(ht + r * kSlabCols + c * 8);
@@ -588,7 +607,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
             }
             __syncthreads();
             const int r_lo = 64 * hh, r_hi = min(tl.rows, 64 * hh + 64);
-            for (int idx = tid; idx < (r_hi - r_lo) * kChunks; idx += kThreads) {
+            for (int idx = tid; idx < (r_hi - r_lo) * kChunks; idx += kNT) {
                 const int r = idx / kChunks, c = idx % kChunks;
                 if (c < col_chunks) {
                     const uint4 v = *reinterpret_cast<const uint4*>(yt + r * kSlabCols + c * 8);
@@ -620,9 +639,9 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     }
 }
 
-template <typename SB, int kMode, bool kS>
-__global__ __launch_bounds__(kThreads, kS ? 2 : 1) void expert_gemm_kernel(GemmArgs p) {
-    using G = Geo<kMode, kS>;
+template <typename SB, int kMode, int kV>
+__global__ __launch_bounds__((Geo<kMode, kV>::kThreadsV), (kV == kSmall ? 2 : 1)) void expert_gemm_kernel(GemmArgs p) {
+    using G = Geo<kMode, kV>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[G::kRingBytes + G::kSBBytes];
     __shared__ int row_src[kTileRows];
     __shared__ int row_dst[kTileRows];
@@ -672,32 +691,33 @@ __global__ __launch_bounds__(kThreads, kS ? 2 : 1) void expert_gemm_kernel(GemmA
     }
     __syncthreads();
 
-    if constexpr (kS) {
+    if constexpr (kV == kSmall) {
         if (mt_count == 1)
-            gemm_tile<SB, kMode, 1, kS>(p, tl, slab, smem, row_src, row_dst);
+            gemm_tile<SB, kMode, 1, kV>(p, tl, slab, smem, row_src, row_dst);
         else
-            gemm_tile<SB, kMode, 2, kS>(p, tl, slab, smem, row_src, row_dst);
+            gemm_tile<SB, kMode, 2, kV>(p, tl, slab, smem, row_src, row_dst);
     } else {
         switch (mt_count) {
-            case 1: gemm_tile<SB, kMode, 1, kS>(p, tl, slab, smem, row_src, row_dst); break;
-            case 2: gemm_tile<SB, kMode, 2, kS>(p, tl, slab, smem, row_src, row_dst); break;
-            case 3: gemm_tile<SB, kMode, 3, kS>(p, tl, slab, smem, row_src, row_dst); break;
-            default: gemm_tile<SB, kMode, kMT, kS>(p, tl, slab, smem, row_src, row_dst); break;
+            case 1: gemm_tile<SB, kMode, 1, kV>(p, tl, slab, smem, row_src, row_dst); break;
+            case 2: gemm_tile<SB, kMode, 2, kV>(p, tl, slab, smem, row_src, row_dst); break;
+            case 3: gemm_tile<SB, kMode, 3, kV>(p, tl, slab, smem, row_src, row_dst); break;
+            default: gemm_tile<SB, kMode, kMT, kV>(p, tl, slab, smem, row_src, row_dst); break;
         }
     }
 }
 
-template <int kMode, bool kS>
+template <int kMode, int kV>
 hipError_t launch_mode(GemmArgs a, int64_t max_tiles, int cols, bool sb_bf16, hipStream_t stream) {
-    a.slabs = (a.N + Geo<kMode, kS>::kSlabCols - 1) / Geo<kMode, kS>::kSlabCols;
+    using G = Geo<kMode, kV>;
+    a.slabs = (a.N + G::kSlabCols - 1) / G::kSlabCols;
     const int64_t grid = (max_tiles + 7) / 8 * 8 * a.slabs;
     (void)cols;
     if (sb_bf16)
-        hipLaunchKernelGGL((expert_gemm_kernel<uint16_t, kMode, kS>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                           a);
+        hipLaunchKernelGGL((expert_gemm_kernel<uint16_t, kMode, kV>), dim3((unsigned)grid), dim3(G::kThreadsV), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((expert_gemm_kernel<float, kMode, kS>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                           a);
+        hipLaunchKernelGGL((expert_gemm_kernel<float, kMode, kV>), dim3((unsigned)grid), dim3(G::kThreadsV), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
@@ -727,8 +747,8 @@ hipError_t launch_gateup(const GemmProblem& pr, const _Float16* x16, _Float16* h
     a.s0 = pr.shared_w.gate;
     a.s1 = pr.shared_w.up;
     a.h = h;
-    return pr.small_tiles ? launch_mode<kGateUp, true>(a, pr.max_tiles, 0, pr.sb_bf16, stream)
-                          : launch_mode<kGateUp, false>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
+    return pr.small_tiles ? launch_mode<kGateUp, kSmall>(a, pr.max_tiles, 0, pr.sb_bf16, stream)
+                          : launch_mode<kGateUp, GEMM_GATEUP_LARGE>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
 }
 
 hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, float* y_slot, float* y_shared,
@@ -745,9 +765,9 @@ hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, 
     a.y16 = y16;
     a.y_slot = y_slot;
     a.y_shared = y_shared;
-    if (!y16) return launch_mode<kDownStore, false>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
-    return pr.small_tiles ? launch_mode<kDownY16, true>(a, pr.max_tiles, 0, pr.sb_bf16, stream)
-                          : launch_mode<kDownY16, false>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
+    if (!y16) return launch_mode<kDownStore, kBig>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
+    return pr.small_tiles ? launch_mode<kDownY16, kSmall>(a, pr.max_tiles, 0, pr.sb_bf16, stream)
+                          : launch_mode<kDownY16, kBig>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
 }
 
 }  // namespace bitmoe
