@@ -11,9 +11,9 @@ device memory, so a step does not find the previous steps' weights in the
 one decode step (T=1) of the Qwen3.6-35B-A3B layer shape (H=2048, 256 experts,
 top-8, shared expert, I=512).
 
-Launch: for T <= 64 the K timed steps are captured once into a HIP graph and
-replayed (how a decode loop issues a launch-bound layer); larger T launches
-eagerly.  The timed region carries no instrumentation.  Per-kernel durations
+Launch: the K timed steps are captured once into a HIP graph and replayed
+(how an engine issues a fixed-shape layer step; ``--mode eager`` launches
+them one by one instead).  The timed region carries no instrumentation.  Per-kernel durations
 for the roofline come from an eager, instrumented run of the same K steps
 through ``moe_layer_events`` (HIP events recorded on the launch stream around
 every kernel; events inside a captured graph do not time kernels).
@@ -198,7 +198,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (three times) for counter calibration")
     ap.add_argument("--mode", choices=("eager", "graph"), default=None,
-                    help="graph: replay one HIP graph holding the K timed steps (default for T <= 64); "
+                    help="graph: replay one HIP graph holding the K timed steps (default); "
                          "eager: one foreign call per layer call")
     args = ap.parse_args()
     if args.copy_calibration:
@@ -242,7 +242,7 @@ def main():
     n_calls = steps * layers_per_step
     counts = torch.zeros(n_calls, sh.E, dtype=torch.int32, device=dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_calls)]
-    mode = args.mode or ("graph" if T <= 64 else "eager")
+    mode = args.mode or "graph"
     torch.cuda.synchronize()
 
     # Pre-built argument tuples of the C entry points: the timed loop is one

@@ -366,10 +366,12 @@ def test_workspace_shared_by_prefill_and_decode():
 # ------------------------------------------------------------------ HIP graph capture
 
 
-@pytest.mark.parametrize("T", [1, 37])
+@pytest.mark.parametrize("T", [1, 37, 1100])
 def test_graph_replays_match_eager(T):
     """moe_layer captured in a HIP graph: several replays, with new inputs copied in
-    eagerly between them, each match an eager call on the same inputs."""
+    eagerly between them, each match an eager call on the same inputs (T=1: the
+    decode kernel; 37: 64-row tiles; 1100: 128-row gate/up tiles and the 64-row
+    down map)."""
     cfg, w, x = _custom(3 * T, 2048, 256, 8, 512, 512, True, seed=800 + T)
     m = bem()
     lw = m.upload_weights(w)
