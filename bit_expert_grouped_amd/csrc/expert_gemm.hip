@@ -313,14 +313,16 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     // ---- activation chunk of each of this lane's direct loads per stage ----
     // load i of wave w is the stage's load j = i kW + w (if j < 4 MT); it fills
     // LDS chunks u = j * 64 + lane: row u / 8, stored position u % 8, which
-    // holds the row's chunk (u % 8) ^ (row % 8)
+    // holds the row's chunk (u % 8) ^ ((row / 2) % 8).  A row is 128 bytes (32
+    // banks), so rows two apart start on the same bank; the XOR by row / 2
+    // puts the 16 rows of one LDS read cycle on 16 distinct 16-byte bank groups
     constexpr int kAL = R::kALoadsMax;
     const char* a_src[kAL];
 #pragma unroll
     for (int i = 0; i < kAL; i++) {
         const int j = min(i * kW + wave, 4 * MT - 1);
         const int u = j * kWave + lane;
-        const int r = u >> 3, c = (u & 7) ^ (r & 7);
+        const int r = u >> 3, c = (u & 7) ^ ((r >> 1) & 7);
         const int src = row_src[r] >= 0 ? row_src[r] : row_src[0];
         a_src[i] = reinterpret_cast<const char*>(p.a + (size_t)src * p.lda) + c * 16;
     }
@@ -401,7 +403,7 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
                                (unsigned)(b_row + (((2 + half) ^ ((col >> 2) & 3)) * 16))};
     unsigned a_off[4];
 #pragma unroll
-    for (int s = 0; s < 4; s++) a_off[s] = col * kStageRowBytes + (((4 * half + s) ^ (col & 7)) * 16);
+    for (int s = 0; s < 4; s++) a_off[s] = col * kStageRowBytes + (((4 * half + s) ^ ((col >> 1) & 7)) * 16);
 
     // exponent-trick constants held in VGPRs (v_and_or_b32 takes one scalar)
     uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;
