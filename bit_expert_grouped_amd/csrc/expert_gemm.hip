@@ -9,8 +9,13 @@
 // the single supported 4-bit checkpoint).
 //
 // Design (gfx950):
-//   - A workgroup (4 waves) owns one row tile of one expert group (<= 128 rows,
-//     from the device tile map) and one slab of output columns.  The grid is
+//   - A workgroup owns one row tile of one expert group (<= 128 rows, from
+//     the device tile map) and one slab of output columns.  Three variants:
+//     8 waves of 2 stripes on 128-row tiles (gate/up at large T: two waves
+//     per SIMD cover each other's stalls); 4 waves of 2 stripes on tiles of
+//     at most 64 rows with half the LDS (two workgroups per compute unit: both
+//     products of small batches, and down at large T); 4 waves on 128-row
+//     tiles (the float32 rows of the step-by-step down).  The grid is
 //     sized from T alone; workgroups read the tile count written by the permute
 //     kernel and leave when there is no work.  Workgroups are dispatched
 //     round-robin over the 8 XCDs; tiles are dealt to XCDs the same way in map
@@ -53,12 +58,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMT = kTileRows / 32;              // 32-row MFMA tiles per full row tile
 constexpr int kStageRowBytes = kGroup * 2;       // one group of float16 per row
-#ifndef GEMM_GATEUP_LARGE
-#define GEMM_GATEUP_LARGE kWide
-#endif
-#ifndef GEMM_SB_ROW_DWORDS
-#define GEMM_SB_ROW_DWORDS 5
-#endif
 
 enum Mode { kGateUp = 0, kDownY16 = 1, kDownStore = 2 };
 
@@ -85,7 +84,7 @@ struct Geo {
     static constexpr int kWaveCols = kMode == kGateUp ? 32 * NS / 2 : 32 * NS;  // output columns per wave
     static constexpr int kSlabCols = kWavesV * kWaveCols;
     static constexpr int kBStageBytes = kWavesV * NS * kWave * 16;  // each lane's 16 bytes per stripe
-    static constexpr int kSBRowDwords = GEMM_SB_ROW_DWORDS;
+    static constexpr int kSBRowDwords = 5;  // 8 bf16 (or 4 fp32) groups per block
     static constexpr int kSBArrayDwords = (32 * kSBRowDwords + kWave - 1) / kWave * kWave;
     static constexpr int kSBWaveBytes = NS * 2 * kSBArrayDwords * 4;
     static constexpr int kSBBytes = kWavesV * kSBWaveBytes;
@@ -750,7 +749,7 @@ hipError_t launch_gateup(const GemmProblem& pr, const _Float16* x16, _Float16* h
     a.s1 = pr.shared_w.up;
     a.h = h;
     return pr.small_tiles ? launch_mode<kGateUp, kSmall>(a, pr.max_tiles, 0, pr.sb_bf16, stream)
-                          : launch_mode<kGateUp, GEMM_GATEUP_LARGE>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
+                          : launch_mode<kGateUp, kWide>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
 }
 
 hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, float* y_slot, float* y_shared,
