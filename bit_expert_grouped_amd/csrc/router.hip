@@ -19,8 +19,8 @@
 //   - logits_kernel: one workgroup per (32 tokens, 32 experts); its four waves
 //     split K and sum through LDS; logits go to the workspace;
 //   - topk_kernel: one wave per token sums and ranks its logits, writes the routing,
-//     counts the expert histogram with atomics and writes the float16 copy of
-//     the token's row (8-column blocks in dequantisation order) that the expert
+//     counts the expert histogram (in LDS per 4 or 16 tokens, then one atomic
+//     per expert) and writes the float16 copy of the token's row (8-column blocks in dequantisation order) that the expert
 //     products read.
 #include "common.h"
 #include "kernels.h"
@@ -206,55 +206,67 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict_
     }
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int S,
+// kTW tokens per top-k workgroup: 16 for large batches (fewer atomics on hot
+// experts' counters), 4 for small ones (more workgroups in flight)
+template <int kTW>
+__global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restrict__ logits, int S,
                                                    const uint16_t* __restrict__ x, int T, int H, int E, int top_k,
                                                    int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w, int32_t* __restrict__ hist,
                                                    _Float16* __restrict__ x16) {
+    // the workgroup's expert counts gather in LDS first: one global atomic per
+    // (workgroup, expert), so a hot expert's counter sees at most T / kTW adds
+    __shared__ int lh[kMaxE];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * kWaves4 + wave;
-    if (t >= T) return;  // no workgroup barrier below
-    const float* lt = logits + (size_t)t * E;
-    const size_t split = (size_t)T * E;
-    // this lane's experts lane + 64 i: sum of the S partial logits, in split
-    // order; the loads of 8 splits go out before their adds
-    constexpr int kPer = kMaxE / kWave;
-    float v[kPer];
+    const int t = blockIdx.x * kTW + wave;
+    if (threadIdx.x < kMaxE) lh[threadIdx.x] = 0;
+    __syncthreads();
+    if (t < T) {
+        const float* lt = logits + (size_t)t * E;
+        const size_t split = (size_t)T * E;
+        // this lane's experts lane + 64 i: sum of the S partial logits, in split
+        // order; the loads of 8 splits go out before their adds
+        constexpr int kPer = kMaxE / kWave;
+        float v[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; i++) v[i] = lane + kWave * i < E ? lt[lane + kWave * i] : 0.0f;
-    for (int z0 = 1; z0 < S; z0 += 8) {
-        float p[8][kPer];
+        for (int i = 0; i < kPer; i++) v[i] = lane + kWave * i < E ? lt[lane + kWave * i] : 0.0f;
+        for (int z0 = 1; z0 < S; z0 += 8) {
+            float p[8][kPer];
 #pragma unroll
-        for (int dz = 0; dz < 8; dz++)
+            for (int dz = 0; dz < 8; dz++)
 #pragma unroll
-            for (int i = 0; i < kPer; i++) {
-                const int e = lane + kWave * i;
-                p[dz][i] = (z0 + dz < S && e < E) ? lt[(size_t)(z0 + dz) * split + e] : 0.0f;
+                for (int i = 0; i < kPer; i++) {
+                    const int e = lane + kWave * i;
+                    p[dz][i] = (z0 + dz < S && e < E) ? lt[(size_t)(z0 + dz) * split + e] : 0.0f;
+                }
+#pragma unroll
+            for (int dz = 0; dz < 8; dz++)
+#pragma unroll
+                for (int i = 0; i < kPer; i++) v[i] += p[dz][i];
+        }
+        int ij;
+        float wj;
+        wave_topk([&](int e) { return v[e / kWave]; }, E, top_k, lane, &ij, &wj);
+        if (lane < top_k) {
+            topk_idx[(size_t)t * top_k + lane] = ij;
+            topk_w[(size_t)t * top_k + lane] = wj;
+            if (ij >= 0 && ij < E) atomicAdd(&lh[ij], 1);
+        }
+        if (x16) {
+            const int nblk = H / 8;
+            for (int blk = lane; blk < nblk; blk += kWave) {
+                const uint4 raw = reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk];
+                const uint16_t* hb = reinterpret_cast<const uint16_t*>(&raw);
+                half8_t o;
+#pragma unroll
+                for (int e = 0; e < 8; e++) o[e] = (_Float16)bf16_to_f32(hb[nibble_of(e)]);
+                reinterpret_cast<half8_t*>(x16 + (size_t)t * H)[blk] = o;
             }
-#pragma unroll
-        for (int dz = 0; dz < 8; dz++)
-#pragma unroll
-            for (int i = 0; i < kPer; i++) v[i] += p[dz][i];
-    }
-    int ij;
-    float wj;
-    wave_topk([&](int e) { return v[e / kWave]; }, E, top_k, lane, &ij, &wj);
-    if (lane < top_k) {
-        topk_idx[(size_t)t * top_k + lane] = ij;
-        topk_w[(size_t)t * top_k + lane] = wj;
-        if (hist && ij >= 0 && ij < E) atomicAdd(hist + ij * kCounterStride, 1);
-    }
-    if (x16) {
-        const int nblk = H / 8;
-        for (int blk = lane; blk < nblk; blk += kWave) {
-            const uint4 raw = reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk];
-            const uint16_t* hb = reinterpret_cast<const uint16_t*>(&raw);
-            half8_t o;
-#pragma unroll
-            for (int e = 0; e < 8; e++) o[e] = (_Float16)bf16_to_f32(hb[nibble_of(e)]);
-            reinterpret_cast<half8_t*>(x16 + (size_t)t * H)[blk] = o;
         }
     }
+    __syncthreads();
+    if (hist && threadIdx.x < E && lh[threadIdx.x] > 0)
+        atomicAdd(hist + threadIdx.x * kCounterStride, lh[threadIdx.x]);
 }
 
 }  // namespace
@@ -286,8 +298,13 @@ hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* log
 hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int top_k, int32_t* topk_idx,
                        float* topk_w, int32_t* hist, _Float16* x16, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3((T + kWaves4 - 1) / kWaves4), dim3(256), 0, stream, logits,
-                       logits_splits(T, H, E), x, T, H, E, top_k, topk_idx, topk_w, hist, x16);
+    const int S = logits_splits(T, H, E);
+    if (T >= 1024)
+        hipLaunchKernelGGL(topk_kernel<16>, dim3((T + 15) / 16), dim3(16 * kWave), 0, stream, logits, S, x, T, H, E,
+                           top_k, topk_idx, topk_w, hist, x16);
+    else
+        hipLaunchKernelGGL(topk_kernel<4>, dim3((T + 3) / 4), dim3(4 * kWave), 0, stream, logits, S, x, T, H, E, top_k,
+                           topk_idx, topk_w, hist, x16);
     return hipGetLastError();
 }
 
