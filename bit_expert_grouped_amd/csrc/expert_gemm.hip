@@ -768,7 +768,7 @@ hipError_t launch_down(const GemmProblem& pr, const _Float16* h, _Float16* y16, 
     a.y_shared = y_shared;
     if (!y16) return launch_mode<kDownStore, kBig>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
     return pr.small_tiles ? launch_mode<kDownY16, kSmall>(a, pr.max_tiles, 0, pr.sb_bf16, stream)
-                          : launch_mode<kDownY16, kBig>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
+                          : launch_mode<kDownY16, kWide>(a, pr.max_tiles, 0, pr.sb_bf16, stream);
 }
 
 }  // namespace bitmoe
