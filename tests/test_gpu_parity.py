@@ -227,6 +227,10 @@ def _custom(T, H, E, k, I, Is, bf16=True, seed=77, bias=None):
     (5, 256, 40, 3, 64, True),         # E not a multiple of 32
     (6, 128, 8, 8, 64, True),          # k == E
     (7, 192, 1, 1, 192, False),        # single expert
+    # large-batch path (T*k > 32*E): 8-wave gate/up on 128-row tiles, down on the 64-row map
+    (600, 384, 16, 2, 192, True),      # ragged H and I: partial column slabs in both products
+    (520, 256, 12, 3, 320, False),     # E not a multiple of 32, fp32 scales, I = 256 + 64
+    (1200, 256, 8, 2, 128, True),      # ~300 rows per expert: several 128-row tiles each
 ])
 def test_edge_shapes(T, H, E, k, I, bf16):
     cfg, w, x = _custom(T, H, E, k, I, I, bf16)
