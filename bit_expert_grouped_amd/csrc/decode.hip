@@ -46,9 +46,10 @@
 //     expert workgroups one of kSelReplicas copies of the top k (lanes 0..k-1
 //     of one wave poll them).
 //   - h goes out as float16 pairs, one pair per {epoch, pair} word; a gate/up
-//     workgroup's 16 values are 8 words stored by 8 lanes of one wave.  The
-//     first wave of a down workgroup polls the slot's I/2 words itself (the
-//     poll is the read), sleeping between rounds.
+//     workgroup's 16 values are 8 words stored by 8 lanes of one wave.  Each
+//     wave of a down workgroup polls the words of its own 64-column groups of
+//     the slot's h (the poll is the read), sleeping between rounds, and adds
+//     their part of the rows' dot products as soon as they are in.
 // Waits are bounded: after kSpinLimit polls a workgroup sets the error control
 // word and carries on (that call's output is then invalid).
 //
@@ -182,6 +183,8 @@ struct RoleShared {
             uint4 dsb[2][256];         // scale and bias of those rows (when they fit)
             _Float16 hh[kMaxDecodeI];  // the slot's h, 8-column blocks in nibble order, blocks rotated per group
             float2 hsum[kMaxDecodeI / 8];  // low/high sums of h per 8 columns
+            float part[kWaves][kDRows];    // each wave's part of every row's dot product
+            int wave_ok[kWaves];           // each wave saw its part of h in time
         } down;
         unsigned long long keys[kDecodeMaxT * kMaxE];  // router role: ranking keys [t][e]
     };
@@ -519,61 +522,66 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     const SB* lds_s = reinterpret_cast<const SB*>(sh.down.dsb[0]);
     const SB* lds_b = reinterpret_cast<const SB*>(sh.down.dsb[1]);
 
-    // wait for the slot's h: wave 0 polls the I/2 words {epoch, float16 pair}
-    // until every one carries this call's epoch.  h is kept as float16 in
-    // nibble order; 8-column block m of group g sits at block g * 8 + (m + g) % 8,
-    // so the 8 groups a wave reads at once hit different banks.
+    // every wave's direct loads of rows and scales have landed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // h of the slot, by 64-column groups: wave w takes groups w, w + 4, ...
+    // (32 words {epoch, float16 pair} each), polls their words itself and, as
+    // soon as they carry this call's epoch, adds their part of every row's dot
+    // product, so the arithmetic overlaps the wait for the other groups.  h is
+    // kept as float16 in nibble order; 8-column block m of group g sits at
+    // block g * 8 + (m + g) % 8, so the 8 groups the lanes read at once hit
+    // different banks.
     const unsigned long long* hsrc = p.h64 + (size_t)slot * I / 2;
     _Float16* hh = sh.down.hh;
     auto h_pos = [](int i) {
         const int b = i >> 3, g = b >> 3, m = b & 7;
         return ((g << 3) + ((m + g) & 7)) * 8 + slot_of_column(i & 7);
     };
-    if (wave == 0) {
-        int ok_h = 1;
-        for (long spins = 0;; spins++) {
-            bool have = true;
-            for (int w = lane; w < I / 2; w += kWave) {
-                const unsigned long long v = peek(hsrc + w);
-                if ((unsigned)(v >> 32) == epoch) {
-                    const half2_t pr = as_half2((uint32_t)v);
-                    hh[h_pos(2 * w)] = pr.x;
-                    hh[h_pos(2 * w + 1)] = pr.y;
-                } else {
-                    have = false;
-                }
+    const int gpw = (gd + kWaves - 1) / kWaves;  // groups per wave
+    const int nw = 32 * gpw;                      // words this wave polls
+    int ok_h = 1;
+    for (long spins = 0;; spins++) {
+        bool have = true;
+        for (int idx = lane; idx < nw; idx += kWave) {
+            const int g = wave + kWaves * (idx / 32);
+            if (g >= gd) continue;
+            const int wd = 32 * g + idx % 32;
+            const unsigned long long v = peek(hsrc + wd);
+            if ((unsigned)(v >> 32) == epoch) {
+                const half2_t pr = as_half2((uint32_t)v);
+                hh[h_pos(2 * wd)] = pr.x;
+                hh[h_pos(2 * wd + 1)] = pr.y;
+            } else {
+                have = false;
             }
-            if (__ballot(!have) == 0) break;
-            if (spins > kSpinLimit) {
-                if (lane == 0) flag_error(p.ctl);
-                ok_h = 0;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(4);
         }
-        if (lane == 0) sh.wait_ok = ok_h;
+        if (__ballot(!have) == 0) break;
+        if (spins > kSpinLimit) {
+            if (lane == 0) flag_error(p.ctl);
+            ok_h = 0;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(4);
     }
-    __syncthreads();
-    const bool ok = sh.wait_ok && sh.ok;
-    for (int b8 = tid; b8 < I / 8; b8 += kThreads) {
-        const int g = b8 >> 3, m = b8 & 7;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's h is in LDS
+    for (int idx = lane; idx < 8 * gpw; idx += kWave) {
+        const int g = wave + kWaves * (idx / 8), m = idx % 8;
+        if (g >= gd) continue;
         const _Float16* hv = hh + ((g << 3) + ((m + g) & 7)) * 8;  // 0,4,1,5,2,6,3,7
-        sh.down.hsum[b8] = make_float2((float)hv[0] + (float)hv[1] + (float)hv[4] + (float)hv[5],
-                                       (float)hv[2] + (float)hv[3] + (float)hv[6] + (float)hv[7]);
+        sh.down.hsum[g * 8 + m] = make_float2((float)hv[0] + (float)hv[1] + (float)hv[4] + (float)hv[5],
+                                              (float)hv[2] + (float)hv[3] + (float)hv[6] + (float)hv[7]);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-    // thread (row r, group g): tpr threads per row, rows-per-pass = 256 / tpr
-    int tpr = 1;
-    while (tpr < gd) tpr <<= 1;
-    const int rpp = kThreads / tpr;
-    const int g = tid % tpr, r_in = tid / tpr;
-    float* orow = p.out + (size_t)t * H + n0;
-    for (int r0 = 0; r0 < n_rows; r0 += rpp) {
-        const int r = r0 + r_in;
-        float y = 0.0f;
-        if (g < gd && r < n_rows) {
+    // lane r: this wave's groups of row r
+    const int r = lane;
+    float y = 0.0f;
+    if (r < n_rows) {
+        for (int j = 0; j < gpw; j++) {
+            const int g = wave + kWaves * j;
+            if (g >= gd) break;
             uint4 v0, v1;
             if (rows_in_lds) {
                 v0 = sh.down.drows[r * u_per_row + ((2 * g) ^ (r & swz_mask))];
@@ -594,10 +602,16 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
             }
             const SB sv = sb_in_lds ? lds_s[r * gd + g] : ds[(size_t)r * gd + g];
             const SB bv = sb_in_lds ? lds_b[r * gd + g] : db[(size_t)r * gd + g];
-            y = sb_to_f32<SB>(sv) * ((alo - 1024.0f * lo) + (ahi - 64.0f * hi)) + sb_to_f32<SB>(bv) * (lo + hi);
+            y += sb_to_f32<SB>(sv) * ((alo - 1024.0f * lo) + (ahi - 64.0f * hi)) + sb_to_f32<SB>(bv) * (lo + hi);
         }
-        y = group_sum(y, tpr);
-        if (g == 0 && r < n_rows && ok) atomicAdd(orow + r, wgt * y);
+    }
+    sh.down.part[wave][lane] = y;
+    if (lane == 0) sh.down.wave_ok[wave] = ok_h;
+    __syncthreads();
+    if (wave == 0 && r < n_rows) {
+        const bool ok = sh.ok && sh.down.wave_ok[0] && sh.down.wave_ok[1] && sh.down.wave_ok[2] && sh.down.wave_ok[3];
+        const float yt = (sh.down.part[0][r] + sh.down.part[1][r]) + (sh.down.part[2][r] + sh.down.part[3][r]);
+        if (ok) atomicAdd(p.out + (size_t)t * H + n0 + r, wgt * yt);
     }
 }
 
