@@ -64,93 +64,100 @@ __device__ __forceinline__ half2_t splat_half2(float v) {
     return r;
 }
 
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+// Order-preserving unsigned key of a finite float: a larger float gives a
+// larger key.  -0 is taken as +0 (they compare equal).  Key 0 is below every
+// finite float's key.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// max with the value of the lane that DPP control kCtrl selects (every lane
+// has one for the controls used here; bound_ctrl lets the move fold into the max)
 template <int kCtrl>
-__device__ __forceinline__ void argmax_dpp_step(float& bv, int& bi) {
-    const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), kCtrl, 0xF, 0xF, false));
-    const int oi = __builtin_amdgcn_mov_dpp(bi, kCtrl, 0xF, 0xF, false);
-    if (ranks_before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-    }
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, true));
 }
 
-// Wave-wide arg-max of (value desc, index asc): DPP butterflies inside each row
-// of 16 lanes (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four
-// row winners through readlane.  Every lane receives the winner.
-__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-    argmax_dpp_step<0xB1>(bv, bi);   // quad_perm 1,0,3,2
-    argmax_dpp_step<0x4E>(bv, bi);   // quad_perm 2,3,0,1
-    argmax_dpp_step<0x141>(bv, bi);  // row_half_mirror
-    argmax_dpp_step<0x140>(bv, bi);  // row_mirror
-    float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-    int i = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-    for (int r = 1; r < 4; r++) {
-        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
-        const int ri = __builtin_amdgcn_readlane(bi, 16 * r);
-        if (ranks_before(rv, ri, v, i)) {
-            v = rv;
-            i = ri;
-        }
-    }
-    bv = v;
-    bi = i;
+// Largest v over the wave, as a wave-uniform value: DPP butterflies inside each
+// row of 16 lanes, then the four row results through readlane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max_dpp<0xB1>(v);   // quad_perm 1,0,3,2
+    v = max_dpp<0x4E>(v);   // quad_perm 2,3,0,1
+    v = max_dpp<0x141>(v);  // row_half_mirror
+    v = max_dpp<0x140>(v);  // row_mirror
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
 }
 
-// Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max on
-// (logit desc, expert index asc), then the softmax of the kept logits (equal to
-// the softmax over all E renormalised over the kept ones).  `logit(e)` returns
-// the logit of expert e < E.  Lane j < k receives rank j: idx_j and w_j.
-template <typename LogitFn>
-__device__ __forceinline__ void wave_topk(LogitFn logit, int E, int top_k, int lane, int* idx_j, float* w_j) {
-    float v[kMaxE / kWave];
-    int id[kMaxE / kWave];
+// Top-k of one token's logits held by one wave: lane l holds the logits of
+// experts l, l + 64, l + 128, l + 192 in held[0..3] (entries of experts >= E are
+// ignored).  Rank order is (logit desc, expert index asc).  Each of the k
+// rounds takes the wave-wide largest order key; the ballots of key == max, in
+// held order then lane order, give the lowest expert index holding it, whose
+// key is then cleared.  Then the softmax of the kept logits (equal to the
+// softmax over all E renormalised over the kept ones), summed in rank order.
+// Lane j < k receives rank j: idx_j and w_j.
+__device__ __forceinline__ void wave_topk_held(const float (&held)[kMaxE / kWave], int E, int top_k, int lane,
+                                               int* idx_j, float* w_j) {
+    constexpr int kPer = kMaxE / kWave;
+    uint32_t key[kPer];
 #pragma unroll
-    for (int i = 0; i < kMaxE / kWave; i++) {
-        id[i] = lane + kWave * i;
-        v[i] = id[i] < E ? logit(id[i]) : -INFINITY;
-        if (id[i] >= E) id[i] = 0x7fffffff;
-    }
-    float kept_v[kMaxTopK];
-    int kept_i[kMaxTopK];
+    for (int i = 0; i < kPer; i++) key[i] = lane + kWave * i < E ? order_key(held[i]) : 0u;
+    uint32_t kept_key = 0;  // lane j: key of rank j
+    int kept_idx = 0;       // lane j: expert of rank j
 #pragma unroll
     for (int j = 0; j < kMaxTopK; j++) {
         if (j >= top_k) break;
-        float bv = v[0];
-        int bi = id[0];
+        uint32_t lm = key[0];
 #pragma unroll
-        for (int i = 1; i < kMaxE / kWave; i++) {
-            if (ranks_before(v[i], id[i], bv, bi)) {
-                bv = v[i];
-                bi = id[i];
+        for (int i = 1; i < kPer; i++) lm = max(lm, key[i]);
+        const uint32_t m = wave_max_u32(lm);
+        int win_i = kPer - 1;
+        uint64_t win_mask = 0;
+#pragma unroll
+        for (int i = kPer - 1; i >= 0; i--) {
+            const uint64_t b = __ballot(key[i] == m);
+            if (b) {
+                win_i = i;
+                win_mask = b;
             }
         }
-        wave_argmax(bv, bi);
-        kept_v[j] = bv;
-        kept_i[j] = bi;
+        const int win_lane = (int)__builtin_ctzll(win_mask);
 #pragma unroll
-        for (int i = 0; i < kMaxE / kWave; i++) {
-            if (id[i] == bi) v[i] = -INFINITY, id[i] = 0x7fffffff;
+        for (int i = 0; i < kPer; i++)
+            if (i == win_i && lane == win_lane) key[i] = 0u;
+        if (lane == j) {
+            kept_key = m;
+            kept_idx = win_lane + kWave * win_i;
         }
     }
-    float z = 0.0f, wj = 0.0f;
-    int ij = 0;
+    const float top = key_float(__builtin_amdgcn_readlane(kept_key, 0));
+    const float p = expf(key_float(kept_key) - top);
+    float z = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; j++) {
         if (j >= top_k) break;
-        const float p = expf(kept_v[j] - kept_v[0]);
-        z += p;
-        if (j == lane) {
-            wj = p;
-            ij = kept_i[j];
-        }
+        z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j));
     }
-    *idx_j = ij;
-    *w_j = wj / z;
+    *idx_j = lane < top_k ? kept_idx : 0;
+    *w_j = lane < top_k ? p / z : 0.0f;
+}
+
+// The same for logits read through `logit(e)` (expert e < E).
+template <typename LogitFn>
+__device__ __forceinline__ void wave_topk(LogitFn logit, int E, int top_k, int lane, int* idx_j, float* w_j) {
+    float held[kMaxE / kWave];
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; i++) {
+        const int e = lane + kWave * i;
+        held[i] = e < E ? logit(e) : -INFINITY;
+    }
+    wave_topk_held(held, E, top_k, lane, idx_j, w_j);
 }
 
 }  // namespace bitmoe

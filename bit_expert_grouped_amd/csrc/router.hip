@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
         }
         int ij;
         float wj;
-        wave_topk([&](int e) { return v[e / kWave]; }, E, top_k, lane, &ij, &wj);
+        wave_topk_held(v, E, top_k, lane, &ij, &wj);
         if (lane < top_k) {
             topk_idx[(size_t)t * top_k + lane] = ij;
             topk_w[(size_t)t * top_k + lane] = wj;
