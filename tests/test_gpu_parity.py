@@ -241,6 +241,52 @@ def test_edge_shapes(T, H, E, k, I, bf16):
     assert_close(out, ref["out"], "edge T%d H%d E%d k%d I%d" % (T, H, E, k, I))
 
 
+def _tied(T, H, E, k, I, seed=91, tau=1e-4):
+    """Router rows repeated in threes (experts 3i, 3i+1, 3i+2 share a row), so
+    every logit is exactly equal to its group's on both sides; with k = 8 the
+    k-th boundary splits a group and only the tie rule (the lower expert index
+    ranks first) decides which members are kept.  Tokens whose distinct top
+    logits come closer than tau (where rounding order could reorder the groups)
+    are left out."""
+    cfg = moe_synth.Config("tied", moe_synth.Shape(T=T, H=H, E=E, top_k=k, I=I, I_shared=I, sb_bf16=True),
+                           seed=seed)
+    w = moe_synth.layer_weights(cfg)
+    R = w["router"].copy()
+    for e in range(0, E - 2, 3):
+        R[e + 1] = R[e]
+        R[e + 2] = R[e]
+    w["router"] = R
+    x = moe_synth.token_rows(cfg, 4 * T)
+    lg = oracle.router_logits(x, R)
+    keep = []
+    for t in range(x.shape[0]):
+        top = np.unique(lg[t])[::-1][: k + 2]
+        if np.min(top[:-1] - top[1:]) >= tau:
+            keep.append(t)
+    assert len(keep) >= T
+    return w, x[np.array(keep[:T])]
+
+
+@pytest.mark.parametrize("T,H,E", [(3, 256, 48), (64, 256, 48), (1, 2048, 256), (600, 2048, 256)])
+def test_exact_logit_ties_go_to_the_lower_index(T, H, E):
+    k = 8
+    w, x = _tied(T, H, E, k, 64)
+    ref = oracle.moe_layer(w, x, k)
+    # the boundary group is split in every token: the rule is exercised
+    for t in range(T):
+        kept = set(ref["idx"][t].tolist())
+        groups = {e // 3 for e in kept}
+        assert any(sum((g * 3 + j) in kept for j in range(3)) not in (0, 3) for g in groups if g * 3 + 2 < E)
+    out, idx, wt, counts = run_layer(w, x, k)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out, ref["out"], "tied logits T%d" % T)
+    m = bem()
+    ridx, rw = m.moe_route(m.bf16_tensor(x), m.bf16_tensor(w["router"]), k)
+    torch.cuda.synchronize()
+    assert_same_routing(ridx.cpu().numpy(), rw.cpu().numpy(), ref["idx"], ref["w"])
+
+
 def test_hot_expert_spans_many_tiles():
     bias = np.zeros(32, dtype=np.float32)
     bias[5] = 50.0
