@@ -79,8 +79,10 @@ constexpr long kSpinLimit = 1l << 20;
 // control words (uint32 indices into the workspace control block); words that
 // many workgroups touch sit on lines of their own
 constexpr int kCtlEpoch = 0;      // epoch of the last completed call
-constexpr int kCtlDone = 64;      // workgroups finished in this call
+constexpr int kCtlDone = 64;      // groups of workgroups finished in this call
 constexpr int kCtlError = 255;    // nonzero: a wait timed out
+constexpr int kCtlGroupDone = 512;  // + 32 g: workgroups of group g (blockIdx % 8 == g) finished
+constexpr int kDoneGroups = 8;
 
 // float16 pairs of 8 activations in the order the exponent trick produces codes
 struct Pairs8 {
@@ -638,17 +640,32 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
         else
             down_role<SB, false>(p, slot, blk, epoch, sh);
     }
-    // the last workgroup to finish resets the done counter and advances the
+    // the last workgroup to finish resets the done counters and advances the
     // epoch for the next call.  Its own stores and atomics need not have
     // landed: the next call starts after this kernel has ended, and every
     // workgroup read the epoch when it started, before it counted itself done.
+    // The count has two levels: workgroup b counts itself in group b % 8 (a
+    // counter on a line of its own), and the last of a group counts the group.
+    // The hundreds of down workgroups finish within a microsecond or two, and
+    // one counter for all of them serializes their atomics at the end of the
+    // kernel.
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned old = __hip_atomic_fetch_add(p.ctl + kCtlDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sh.last = old == gridDim.x - 1;
+        const unsigned g = blockIdx.x % kDoneGroups;
+        const unsigned members = (gridDim.x - g + kDoneGroups - 1) / kDoneGroups;
+        const unsigned groups = min(gridDim.x, (unsigned)kDoneGroups);
+        bool last = false;
+        const unsigned old = __hip_atomic_fetch_add(p.ctl + kCtlGroupDone + 32 * g, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (old == members - 1)
+            last = __hip_atomic_fetch_add(p.ctl + kCtlDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   groups - 1;
+        sh.last = last;
     }
     __syncthreads();
     if (sh.last && threadIdx.x == 0) {
+        for (int g = 0; g < kDoneGroups; g++)
+            __hip_atomic_store(p.ctl + kCtlGroupDone + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(p.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(p.ctl + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

@@ -379,6 +379,13 @@ def control_words(ws):
     return int(words[0]), int(words[255])
 
 
+def done_counters(ws):
+    """The decode kernel's completion counters (uint32 word 64: finished groups; word
+    512 + 32 g: finished workgroups of group g), all back to zero after a call."""
+    words = ws[:4096].view(torch.int32).cpu().numpy()
+    return [int(words[64])] + [int(words[512 + 32 * g]) for g in range(8)]
+
+
 def test_decode_repeated_calls_and_control_words():
     """Successive decode calls on one workspace each match the oracle; the call
     counter advances by one per call and no wait times out."""
@@ -393,6 +400,7 @@ def test_decode_repeated_calls_and_control_words():
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ref["out"], "decode call %d" % t)
         assert control_words(ws) == (t + 1, 0)
+        assert done_counters(ws) == [0] * 9
 
 
 def test_workspace_shared_by_prefill_and_decode():
