@@ -620,7 +620,11 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
 template <typename SB>
 __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
     __shared__ RoleShared sh;
-    unsigned epoch = __hip_atomic_load(p.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    // a plain load: the word was stored by the previous call (visible once that
+    // kernel has ended) and changes only after every workgroup of this call has
+    // read it, so each XCD's L2 can serve it instead of every workgroup going to
+    // memory for the same word
+    unsigned epoch = p.ctl[kCtlEpoch] + 1;
     if (epoch == 0) epoch = 1;  // words of a zero-filled workspace carry epoch 0
     const int b = blockIdx.x;
     if (b < p.router_wgs) {
