@@ -47,6 +47,7 @@ KIND_GATE_Q, KIND_GATE_S, KIND_GATE_B = 2, 3, 4
 KIND_UP_Q, KIND_UP_S, KIND_UP_B = 5, 6, 7
 KIND_DOWN_Q, KIND_DOWN_S, KIND_DOWN_B = 8, 9, 10
 KIND_ZIPF_RANK = 11
+KIND_SHARED_EXPERT_GATE = 12
 KIND_X = 100
 SHARED_EXPERT = 1 << 20  # expert slot used in seed sequences for the shared expert
 
@@ -157,6 +158,15 @@ def router_weights(cfg: Config, layer: int = 0) -> np.ndarray:
     """Router matrix [E][H] as bf16 bits."""
     sh = cfg.shape
     return _normal(_rng(cfg.seed, layer, KIND_ROUTER, 0), ROUTER_STD, (sh.E, sh.H))
+
+
+def shared_expert_gate(cfg: Config, layer: int = 0) -> np.ndarray:
+    """Gate vector [H] of the shared expert as bf16 bits, drawn like a router row.
+
+    An optional checkpoint detail the configs do not use; the tests of the
+    gated shared expert add it to a layer's weights under "shared_expert_gate".
+    """
+    return _normal(_rng(cfg.seed, layer, KIND_SHARED_EXPERT_GATE, 0), ROUTER_STD, (cfg.shape.H,))
 
 
 def layer_weights(cfg: Config, layer: int = 0) -> dict:

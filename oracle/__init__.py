@@ -45,7 +45,7 @@ class Layer(C.Structure):
                     "x", "router", "logit_bias",
                     "gate_q", "up_q", "down_q", "gate_s", "gate_b", "up_s", "up_b", "down_s", "down_b",
                     "sh_gate_q", "sh_up_q", "sh_down_q", "sh_gate_s", "sh_gate_b", "sh_up_s", "sh_up_b",
-                    "sh_down_s", "sh_down_b")])
+                    "sh_down_s", "sh_down_b", "sh_expert_gate")])
 
 
 def lib():
@@ -68,7 +68,9 @@ def lib():
         L.oracle_permute.restype = None
         L.oracle_expert_ffn.argtypes = [C.POINTER(QMat)] * 3 + [i32, P, P, P, P]
         L.oracle_expert_ffn.restype = None
-        L.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P]
+        L.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P, P]
+        L.oracle_shared_gate.argtypes = [i32, i32, P, P, P]
+        L.oracle_shared_gate.restype = None
         L.oracle_combine.restype = None
         L.oracle_moe_layer.argtypes = [C.POINTER(Layer), i32, P, P, P, P, P, P, P, P]
         L.oracle_moe_layer.restype = C.c_int
@@ -162,14 +164,24 @@ def expert_ffn(gate, up, down, x_rows, group=64, want_gu=False):
     return (y, g, u) if want_gu else y
 
 
-def combine(y_slot, w, y_shared=None):
-    """y_slot [n][k][H], w [n][k], y_shared [n][H] or None."""
+def combine(y_slot, w, y_shared=None, shared_w=None):
+    """y_slot [n][k][H], w [n][k], y_shared [n][H] or None, shared_w [n] or None (weight 1)."""
     y_slot = _c(y_slot, np.float64)
     w = _c(w, np.float64)
     ys = _c(y_shared, np.float64)
+    sw = _c(shared_w, np.float64)
     n, k, H = y_slot.shape
     out = np.empty((n, H), dtype=np.float64)
-    lib().oracle_combine(n, k, H, y_slot.ctypes.data, w.ctypes.data, _ptr(ys), out.ctypes.data)
+    lib().oracle_combine(n, k, H, y_slot.ctypes.data, w.ctypes.data, _ptr(ys), _ptr(sw), out.ctypes.data)
+    return out
+
+
+def shared_gate(x, gate):
+    """Weight of the shared expert per token: sigmoid(x[t] . gate), x [T][H] and gate [H] bf16 bits."""
+    x = _c(x, np.uint16)
+    g = _c(gate, np.uint16)
+    out = np.empty(x.shape[0], dtype=np.float64)
+    lib().oracle_shared_gate(x.shape[0], x.shape[1], x.ctypes.data, g.ctypes.data, out.ctypes.data)
     return out
 
 
@@ -219,6 +231,8 @@ def moe_layer(weights: dict, x, top_k: int, group: int = 64, tokens=None, want_l
             setattr(L, "sh_" + name, arr("shared_" + name, sbd).ctypes.data)
     else:
         L.I_shared = 0
+    seg = arr("shared_expert_gate", np.uint16)
+    L.sh_expert_gate = _ptr(seg)
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
     n = T if tok is None else len(tok)
     out = np.empty((n, H), dtype=np.float64)

@@ -4,11 +4,12 @@ TEST INFRASTRUCTURE ONLY.  A second, independent statement of what the layer
 computes, used to check the C oracle: it evaluates EVERY expert on EVERY token
 and masks the results with the top-k selection,
 
-    y[t] = sum_e M[t,e] * r[t,e] * F_e(x_t) + F_shared(x_t),
+    y[t] = sum_e M[t,e] * r[t,e] * F_e(x_t) + s_t * F_shared(x_t),
 
 where M is the top-k mask from a full stable sort of the float32-rounded
 router logits (larger first, lower index first on equal values) and r is the
-softmax over all experts renormalised over the mask.  It shares no code with
+softmax over all experts renormalised over the mask; s_t = sigmoid(x_t . g) with
+an optional shared-expert gate vector g, else 1.  It shares no code with
 ``moe_oracle.c``: nibbles are unpacked with numpy shifts, products are numpy
 matrix multiplications, selection is a lexicographic sort.
 
@@ -77,7 +78,13 @@ def layer(weights: dict, x_bits, top_k: int, group: int = 64):
                  dense_matrix(weights["down_q"][e], weights["down_s"][e], weights["down_b"][e], group), X)
         y += r[:, e:e + 1] * Fe
     if weights.get("shared_gate_q") is not None:
-        y += ffn(dense_matrix(weights["shared_gate_q"][0], weights["shared_gate_s"][0], weights["shared_gate_b"][0], group),
+        # optional shared-expert gate (a checkpoint detail the pages do not
+        # mention): the shared output is scaled by sigmoid(x . g)
+        sw = np.ones((X.shape[0], 1))
+        if weights.get("shared_expert_gate") is not None:
+            z = X @ _bf16(weights["shared_expert_gate"])
+            sw = (1.0 / (1.0 + np.exp(-z)))[:, None]
+        y += sw * ffn(dense_matrix(weights["shared_gate_q"][0], weights["shared_gate_s"][0], weights["shared_gate_b"][0], group),
                  dense_matrix(weights["shared_up_q"][0], weights["shared_up_s"][0], weights["shared_up_b"][0], group),
                  dense_matrix(weights["shared_down_q"][0], weights["shared_down_s"][0], weights["shared_down_b"][0], group), X)
     return dict(out=y, mask=M, r=r, logits=logits)

@@ -37,6 +37,10 @@
  *      groups are 64 consecutive input columns of one output row;
  *      dequantised value = scale * code + bias;
  *   R7 combine: out[t] = sum_j w[t][j] * y[t][j] + y_shared[t].
+ *   R14 (checkpoint conformity, not on the pages) an optional gate on the
+ *      shared expert: a bfloat16 vector g [H] scales the shared expert's
+ *      output by sigmoid(sum_h x[t][h] * g[h]); without g the weight is one (R5).
+ *      This is the shared-expert gate of Qwen's mixture-of-experts checkpoints.
  */
 #include <math.h>
 #include <stdint.h>
@@ -63,6 +67,7 @@ typedef struct {
     /* shared expert (single); gate_q == NULL means no shared expert */
     const uint32_t *sh_gate_q, *sh_up_q, *sh_down_q;
     const void *sh_gate_s, *sh_gate_b, *sh_up_s, *sh_up_b, *sh_down_s, *sh_down_b;
+    const uint16_t *sh_expert_gate; /* [H] bfloat16 bits, or NULL: shared weight 1 (R14) */
 } oracle_layer;
 
 static double bf16_bits_value(uint16_t bits)
@@ -231,9 +236,21 @@ void oracle_expert_ffn(const oracle_qmat *gate, const oracle_qmat *up, const ora
     free(Wg);
 }
 
-/* out[t] = sum_j w[t][j] * y_slot[t][j] + y_shared[t]  (R5, R7), j in slot order. */
+/* Weight of the shared expert for each of T tokens: s[t] = sigmoid(sum_h x[t][h] * g[h])  (R14). */
+void oracle_shared_gate(int32_t T, int32_t H, const uint16_t *x, const uint16_t *g, double *s)
+{
+    for (int32_t t = 0; t < T; t++) {
+        double z = 0.0;
+        for (int32_t h = 0; h < H; h++)
+            z += bf16_bits_value(x[(size_t)t * H + h]) * bf16_bits_value(g[h]);
+        s[t] = 1.0 / (1.0 + exp(-z));
+    }
+}
+
+/* out[t] = sum_j w[t][j] * y_slot[t][j] + s[t] * y_shared[t]  (R5, R7, R14), j in slot
+   order; s[t] = shared_w[t], or 1 when shared_w is NULL. */
 void oracle_combine(int32_t n, int32_t k, int32_t H, const double *y_slot, const double *w,
-                    const double *y_shared, double *out)
+                    const double *y_shared, const double *shared_w, double *out)
 {
     for (int32_t t = 0; t < n; t++) {
         for (int32_t h = 0; h < H; h++) {
@@ -241,7 +258,7 @@ void oracle_combine(int32_t n, int32_t k, int32_t H, const double *y_slot, const
             for (int32_t j = 0; j < k; j++)
                 acc += w[(size_t)t * k + j] * y_slot[((size_t)t * k + j) * H + h];
             if (y_shared)
-                acc += y_shared[(size_t)t * H + h];
+                acc += (shared_w ? shared_w[t] : 1.0) * y_shared[(size_t)t * H + h];
             out[(size_t)t * H + h] = acc;
         }
     }
@@ -288,7 +305,9 @@ int oracle_moe_layer(const oracle_layer *L, int32_t n_tok, const int32_t *tok, d
     const uint16_t **rows = (const uint16_t **)malloc(sizeof(uint16_t *) * ((size_t)nt * k + 1));
     int32_t *rdst = (int32_t *)malloc(sizeof(int32_t) * ((size_t)nt * k + 1));
     double *ybuf = (double *)malloc(sizeof(double) * ((size_t)nt * k + 1) * H);
-    if (!lg || !ss || !pos || !y_slot || (L->sh_gate_q && !y_sh) || !w_sub || !rows || !rdst || !ybuf)
+    double *s_sh = L->sh_expert_gate ? (double *)malloc(sizeof(double) * ((size_t)nt + 1)) : NULL;
+    if (!lg || !ss || !pos || !y_slot || (L->sh_gate_q && !y_sh) || !w_sub || !rows || !rdst || !ybuf ||
+        (L->sh_expert_gate && !s_sh))
         return -1;
 
     oracle_router_logits(T, H, E, L->x, L->router, L->logit_bias, lg);
@@ -333,7 +352,12 @@ int oracle_moe_layer(const oracle_layer *L, int32_t n_tok, const int32_t *tok, d
         for (int32_t j = 0; j < k; j++)
             w_sub[(size_t)i * k + j] = w[(size_t)t * k + j];
     }
-    oracle_combine(nt, k, H, y_slot, w_sub, y_sh, out);
+    if (s_sh)
+        for (int32_t i = 0; i < nt; i++)
+            oracle_shared_gate(1, H, L->x + (size_t)(tok ? tok[i] : i) * H, L->sh_expert_gate, s_sh + i);
+    oracle_combine(nt, k, H, y_slot, w_sub, y_sh, s_sh, out);
+
+    free(s_sh);
 
     free(ybuf);
     free(rdst);

@@ -287,6 +287,47 @@ def test_logit_bias_enters_selection_and_softmax():
     assert np.abs(res["out"] - bf["out"]).max() <= 1e-9 * _rms(bf["out"])
 
 
+# ---------------------------------------------------------------- optional shared-expert gate (R14)
+
+
+def _bf16_bits(vals):
+    return (np.asarray(vals, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("ex", _load("shared_gate_examples.json")["examples"], ids=str)
+def test_shared_gate_hand_examples(ex):
+    x = _bf16_bits(ex["x"])[None, :]
+    g = _bf16_bits(ex["g"])
+    np.testing.assert_allclose(oracle.shared_gate(x, g), [ex["s"]], rtol=1e-15, atol=0)
+
+
+def test_zero_shared_gate_halves_the_shared_expert():
+    cfg = small_cfg(T=5, E=6, k=2)
+    w = moe_synth.layer_weights(cfg)
+    x = moe_synth.token_rows(cfg)
+    full = oracle.moe_layer(w, x, 2)["out"]
+    w_s0 = dict(w)
+    _zero_sb(w_s0, "shared_")
+    routed_only = oracle.moe_layer(w_s0, x, 2)["out"]
+    wg = dict(w)
+    wg["shared_expert_gate"] = np.zeros(cfg.shape.H, dtype=np.uint16)  # sigmoid(0) = 1/2 exactly
+    gated = oracle.moe_layer(wg, x, 2)["out"]
+    np.testing.assert_allclose(gated, (full + routed_only) / 2, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_shared_gate_against_brute_force(seed):
+    cfg = small_cfg(T=7, H=192, E=5, k=2, I=64, Is=128, bf16=bool(seed % 2), seed=seed)
+    w = moe_synth.layer_weights(cfg)
+    w["shared_expert_gate"] = moe_synth.shared_expert_gate(cfg)
+    x = moe_synth.token_rows(cfg)
+    res = oracle.moe_layer(w, x, 2)
+    bf = brute.layer(w, x, 2)
+    assert np.abs(res["out"] - bf["out"]).max() <= 1e-9 * _rms(bf["out"])
+    s = oracle.shared_gate(x, w["shared_expert_gate"])
+    assert 0.1 < s.min() and s.max() < 0.9 and s.std() > 0.01  # the gate does vary across tokens
+
+
 # ---------------------------------------------------------------- invariances
 
 

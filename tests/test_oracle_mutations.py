@@ -32,8 +32,10 @@ MUTATIONS = {
     "gate and up swapped": ("a[i] = silu(g) * u;", "a[i] = silu(u) * g;"),
     "down operand transposed": ("acc += Wd[(size_t)o * I + i] * a[i];", "acc += Wd[((size_t)i * H + o) % ((size_t)H * I)] * a[i];"),
     "routing weight ignored": ("acc += w[(size_t)t * k + j] * y_slot", "acc += 1.0 * y_slot"),
-    "shared expert dropped": ("acc += y_shared[(size_t)t * H + h];", "acc += 0.0 * y_shared[(size_t)t * H + h];"),
+    "shared expert dropped": ("* y_shared[(size_t)t * H + h];", "* 0.0 * y_shared[(size_t)t * H + h];"),
     "router row index wrong": ("bf16_bits_value(router[(size_t)e * H + h])", "bf16_bits_value(router[(size_t)((e + 1) % E) * H + h])"),
+    "shared gate sign flipped": ("s[t] = 1.0 / (1.0 + exp(-z));", "s[t] = 1.0 / (1.0 + exp(z));"),
+    "shared gate ignored": ("(shared_w ? shared_w[t] : 1.0)", "(shared_w ? 1.0 : 1.0)"),
     "permute not stable": ("sorted_slot[cursor[idx[s]]++] = s;", "sorted_slot[offsets[idx[s] + 1] - 1 - (cursor[idx[s]]++ - offsets[idx[s]])] = s;"),
 }
 
