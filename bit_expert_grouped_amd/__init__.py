@@ -20,8 +20,9 @@ LIB_PATH = os.path.join(HERE, "libbitmoe.so")
 MOE_BF16, MOE_F32 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
-           "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name", "moe_status_string")
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_shared_gate",
+           "moe_combine_gated", "moe_layer", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
+           "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -44,7 +45,8 @@ class Ffn(C.Structure):
 
 
 class Weights(C.Structure):
-    _fields_ = [("router", C.c_void_p), ("logit_bias", C.c_void_p), ("experts", Ffn), ("shared", Ffn)]
+    _fields_ = [("router", C.c_void_p), ("logit_bias", C.c_void_p), ("experts", Ffn), ("shared", Ffn),
+                ("shared_expert_gate", C.c_void_p)]
 
 
 _lib = None
@@ -66,13 +68,16 @@ def lib():
         L.moe_permute.argtypes = [D, P, P, P, P, P, C.c_size_t, P]
         L.moe_expert_ffn.argtypes = [D, P, P, P, C.POINTER(Ffn), C.POINTER(Ffn), P, P, P, C.c_size_t, P]
         L.moe_combine.argtypes = [D, P, P, P, P, P]
+        L.moe_combine_gated.argtypes = [D, P, P, P, P, P, P]
+        L.moe_shared_gate.argtypes = [D, P, P, P, P]
         L.moe_layer.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P]
         L.moe_layer_events.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P, P, C.c_int32]
         L.moe_layer_stage_count.argtypes = [D]
         L.moe_layer_stage_count.restype = C.c_int32
         L.moe_layer_stage_name.argtypes = [D, C.c_int32]
         L.moe_layer_stage_name.restype = C.c_char_p
-        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer", "moe_layer_events"):
+        for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_combine_gated",
+                     "moe_shared_gate", "moe_layer", "moe_layer_events"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -139,7 +144,8 @@ class LayerWeights:
         self.experts = Ffn(qm("", "gate"), qm("", "up"), qm("", "down"))
         self.shared = (Ffn(qm("shared_", "gate"), qm("shared_", "up"), qm("shared_", "down"))
                        if self.I_shared else Ffn())
-        self.struct = Weights(_p(tensors["router"]), _p(tensors.get("logit_bias")), self.experts, self.shared)
+        self.struct = Weights(_p(tensors["router"]), _p(tensors.get("logit_bias")), self.experts, self.shared,
+                              _p(tensors.get("shared_expert_gate")))
 
     def dims(self, T, top_k) -> Dims:
         return dims(T, self.H, self.E, top_k, self.I, self.I_shared, self.sb_bf16)
@@ -222,7 +228,8 @@ def moe_expert_ffn(x, offsets, sorted_slot, weights: LayerWeights, top_k, with_s
     return y_slot, y_shared
 
 
-def moe_combine(y_slot, topk_w, y_shared=None, out=None):
+def moe_combine(y_slot, topk_w, y_shared=None, out=None, shared_w=None):
+    """shared_w [T] float32 (optional): the shared expert's weight per token (moe_combine_gated)."""
     import torch
 
     T, k = topk_w.shape
@@ -230,8 +237,25 @@ def moe_combine(y_slot, topk_w, y_shared=None, out=None):
     d = dims(T, H, max(k, 1), k, 64, 0)
     if out is None:
         out = torch.empty(T, H, dtype=torch.float32, device=y_slot.device)
-    _check(lib().moe_combine(C.byref(d), _p(y_slot), _p(topk_w), _p(y_shared), _p(out), _stream()), "moe_combine")
+    if shared_w is None:
+        _check(lib().moe_combine(C.byref(d), _p(y_slot), _p(topk_w), _p(y_shared), _p(out), _stream()),
+               "moe_combine")
+    else:
+        _check(lib().moe_combine_gated(C.byref(d), _p(y_slot), _p(topk_w), _p(y_shared), _p(shared_w), _p(out),
+                                       _stream()), "moe_combine_gated")
     return out
+
+
+def moe_shared_gate(x, gate, shared_w=None):
+    """shared_w [T] float32 = sigmoid(x[t] . gate): the shared expert's weight under its optional gate."""
+    import torch
+
+    T, H = x.shape
+    d = dims(T, H, 1, 1, 64, 0)
+    if shared_w is None:
+        shared_w = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check(lib().moe_shared_gate(C.byref(d), _p(x), _p(gate), _p(shared_w), _stream()), "moe_shared_gate")
+    return shared_w
 
 
 def moe_layer_stages(d: Dims):

@@ -193,6 +193,7 @@ struct RoleShared {
     float hrow[kGURows];  // gate/up role: this workgroup's h
     int ex;
     float wgt;
+    float gatew;  // down role of the shared expert: its weight under an optional gate
     int ok;       // routing read in time
     int wait_ok;  // result of the last wait on published values
     int last;     // this workgroup finished last
@@ -528,6 +529,24 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // the shared expert's weight under an optional gate g (a checkpoint detail):
+    // sigmoid(x[t] . g), float32 sum of exact bf16 products, by wave 0 while h
+    // is still being computed elsewhere
+    if (!kRouted && p.shared_gate && wave == 0) {
+        const uint4* xr = reinterpret_cast<const uint4*>(p.x + (size_t)t * H);
+        const uint4* gr = reinterpret_cast<const uint4*>(p.shared_gate);
+        float z = 0.0f;
+        for (int blk = lane; blk < H / 8; blk += kWave) {
+            const uint4 a = xr[blk], g = gr[blk];
+            const uint16_t* ab = reinterpret_cast<const uint16_t*>(&a);
+            const uint16_t* gb = reinterpret_cast<const uint16_t*>(&g);
+#pragma unroll
+            for (int e = 0; e < 8; e++) z += bf16_to_f32(ab[e]) * bf16_to_f32(gb[e]);
+        }
+        z = group_sum(z, kWave);
+        if (lane == 0) sh.gatew = 1.0f / (1.0f + expf(-z));
+    }
+
     // h of the slot, by 64-column groups: wave w takes groups w, w + 4, ...
     // (32 words {epoch, float16 pair} each), polls their words itself and, as
     // soon as they carry this call's epoch, adds their part of every row's dot
@@ -613,7 +632,8 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     if (wave == 0 && r < n_rows) {
         const bool ok = sh.ok && sh.down.wave_ok[0] && sh.down.wave_ok[1] && sh.down.wave_ok[2] && sh.down.wave_ok[3];
         const float yt = (sh.down.part[0][r] + sh.down.part[1][r]) + (sh.down.part[2][r] + sh.down.part[3][r]);
-        if (ok) atomicAdd(p.out + (size_t)t * H + n0 + r, wgt * yt);
+        const float wt = (!kRouted && p.shared_gate) ? sh.gatew : wgt;
+        if (ok) atomicAdd(p.out + (size_t)t * H + n0 + r, wt * yt);
     }
 }
 

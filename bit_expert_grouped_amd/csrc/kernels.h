@@ -71,8 +71,11 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* log
 constexpr int kCounterStride = 32;
 hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H, int E,
                          float* logits, int32_t* zero0, int32_t* zero1, hipStream_t stream);
+// sgate (nullable, needs x16): the shared expert's gate vector [H] bf16; then
+// shared_w [T] receives sigmoid(x[t] . sgate)
 hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int top_k, int32_t* topk_idx,
-                       float* topk_w, int32_t* hist, _Float16* x16, hipStream_t stream);
+                       float* topk_w, int32_t* hist, _Float16* x16, const uint16_t* sgate, float* shared_w,
+                       hipStream_t stream);
 
 hipError_t launch_convert_x(const uint16_t* x, int T, int H, _Float16* x16, hipStream_t stream);
 
@@ -148,6 +151,7 @@ struct DecodeArgs {
     int32_t* counts_out;
     float* out;                  // [T][H]
     FfnPtr experts, shared;      // shared.gate.q == nullptr: no shared expert
+    const uint16_t* shared_gate; // [H] bf16 gate vector of the shared expert, or nullptr (weight 1)
 };
 
 int decode_router_wgs(int E);
@@ -155,11 +159,18 @@ int decode_gateup_wgs(int T, int k, bool shared, int I);
 int decode_down_wgs(int T, int k, bool shared, int H);
 hipError_t launch_decode(const DecodeArgs& a, bool sb_bf16, hipStream_t stream);
 
-hipError_t launch_combine(const float* y_slot, const float* topk_w, const float* y_shared, int T, int H,
-                          int k, float* out, hipStream_t stream);
+// out[t] = sum_j topk_w[t][j] * y_slot[t*k+j] + s[t] * y_shared[t] (y_shared
+// nullable); s = shared_w (nullable: 1)
+hipError_t launch_combine(const float* y_slot, const float* topk_w, const float* y_shared, const float* shared_w,
+                          int T, int H, int k, float* out, hipStream_t stream);
 
-// out[t] = sum_j topk_w[t][j] * y16[t*k+j] (+ y16[T*k+t] when shared), float32.
-hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool shared, int T, int H, int k, float* out,
-                            hipStream_t stream);
+// out[t] = sum_j topk_w[t][j] * y16[t*k+j] (+ s[t] * y16[T*k+t] when shared; s =
+// shared_w, nullable: 1), float32.
+hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool shared, const float* shared_w, int T,
+                            int H, int k, float* out, hipStream_t stream);
+
+// shared_w[t] = sigmoid(x[t] . g), x [T][H] and g [H] bf16
+hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* g, int T, int H, float* shared_w,
+                              hipStream_t stream);
 
 }  // namespace bitmoe

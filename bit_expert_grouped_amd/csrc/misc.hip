@@ -23,17 +23,24 @@ __global__ __launch_bounds__(256) void convert_x_kernel(const uint16_t* __restri
 
 // Pages: one shared expert is added to the routed experts' output (aimanavo.com
 // page, section "Qwen3.6's 256 experts and two layer types make the MLX-Lily gap").
-// out[t][h] = sum_j w[t][j] * y_slot[t*k+j][h] + y_shared[t][h]; 4 columns per thread.
+// out[t][h] = sum_j w[t][j] * y_slot[t*k+j][h] + s[t] * y_shared[t][h]; s[t] =
+// shared_w[t] (an optional shared-expert gate, a checkpoint detail), else 1;
+// 4 columns per thread.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_slot,
                                                       const float* __restrict__ topk_w,
-                                                      const float* __restrict__ y_shared, int T, int H, int k,
+                                                      const float* __restrict__ y_shared,
+                                                      const float* __restrict__ shared_w, int T, int H, int k,
                                                       float* __restrict__ out) {
     const int h4 = H / 4;
     const int64_t n = (int64_t)T * h4;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         const int t = (int)(i / h4), c = (int)(i % h4);
-        float4 acc = y_shared ? reinterpret_cast<const float4*>(y_shared + (size_t)t * H)[c]
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (y_shared) {
+            const float s = shared_w ? shared_w[t] : 1.0f;
+            const float4 y = reinterpret_cast<const float4*>(y_shared + (size_t)t * H)[c];
+            acc = make_float4(s * y.x, s * y.y, s * y.z, s * y.w);
+        }
         for (int j = 0; j < k; j++) {
             const float w = topk_w[(size_t)t * k + j];
             const float4 y = reinterpret_cast<const float4*>(y_slot + ((size_t)t * k + j) * H)[c];
@@ -47,10 +54,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // The layer's combine over float16 expert rows: 8 columns per thread, float32
-// accumulation in slot order, then the shared expert's row.
+// accumulation in slot order, then the shared expert's row (times shared_w[t]
+// when the shared expert is gated).
 __global__ __launch_bounds__(256) void combine16_kernel(const _Float16* __restrict__ y16,
-                                                        const float* __restrict__ topk_w, int shared, int T, int H,
-                                                        int k, float* __restrict__ out) {
+                                                        const float* __restrict__ topk_w, int shared,
+                                                        const float* __restrict__ shared_w, int T, int H, int k,
+                                                        float* __restrict__ out) {
     const int h8 = H / 8;
     const int64_t n = (int64_t)T * h8;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -64,13 +73,36 @@ __global__ __launch_bounds__(256) void combine16_kernel(const _Float16* __restri
         }
         if (shared) {
             const half8_t y = reinterpret_cast<const half8_t*>(y16 + ((size_t)T * k + t) * H)[c];
+            const float s = shared_w ? shared_w[t] : 1.0f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[e] += (float)y[e];
+            for (int e = 0; e < 8; e++) acc[e] += s * (float)y[e];
         }
         float4* o = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * c;
         o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
+}
+
+// Weight of the shared expert per token under an optional shared-expert gate g
+// (a checkpoint detail): shared_w[t] = sigmoid(sum_h x[t][h] * g[h]), float32 sum
+// of exact bf16 products; one wave per token.
+__global__ __launch_bounds__(256) void shared_gate_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ g, int T, int H,
+                                                          float* __restrict__ shared_w) {
+    const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (t >= T) return;
+    float z = 0.0f;
+    for (int blk = lane; blk < H / 8; blk += kWave) {
+        const uint4 xr = reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk];
+        const uint4 gr = reinterpret_cast<const uint4*>(g)[blk];
+        const uint16_t* xb = reinterpret_cast<const uint16_t*>(&xr);
+        const uint16_t* gb = reinterpret_cast<const uint16_t*>(&gr);
+#pragma unroll
+        for (int e = 0; e < 8; e++) z += bf16_to_f32(xb[e]) * bf16_to_f32(gb[e]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    if (lane == 0) shared_w[t] = 1.0f / (1.0f + expf(-z));
 }
 
 int grid_for(int64_t n) {
@@ -80,12 +112,19 @@ int grid_for(int64_t n) {
 
 }  // namespace
 
-hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool shared, int T, int H, int k, float* out,
-                            hipStream_t stream) {
+hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool shared, const float* shared_w, int T,
+                            int H, int k, float* out, hipStream_t stream) {
     const int64_t n = (int64_t)T * (H / 8);
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine16_kernel, dim3(grid_for(n)), dim3(256), 0, stream, y16, topk_w, shared ? 1 : 0, T, H,
-                       k, out);
+    hipLaunchKernelGGL(combine16_kernel, dim3(grid_for(n)), dim3(256), 0, stream, y16, topk_w, shared ? 1 : 0,
+                       shared_w, T, H, k, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* g, int T, int H, float* shared_w,
+                              hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(shared_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, x, g, T, H, shared_w);
     return hipGetLastError();
 }
 
@@ -96,12 +135,12 @@ hipError_t launch_convert_x(const uint16_t* x, int T, int H, _Float16* x16, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* y_slot, const float* topk_w, const float* y_shared, int T, int H, int k,
-                          float* out, hipStream_t stream) {
+hipError_t launch_combine(const float* y_slot, const float* topk_w, const float* y_shared, const float* shared_w,
+                          int T, int H, int k, float* out, hipStream_t stream) {
     const int64_t n = (int64_t)T * (H / 4);
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n)), dim3(256), 0, stream, y_slot, topk_w, y_shared, T, H, k,
-                       out);
+    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n)), dim3(256), 0, stream, y_slot, topk_w, y_shared, shared_w, T,
+                       H, k, out);
     return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ moe_status check_dims(const moe_dims* d) {
 struct Layout {
     size_t ctl, xch, sel, hbuf;                          // decode region
     size_t x16, h, y16, logits, hist, cursor;            // prefill buffers
-    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, total;
+    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, shared_w, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -89,6 +89,8 @@ Layout layout_of(const moe_dims* d) {
     o = up256(o + (size_t)max_tiles(d->T, d->top_k, d->E, shared, 64) * sizeof(Tile));
     L.n_tiles64 = o;
     o = up256(o + 4);
+    L.shared_w = o;  // the shared expert's weight per token under its optional gate
+    o = up256(o + T * 4);
     L.total = o;
     return L;
 }
@@ -241,7 +243,28 @@ moe_status moe_combine(const moe_dims* d, const float* y_slot, const float* topk
     if (d->T == 0) return MOE_OK;
     MOE_TRY(check_ptrs({y_slot, topk_w, out}));
     MOE_TRY(check_opt({y_shared}));
-    HIP_TRY(launch_combine(y_slot, topk_w, y_shared, d->T, d->H, d->top_k, static_cast<float*>(out), stream));
+    HIP_TRY(launch_combine(y_slot, topk_w, y_shared, nullptr, d->T, d->H, d->top_k, static_cast<float*>(out),
+                           stream));
+    return MOE_OK;
+}
+
+moe_status moe_combine_gated(const moe_dims* d, const float* y_slot, const float* topk_w, const float* y_shared,
+                             const float* shared_w, void* out, hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({y_slot, topk_w, out}));
+    MOE_TRY(check_opt({y_shared, shared_w}));
+    HIP_TRY(launch_combine(y_slot, topk_w, y_shared, shared_w, d->T, d->H, d->top_k, static_cast<float*>(out),
+                           stream));
+    return MOE_OK;
+}
+
+moe_status moe_shared_gate(const moe_dims* d, const uint16_t* x, const uint16_t* gate, float* shared_w,
+                           hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, gate, shared_w}));
+    HIP_TRY(launch_shared_gate(x, gate, d->T, d->H, shared_w, stream));
     return MOE_OK;
 }
 
@@ -268,9 +291,10 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     const bool shared = d->I_shared > 0;
     if (shared) {
         MOE_TRY(check_ffn(&wts->shared));
-    } else if (wts->shared.gate.q) {
+    } else if (wts->shared.gate.q || wts->shared_expert_gate) {
         return MOE_ERR_SHAPE;
     }
+    MOE_TRY(check_opt({wts->shared_expert_gate}));
     MOE_TRY(check_ws(d, ws, ws_bytes));
     const int n_stages = stage_count(d);
     if (events) {
@@ -304,6 +328,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.out = static_cast<float*>(out);
         a.experts = to_ptr(&wts->experts);
         a.shared = shared ? to_ptr(&wts->shared) : FfnPtr{};
+        a.shared_gate = wts->shared_expert_gate;
         if (!mark(0)) return MOE_ERR_HIP;
         HIP_TRY(launch_decode(a, d->sb_dtype == MOE_BF16, stream));
         if (!mark(1)) return MOE_ERR_HIP;
@@ -345,7 +370,9 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     HIP_TRY(launch_logits(x, wts->router, wts->logit_bias, d->T, d->H, d->E, at<float>(ws, L.logits), hist, cursor,
                           stream));
     if (!mark(1)) return MOE_ERR_HIP;
-    HIP_TRY(launch_topk(at<float>(ws, L.logits), x, d->T, d->H, d->E, d->top_k, idx, w, hist, x16, stream));
+    float* shared_w = wts->shared_expert_gate ? at<float>(ws, L.shared_w) : nullptr;
+    HIP_TRY(launch_topk(at<float>(ws, L.logits), x, d->T, d->H, d->E, d->top_k, idx, w, hist, x16,
+                        wts->shared_expert_gate, shared_w, stream));
     if (!mark(2)) return MOE_ERR_HIP;
     // large batches: down (short K, so per-tile overheads weigh more) runs on
     // a second map of 64-row tiles with two workgroups per compute unit
@@ -365,7 +392,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     }
     HIP_TRY(launch_down(pd, h, y16, nullptr, nullptr, stream));
     if (!mark(5)) return MOE_ERR_HIP;
-    HIP_TRY(launch_combine16(y16, w, shared, d->T, d->H, d->top_k, o, stream));
+    HIP_TRY(launch_combine16(y16, w, shared, shared_w, d->T, d->H, d->top_k, o, stream));
     if (!mark(6)) return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -213,7 +213,8 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
                                                    const uint16_t* __restrict__ x, int T, int H, int E, int top_k,
                                                    int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w, int32_t* __restrict__ hist,
-                                                   _Float16* __restrict__ x16) {
+                                                   _Float16* __restrict__ x16, const uint16_t* __restrict__ sgate,
+                                                   float* __restrict__ shared_w) {
     // the workgroup's expert counts gather in LDS first: one global atomic per
     // (workgroup, expert), so a hot expert's counter sees at most T / kTW adds
     __shared__ int lh[kMaxE];
@@ -253,7 +254,11 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
             if (ij >= 0 && ij < E) atomicAdd(&lh[ij], 1);
         }
         if (x16) {
+            // the float16 copy of the row; with a shared-expert gate g, also the
+            // shared expert's weight sigmoid(x . g) (float32 sum of exact bf16
+            // products, reduced over the wave)
             const int nblk = H / 8;
+            float z = 0.0f;
             for (int blk = lane; blk < nblk; blk += kWave) {
                 const uint4 raw = reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk];
                 const uint16_t* hb = reinterpret_cast<const uint16_t*>(&raw);
@@ -261,6 +266,17 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
 #pragma unroll
                 for (int e = 0; e < 8; e++) o[e] = (_Float16)bf16_to_f32(hb[nibble_of(e)]);
                 reinterpret_cast<half8_t*>(x16 + (size_t)t * H)[blk] = o;
+                if (sgate) {
+                    const uint4 graw = reinterpret_cast<const uint4*>(sgate)[blk];
+                    const uint16_t* gb = reinterpret_cast<const uint16_t*>(&graw);
+#pragma unroll
+                    for (int e = 0; e < 8; e++) z += bf16_to_f32(hb[e]) * bf16_to_f32(gb[e]);
+                }
+            }
+            if (sgate) {
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+                if (lane == 0) shared_w[t] = 1.0f / (1.0f + expf(-z));
             }
         }
     }
@@ -296,15 +312,16 @@ hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* log
 }
 
 hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int top_k, int32_t* topk_idx,
-                       float* topk_w, int32_t* hist, _Float16* x16, hipStream_t stream) {
+                       float* topk_w, int32_t* hist, _Float16* x16, const uint16_t* sgate, float* shared_w,
+                       hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     const int S = logits_splits(T, H, E);
     if (T >= 1024)
         hipLaunchKernelGGL(topk_kernel<16>, dim3((T + 15) / 16), dim3(16 * kWave), 0, stream, logits, S, x, T, H, E,
-                           top_k, topk_idx, topk_w, hist, x16);
+                           top_k, topk_idx, topk_w, hist, x16, sgate, shared_w);
     else
         hipLaunchKernelGGL(topk_kernel<4>, dim3((T + 3) / 4), dim3(4 * kWave), 0, stream, logits, S, x, T, H, E, top_k,
-                           topk_idx, topk_w, hist, x16);
+                           topk_idx, topk_w, hist, x16, sgate, shared_w);
     return hipGetLastError();
 }
 

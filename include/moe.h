@@ -98,6 +98,12 @@ typedef struct {
     const float *logit_bias;  /* [E] or NULL */
     moe_ffn experts;          /* E routed experts */
     moe_ffn shared;           /* the shared expert; shared.gate.q == NULL iff I_shared == 0 */
+    /* Optional gate of the shared expert, [H] bf16, or NULL.  Not on the pages: a
+     * detail of Qwen's mixture-of-experts checkpoints.  When set, the shared
+     * expert's output is scaled by sigmoid(sum_h x[t][h] * gate[h]) (float32
+     * sum of exact bf16 products) instead of being added with weight 1.  Must
+     * be NULL without a shared expert (MOE_ERR_SHAPE). */
+    const uint16_t *shared_expert_gate;
 } moe_weights;
 
 /* Bytes of device workspace the calls below need for these dims (host-only,
@@ -146,6 +152,19 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x, const int32_t
  * out [T][H] float32. */
 moe_status moe_combine(const moe_dims *dims, const float *y_slot, const float *topk_w,
                        const float *y_shared, void *out, hipStream_t stream);
+
+/* Weight of the shared expert under its optional gate (see moe_weights; a
+ * checkpoint detail, not on the pages): shared_w[t] = sigmoid(sum_h x[t][h] *
+ * gate[h]), float32 sum of exact bf16 products.  x [T][H] bf16, gate [H] bf16,
+ * shared_w [T] float32. */
+moe_status moe_shared_gate(const moe_dims *dims, const uint16_t *x, const uint16_t *gate, float *shared_w,
+                           hipStream_t stream);
+
+/* moe_combine with the shared expert's row scaled per token:
+ * out[t] = sum_j topk_w[t][j] * y_slot[t*top_k+j] + shared_w[t] * y_shared[t]
+ * (y_shared nullable; shared_w nullable: weight 1, as moe_combine). */
+moe_status moe_combine_gated(const moe_dims *dims, const float *y_slot, const float *topk_w,
+                             const float *y_shared, const float *shared_w, void *out, hipStream_t stream);
 
 /* The whole layer as one device-side pipeline, shared expert included;
  * out [T][H] float32.  Optional copies of the routing: topk_idx_out [T][top_k],

@@ -100,6 +100,25 @@ def test_layer_argument_checks(lib):
     assert lib.moe_layer(None, C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -1
 
 
+def test_shared_expert_gate_checks(lib):
+    d = qwen_dims(8)
+    need = bem.moe_workspace_size(d)
+    w = _weights()
+    w.shared_expert_gate = FAKE + 2  # misaligned
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -4
+    noshared = _weights(shared=False)
+    noshared.shared_expert_gate = FAKE  # a gate without a shared expert
+    d0 = qwen_dims(8, I_shared=0)
+    assert lib.moe_layer(C.byref(d0), C.byref(noshared), FAKE, FAKE, None, None, None, FAKE, need, None) == -2
+    assert lib.moe_shared_gate(C.byref(d), FAKE, None, FAKE, None) == -1
+    assert lib.moe_shared_gate(C.byref(d), FAKE, FAKE + 2, FAKE, None) == -4
+    assert lib.moe_combine_gated(C.byref(d), FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == -4
+    assert lib.moe_combine_gated(C.byref(d), None, FAKE, None, None, FAKE, None) == -1
+    e = qwen_dims(0)
+    assert lib.moe_shared_gate(C.byref(e), None, None, None, None) == 0
+    assert lib.moe_combine_gated(C.byref(e), None, None, None, None, None, None) == 0
+
+
 def test_empty_call_enqueues_nothing(lib):
     d = qwen_dims(0)
     assert lib.moe_layer(C.byref(d), None, None, None, None, None, None, None, 0, None) == 0

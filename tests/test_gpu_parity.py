@@ -287,6 +287,50 @@ def test_exact_logit_ties_go_to_the_lower_index(T, H, E):
     assert_same_routing(ridx.cpu().numpy(), rw.cpu().numpy(), ref["idx"], ref["w"])
 
 
+@pytest.mark.parametrize("T,H,E,k,I,bf16", [
+    (16, 256, 16, 2, 64, False),     # tiny shapes, fp32 scales (prefill path)
+    (1, 2048, 256, 8, 512, True),    # decode
+    (3, 2048, 256, 8, 512, True),    # decode, several tokens
+    (64, 2048, 256, 8, 512, True),   # batched decode on the prefill path
+    (600, 384, 16, 2, 192, True),    # large-batch path
+])
+def test_gated_shared_expert(T, H, E, k, I, bf16):
+    """The optional shared-expert gate (a checkpoint detail): the shared output
+    scaled by sigmoid(x . g) on every path, against the oracle."""
+    cfg, w, x = _custom(T, H, E, k, I, I, bf16, seed=500 + T)
+    w["shared_expert_gate"] = moe_synth.shared_expert_gate(cfg)
+    ref = oracle.moe_layer(w, x, k)
+    out, idx, wt, counts = run_layer(w, x, k)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out, ref["out"], "gated shared expert T%d" % T)
+    w0 = {key: v for key, v in w.items() if key != "shared_expert_gate"}
+    ungated = oracle.moe_layer(w0, x, k)["out"]
+    assert np.abs(ungated - ref["out"]).max() > 4 * TOL * rms(ref["out"])  # the gate matters at this tolerance
+
+
+def test_shared_gate_and_gated_combine_steps():
+    cfg, w, x = _custom(37, 2048, 256, 8, 512, 512, True, seed=808)
+    g = moe_synth.shared_expert_gate(cfg)
+    m = bem()
+    s = m.moe_shared_gate(m.bf16_tensor(x), m.bf16_tensor(g))
+    torch.cuda.synchronize()
+    s_ref = oracle.shared_gate(x, g)
+    np.testing.assert_allclose(s.cpu().numpy(), s_ref, rtol=0, atol=2e-5)
+    rng = np.random.default_rng(5)
+    T, k, H = 37, 8, 2048
+    y_slot = rng.standard_normal((T * k, H)).astype(np.float32)
+    y_sh = rng.standard_normal((T, H)).astype(np.float32)
+    wt = rng.random((T, k)).astype(np.float32)
+    wt /= wt.sum(axis=1, keepdims=True)
+    sw = s_ref.astype(np.float32)
+    out = m.moe_combine(torch.from_numpy(y_slot).cuda(), torch.from_numpy(wt).cuda(), torch.from_numpy(y_sh).cuda(),
+                        shared_w=torch.from_numpy(sw).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.combine(y_slot.reshape(T, k, H), wt, y_sh, shared_w=sw)
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+
+
 def test_hot_expert_spans_many_tiles():
     bias = np.zeros(32, dtype=np.float32)
     bias[5] = 50.0
