@@ -67,7 +67,10 @@ __global__ __launch_bounds__(256) void combine16_kernel(const _Float16* __restri
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int j = 0; j < k; j++) {
             const float w = topk_w[(size_t)t * k + j];
-            const half8_t y = reinterpret_cast<const half8_t*>(y16 + ((size_t)t * k + j) * H)[c];
+            // each row is read exactly once: nontemporal loads and stores keep the
+            // stream from displacing other data in the caches
+            const half8_t y =
+                __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(y16 + ((size_t)t * k + j) * H) + c);
 #pragma unroll
             for (int e = 0; e < 8; e++) acc[e] += w * (float)y[e];
         }
@@ -77,9 +80,10 @@ __global__ __launch_bounds__(256) void combine16_kernel(const _Float16* __restri
 #pragma unroll
             for (int e = 0; e < 8; e++) acc[e] += s * (float)y[e];
         }
-        float4* o = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * c;
-        o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        typedef float fx4 __attribute__((ext_vector_type(4)));
+        fx4* o = reinterpret_cast<fx4*>(out + (size_t)t * H) + 2 * c;
+        __builtin_nontemporal_store(fx4{acc[0], acc[1], acc[2], acc[3]}, o);
+        __builtin_nontemporal_store(fx4{acc[4], acc[5], acc[6], acc[7]}, o + 1);
     }
 }
 
