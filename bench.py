@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (three times) for counter calibration")
+    ap.add_argument("--shared-gate", action="store_true",
+                    help="give the shared expert a sigmoid gate vector (an optional checkpoint detail; the "
+                         "configs have none)")
     ap.add_argument("--mode", choices=("eager", "graph"), default=None,
                     help="graph: replay one HIP graph holding the K timed steps (default); "
                          "eager: one foreign call per layer call")
@@ -232,7 +235,12 @@ def main():
     torch.cuda.set_device(dev)
     bem.lib()
     alpha = moe_synth.zipf_alpha() if cfg.zipf else None
-    sets = [bem.LayerWeights(moe_synth.device_layer(sh, cfg.seed, l, dev, alpha)) for l in range(n_sets)]
+    tensors = [moe_synth.device_layer(sh, cfg.seed, l, dev, alpha) for l in range(n_sets)]
+    if args.shared_gate:
+        for l, t in enumerate(tensors):
+            gbits = moe_synth.shared_expert_gate(cfg, l)
+            t["shared_expert_gate"] = torch.from_numpy(gbits.view("int16")).to(dev).view(torch.bfloat16)
+    sets = [bem.LayerWeights(t) for t in tensors]
     n_x = min(steps + warmup, 64) if not big else 4
     xs = [moe_synth.device_tokens(sh, T, cfg.seed, i, dev) for i in range(n_x)]
     d = sets[0].dims(T, sh.top_k)
@@ -393,6 +401,7 @@ def main():
         "config": {"workload": args.workload, "T": T, "H": sh.H, "E": sh.E, "top_k": sh.top_k, "I": sh.I,
                    "I_shared": sh.I_shared, "layers_per_step": layers_per_step, "weight_sets": n_sets,
                    "weights": "affine 4-bit g64, bf16 scales/biases", "activations": "bf16",
+                   "shared_expert_gate": bool(args.shared_gate),
                    "products": "f16 MFMA, fp32 accumulation; router bf16 MFMA; fp32 output"},
         "us_per_layer": round(us_layer, 3),
         "layer_hbm_frac": round(layer_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

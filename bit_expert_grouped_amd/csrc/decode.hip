@@ -484,6 +484,23 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     const int t = routed ? slot / p.top_k : slot - TK;
     const int n0 = blk * kDRows;
 
+    // the shared expert's weight under an optional gate g (a checkpoint detail):
+    // sigmoid(x[t] . g), float32 sum of exact bf16 products, by wave 1 while
+    // wave 0 waits for the routing (route_slot ends with a barrier)
+    if (!kRouted && p.shared_gate && wave == 1) {
+        const uint4* xr = reinterpret_cast<const uint4*>(p.x + (size_t)t * H);
+        const uint4* gr = reinterpret_cast<const uint4*>(p.shared_gate);
+        float z = 0.0f;
+        for (int blk = lane; blk < H / 8; blk += kWave) {
+            const uint4 a = xr[blk], g = gr[blk];
+            const uint16_t* ab = reinterpret_cast<const uint16_t*>(&a);
+            const uint16_t* gb = reinterpret_cast<const uint16_t*>(&g);
+#pragma unroll
+            for (int e = 0; e < 8; e++) z += bf16_to_f32(ab[e]) * bf16_to_f32(gb[e]);
+        }
+        z = group_sum(z, kWave);
+        if (lane == 0) sh.gatew = 1.0f / (1.0f + expf(-z));
+    }
     // every down workgroup waits for its token's logits, shared ones too: the
     // router clears the output rows before it publishes them
     route_slot(p, slot, t, routed, epoch, sh);
@@ -529,23 +546,6 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // the shared expert's weight under an optional gate g (a checkpoint detail):
-    // sigmoid(x[t] . g), float32 sum of exact bf16 products, by wave 0 while h
-    // is still being computed elsewhere
-    if (!kRouted && p.shared_gate && wave == 0) {
-        const uint4* xr = reinterpret_cast<const uint4*>(p.x + (size_t)t * H);
-        const uint4* gr = reinterpret_cast<const uint4*>(p.shared_gate);
-        float z = 0.0f;
-        for (int blk = lane; blk < H / 8; blk += kWave) {
-            const uint4 a = xr[blk], g = gr[blk];
-            const uint16_t* ab = reinterpret_cast<const uint16_t*>(&a);
-            const uint16_t* gb = reinterpret_cast<const uint16_t*>(&g);
-#pragma unroll
-            for (int e = 0; e < 8; e++) z += bf16_to_f32(ab[e]) * bf16_to_f32(gb[e]);
-        }
-        z = group_sum(z, kWave);
-        if (lane == 0) sh.gatew = 1.0f / (1.0f + expf(-z));
-    }
 
     // h of the slot, by 64-column groups: wave w takes groups w, w + 4, ...
     // (32 words {epoch, float16 pair} each), polls their words itself and, as
