@@ -112,6 +112,53 @@ def test_layer_stack40_sampled_layers(layer):
     assert_close(out[tokens], ref["out"], "stack40 layer %d" % layer)
 
 
+def _host(tensors):
+    """Device weights in the bench's layout -> numpy arrays in the oracle's formats."""
+    out = {}
+    for key, v in tensors.items():
+        if v is None:
+            out[key] = None
+        elif v.dtype == torch.int32:
+            out[key] = v.cpu().numpy().view(np.uint32)
+        elif v.dtype == torch.bfloat16:
+            out[key] = v.view(torch.int16).cpu().numpy().view(np.uint16)
+        else:
+            out[key] = v.cpu().numpy()
+    return out
+
+
+@pytest.mark.parametrize("name,layer,n_sample", [("decode", 0, 1), ("decode", 17, 1), ("decode64", 2, 16),
+                                                 ("prefill512", 1, 16), ("stack40", 3, 8)])
+def test_bench_inputs_against_oracle(name, layer, n_sample):
+    """The weights and tokens that bench.py draws on the device (and times) give
+    the oracle's result on sampled tokens.  Tokens whose k-th and (k+1)-th logits
+    are closer than 1e-4 are left out (there two correct implementations may pick
+    differently; the parity inputs re-draw such rows, the bench's do not)."""
+    cfg = moe_synth.CONFIGS[name]
+    sh = cfg.shape
+    alpha = moe_synth.zipf_alpha() if cfg.zipf else None
+    t = moe_synth.device_layer(sh, cfg.seed, layer, "cuda", alpha)
+    x = moe_synth.device_tokens(sh, sh.T, cfg.seed, layer, "cuda")
+    m = bem()
+    out, idx, wt, counts = m.moe_layer(x, m.LayerWeights(t), sh.top_k, want_routing=True)
+    torch.cuda.synchronize()
+    w = _host(t)
+    xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    lg = oracle.router_logits(xb, w["router"], w.get("logit_bias"))
+    srt = -np.sort(-lg.astype(np.float32).astype(np.float64), axis=1)
+    clear = np.nonzero(srt[:, sh.top_k - 1] - srt[:, sh.top_k] >= 1e-4)[0]
+    if len(clear) == 0:
+        pytest.skip("every token of this draw is a near-tie")
+    rng = np.random.default_rng(99 + layer)
+    tokens = np.sort(rng.choice(clear, min(n_sample, len(clear)), replace=False)).astype(np.int32)
+    ref = oracle.moe_layer(w, xb, sh.top_k, tokens=tokens)
+    idx = idx.cpu().numpy()
+    np.testing.assert_array_equal(np.sort(idx[tokens], 1), np.sort(ref["idx"][tokens], 1))
+    if len(clear) == sh.T:
+        np.testing.assert_array_equal(counts.cpu().numpy(), ref["counts"])
+    assert_close(out.cpu().numpy()[tokens], ref["out"], "bench inputs %s layer %d" % (name, layer))
+
+
 # ------------------------------------------------------------------ step-by-step ABI
 
 
