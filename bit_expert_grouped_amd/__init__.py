@@ -21,7 +21,7 @@ MOE_BF16, MOE_F32 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_shared_gate",
-           "moe_combine_gated", "moe_layer", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
+           "moe_combine_gated", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
            "moe_status_string")
 
 
@@ -71,13 +71,14 @@ def lib():
         L.moe_combine_gated.argtypes = [D, P, P, P, P, P, P]
         L.moe_shared_gate.argtypes = [D, P, P, P, P]
         L.moe_layer.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P]
+        L.moe_layer_residual.argtypes = [D, C.POINTER(Weights), P, P, P, P, C.c_size_t, P]
         L.moe_layer_events.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P, P, C.c_int32]
         L.moe_layer_stage_count.argtypes = [D]
         L.moe_layer_stage_count.restype = C.c_int32
         L.moe_layer_stage_name.argtypes = [D, C.c_int32]
         L.moe_layer_stage_name.restype = C.c_char_p
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_combine_gated",
-                     "moe_shared_gate", "moe_layer", "moe_layer_events"):
+                     "moe_shared_gate", "moe_layer", "moe_layer_residual", "moe_layer_events"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -256,6 +257,22 @@ def moe_shared_gate(x, gate, shared_w=None):
         shared_w = torch.empty(T, dtype=torch.float32, device=x.device)
     _check(lib().moe_shared_gate(C.byref(d), _p(x), _p(gate), _p(shared_w), _stream()), "moe_shared_gate")
     return shared_w
+
+
+def moe_layer_residual(x, weights: "LayerWeights", top_k, residual=None, out=None, ws=None):
+    """out [T][H] bf16 = bf16(residual + layer(x)); residual (bf16, optional) may be ``out`` itself."""
+    import torch
+
+    T, H = x.shape
+    d = weights.dims(T, top_k)
+    d.out_dtype = MOE_BF16
+    if ws is None:
+        ws = workspace(d, x.device)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    _check(lib().moe_layer_residual(C.byref(d), C.byref(weights.struct), _p(x), _p(residual), _p(out), _p(ws),
+                                    ws.numel(), _stream()), "moe_layer_residual")
+    return out
 
 
 def moe_layer_stages(d: Dims):

@@ -165,9 +165,14 @@ hipError_t launch_combine(const float* y_slot, const float* topk_w, const float*
                           int T, int H, int k, float* out, hipStream_t stream);
 
 // out[t] = sum_j topk_w[t][j] * y16[t*k+j] (+ s[t] * y16[T*k+t] when shared; s =
-// shared_w, nullable: 1), float32.
+// shared_w, nullable: 1), float32.  out16 != nullptr: out16 = bf16(residual +
+// that sum) instead (residual nullable, may alias out16).
 hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool shared, const float* shared_w, int T,
-                            int H, int k, float* out, hipStream_t stream);
+                            int H, int k, float* out, const uint16_t* residual, uint16_t* out16, hipStream_t stream);
+
+// out16 [T][H] = bf16(residual + y) (residual nullable, may alias out16)
+hipError_t launch_residual_bf16(const float* y, const uint16_t* residual, int T, int H, uint16_t* out16,
+                                hipStream_t stream);
 
 // shared_w[t] = sigmoid(x[t] . g), x [T][H] and g [H] bf16
 hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* g, int T, int H, float* shared_w,

@@ -53,13 +53,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
 }
 
+// float32 -> bfloat16, round to nearest even (finite values)
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// 8 float32 values plus 8 bf16 residuals (nullable) -> 8 bf16, one rounding each
+__device__ __forceinline__ uint4 residual_bf16x8(const float (&v)[8], const uint16_t* res) {
+    float r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (res) {
+        const uint4 rr = *reinterpret_cast<const uint4*>(res);
+        const uint16_t* rb = reinterpret_cast<const uint16_t*>(&rr);
+#pragma unroll
+        for (int e = 0; e < 8; e++) r[e] = bf16_to_f32(rb[e]);
+    }
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) b[e] = bf16_bits_rne(v[e] + r[e]);
+    return make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+}
+
 // The layer's combine over float16 expert rows: 8 columns per thread, float32
 // accumulation in slot order, then the shared expert's row (times shared_w[t]
-// when the shared expert is gated).
+// when the shared expert is gated).  out16 != nullptr: the result goes to the
+// bf16 residual stream instead, out16 = bf16(residual + sum) (residual
+// nullable, and it may be the same buffer as out16: each thread reads its 8
+// residuals before it writes them).
 __global__ __launch_bounds__(256) void combine16_kernel(const _Float16* __restrict__ y16,
                                                         const float* __restrict__ topk_w, int shared,
                                                         const float* __restrict__ shared_w, int T, int H, int k,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ out, const uint16_t* residual,
+                                                        uint16_t* out16) {
     const int h8 = H / 8;
     const int64_t n = (int64_t)T * h8;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -79,6 +104,11 @@ __global__ __launch_bounds__(256) void combine16_kernel(const _Float16* __restri
             const float s = shared_w ? shared_w[t] : 1.0f;
 #pragma unroll
             for (int e = 0; e < 8; e++) acc[e] += s * (float)y[e];
+        }
+        if (out16) {
+            const size_t at = (size_t)t * H + 8 * (size_t)c;
+            *reinterpret_cast<uint4*>(out16 + at) = residual_bf16x8(acc, residual ? residual + at : nullptr);
+            continue;
         }
         typedef float fx4 __attribute__((ext_vector_type(4)));
         fx4* o = reinterpret_cast<fx4*>(out + (size_t)t * H) + 2 * c;
@@ -109,6 +139,19 @@ __global__ __launch_bounds__(256) void shared_gate_kernel(const uint16_t* __rest
     if (lane == 0) shared_w[t] = 1.0f / (1.0f + expf(-z));
 }
 
+// out16 = bf16(residual + y) for n8 blocks of 8 elements (the decode path's
+// float32 layer output into the bf16 residual stream; residual nullable, may
+// alias out16)
+__global__ __launch_bounds__(256) void residual_bf16_kernel(const float* __restrict__ y, const uint16_t* residual,
+                                                            int64_t n8, uint16_t* out16) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+        float v[8];
+        const float4 a = reinterpret_cast<const float4*>(y)[2 * i], b = reinterpret_cast<const float4*>(y)[2 * i + 1];
+        v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+        *reinterpret_cast<uint4*>(out16 + 8 * i) = residual_bf16x8(v, residual ? residual + 8 * i : nullptr);
+    }
+}
+
 int grid_for(int64_t n) {
     int64_t g = (n + 255) / 256;
     return (int)(g < 1 ? 1 : (g > 8192 ? 8192 : g));
@@ -117,11 +160,19 @@ int grid_for(int64_t n) {
 }  // namespace
 
 hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool shared, const float* shared_w, int T,
-                            int H, int k, float* out, hipStream_t stream) {
+                            int H, int k, float* out, const uint16_t* residual, uint16_t* out16, hipStream_t stream) {
     const int64_t n = (int64_t)T * (H / 8);
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(combine16_kernel, dim3(grid_for(n)), dim3(256), 0, stream, y16, topk_w, shared ? 1 : 0,
-                       shared_w, T, H, k, out);
+                       shared_w, T, H, k, out, residual, out16);
+    return hipGetLastError();
+}
+
+hipError_t launch_residual_bf16(const float* y, const uint16_t* residual, int T, int H, uint16_t* out16,
+                                hipStream_t stream) {
+    const int64_t n8 = (int64_t)T * H / 8;
+    if (n8 <= 0) return hipSuccess;
+    hipLaunchKernelGGL(residual_bf16_kernel, dim3(grid_for(n8)), dim3(256), 0, stream, y, residual, n8, out16);
     return hipGetLastError();
 }
 

@@ -31,7 +31,6 @@ moe_status check_dims(const moe_dims* d) {
     if (d->H > kMaxH || d->I > kMaxI) return MOE_ERR_UNSUPPORTED;
     if (d->I_shared != 0 && d->I_shared != d->I) return MOE_ERR_UNSUPPORTED;
     if ((int64_t)d->T > kMaxT) return MOE_ERR_UNSUPPORTED;
-    if (d->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -39,7 +38,7 @@ moe_status check_dims(const moe_dims* d) {
 struct Layout {
     size_t ctl, xch, sel, hbuf;                          // decode region
     size_t x16, h, y16, logits, hist, cursor;            // prefill buffers
-    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, shared_w, total;
+    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, shared_w, yacc, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -91,6 +90,8 @@ Layout layout_of(const moe_dims* d) {
     o = up256(o + 4);
     L.shared_w = o;  // the shared expert's weight per token under its optional gate
     o = up256(o + T * 4);
+    L.yacc = o;  // decode with a bf16 output: the float32 layer output before the residual add
+    o = up256(o + (T <= (size_t)kDecodeMaxT ? T * H * 4 : 0));
     L.total = o;
     return L;
 }
@@ -279,13 +280,18 @@ bool use_decode_path(const moe_dims* d) { return d->T <= kDecodeMaxT && d->I <= 
 
 int stage_count(const moe_dims* d) { return use_decode_path(d) ? kDecodeStageCount : kPrefillStageCount; }
 
+// out16 != nullptr: the bf16 residual-stream output (out unused), out16 =
+// bf16(residual + layer); else the float32 output `out`
 moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out,
                       int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                      hipStream_t stream, hipEvent_t* events, int32_t n_events) {
+                      hipStream_t stream, hipEvent_t* events, int32_t n_events, const uint16_t* residual = nullptr,
+                      uint16_t* out16 = nullptr) {
     MOE_TRY(check_dims(d));
+    if (d->out_dtype != (out16 ? MOE_BF16 : MOE_F32)) return MOE_ERR_UNSUPPORTED;
     if (d->T == 0) return MOE_OK;
     if (!wts) return MOE_ERR_NULL;
-    MOE_TRY(check_ptrs({x, out, wts->router}));
+    MOE_TRY(check_ptrs({x, out16 ? static_cast<const void*>(out16) : out, wts->router}));
+    MOE_TRY(check_opt({residual}));
     MOE_TRY(check_opt({wts->logit_bias, topk_idx_out, topk_w_out, counts_out}));
     MOE_TRY(check_ffn(&wts->experts));
     const bool shared = d->I_shared > 0;
@@ -325,12 +331,13 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.idx_out = topk_idx_out;
         a.w_out = topk_w_out;
         a.counts_out = counts_out;
-        a.out = static_cast<float*>(out);
+        a.out = out16 ? at<float>(ws, L.yacc) : static_cast<float*>(out);
         a.experts = to_ptr(&wts->experts);
         a.shared = shared ? to_ptr(&wts->shared) : FfnPtr{};
         a.shared_gate = wts->shared_expert_gate;
         if (!mark(0)) return MOE_ERR_HIP;
         HIP_TRY(launch_decode(a, d->sb_dtype == MOE_BF16, stream));
+        if (out16) HIP_TRY(launch_residual_bf16(a.out, residual, d->T, d->H, out16, stream));
         if (!mark(1)) return MOE_ERR_HIP;
         return MOE_OK;
     }
@@ -392,7 +399,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     }
     HIP_TRY(launch_down(pd, h, y16, nullptr, nullptr, stream));
     if (!mark(5)) return MOE_ERR_HIP;
-    HIP_TRY(launch_combine16(y16, w, shared, shared_w, d->T, d->H, d->top_k, o, stream));
+    HIP_TRY(launch_combine16(y16, w, shared, shared_w, d->T, d->H, d->top_k, o, residual, out16, stream));
     if (!mark(6)) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -402,6 +409,15 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
 moe_status moe_layer(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out, int32_t* topk_idx_out,
                      float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
     return layer_impl(d, wts, x, out, topk_idx_out, topk_w_out, counts_out, ws, ws_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_layer_residual(const moe_dims* d, const moe_weights* wts, const uint16_t* x, const uint16_t* residual,
+                              uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d->T == 0) return MOE_OK;
+    if (!out) return MOE_ERR_NULL;
+    return layer_impl(d, wts, x, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream, nullptr, 0, residual, out);
 }
 
 moe_status moe_layer_events(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out,

@@ -76,7 +76,8 @@ typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
  *   group == 64; H % 64 == 0, 64 <= H <= 16384; I % 64 == 0, 64 <= I <= 4096;
  *   I_shared == 0 (no shared expert) or as I; 1 <= top_k <= 8; top_k <= E <= 256;
  *   0 <= T <= 2^22 (T == 0 is a valid empty call that enqueues nothing);
- *   sb_dtype MOE_BF16 or MOE_F32; out_dtype MOE_F32 (MOE_BF16 is unsupported). */
+ *   sb_dtype MOE_BF16 or MOE_F32; out_dtype MOE_F32 for moe_layer, MOE_BF16 for
+ *   moe_layer_residual (the other calls' outputs are float32 whatever it says). */
 typedef struct {
     int32_t T, H, E, top_k, I, I_shared, group;
     int32_t sb_dtype;  /* moe_dtype of expert scales and biases */
@@ -178,6 +179,18 @@ moe_status moe_combine_gated(const moe_dims *dims, const float *y_slot, const fl
 moe_status moe_layer(const moe_dims *dims, const moe_weights *weights /* host */,
                      const uint16_t *x, void *out, int32_t *topk_idx_out, float *topk_w_out,
                      int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer writing into a bf16 residual stream (not on the pages: how a
+ * decoder consumes the layer; the survey's checkpoint-conformity step):
+ * out[t][h] = bf16(residual[t][h] + layer(x)[t][h]), the layer computed as in
+ * moe_layer (float32), the residual added in float32, then one
+ * round-to-nearest-even to bf16.  residual [T][H] bf16 is nullable (then 0)
+ * and may be the same buffer as out (an in-place update of the stream).
+ * Requires dims->out_dtype == MOE_BF16 (else MOE_ERR_UNSUPPORTED).  Decode
+ * (T <= 4) adds one small kernel after the layer kernel. */
+moe_status moe_layer_residual(const moe_dims *dims, const moe_weights *weights /* host */, const uint16_t *x,
+                              const uint16_t *residual, uint16_t *out, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /* Instrumentation variant of moe_layer: the same work, plus HIP events recorded
  * on `stream` around its kernels.  events (host array) holds

@@ -59,7 +59,7 @@ def test_workspace_size(lib):
 @pytest.mark.parametrize("field,value,status", [
     ("H", 100, -2), ("I", 96, -2), ("top_k", 0, -2), ("top_k", 300, -2), ("T", -1, -2), ("E", 0, -2),
     ("group", 32, -3), ("E", 512, -3), ("top_k", 9, -3), ("H", 32768, -3), ("I_shared", 1024, -3),
-    ("out_dtype", 0, -3), ("sb_dtype", 7, -2),
+    ("out_dtype", 5, -2), ("sb_dtype", 7, -2),
 ])
 def test_invalid_dims(lib, field, value, status):
     d = qwen_dims(8, **{field: value})
@@ -117,6 +117,22 @@ def test_shared_expert_gate_checks(lib):
     e = qwen_dims(0)
     assert lib.moe_shared_gate(C.byref(e), None, None, None, None) == 0
     assert lib.moe_combine_gated(C.byref(e), None, None, None, None, None, None) == 0
+
+
+def test_output_dtype_per_entry_point(lib):
+    """moe_layer writes float32 only; moe_layer_residual writes the bf16 residual stream only."""
+    w = _weights()
+    d32 = qwen_dims(8)
+    d16 = qwen_dims(8, out_dtype=bem.MOE_BF16)
+    need = bem.moe_workspace_size(d16)
+    assert need > 0 and bem.moe_workspace_size(d32) > 0
+    assert lib.moe_layer(C.byref(d16), C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -3
+    assert lib.moe_layer_residual(C.byref(d32), C.byref(w), FAKE, None, FAKE, FAKE, need, None) == -3
+    assert lib.moe_layer_residual(C.byref(d16), C.byref(w), FAKE, None, None, FAKE, need, None) == -1
+    assert lib.moe_layer_residual(C.byref(d16), C.byref(w), FAKE, FAKE + 2, FAKE, FAKE, need, None) == -4
+    assert lib.moe_layer_residual(C.byref(d16), C.byref(w), FAKE, None, FAKE, FAKE, need - 1, None) == -5
+    e = qwen_dims(0, out_dtype=bem.MOE_BF16)
+    assert lib.moe_layer_residual(C.byref(e), None, None, None, None, None, 0, None) == 0
 
 
 def test_empty_call_enqueues_nothing(lib):

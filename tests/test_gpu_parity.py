@@ -378,6 +378,36 @@ def test_shared_gate_and_gated_combine_steps():
     np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("T,H,E,k,I,bf16,res", [
+    (1, 2048, 256, 8, 512, True, "none"),      # decode
+    (1, 2048, 256, 8, 512, True, "inplace"),
+    (3, 2048, 256, 8, 512, True, "separate"),
+    (64, 2048, 256, 8, 512, True, "inplace"),  # prefill path
+    (600, 384, 16, 2, 192, True, "separate"),  # large-batch path
+    (16, 256, 16, 2, 64, False, "inplace"),    # tiny shapes, fp32 scales
+])
+def test_layer_into_bf16_residual_stream(T, H, E, k, I, bf16, res):
+    """moe_layer_residual: out = bf16(residual + layer).  Bar: the layer's own
+    2e-2 * RMS plus one bf16 rounding of the total (2^-8 relative)."""
+    cfg, w, x = _custom(T, H, E, k, I, I, bf16, seed=900 + T)
+    ref = oracle.moe_layer(w, x, k)["out"]
+    rng = np.random.default_rng(T + 7)
+    res_bits = moe_synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    total = ref + (moe_synth.bf16_bits_to_f32(res_bits).astype(np.float64) if res != "none" else 0.0)
+    m = bem()
+    lw = m.upload_weights(w)
+    res_t = m.bf16_tensor(res_bits) if res != "none" else None
+    out = m.moe_layer_residual(m.bf16_tensor(x), lw, k, residual=res_t, out=res_t if res == "inplace" else None)
+    torch.cuda.synchronize()
+    if res == "inplace":
+        assert out.data_ptr() == res_t.data_ptr()
+    got = moe_synth.bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    err = np.abs(got - total)
+    bound = TOL * rms(ref) + 2.0 ** -8 * np.abs(total)
+    print("bf16 residual T%d %s: max err/bound %.3f" % (T, res, float((err / bound).max())))
+    assert np.all(np.isfinite(got)) and np.all(err <= bound)
+
+
 def test_hot_expert_spans_many_tiles():
     bias = np.zeros(32, dtype=np.float32)
     bias[5] = 50.0
