@@ -45,7 +45,8 @@ inline int64_t max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
     return max_tiles(T, k, E, shared, kTileRows);
 }
 
-// Tokens (and experts) per workgroup of the layer's logits kernel, and the
+// Tokens (and experts) per workgroup of the layer's logits kernel (64: the
+// LDS-staged kernel for large batches; 32: the register-fed one), and the
 // number of K slices it splits the router product into (a power of two with
 // H / (64 S) whole; more slices for small batches, so that a few hundred
 // workgroups share the router's rows).  The logits workspace holds S x T x E

@@ -16,8 +16,10 @@
 // That single kernel serves the step-by-step moe_route call.  The whole-layer
 // call spreads the router over the chip instead (a workgroup reading the whole
 // 1 MiB router on its own is bound by one compute unit's bandwidth):
-//   - logits_kernel: one workgroup per (32 tokens, 32 experts); its four waves
-//     split K and sum through LDS; logits go to the workspace;
+//   - logits_kernel (small batches): one workgroup per (32 tokens, 32 experts,
+//     1/S of K); its four waves split K and sum through LDS; logits_staged_kernel
+//     (T >= 2048): one workgroup per (64 tokens, 64 experts), operands staged
+//     through LDS; partial logits go to the workspace;
 //   - topk_kernel: one wave per token sums and ranks its logits, writes the routing,
 //     counts the expert histogram (in LDS per 4 or 16 tokens, then one atomic
 //     per expert) and writes the float16 copy of the token's row (8-column blocks in dequantisation order) that the expert
@@ -105,9 +107,9 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
 // logits_kernel: one workgroup per (TM tokens, TM experts, 1/S of K).  Its four
 // waves split the workgroup's K range and sum through LDS; split z writes its
 // partial logits to partial[z][T][E] (split 0 adds the bias) and topk_kernel
-// sums the S splits in order.  TM = 64 for large batches (each x row and router
-// row is read by half as many workgroups), 32 with K split S ways for small
-// ones, so that the router's 1 MiB is spread over a few hundred workgroups.
+// sums the S splits in order.  It runs with TM = 32 for batches below 2048
+// tokens, with K split S ways so that the router's 1 MiB is spread over a few
+// hundred workgroups (larger batches use logits_staged_kernel below).
 template <int TM>
 __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                                                      const float* __restrict__ logit_bias, int T, int H, int E, int S,
@@ -203,6 +205,143 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict_
             if (z == 0 && logit_bias) v += logit_bias[e];
             partial[((size_t)z * T + t) * E + e] = v;
         }
+    }
+}
+
+// logits_staged_kernel: one workgroup per (64 tokens, 64 experts, 1/S of K),
+// for large batches.  Its eight waves load 64-column chunks of the 64 x rows
+// and the 64 router rows into LDS with direct loads (global_load_lds_dwordx4,
+// whole 128-byte row segments per 8 lanes), several chunks in flight.  Wave w
+// computes the 32 x 32 block (tokens 32 ((w / 2) % 2), experts 32 (w % 2)) on
+// K steps 2 (w / 4) and 2 (w / 4) + 1 of every chunk; the two waves of a block
+// add their sums through LDS at the end.  Two waves per SIMD let one wave's
+// LDS reads overlap the other's matrix products.  A row's 16-byte chunk c sits
+// at LDS position c ^ ((row / 2) % 8): the 16 rows that one LDS read cycle
+// serves fall on distinct banks.  The loads are waited for by count (the
+// compiler does not see the LDS reads, which are inline asm) and the stages
+// are handed over with bare barriers, so no wait for the loads still in
+// flight is inserted.
+constexpr int kStagedTile = 64;     // tokens and experts per workgroup
+constexpr int kStagedChunk = 64;    // K columns per stage
+constexpr int kStagedStages = 4;    // 64 KiB of LDS: three chunks in flight
+constexpr int kStagedThreads = 512;
+constexpr int kStagedRowBytes = kStagedChunk * 2;
+constexpr int kStagedOperandBytes = kStagedTile * kStagedRowBytes;  // 8 KiB
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+template <typename V>
+__device__ __forceinline__ void after_wait(V& v) {
+    asm volatile("" : "+v"(v));
+}
+__device__ __forceinline__ int staged_pos(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+__global__ __launch_bounds__(kStagedThreads) void logits_staged_kernel(const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ wr,
+                                                                       const float* __restrict__ logit_bias,
+                                                                       int T, int H, int E, int S,
+                                                                       float* __restrict__ partial,
+                                                                       int32_t* __restrict__ zero0,
+                                                                       int32_t* __restrict__ zero1) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kStagedStages][2][kStagedOperandBytes];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int t0 = blockIdx.x * kStagedTile, e0 = blockIdx.y * kStagedTile, z = blockIdx.z;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && z == 0) {
+        for (int i = tid; i < E; i += blockDim.x) {
+            if (zero0) __hip_atomic_store(zero0 + i * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (zero1) __hip_atomic_store(zero1 + i * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    const int kb = z * (H / S);
+    const int nc = H / (S * kStagedChunk);
+
+    // wave w fills rows 8 w .. 8 w + 7 of both operands: lane i -> row
+    // 8 w + i / 8, LDS position i % 8, which holds the row's chunk
+    // staged_pos(row, i % 8)
+    const int lr = 8 * wave + lane / 8;
+    const int lc = staged_pos(lr, lane % 8);
+    const uint16_t* a_src = x + (size_t)min(t0 + lr, T - 1) * H + kb + lc * 8;
+    const uint16_t* b_src = wr + (size_t)min(e0 + lr, E - 1) * H + kb + lc * 8;
+    auto issue = [&](int chunk, int stage) {
+        __builtin_amdgcn_global_load_lds(a_src + chunk * kStagedChunk, &smem[stage][0][wave * kWave * 16], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(b_src + chunk * kStagedChunk, &smem[stage][1][wave * kWave * 16], 16, 0, 0);
+    };
+
+    // MFMA operands: lane -> row lane % 32 of the wave's block, 16-byte chunk
+    // 2 s + lane / 32 of the stage for K step s of the wave's two
+    const int row = lane % 32, half = lane / 32;
+    const int mb = (wave / 2) % 2, nb = wave % 2, kh = wave / 4;
+    unsigned a_off[2], b_off[2];
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+        const int c = 2 * (2 * kh + s) + half;
+        const int ar = mb * 32 + row, br = nb * 32 + row;
+        a_off[s] = (unsigned)(ar * kStagedRowBytes + staged_pos(ar, c) * 16);
+        b_off[s] = (unsigned)(kStagedOperandBytes + br * kStagedRowBytes + staged_pos(br, c) * 16);
+    }
+    const unsigned lds0 = (unsigned)reinterpret_cast<uintptr_t>(&smem[0][0][0]);
+    constexpr unsigned kStageBytes = 2 * kStagedOperandBytes;
+
+    // chunks i + 1 .. i + kAhead - 1 stay in flight while chunk i is used
+    constexpr int kAhead = kStagedStages - 1;
+    floatx16 acc = floatx16{0};
+#pragma unroll
+    for (int c = 0; c < kAhead; c++) issue(min(c, nc - 1), c);
+    for (int i = 0; i < nc; i++) {
+        // this wave's loads of chunk i have landed (the two of each later
+        // chunk may be in flight); after the barrier every wave's have, and
+        // every wave is done reading chunk i - 1, whose stage the loads of
+        // chunk i + kAhead reuse (past the last chunk they reload it into a
+        // stage that is no longer read)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kAhead - 1)) : "memory");
+        asm volatile("s_barrier" ::: "memory");
+        issue(min(i + kAhead, nc - 1), (i + kAhead) % kStagedStages);
+        const unsigned base = lds0 + (unsigned)(i % kStagedStages) * kStageBytes;
+        u32x4 a[2], b[2];
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            a[s] = lds_read16(base + a_off[s]);
+            b[s] = lds_read16(base + b_off[s]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            after_wait(a[s]);
+            after_wait(b[s]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[s]),
+                                                          __builtin_bit_cast(bf16x8_t, b[s]), acc, 0, 0, 0);
+        }
+    }
+    // no load may still write LDS: the stages are reused for the sums below
+    // and must be quiet before the workgroup ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(&smem[0][0][0]);  // [4 blocks][16][64 lanes]
+    const int blk = wave % 4;
+    if (kh == 1) {
+#pragma unroll
+        for (int q = 0; q < 16; q++) red[(blk * 16 + q) * kWave + lane] = acc[q];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+
+    // C layout of 32x32 MFMA: lane holds column (lane % 32) = expert, rows
+    // 8 i + 4 (lane / 32) + j = tokens
+    const int e = e0 + nb * 32 + row;
+    if (e < E) {
+        const float bias = (z == 0 && logit_bias) ? logit_bias[e] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int q = 4 * i + j;
+                const int t = t0 + mb * 32 + 8 * i + 4 * half + j;
+                if (t < T) partial[((size_t)z * T + t) * E + e] = (acc[q] + red[(blk * 16 + q) * kWave + lane]) + bias;
+            }
     }
 }
 
@@ -303,8 +442,8 @@ hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* log
     const int S = logits_splits(T, H, E);
     const dim3 grid((T + tm - 1) / tm, (E + tm - 1) / tm, S);
     if (tm == 64)
-        hipLaunchKernelGGL(logits_kernel<64>, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E, S, logits, zero0,
-                           zero1);
+        hipLaunchKernelGGL(logits_staged_kernel, grid, dim3(kStagedThreads), 0, stream, x, wr, logit_bias, T, H, E, S, logits,
+                           zero0, zero1);
     else
         hipLaunchKernelGGL(logits_kernel<32>, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E, S, logits, zero0,
                            zero1);
