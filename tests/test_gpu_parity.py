@@ -423,6 +423,20 @@ def test_hot_expert_spans_many_tiles():
     assert_close(out, ref["out"], "hot expert")
 
 
+def test_large_batch_router_with_logit_bias():
+    """The LDS-staged router (T >= 2048) with K split in two: only split 0 adds
+    the bias; skewed routing from a Zipf-ranked per-expert offset."""
+    shape = moe_synth.Shape(T=2100, H=1024, E=256, top_k=8, I=64, I_shared=64, sb_bf16=True)
+    bias = moe_synth.zipf_bias(moe_synth.Config("custom", shape, seed=31), 3)
+    cfg, w, x = _custom(2100, 1024, 256, 8, 64, 64, True, seed=31, bias=bias)
+    ref = oracle.moe_layer(w, x, 8)
+    out, idx, wt, counts = run_layer(w, x, 8)
+    assert counts.max() > 4 * counts.mean()  # the offsets skew the routing
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out, ref["out"], "large-batch router with bias")
+
+
 def test_no_shared_expert():
     cfg, w, x = _custom(20, 256, 16, 2, 64, 64, True)
     w = {key: v for key, v in w.items() if not key.startswith("shared_")}
