@@ -361,6 +361,17 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
     const int t = blockIdx.x * kTW + wave;
     if (threadIdx.x < kMaxE) lh[threadIdx.x] = 0;
     __syncthreads();
+    // the first kXPre 16-byte blocks of each lane's part of the token's x row
+    // (all of it for H <= 2048) go out before the logits, so their latency
+    // overlaps the loads and the selection below
+    constexpr int kXPre = 4;
+    const int nblk = H / 8;
+    uint4 xr[kXPre];
+    {
+        const uint4* xrow = reinterpret_cast<const uint4*>(x + (size_t)min(t, T - 1) * H);
+#pragma unroll
+        for (int i = 0; i < kXPre; i++) xr[i] = xrow[min(lane + kWave * i, nblk - 1)];
+    }
     if (t < T) {
         const float* lt = logits + (size_t)t * E;
         const size_t split = (size_t)T * E;
@@ -396,10 +407,8 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
             // the float16 copy of the row; with a shared-expert gate g, also the
             // shared expert's weight sigmoid(x . g) (float32 sum of exact bf16
             // products, reduced over the wave)
-            const int nblk = H / 8;
             float z = 0.0f;
-            for (int blk = lane; blk < nblk; blk += kWave) {
-                const uint4 raw = reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk];
+            auto convert = [&](int blk, const uint4& raw) {
                 const uint16_t* hb = reinterpret_cast<const uint16_t*>(&raw);
                 half8_t o;
 #pragma unroll
@@ -411,7 +420,12 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
 #pragma unroll
                     for (int e = 0; e < 8; e++) z += bf16_to_f32(hb[e]) * bf16_to_f32(gb[e]);
                 }
-            }
+            };
+#pragma unroll
+            for (int i = 0; i < kXPre; i++)
+                if (lane + kWave * i < nblk) convert(lane + kWave * i, xr[i]);
+            for (int blk = lane + kWave * kXPre; blk < nblk; blk += kWave)
+                convert(blk, reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk]);
             if (sgate) {
 #pragma unroll
                 for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
