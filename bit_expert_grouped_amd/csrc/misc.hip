@@ -80,30 +80,37 @@ __device__ __forceinline__ uint4 residual_bf16x8(const float (&v)[8], const uint
 // bf16 residual stream instead, out16 = bf16(residual + sum) (residual
 // nullable, and it may be the same buffer as out16: each thread reads its 8
 // residuals before it writes them).
+template <int K, bool kShared>
 __global__ __launch_bounds__(256) void combine16_kernel(const _Float16* __restrict__ y16,
-                                                        const float* __restrict__ topk_w, int shared,
-                                                        const float* __restrict__ shared_w, int T, int H, int k,
+                                                        const float* __restrict__ topk_w,
+                                                        const float* __restrict__ shared_w, int T, int H,
                                                         float* __restrict__ out, const uint16_t* residual,
                                                         uint16_t* out16) {
     const int h8 = H / 8;
     const int64_t n = (int64_t)T * h8;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         const int t = (int)(i / h8), c = (int)(i % h8);
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < k; j++) {
-            const float w = topk_w[(size_t)t * k + j];
-            // each row is read exactly once: nontemporal loads and stores keep the
-            // stream from displacing other data in the caches
-            const half8_t y =
-                __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(y16 + ((size_t)t * k + j) * H) + c);
+        // all K routed rows (and the shared row) go out before the first add,
+        // so their latencies overlap; each row is read exactly once, so the
+        // loads and stores are nontemporal and do not displace other data
+        half8_t y[K + 1];
+        float w[K];
+        const float s = !kShared ? 0.0f : shared_w ? shared_w[t] : 1.0f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[e] += w * (float)y[e];
+        for (int j = 0; j < K; j++) {
+            w[j] = topk_w[(size_t)t * K + j];
+            y[j] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(y16 + ((size_t)t * K + j) * H) + c);
         }
-        if (shared) {
-            const half8_t y = reinterpret_cast<const half8_t*>(y16 + ((size_t)T * k + t) * H)[c];
-            const float s = shared_w ? shared_w[t] : 1.0f;
+        if (kShared)
+            y[K] = __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(y16 + ((size_t)T * K + t) * H) + c);
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[e] += s * (float)y[e];
+        for (int j = 0; j < K; j++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[e] += w[j] * (float)y[j][e];
+        if (kShared) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[e] += s * (float)y[K][e];
         }
         if (out16) {
             const size_t at = (size_t)t * H + 8 * (size_t)c;
@@ -163,8 +170,21 @@ hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool share
                             int H, int k, float* out, const uint16_t* residual, uint16_t* out16, hipStream_t stream) {
     const int64_t n = (int64_t)T * (H / 8);
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine16_kernel, dim3(grid_for(n)), dim3(256), 0, stream, y16, topk_w, shared ? 1 : 0,
-                       shared_w, T, H, k, out, residual, out16);
+#define BITMOE_COMBINE16(K)                                                                                  \
+    case K:                                                                                                  \
+        if (shared)                                                                                          \
+            hipLaunchKernelGGL((combine16_kernel<K, true>), dim3(grid_for(n)), dim3(256), 0, stream, y16,     \
+                               topk_w, shared_w, T, H, out, residual, out16);                                \
+        else                                                                                                 \
+            hipLaunchKernelGGL((combine16_kernel<K, false>), dim3(grid_for(n)), dim3(256), 0, stream, y16,    \
+                               topk_w, shared_w, T, H, out, residual, out16);                                \
+        break;
+    switch (k) {
+        BITMOE_COMBINE16(1) BITMOE_COMBINE16(2) BITMOE_COMBINE16(3) BITMOE_COMBINE16(4)
+        BITMOE_COMBINE16(5) BITMOE_COMBINE16(6) BITMOE_COMBINE16(7) BITMOE_COMBINE16(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef BITMOE_COMBINE16
     return hipGetLastError();
 }
 

@@ -154,6 +154,10 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
     __shared__ int tmp[kThreads / kWave];
     const int tid = threadIdx.x;
     const int n = T * k;
+    // this thread's slot goes out first: its load overlaps the counts' loads
+    // and the scan below
+    const int s = blockIdx.x * kThreads + tid;
+    const int e = topk_idx[min(s, n - 1)];
     if (tid < kMaxE) local[tid] = 0;
     const int c =
         tid < E ? __hip_atomic_load(hist + tid * kCounterStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
@@ -179,9 +183,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
     __syncthreads();
     // rank each slot among this workgroup's slots of its expert (LDS atomics),
     // then reserve the workgroup's run of each expert with one global atomic
-    const int s = blockIdx.x * kThreads + tid;
-    const int e = s < n ? topk_idx[s] : -1;
-    const bool valid = e >= 0 && e < E;
+    const bool valid = s < n && e >= 0 && e < E;
     const int rank = valid ? atomicAdd(&local[e], 1) : 0;
     __syncthreads();
     if (tid < E && local[tid] > 0) local[tid] = off[tid] + atomicAdd(cursor + tid * kCounterStride, local[tid]);
