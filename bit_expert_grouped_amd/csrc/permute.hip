@@ -186,7 +186,10 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
     const bool valid = s < n && e >= 0 && e < E;
     const int rank = valid ? atomicAdd(&local[e], 1) : 0;
     __syncthreads();
-    if (tid < E && local[tid] > 0) local[tid] = off[tid] + atomicAdd(cursor + tid * kCounterStride, local[tid]);
+    // a lone workgroup holds every slot: its runs start at the offsets, with
+    // no global cursor to reserve them from
+    if (tid < E && local[tid] > 0)
+        local[tid] = off[tid] + (gridDim.x == 1 ? 0 : atomicAdd(cursor + tid * kCounterStride, local[tid]));
     __syncthreads();
     if (valid) sorted_slot[local[e] + rank] = s;
 }
