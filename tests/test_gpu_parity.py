@@ -423,6 +423,20 @@ def test_hot_expert_spans_many_tiles():
     assert_close(out, ref["out"], "hot expert")
 
 
+@pytest.mark.parametrize("k", [4, 5, 6, 7])
+def test_every_top_k_width(k):
+    """The combine is specialised per k (1..8): the widths the other cases do
+    not reach, each with and without the shared expert."""
+    cfg, w, x = _custom(45, 256, 24, k, 64, 64, True, seed=900 + k)
+    for shared in (True, False):
+        wk = w if shared else {key: v for key, v in w.items() if not key.startswith("shared_")}
+        ref = oracle.moe_layer(wk, x, k)
+        out, idx, wt, counts = run_layer(wk, x, k)
+        assert_same_routing(idx, wt, ref["idx"], ref["w"])
+        np.testing.assert_array_equal(counts, ref["counts"])
+        assert_close(out, ref["out"], "k=%d shared=%s" % (k, shared))
+
+
 def test_large_batch_router_with_logit_bias():
     """The LDS-staged router (T >= 2048) with K split in two: only split 0 adds
     the bias; skewed routing from a Zipf-ranked per-expert offset."""
