@@ -181,7 +181,7 @@ moe_status moe_layer(const moe_dims *dims, const moe_weights *weights /* host */
                      int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* moe_layer writing into a bf16 residual stream (not on the pages: how a
- * decoder consumes the layer; the survey's checkpoint-conformity step):
+ * decoder consumes the layer, a real-checkpoint detail):
  * out[t][h] = bf16(residual[t][h] + layer(x)[t][h]), the layer computed as in
  * moe_layer (float32), the residual added in float32, then one
  * round-to-nearest-even to bf16.  residual [T][H] bf16 is nullable (then 0)
