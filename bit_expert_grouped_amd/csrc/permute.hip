@@ -55,29 +55,71 @@ __device__ int block_inclusive_scan(int v, int* tmp, int* total = nullptr) {
 // fewer), so the grouped products start the long work first and end on short
 // tiles.  Tiles beyond `cap` (the workspace capacity) are dropped, so
 // inconsistent caller offsets cannot write outside the tile array.
-__device__ void write_tiles(int g_rows, int row_base, int* tmp, Tile* tiles, int32_t* n_tiles, int cap, int tr) {
-    const int n = max(g_rows, 0);
+//
+// The positions are exclusive scans of each height class's tile counts over
+// the groups, one class per wave, all classes at once: lane l of wave q sums
+// groups 5 l .. 5 l + 4 of class q, and one wave-wide scan of those sums gives
+// every group's start within the class.
+constexpr int kTileGroups = kMaxE + 1;                      // routed experts + the shared one
+constexpr int kGroupsPerLane = (kTileGroups + kWave - 1) / kWave;  // 5
+constexpr int kMaxClasses = kTileRows / 32;                 // 4
+
+__device__ void write_tiles(int g_rows, int row_base, Tile* tiles, int32_t* n_tiles, int cap, int tr) {
+    __shared__ int cnt[kMaxClasses][kGroupsPerLane * kWave];
+    __shared__ int start[kMaxClasses][kGroupsPerLane * kWave];
+    __shared__ int total[kMaxClasses];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int nq = tr / 32;  // class q holds tiles of 32 (nq - q) rows
+    const int n = tid < kTileGroups ? max(g_rows, 0) : 0;
     const int full = n / tr, rem = n % tr;
-    const int mt_rem = (rem + 31) / 32;  // 0 .. tr / 32
+    const int mt_rem = (rem + 31) / 32;  // 0 .. nq
+    auto count = [&](int q) { return (q == 0 ? full : 0) + (mt_rem == nq - q ? 1 : 0); };
+    for (int i = tid; i < kGroupsPerLane * kWave; i += blockDim.x)
+        for (int q = 0; q < nq; q++) cnt[q][i] = 0;
+    __syncthreads();
+    if (tid < kTileGroups)
+        for (int q = 0; q < nq; q++) cnt[q][tid] = count(q);
+    __syncthreads();
+    if (wave < nq) {
+        const int q = wave;
+        int v[kGroupsPerLane], sum = 0;
+#pragma unroll
+        for (int i = 0; i < kGroupsPerLane; i++) {
+            v[i] = cnt[q][lane * kGroupsPerLane + i];
+            sum += v[i];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        int run = incl - sum;
+#pragma unroll
+        for (int i = 0; i < kGroupsPerLane; i++) {
+            start[q][lane * kGroupsPerLane + i] = run;
+            run += v[i];
+        }
+        if (lane == kWave - 1) total[q] = incl;
+    }
+    __syncthreads();
     int first_of_class = 0;
-    // classes: tr/32 (full tiles and remainders of that height), then shorter remainders
-    for (int c = tr / 32; c >= 1; c--) {
-        const int cnt = (c == tr / 32 ? full : 0) + (mt_rem == c ? 1 : 0);
-        int total;
-        const int incl = block_inclusive_scan(cnt, tmp, &total);
-        int pos = first_of_class + incl - cnt;
-        for (int j = 0; j < cnt && pos < cap; j++, pos++) {
-            const bool is_rem = j == cnt - 1 && mt_rem == c;
+    for (int q = 0; q < nq; q++) {
+        const int c = count(q);
+        int pos = first_of_class + (tid < kTileGroups ? start[q][tid] : 0);
+        for (int j = 0; j < c && pos < cap; j++, pos++) {
+            const bool is_rem = j == c - 1 && mt_rem == nq - q;
             Tile t;
-            t.group = threadIdx.x;
+            t.group = tid;
             t.row0 = row_base + (is_rem ? full : j) * tr;
             t.rows = is_rem ? rem : tr;
             t.pad = 0;
             tiles[pos] = t;
         }
-        first_of_class += total;
+        first_of_class += total[q];
     }
-    if (threadIdx.x == 0) *n_tiles = min(first_of_class, cap);
+    if (tid == 0) *n_tiles = min(first_of_class, cap);
+    __syncthreads();  // the LDS arrays may be reused by a following call
 }
 
 __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ topk_idx, int T,
@@ -110,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     if (tid == E - 1) offsets[E] = incl;
     const int g_rows = tid < E ? c : ((tid == E && shared) ? T : 0);
     const int row_base = tid < E ? excl : n;
-    write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap, kTileRows);
+    write_tiles(g_rows, row_base, tiles, n_tiles, cap, kTileRows);
     __syncthreads();
     for (int s = tid; s < n; s += kThreads) {
         const int e = topk_idx[s];
@@ -121,7 +163,6 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
 __global__ __launch_bounds__(kThreads) void tiles_kernel(const int32_t* __restrict__ offsets, int T, int k,
                                                          int E, int shared, Tile* __restrict__ tiles,
                                                          int32_t* __restrict__ n_tiles, int cap) {
-    __shared__ int tmp[kThreads / kWave];
     const int tid = threadIdx.x;
     int g_rows = 0, row_base = T * k;
     if (tid < E) {
@@ -130,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void tiles_kernel(const int32_t* __restri
     } else if (tid == E && shared) {
         g_rows = T;
     }
-    write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap, kTileRows);
+    write_tiles(g_rows, row_base, tiles, n_tiles, cap, kTileRows);
 }
 
 // The layer's permute after topk_kernel has counted the histogram: every
@@ -172,13 +213,13 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
         if (tid == E - 1) offsets[E] = incl;
         const int g_rows = tid < E ? c : ((tid == E && shared) ? T : 0);
         const int row_base = tid < E ? excl : n;
-        write_tiles(g_rows, row_base, tmp, tiles, n_tiles, cap, tr);
+        write_tiles(g_rows, row_base, tiles, n_tiles, cap, tr);
     }
     // the second map from workgroup 1 (0 if alone), beside workgroup 0's
     if (tiles2 && blockIdx.x == (gridDim.x > 1 ? 1u : 0u)) {
         const int g_rows = tid < E ? c : ((tid == E && shared) ? T : 0);
         const int row_base = tid < E ? excl : n;
-        write_tiles(g_rows, row_base, tmp, tiles2, n_tiles2, cap2, 64);
+        write_tiles(g_rows, row_base, tiles2, n_tiles2, cap2, 64);
     }
     __syncthreads();
     // rank each slot among this workgroup's slots of its expert (LDS atomics),
