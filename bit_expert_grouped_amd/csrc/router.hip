@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kStagedThreads) void logits_staged_kernel(const uin
 
 // kTW tokens per top-k workgroup: 16 for large batches (fewer atomics on hot
 // experts' counters), 4 for small ones (more workgroups in flight)
-template <int kTW>
+template <int kTW, bool kGate>
 __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restrict__ logits, int S,
                                                    const uint16_t* __restrict__ x, int T, int H, int E, int top_k,
                                                    int32_t* __restrict__ topk_idx,
@@ -366,11 +366,14 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
     // overlaps the loads and the selection below
     constexpr int kXPre = 4;
     const int nblk = H / 8;
-    uint4 xr[kXPre];
+    uint4 xr[kXPre], gr[kXPre];
     {
         const uint4* xrow = reinterpret_cast<const uint4*>(x + (size_t)min(t, T - 1) * H);
 #pragma unroll
-        for (int i = 0; i < kXPre; i++) xr[i] = xrow[min(lane + kWave * i, nblk - 1)];
+        for (int i = 0; i < kXPre; i++) {
+            xr[i] = xrow[min(lane + kWave * i, nblk - 1)];
+            if (kGate) gr[i] = reinterpret_cast<const uint4*>(sgate)[min(lane + kWave * i, nblk - 1)];
+        }
     }
     if (t < T) {
         const float* lt = logits + (size_t)t * E;
@@ -408,14 +411,13 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
             // shared expert's weight sigmoid(x . g) (float32 sum of exact bf16
             // products, reduced over the wave)
             float z = 0.0f;
-            auto convert = [&](int blk, const uint4& raw) {
+            auto convert = [&](int blk, const uint4& raw, const uint4& graw) {
                 const uint16_t* hb = reinterpret_cast<const uint16_t*>(&raw);
                 half8_t o;
 #pragma unroll
                 for (int e = 0; e < 8; e++) o[e] = (_Float16)bf16_to_f32(hb[nibble_of(e)]);
                 reinterpret_cast<half8_t*>(x16 + (size_t)t * H)[blk] = o;
-                if (sgate) {
-                    const uint4 graw = reinterpret_cast<const uint4*>(sgate)[blk];
+                if (kGate) {
                     const uint16_t* gb = reinterpret_cast<const uint16_t*>(&graw);
 #pragma unroll
                     for (int e = 0; e < 8; e++) z += bf16_to_f32(hb[e]) * bf16_to_f32(gb[e]);
@@ -423,10 +425,12 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
             };
 #pragma unroll
             for (int i = 0; i < kXPre; i++)
-                if (lane + kWave * i < nblk) convert(lane + kWave * i, xr[i]);
-            for (int blk = lane + kWave * kXPre; blk < nblk; blk += kWave)
-                convert(blk, reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk]);
-            if (sgate) {
+                if (lane + kWave * i < nblk) convert(lane + kWave * i, xr[i], kGate ? gr[i] : xr[i]);
+            for (int blk = lane + kWave * kXPre; blk < nblk; blk += kWave) {
+                const uint4 raw = reinterpret_cast<const uint4*>(x + (size_t)t * H)[blk];
+                convert(blk, raw, kGate ? reinterpret_cast<const uint4*>(sgate)[blk] : raw);
+            }
+            if (kGate) {
 #pragma unroll
                 for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
                 if (lane == 0) shared_w[t] = 1.0f / (1.0f + expf(-z));
@@ -469,12 +473,17 @@ hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int
                        hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     const int S = logits_splits(T, H, E);
-    if (T >= 1024)
-        hipLaunchKernelGGL(topk_kernel<16>, dim3((T + 15) / 16), dim3(16 * kWave), 0, stream, logits, S, x, T, H, E,
-                           top_k, topk_idx, topk_w, hist, x16, sgate, shared_w);
-    else
-        hipLaunchKernelGGL(topk_kernel<4>, dim3((T + 3) / 4), dim3(4 * kWave), 0, stream, logits, S, x, T, H, E, top_k,
-                           topk_idx, topk_w, hist, x16, sgate, shared_w);
+    // the gate's dot product needs the f16 copy's pass over x
+    if (sgate && !x16) return hipErrorInvalidValue;
+#define BITMOE_TOPK(TW, GATE)                                                                              \
+    hipLaunchKernelGGL((topk_kernel<TW, GATE>), dim3((T + TW - 1) / TW), dim3(TW * kWave), 0, stream, logits, S, x, \
+                       T, H, E, top_k, topk_idx, topk_w, hist, x16, sgate, shared_w)
+    if (T >= 1024) {
+        if (sgate) BITMOE_TOPK(16, true); else BITMOE_TOPK(16, false);
+    } else {
+        if (sgate) BITMOE_TOPK(4, true); else BITMOE_TOPK(4, false);
+    }
+#undef BITMOE_TOPK
     return hipGetLastError();
 }
 
