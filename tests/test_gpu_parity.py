@@ -437,6 +437,23 @@ def test_every_top_k_width(k):
         assert_close(out, ref["out"], "k=%d shared=%s" % (k, shared))
 
 
+@pytest.mark.parametrize("T", [37, 600, 2100])
+def test_prefill_path_is_bitwise_reproducible(T):
+    """Slots of one expert land in atomic order, but every row's products run
+    in a fixed K order and the combine adds in slot order, so two calls give
+    identical bits (the decode kernel's float32 atomics do not promise this)."""
+    cfg, w, x = _custom(T, 512, 64, 8, 128, 128, True, seed=950 + T)
+    m = bem()
+    lw = m.upload_weights(w)
+    xt = m.bf16_tensor(x)
+    outs = []
+    for _ in range(3):
+        outs.append(m.moe_layer(xt, lw, 8).cpu().numpy())
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+
+
 def test_large_batch_router_with_logit_bias():
     """The LDS-staged router (T >= 2048) with K split in two: only split 0 adds
     the bias; skewed routing from a Zipf-ranked per-expert offset."""
