@@ -281,6 +281,7 @@ def _custom(T, H, E, k, I, Is, bf16=True, seed=77, bias=None):
     # large-batch router (T >= 2048): LDS-staged 64 x 64 logit tiles with K split S ways
     (2100, 1024, 256, 8, 64, True),    # ragged last token tile, S = 2 (8 chunks of 64 columns)
     (2100, 256, 40, 3, 64, False),     # one 64-expert tile with 24 clamped rows, S = 4 (one chunk)
+    (2050, 192, 48, 2, 64, True),      # H = 192: S = 1 with an odd count of 3 chunks; a 2-token last tile
 ])
 def test_edge_shapes(T, H, E, k, I, bf16):
     cfg, w, x = _custom(T, H, E, k, I, I, bf16)
