@@ -48,6 +48,7 @@ KIND_UP_Q, KIND_UP_S, KIND_UP_B = 5, 6, 7
 KIND_DOWN_Q, KIND_DOWN_S, KIND_DOWN_B = 8, 9, 10
 KIND_ZIPF_RANK = 11
 KIND_SHARED_EXPERT_GATE = 12
+KIND_ROUTER_Q8_Q, KIND_ROUTER_Q8_S, KIND_ROUTER_Q8_B = 13, 14, 15
 KIND_X = 100
 SHARED_EXPERT = 1 << 20  # expert slot used in seed sequences for the shared expert
 
@@ -167,6 +168,25 @@ def shared_expert_gate(cfg: Config, layer: int = 0) -> np.ndarray:
     gated shared expert add it to a layer's weights under "shared_expert_gate".
     """
     return _normal(_rng(cfg.seed, layer, KIND_SHARED_EXPERT_GATE, 0), ROUTER_STD, (cfg.shape.H,))
+
+
+def router_q8(cfg: Config, layer: int = 0) -> dict:
+    """An 8-bit router in the MLX affine layout (4 codes per uint32 word, low
+    byte first; a scale and a bias per 64 columns in the config's scale dtype).
+
+    Codes are uniform bytes; scales ~U(1.5e-4, 2.5e-4) and biases near
+    -127.5 * scale, so the restored weights spread like the dense router's
+    N(0, 0.02).  An optional checkpoint detail the configs do not use.
+    """
+    sh = cfg.shape
+    E, H = sh.E, sh.H
+    q = _words(_rng(cfg.seed, layer, KIND_ROUTER_Q8_Q, 0), (E, H // 4))
+    s = _rng(cfg.seed, layer, KIND_ROUTER_Q8_S, 0).uniform(1.5e-4, 2.5e-4, size=(E, H // GROUP))
+    b = -127.5 * s + _rng(cfg.seed, layer, KIND_ROUTER_Q8_B, 0).uniform(-2e-3, 2e-3, size=(E, H // GROUP))
+    s, b = s.astype(np.float32), b.astype(np.float32)
+    if sh.sb_bf16:
+        s, b = f32_to_bf16_bits(s), f32_to_bf16_bits(b)
+    return {"router_q8": q, "router_scale": s, "router_bias": b}
 
 
 def layer_weights(cfg: Config, layer: int = 0) -> dict:

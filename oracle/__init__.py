@@ -60,6 +60,8 @@ def lib():
         L.oracle_code.restype = i32
         L.oracle_dequant.argtypes = [C.POINTER(QMat), P]
         L.oracle_dequant.restype = None
+        L.oracle_router_dequant_q8.argtypes = [i32, i32, P, P, P, i32, P]
+        L.oracle_router_dequant_q8.restype = None
         L.oracle_router_logits.argtypes = [i32, i32, i32, P, P, P, P]
         L.oracle_router_logits.restype = None
         L.oracle_select.argtypes = [i32, i32, i32, P, P, P]
@@ -115,6 +117,27 @@ def dequant(q, s, b, group=64):
     W = np.empty((m.N, m.K), dtype=np.float64)
     lib().oracle_dequant(C.byref(m), W.ctypes.data)
     return W
+
+
+def router_dequant_q8(codes, scale, bias):
+    """8-bit router (R16): codes [E][H/4] uint32, scale/bias [E][H/64] (bf16 bits
+    as uint16, or float32) -> the bfloat16 router [E][H] as uint16 bits."""
+    codes = _c(codes, np.uint32)
+    sb_bf16 = np.asarray(scale).dtype == np.uint16
+    dt = np.uint16 if sb_bf16 else np.float32
+    scale, bias = _c(scale, dt), _c(bias, dt)
+    E, H = codes.shape[0], codes.shape[1] * 4
+    out = np.empty((E, H), dtype=np.uint16)
+    lib().oracle_router_dequant_q8(E, H, codes.ctypes.data, scale.ctypes.data, bias.ctypes.data, int(sb_bf16),
+                                   out.ctypes.data)
+    return out
+
+
+def layer_router(weights):
+    """The layer's bfloat16 router: the dense one, or the 8-bit one restored (R16)."""
+    if weights.get("router_q8") is not None:
+        return router_dequant_q8(weights["router_q8"], weights["router_scale"], weights["router_bias"])
+    return weights["router"]
 
 
 def router_logits(x, router, logit_bias=None):
@@ -195,7 +218,7 @@ def moe_layer(weights: dict, x, top_k: int, group: int = 64, tokens=None, want_l
     """
     x = _c(x, np.uint16)
     T, H = x.shape
-    router = _c(weights["router"], np.uint16)
+    router = _c(layer_router(weights), np.uint16)
     E = router.shape[0]
     gq = _c(weights["gate_q"], np.uint32)
     I = gq.shape[1]

@@ -41,6 +41,14 @@
  *      shared expert: a bfloat16 vector g [H] scales the shared expert's
  *      output by sigmoid(sum_h x[t][h] * g[h]); without g the weight is one (R5).
  *      This is the shared-expert gate of Qwen's mixture-of-experts checkpoints.
+ *   R16 (checkpoint conformity, not on the pages) an optional 8-bit router in
+ *      the MLX affine layout: byte k of a row sits at bits [8*(k%4), 8*(k%4)+8)
+ *      of word k/4, groups of 64 columns carry a scale and a bias, and the
+ *      router weight is the float32 fused multiply-add scale * code + bias
+ *      rounded to bfloat16 (nearest, ties to even); the scores then follow R1
+ *      with that bfloat16 matrix.  The router is restored to the precision the
+ *      dense router has, so both sides take every ranking decision on the
+ *      same matrix.
  */
 #include <math.h>
 #include <stdint.h>
@@ -104,6 +112,34 @@ void oracle_dequant(const oracle_qmat *m, double *W)
             W[(size_t)n * (size_t)m->K + (size_t)k] = s * (double)oracle_code(m, n, k) + b;
         }
     }
+}
+
+/* float32 -> bfloat16 bits, nearest with ties to even (finite inputs). */
+static uint16_t f32_to_bf16_nearest_even(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint32_t lower = u & 0xFFFFu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1;
+    return (uint16_t)upper;
+}
+
+/* The 8-bit router restored to bfloat16: out[e][h] = bf16(fmaf(s, q, b)) with
+ * q byte h % 4 of word [e][h / 4] and (s, b) of group h / 64: R16. */
+void oracle_router_dequant_q8(int32_t E, int32_t H, const uint32_t *codes, const void *scale,
+                              const void *bias, int32_t sb_bf16, uint16_t *out)
+{
+    const int32_t groups = H / 64;
+    for (int32_t e = 0; e < E; e++)
+        for (int32_t h = 0; h < H; h++) {
+            const uint32_t word = codes[(size_t)e * (H / 4) + h / 4];
+            const uint32_t q = (word >> (8 * (h % 4))) & 0xFFu;
+            const float sv = (float)sb_value(scale, sb_bf16, (size_t)e * groups + h / 64);
+            const float bv = (float)sb_value(bias, sb_bf16, (size_t)e * groups + h / 64);
+            out[(size_t)e * H + h] = f32_to_bf16_nearest_even(fmaf(sv, (float)q, bv));
+        }
 }
 
 /* Router logits l[t][e] = sum_h x[t][h] * router[e][h] (+ logit_bias[e]): R1, R3. */

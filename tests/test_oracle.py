@@ -407,3 +407,49 @@ def test_generator_formats():
     w1 = moe_synth.layer_weights(moe_synth.CONFIGS["tiny"])
     np.testing.assert_array_equal(w1["up_q"], w["up_q"])
     assert math.isclose(moe_synth.bf16_bits_to_f32(np.array([0x3F80], np.uint16))[0], 1.0)
+
+
+# ---------------------------------------------------------------- 8-bit router (R16)
+
+@pytest.mark.parametrize("ex", _load("router_q8_examples.json")["cases"], ids=lambda e: e["what"][:24])
+def test_router_q8_hand_examples(ex):
+    codes = np.zeros((1, 16), dtype=np.uint32)  # one row of 64 columns: one group
+    codes[0, 0] = ex["word"]
+    for bf16_sb in (True, False):
+        sc = np.array([[ex["scale"]]], dtype=np.float32)
+        bi = np.array([[ex["bias"]]], dtype=np.float32)
+        if bf16_sb:
+            sc, bi = moe_synth.f32_to_bf16_bits(sc), moe_synth.f32_to_bf16_bits(bi)
+        w = moe_synth.bf16_bits_to_f32(oracle.router_dequant_q8(codes, sc, bi))
+        np.testing.assert_array_equal(w[0, :4], np.array(ex["weights"], dtype=np.float32))
+        np.testing.assert_array_equal(w[0, 4:], np.float32(ex["bias"]))  # code 0 restores the bias
+
+
+def test_router_q8_against_brute_force():
+    """Every byte, scale and bias position: bf16 scales and biases make
+    s * q + b exact in float64, so one rounding to float32 is the fused
+    multiply-add's, then nearest-even to bfloat16."""
+    cfg = small_cfg(T=2, E=5, k=2)
+    r = moe_synth.router_q8(cfg, 3)
+    got = oracle.router_dequant_q8(r["router_q8"], r["router_scale"], r["router_bias"])
+    E, H = got.shape
+    q = np.stack([(r["router_q8"] >> (8 * i)) & 0xFF for i in range(4)], axis=-1).reshape(E, H).astype(np.float64)
+    s = np.repeat(moe_synth.bf16_bits_to_f32(r["router_scale"]).astype(np.float64), 64, axis=1)
+    b = np.repeat(moe_synth.bf16_bits_to_f32(r["router_bias"]).astype(np.float64), 64, axis=1)
+    want = moe_synth.f32_to_bf16_bits((s * q + b).astype(np.float32))
+    np.testing.assert_array_equal(got, want)
+    assert np.abs(moe_synth.bf16_bits_to_f32(got)).max() < 0.06  # spread like the dense router
+
+
+def test_layer_with_q8_router_uses_the_restored_matrix():
+    cfg = small_cfg(T=7, E=6, k=2)
+    w = moe_synth.layer_weights(cfg)
+    x = moe_synth.token_rows(cfg)
+    wq = dict(w)
+    wq.update(moe_synth.router_q8(cfg, 0))
+    wq["router"] = None
+    dense = dict(w)
+    dense["router"] = oracle.router_dequant_q8(wq["router_q8"], wq["router_scale"], wq["router_bias"])
+    a, b = oracle.moe_layer(wq, x, 2), oracle.moe_layer(dense, x, 2)
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    np.testing.assert_array_equal(a["out"], b["out"])

@@ -36,6 +36,9 @@ MUTATIONS = {
     "router row index wrong": ("bf16_bits_value(router[(size_t)e * H + h])", "bf16_bits_value(router[(size_t)((e + 1) % E) * H + h])"),
     "shared gate sign flipped": ("s[t] = 1.0 / (1.0 + exp(-z));", "s[t] = 1.0 / (1.0 + exp(z));"),
     "shared gate ignored": ("(shared_w ? shared_w[t] : 1.0)", "(shared_w ? 1.0 : 1.0)"),
+    "q8 router byte order reversed": ("(word >> (8 * (h % 4)))", "(word >> (8 * (3 - h % 4)))"),
+    "q8 router ties rounded up": ("(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
+    "q8 router scale and bias swapped": ("fmaf(sv, (float)q, bv)", "fmaf(bv, (float)q, sv)"),
     "permute not stable": ("sorted_slot[cursor[idx[s]]++] = s;", "sorted_slot[offsets[idx[s] + 1] - 1 - (cursor[idx[s]]++ - offsets[idx[s]])] = s;"),
 }
 
