@@ -21,7 +21,7 @@ MOE_BF16, MOE_F32 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_shared_gate",
-           "moe_combine_gated", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
+           "moe_combine_gated", "moe_router_dequant", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
            "moe_status_string")
 
 
@@ -46,7 +46,8 @@ class Ffn(C.Structure):
 
 class Weights(C.Structure):
     _fields_ = [("router", C.c_void_p), ("logit_bias", C.c_void_p), ("experts", Ffn), ("shared", Ffn),
-                ("shared_expert_gate", C.c_void_p)]
+                ("shared_expert_gate", C.c_void_p), ("router_q8", C.c_void_p), ("router_scale", C.c_void_p),
+                ("router_bias", C.c_void_p)]
 
 
 _lib = None
@@ -70,6 +71,7 @@ def lib():
         L.moe_combine.argtypes = [D, P, P, P, P, P]
         L.moe_combine_gated.argtypes = [D, P, P, P, P, P, P]
         L.moe_shared_gate.argtypes = [D, P, P, P, P]
+        L.moe_router_dequant.argtypes = [D, P, P, P, P, P]
         L.moe_layer.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P]
         L.moe_layer_residual.argtypes = [D, C.POINTER(Weights), P, P, P, P, C.c_size_t, P]
         L.moe_layer_events.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P, P, C.c_int32]
@@ -145,8 +147,9 @@ class LayerWeights:
         self.experts = Ffn(qm("", "gate"), qm("", "up"), qm("", "down"))
         self.shared = (Ffn(qm("shared_", "gate"), qm("shared_", "up"), qm("shared_", "down"))
                        if self.I_shared else Ffn())
-        self.struct = Weights(_p(tensors["router"]), _p(tensors.get("logit_bias")), self.experts, self.shared,
-                              _p(tensors.get("shared_expert_gate")))
+        self.struct = Weights(_p(tensors.get("router")), _p(tensors.get("logit_bias")), self.experts, self.shared,
+                              _p(tensors.get("shared_expert_gate")), _p(tensors.get("router_q8")),
+                              _p(tensors.get("router_scale")), _p(tensors.get("router_bias")))
 
     def dims(self, T, top_k) -> Dims:
         return dims(T, self.H, self.E, top_k, self.I, self.I_shared, self.sb_bf16)
@@ -257,6 +260,19 @@ def moe_shared_gate(x, gate, shared_w=None):
         shared_w = torch.empty(T, dtype=torch.float32, device=x.device)
     _check(lib().moe_shared_gate(C.byref(d), _p(x), _p(gate), _p(shared_w), _stream()), "moe_shared_gate")
     return shared_w
+
+
+def moe_router_dequant(router_q8, scale, bias, out=None):
+    """The 8-bit router (codes [E][H/4] int32, scale/bias [E][H/64]) restored to bf16 [E][H]."""
+    import torch
+
+    E, H = router_q8.shape[0], router_q8.shape[1] * 4
+    d = dims(1, H, E, 1, 64, 0, scale.element_size() == 2)
+    if out is None:
+        out = torch.empty(E, H, dtype=torch.bfloat16, device=router_q8.device)
+    _check(lib().moe_router_dequant(C.byref(d), _p(router_q8), _p(scale), _p(bias), _p(out), _stream()),
+           "moe_router_dequant")
+    return out
 
 
 def moe_layer_residual(x, weights: "LayerWeights", top_k, residual=None, out=None, ws=None):

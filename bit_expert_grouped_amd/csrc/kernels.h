@@ -60,6 +60,11 @@ inline int logits_splits(int64_t T, int64_t H, int64_t E) {
     return S;
 }
 
+// An 8-bit router (four codes per word, low byte first; a scale and a bias per
+// 64 columns) restored to bf16: out = bf16_nearest_even(fmaf(s, code, b)).
+hipError_t launch_router_dequant(const uint32_t* q, const void* s, const void* b, bool sb_bf16, int E, int H,
+                                 uint16_t* out, hipStream_t stream);
+
 // Router + top-k in one kernel (32 tokens x all experts per workgroup).
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H,
                          int E, int top_k, int32_t* topk_idx, float* topk_w, hipStream_t stream);

@@ -38,7 +38,7 @@ moe_status check_dims(const moe_dims* d) {
 struct Layout {
     size_t ctl, xch, sel, hbuf;                          // decode region
     size_t x16, h, y16, logits, hist, cursor;            // prefill buffers
-    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, shared_w, yacc, total;
+    size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, shared_w, yacc, router16, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -92,6 +92,8 @@ Layout layout_of(const moe_dims* d) {
     o = up256(o + T * 4);
     L.yacc = o;  // decode with a bf16 output: the float32 layer output before the residual add
     o = up256(o + (T <= (size_t)kDecodeMaxT ? T * H * 4 : 0));
+    L.router16 = o;  // an 8-bit router restored to bf16 [E][H]
+    o = up256(o + E * H * 2);
     L.total = o;
     return L;
 }
@@ -271,6 +273,14 @@ moe_status moe_shared_gate(const moe_dims* d, const uint16_t* x, const uint16_t*
 
 namespace {
 
+moe_status moe_router_dequant(const moe_dims* d, const uint32_t* router_q8, const void* scale, const void* bias,
+                              uint16_t* router_out, hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    MOE_TRY(check_ptrs({router_q8, scale, bias, router_out}));
+    HIP_TRY(launch_router_dequant(router_q8, scale, bias, d->sb_dtype == MOE_BF16, d->E, d->H, router_out, stream));
+    return MOE_OK;
+}
+
 const char* const kPrefillStages[] = {"router", "topk", "permute", "gate_up", "down", "combine"};
 constexpr int kPrefillStageCount = 6;
 const char* const kDecodeStages[] = {"decode_layer"};
@@ -290,7 +300,11 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     if (d->out_dtype != (out16 ? MOE_BF16 : MOE_F32)) return MOE_ERR_UNSUPPORTED;
     if (d->T == 0) return MOE_OK;
     if (!wts) return MOE_ERR_NULL;
-    MOE_TRY(check_ptrs({x, out16 ? static_cast<const void*>(out16) : out, wts->router}));
+    // exactly one router: the bf16 matrix, or the 8-bit one restored per call
+    if (wts->router && wts->router_q8) return MOE_ERR_SHAPE;
+    MOE_TRY(check_ptrs({x, out16 ? static_cast<const void*>(out16) : out,
+                        wts->router_q8 ? static_cast<const void*>(wts->router_q8) : wts->router}));
+    if (wts->router_q8) MOE_TRY(check_ptrs({wts->router_scale, wts->router_bias}));
     MOE_TRY(check_opt({residual}));
     MOE_TRY(check_opt({wts->logit_bias, topk_idx_out, topk_w_out, counts_out}));
     MOE_TRY(check_ffn(&wts->experts));
@@ -310,6 +324,14 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     }
     const Layout L = layout_of(d);
     auto mark = [&](int i) -> bool { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
+    // the router the kernels score with; an 8-bit one is restored first, inside
+    // the first stage
+    const uint16_t* router = wts->router_q8 ? at<uint16_t>(ws, L.router16) : wts->router;
+    auto restore_router = [&]() -> hipError_t {
+        if (!wts->router_q8) return hipSuccess;
+        return launch_router_dequant(wts->router_q8, wts->router_scale, wts->router_bias, d->sb_dtype == MOE_BF16,
+                                     d->E, d->H, at<uint16_t>(ws, L.router16), stream);
+    };
 
     if (use_decode_path(d)) {
         DecodeArgs a;
@@ -322,7 +344,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.gateup_wgs = decode_gateup_wgs(d->T, d->top_k, shared, d->I);
         a.down_wgs = decode_down_wgs(d->T, d->top_k, shared, d->H);
         a.x = x;
-        a.router = wts->router;
+        a.router = router;
         a.logit_bias = wts->logit_bias;
         a.ctl = at<unsigned>(ws, L.ctl);
         a.xch64 = at<unsigned long long>(ws, L.xch);
@@ -336,6 +358,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.shared = shared ? to_ptr(&wts->shared) : FfnPtr{};
         a.shared_gate = wts->shared_expert_gate;
         if (!mark(0)) return MOE_ERR_HIP;
+        HIP_TRY(restore_router());
         HIP_TRY(launch_decode(a, d->sb_dtype == MOE_BF16, stream));
         if (out16) HIP_TRY(launch_residual_bf16(a.out, residual, d->T, d->H, out16, stream));
         if (!mark(1)) return MOE_ERR_HIP;
@@ -374,7 +397,8 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     if (!mark(0)) return MOE_ERR_HIP;
     int32_t* hist = at<int32_t>(ws, L.hist);
     int32_t* cursor = at<int32_t>(ws, L.cursor);
-    HIP_TRY(launch_logits(x, wts->router, wts->logit_bias, d->T, d->H, d->E, at<float>(ws, L.logits), hist, cursor,
+    HIP_TRY(restore_router());
+    HIP_TRY(launch_logits(x, router, wts->logit_bias, d->T, d->H, d->E, at<float>(ws, L.logits), hist, cursor,
                           stream));
     if (!mark(1)) return MOE_ERR_HIP;
     float* shared_w = wts->shared_expert_gate ? at<float>(ws, L.shared_w) : nullptr;

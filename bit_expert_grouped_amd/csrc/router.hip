@@ -24,6 +24,8 @@
 //     counts the expert histogram (in LDS per 4 or 16 tokens, then one atomic
 //     per expert) and writes the float16 copy of the token's row (8-column blocks in dequantisation order) that the expert
 //     products read.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -101,6 +103,32 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
             topk_idx[(size_t)t * top_k + lane] = ij;
             topk_w[(size_t)t * top_k + lane] = wj;
         }
+    }
+}
+
+// The 8-bit router restored to bf16 (a checkpoint detail, not on the pages):
+// one thread per 8 columns (two code words), fused multiply-add in float32,
+// then round to nearest even.  The result is the matrix every router kernel
+// here scores with.
+template <typename SB>
+__global__ __launch_bounds__(256) void router_dequant_kernel(const uint32_t* __restrict__ q,
+                                                             const SB* __restrict__ s, const SB* __restrict__ b,
+                                                             int E, int H, uint16_t* __restrict__ out) {
+    const int64_t n = (int64_t)E * (H / 8);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int e = (int)(i / (H / 8)), c8 = (int)(i % (H / 8));  // columns 8 c8 .. 8 c8 + 7
+        const uint2 w = reinterpret_cast<const uint2*>(q + (size_t)e * (H / 4))[c8];
+        const size_t g = (size_t)e * (H / 64) + c8 / 8;
+        const float sv = sb_to_f32<SB>(s[g]), bv = sb_to_f32<SB>(b[g]);
+        uint32_t r[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const uint32_t code = ((k < 4 ? w.x : w.y) >> (8 * (k % 4))) & 0xFFu;
+            const uint32_t u = __float_as_uint(__builtin_fmaf(sv, (float)code, bv));
+            r[k] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+        }
+        reinterpret_cast<uint4*>(out + (size_t)e * H)[c8] =
+            make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
     }
 }
 
@@ -443,6 +471,20 @@ __global__ __launch_bounds__(kTW * kWave) void topk_kernel(const float* __restri
 }
 
 }  // namespace
+
+hipError_t launch_router_dequant(const uint32_t* q, const void* s, const void* b, bool sb_bf16, int E, int H,
+                                 uint16_t* out, hipStream_t stream) {
+    const int64_t n = (int64_t)E * (H / 8);
+    if (n <= 0) return hipSuccess;
+    const int grid = (int)std::min<int64_t>((n + 255) / 256, 4096);
+    if (sb_bf16)
+        hipLaunchKernelGGL(router_dequant_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, q,
+                           static_cast<const uint16_t*>(s), static_cast<const uint16_t*>(b), E, H, out);
+    else
+        hipLaunchKernelGGL(router_dequant_kernel<float>, dim3(grid), dim3(256), 0, stream, q,
+                           static_cast<const float*>(s), static_cast<const float*>(b), E, H, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H,
                          int E, int top_k, int32_t* topk_idx, float* topk_w, hipStream_t stream) {

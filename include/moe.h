@@ -95,7 +95,7 @@ typedef struct {
 } moe_ffn;
 
 typedef struct {
-    const uint16_t *router;   /* [E][H] bf16 */
+    const uint16_t *router;   /* [E][H] bf16, or NULL when router_q8 is set */
     const float *logit_bias;  /* [E] or NULL */
     moe_ffn experts;          /* E routed experts */
     moe_ffn shared;           /* the shared expert; shared.gate.q == NULL iff I_shared == 0 */
@@ -105,6 +105,17 @@ typedef struct {
      * sum of exact bf16 products) instead of being added with weight 1.  Must
      * be NULL without a shared expert (MOE_ERR_SHAPE). */
     const uint16_t *shared_expert_gate;
+    /* Optional 8-bit router in the MLX affine layout, in place of `router`
+     * (both set: MOE_ERR_SHAPE; neither: MOE_ERR_NULL).  Not on the pages: a
+     * checkpoint may quantise its router too.  router_q8 [E][H/4] holds four
+     * codes per word, low byte first; router_scale and router_bias [E][H/64]
+     * use dims->sb_dtype; all three 16-byte aligned.  Each layer call first
+     * restores the bf16 router into its workspace, w =
+     * bf16_nearest_even(fmaf(scale, code, bias)) (see moe_router_dequant), and
+     * then scores with it exactly as with `router`. */
+    const uint32_t *router_q8;
+    const void *router_scale;
+    const void *router_bias;
 } moe_weights;
 
 /* Bytes of device workspace the calls below need for these dims (host-only,
@@ -179,6 +190,15 @@ moe_status moe_combine_gated(const moe_dims *dims, const float *y_slot, const fl
 moe_status moe_layer(const moe_dims *dims, const moe_weights *weights /* host */,
                      const uint16_t *x, void *out, int32_t *topk_idx_out, float *topk_w_out,
                      int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Restores an 8-bit router (the MLX affine layout of moe_weights.router_q8)
+ * to bf16: router_out[e][h] = bf16_nearest_even(fmaf(scale[e][h/64],
+ * code[e][h], bias[e][h/64])), code[e][h] = byte h%4 (low byte first) of word
+ * router_q8[e][h/4]; scale and bias use dims->sb_dtype.  Not on the pages: a
+ * checkpoint detail.  The output [E][H] feeds moe_route.  Device pointers,
+ * all 16-byte aligned (MOE_ERR_ALIGN); NULL pointers: MOE_ERR_NULL. */
+moe_status moe_router_dequant(const moe_dims *dims, const uint32_t *router_q8, const void *scale, const void *bias,
+                              uint16_t *router_out, hipStream_t stream);
 
 /* moe_layer writing into a bf16 residual stream (not on the pages: how a
  * decoder consumes the layer, a real-checkpoint detail):

@@ -119,6 +119,26 @@ def test_shared_expert_gate_checks(lib):
     assert lib.moe_combine_gated(C.byref(e), None, None, None, None, None, None) == 0
 
 
+def test_q8_router_checks(lib):
+    d = qwen_dims(8)
+    need = bem.moe_workspace_size(d)
+    w = _weights()
+    w.router_q8, w.router_scale, w.router_bias = FAKE, FAKE, FAKE
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -2  # both routers
+    w.router = None
+    w.router_scale = None
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -1
+    w.router_scale = FAKE + 4
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -4
+    w.router_q8 = None
+    w.router_scale = FAKE
+    assert lib.moe_layer(C.byref(d), C.byref(w), FAKE, FAKE, None, None, None, FAKE, need, None) == -1  # no router
+    assert lib.moe_router_dequant(C.byref(d), FAKE, FAKE, None, FAKE, None) == -1
+    assert lib.moe_router_dequant(C.byref(d), FAKE + 8, FAKE, FAKE, FAKE, None) == -4
+    bad = qwen_dims(8, H=100)
+    assert lib.moe_router_dequant(C.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == -2
+
+
 def test_output_dtype_per_entry_point(lib):
     """moe_layer writes float32 only; moe_layer_residual writes the bf16 residual stream only."""
     w = _weights()

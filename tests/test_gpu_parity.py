@@ -455,6 +455,53 @@ def test_prefill_path_is_bitwise_reproducible(T):
         np.testing.assert_array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
+def _custom_q8(T, H, E, k, I, bf16=True, seed=61):
+    """A layer whose router is 8-bit (the MLX affine layout); tokens drawn
+    away from near-ties of the restored router."""
+    cfg = moe_synth.Config("custom", moe_synth.Shape(T=T, H=H, E=E, top_k=k, I=I, I_shared=I, sb_bf16=bf16),
+                           seed=seed)
+    w = moe_synth.layer_weights(cfg)
+    w.update(moe_synth.router_q8(cfg, 0))
+    w["router"] = None
+    x = tie_filter.tokens_for(cfg, oracle.layer_router(w), None)
+    return cfg, w, x
+
+
+@pytest.mark.parametrize("E,H,bf16", [(256, 2048, True), (40, 192, False), (3, 64, True)])
+def test_router_dequant_step(E, H, bf16):
+    cfg = moe_synth.Config("custom", moe_synth.Shape(T=1, H=H, E=E, top_k=1, I=64, I_shared=64, sb_bf16=bf16),
+                           seed=5 + E)
+    r = moe_synth.router_q8(cfg, 2)
+    want = oracle.router_dequant_q8(r["router_q8"], r["router_scale"], r["router_bias"])
+    m = bem()
+    q = torch.from_numpy(r["router_q8"].view(np.int32)).cuda()
+    if bf16:
+        sc = torch.from_numpy(r["router_scale"].view(np.int16)).cuda().view(torch.bfloat16)
+        bi = torch.from_numpy(r["router_bias"].view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        sc, bi = torch.from_numpy(r["router_scale"]).cuda(), torch.from_numpy(r["router_bias"]).cuda()
+    got = m.moe_router_dequant(q, sc, bi)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+@pytest.mark.parametrize("T,H,E,k,I", [
+    (1, 2048, 256, 8, 512),    # decode kernel
+    (3, 2048, 256, 8, 512),    # decode kernel, several tokens
+    (64, 2048, 256, 8, 512),   # batched decode on the prefill path
+    (600, 512, 64, 8, 128),    # large-batch path
+    (2100, 1024, 256, 8, 64),  # the LDS-staged router
+])
+def test_layer_with_q8_router(T, H, E, k, I):
+    cfg, w, x = _custom_q8(T, H, E, k, I, seed=70 + T)
+    print("case q8 router T", T, flush=True)
+    ref = oracle.moe_layer(w, x, k)
+    out, idx, wt, counts = run_layer(w, x, k)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out, ref["out"], "q8 router T%d" % T)
+
+
 def test_large_batch_router_with_logit_bias():
     """The LDS-staged router (T >= 2048) with K split in two: only split 0 adds
     the bias; skewed routing from a Zipf-ranked per-expert offset."""
