@@ -200,6 +200,9 @@ def main():
     ap.add_argument("--shared-gate", action="store_true",
                     help="give the shared expert a sigmoid gate vector (an optional checkpoint detail; the "
                          "configs have none)")
+    ap.add_argument("--router-q8", action="store_true",
+                    help="store the router as 8-bit codes in the MLX affine layout (an optional checkpoint "
+                         "detail; the configs use a bf16 router)")
     ap.add_argument("--mode", choices=("eager", "graph"), default=None,
                     help="graph: replay one HIP graph holding the K timed steps (default); "
                          "eager: one foreign call per layer call")
@@ -240,6 +243,15 @@ def main():
         for l, t in enumerate(tensors):
             gbits = moe_synth.shared_expert_gate(cfg, l)
             t["shared_expert_gate"] = torch.from_numpy(gbits.view("int16")).to(dev).view(torch.bfloat16)
+    if args.router_q8:
+        for l, t in enumerate(tensors):
+            r = moe_synth.router_q8(cfg, l)
+            t["router"] = None
+            t["router_q8"] = torch.from_numpy(r["router_q8"].view("int32")).to(dev)
+            for key in ("router_scale", "router_bias"):
+                v = r[key]
+                t[key] = (torch.from_numpy(v.view("int16")).to(dev).view(torch.bfloat16) if v.dtype.itemsize == 2
+                          else torch.from_numpy(v).to(dev))
     sets = [bem.LayerWeights(t) for t in tensors]
     n_x = min(steps + warmup, 64) if not big else 4
     xs = [moe_synth.device_tokens(sh, T, cfg.seed, i, dev) for i in range(n_x)]
@@ -401,7 +413,7 @@ def main():
         "config": {"workload": args.workload, "T": T, "H": sh.H, "E": sh.E, "top_k": sh.top_k, "I": sh.I,
                    "I_shared": sh.I_shared, "layers_per_step": layers_per_step, "weight_sets": n_sets,
                    "weights": "affine 4-bit g64, bf16 scales/biases", "activations": "bf16",
-                   "shared_expert_gate": bool(args.shared_gate),
+                   "shared_expert_gate": bool(args.shared_gate), "router_q8": bool(args.router_q8),
                    "products": "f16 MFMA, fp32 accumulation; router bf16 MFMA; fp32 output"},
         "us_per_layer": round(us_layer, 3),
         "layer_hbm_frac": round(layer_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -296,6 +296,21 @@ __device__ void route_slot(const DecodeArgs& p, int slot, int t, bool routed, un
 
 // ------------------------------------------------------------------ router role
 
+// 8 codes of an 8-bit router row (two words, low byte first) restored to the
+// bf16 weights the dense router would hold: nearest-even bf16 of the float32
+// fused multiply-add scale * code + bias
+__device__ __forceinline__ uint4 restore_q8x8(uint2 w, float s, float b) {
+    uint32_t r[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const uint32_t code = ((k < 4 ? w.x : w.y) >> (8 * (k % 4))) & 0xFFu;
+        const uint32_t u = __float_as_uint(__builtin_fmaf(s, (float)code, b));
+        r[k] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    }
+    return make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
+}
+
+template <typename SB, bool kQ8>
 __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShared& sh) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int H = p.H, T = p.T, E = p.E;
@@ -309,18 +324,36 @@ __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShar
     float acc[kDecodeMaxT];
 #pragma unroll
     for (int t = 0; t < kDecodeMaxT; t++) acc[t] = 0.0f;
-    const uint4* wr = reinterpret_cast<const uint4*>(p.router + (size_t)min(e, E - 1) * H);
+    const int er = min(e, E - 1);
+    const uint4* wr = reinterpret_cast<const uint4*>(p.router + (size_t)er * H);
+    // 8-bit router: the row's codes (8 per 8-byte pair of words) and the scale
+    // and bias of each 64-column group
+    const uint2* wq = reinterpret_cast<const uint2*>(p.router_q8 + (size_t)er * (H / 4));
+    const SB* rs = static_cast<const SB*>(p.router_s) + (size_t)er * (H / 64);
+    const SB* rb = static_cast<const SB*>(p.router_b) + (size_t)er * (H / 64);
     for (int c0 = 0; c0 < nblk; c0 += 4 * kWave) {
         uint4 a[4], xv[kDecodeMaxT][4];
+        uint2 aq[4];
+        SB sq[4], bq[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int c = min(c0 + lane + kWave * j, nblk - 1);
-            a[j] = wr[c];
+            if (kQ8) {
+                aq[j] = wq[c];
+                sq[j] = rs[c / 8];
+                bq[j] = rb[c / 8];
+            } else {
+                a[j] = wr[c];
+            }
 #pragma unroll
             for (int t = 0; t < kDecodeMaxT; t++)
                 xv[t][j] = reinterpret_cast<const uint4*>(p.x + (size_t)min(t, T - 1) * H)[c];
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (kQ8) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) a[j] = restore_q8x8(aq[j], sb_to_f32<SB>(sq[j]), sb_to_f32<SB>(bq[j]));
+        }
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             if (c0 + lane + kWave * j >= nblk) continue;
@@ -637,7 +670,7 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     }
 }
 
-template <typename SB>
+template <typename SB, bool kQ8>
 __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
     __shared__ RoleShared sh;
     // a plain load: the word was stored by the previous call (visible once that
@@ -648,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
     if (epoch == 0) epoch = 1;  // words of a zero-filled workspace carry epoch 0
     const int b = blockIdx.x;
     if (b < p.router_wgs) {
-        router_role(p, b, epoch, sh);
+        router_role<SB, kQ8>(p, b, epoch, sh);
     } else if (b < p.router_wgs + p.gateup_wgs) {
         const int unit = b - p.router_wgs, nblk = p.I / kGURows;
         const int slot = unit / nblk, blk = unit % nblk;
@@ -737,10 +770,15 @@ int decode_down_wgs(int T, int k, bool shared, int H) {
 
 hipError_t launch_decode(const DecodeArgs& a, bool sb_bf16, hipStream_t stream) {
     const dim3 grid(a.router_wgs + a.gateup_wgs + a.down_wgs);
-    if (sb_bf16)
-        hipLaunchKernelGGL(decode_layer_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, a);
+    const bool q8 = a.router_q8 != nullptr;
+    if (sb_bf16 && !q8)
+        hipLaunchKernelGGL((decode_layer_kernel<uint16_t, false>), grid, dim3(kThreads), 0, stream, a);
+    else if (sb_bf16)
+        hipLaunchKernelGGL((decode_layer_kernel<uint16_t, true>), grid, dim3(kThreads), 0, stream, a);
+    else if (!q8)
+        hipLaunchKernelGGL((decode_layer_kernel<float, false>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(decode_layer_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((decode_layer_kernel<float, true>), grid, dim3(kThreads), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (a.idx_out || a.w_out || a.counts_out) {

@@ -147,6 +147,9 @@ struct DecodeArgs {
     int router_wgs, gateup_wgs, down_wgs;  // workgroups per role (decode_*_wgs)
     const uint16_t* x;
     const uint16_t* router;
+    const uint32_t* router_q8;   // or an 8-bit router, restored in the router workgroups
+    const void* router_s;        // its scales and biases [E][H/64] (the experts' dtype)
+    const void* router_b;
     const float* logit_bias;
     unsigned* ctl;               // control words and counters
     unsigned long long* xch64;   // kDecodeXchReplicas copies of [kDecodeMaxT][256] {epoch, logit}

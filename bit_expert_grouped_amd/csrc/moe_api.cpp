@@ -344,7 +344,11 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.gateup_wgs = decode_gateup_wgs(d->T, d->top_k, shared, d->I);
         a.down_wgs = decode_down_wgs(d->T, d->top_k, shared, d->H);
         a.x = x;
-        a.router = router;
+        // the router workgroups restore an 8-bit router themselves
+        a.router = wts->router;
+        a.router_q8 = wts->router_q8;
+        a.router_s = wts->router_scale;
+        a.router_b = wts->router_bias;
         a.logit_bias = wts->logit_bias;
         a.ctl = at<unsigned>(ws, L.ctl);
         a.xch64 = at<unsigned long long>(ws, L.xch);
@@ -358,7 +362,6 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.shared = shared ? to_ptr(&wts->shared) : FfnPtr{};
         a.shared_gate = wts->shared_expert_gate;
         if (!mark(0)) return MOE_ERR_HIP;
-        HIP_TRY(restore_router());
         HIP_TRY(launch_decode(a, d->sb_dtype == MOE_BF16, stream));
         if (out16) HIP_TRY(launch_residual_bf16(a.out, residual, d->T, d->H, out16, stream));
         if (!mark(1)) return MOE_ERR_HIP;
