@@ -58,6 +58,20 @@ template <typename SB> __device__ __forceinline__ float sb_to_f32(SB v);
 template <> __device__ __forceinline__ float sb_to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
 template <> __device__ __forceinline__ float sb_to_f32<float>(float v) { return v; }
 
+// 8 codes of an 8-bit router row (two words, low byte first) restored to the
+// bf16 weights a dense router would hold: nearest-even bf16 of the float32
+// fused multiply-add scale * code + bias
+__device__ __forceinline__ uint4 restore_q8x8(uint2 w, float s, float b) {
+    uint32_t r[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const uint32_t code = ((k < 4 ? w.x : w.y) >> (8 * (k % 4))) & 0xFFu;
+        const uint32_t u = __float_as_uint(__builtin_fmaf(s, (float)code, b));
+        r[k] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    }
+    return make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
+}
+
 __device__ __forceinline__ half2_t splat_half2(float v) {
     _Float16 h = (_Float16)v;
     half2_t r = {h, h};

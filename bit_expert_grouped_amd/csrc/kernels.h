@@ -75,8 +75,12 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* log
 // (kCounterStride ints apart); launch_logits zeroes zero0[e * kCounterStride]
 // and zero1[e * kCounterStride].
 constexpr int kCounterStride = 32;
-hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H, int E,
-                         float* logits, int32_t* zero0, int32_t* zero1, hipStream_t stream);
+// The router is the bf16 matrix wr, or (wq non-null, batches below 2048 tokens)
+// an 8-bit one that the logits kernel restores in registers; the staged kernel
+// of larger batches needs wr.
+hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const uint32_t* wq, const void* wsc, const void* wbi,
+                         bool sb_bf16, const float* logit_bias, int T, int H, int E, float* logits, int32_t* zero0,
+                         int32_t* zero1, hipStream_t stream);
 // sgate (nullable, needs x16): the shared expert's gate vector [H] bf16; then
 // shared_w [T] receives sigmoid(x[t] . sgate)
 hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int top_k, int32_t* topk_idx,

@@ -400,9 +400,13 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
     if (!mark(0)) return MOE_ERR_HIP;
     int32_t* hist = at<int32_t>(ws, L.hist);
     int32_t* cursor = at<int32_t>(ws, L.cursor);
-    HIP_TRY(restore_router());
-    HIP_TRY(launch_logits(x, router, wts->logit_bias, d->T, d->H, d->E, at<float>(ws, L.logits), hist, cursor,
-                          stream));
+    // an 8-bit router: the register-fed logits kernel restores it in place;
+    // the staged one (large batches) reads the copy restored into the workspace
+    const bool restore_in_logits = wts->router_q8 && logits_tile(d->T) != 64;
+    if (!restore_in_logits) HIP_TRY(restore_router());
+    HIP_TRY(launch_logits(x, restore_in_logits ? nullptr : router, restore_in_logits ? wts->router_q8 : nullptr,
+                          wts->router_scale, wts->router_bias, d->sb_dtype == MOE_BF16, wts->logit_bias, d->T, d->H,
+                          d->E, at<float>(ws, L.logits), hist, cursor, stream));
     if (!mark(1)) return MOE_ERR_HIP;
     float* shared_w = wts->shared_expert_gate ? at<float>(ws, L.shared_w) : nullptr;
     HIP_TRY(launch_topk(at<float>(ws, L.logits), x, d->T, d->H, d->E, d->top_k, idx, w, hist, x16,

@@ -119,16 +119,7 @@ __global__ __launch_bounds__(256) void router_dequant_kernel(const uint32_t* __r
         const int e = (int)(i / (H / 8)), c8 = (int)(i % (H / 8));  // columns 8 c8 .. 8 c8 + 7
         const uint2 w = reinterpret_cast<const uint2*>(q + (size_t)e * (H / 4))[c8];
         const size_t g = (size_t)e * (H / 64) + c8 / 8;
-        const float sv = sb_to_f32<SB>(s[g]), bv = sb_to_f32<SB>(b[g]);
-        uint32_t r[8];
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const uint32_t code = ((k < 4 ? w.x : w.y) >> (8 * (k % 4))) & 0xFFu;
-            const uint32_t u = __float_as_uint(__builtin_fmaf(sv, (float)code, bv));
-            r[k] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-        }
-        reinterpret_cast<uint4*>(out + (size_t)e * H)[c8] =
-            make_uint4(r[0] | (r[1] << 16), r[2] | (r[3] << 16), r[4] | (r[5] << 16), r[6] | (r[7] << 16));
+        reinterpret_cast<uint4*>(out + (size_t)e * H)[c8] = restore_q8x8(w, sb_to_f32<SB>(s[g]), sb_to_f32<SB>(b[g]));
     }
 }
 
@@ -138,8 +129,12 @@ __global__ __launch_bounds__(256) void router_dequant_kernel(const uint32_t* __r
 // sums the S splits in order.  It runs with TM = 32 for batches below 2048
 // tokens, with K split S ways so that the router's 1 MiB is spread over a few
 // hundred workgroups (larger batches use logits_staged_kernel below).
-template <int TM>
+// kQ8: the router is 8-bit (codes wq, scales wsc and biases wbi per 64
+// columns) and each lane restores its 8-column chunks to bf16 in registers.
+template <int TM, typename SB, bool kQ8>
 __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                     const uint32_t* __restrict__ wq, const SB* __restrict__ wsc,
+                                                     const SB* __restrict__ wbi,
                                                      const float* __restrict__ logit_bias, int T, int H, int E, int S,
                                                      float* __restrict__ partial, int32_t* __restrict__ zero0,
                                                      int32_t* __restrict__ zero1) {
@@ -161,25 +156,59 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict_
     const int kb = z * (H / S) + wave * kq;
     const uint4* arow[MB];
     const uint4* brow[MB];
+    const uint2* qrow[MB];
+    const SB* srow[MB];
+    const SB* bsrow[MB];
 #pragma unroll
     for (int m = 0; m < MB; m++) {
+        const size_t er = (size_t)min(e0 + 32 * m + row, E - 1);
         arow[m] = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + 32 * m + row, T - 1) * H + kb);
-        brow[m] = reinterpret_cast<const uint4*>(wr + (size_t)min(e0 + 32 * m + row, E - 1) * H + kb);
+        if (kQ8) {
+            qrow[m] = reinterpret_cast<const uint2*>(wq + er * (H / 4)) + kb / 8;
+            srow[m] = wsc + er * (H / 64);
+            bsrow[m] = wbi + er * (H / 64);
+        } else {
+            brow[m] = reinterpret_cast<const uint4*>(wr + er * H + kb);
+        }
     }
+    // router chunk c (8 columns from kb + 8 c): bf16 directly, or codes, scale
+    // and bias to restore once they have landed
+    struct RawB {
+        uint2 q;
+        SB s, b;
+    };
+    auto fetch_b = [&](int m, int c, uint4& bf, RawB& raw) {
+        if (kQ8) {
+            const int g = (kb / 8 + c) / 8;
+            raw.q = qrow[m][c];
+            raw.s = srow[m][g];
+            raw.b = bsrow[m][g];
+        } else {
+            bf = brow[m][c];
+        }
+    };
+    auto restore = [](const RawB& raw) { return restore_q8x8(raw.q, sb_to_f32<SB>(raw.s), sb_to_f32<SB>(raw.b)); };
     floatx16 acc[MB][MB];
 #pragma unroll
     for (int m = 0; m < MB; m++)
 #pragma unroll
         for (int n = 0; n < MB; n++) acc[m][n] = floatx16{0};
     uint4 a[kSteps][MB], b[kSteps][MB], an[kSteps][MB], bn[kSteps][MB];
+    RawB rb[kSteps][MB], rbn[kSteps][MB];
 #pragma unroll
     for (int j = 0; j < kSteps; j++) {
         const int c = 2 * min(j, nk - 1) + half;
 #pragma unroll
         for (int m = 0; m < MB; m++) {
             a[j][m] = arow[m][c];
-            b[j][m] = brow[m][c];
+            fetch_b(m, c, b[j][m], rb[j][m]);
         }
+    }
+    if (kQ8) {
+#pragma unroll
+        for (int j = 0; j < kSteps; j++)
+#pragma unroll
+            for (int m = 0; m < MB; m++) b[j][m] = restore(rb[j][m]);
     }
     for (int kk = 0; kk < nk; kk += kSteps) {
         const bool more = kk + kSteps < nk;
@@ -190,7 +219,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict_
 #pragma unroll
                 for (int m = 0; m < MB; m++) {
                     an[j][m] = arow[m][c];
-                    bn[j][m] = brow[m][c];
+                    fetch_b(m, c, bn[j][m], rbn[j][m]);
                 }
             }
         }
@@ -211,7 +240,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t* __restrict_
 #pragma unroll
                 for (int m = 0; m < MB; m++) {
                     a[j][m] = an[j][m];
-                    b[j][m] = bn[j][m];
+                    b[j][m] = kQ8 ? restore(rbn[j][m]) : bn[j][m];
                 }
         }
     }
@@ -495,18 +524,29 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wr, const float* log
     return hipGetLastError();
 }
 
-hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const float* logit_bias, int T, int H, int E,
-                         float* logits, int32_t* zero0, int32_t* zero1, hipStream_t stream) {
+hipError_t launch_logits(const uint16_t* x, const uint16_t* wr, const uint32_t* wq, const void* wsc, const void* wbi,
+                         bool sb_bf16, const float* logit_bias, int T, int H, int E, float* logits, int32_t* zero0,
+                         int32_t* zero1, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     const int tm = logits_tile(T);
     const int S = logits_splits(T, H, E);
     const dim3 grid((T + tm - 1) / tm, (E + tm - 1) / tm, S);
-    if (tm == 64)
-        hipLaunchKernelGGL(logits_staged_kernel, grid, dim3(kStagedThreads), 0, stream, x, wr, logit_bias, T, H, E, S, logits,
-                           zero0, zero1);
-    else
-        hipLaunchKernelGGL(logits_kernel<32>, grid, dim3(256), 0, stream, x, wr, logit_bias, T, H, E, S, logits, zero0,
-                           zero1);
+    if (tm == 64) {
+        if (!wr) return hipErrorInvalidValue;  // the staged kernel reads a bf16 router
+        hipLaunchKernelGGL(logits_staged_kernel, grid, dim3(kStagedThreads), 0, stream, x, wr, logit_bias, T, H, E, S,
+                           logits, zero0, zero1);
+    } else if (!wq) {
+        hipLaunchKernelGGL((logits_kernel<32, uint16_t, false>), grid, dim3(256), 0, stream, x, wr, nullptr,
+                           nullptr, nullptr, logit_bias, T, H, E, S, logits, zero0, zero1);
+    } else if (sb_bf16) {
+        hipLaunchKernelGGL((logits_kernel<32, uint16_t, true>), grid, dim3(256), 0, stream, x, nullptr, wq,
+                           static_cast<const uint16_t*>(wsc), static_cast<const uint16_t*>(wbi), logit_bias, T, H, E,
+                           S, logits, zero0, zero1);
+    } else {
+        hipLaunchKernelGGL((logits_kernel<32, float, true>), grid, dim3(256), 0, stream, x, nullptr, wq,
+                           static_cast<const float*>(wsc), static_cast<const float*>(wbi), logit_bias, T, H, E, S,
+                           logits, zero0, zero1);
+    }
     return hipGetLastError();
 }
 
