@@ -485,15 +485,17 @@ def test_router_dequant_step(E, H, bf16):
     np.testing.assert_array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), want)
 
 
-@pytest.mark.parametrize("T,H,E,k,I", [
-    (1, 2048, 256, 8, 512),    # decode kernel
-    (3, 2048, 256, 8, 512),    # decode kernel, several tokens
-    (64, 2048, 256, 8, 512),   # batched decode on the prefill path
-    (600, 512, 64, 8, 128),    # large-batch path
-    (2100, 1024, 256, 8, 64),  # the LDS-staged router
+@pytest.mark.parametrize("T,H,E,k,I,bf16", [
+    (1, 2048, 256, 8, 512, True),    # decode kernel
+    (3, 2048, 256, 8, 512, True),    # decode kernel, several tokens
+    (2, 256, 24, 3, 64, False),      # decode kernel, float32 scales and biases
+    (64, 2048, 256, 8, 512, True),   # batched decode on the prefill path (restored in the logits kernel)
+    (40, 256, 24, 3, 64, False),     # the same with float32 scales and biases
+    (600, 512, 64, 8, 128, True),    # large-batch path
+    (2100, 1024, 256, 8, 64, True),  # the LDS-staged router (restored into the workspace first)
 ])
-def test_layer_with_q8_router(T, H, E, k, I):
-    cfg, w, x = _custom_q8(T, H, E, k, I, seed=70 + T)
+def test_layer_with_q8_router(T, H, E, k, I, bf16):
+    cfg, w, x = _custom_q8(T, H, E, k, I, bf16=bf16, seed=70 + T)
     print("case q8 router T", T, flush=True)
     ref = oracle.moe_layer(w, x, k)
     out, idx, wt, counts = run_layer(w, x, k)
