@@ -2,14 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|decode64|prefill512|prefill4096|stack40]
 
+With no --workload, one process times every workload: the decode step (T=1)
+is the headline line, and decode64, prefill512, prefill4096 and stack40 are
+extra keys of the same JSON line, each with its own roofline and CPU baseline.
+
 A step is one pass of the whole layer (routing, permute, gate/up + SwiGLU,
 down + weighted combine + shared expert) over one batch of synthetic tokens,
 through the C ABI entry point ``moe_layer``.  Inputs are resident in HBM before
 timing starts.  Successive steps cycle through distinct weight sets drawn in
 device memory, so a step does not find the previous steps' weights in the
-256 MB last-level cache, and use fresh activations.  The default workload is
+256 MB last-level cache, and use fresh activations.  The headline workload is
 one decode step (T=1) of the Qwen3.6-35B-A3B layer shape (H=2048, 256 experts,
-top-8, shared expert, I=512).
+top-8, shared expert, I=512).  After the timed region the decode path's
+control words are read back: a device-side wait that timed out (workspace word
+255) or a call counter that did not advance once per call ends the run with an
+error.
 
 Launch: the K timed steps are captured once into a HIP graph and replayed
 (how an engine issues a fixed-shape layer step; ``--mode eager`` launches
@@ -26,7 +33,7 @@ SHA-256 of the kernel's source file; when the source has changed since, the
 field is null.
 
 Prints one JSON line.  ``cpu_baseline`` times the CPU oracle (single-threaded
-C) on a bounded sample of the same workload.
+C, pinned to one core) on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -148,32 +155,66 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
 
 
-def cpu_baseline(cfg, T, seconds):
-    """Time the CPU oracle on a bounded sample of the workload (tokens/s)."""
-    import numpy as np
+def cpu_baseline(cfg, T, seconds, layers=1):
+    """Time the CPU oracle (single-threaded C, pinned to one core) on a bounded
+    sample of the workload; tokens/s.
 
-    import moe_synth
+    Decode (T <= 4): whole oracle calls of T tokens.  Larger batches: oracle
+    calls on 64-token sub-batches of the workload's tokens; each call routes its
+    tokens and restores every expert they touch, so the per-token cost sits
+    above that of one call over the whole batch.  For a layer stack the rate is
+    per layer (every layer costs the same)."""
     import oracle
 
-    w = moe_synth.layer_weights(cfg)
-    n = T if T <= 4 else 4  # tokens per oracle call
-    x_all = moe_synth.token_rows(cfg, 64)
-    done_tokens, calls = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        x = x_all[(calls * n) % 64:(calls * n) % 64 + n]
-        oracle.moe_layer(w, x, cfg.shape.top_k)
-        done_tokens += x.shape[0]
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    import moe_synth
+
+    pinned = _pin_one_core()
+    try:
+        w = moe_synth.layer_weights(cfg)
+        n = T if T <= 4 else 64  # tokens per oracle call
+        pool = 64 if T <= 4 else 256
+        x_all = moe_synth.token_rows(cfg, pool)
+        done_tokens, calls = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            lo = (calls * n) % pool
+            oracle.moe_layer(w, x_all[lo:lo + n], cfg.shape.top_k)
+            done_tokens += n
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        _unpin(pinned)
+    what = ("%d oracle calls of %d token(s) each" % (calls, n) if T <= 4 else
+            "%d oracle calls on 64-token sub-batches of the T=%d batch (each call routes its tokens and restores "
+            "every expert they touch)" % (calls, T))
+    if layers > 1:
+        what += "; one layer of the %d-layer stack, rate per layer" % layers
     return {"value": round(done_tokens / el, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d oracle calls of %d token(s) each on one %s layer (H=%d, E=%d, top-%d, I=%d), "
-                      "%.1f s single-threaded; per-token cost includes routing all experts and dequantising "
-                      "every touched expert" % (calls, n, cfg.name, cfg.shape.H, cfg.shape.E, cfg.shape.top_k,
-                                                cfg.shape.I, el),
-            "seconds": round(el, 2), "cpu": _cpu_model()}
+            "sample": "%s on one %s layer (H=%d, E=%d, top-%d, I=%d), %.1f s single-threaded, pinned to core %s"
+                      % (what, cfg.name, cfg.shape.H, cfg.shape.E, cfg.shape.top_k, cfg.shape.I, el,
+                         pinned[1] if pinned else "none"),
+            "seconds": round(el, 2), "cpu": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def _pin_one_core():
+    """Pin this process to one core of its allowed set; returns (old set, core) or None."""
+    try:
+        old = os.sched_getaffinity(0)
+        core = max(old)
+        os.sched_setaffinity(0, {core})
+        return old, core
+    except (AttributeError, OSError):
+        return None
+
+
+def _unpin(pinned):
+    if pinned:
+        try:
+            os.sched_setaffinity(0, pinned[0])
+        except OSError:
+            pass
 
 
 def _cpu_model():
@@ -186,14 +227,287 @@ def _cpu_model():
     return "unknown"
 
 
+def check_decode_words(ws, decode_calls_expected=None):
+    """The decode path's control words after a run: the timeout flag (word 255)
+    must be clear; the call counter (word 0) must have advanced by the number
+    of decode calls made, when that is known.  Raises on a violation."""
+    import torch
+
+    words = ws[:1024].view(torch.int32).cpu()
+    calls, flag = int(words[0]), int(words[255])
+    if flag != 0:
+        raise RuntimeError("a device-side wait of the decode kernel timed out (workspace word 255 = %d): "
+                           "the timed outputs are invalid" % flag)
+    if decode_calls_expected is not None and calls != decode_calls_expected:
+        raise RuntimeError("decode call counter reads %d after %d decode calls" % (calls, decode_calls_expected))
+    return calls
+
+
+def run_workload(name, steps_arg, warmup_arg, args, with_cpu=True, cpu_seconds=None):
+    """Time one workload; returns its record (the fields of the JSON line)."""
+    import torch
+
+    import bit_expert_grouped_amd as bem
+    import moe_synth
+
+    cfg_name, layers_per_step, bound, default_sets = WORKLOADS[name]
+    cfg = moe_synth.CONFIGS[cfg_name]
+    sh = cfg.shape
+    T = sh.T
+    big = T >= 512
+    steps = steps_arg if steps_arg is not None else (20 if big else 200)
+    warmup = warmup_arg if warmup_arg is not None else (3 if big else 20)
+    n_sets = args.weight_sets or default_sets
+    if layers_per_step > 1:
+        n_sets = layers_per_step
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    alpha = moe_synth.zipf_alpha() if cfg.zipf else None
+    tensors = [moe_synth.device_layer(sh, cfg.seed, l, dev, alpha) for l in range(n_sets)]
+    if args.shared_gate:
+        for l, t in enumerate(tensors):
+            gbits = moe_synth.shared_expert_gate(cfg, l)
+            t["shared_expert_gate"] = torch.from_numpy(gbits.view("int16")).to(dev).view(torch.bfloat16)
+    if args.router_q8:
+        for l, t in enumerate(tensors):
+            r = moe_synth.router_q8(cfg, l)
+            t["router"] = None
+            t["router_q8"] = torch.from_numpy(r["router_q8"].view("int32")).to(dev)
+            for key in ("router_scale", "router_bias"):
+                v = r[key]
+                t[key] = (torch.from_numpy(v.view("int16")).to(dev).view(torch.bfloat16) if v.dtype.itemsize == 2
+                          else torch.from_numpy(v).to(dev))
+    sets = [bem.LayerWeights(t) for t in tensors]
+    n_x = min(steps + warmup, 64) if not big else 4
+    xs = [moe_synth.device_tokens(sh, T, cfg.seed, i, dev) for i in range(n_x)]
+    d = sets[0].dims(T, sh.top_k)
+    ws = bem.workspace(d, dev)
+    out = torch.empty(T, sh.H, dtype=torch.float32, device=dev)
+    stages = bem.moe_layer_stages(d)
+    is_decode = stages == ["decode_layer"]
+    n_calls = steps * layers_per_step
+    counts = torch.zeros(n_calls, sh.E, dtype=torch.int32, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_calls)]
+    mode = args.mode or "graph"
+    torch.cuda.synchronize()
+
+    # Pre-built argument tuples of the C entry points: the timed loop is one
+    # foreign call per layer call.
+    stream = torch.cuda.current_stream()
+    lib = bem.lib()
+    dref = ctypes.byref(d)
+    for e in evs:
+        for ev in e:
+            ev.record()
+    torch.cuda.synchronize()
+    decode_calls = 0
+
+    def call_args(i, li, s_handle, with_events, set_offset=0):
+        w = sets[li % n_sets] if layers_per_step > 1 else sets[(i + set_offset) % n_sets]
+        x = xs[i % n_x]
+        c = i * layers_per_step + li
+        base = (dref, ctypes.byref(w.struct), x.data_ptr(), out.data_ptr(), None, None, None, ws.data_ptr(),
+                ws.numel(), s_handle)
+        if not with_events:
+            return base
+        arr = (ctypes.c_void_p * len(evs[c]))(*[ev.cuda_event for ev in evs[c]])
+        return base + (ctypes.cast(arr, ctypes.c_void_p), len(evs[c])), arr
+
+    def run_eager(record):
+        keep = []
+        for i in range(steps):
+            for li in range(layers_per_step):
+                if record:
+                    a, arr = call_args(i, li, stream.cuda_stream, True)
+                    keep.append(arr)
+                    st = lib.moe_layer_events(*a)
+                else:
+                    st = lib.moe_layer(*call_args(i, li, stream.cuda_stream, False))
+                if st != 0:
+                    raise bem.MoeError(st, "moe_layer")
+        return keep
+
+    # warm-up (eager)
+    for i in range(warmup):
+        for li in range(layers_per_step):
+            st = lib.moe_layer(*call_args(i + 1000, li, stream.cuda_stream, False))
+            if st != 0:
+                raise bem.MoeError(st, "moe_layer")
+    decode_calls += warmup * layers_per_step
+    torch.cuda.synchronize()
+
+    def capture(set_offset):
+        """One HIP graph holding all K steps (weight sets shifted by set_offset)."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            prepared = [call_args(i, li, side.cuda_stream, False, set_offset)
+                        for i in range(steps) for li in range(layers_per_step)]
+            with torch.cuda.graph(g, stream=side):
+                for a in prepared:
+                    st = lib.moe_layer(*a)
+                    if st != 0:
+                        raise bem.MoeError(st, "moe_layer (capture)")
+        torch.cuda.synchronize()
+        return g
+
+    plain = None
+    if mode == "graph":
+        # the timed graph runs weight sets 0..K-1; an untimed replay of it, then
+        # one of a graph over the other sets, so that the timed replay finds its
+        # weights evicted from the last-level cache (when there are 2K sets)
+        plain = capture(0)
+        plain.replay()
+        torch.cuda.synchronize()
+        if layers_per_step == 1 and n_sets > steps:
+            other = capture(steps)
+            other.replay()
+            torch.cuda.synchronize()
+            decode_calls += n_calls
+        decode_calls += n_calls
+
+    # ---- timed region: exactly K steps, no instrumentation ----
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    start.record()
+    if plain is not None:
+        plain.replay()
+    else:
+        for i in range(steps):
+            for li in range(layers_per_step):
+                st = lib.moe_layer(*call_args(i, li, stream.cuda_stream, False))
+                if st != 0:
+                    raise bem.MoeError(st, "moe_layer")
+    stop.record()
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - t_host0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / steps
+    decode_calls += n_calls
+    if is_decode:
+        check_decode_words(ws, decode_calls)
+
+    # ---- instrumented eager run of the same K steps: HIP events around every kernel ----
+    _keep = run_eager(True)
+    torch.cuda.synchronize()
+    decode_calls += n_calls
+
+    # per-stage durations
+    stage_us = {st_name: 0.0 for st_name in stages}
+    for e in evs:
+        for j, st_name in enumerate(stages):
+            stage_us[st_name] += e[j].elapsed_time(e[j + 1]) * 1000.0
+    for st_name in stages:
+        stage_us[st_name] /= n_calls
+    # experts touched per call (outside the timed region: the same calls again,
+    # with the per-expert counts requested)
+    n_count = 0
+    for i in range(min(steps, 16)):
+        for li in range(layers_per_step if layers_per_step <= 4 else 4):
+            a = call_args(i, li, stream.cuda_stream, False)
+            st = lib.moe_layer(*(a[:6] + (counts[i * layers_per_step + li].data_ptr(),) + a[7:]))
+            if st != 0:
+                raise bem.MoeError(st, "moe_layer")
+            n_count += 1
+    torch.cuda.synchronize()
+    decode_calls += n_count
+    if is_decode:
+        check_decode_words(ws, decode_calls)
+    c = counts.cpu()
+    c = c[(c.sum(dim=1) > 0)]
+    touched = float((c > 0).sum(dim=1).double().mean())
+    shared = sh.I_shared > 0
+    dominant = max(stages, key=lambda st_name: stage_us[st_name])
+    nbytes, flops = stage_work(dominant, sh, T, touched, shared)
+    us_layer = total_ms * 1000.0 / n_calls
+    # A layer that is one kernel: its duration is the timed region's per-call
+    # time (back-to-back launches); else the instrumented per-kernel events.
+    kernel_us = us_layer if len(stages) == 1 else stage_us[dominant]
+    dur_s = kernel_us * 1e-6
+    if bound == "hbm":
+        achieved = nbytes / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["traffic"] = measured_traffic(dominant, name)
+    roof.update({"kernel": dominant, "kernel_us": round(kernel_us, 2),
+                 "kernel_us_source": "timed region per call" if len(stages) == 1 else "instrumented events",
+                 "algorithmic_bytes_per_launch": int(nbytes), "algorithmic_flops_per_launch": flops})
+
+    tokens = T * steps * layers_per_step
+    value = tokens / (total_ms / 1000.0)
+    layer_bytes = sum(stage_work(st_name, sh, T, touched, shared)[0] for st_name in stages)
+    layer_flops = sum(stage_work(st_name, sh, T, touched, shared)[1] for st_name in stages)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": name, "T": T, "H": sh.H, "E": sh.E, "top_k": sh.top_k, "I": sh.I,
+                   "I_shared": sh.I_shared, "layers_per_step": layers_per_step, "weight_sets": n_sets,
+                   "weights": "affine 4-bit g64, bf16 scales/biases", "activations": "bf16",
+                   "routing": "Zipf(1.1)-skewed logit offsets" if cfg.zipf else "random router weights",
+                   "shared_expert_gate": bool(args.shared_gate), "router_q8": bool(args.router_q8),
+                   "products": "f16 MFMA, fp32 accumulation; router bf16 MFMA; fp32 output"},
+        "us_per_layer": round(us_layer, 3),
+        "layer_hbm_frac": round(layer_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_mfma_frac": round(layer_flops / (us_layer * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "touched_experts": round(touched, 2),
+        "stages_us": {k_: round(v, 2) for k_, v in stage_us.items()},
+        "stages_note": "per-kernel durations from HIP events around each kernel in an eager instrumented run of "
+                       "the same K steps (the timed region itself carries no per-kernel events)",
+        "host_wall_s": round(host_s, 4),
+        "launch": mode,
+        "timed_weight_sets": "0..%d of %d (the untimed replay just before ran sets %s)" % (
+            min(steps, n_sets) - 1, n_sets,
+            "%d..%d" % (steps, min(2 * steps, n_sets) - 1) if (mode == "graph" and layers_per_step == 1
+                                                                and n_sets > steps) else "0..%d" % (n_sets - 1)),
+        "roofline": roof,
+    }
+    if is_decode:
+        rec["decode_timeout_flag"] = 0  # checked: a set flag raises before this point
+    del sets, tensors, xs, ws, out, counts
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if with_cpu and not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, T, cpu_seconds or args.cpu_seconds, layers_per_step)
+    return rec
+
+
+# workloads the default run times beside the headline decode line
+EXTRA_WORKLOADS = ("decode64", "prefill512", "prefill4096", "stack40")
+EXTRA_KEYS = ("value", "unit", "ms_per_step", "us_per_layer", "steps", "warmup", "config", "layer_hbm_frac",
+              "layer_mfma_frac", "touched_experts", "stages_us", "launch", "timed_weight_sets", "roofline",
+              "cpu_baseline")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+                    help="time one workload only (default: the decode headline line plus every other "
+                         "workload as extra keys)")
     ap.add_argument("--weight-sets", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--extra-cpu-seconds", type=float, default=8.0,
+                    help="oracle seconds for each extra workload of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (three times) for counter calibration")
@@ -218,216 +532,19 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
     import bit_expert_grouped_amd as bem
-    import moe_synth
 
-    cfg_name, layers_per_step, bound, default_sets = WORKLOADS[args.workload]
-    cfg = moe_synth.CONFIGS[cfg_name]
-    sh = cfg.shape
-    T = sh.T
-    big = T >= 512
-    steps = args.steps if args.steps is not None else (20 if big else 200)
-    warmup = args.warmup if args.warmup is not None else (3 if big else 20)
-    n_sets = args.weight_sets or default_sets
-    if layers_per_step > 1:
-        n_sets = layers_per_step
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     bem.lib()
-    alpha = moe_synth.zipf_alpha() if cfg.zipf else None
-    tensors = [moe_synth.device_layer(sh, cfg.seed, l, dev, alpha) for l in range(n_sets)]
-    if args.shared_gate:
-        for l, t in enumerate(tensors):
-            gbits = moe_synth.shared_expert_gate(cfg, l)
-            t["shared_expert_gate"] = torch.from_numpy(gbits.view("int16")).to(dev).view(torch.bfloat16)
-    if args.router_q8:
-        for l, t in enumerate(tensors):
-            r = moe_synth.router_q8(cfg, l)
-            t["router"] = None
-            t["router_q8"] = torch.from_numpy(r["router_q8"].view("int32")).to(dev)
-            for key in ("router_scale", "router_bias"):
-                v = r[key]
-                t[key] = (torch.from_numpy(v.view("int16")).to(dev).view(torch.bfloat16) if v.dtype.itemsize == 2
-                          else torch.from_numpy(v).to(dev))
-    sets = [bem.LayerWeights(t) for t in tensors]
-    n_x = min(steps + warmup, 64) if not big else 4
-    xs = [moe_synth.device_tokens(sh, T, cfg.seed, i, dev) for i in range(n_x)]
-    d = sets[0].dims(T, sh.top_k)
-    ws = bem.workspace(d, dev)
-    out = torch.empty(T, sh.H, dtype=torch.float32, device=dev)
-    stages = bem.moe_layer_stages(d)
-    n_calls = steps * layers_per_step
-    counts = torch.zeros(n_calls, sh.E, dtype=torch.int32, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_calls)]
-    mode = args.mode or "graph"
-    torch.cuda.synchronize()
-
-    # Pre-built argument tuples of the C entry points: the timed loop is one
-    # foreign call per layer call.
-    stream = torch.cuda.current_stream()
-    lib = bem.lib()
-    dref = ctypes.byref(d)
-    for e in evs:
-        for ev in e:
-            ev.record()
-    torch.cuda.synchronize()
-
-    def call_args(i, li, s_handle, with_events):
-        w = sets[li % n_sets] if layers_per_step > 1 else sets[i % n_sets]
-        x = xs[i % n_x]
-        c = i * layers_per_step + li
-        base = (dref, ctypes.byref(w.struct), x.data_ptr(), out.data_ptr(), None, None, None, ws.data_ptr(),
-                ws.numel(), s_handle)
-        if not with_events:
-            return base
-        arr = (ctypes.c_void_p * len(evs[c]))(*[ev.cuda_event for ev in evs[c]])
-        return base + (ctypes.cast(arr, ctypes.c_void_p), len(evs[c])), arr
-
-    def run_eager(i_offset, record):
-        keep = []
-        for i in range(steps):
-            for li in range(layers_per_step):
-                if record:
-                    a, arr = call_args(i, li, stream.cuda_stream, True)
-                    keep.append(arr)
-                    st = lib.moe_layer_events(*a)
-                else:
-                    st = lib.moe_layer(*call_args(i + i_offset, li, stream.cuda_stream, False))
-                if st != 0:
-                    raise bem.MoeError(st, "moe_layer")
-        return keep
-
-    # warm-up (eager)
-    for i in range(warmup):
-        for li in range(layers_per_step):
-            st = lib.moe_layer(*call_args(i + 1000, li, stream.cuda_stream, False))
-            if st != 0:
-                raise bem.MoeError(st, "moe_layer")
-    torch.cuda.synchronize()
-
-    def capture():
-        """One HIP graph holding all K steps."""
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            prepared = [call_args(i, li, side.cuda_stream, False)
-                        for i in range(steps) for li in range(layers_per_step)]
-            with torch.cuda.graph(g, stream=side):
-                for a in prepared:
-                    st = lib.moe_layer(*a)
-                    if st != 0:
-                        raise bem.MoeError(st, "moe_layer (capture)")
-        torch.cuda.synchronize()
-        g.replay()  # one untimed replay
-        torch.cuda.synchronize()
-        return g
-
-    plain = capture() if mode == "graph" else None
-
-    # ---- timed region: exactly K steps, no instrumentation ----
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_host0 = time.perf_counter()
-    start.record()
-    if plain is not None:
-        plain.replay()
-    else:
-        for i in range(steps):
-            for li in range(layers_per_step):
-                st = lib.moe_layer(*call_args(i, li, stream.cuda_stream, False))
-                if st != 0:
-                    raise bem.MoeError(st, "moe_layer")
-    stop.record()
-    torch.cuda.synchronize()
-    host_s = time.perf_counter() - t_host0
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / steps
-
-    # ---- instrumented eager run of the same K steps: HIP events around every kernel ----
-    _keep = run_eager(0, True)
-    torch.cuda.synchronize()
-
-    # per-stage durations inside the timed region
-    stage_us = {s: 0.0 for s in stages}
-    for e in evs:
-        for j, s in enumerate(stages):
-            stage_us[s] += e[j].elapsed_time(e[j + 1]) * 1000.0
-    for s in stages:
-        stage_us[s] /= n_calls
-    # experts touched per call (outside the timed region: the same calls again,
-    # with the per-expert counts requested)
-    for i in range(min(steps, 16)):
-        for li in range(layers_per_step if layers_per_step <= 4 else 4):
-            a = call_args(i, li, stream.cuda_stream, False)
-            st = lib.moe_layer(*(a[:6] + (counts[i * layers_per_step + li].data_ptr(),) + a[7:]))
-            if st != 0:
-                raise bem.MoeError(st, "moe_layer")
-    torch.cuda.synchronize()
-    c = counts.cpu()
-    c = c[(c.sum(dim=1) > 0)]
-    touched = float((c > 0).sum(dim=1).double().mean())
-    shared = sh.I_shared > 0
-    dominant = max(stages, key=lambda s: stage_us[s])
-    nbytes, flops = stage_work(dominant, sh, T, touched, shared)
-    us_layer = total_ms * 1000.0 / n_calls
-    # A layer that is one kernel: its duration is the timed region's per-call
-    # time (back-to-back launches); else the instrumented per-kernel events.
-    kernel_us = us_layer if len(stages) == 1 else stage_us[dominant]
-    dur_s = kernel_us * 1e-6
-    if bound == "hbm":
-        achieved = nbytes / dur_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        achieved = flops / dur_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    traffic = measured_traffic(dominant, args.workload)
-    roof["traffic"] = traffic
-    roof.update({"kernel": dominant, "kernel_us": round(kernel_us, 2),
-                 "kernel_us_source": "timed region per call" if len(stages) == 1 else "instrumented events",
-                 "algorithmic_bytes_per_launch": int(nbytes), "algorithmic_flops_per_launch": flops})
-
-    tokens = T * steps * layers_per_step
-    value = tokens / (total_ms / 1000.0)
-    layer_bytes = sum(stage_work(s, sh, T, touched, shared)[0] for s in stages)
-    layer_flops = sum(stage_work(s, sh, T, touched, shared)[1] for s in stages)
-    rec = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "H": sh.H, "E": sh.E, "top_k": sh.top_k, "I": sh.I,
-                   "I_shared": sh.I_shared, "layers_per_step": layers_per_step, "weight_sets": n_sets,
-                   "weights": "affine 4-bit g64, bf16 scales/biases", "activations": "bf16",
-                   "shared_expert_gate": bool(args.shared_gate), "router_q8": bool(args.router_q8),
-                   "products": "f16 MFMA, fp32 accumulation; router bf16 MFMA; fp32 output"},
-        "us_per_layer": round(us_layer, 3),
-        "layer_hbm_frac": round(layer_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "layer_mfma_frac": round(layer_flops / (us_layer * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-        "touched_experts": round(touched, 2),
-        "stages_us": {s: round(v, 2) for s, v in stage_us.items()},
-        "stages_note": "per-kernel durations from HIP events around each kernel in an eager instrumented run of "
-                       "the same K steps (the timed region itself carries no per-kernel events)",
-        "host_wall_s": round(host_s, 4),
-        "launch": mode,
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, T, args.cpu_seconds)
+    if args.workload is not None:
+        rec = run_workload(args.workload, args.steps, args.warmup, args)
+        print(json.dumps(rec))
+        return
+    # default: the decode headline line, every other workload as an extra key
+    rec = run_workload("decode", args.steps, args.warmup, args)
+    for name in EXTRA_WORKLOADS:
+        sub = run_workload(name, args.steps, args.warmup, args, cpu_seconds=args.extra_cpu_seconds)
+        rec[name] = {k_: sub[k_] for k_ in EXTRA_KEYS if k_ in sub}
+        print("bench: %s %.3f us/layer" % (name, sub["us_per_layer"]), file=sys.stderr, flush=True)
     print(json.dumps(rec))
 
 

@@ -59,6 +59,11 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libbitmoe.so is not built; run `python -m bit_expert_grouped_amd.build`")
+        # torch ships its own HIP runtime under the same soname as the system's
+        # (libamdhip64.so.7), and the first one loaded serves the whole process;
+        # load torch's first so that the library and torch's streams share it
+        import torch  # noqa: F401
+
         L = C.CDLL(LIB_PATH)
         P, D = C.c_void_p, C.POINTER(Dims)
         L.moe_workspace_size.argtypes = [D]

@@ -15,6 +15,7 @@ namespace {
 constexpr int kMaxH = 16384;
 constexpr int kMaxI = 4096;
 constexpr int64_t kMaxT = int64_t(1) << 22;
+constexpr int64_t kMaxPermuteSlots = int64_t(1) << 22;  // T * top_k of one moe_permute call
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -192,6 +193,9 @@ moe_status moe_permute(const moe_dims* d, const int32_t* topk_idx, int32_t* coun
                        int32_t* sorted_slot, void* ws, size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(check_dims(d));
     if (d->T == 0) return MOE_OK;
+    // one workgroup sorts every slot of this call, so its run time grows with
+    // T * top_k; the header bounds that product
+    if ((int64_t)d->T * d->top_k > kMaxPermuteSlots) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(check_ptrs({topk_idx, counts, offsets, sorted_slot}));
     MOE_TRY(check_ws(d, ws, ws_bytes));
     const Layout L = layout_of(d);
@@ -271,8 +275,6 @@ moe_status moe_shared_gate(const moe_dims* d, const uint16_t* x, const uint16_t*
     return MOE_OK;
 }
 
-namespace {
-
 moe_status moe_router_dequant(const moe_dims* d, const uint32_t* router_q8, const void* scale, const void* bias,
                               uint16_t* router_out, hipStream_t stream) {
     MOE_TRY(check_dims(d));
@@ -280,6 +282,8 @@ moe_status moe_router_dequant(const moe_dims* d, const uint32_t* router_q8, cons
     HIP_TRY(launch_router_dequant(router_q8, scale, bias, d->sb_dtype == MOE_BF16, d->E, d->H, router_out, stream));
     return MOE_OK;
 }
+
+namespace {
 
 const char* const kPrefillStages[] = {"router", "topk", "permute", "gate_up", "down", "combine"};
 constexpr int kPrefillStageCount = 6;

@@ -175,6 +175,17 @@ def test_other_calls_check_arguments(lib):
     assert lib.moe_combine(C.byref(d), FAKE, None, None, FAKE, None) == -1
 
 
+def test_permute_slot_limit(lib):
+    """moe_permute sorts at most 2^22 slots (T * top_k) in one call."""
+    big = qwen_dims(1 << 20, top_k=4)  # exactly 2^22 slots: within the limit
+    need = bem.moe_workspace_size(big)
+    assert need > 0
+    # within the limit the call reaches the workspace check (a too-small size is refused)
+    assert lib.moe_permute(C.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, need - 256, None) == -5
+    over = qwen_dims(1 << 20, top_k=5)  # 5 * 2^20 slots
+    assert lib.moe_permute(C.byref(over), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == -3
+
+
 def test_status_strings(lib):
     for code in bem.STATUS:
         assert len(bem.status_string(code)) >= 2

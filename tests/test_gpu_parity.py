@@ -412,6 +412,23 @@ def test_layer_into_bf16_residual_stream(T, H, E, k, I, bf16, res):
     assert np.all(np.isfinite(got)) and np.all(err <= bound)
 
 
+@pytest.mark.parametrize("T,H,E,k,I,bf16,n_sample", [
+    (40, 2560, 16, 4, 768, True, None),    # small-tile prefill path, H > 2048 and I > 512
+    (700, 2304, 16, 2, 1024, False, 24),   # large-batch path, fp32 scales, sampled tokens
+])
+def test_prefill_wide_shapes(T, H, E, k, I, bf16, n_sample):
+    cfg, w, x = _custom(T, H, E, k, I, I, bf16, seed=300 + T)
+    tokens = None
+    if n_sample is not None:
+        rng = np.random.default_rng(T)
+        tokens = np.sort(rng.choice(T, n_sample, replace=False)).astype(np.int32)
+    ref = oracle.moe_layer(w, x, k, tokens=tokens)
+    out, idx, wt, counts = run_layer(w, x, k)
+    assert_same_routing(idx, wt, ref["idx"], ref["w"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    assert_close(out if tokens is None else out[tokens], ref["out"], "wide prefill T%d H%d I%d" % (T, H, I))
+
+
 def test_hot_expert_spans_many_tiles():
     bias = np.zeros(32, dtype=np.float32)
     bias[5] = 50.0
@@ -580,6 +597,11 @@ def test_decode_path_real_shapes(T):
     (2, 512, 40, 3, 128, True, True),
     (1, 128, 8, 8, 64, True, False),
     (4, 2560, 64, 4, 192, True, True),
+    # down rows too long for LDS (I > 512): the down workgroups read them from memory
+    (2, 1024, 16, 2, 1024, False, True),
+    # ... and float32 scales and biases of I = 2048 that do not fit beside them either
+    (1, 512, 8, 2, 2048, False, True),
+    (3, 4096, 16, 4, 4096, True, True),    # the largest intermediate size the library accepts
 ])
 def test_decode_path_other_shapes(T, H, E, k, I, bf16, shared):
     cfg, w, x = _custom(T, H, E, k, I, I, bf16, seed=600 + T + E)
@@ -680,3 +702,38 @@ def test_graph_replays_match_eager(T):
         ref = o_e.cpu().numpy().astype(np.float64)
         assert np.abs(out.cpu().numpy() - ref).max() <= 1e-3 * rms(ref)
         assert control_words(ws)[1] == 0
+
+
+def test_back_to_back_decode_calls_in_one_graph():
+    """Ten decode calls captured into one graph, each with its own input and
+    output and no synchronisation between them: every output matches the oracle,
+    no wait timed out (word 255) and the call counter (word 0) advanced by the
+    number of calls on every replay.  This is how the timed decode steps run."""
+    n = 10
+    cfg, w, x = _custom(n, 2048, 256, 8, 512, 512, True, seed=1500)
+    m = bem()
+    lw = m.upload_weights(w)
+    d = lw.dims(1, 8)
+    ws = m.workspace(d)
+    xs = [m.bf16_tensor(x[i:i + 1]) for i in range(n)]
+    outs = [torch.full((1, 2048), float("nan"), device="cuda") for _ in range(n)]
+    refs = [oracle.moe_layer(w, x[i:i + 1], 8)["out"] for i in range(n)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n):
+                m.moe_layer(xs[i], lw, 8, out=outs[i], ws=ws)
+    torch.cuda.synchronize()
+    assert control_words(ws) == (0, 0)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert control_words(ws) == ((rep + 1) * n, 0)
+        assert done_counters(ws) == [0] * 9
+        for i in range(n):
+            assert_close(outs[i].cpu().numpy(), refs[i], "graph replay %d call %d" % (rep, i))
