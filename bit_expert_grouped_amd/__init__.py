@@ -22,7 +22,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNS
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_shared_gate",
            "moe_combine_gated", "moe_router_dequant", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
-           "moe_status_string")
+           "moe_layer_no_alloc", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -80,12 +80,13 @@ def lib():
         L.moe_layer.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P]
         L.moe_layer_residual.argtypes = [D, C.POINTER(Weights), P, P, P, P, C.c_size_t, P]
         L.moe_layer_events.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P, P, C.c_int32]
+        L.moe_layer_no_alloc.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P]
         L.moe_layer_stage_count.argtypes = [D]
         L.moe_layer_stage_count.restype = C.c_int32
         L.moe_layer_stage_name.argtypes = [D, C.c_int32]
         L.moe_layer_stage_name.restype = C.c_char_p
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_combine_gated",
-                     "moe_shared_gate", "moe_layer", "moe_layer_residual", "moe_layer_events"):
+                     "moe_shared_gate", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_no_alloc"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -293,6 +294,29 @@ def moe_layer_residual(x, weights: "LayerWeights", top_k, residual=None, out=Non
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
     _check(lib().moe_layer_residual(C.byref(d), C.byref(weights.struct), _p(x), _p(residual), _p(out), _p(ws),
                                     ws.numel(), _stream()), "moe_layer_residual")
+    return out
+
+
+NO_ALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NO_ALLOC_SCRATCH_BYTES
+
+
+def moe_layer_no_alloc(x, weights: "LayerWeights", top_k, out=None, want_routing=False):
+    """moe_layer on the library's static per-device scratch (no workspace argument)."""
+    import torch
+
+    T, H = x.shape
+    d = weights.dims(T, top_k)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.float32, device=x.device)
+    idx = w = counts = None
+    if want_routing:
+        idx = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+        w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+        counts = torch.empty(weights.E, dtype=torch.int32, device=x.device)
+    _check(lib().moe_layer_no_alloc(C.byref(d), C.byref(weights.struct), _p(x), _p(out), _p(idx), _p(w),
+                                    _p(counts), _stream()), "moe_layer_no_alloc")
+    if want_routing:
+        return out, idx, w, counts
     return out
 
 

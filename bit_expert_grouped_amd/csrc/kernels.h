@@ -187,6 +187,9 @@ hipError_t launch_combine16(const _Float16* y16, const float* topk_w, bool share
 hipError_t launch_residual_bf16(const float* y, const uint16_t* residual, int T, int H, uint16_t* out16,
                                 hipStream_t stream);
 
+// bytes (a multiple of 16) from p on set to zero, by a kernel
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+
 // shared_w[t] = sigmoid(x[t] . g), x [T][H] and g [H] bf16
 hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* g, int T, int H, float* shared_w,
                               hipStream_t stream);

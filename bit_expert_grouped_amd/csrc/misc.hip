@@ -1,6 +1,8 @@
 // Small elementwise kernels for gfx950: the float16 activation copy used by the
 // expert products of the step-by-step API, the stand-alone weighted combine,
 // and the layer's combine over float16 expert rows.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -51,6 +53,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         }
         reinterpret_cast<float4*>(out + (size_t)t * H)[c] = acc;
     }
+}
+
+// n 16-byte units from p on set to zero (a kernel rather than a memset, so that
+// a captured graph replays it exactly)
+__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // float32 -> bfloat16, round to nearest even (finite values)
@@ -200,6 +209,14 @@ hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* g, int T, int H
                               hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(shared_gate_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, x, g, T, H, shared_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+    const int64_t n = (int64_t)(bytes / 16);
+    if (n == 0) return hipSuccess;
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint4*>(p), n);
     return hipGetLastError();
 }
 

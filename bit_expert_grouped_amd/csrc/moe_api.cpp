@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -299,7 +301,7 @@ int stage_count(const moe_dims* d) { return use_decode_path(d) ? kDecodeStageCou
 moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out,
                       int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                       hipStream_t stream, hipEvent_t* events, int32_t n_events, const uint16_t* residual = nullptr,
-                      uint16_t* out16 = nullptr) {
+                      uint16_t* out16 = nullptr, bool validate_only = false) {
     MOE_TRY(check_dims(d));
     if (d->out_dtype != (out16 ? MOE_BF16 : MOE_F32)) return MOE_ERR_UNSUPPORTED;
     if (d->T == 0) return MOE_OK;
@@ -326,6 +328,7 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         for (int i = 0; i <= n_stages; i++)
             if (!events[i]) return MOE_ERR_NULL;
     }
+    if (validate_only) return MOE_OK;
     const Layout L = layout_of(d);
     auto mark = [&](int i) -> bool { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
     // the router the kernels score with; an 8-bit one is restored first, inside
@@ -461,6 +464,75 @@ moe_status moe_layer_events(const moe_dims* d, const moe_weights* wts, const uin
     if (!events) return MOE_ERR_NULL;
     return layer_impl(d, wts, x, out, topk_idx_out, topk_w_out, counts_out, ws, ws_bytes, stream, events,
                       n_events);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ------------------------------------------------------- moe_layer_no_alloc
+// The workspace of moe_layer_no_alloc: a file-scope device array, one copy per
+// device, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (in host code the name only stands for the device
+// variable); it looks up each device's address once with hipGetSymbolAddress
+// and uses that.
+constexpr size_t kNoAllocBytes = MOE_NO_ALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+bool g_scratch_ready[kMaxDevices];  // its decode region was cleared by a call outside graph capture
+
+// The current device's scratch address (looked up on the device's first call).
+moe_status scratch_address(int* dev_out, void** ptr_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *dev_out = dev;
+    *ptr_out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+// The layer's workspace contract needs a zero decode region before the first
+// call (the rest of the workspace is written before it is read in every call).
+// Until a call outside graph capture has cleared it, every call clears it
+// first with a kernel on its stream; a captured clearing kernel then runs on
+// every replay, which leaves the region as consistent as a first call does.
+moe_status scratch_prepare(int dev, void* ptr, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ready[dev]) return MOE_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_zero(ptr, kDecodeRegionBytes, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (cs == hipStreamCaptureStatusNone) g_scratch_ready[dev] = true;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_no_alloc(const moe_dims* d, const moe_weights* wts, const uint16_t* x, void* out,
+                              int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+    if (d->T == 0) return MOE_OK;
+    if (layout_of(d).total > kNoAllocBytes) return MOE_ERR_WORKSPACE;
+    int dev = 0;
+    void* ws = nullptr;
+    MOE_TRY(scratch_address(&dev, &ws));
+    // every argument is checked before anything is enqueued
+    MOE_TRY(layer_impl(d, wts, x, out, topk_idx_out, topk_w_out, counts_out, ws, kNoAllocBytes, stream, nullptr, 0,
+                       nullptr, nullptr, true));
+    MOE_TRY(scratch_prepare(dev, ws, stream));
+    return layer_impl(d, wts, x, out, topk_idx_out, topk_w_out, counts_out, ws, kNoAllocBytes, stream, nullptr, 0);
 }
 
 int32_t moe_layer_stage_count(const moe_dims* d) {

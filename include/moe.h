@@ -20,9 +20,10 @@
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
  *     every buffer (weights, activations, outputs, workspace); the library
  *     allocates nothing, frees nothing, keeps no pointer after returning and
- *     holds no mutable global state.  Calls only ENQUEUE work on `stream`
- *     (stream-ordered: buffers must stay valid until that work completes);
- *     none synchronises the host.
+ *     holds no mutable global state, except the static per-device scratch of
+ *     moe_layer_no_alloc and its host-side record of each device's address.
+ *     Calls only ENQUEUE work on `stream` (stream-ordered: buffers must stay
+ *     valid until that work completes); none synchronises the host.
  *   - Every check runs on the host before anything is enqueued.  A status other
  *     than MOE_OK means nothing was enqueued, except MOE_ERR_HIP, which reports
  *     a failed launch (the stream may then hold part of the work).
@@ -210,6 +211,30 @@ moe_status moe_router_dequant(const moe_dims *dims, const uint32_t *router_q8, c
  * (T <= 4) adds one small kernel after the layer kernel. */
 moe_status moe_layer_residual(const moe_dims *dims, const moe_weights *weights /* host */, const uint16_t *x,
                               const uint16_t *residual, uint16_t *out, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Bytes of the device scratch that moe_layer_no_alloc uses in place of a
+ * workspace (32 MiB per device; enough for every T up to 512 at H=2048, E=256,
+ * top_k=8, I=512). */
+#define MOE_NO_ALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* moe_layer for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The same work and outputs as moe_layer, on the current
+ * device (hipGetDevice; `stream` must belong to it), with the workspace taken
+ * from a static device array of MOE_NO_ALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends.  Nothing is
+ * allocated or freed.  Dims whose moe_workspace_size() exceeds that:
+ * MOE_ERR_WORKSPACE; dims->out_dtype must be MOE_F32 (else
+ * MOE_ERR_UNSUPPORTED).  Every argument is checked before anything is
+ * enqueued.  The scratch keeps what the last call left; until a call outside
+ * graph capture has run on a device, each call first clears the decode region
+ * of the scratch with a small kernel on `stream` (captured, that kernel runs
+ * on every replay).  All calls on one device share the one scratch: calls that
+ * overlap in time on one device (on different streams, or from different
+ * threads without ordering) race and give undefined results. */
+moe_status moe_layer_no_alloc(const moe_dims *dims, const moe_weights *weights /* host */, const uint16_t *x,
+                              void *out, int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out,
                               hipStream_t stream);
 
 /* Instrumentation variant of moe_layer: the same work, plus HIP events recorded

@@ -186,6 +186,21 @@ def test_permute_slot_limit(lib):
     assert lib.moe_permute(C.byref(over), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == -3
 
 
+def test_no_alloc_checks(lib):
+    """moe_layer_no_alloc: dims beyond its static scratch and bad arguments are
+    refused on the host, before any device call."""
+    big = qwen_dims(1024)
+    assert bem.moe_workspace_size(big) > bem.NO_ALLOC_SCRATCH_BYTES
+    w = _weights()
+    assert lib.moe_layer_no_alloc(C.byref(big), C.byref(w), FAKE, FAKE, None, None, None, None) == -5
+    assert lib.moe_layer_no_alloc(C.byref(qwen_dims(8, out_dtype=bem.MOE_BF16)), C.byref(w), FAKE, FAKE,
+                                  None, None, None, None) == -3
+    assert lib.moe_layer_no_alloc(C.byref(qwen_dims(8, H=100)), C.byref(w), FAKE, FAKE, None, None, None,
+                                  None) == -2
+    e = qwen_dims(0)
+    assert lib.moe_layer_no_alloc(C.byref(e), None, None, None, None, None, None, None) == 0
+
+
 def test_status_strings(lib):
     for code in bem.STATUS:
         assert len(bem.status_string(code)) >= 2
