@@ -74,6 +74,8 @@ def lib():
         L.oracle_shared_gate.argtypes = [i32, i32, P, P, P]
         L.oracle_shared_gate.restype = None
         L.oracle_combine.restype = None
+        L.oracle_rmsnorm.argtypes = [i32, P, P, C.c_double, P]
+        L.oracle_rmsnorm.restype = None
         L.oracle_moe_layer.argtypes = [C.POINTER(Layer), i32, P, P, P, P, P, P, P, P]
         L.oracle_moe_layer.restype = C.c_int
         _lib = L
@@ -205,6 +207,20 @@ def shared_gate(x, gate):
     g = _c(gate, np.uint16)
     out = np.empty(x.shape[0], dtype=np.float64)
     lib().oracle_shared_gate(x.shape[0], x.shape[1], x.ctypes.data, g.ctypes.data, out.ctypes.data)
+    return out
+
+
+RMSNORM_EPS = 1e-6  # the epsilon of the decode stack's normalisation (R17)
+
+
+def rmsnorm(x, gamma=None, eps=RMSNORM_EPS):
+    """R17: bf16(x / sqrt(mean(x^2) + eps) * gamma) of each row of x [n][H] (bf16
+    bits); gamma [H] bf16 bits or None (1).  Returns bf16 bits [n][H]."""
+    x = _c(np.atleast_2d(x), np.uint16)
+    g = _c(gamma, np.uint16)
+    out = np.empty_like(x)
+    for r in range(x.shape[0]):
+        lib().oracle_rmsnorm(x.shape[1], x[r].ctypes.data, _ptr(g), float(eps), out[r].ctypes.data)
     return out
 
 

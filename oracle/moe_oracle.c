@@ -41,6 +41,10 @@
  *      shared expert: a bfloat16 vector g [H] scales the shared expert's
  *      output by sigmoid(sum_h x[t][h] * g[h]); without g the weight is one (R5).
  *      This is the shared-expert gate of Qwen's mixture-of-experts checkpoints.
+ *   R17 (decode stack, not on the pages) each layer of a stack of layers reads
+ *      the root-mean-square normalisation of the bf16 residual stream,
+ *      bf16(x / sqrt(mean(x^2) + eps) * gamma), and adds its output to the
+ *      stream: how a pre-norm decoder feeds its mixture-of-experts blocks.
  *   R16 (checkpoint conformity, not on the pages) an optional 8-bit router in
  *      the MLX affine layout: byte k of a row sits at bits [8*(k%4), 8*(k%4)+8)
  *      of word k/4, groups of 64 columns carry a scale and a bias, and the
@@ -124,6 +128,41 @@ static uint16_t f32_to_bf16_nearest_even(float f)
     if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
         upper += 1;
     return (uint16_t)upper;
+}
+
+/* double -> bfloat16 bits, rounded once to the nearest (ties to even): the
+ * value's significand is rounded to 8 bits in double precision, which is
+ * exact, and the result is then exactly representable in float32. */
+static uint16_t f64_to_bf16_nearest_even(double v)
+{
+    if (v == 0.0)
+        return signbit(v) ? 0x8000u : 0u;
+    int e;
+    const double m = frexp(v, &e);            /* v = m * 2^e, 0.5 <= |m| < 1 */
+    const double r = nearbyint(ldexp(m, 8));  /* 8 significant bits, ties to even */
+    const float f = (float)ldexp(r, e - 8);
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Root-mean-square normalisation of one row of the residual stream, the input
+ * of each layer of a decode stack (R17, not on the pages: how a pre-norm
+ * decoder feeds its mixture-of-experts block):
+ *   out[h] = bf16(x[h] / sqrt(mean_h x[h]^2 + eps) * gamma[h]),
+ * gamma[h] = 1 when gamma is NULL; double precision, rounded once to bf16. */
+void oracle_rmsnorm(int32_t H, const uint16_t *x, const uint16_t *gamma, double eps, uint16_t *out)
+{
+    double ss = 0.0;
+    for (int32_t h = 0; h < H; h++) {
+        const double v = bf16_bits_value(x[h]);
+        ss += v * v;
+    }
+    const double r = 1.0 / sqrt(ss / (double)H + eps);
+    for (int32_t h = 0; h < H; h++) {
+        const double g = gamma ? bf16_bits_value(gamma[h]) : 1.0;
+        out[h] = f64_to_bf16_nearest_even(bf16_bits_value(x[h]) * r * g);
+    }
 }
 
 /* The 8-bit router restored to bfloat16: out[e][h] = bf16(fmaf(s, q, b)) with

@@ -453,3 +453,40 @@ def test_layer_with_q8_router_uses_the_restored_matrix():
     a, b = oracle.moe_layer(wq, x, 2), oracle.moe_layer(dense, x, 2)
     np.testing.assert_array_equal(a["idx"], b["idx"])
     np.testing.assert_array_equal(a["out"], b["out"])
+
+
+# ------------------------------------------------------------------ RMSNorm of the residual stream (R17)
+
+
+@pytest.mark.parametrize("ex", _load("rmsnorm_examples.json")["examples"], ids=str)
+def test_rmsnorm_hand_examples(ex):
+    x = moe_synth.f32_to_bf16_bits(np.array(ex["x"], dtype=np.float32))
+    g = None if ex["gamma"] is None else moe_synth.f32_to_bf16_bits(np.array(ex["gamma"], dtype=np.float32))
+    y = moe_synth.bf16_bits_to_f32(oracle.rmsnorm(x, g, eps=ex["eps"])[0])
+    np.testing.assert_array_equal(y, np.array(ex["y"], dtype=np.float32))
+
+
+def test_rmsnorm_power_of_two_scale_invariance():
+    """eps = 0: scaling the row by 2^k scales mean(x^2) by 4^k and leaves every
+    output bit as it was."""
+    rng = np.random.default_rng(11)
+    x = moe_synth.f32_to_bf16_bits(rng.standard_normal(2048).astype(np.float32))
+    base = oracle.rmsnorm(x, eps=0.0)
+    for k in (-3, 5, 9):
+        xs = moe_synth.f32_to_bf16_bits(moe_synth.bf16_bits_to_f32(x) * np.float32(2.0 ** k))
+        np.testing.assert_array_equal(oracle.rmsnorm(xs, eps=0.0), base)
+
+
+def test_rmsnorm_unit_rms_and_gamma():
+    """gamma absent: the output's root mean square is 1 up to bf16 rounding; a
+    gamma of 2 doubles every output exactly; a gamma of -1 negates it."""
+    rng = np.random.default_rng(12)
+    x = moe_synth.f32_to_bf16_bits((rng.standard_normal(2048) * 37.0).astype(np.float32))
+    y = moe_synth.bf16_bits_to_f32(oracle.rmsnorm(x, eps=0.0)[0]).astype(np.float64)
+    assert abs(np.sqrt(np.mean(y * y)) - 1.0) < 2.0 ** -8
+    two = moe_synth.f32_to_bf16_bits(np.full(2048, 2.0, dtype=np.float32))
+    y2 = moe_synth.bf16_bits_to_f32(oracle.rmsnorm(x, two, eps=0.0)[0]).astype(np.float64)
+    np.testing.assert_array_equal(y2, 2.0 * y)
+    neg = moe_synth.f32_to_bf16_bits(np.full(2048, -1.0, dtype=np.float32))
+    yn = moe_synth.bf16_bits_to_f32(oracle.rmsnorm(x, neg, eps=0.0)[0]).astype(np.float64)
+    np.testing.assert_array_equal(yn, -y)

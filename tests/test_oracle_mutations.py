@@ -39,6 +39,10 @@ MUTATIONS = {
     "q8 router byte order reversed": ("(word >> (8 * (h % 4)))", "(word >> (8 * (3 - h % 4)))"),
     "q8 router ties rounded up": ("(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
     "q8 router scale and bias swapped": ("fmaf(sv, (float)q, bv)", "fmaf(bv, (float)q, sv)"),
+    "rmsnorm sum instead of mean": ("sqrt(ss / (double)H + eps)", "sqrt(ss + eps)"),
+    "rmsnorm eps ignored": ("sqrt(ss / (double)H + eps)", "sqrt(ss / (double)H)"),
+    "rmsnorm gamma ignored": ("const double g = gamma ? bf16_bits_value(gamma[h]) : 1.0;", "const double g = 1.0;"),
+    "rmsnorm rounds toward zero": ("nearbyint(ldexp(m, 8))", "trunc(ldexp(m, 8))"),
     "permute not stable": ("sorted_slot[cursor[idx[s]]++] = s;", "sorted_slot[offsets[idx[s] + 1] - 1 - (cursor[idx[s]]++ - offsets[idx[s]])] = s;"),
 }
 
