@@ -60,6 +60,8 @@ WORKLOADS = {
     "prefill512": ("prefill512", 1, "hbm", 4),
     "prefill4096": ("prefill4096", 1, "mfma", 4),
     "stack40": ("stack40", 40, "mfma", 40),
+    # one decode step (one token) through 40 layers in one launch of moe_decode_stack
+    "decode_stack40": ("decode", 40, "hbm", 40),
 }
 
 
@@ -105,6 +107,7 @@ def stage_work(name, sh, T, touched, shared):
 # kernel name -> source file that holds it (for the counter figures' freshness)
 KERNEL_SOURCES = {
     "decode_layer": "bit_expert_grouped_amd/csrc/decode.hip",
+    "decode_stack": "bit_expert_grouped_amd/csrc/decode_stack.hip",
     "router": "bit_expert_grouped_amd/csrc/router.hip",
     "topk": "bit_expert_grouped_amd/csrc/router.hip",
     "permute": "bit_expert_grouped_amd/csrc/permute.hip",
@@ -489,8 +492,117 @@ def run_workload(name, steps_arg, warmup_arg, args, with_cpu=True, cpu_seconds=N
     return rec
 
 
+def run_decode_stack(name, steps_arg, warmup_arg, args, with_cpu=True, cpu_seconds=None):
+    """One decode step of one token through a stack of 40 layers per launch
+    (moe_decode_stack: each layer reads the RMS-normalised residual stream and
+    adds its output to it).  40 distinct layers (centred biases, the stack's
+    weight recipe) are resident: a step streams every layer's touched experts
+    (about 680 MB), far beyond the 256 MB last-level cache."""
+    import torch
+
+    import bit_expert_grouped_amd as bem
+    import moe_synth
+
+    cfg_name, n_layers, bound, _ = WORKLOADS[name]
+    cfg = moe_synth.CONFIGS[cfg_name]
+    sh = cfg.shape
+    steps = steps_arg if steps_arg is not None else 20
+    warmup = warmup_arg if warmup_arg is not None else 5
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stack = bem.StackWeights(moe_synth.device_stack(sh, cfg.seed, n_layers, dev))
+    lib = bem.lib()
+    d = stack.dims(sh.top_k)
+    ws = bem.workspace(d, dev)
+    n_x = min(steps + warmup, 32)
+    xs = [moe_synth.device_tokens(sh, 1, cfg.seed, 5000 + i, dev) for i in range(n_x)]
+    outs = [torch.empty(1, sh.H, dtype=torch.bfloat16, device=dev) for _ in range(n_x)]
+    stream = torch.cuda.current_stream()
+
+    def args_for(i, s_handle):
+        return (ctypes.byref(d), ctypes.byref(stack.layer0.struct), None, ctypes.byref(stack.strides), n_layers,
+                xs[i % n_x].data_ptr(), outs[i % n_x].data_ptr(), None, None, None, None, None, ws.data_ptr(),
+                ws.numel(), s_handle)
+
+    calls = 0
+    for i in range(warmup):
+        st = lib.moe_decode_stack(*args_for(i, stream.cuda_stream))
+        if st != 0:
+            raise bem.MoeError(st, "moe_decode_stack")
+        calls += 1
+    torch.cuda.synchronize()
+    mode = args.mode or "graph"
+    g = None
+    if mode == "graph":
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            prepared = [args_for(i, side.cuda_stream) for i in range(steps)]
+            with torch.cuda.graph(g, stream=side):
+                for a in prepared:
+                    st = lib.moe_decode_stack(*a)
+                    if st != 0:
+                        raise bem.MoeError(st, "moe_decode_stack (capture)")
+        torch.cuda.synchronize()
+        g.replay()  # one untimed replay
+        torch.cuda.synchronize()
+        calls += steps
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            st = lib.moe_decode_stack(*args_for(i, stream.cuda_stream))
+            if st != 0:
+                raise bem.MoeError(st, "moe_decode_stack")
+    stop.record()
+    torch.cuda.synchronize()
+    calls += steps
+    total_ms = start.elapsed_time(stop)
+    words = ws[:16384].view(torch.int32).cpu()
+    if int(words[255]) != 0:
+        raise RuntimeError("a device-side wait of the stack kernel timed out (workspace word 255)")
+    if int(words[2048]) != calls * n_layers:
+        raise RuntimeError("stack epoch reads %d after %d calls of %d layers" % (int(words[2048]), calls, n_layers))
+    us_step = total_ms * 1000.0 / steps
+    us_layer = us_step / n_layers
+    nbytes, flops = stage_work("decode_layer", sh, 1, float(sh.top_k), sh.I_shared > 0)
+    launch_bytes, launch_flops = nbytes * n_layers, flops * n_layers
+    achieved = launch_bytes / (us_step * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode_stack", name),
+            "kernel": "decode_stack", "kernel_us": round(us_step, 2),
+            "kernel_us_source": "timed region per launch (one launch per step)",
+            "algorithmic_bytes_per_launch": int(launch_bytes), "algorithmic_flops_per_launch": launch_flops}
+    rec = {
+        "metric": METRIC, "value": round(n_layers * steps / (total_ms / 1000.0), 2), "unit": "token-layers/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(total_ms / steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": name, "T": 1, "H": sh.H, "E": sh.E, "top_k": sh.top_k, "I": sh.I,
+                   "I_shared": sh.I_shared, "layers_per_step": n_layers, "weight_sets": n_layers,
+                   "weights": "affine 4-bit g64, bf16 scales/biases, biases centred on the code midpoint",
+                   "activations": "bf16 residual stream, RMS-normalised before each layer",
+                   "products": "f16 dot products, fp32 accumulation; output sums in a fixed order"},
+        "us_per_layer": round(us_layer, 3),
+        "layer_hbm_frac": roof["frac"],
+        "touched_experts": float(sh.top_k),
+        "launch": mode,
+        "roofline": roof,
+    }
+    del stack, xs, outs, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if with_cpu and not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, 1, cpu_seconds or args.cpu_seconds, n_layers)
+    return rec
+
+
 # workloads the default run times beside the headline decode line
-EXTRA_WORKLOADS = ("decode64", "prefill512", "prefill4096", "stack40")
+EXTRA_WORKLOADS = ("decode_stack40", "decode64", "prefill512", "prefill4096", "stack40")
 EXTRA_KEYS = ("value", "unit", "ms_per_step", "us_per_layer", "steps", "warmup", "config", "layer_hbm_frac",
               "layer_mfma_frac", "touched_experts", "stages_us", "launch", "timed_weight_sets", "roofline",
               "cpu_baseline")
@@ -535,14 +647,17 @@ def main():
     import bit_expert_grouped_amd as bem
 
     bem.lib()
+    def run(name, **kw):
+        fn = run_decode_stack if name.startswith("decode_stack") else run_workload
+        return fn(name, args.steps, args.warmup, args, **kw)
+
     if args.workload is not None:
-        rec = run_workload(args.workload, args.steps, args.warmup, args)
-        print(json.dumps(rec))
+        print(json.dumps(run(args.workload)))
         return
     # default: the decode headline line, every other workload as an extra key
-    rec = run_workload("decode", args.steps, args.warmup, args)
+    rec = run("decode")
     for name in EXTRA_WORKLOADS:
-        sub = run_workload(name, args.steps, args.warmup, args, cpu_seconds=args.extra_cpu_seconds)
+        sub = run(name, cpu_seconds=args.extra_cpu_seconds)
         rec[name] = {k_: sub[k_] for k_ in EXTRA_KEYS if k_ in sub}
         print("bench: %s %.3f us/layer" % (name, sub["us_per_layer"]), file=sys.stderr, flush=True)
     print(json.dumps(rec))

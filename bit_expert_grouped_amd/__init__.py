@@ -22,7 +22,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNS
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_shared_gate",
            "moe_combine_gated", "moe_router_dequant", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
-           "moe_layer_no_alloc", "moe_status_string")
+           "moe_layer_no_alloc", "moe_decode_stack", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -42,6 +42,19 @@ class QMat(C.Structure):
 
 class Ffn(C.Structure):
     _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+class QMatStride(C.Structure):
+    _fields_ = [("q", C.c_int64), ("scale", C.c_int64), ("bias", C.c_int64)]
+
+
+class FfnStride(C.Structure):
+    _fields_ = [("gate", QMatStride), ("up", QMatStride), ("down", QMatStride)]
+
+
+class LayerStrides(C.Structure):
+    _fields_ = [("router", C.c_int64), ("logit_bias", C.c_int64), ("norm_weight", C.c_int64), ("experts", FfnStride),
+                ("shared", FfnStride)]
 
 
 class Weights(C.Structure):
@@ -81,12 +94,15 @@ def lib():
         L.moe_layer_residual.argtypes = [D, C.POINTER(Weights), P, P, P, P, C.c_size_t, P]
         L.moe_layer_events.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P, C.c_size_t, P, P, C.c_int32]
         L.moe_layer_no_alloc.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P]
+        L.moe_decode_stack.argtypes = [D, C.POINTER(Weights), P, C.POINTER(LayerStrides), C.c_int32, P, P, P, P, P,
+                                       P, P, P, C.c_size_t, P]
         L.moe_layer_stage_count.argtypes = [D]
         L.moe_layer_stage_count.restype = C.c_int32
         L.moe_layer_stage_name.argtypes = [D, C.c_int32]
         L.moe_layer_stage_name.restype = C.c_char_p
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_combine_gated",
-                     "moe_shared_gate", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_no_alloc"):
+                     "moe_shared_gate", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_no_alloc",
+                     "moe_decode_stack"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -295,6 +311,65 @@ def moe_layer_residual(x, weights: "LayerWeights", top_k, residual=None, out=Non
     _check(lib().moe_layer_residual(C.byref(d), C.byref(weights.struct), _p(x), _p(residual), _p(out), _p(ws),
                                     ws.numel(), _stream()), "moe_layer_residual")
     return out
+
+
+class StackWeights:
+    """Device tensors of n_layers stacked layers (every tensor with a leading
+    layer dimension, as moe_synth.device_stack draws them) plus the C structs
+    of moe_decode_stack: layer 0's pointers and each tensor's layer stride."""
+
+    def __init__(self, tensors: dict):
+        self.t = tensors
+        self.n_layers = tensors["gate_q"].shape[0]
+        self.layer0 = LayerWeights({k: (None if v is None else v[0]) for k, v in tensors.items()
+                                    if k != "norm_weight"})
+        self.E, self.I, self.H, self.I_shared = self.layer0.E, self.layer0.I, self.layer0.H, self.layer0.I_shared
+        self.sb_bf16 = self.layer0.sb_bf16
+
+        def st(name):
+            v = tensors.get(name)
+            return 0 if v is None else v.stride(0) * v.element_size()
+
+        def qs(prefix, name):
+            return QMatStride(st(prefix + name + "_q"), st(prefix + name + "_s"), st(prefix + name + "_b"))
+
+        self.norm_weight = tensors.get("norm_weight")
+        self.strides = LayerStrides(st("router"), st("logit_bias"), st("norm_weight"),
+                                    FfnStride(qs("", "gate"), qs("", "up"), qs("", "down")),
+                                    FfnStride(qs("shared_", "gate"), qs("shared_", "up"), qs("shared_", "down"))
+                                    if self.I_shared else FfnStride())
+
+    def dims(self, top_k) -> Dims:
+        return dims(1, self.H, self.E, top_k, self.I, self.I_shared, self.sb_bf16, out_dtype=MOE_BF16)
+
+
+def moe_decode_stack(x, stack: StackWeights, top_k, x_out=None, ws=None, record=False):
+    """One token x [1][H] bf16 through every layer of ``stack`` in one kernel:
+    x(l+1) = bf16(x(l) + layer_l(rmsnorm(x(l)))).  Returns x_out, or with
+    record=True (x_out, layer_x [L][H] bf16, layer_in [L][H] bf16, layer_out
+    [L][H] float32, topk_idx [L][k], topk_w [L][k])."""
+    import torch
+
+    d = stack.dims(top_k)
+    H, L = stack.H, stack.n_layers
+    if ws is None:
+        ws = workspace(d, x.device)
+    if x_out is None:
+        x_out = torch.empty(1, H, dtype=torch.bfloat16, device=x.device)
+    rec = [None] * 5
+    if record:
+        rec = [torch.empty(L, H, dtype=torch.bfloat16, device=x.device),
+               torch.empty(L, H, dtype=torch.bfloat16, device=x.device),
+               torch.empty(L, H, dtype=torch.float32, device=x.device),
+               torch.empty(L, top_k, dtype=torch.int32, device=x.device),
+               torch.empty(L, top_k, dtype=torch.float32, device=x.device)]
+    nw = stack.norm_weight
+    _check(lib().moe_decode_stack(C.byref(d), C.byref(stack.layer0.struct), _p(nw[0]) if nw is not None else None,
+                                  C.byref(stack.strides), L, _p(x), _p(x_out), *[_p(r) for r in rec], _p(ws),
+                                  ws.numel(), _stream()), "moe_decode_stack")
+    if record:
+        return tuple([x_out] + rec)
+    return x_out
 
 
 NO_ALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NO_ALLOC_SCRATCH_BYTES

@@ -167,6 +167,71 @@ struct DecodeArgs {
     const uint16_t* shared_gate; // [H] bf16 gate vector of the shared expert, or nullptr (weight 1)
 };
 
+// Persistent multi-layer decode (one token through L stacked layers in one
+// launch, each layer reading the RMS-normalised residual stream): a grid of kStackGrid workgroups, all resident at once, that hand
+// values over through words of the stack region below (fixed offsets after the
+// one-layer decode region, zero before the first call).  Limits: T = 1,
+// H <= kStackMaxH, I <= kStackMaxI, top_k * I / 16 <= kStackGrid and
+// top_k * H / 64 <= kStackGrid.
+constexpr int kStackGrid = 256;
+constexpr int kStackMaxH = 2048;
+constexpr int kStackMaxI = 512;
+// Copies of the values every workgroup (or a slot's workgroups) read, so that
+// each copy has few readers: polled words are what floods the memory system.
+constexpr int kStackLogitCopies = 32;    // of the logits: 8 readers each
+constexpr int kStackSharedHCopies = 32;  // of the shared expert's h: 8 readers each
+constexpr int kStackRoutedHCopies = 4;   // of each routed slot's h: 8 readers each
+constexpr int kStackXCopies = 32;        // of the stream entering a layer: 8 readers each
+constexpr int kStackXWords = kStackMaxH / 8 * 3;  // per copy: 3 words {16-bit tag, 3 bf16} per 8 columns
+constexpr int kStackSlots = 8 + 1;       // contribution arrays: k routed slots, then the shared expert
+// every region twice: layer l uses the half of its epoch's parity
+constexpr size_t kStackLogitWords = (size_t)2 * kStackLogitCopies * 256;
+constexpr size_t kStackSharedHWords = (size_t)2 * kStackSharedHCopies * (kStackMaxI / 2);
+constexpr size_t kStackRoutedHWords = (size_t)2 * 8 * kStackRoutedHCopies * (kStackMaxI / 2);
+constexpr size_t kStackPartWords = (size_t)2 * kStackSlots * kStackMaxH;
+constexpr size_t kStackXPubWords = (size_t)2 * kStackXCopies * kStackXWords;
+constexpr size_t kStackRegionBytes =
+    8 * (kStackLogitWords + kStackSharedHWords + kStackRoutedHWords + kStackPartWords + kStackXPubWords);
+// every region at fixed offsets at the start of the workspace
+constexpr size_t kFixedRegionBytes = kDecodeRegionBytes + kStackRegionBytes;
+
+struct QMatStride {
+    int64_t q, s, b;  // bytes from one layer's tensor to the next layer's
+};
+struct FfnStride {
+    QMatStride gate, up, down;
+};
+
+struct StackArgs {
+    int H, E, top_k, I, I_shared, L;
+    const uint16_t* x_in;   // [H] bf16, the first layer's input
+    uint16_t* x_out;        // [H] bf16, x after the last layer (may alias x_in)
+    float* layer_out;       // [L][H] float32 layer outputs, or nullptr
+    uint16_t* layer_x;      // [L][H] bf16 residual stream entering every layer, or nullptr
+    uint16_t* layer_in;     // [L][H] bf16 normalised input of every layer, or nullptr
+    const uint16_t* norm_w;  // [H] bf16 normalisation weight of layer 0 (layer l at + l * norm_stride), or nullptr
+    int64_t norm_stride;
+    int32_t* idx_out;       // [L][top_k] routing per layer, or nullptr
+    float* w_out;           // [L][top_k], or nullptr
+    const uint16_t* router;  // layer 0; layer l at + l * router_stride bytes
+    int64_t router_stride;
+    const float* logit_bias;  // or nullptr
+    int64_t bias_stride;
+    FfnPtr experts, shared;   // shared.gate.q == nullptr: no shared expert
+    FfnStride experts_stride, shared_stride;
+    unsigned* ctl;               // the workspace's control words
+    // exchange words, each region [2 parities][...]
+    unsigned long long* logits;  // [kStackLogitCopies][256] {epoch, logit}
+    unsigned long long* sh_h;    // [kStackSharedHCopies][kStackMaxI / 2] {epoch, float16 pair}
+    unsigned long long* rt_h;    // [8 slots][kStackRoutedHCopies][kStackMaxI / 2] {epoch, float16 pair}
+    unsigned long long* part;    // [kStackSlots][kStackMaxH] {epoch, float32 contribution}
+    unsigned long long* xpub;    // [kStackXCopies][kStackXWords] {16-bit tag, 3 bf16}
+};
+
+// Workgroups the stack kernel can keep resident on the current device (0 on error).
+int stack_resident_capacity();
+hipError_t launch_decode_stack(const StackArgs& a, bool sb_bf16, hipStream_t stream);
+
 int decode_router_wgs(int E);
 int decode_gateup_wgs(int T, int k, bool shared, int I);
 int decode_down_wgs(int T, int k, bool shared, int H);

@@ -39,7 +39,7 @@ moe_status check_dims(const moe_dims* d) {
 
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
-    size_t ctl, xch, sel, hbuf;                          // decode region
+    size_t ctl, xch, sel, hbuf, stack;                   // decode regions (fixed offsets)
     size_t x16, h, y16, logits, hist, cursor;            // prefill buffers
     size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, shared_w, yacc, router16, total;
 };
@@ -61,6 +61,8 @@ Layout layout_of(const moe_dims* d) {
     o += kDecodeSelBytes;
     L.hbuf = o;
     o = up256(o + kDecodeHBytes);
+    L.stack = o;  // exchange words of the persistent multi-layer decode kernel
+    o = up256(o + kStackRegionBytes);
     L.x16 = o;
     o = up256(o + T * H * 2);
     L.h = o;
@@ -470,6 +472,123 @@ moe_status moe_layer_events(const moe_dims* d, const moe_weights* wts, const uin
 
 namespace {
 
+// ------------------------------------------------------- moe_decode_stack
+
+bool stride16(int64_t v) { return v % 16 == 0; }
+
+moe_status check_stride(const moe_qmat_stride& s) {
+    return stride16(s.q) && stride16(s.scale) && stride16(s.bias) ? MOE_OK : MOE_ERR_ALIGN;
+}
+
+QMatStride to_stride(const moe_qmat_stride& s) { return QMatStride{s.q, s.scale, s.bias}; }
+
+FfnStride to_stride(const moe_ffn_stride& s) { return FfnStride{to_stride(s.gate), to_stride(s.up), to_stride(s.down)}; }
+
+// strides of tensors stacked contiguously over layers: one layer's size
+moe_layer_strides contiguous_strides(const moe_dims* d) {
+    const int64_t H = d->H, I = d->I, E = d->E, Is = d->I_shared, sb = d->sb_dtype == MOE_BF16 ? 2 : 4;
+    auto mat = [&](int64_t n, int64_t N, int64_t K) {
+        return moe_qmat_stride{n * N * K / 2, n * N * (K / kGroup) * sb, n * N * (K / kGroup) * sb};
+    };
+    moe_layer_strides s;
+    s.router = E * H * 2;
+    s.logit_bias = E * 4;
+    s.norm_weight = H * 2;
+    s.experts = moe_ffn_stride{mat(E, I, H), mat(E, I, H), mat(E, H, I)};
+    s.shared = moe_ffn_stride{mat(1, Is, H), mat(1, Is, H), mat(1, H, Is)};
+    return s;
+}
+
+// workgroups of the stack kernel the current device holds at once (looked up
+// once per device; a property of the device and the kernel)
+std::mutex g_capacity_mu;
+int g_capacity[64];
+
+int resident_capacity() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(g_capacity_mu);
+    if (g_capacity[dev] == 0) g_capacity[dev] = stack_resident_capacity();
+    return g_capacity[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_decode_stack(const moe_dims* d, const moe_weights* wts, const uint16_t* norm_weight,
+                            const moe_layer_strides* strides, int32_t n_layers, const uint16_t* x_in,
+                            uint16_t* x_out, uint16_t* layer_x, uint16_t* layer_in, float* layer_out,
+                            int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    MOE_TRY(check_dims(d));
+    if (d->T == 0) return MOE_OK;
+    if (n_layers < 1) return MOE_ERR_SHAPE;
+    if (d->T != 1 || d->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d->H > kStackMaxH || d->I > kStackMaxI) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)d->top_k * (d->I / 16) > kStackGrid || (int64_t)d->top_k * ((d->H + 63) / 64) > kStackGrid)
+        return MOE_ERR_UNSUPPORTED;
+    if (!wts) return MOE_ERR_NULL;
+    if (wts->router_q8 || wts->shared_expert_gate) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_ptrs({x_in, x_out, wts->router}));
+    MOE_TRY(check_opt({wts->logit_bias, norm_weight, layer_out, layer_x, layer_in, topk_idx_out, topk_w_out}));
+    MOE_TRY(check_ffn(&wts->experts));
+    const bool shared = d->I_shared > 0;
+    if (shared) {
+        MOE_TRY(check_ffn(&wts->shared));
+    } else if (wts->shared.gate.q) {
+        return MOE_ERR_SHAPE;
+    }
+    const moe_layer_strides st = strides ? *strides : contiguous_strides(d);
+    if (!stride16(st.router) || !stride16(st.norm_weight) || st.logit_bias % 4 != 0) return MOE_ERR_ALIGN;
+    MOE_TRY(check_stride(st.experts.gate));
+    MOE_TRY(check_stride(st.experts.up));
+    MOE_TRY(check_stride(st.experts.down));
+    MOE_TRY(check_stride(st.shared.gate));
+    MOE_TRY(check_stride(st.shared.up));
+    MOE_TRY(check_stride(st.shared.down));
+    MOE_TRY(check_ws(d, ws, ws_bytes));
+    if (resident_capacity() < kStackGrid) return MOE_ERR_UNSUPPORTED;
+    const Layout L = layout_of(d);
+    StackArgs a;
+    a.H = d->H;
+    a.E = d->E;
+    a.top_k = d->top_k;
+    a.I = d->I;
+    a.I_shared = d->I_shared;
+    a.L = n_layers;
+    a.x_in = x_in;
+    a.x_out = x_out;
+    a.layer_out = layer_out;
+    a.layer_x = layer_x;
+    a.layer_in = layer_in;
+    a.norm_w = norm_weight;
+    a.norm_stride = st.norm_weight;
+    a.idx_out = topk_idx_out;
+    a.w_out = topk_w_out;
+    a.router = wts->router;
+    a.router_stride = st.router;
+    a.logit_bias = wts->logit_bias;
+    a.bias_stride = st.logit_bias;
+    a.experts = to_ptr(&wts->experts);
+    a.shared = shared ? to_ptr(&wts->shared) : FfnPtr{};
+    a.experts_stride = to_stride(st.experts);
+    a.shared_stride = to_stride(st.shared);
+    a.ctl = at<unsigned>(ws, L.ctl);
+    unsigned long long* sw = at<unsigned long long>(ws, L.stack);
+    a.logits = sw;
+    a.sh_h = sw + kStackLogitWords;
+    a.rt_h = a.sh_h + kStackSharedHWords;
+    a.part = a.rt_h + kStackRoutedHWords;
+    a.xpub = a.part + kStackPartWords;
+    HIP_TRY(launch_decode_stack(a, d->sb_dtype == MOE_BF16, stream));
+    return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
 // ------------------------------------------------------- moe_layer_no_alloc
 // The workspace of moe_layer_no_alloc: a file-scope device array, one copy per
 // device, held until the process ends.  Host code never passes `scratch`
@@ -500,7 +619,7 @@ moe_status scratch_address(int* dev_out, void** ptr_out) {
     return MOE_OK;
 }
 
-// The layer's workspace contract needs a zero decode region before the first
+// The layer's workspace contract needs zero decode regions before the first
 // call (the rest of the workspace is written before it is read in every call).
 // Until a call outside graph capture has cleared it, every call clears it
 // first with a kernel on its stream; a captured clearing kernel then runs on
@@ -510,7 +629,7 @@ moe_status scratch_prepare(int dev, void* ptr, hipStream_t stream) {
     if (g_scratch_ready[dev]) return MOE_OK;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_zero(ptr, kDecodeRegionBytes, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_zero(ptr, kFixedRegionBytes, stream) != hipSuccess) return MOE_ERR_HIP;
     if (cs == hipStreamCaptureStatusNone) g_scratch_ready[dev] = true;
     return MOE_OK;
 }

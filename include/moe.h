@@ -213,6 +213,63 @@ moe_status moe_layer_residual(const moe_dims *dims, const moe_weights *weights /
                               const uint16_t *residual, uint16_t *out, void *ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* Bytes from one layer's copy of a tensor to the next layer's, for stacks of
+ * layers (moe_decode_stack).  Each stride is a multiple of 16 (logit_bias: of
+ * 4) and may be 0 (every layer shares the tensor). */
+typedef struct {
+    int64_t q, scale, bias;
+} moe_qmat_stride;
+
+typedef struct {
+    moe_qmat_stride gate, up, down;
+} moe_ffn_stride;
+
+typedef struct {
+    int64_t router, logit_bias, norm_weight;
+    moe_ffn_stride experts, shared;
+} moe_layer_strides;
+
+/* A decode step of one token through a stack of n_layers MoE layers of a
+ * pre-norm decoder in ONE kernel launch.  Each layer reads the root-mean-square
+ * normalisation of the bf16 residual stream and adds its output to it:
+ *     n(l)   = bf16(x(l) / sqrt(mean(x(l)^2) + 1e-6) * gamma_l)
+ *     x(l+1) = bf16(x(l) + layer_l(n(l)))   (float32 sum, one round to nearest even)
+ * with x(0) = x_in and x_out = x(n_layers); layer_l is moe_layer's layer with
+ * layer l's weights, gamma_l layer l's norm_weight (1 when NULL).  The
+ * normalisation is not on the pages: it is how a decoder feeds its MoE blocks,
+ * and without it the stream grows by orders of magnitude per layer.  Pages: a
+ * decode step is one chain of dependent stages that the engine overlaps
+ * instead of running its kernels one after the other (aimanavo.com page,
+ * section "Lily does not treat prefill and decode as the same job"), and its
+ * routing stays on the GPU (same section; dzen.guru page, section "Where does
+ * the speed-up come from?").  The kernel reads each layer's router and shared
+ * expert ahead, while the layer before runs, and hands values between its
+ * workgroups through the workspace's fixed-offset decode region (word 255 is
+ * set if a device-side wait timed out; the outputs of that call are then
+ * invalid).
+ *   weights, norm_weight: layer 0's tensors (norm_weight [H] bf16, nullable);
+ *     layer l's are at + l * strides (host struct; strides NULL: each tensor
+ *     of a layer directly follows the previous layer's, i.e. stacked
+ *     [n_layers][...] tensors).  router must be the bf16 matrix (router_q8 and
+ *     shared_expert_gate: MOE_ERR_UNSUPPORTED).
+ *   x_in [H] bf16; x_out [H] bf16 (may be x_in: an in-place update).
+ *   Optional records (nullable), [n_layers][...]: layer_x [H] bf16, the stream
+ *     entering each layer; layer_in [H] bf16, its normalisation; layer_out [H]
+ *     float32, each layer's output; topk_idx_out, topk_w_out [top_k], the
+ *     routing in rank order.
+ * Each element of a layer's output is the float32 sum, in a fixed order
+ * (the routed experts in rank order, then the shared expert), of its expert
+ * contributions, so outputs are the same bit for bit on every call.  Limits (MOE_ERR_UNSUPPORTED): T == 1 (T == 0: nothing to do);
+ * H <= 2048; I <= 512; top_k * I / 16 <= 256; top_k * ceil(H / 64) <= 256;
+ * dims->out_dtype == MOE_BF16; n_layers >= 1 (else MOE_ERR_SHAPE); the device
+ * must hold 256 workgroups of 512 threads at once (all of them run together
+ * and wait on each other; launch nothing else on the device concurrently). */
+moe_status moe_decode_stack(const moe_dims *dims, const moe_weights *weights /* host */,
+                            const uint16_t *norm_weight, const moe_layer_strides *strides /* host, nullable */,
+                            int32_t n_layers, const uint16_t *x_in, uint16_t *x_out, uint16_t *layer_x,
+                            uint16_t *layer_in, float *layer_out, int32_t *topk_idx_out, float *topk_w_out,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Bytes of the device scratch that moe_layer_no_alloc uses in place of a
  * workspace (32 MiB per device; enough for every T up to 512 at H=2048, E=256,
  * top_k=8, I=512). */

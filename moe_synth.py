@@ -135,22 +135,38 @@ def _words(rng, size):
     return rng.integers(0, 1 << 32, size=size, dtype=np.uint32)
 
 
-def _matrix(seed, layer, expert, kinds, N, K, sb_bf16):
+# Centred biases: shifted by -CODE_MIDPOINT * scale, so that the weights average
+# to about zero as an affine quantisation of zero-mean weights does (its bias
+# is near -7.5 * scale).  The decode stack draws its layers this way: with the
+# configs' uncentred biases every weight averages about +0.09, each layer adds a
+# large common-mode vector to the residual stream, and after one layer the
+# normalised stream drives every gate to saturation.
+CODE_MIDPOINT = 7.5
+
+
+def _matrix(seed, layer, expert, kinds, N, K, sb_bf16, centred=False):
     kq, ks, kb = kinds
     q = _words(_rng(seed, layer, kq, expert), (N, K // 8))
-    s = _uniform(_rng(seed, layer, ks, expert), *SCALE_RANGE, (N, K // GROUP), sb_bf16)
-    b = _uniform(_rng(seed, layer, kb, expert), *BIAS_RANGE, (N, K // GROUP), sb_bf16)
+    if not centred:
+        s = _uniform(_rng(seed, layer, ks, expert), *SCALE_RANGE, (N, K // GROUP), sb_bf16)
+        b = _uniform(_rng(seed, layer, kb, expert), *BIAS_RANGE, (N, K // GROUP), sb_bf16)
+        return q, s, b
+    s = _rng(seed, layer, ks, expert).uniform(*SCALE_RANGE, size=(N, K // GROUP)).astype(np.float32)
+    b = _rng(seed, layer, kb, expert).uniform(*BIAS_RANGE, size=(N, K // GROUP)).astype(np.float32)
+    b = (b - np.float32(CODE_MIDPOINT) * s).astype(np.float32)
+    if sb_bf16:
+        s, b = f32_to_bf16_bits(s), f32_to_bf16_bits(b)
     return q, s, b
 
 
-def expert_tensors(shape: Shape, seed: int, layer: int, expert: int, intermediate: int):
+def expert_tensors(shape: Shape, seed: int, layer: int, expert: int, intermediate: int, centred: bool = False):
     """gate/up ([I][H/8] words) and down ([H][I/8] words) of one expert."""
     H, I, bf = shape.H, intermediate, shape.sb_bf16
     out = {}
     for name, kinds, N, K in (("gate", (KIND_GATE_Q, KIND_GATE_S, KIND_GATE_B), I, H),
                               ("up", (KIND_UP_Q, KIND_UP_S, KIND_UP_B), I, H),
                               ("down", (KIND_DOWN_Q, KIND_DOWN_S, KIND_DOWN_B), H, I)):
-        q, s, b = _matrix(seed, layer, expert, kinds, N, K, bf)
+        q, s, b = _matrix(seed, layer, expert, kinds, N, K, bf, centred)
         out[name + "_q"], out[name + "_s"], out[name + "_b"] = q, s, b
     return out
 
@@ -189,14 +205,14 @@ def router_q8(cfg: Config, layer: int = 0) -> dict:
     return {"router_q8": q, "router_scale": s, "router_bias": b}
 
 
-def layer_weights(cfg: Config, layer: int = 0) -> dict:
+def layer_weights(cfg: Config, layer: int = 0, centred: bool = False) -> dict:
     """All weights of one layer: router, the E routed experts (stacked), the shared expert."""
     sh = cfg.shape
     w = {"router": router_weights(cfg, layer)}
-    per = [expert_tensors(sh, cfg.seed, layer, e, sh.I) for e in range(sh.E)]
+    per = [expert_tensors(sh, cfg.seed, layer, e, sh.I, centred) for e in range(sh.E)]
     for key in per[0]:
         w[key] = np.stack([p[key] for p in per])
-    shared = expert_tensors(sh, cfg.seed, layer, SHARED_EXPERT, sh.I_shared)
+    shared = expert_tensors(sh, cfg.seed, layer, SHARED_EXPERT, sh.I_shared, centred)
     for key, v in shared.items():
         w["shared_" + key] = v[None]
     w["logit_bias"] = zipf_bias(cfg, layer) if cfg.zipf else None
@@ -237,7 +253,8 @@ def zipf_bias(cfg: Config, layer: int, alpha: float | None = None) -> np.ndarray
 # device-side generation for timing runs (same distributions, torch's RNG)
 # ---------------------------------------------------------------------------
 
-def device_layer(shape: Shape, seed: int, layer: int, device, zipf_alpha_value: float | None = None):
+def device_layer(shape: Shape, seed: int, layer: int, device, zipf_alpha_value: float | None = None,
+                 centred: bool = False):
     """One layer's weights drawn directly in device memory with torch's generator.
 
     Used where many distinct weight sets are needed (timing runs that must not
@@ -261,8 +278,16 @@ def device_layer(shape: Shape, seed: int, layer: int, device, zipf_alpha_value: 
         d = {}
         for name, N, K in (("gate", inter, H), ("up", inter, H), ("down", H, inter)):
             d[name + "_q"] = words(n, N, K // 8)
-            d[name + "_s"] = unif(*SCALE_RANGE, n, N, K // GROUP)
-            d[name + "_b"] = unif(*BIAS_RANGE, n, N, K // GROUP)
+            if centred:
+                sv = torch.rand((n, N, K // GROUP), dtype=torch.float32, device=device, generator=g)
+                sv = sv * (SCALE_RANGE[1] - SCALE_RANGE[0]) + SCALE_RANGE[0]
+                bv = torch.rand((n, N, K // GROUP), dtype=torch.float32, device=device, generator=g)
+                bv = bv * (BIAS_RANGE[1] - BIAS_RANGE[0]) + BIAS_RANGE[0] - CODE_MIDPOINT * sv
+                dt = torch.bfloat16 if shape.sb_bf16 else torch.float32
+                d[name + "_s"], d[name + "_b"] = sv.to(dt), bv.to(dt)
+            else:
+                d[name + "_s"] = unif(*SCALE_RANGE, n, N, K // GROUP)
+                d[name + "_b"] = unif(*BIAS_RANGE, n, N, K // GROUP)
         return d
 
     w = {"router": (torch.randn(E, H, device=device, generator=g) * ROUTER_STD).to(torch.bfloat16)}
@@ -275,6 +300,31 @@ def device_layer(shape: Shape, seed: int, layer: int, device, zipf_alpha_value: 
     else:
         w["logit_bias"] = None
     return w
+
+
+def device_stack(shape: Shape, seed: int, n_layers: int, device, zipf_alpha_value: float | None = None,
+                 centred: bool = True):
+    """n_layers layers drawn directly in device memory, every tensor stacked
+    with a leading layer dimension ([n_layers][...]), for the multi-layer
+    decode kernel.  Layer l holds exactly what :func:`device_layer` draws for
+    layer l (centred biases by default: see CODE_MIDPOINT)."""
+    import torch
+
+    layers = [device_layer(shape, seed, l, device, zipf_alpha_value, centred) for l in range(n_layers)]
+    out = {}
+    for key in layers[0]:
+        vals = [lw[key] for lw in layers]
+        out[key] = None if vals[0] is None else torch.stack(vals)
+        for lw in layers:
+            lw[key] = None
+    return out
+
+
+def host_stack(cfg: Config, n_layers: int, centred: bool = True) -> dict:
+    """n_layers layers of :func:`layer_weights` (host, numpy), stacked with a
+    leading layer dimension (centred biases by default: see CODE_MIDPOINT)."""
+    layers = [layer_weights(cfg, l, centred) for l in range(n_layers)]
+    return {key: (None if layers[0][key] is None else np.stack([lw[key] for lw in layers])) for key in layers[0]}
 
 
 def device_tokens(shape: Shape, T: int, seed: int, step: int, device):

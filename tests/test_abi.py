@@ -201,6 +201,47 @@ def test_no_alloc_checks(lib):
     assert lib.moe_layer_no_alloc(C.byref(e), None, None, None, None, None, None, None) == 0
 
 
+def test_decode_stack_checks(lib):
+    """moe_decode_stack refuses, on the host, what it does not support."""
+    w = _weights()
+    d = qwen_dims(1, out_dtype=bem.MOE_BF16)
+    need = bem.moe_workspace_size(d)
+
+    def call(dims, weights=w, strides=None, n=4, x=FAKE, ws=FAKE, ws_bytes=need):
+        return lib.moe_decode_stack(C.byref(dims), C.byref(weights) if weights is not None else None, None,
+                                    C.byref(strides) if strides is not None else None, n, x, FAKE, None, None,
+                                    None, None, None, ws, ws_bytes, None)
+
+    assert call(qwen_dims(0, out_dtype=bem.MOE_BF16)) == 0          # nothing to do
+    assert call(d, n=0) == -2
+    assert call(qwen_dims(2, out_dtype=bem.MOE_BF16)) == -3          # one token only
+    assert call(qwen_dims(1)) == -3                                  # the residual stream is bf16
+    assert call(qwen_dims(1, H=4096, out_dtype=bem.MOE_BF16)) == -3
+    assert call(qwen_dims(1, I=1024, I_shared=1024, out_dtype=bem.MOE_BF16)) == -3
+    assert call(d, weights=None) == -1
+    assert call(d, x=None) == -1
+    assert call(d, x=FAKE + 8) == -4
+    q8 = _weights()
+    q8.router_q8 = FAKE
+    assert call(d, weights=q8) == -3
+    gated = _weights()
+    gated.shared_expert_gate = FAKE
+    assert call(d, weights=gated) == -3
+    st = bem.LayerStrides()
+    st.experts.down.q = 24  # not a multiple of 16
+    assert call(d, strides=st) == -4
+    st = bem.LayerStrides()
+    st.logit_bias = 6
+    assert call(d, strides=st) == -4
+    st = bem.LayerStrides()
+    st.norm_weight = 8
+    assert call(d, strides=st) == -4
+    assert lib.moe_decode_stack(C.byref(d), C.byref(w), FAKE + 2, None, 4, FAKE, FAKE, None, None, None, None,
+                                None, FAKE, need, None) == -4  # misaligned norm weight
+    assert call(d, ws=FAKE + 16) == -4
+    assert call(d, ws_bytes=need - 1) == -5
+
+
 def test_status_strings(lib):
     for code in bem.STATUS:
         assert len(bem.status_string(code)) >= 2
