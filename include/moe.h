@@ -27,10 +27,18 @@
  *   - Every check runs on the host before anything is enqueued.  A status other
  *     than MOE_OK means nothing was enqueued, except MOE_ERR_HIP, which reports
  *     a failed launch (the stream may then hold part of the work).
+ *   - Range of the float16 products.  The expert products take float16
+ *     operands with float32 accumulation: x, h = silu(gate)*up and, on the
+ *     prefill path of moe_layer (T > 4), each expert's unweighted output row
+ *     are rounded to float16 (nearest even; bf16 inputs up to 65280 in
+ *     magnitude are exact).  A value of magnitude >= 65520 there becomes
+ *     +-inf, and every output element computed from it is inf or NaN.  So a
+ *     finite output element always meets the layer's accuracy, and a
+ *     non-finite one marks a value beyond the float16 range.  The router
+ *     (logits, selection, weights) and the decode path's expert outputs are
+ *     float32 throughout.
  *   - Device-side preconditions that are documented but not checked: weights
- *     and activations are finite; |x| and |silu(gate)*up| stay below 65504
- *     (the expert products run in float16 with float32 accumulation); every
- *     topk_idx entry handed to moe_permute lies in [0, E) with top_k distinct
+ *     and activations are finite; every topk_idx entry handed to moe_permute lies in [0, E) with top_k distinct
  *     entries per token; offsets/sorted_slot handed to moe_expert_ffn are a
  *     valid permutation such as moe_permute produces.
  *   - Alignment: every pointer must be 16-byte aligned (MOE_ERR_ALIGN).
@@ -61,6 +69,12 @@
 extern "C" {
 #endif
 
+/* Status of every call.  Every argument is validated on the host before any
+ * launch, and an unsupported layout is refused with a status instead of being
+ * run: the fail-early rule of the engine, which checks the model's
+ * architecture and quantisation layout at load and refuses an incompatible
+ * checkpoint (news.mantis.guru page, section "Rust drives the model, Metal
+ * does the compute"). */
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_NULL = -1,        /* a required pointer is NULL */
@@ -120,7 +134,9 @@ typedef struct {
 } moe_weights;
 
 /* Bytes of device workspace the calls below need for these dims (host-only,
- * pure; 0 when the dims are invalid).  One workspace serves every entry point.
+ * pure; 0 when the dims are invalid: the fail-early validation of
+ * news.mantis.guru page, section "Rust drives the model, Metal does the
+ * compute", applied before anything is sized).  One workspace serves every entry point.
  * Zero-fill the whole workspace once after allocating it; after that, every
  * call leaves it ready for the next one, whatever the dims of either.  The
  * first 16384 bytes are control words of the decode path: word 0 counts its
@@ -130,7 +146,13 @@ typedef struct {
  * workspace per stream). */
 size_t moe_workspace_size(const moe_dims *dims /* host */);
 
-/* Router and top-k (pages: score every expert, keep top_k, on the GPU).
+/* Router and top-k.  Every token scores all E routed experts and keeps top_k
+ * of them (aimanavo.com page, section "Qwen3.6's 256 experts and two layer
+ * types make the MLX-Lily gap": 8 of 256), on the GPU with no return to the
+ * host (aimanavo.com page, section "Lily does not treat prefill and decode as
+ * the same job"; dzen.guru page, section "Where does the speed-up come
+ * from?").  The softmax, renormalisation and tie rule are not stated there and
+ * are readings.
  * logits l[t][e] = sum_h x[t][h]*router[e][h] (+ logit_bias[e]), float32
  * accumulation of exact bf16 products; the top_k largest logits in rank order
  * (equal logits: lower expert index first); topk_w[t][j] = softmax of the
@@ -139,8 +161,11 @@ size_t moe_workspace_size(const moe_dims *dims /* host */);
 moe_status moe_route(const moe_dims *dims, const uint16_t *x, const uint16_t *router,
                      const float *logit_bias, int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
-/* Permute (pages: routing closed on the GPU, no per-layer host sync): counting
- * sort of the T*top_k slots by expert.  counts [E], offsets [E+1] (exclusive
+/* Permute: the grouping of slots by expert that keeps the routing closed on
+ * the GPU, with no host synchronisation per layer (aimanavo.com page, section
+ * "Lily does not treat prefill and decode as the same job"; dzen.guru page,
+ * section "Where does the speed-up come from?").  A counting sort of the
+ * T*top_k slots by expert.  counts [E], offsets [E+1] (exclusive
  * prefix sum of counts), sorted_slot [T*top_k]: the slots of expert e occupy
  * sorted_slot[offsets[e] .. offsets[e+1]), in unspecified order within e.
  * Uses the workspace.  Requires T*top_k <= 2^22 for this call. */
@@ -148,8 +173,13 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_idx, int32_t *c
                        int32_t *offsets, int32_t *sorted_slot, void *ws, size_t ws_bytes,
                        hipStream_t stream);
 
-/* Grouped expert FFN with dequantisation inside the products (pages: 4-bit
- * weights restored inside the grouped GEMM).  For every slot s of expert e,
+/* Grouped expert FFN with the 4-bit weights restored inside the grouped
+ * products, never written out dequantised (aimanavo.com page, section "Lily
+ * does not treat prefill and decode as the same job"; dzen.guru page, section
+ * "Where does the speed-up come from?"); the weights are MLX affine 4-bit with
+ * group size 64 (aimanavo.com page, section "Only one 4-bit checkpoint at a
+ * pinned revision runs"; news.mantis.guru page, section "Rust drives the
+ * model, Metal does the compute").  The SwiGLU form is a reading.  For every slot s of expert e,
  * with t = s / top_k:  y_slot[s] = W_down,e (silu(W_gate,e x[t]) * (W_up,e x[t])).
  * y_shared[t] = the shared expert applied to x[t] (skipped when shared or
  * y_shared is NULL).  offsets/sorted_slot as produced by moe_permute.
@@ -160,7 +190,9 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x, const int32_t
                           float *y_shared /* nullable */, void *ws, size_t ws_bytes,
                           hipStream_t stream);
 
-/* Weighted combine plus shared expert (pages: add one shared expert):
+/* Weighted combine plus the one always-on shared expert (aimanavo.com page,
+ * section "Qwen3.6's 256 experts and two layer types make the MLX-Lily gap";
+ * the weighting by the routing weights is a reading):
  * out[t] = sum_j topk_w[t][j] * y_slot[t*top_k+j] + y_shared[t] (y_shared nullable).
  * out [T][H] float32. */
 moe_status moe_combine(const moe_dims *dims, const float *y_slot, const float *topk_w,
@@ -179,12 +211,16 @@ moe_status moe_shared_gate(const moe_dims *dims, const uint16_t *x, const uint16
 moe_status moe_combine_gated(const moe_dims *dims, const float *y_slot, const float *topk_w,
                              const float *y_shared, const float *shared_w, void *out, hipStream_t stream);
 
-/* The whole layer as one device-side pipeline, shared expert included;
- * out [T][H] float32.  Optional copies of the routing: topk_idx_out [T][top_k],
+/* The whole layer as one device-side pipeline, shared expert included: the
+ * steps above in the pages' order (aimanavo.com page, sections "Qwen3.6's 256
+ * experts and two layer types make the MLX-Lily gap" and "Lily does not treat
+ * prefill and decode as the same job"; prefill and decode are separate
+ * workloads: same section, and news.mantis.guru page, section "Prefill and
+ * decode are optimised as different modes").  out [T][H] float32.  Optional copies of the routing: topk_idx_out [T][top_k],
  * topk_w_out [T][top_k], counts_out [E] (each nullable).
  * Prefill (T > 4): route, permute, gate/up with SwiGLU, down storing float16
- * rows per slot, then the weighted combine with the shared expert.  Decode (T <= 4; pages: decode is a
- * bandwidth-bound workload of its own): a single kernel whose router workgroups
+ * rows per slot, then the weighted combine with the shared expert.  Decode
+ * (T <= 4, a bandwidth-bound workload of its own): a single kernel whose router workgroups
  * rank the experts on the device and whose expert workgroups run the SwiGLU
  * experts and combine into out with atomics.  Uses the workspace's decode region
  * and control words (see moe_workspace_size). */
@@ -311,7 +347,9 @@ int32_t moe_layer_stage_count(const moe_dims *dims /* host */);
 /* Static name of kernel i (0-based) of moe_layer for these dims, or NULL. */
 const char *moe_layer_stage_name(const moe_dims *dims /* host */, int32_t i);
 
-/* Static English text for a status code (host). */
+/* Static English text for a status code (host): the refusal message of the
+ * fail-early validation (news.mantis.guru page, section "Rust drives the
+ * model, Metal does the compute"). */
 const char *moe_status_string(moe_status status);
 
 #ifdef __cplusplus
