@@ -78,6 +78,8 @@ def lib():
         L.oracle_rmsnorm.restype = None
         L.oracle_moe_layer.argtypes = [C.POINTER(Layer), i32, P, P, P, P, P, P, P, P]
         L.oracle_moe_layer.restype = C.c_int
+        L.oracle_gqa_decode.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, C.c_double, P]
+        L.oracle_gqa_decode.restype = C.c_int
         _lib = L
     return _lib
 
@@ -221,6 +223,26 @@ def rmsnorm(x, gamma=None, eps=RMSNORM_EPS):
     out = np.empty_like(x)
     for r in range(x.shape[0]):
         lib().oracle_rmsnorm(x.shape[1], x[r].ctypes.data, _ptr(g), float(eps), out[r].ctypes.data)
+    return out
+
+
+def gqa_decode(q, k, v, seq_len, scale=None):
+    """R19: decode attention with grouped-query KV sharing.  q [B][Hq][D], k and v
+    [B][Hkv][S_max][D] (bf16 bits), seq_len [B]; scale defaults to 1/sqrt(D).
+    Returns out [B][Hq][D] float64."""
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k.shape
+    if k.shape != (B, Hkv, S_max, D) or v.shape != k.shape or Hq % Hkv:
+        raise ValueError("gqa_decode: inconsistent shapes")
+    n = _c(seq_len, np.int32)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    if lib().oracle_gqa_decode(B, Hq, Hkv, D, S_max, q.ctypes.data, k.ctypes.data, v.ctypes.data, n.ctypes.data,
+                               sc, out.ctypes.data) != 0:
+        raise MemoryError("oracle_gqa_decode could not allocate its working buffer")
     return out
 
 

@@ -53,6 +53,16 @@
  *      with that bfloat16 matrix.  The router is restored to the precision the
  *      dense router has, so both sides take every ranking decision on the
  *      same matrix.
+ *   R19 (decode attention, the pages' GQA packing) a full-attention layer's
+ *      decode step for one token per sequence: 16 query heads share 2 KV
+ *      heads, 8 query heads per KV head (aimanavo.com page, section
+ *      "Qwen3.6's 256 experts and two layer types make the MLX-Lily gap"),
+ *      consecutive query heads sharing one KV head, h -> h / (Hq / Hkv).
+ *      The pages name the packing (each KV row read once for the query heads
+ *      that share it) but not the formula: the plain one is taken, scores
+ *      s_j = scale * q_h . k_j over the sequence's cached rows, softmax over
+ *      them, out_h = sum_j p_j v_j, with the current token's key and value
+ *      already in the cache.  A sequence with no rows gives zeros.
  */
 #include <math.h>
 #include <stdint.h>
@@ -445,5 +455,64 @@ int oracle_moe_layer(const oracle_layer *L, int32_t n_tok, const int32_t *tok, d
         free(ss);
     if (!logits)
         free(lg);
+    return 0;
+}
+
+/* Decode attention with grouped-query KV sharing (R19).  q [B][Hq][D],
+ * k and v [B][Hkv][S_max][D] (bfloat16 bits), seq_len [B] (values clamped to
+ * [0, S_max]); out [B][Hq][D].  For sequence b, query head h and its KV head
+ * g = h / (Hq / Hkv):
+ *     s_j = scale * sum_d q[b][h][d] * k[b][g][j][d],   j < seq_len[b],
+ *     p_j = exp(s_j - max_j s_j) / sum_j exp(s_j - max_j s_j),
+ *     out[b][h][d] = sum_j p_j * v[b][g][j][d].
+ * Double precision throughout.  Returns 0, or -1 if a buffer could not be
+ * allocated. */
+int oracle_gqa_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max, const uint16_t *q,
+                      const uint16_t *k, const uint16_t *v, const int32_t *seq_len, double scale, double *out)
+{
+    const int32_t per_kv = Hq / Hkv;
+    double *p = malloc(sizeof(double) * (size_t)(S_max > 0 ? S_max : 1));
+    if (!p)
+        return -1;
+    for (int32_t b = 0; b < B; b++) {
+        int32_t n = seq_len[b];
+        if (n < 0)
+            n = 0;
+        if (n > S_max)
+            n = S_max;
+        for (int32_t h = 0; h < Hq; h++) {
+            const int32_t g = h / per_kv;
+            const uint16_t *qh = q + ((size_t)b * Hq + h) * D;
+            const uint16_t *kg = k + ((size_t)b * Hkv + g) * S_max * D;
+            const uint16_t *vg = v + ((size_t)b * Hkv + g) * S_max * D;
+            double *o = out + ((size_t)b * Hq + h) * D;
+            if (n == 0) {
+                for (int32_t d = 0; d < D; d++)
+                    o[d] = 0.0;
+                continue;
+            }
+            double smax = -INFINITY;
+            for (int32_t j = 0; j < n; j++) {
+                double acc = 0.0;
+                for (int32_t d = 0; d < D; d++)
+                    acc += bf16_bits_value(qh[d]) * bf16_bits_value(kg[(size_t)j * D + d]);
+                p[j] = scale * acc;
+                if (p[j] > smax)
+                    smax = p[j];
+            }
+            double z = 0.0;
+            for (int32_t j = 0; j < n; j++) {
+                p[j] = exp(p[j] - smax);
+                z += p[j];
+            }
+            for (int32_t d = 0; d < D; d++) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < n; j++)
+                    acc += p[j] * bf16_bits_value(vg[(size_t)j * D + d]);
+                o[d] = acc / z;
+            }
+        }
+    }
+    free(p);
     return 0;
 }

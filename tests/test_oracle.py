@@ -490,3 +490,110 @@ def test_rmsnorm_unit_rms_and_gamma():
     neg = moe_synth.f32_to_bf16_bits(np.full(2048, -1.0, dtype=np.float32))
     yn = moe_synth.bf16_bits_to_f32(oracle.rmsnorm(x, neg, eps=0.0)[0]).astype(np.float64)
     np.testing.assert_array_equal(yn, -y)
+
+
+# ---------------------------------------------------------------- decode attention (R19)
+
+
+def _bits(a):
+    return moe_synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def _values(bits):
+    return moe_synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _gqa_inputs(B, Hq, Hkv, D, S, seed, q_scale=1.0):
+    rng = np.random.default_rng(seed)
+    q = _bits(rng.standard_normal((B, Hq, D)) * q_scale)
+    k = _bits(rng.standard_normal((B, Hkv, S, D)))
+    v = _bits(rng.standard_normal((B, Hkv, S, D)))
+    return q, k, v
+
+
+@pytest.mark.parametrize("ex", _load("gqa_examples.json")["examples"], ids=lambda e: e["name"])
+def test_gqa_hand_examples(ex):
+    out = oracle.gqa_decode(_bits(ex["q"]), _bits(ex["k"]), _bits(ex["v"]), np.array(ex["seq_len"]), ex["scale"])
+    np.testing.assert_allclose(out, np.array(ex["out"], dtype=np.float64), rtol=1e-14, atol=1e-14)
+
+
+def test_gqa_against_torch_attention_with_shared_kv_heads():
+    """torch's float64 scaled_dot_product_attention with enable_gqa (the KV heads
+    repeated for consecutive query heads), per sequence on its valid rows."""
+    B, Hq, Hkv, D, S = 3, 16, 2, 64, 50
+    q, k, v = _gqa_inputs(B, Hq, Hkv, D, S, 21, q_scale=2.0)
+    lens = np.array([50, 17, 1], dtype=np.int32)
+    out = oracle.gqa_decode(q, k, v, lens)
+    for b in range(B):
+        n = lens[b]
+        tq = torch.from_numpy(_values(q[b]))[None, :, None, :]
+        tk = torch.from_numpy(_values(k[b, :, :n]))[None]
+        tv = torch.from_numpy(_values(v[b, :, :n]))[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, enable_gqa=True)[0, :, 0].numpy()
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_single_row_returns_its_value_row():
+    """One cached row: its softmax weight is 1 and each head returns the value row exactly."""
+    q, k, v = _gqa_inputs(2, 8, 2, 32, 5, 22)
+    out = oracle.gqa_decode(q, k, v, np.array([1, 1]))
+    for h in range(8):
+        np.testing.assert_array_equal(out[:, h], _values(v[:, h // 4, 0]))
+
+
+def test_gqa_zero_query_averages_the_values():
+    """q = 0 gives equal scores: the output is the mean of the valid value rows."""
+    q, k, v = _gqa_inputs(1, 4, 2, 16, 9, 23)
+    q[:] = 0
+    out = oracle.gqa_decode(q, k, v, np.array([7]))
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], _values(v[0, h // 2, :7]).mean(axis=0), rtol=1e-14, atol=1e-15)
+
+
+def test_gqa_each_head_reads_its_own_kv_head():
+    """Value rows constant per KV head (g + 1): every query head returns the
+    constant of KV head h / (Hq / Hkv), whatever the scores."""
+    B, Hq, Hkv, D, S = 2, 16, 4, 8, 6
+    q, k, v = _gqa_inputs(B, Hq, Hkv, D, S, 24, q_scale=3.0)
+    for g in range(Hkv):
+        v[:, g] = _bits(np.full((B, S, D), g + 1.0))
+    out = oracle.gqa_decode(q, k, v, np.array([6, 3]))
+    for h in range(Hq):
+        np.testing.assert_allclose(out[:, h], h // (Hq // Hkv) + 1.0, rtol=1e-14)
+
+
+def test_gqa_row_order_does_not_matter():
+    """Permuting the valid rows of K and V together leaves the output unchanged."""
+    q, k, v = _gqa_inputs(1, 8, 2, 32, 40, 25, q_scale=2.0)
+    perm = np.random.default_rng(26).permutation(33)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, :33] = k[:, :, perm]
+    v2[:, :, :33] = v[:, :, perm]
+    np.testing.assert_allclose(oracle.gqa_decode(q, k2, v2, np.array([33])), oracle.gqa_decode(q, k, v, np.array([33])),
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_gqa_dominant_key_selects_its_value_row():
+    """A key aligned with the query at a scale far above the rest takes all the weight."""
+    q, k, v = _gqa_inputs(1, 2, 1, 16, 12, 27)
+    k[0, 0, 5] = _bits(64.0 * _values(q[0, 0]))
+    out = oracle.gqa_decode(q, k, v, np.array([12]))
+    np.testing.assert_allclose(out[0, 0], _values(v[0, 0, 5]), rtol=0, atol=1e-12)
+
+
+def test_gqa_scale_equals_scaled_query():
+    """scale * (q.k) with scale 4 equals the default scale applied to 4 q (exact in bf16)."""
+    q, k, v = _gqa_inputs(2, 4, 2, 16, 10, 28)
+    q4 = _bits(4.0 * _values(q))
+    a = oracle.gqa_decode(q, k, v, np.array([10, 4]), scale=4.0 / np.sqrt(16))
+    b = oracle.gqa_decode(q4, k, v, np.array([10, 4]))
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
+def test_gqa_rows_past_the_length_are_not_read():
+    """A sequence of n rows in a larger cache equals the same rows in a cache of exactly n."""
+    q, k, v = _gqa_inputs(1, 8, 2, 32, 30, 29)
+    v[:, :, 20:] = _bits(np.full((1, 2, 10, 32), 1000.0))
+    a = oracle.gqa_decode(q, k, v, np.array([20]))
+    b = oracle.gqa_decode(q, np.ascontiguousarray(k[:, :, :20]), np.ascontiguousarray(v[:, :, :20]), np.array([20]))
+    np.testing.assert_array_equal(a, b)

@@ -43,6 +43,11 @@ MUTATIONS = {
     "rmsnorm eps ignored": ("sqrt(ss / (double)H + eps)", "sqrt(ss / (double)H)"),
     "rmsnorm gamma ignored": ("const double g = gamma ? bf16_bits_value(gamma[h]) : 1.0;", "const double g = 1.0;"),
     "rmsnorm rounds toward zero": ("nearbyint(ldexp(m, 8))", "trunc(ldexp(m, 8))"),
+    "gqa group index modulo": ("const int32_t g = h / per_kv;", "const int32_t g = h % Hkv;"),
+    "gqa scale ignored": ("p[j] = scale * acc;", "p[j] = acc;"),
+    "gqa current row dropped": ("int32_t n = seq_len[b];", "int32_t n = seq_len[b] - 1;"),
+    "gqa normaliser dropped": ("o[d] = acc / z;", "o[d] = acc;"),
+    "gqa values read from the keys": ("acc += p[j] * bf16_bits_value(vg[", "acc += p[j] * bf16_bits_value(kg["),
     "permute not stable": ("sorted_slot[cursor[idx[s]]++] = s;", "sorted_slot[offsets[idx[s] + 1] - 1 - (cursor[idx[s]]++ - offsets[idx[s]])] = s;"),
 }
 
