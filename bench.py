@@ -62,6 +62,8 @@ WORKLOADS = {
     "stack40": ("stack40", 40, "mfma", 40),
     # one decode step (one token) through 40 layers in one launch of moe_decode_stack
     "decode_stack40": ("decode", 40, "hbm", 40),
+    # decode attention of one token at 32K context (16 query / 2 KV heads, D = 128)
+    "gqa32k": ("gqa32k", 1, "hbm", 12),
 }
 
 
@@ -108,6 +110,7 @@ def stage_work(name, sh, T, touched, shared):
 KERNEL_SOURCES = {
     "decode_layer": "bit_expert_grouped_amd/csrc/decode.hip",
     "decode_stack": "bit_expert_grouped_amd/csrc/decode_stack.hip",
+    "gqa_partial": "bit_expert_grouped_amd/csrc/gqa_decode.hip",
     "router": "bit_expert_grouped_amd/csrc/router.hip",
     "topk": "bit_expert_grouped_amd/csrc/router.hip",
     "permute": "bit_expert_grouped_amd/csrc/permute.hip",
@@ -601,9 +604,136 @@ def run_decode_stack(name, steps_arg, warmup_arg, args, with_cpu=True, cpu_secon
     return rec
 
 
+def gqa_bytes(shape, n):
+    """Algorithmic bytes of one decode-attention call: every valid K and V row
+    once (the packing reads each for all query heads of its KV head), q in, out."""
+    return shape.B * shape.Hkv * n * shape.D * 2 * 2 + shape.B * shape.Hq * shape.D * (2 + 4) + shape.B * 4
+
+
+def cpu_baseline_gqa(shape, seconds):
+    """The oracle (single-threaded C, fp64, pinned to one core) on whole calls of
+    the same attention workload; tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    import moe_synth
+
+    q, k, v = moe_synth.attn_inputs(shape, 5)
+    lens = np.full(shape.B, shape.S, dtype=np.int32)
+    pinned = _pin_one_core()
+    try:
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.gqa_decode(q, k, v, lens)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        _unpin(pinned)
+    return {"value": round(calls * shape.B / el, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d whole oracle calls (B=%d, %d query / %d KV heads, D=%d, %d cached rows), %.1f s "
+                      "single-threaded, pinned to core %s" % (calls, shape.B, shape.Hq, shape.Hkv, shape.D, shape.S,
+                                                              el, pinned[1] if pinned else "none"),
+            "seconds": round(el, 2), "cpu": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def run_gqa(name, steps_arg, warmup_arg, args, with_cpu=True, cpu_seconds=None):
+    """Decode attention of one token per sequence over a 32K-row KV cache
+    (moe_gqa_decode).  Distinct caches are rotated (12 x 33.5 MB, past the
+    256 MB last-level cache), so every step streams its K and V from HBM."""
+    import torch
+
+    import bit_expert_grouped_amd as bem
+    import moe_synth
+
+    shape = moe_synth.GQA32K
+    n_sets = args.weight_sets or WORKLOADS[name][3]
+    steps = steps_arg if steps_arg is not None else 20
+    warmup = warmup_arg if warmup_arg is not None else 5
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sets = [moe_synth.device_attn(shape, 100 + i, dev) for i in range(n_sets)]
+    lens = torch.full((shape.B,), shape.S, dtype=torch.int32, device=dev)
+    d = bem.gqa_dims(shape.B, shape.Hq, shape.Hkv, shape.D, shape.S)
+    ws = bem.gqa_workspace(d, dev)
+    out = torch.empty(shape.B, shape.Hq, shape.D, dtype=torch.float32, device=dev)
+
+    def call(i, events=None):
+        q, k, v = sets[i % n_sets]
+        bem.gqa_decode(q, k, v, lens, out=out, ws=ws, events=events)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    mode = args.mode or "graph"
+    g = None
+    if mode == "graph":
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(steps):
+                    call(i)
+        torch.cuda.synchronize()
+        g.replay()  # one untimed replay
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            call(i)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    # the two kernels, timed with events on the launch stream in an eager run of the same steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        call(i, evs[i])
+    torch.cuda.synchronize()
+    part_us = sum(e[0].elapsed_time(e[1]) for e in evs) * 1000.0 / steps
+    merge_us = sum(e[1].elapsed_time(e[2]) for e in evs) * 1000.0 / steps
+    us_call = total_ms * 1000.0 / steps
+    nbytes = gqa_bytes(shape, shape.S)
+    achieved = nbytes / (part_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gqa_partial", name),
+            "kernel": "gqa_partial", "kernel_us": round(part_us, 2),
+            "kernel_us_source": "HIP events around the kernel on its stream, eager run of the same steps",
+            "algorithmic_bytes_per_launch": int(nbytes)}
+    rec = {
+        "metric": METRIC, "value": round(shape.B * steps / (total_ms / 1000.0), 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(total_ms / steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "B": shape.B, "n_q_heads": shape.Hq, "n_kv_heads": shape.Hkv,
+                   "head_dim": shape.D, "context": shape.S, "kv_sets": n_sets,
+                   "inputs": "q, K, V ~ N(0, 1) in bf16, scale 1/sqrt(D)",
+                   "products": "bf16 MFMA, fp32 accumulation; probabilities rounded to bf16"},
+        "us_per_call": round(us_call, 3),
+        "us_per_layer": round(us_call, 3),
+        "stages_us": {"gqa_partial": round(part_us, 2), "gqa_merge": round(merge_us, 2)},
+        "call_hbm_frac": round(nbytes / (us_call * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "launch": mode,
+        "roofline": roof,
+    }
+    del sets, ws, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if with_cpu and not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_gqa(shape, cpu_seconds or args.cpu_seconds)
+    return rec
+
+
 # workloads the default run times beside the headline decode line
-EXTRA_WORKLOADS = ("decode_stack40", "decode64", "prefill512", "prefill4096", "stack40")
-EXTRA_KEYS = ("value", "unit", "ms_per_step", "us_per_layer", "steps", "warmup", "config", "layer_hbm_frac",
+EXTRA_WORKLOADS = ("decode_stack40", "gqa32k", "decode64", "prefill512", "prefill4096", "stack40")
+EXTRA_KEYS = ("value", "unit", "ms_per_step", "us_per_layer", "us_per_call", "call_hbm_frac", "steps", "warmup", "config", "layer_hbm_frac",
               "layer_mfma_frac", "touched_experts", "stages_us", "launch", "timed_weight_sets", "roofline",
               "cpu_baseline")
 
@@ -648,7 +778,8 @@ def main():
 
     bem.lib()
     def run(name, **kw):
-        fn = run_decode_stack if name.startswith("decode_stack") else run_workload
+        fn = (run_decode_stack if name.startswith("decode_stack") else run_gqa if name.startswith("gqa")
+              else run_workload)
         return fn(name, args.steps, args.warmup, args, **kw)
 
     if args.workload is not None:

@@ -12,6 +12,7 @@ Names follow the C ABI: ``moe_workspace_size``, ``moe_route``,
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -22,7 +23,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNS
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_shared_gate",
            "moe_combine_gated", "moe_router_dequant", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
-           "moe_layer_no_alloc", "moe_decode_stack", "moe_status_string")
+           "moe_layer_no_alloc", "moe_decode_stack", "moe_gqa_workspace_size", "moe_gqa_decode", "moe_gqa_decode_events",
+           "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -34,6 +36,10 @@ class MoeError(RuntimeError):
 class Dims(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("T", "H", "E", "top_k", "I", "I_shared", "group", "sb_dtype",
                                           "out_dtype")]
+
+
+class GqaDims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("B", "n_q_heads", "n_kv_heads", "head_dim", "max_seq")]
 
 
 class QMat(C.Structure):
@@ -96,13 +102,18 @@ def lib():
         L.moe_layer_no_alloc.argtypes = [D, C.POINTER(Weights), P, P, P, P, P, P]
         L.moe_decode_stack.argtypes = [D, C.POINTER(Weights), P, C.POINTER(LayerStrides), C.c_int32, P, P, P, P, P,
                                        P, P, P, C.c_size_t, P]
+        L.moe_gqa_workspace_size.argtypes = [C.POINTER(GqaDims)]
+        L.moe_gqa_workspace_size.restype = C.c_size_t
+        L.moe_gqa_decode.argtypes = [C.POINTER(GqaDims), P, P, P, P, C.c_float, P, P, C.c_size_t, P]
+        L.moe_gqa_decode_events.argtypes = [C.POINTER(GqaDims), P, P, P, P, C.c_float, P, P, C.c_size_t, P, P,
+                                            C.c_int32]
         L.moe_layer_stage_count.argtypes = [D]
         L.moe_layer_stage_count.restype = C.c_int32
         L.moe_layer_stage_name.argtypes = [D, C.c_int32]
         L.moe_layer_stage_name.restype = C.c_char_p
         for name in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_combine_gated",
                      "moe_shared_gate", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_no_alloc",
-                     "moe_decode_stack"):
+                     "moe_decode_stack", "moe_gqa_decode", "moe_gqa_decode_events"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -438,4 +449,50 @@ def moe_layer(x, weights: LayerWeights, top_k, out=None, ws=None, want_routing=F
                                       len(events)), "moe_layer_events")
     if want_routing:
         return out, idx, w, counts
+    return out
+
+
+# ---------------------------------------------------------------- decode attention
+
+
+def gqa_dims(B, n_q_heads, n_kv_heads, head_dim, max_seq) -> GqaDims:
+    return GqaDims(B, n_q_heads, n_kv_heads, head_dim, max_seq)
+
+
+def gqa_workspace(d: GqaDims, device="cuda"):
+    """A workspace tensor of moe_gqa_workspace_size(d) bytes (no clearing needed)."""
+    import torch
+
+    n = lib().moe_gqa_workspace_size(C.byref(d))
+    if n == 0:
+        raise MoeError(-2, "moe_gqa_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def gqa_decode(q, k_cache, v_cache, seq_len, scale=None, out=None, ws=None, events=None):
+    """out [B][Hq][D] float32 = decode attention of q [B][Hq][D] over k_cache,
+    v_cache [B][Hkv][S_max][D] (bf16 tensors) with seq_len [B] int32 rows each;
+    scale defaults to 1/sqrt(D).  events: optional 3 torch.cuda.Event (timing
+    enabled) recorded around the two kernels (moe_gqa_decode_events)."""
+    import torch
+
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    d = gqa_dims(B, Hq, Hkv, D, S_max)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = gqa_workspace(d, q.device)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if events is None:
+        _check(lib().moe_gqa_decode(C.byref(d), _p(q), _p(k_cache), _p(v_cache), _p(seq_len), sc, _p(out), _p(ws),
+                                    ws.numel(), _stream()), "moe_gqa_decode")
+    else:
+        for e in events:
+            if not e.cuda_event:  # torch creates the HIP event lazily, on first record
+                e.record()
+        ev = (C.c_void_p * len(events))(*[e.cuda_event for e in events])
+        _check(lib().moe_gqa_decode_events(C.byref(d), _p(q), _p(k_cache), _p(v_cache), _p(seq_len), sc, _p(out),
+                                           _p(ws), ws.numel(), _stream(), C.cast(ev, C.c_void_p), len(events)),
+               "moe_gqa_decode_events")
     return out

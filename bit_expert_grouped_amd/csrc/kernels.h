@@ -255,6 +255,26 @@ hipError_t launch_residual_bf16(const float* y, const uint16_t* residual, int T,
 // bytes (a multiple of 16) from p on set to zero, by a kernel
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
+// Decode attention with grouped-query KV sharing (two passes: per-run
+// partials, then their merge).  q [B][Hq][D], k/v [B][Hkv][S_max][D] bf16,
+// seq_len [B]; part: B * Hkv * n_split partials of G * D + 32 floats (o [G][D],
+// then m and l, 16 slots each); out [B][Hq][D] float32.  c = scale * log2(e).
+struct GqaArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* seq_len;
+    float* part;
+    float* out;
+    int B, Hq, Hkv, G, D, S_max, n_split;
+    float c;
+};
+
+// rows of the cache one pass-1 workgroup covers (the run length of a partial)
+int gqa_rows_per_split(int D);
+// events (nullable): 3 events recorded before pass 1, between the passes and after pass 2
+hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream, hipEvent_t* events);
+
 // shared_w[t] = sigmoid(x[t] . g), x [T][H] and g [H] bf16
 hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* g, int T, int H, float* shared_w,
                               hipStream_t stream);

@@ -665,4 +665,97 @@ const char* moe_layer_stage_name(const moe_dims* d, int32_t i) {
     return use_decode_path(d) ? kDecodeStages[i] : kPrefillStages[i];
 }
 
+// ---------------------------------------------------------------- decode attention
+
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kMaxGqaSeq = int64_t(1) << 24;
+
+moe_status check_gqa_dims(const moe_gqa_dims* d) {
+    if (!d) return MOE_ERR_NULL;
+    if (d->B < 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 || d->max_seq <= 0)
+        return MOE_ERR_SHAPE;
+    if (d->n_q_heads % d->n_kv_heads != 0) return MOE_ERR_SHAPE;
+    if (d->n_q_heads / d->n_kv_heads > 16) return MOE_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return MOE_ERR_UNSUPPORTED;
+    if (d->B > 65535 || d->n_kv_heads > 65535 || (int64_t)d->max_seq > kMaxGqaSeq) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int gqa_splits(const moe_gqa_dims* d) {
+    const int r = gqa_rows_per_split(d->head_dim);
+    return (d->max_seq + r - 1) / r;
+}
+
+size_t gqa_ws_bytes(const moe_gqa_dims* d) {
+    const size_t G = (size_t)(d->n_q_heads / d->n_kv_heads);
+    const size_t bytes = (size_t)d->B * d->n_kv_heads * (size_t)gqa_splits(d) * (G * d->head_dim + 32) * 4;
+    return (bytes + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_gqa_workspace_size(const moe_gqa_dims* dims) {
+    if (check_gqa_dims(dims) != MOE_OK) return 0;
+    return gqa_ws_bytes(dims);
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status gqa_impl(const moe_gqa_dims* d, const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                    const int32_t* seq_len, float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                    hipEvent_t* events) {
+    MOE_TRY(check_gqa_dims(d));
+    const float c = scale * 1.4426950408889634f;  // scores in log2 units
+    if (!(c == c) || c - c != 0.0f) return MOE_ERR_SHAPE;  // NaN or infinite
+    if (d->B == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({q, k_cache, v_cache, out}));
+    if (!seq_len) return MOE_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(seq_len) & 3u) != 0) return MOE_ERR_ALIGN;
+    if (!ws) return MOE_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_ALIGN;
+    if (ws_bytes < gqa_ws_bytes(d)) return MOE_ERR_WORKSPACE;
+    GqaArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.seq_len = seq_len;
+    a.part = static_cast<float*>(ws);
+    a.out = out;
+    a.B = d->B;
+    a.Hq = d->n_q_heads;
+    a.Hkv = d->n_kv_heads;
+    a.G = d->n_q_heads / d->n_kv_heads;
+    a.D = d->head_dim;
+    a.S_max = d->max_seq;
+    a.n_split = gqa_splits(d);
+    a.c = c;
+    HIP_TRY(launch_gqa_decode(a, stream, events));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_gqa_decode(const moe_gqa_dims* d, const uint16_t* q, const uint16_t* k_cache,
+                          const uint16_t* v_cache, const int32_t* seq_len, float scale, float* out, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    return gqa_impl(d, q, k_cache, v_cache, seq_len, scale, out, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_gqa_decode_events(const moe_gqa_dims* d, const uint16_t* q, const uint16_t* k_cache,
+                                 const uint16_t* v_cache, const int32_t* seq_len, float scale, float* out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream, hipEvent_t* events, int32_t n_events) {
+    if (!events) return MOE_ERR_NULL;
+    if (n_events < 3) return MOE_ERR_SHAPE;
+    return gqa_impl(d, q, k_cache, v_cache, seq_len, scale, out, ws, ws_bytes, stream, events);
+}
+
 }  // extern "C"

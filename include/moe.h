@@ -340,6 +340,62 @@ moe_status moe_layer_events(const moe_dims *dims, const moe_weights *weights /* 
                             int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream,
                             hipEvent_t *events /* host */, int32_t n_events);
 
+/* Decode attention of a full-attention layer with grouped-query KV sharing:
+ * the layer next to the MoE block in the same decode step.  The model's
+ * full-attention layers have 16 query heads over 2 KV heads (aimanavo.com
+ * page, section "Qwen3.6's 256 experts and two layer types make the MLX-Lily
+ * gap"), and the decode kernel packs the query heads of a KV head so that each
+ * K and V row is read once for all of them (aimanavo.com page, section "Lily
+ * does not treat prefill and decode as the same job"; dzen.guru page, section
+ * "Where does the speed-up come from?").  The formula is not on the pages; the
+ * plain one is computed.  For sequence b with n = seq_len[b] cached rows
+ * (clamped to [0, max_seq]) and query head h, whose KV head is
+ * g = h / (n_q_heads / n_kv_heads):
+ *     s_j = scale * sum_d q[b][h][d] * k_cache[b][g][j][d]       (j < n)
+ *     out[b][h][d] = sum_j softmax(s)_j * v_cache[b][g][j][d]
+ * float32 accumulation of exact bf16 products; the probabilities enter the
+ * second product rounded to bf16, and the normaliser sums those rounded values,
+ * so |error| <= 2^-8 * max_j |v_j| per element, far less on average.  n == 0
+ * gives zeros.  Rows j >= n are never read.
+ * Host struct; limits (MOE_ERR_UNSUPPORTED beyond them): head_dim 64, 128 or
+ * 256; n_q_heads / n_kv_heads <= 16; B and n_kv_heads <= 65535; max_seq <=
+ * 2^24.  n_q_heads a multiple of n_kv_heads, all sizes positive (B >= 0):
+ * else MOE_ERR_SHAPE. */
+typedef struct {
+    int32_t B;          /* sequences, one query token each; 0: nothing to do */
+    int32_t n_q_heads;  /* Hq */
+    int32_t n_kv_heads; /* Hkv */
+    int32_t head_dim;   /* D */
+    int32_t max_seq;    /* rows per (sequence, KV head) in the cache */
+} moe_gqa_dims;
+
+/* Bytes of device workspace moe_gqa_decode needs (host-only, pure; 0 when the
+ * dims are invalid): B * n_kv_heads * ceil(max_seq / R) partials of
+ * (G * head_dim + 32) floats, R = 256 rows (128 at head_dim 256).  It needs no
+ * clearing.  Not shared with moe_workspace_size's workspace contract: any
+ * buffer of this size will do, reused freely between calls that do not
+ * overlap in time. */
+size_t moe_gqa_workspace_size(const moe_gqa_dims *dims /* host */);
+
+/* q [B][Hq][D] bf16; k_cache, v_cache [B][Hkv][max_seq][D] bf16 (16-byte
+ * aligned, each head's rows contiguous); seq_len [B] int32 (4-byte aligned);
+ * out [B][Hq][D] float32; scale finite (1/sqrt(D) is the usual one; NaN or
+ * infinite: MOE_ERR_SHAPE); ws of moe_gqa_workspace_size bytes, 256-byte
+ * aligned (MOE_ERR_WORKSPACE when smaller).  Two kernels on `stream`. */
+moe_status moe_gqa_decode(const moe_gqa_dims *dims /* host */, const uint16_t *q, const uint16_t *k_cache,
+                          const uint16_t *v_cache, const int32_t *seq_len, float scale, float *out, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* moe_gqa_decode plus HIP events, for instrumentation: events[0] is recorded
+ * on `stream` before the first of its two kernels (the per-run partials),
+ * events[1] between them and events[2] after the second (their merge).
+ * events NULL: MOE_ERR_NULL; n_events < 3: MOE_ERR_SHAPE.  B == 0 records
+ * nothing. */
+moe_status moe_gqa_decode_events(const moe_gqa_dims *dims /* host */, const uint16_t *q, const uint16_t *k_cache,
+                                 const uint16_t *v_cache, const int32_t *seq_len, float scale, float *out, void *ws,
+                                 size_t ws_bytes, hipStream_t stream, hipEvent_t *events /* host */,
+                                 int32_t n_events);
+
 /* Number of kernels moe_layer launches for these dims (host-only, pure; 0 when
  * the dims are invalid or T == 0). */
 int32_t moe_layer_stage_count(const moe_dims *dims /* host */);

@@ -333,3 +333,45 @@ def device_tokens(shape: Shape, T: int, seed: int, step: int, device):
     g = torch.Generator(device=device)
     g.manual_seed((seed << 24) ^ (step * 104729 + 3))
     return torch.randn(T, shape.H, device=device, generator=g).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- decode attention inputs
+
+KIND_ATTN_Q, KIND_ATTN_K, KIND_ATTN_V = 200, 201, 202
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnShape:
+    """Decode attention: B sequences of one query token, Hq query heads over Hkv
+    KV heads of size D, a cache of S rows per (sequence, KV head)."""
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    S: int
+
+
+# the model's full-attention layer at 32K context, one sequence (the context the
+# pages quote the packing gain at); head size H / Hq
+GQA32K = AttnShape(B=1, Hq=16, Hkv=2, D=128, S=32768)
+
+
+def attn_inputs(shape: AttnShape, seed: int, q_std: float = 1.0):
+    """Host bf16 bits: q [B][Hq][D] ~ N(0, q_std^2), k and v [B][Hkv][S][D] ~ N(0, 1)."""
+    q = _normal(_rng(seed, KIND_ATTN_Q, 0, 0), q_std, (shape.B, shape.Hq, shape.D))
+    k = _normal(_rng(seed, KIND_ATTN_K, 0, 0), 1.0, (shape.B, shape.Hkv, shape.S, shape.D))
+    v = _normal(_rng(seed, KIND_ATTN_V, 0, 0), 1.0, (shape.B, shape.Hkv, shape.S, shape.D))
+    return q, k, v
+
+
+def device_attn(shape: AttnShape, seed: int, device, q_std: float = 1.0):
+    """The same distributions as :func:`attn_inputs`, drawn in device memory with
+    torch's generator (different streams): bf16 tensors q, k, v."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed((seed << 16) ^ 0xA77)
+    q = (torch.randn(shape.B, shape.Hq, shape.D, device=device, generator=g) * q_std).to(torch.bfloat16)
+    k = torch.randn(shape.B, shape.Hkv, shape.S, shape.D, device=device, generator=g).to(torch.bfloat16)
+    v = torch.randn(shape.B, shape.Hkv, shape.S, shape.D, device=device, generator=g).to(torch.bfloat16)
+    return q, k, v

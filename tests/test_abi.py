@@ -242,6 +242,42 @@ def test_decode_stack_checks(lib):
     assert call(d, ws_bytes=need - 1) == -5
 
 
+def test_gqa_workspace_and_checks(lib):
+    """moe_gqa_workspace_size and moe_gqa_decode's host-side checks."""
+    d = bem.gqa_dims(1, 16, 2, 128, 32768)
+    n = lib.moe_gqa_workspace_size(C.byref(d))
+    # 128 runs of 256 rows per KV head, each partial 8 heads x 128 columns + 32 floats
+    assert n == 2 * 128 * (8 * 128 + 32) * 4
+    assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(1, 16, 2, 256, 32768))) == 2 * 256 * (8 * 256 + 32) * 4
+    assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(3, 16, 2, 128, 100))) == 3 * 2 * 1 * (8 * 128 + 32) * 4
+    assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(1, 16, 3, 128, 10))) == 0
+
+    def call(dims, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, scale=0.088, out=FAKE, ws=FAKE, ws_bytes=n):
+        return lib.moe_gqa_decode(C.byref(dims), q, k, v, lens, scale, out, ws, ws_bytes, None)
+
+    assert call(bem.gqa_dims(0, 16, 2, 128, 32768), q=None) == 0       # nothing to do
+    assert call(bem.gqa_dims(1, 16, 3, 128, 64)) == -2                 # heads not a multiple
+    assert call(bem.gqa_dims(1, 16, 2, 128, 0)) == -2
+    assert call(bem.gqa_dims(-1, 16, 2, 128, 64)) == -2
+    assert call(bem.gqa_dims(1, 16, 2, 96, 64)) == -3                  # head size
+    assert call(bem.gqa_dims(1, 34, 2, 128, 64)) == -3                 # 17 query heads per KV head
+    assert call(bem.gqa_dims(1, 16, 2, 128, (1 << 24) + 1)) == -3
+    assert call(d, scale=float("nan")) == -2
+    assert call(d, scale=float("inf")) == -2
+    assert call(d, scale=3e38) == -2                                   # infinite in log2 units
+    assert call(d, q=None) == -1
+    assert call(d, lens=None) == -1
+    assert call(d, v=FAKE + 8) == -4
+    assert call(d, lens=FAKE + 2) == -4
+    assert call(d, ws=None) == -1
+    assert call(d, ws=FAKE + 16) == -4
+    assert call(d, ws_bytes=n - 1) == -5
+    ev = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
+    assert lib.moe_gqa_decode_events(C.byref(d), FAKE, FAKE, FAKE, FAKE, 0.088, FAKE, FAKE, n, None, None, 3) == -1
+    assert lib.moe_gqa_decode_events(C.byref(d), FAKE, FAKE, FAKE, FAKE, 0.088, FAKE, FAKE, n, None, ev, 2) == -2
+    assert lib.moe_gqa_decode_events(C.byref(d), None, FAKE, FAKE, FAKE, 0.088, FAKE, FAKE, n, None, ev, 3) == -1
+
+
 def test_status_strings(lib):
     for code in bem.STATUS:
         assert len(bem.status_string(code)) >= 2
