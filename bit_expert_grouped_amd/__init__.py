@@ -24,6 +24,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNS
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_shared_gate",
            "moe_combine_gated", "moe_router_dequant", "moe_layer", "moe_layer_residual", "moe_layer_events", "moe_layer_stage_count", "moe_layer_stage_name",
            "moe_layer_no_alloc", "moe_decode_stack", "moe_gqa_workspace_size", "moe_gqa_decode", "moe_gqa_decode_events",
+           "moe_gqa_decode_kernels",
            "moe_status_string")
 
 
@@ -105,6 +106,8 @@ def lib():
         L.moe_gqa_workspace_size.argtypes = [C.POINTER(GqaDims)]
         L.moe_gqa_workspace_size.restype = C.c_size_t
         L.moe_gqa_decode.argtypes = [C.POINTER(GqaDims), P, P, P, P, C.c_float, P, P, C.c_size_t, P]
+        L.moe_gqa_decode_kernels.argtypes = [C.POINTER(GqaDims)]
+        L.moe_gqa_decode_kernels.restype = C.c_int32
         L.moe_gqa_decode_events.argtypes = [C.POINTER(GqaDims), P, P, P, P, C.c_float, P, P, C.c_size_t, P, P,
                                             C.c_int32]
         L.moe_layer_stage_count.argtypes = [D]
@@ -460,13 +463,28 @@ def gqa_dims(B, n_q_heads, n_kv_heads, head_dim, max_seq) -> GqaDims:
 
 
 def gqa_workspace(d: GqaDims, device="cuda"):
-    """A workspace tensor of moe_gqa_workspace_size(d) bytes (no clearing needed)."""
+    """A zeroed workspace tensor of moe_gqa_workspace_size(d) bytes."""
     import torch
 
     n = lib().moe_gqa_workspace_size(C.byref(d))
     if n == 0:
         raise MoeError(-2, "moe_gqa_workspace_size")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    # the library requires a zero-filled workspace before its first use
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gqa_decode_kernels(d: GqaDims) -> int:
+    """Kernels a moe_gqa_decode call with dims d launches on the current device (1: merge fused)."""
+    return lib().moe_gqa_decode_kernels(C.byref(d))
+
+
+def gqa_timed_out(ws, d: GqaDims) -> bool:
+    """The workspace's sticky timeout word, the first of its last 256 bytes (a
+    device-side wait of a call gave up; that call's output is invalid)."""
+    import torch
+
+    n = lib().moe_gqa_workspace_size(C.byref(d))
+    return bool(int(ws[n - 256:n - 252].view(torch.int32).item()))
 
 
 def gqa_decode(q, k_cache, v_cache, seq_len, scale=None, out=None, ws=None, events=None):

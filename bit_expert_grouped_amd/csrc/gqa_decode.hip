@@ -31,10 +31,17 @@
 //     are merged in LDS and the workgroup stores one partial: the running max
 //     m (log2 units), the sum l of the rounded probabilities and the
 //     unnormalised output o.
-//   - pass 2 (gqa_merge_kernel): one wave per (sequence, query head, 8 output
-//     columns) merges the partials of all runs, o_total = sum_s 2^(m_s - M) o_s
-//     over l_total likewise, spread over ~B * Hq * D / 8 waves so that the merge
-//     is not bound by one compute unit's bandwidth.
+//   - merge: one wave per (sequence, query head, 8 output columns) combines
+//     the partials of all runs, o_total = sum_s 2^(m_s - M) o_s over l_total
+//     likewise, spread over ~B * Hq * D / 8 waves so that the merge is not bound
+//     by one compute unit's bandwidth.  When the whole grid fits on the device
+//     at once, the merge runs in the same launch: each workgroup counts itself
+//     in on its (sequence, KV head)'s arrival counter after storing its
+//     partial; the last to arrive resets the counter and raises the call's
+//     epoch in 16 copies of a flag (so that no cache line has more than ~8
+//     readers); the others wait (bounded) for their copy, and every workgroup
+//     then merges its share of the head's outputs.  Otherwise a second kernel
+//     (gqa_merge_kernel) merges.
 //
 // Rows past a sequence's length are never read: their loads are clamped to the
 // last valid row (whose values are finite) and their scores set to -inf.
@@ -51,6 +58,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
+constexpr long kSpinLimit = 1l << 20;  // bound of the fused merge's wait (s_sleep rounds)
+constexpr int kFlagCopies = 16;         // copies of the merge's completion flag
+constexpr int kCtlWords = 64 + 32 * kFlagCopies;  // control words per (sequence, KV head)
+static_assert(kCtlWords * 4 <= 4096, "control block of a (sequence, KV head)");
 
 // rows per wave: D <= 128 keeps 64 rows (16 KB of K and 16 KB of V per wave in
 // flight); D = 256 keeps 32
@@ -66,7 +77,105 @@ __device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m); }
 
-template <int D>
+// Partials that another workgroup of the same launch merges go through
+// agent-scope stores and loads, which pass the per-XCD L2 (written through on
+// store, missed on load), so no L2 write-back or invalidation is needed; with
+// the merge in a second kernel, plain accesses do.
+template <bool kCoherent>
+__device__ __forceinline__ void put_f(float* p, float v) {
+    if (kCoherent)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
+template <bool kCoherent>
+__device__ __forceinline__ float get_f(const float* p) {
+    if (kCoherent) return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return *p;
+}
+
+// two consecutive floats (8-byte aligned)
+template <bool kCoherent>
+__device__ __forceinline__ void put_f2(float* p, float x, float y) {
+    const unsigned long long w = ((unsigned long long)__float_as_uint(y) << 32) | __float_as_uint(x);
+    if (kCoherent)
+        __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *reinterpret_cast<unsigned long long*>(p) = w;
+}
+
+template <bool kCoherent>
+__device__ __forceinline__ float2 get_f2(const float* p) {
+    unsigned long long w;
+    if (kCoherent)
+        w = __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    else
+        w = *reinterpret_cast<const unsigned long long*>(p);
+    return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
+}
+
+// One wave merges output columns [8 chunk, 8 chunk + 8) of query head h of
+// sequence b over its ns partials.  Each lane takes two runs per round and
+// issues both runs' loads before any arithmetic (clamped indices, unused runs
+// weighted 0), keeping a running (max, sum, output) rescaled as it goes; the
+// lanes are combined at the end.
+template <int D, bool kCoherent>
+__device__ void merge_item(const GqaArgs& a, int b, int h, int chunk, int ns, int lane) {
+    const int G = a.G, g = h / G, hh = h % G;
+    const size_t stride = (size_t)(G * D + 32);
+    const float* base = a.part + ((size_t)b * a.Hkv + g) * a.n_split * stride;
+    float M = -INFINITY, L = 0.0f;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s0 = 0; s0 < ns; s0 += 2 * kWave) {
+        float mr[2], lr[2], ov[2][8];
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const float* p = base + (size_t)min(s0 + r * kWave + lane, ns - 1) * stride;
+            mr[r] = get_f<kCoherent>(p + G * D + hh);
+            lr[r] = get_f<kCoherent>(p + G * D + 16 + hh);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float2 v = get_f2<kCoherent>(p + hh * D + 8 * chunk + 2 * i);
+                ov[r][2 * i] = v.x;
+                ov[r][2 * i + 1] = v.y;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            if (s0 + r * kWave + lane >= ns) continue;
+            const float Mn = fmaxf(M, mr[r]);
+            const float keep = M == -INFINITY ? 0.0f : exp2f(M - Mn);
+            const float w = exp2f(mr[r] - Mn);
+            M = Mn;
+            L = L * keep + w * lr[r];
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[i] = acc[i] * keep + w * ov[r][i];
+        }
+    }
+    float Mw = M;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, o));
+    const float sc = M == -INFINITY ? 0.0f : exp2f(M - Mw);
+    L *= sc;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] *= sc;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        L += __shfl_xor(L, o);
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[i] += __shfl_xor(acc[i], o);
+    }
+    if (lane == 0) {
+        float* out = a.out + ((size_t)b * a.Hq + h) * D + 8 * chunk;
+        const float inv = ns > 0 ? 1.0f / L : 0.0f;
+        *reinterpret_cast<float4*>(out) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    }
+}
+
+template <int D, bool kFused>
 __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
     constexpr int RW = rows_per_wave<D>();
     constexpr int KK = D / 32;           // score steps per 16-row block
@@ -88,9 +197,19 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
     const int li = lane % 16, lg = lane / 16;
     const int n = min(max(a.seq_len[b], 0), a.S_max);
     const int row0 = split * kWaves * RW;
-    if (row0 >= n) return;  // the whole workgroup: no rows of this sequence here
     const int G = a.G;
+    if (row0 >= n) {
+        // no rows of this sequence here; with the merge in this launch, the
+        // first run of an empty sequence writes its zeros
+        if (kFused && n == 0 && split == 0)
+            for (int e = threadIdx.x; e < G * D; e += kThreads) a.out[((size_t)b * a.Hq + g * G) * D + e] = 0.0f;
+        return;
+    }
     const int wrow0 = row0 + wave * RW;
+    // the merge's control words: arrival counter, epoch, 16 flag copies, one line each
+    unsigned* ctl = a.cnt + ((size_t)b * a.Hkv + g) * kCtlWords;
+    unsigned epoch = 0;
+    if (kFused && threadIdx.x == 0) epoch = __hip_atomic_load(ctl + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const size_t head_base = ((size_t)b * a.Hkv + g) * (size_t)a.S_max * D;
     const uint16_t* kb = a.k + head_base;
     const uint16_t* vb = a.v + head_base;
@@ -209,18 +328,19 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
         for (int i = 0; i < 4; i++) ob[((size_t)wave * 16 + 4 * lg + i) * D + 16 * db + li] = oacc[db][i];
     __syncthreads();
     float* part = a.part + (((size_t)b * a.Hkv + g) * a.n_split + split) * (size_t)(G * D + 32);
-    for (int e = threadIdx.x; e < G * D; e += kThreads) {
+    for (int e = 2 * threadIdx.x; e < G * D; e += 2 * kThreads) {
         const int hh = e / D, d = e % D;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) M = fmaxf(M, red_m[w][hh]);
-        float o = 0.0f;
+        float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) {
             const float sc = red_m[w][hh] == -INFINITY ? 0.0f : exp2f(red_m[w][hh] - M);
-            o += sc * ob[((size_t)w * 16 + hh) * D + d];
+            o0 += sc * ob[((size_t)w * 16 + hh) * D + d];
+            o1 += sc * ob[((size_t)w * 16 + hh) * D + d + 1];
         }
-        part[e] = o;
+        put_f2<kFused>(part + e, o0, o1);
     }
     if (threadIdx.x < G) {
         const int hh = threadIdx.x;
@@ -231,9 +351,39 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; w++)
             L += (red_m[w][hh] == -INFINITY ? 0.0f : exp2f(red_m[w][hh] - M)) * red_l[w][hh];
-        part[G * D + hh] = M;
-        part[G * D + 16 + hh] = L;
+        put_f<kFused>(part + G * D + hh, M);
+        put_f<kFused>(part + G * D + 16 + hh, L);
     }
+    if (!kFused) return;
+
+    // ---- the merge in this launch: wait for every run of this (sequence, KV head)
+    const int ns = (n + kWaves * RW - 1) / (kWaves * RW);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores acknowledged (written through)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned next = epoch + 1u;
+        if (atomicAdd(ctl, 1u) == (unsigned)ns - 1) {
+            // the last run of this head: reset the counter, raise the epoch
+            __hip_atomic_store(ctl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ctl + 32, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int c = 0; c < kFlagCopies; c++)
+                __hip_atomic_store(ctl + 64 + 32 * c, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            unsigned* flag = ctl + 64 + 32 * (split % kFlagCopies);
+            for (long spins = 0; __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != next;
+                 spins++) {
+                if (spins > kSpinLimit) {
+                    __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+    }
+    __syncthreads();
+    const int items = G * (D / 8);
+    for (int it = split + ns * wave; it < items; it += ns * kWaves)
+        merge_item<D, true>(a, b, g * G + it / (D / 8), it % (D / 8), ns, lane);
 }
 
 // One wave per (sequence, query head, 8 output columns): merge the partials of
@@ -248,44 +398,8 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(GqaArgs a) {
     const int chunk = (int)(item % (D / 8));
     const int h = (int)((item / (D / 8)) % a.Hq);
     const int b = (int)(item / ((long)(D / 8) * a.Hq));
-    const int G = a.G, g = h / G, hh = h % G;
     const int n = min(max(a.seq_len[b], 0), a.S_max);
-    const int ns = (n + RWG - 1) / RWG;
-    const size_t stride = (size_t)(G * D + 32);
-    const float* base = a.part + ((size_t)b * a.Hkv + g) * a.n_split * stride;
-    float M = -INFINITY;
-    for (int s = lane; s < ns; s += kWave) M = fmaxf(M, base[(size_t)s * stride + G * D + hh]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float L = 0.0f;
-    for (int s = lane; s < ns; s += kWave) {
-        const float* p = base + (size_t)s * stride;
-        const float w = exp2f(p[G * D + hh] - M);
-        L += w * p[G * D + 16 + hh];
-        const float4 o0 = *reinterpret_cast<const float4*>(p + hh * D + 8 * chunk);
-        const float4 o1 = *reinterpret_cast<const float4*>(p + hh * D + 8 * chunk + 4);
-        acc[0] += w * o0.x;
-        acc[1] += w * o0.y;
-        acc[2] += w * o0.z;
-        acc[3] += w * o0.w;
-        acc[4] += w * o1.x;
-        acc[5] += w * o1.y;
-        acc[6] += w * o1.z;
-        acc[7] += w * o1.w;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        L += __shfl_xor(L, o);
-#pragma unroll
-        for (int i = 0; i < 8; i++) acc[i] += __shfl_xor(acc[i], o);
-    }
-    if (lane == 0) {
-        float* out = a.out + ((size_t)b * a.Hq + h) * D + 8 * chunk;
-        const float inv = ns > 0 ? 1.0f / L : 0.0f;
-        *reinterpret_cast<float4*>(out) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-        *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-    }
+    merge_item<D, false>(a, b, h, chunk, (n + RWG - 1) / RWG, lane);
 }
 
 template <int D>
@@ -293,7 +407,14 @@ hipError_t launch_gqa_d(const GqaArgs& a, hipStream_t stream, hipEvent_t* events
     hipError_t e;
     if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
     const dim3 grid1((unsigned)a.n_split, (unsigned)a.Hkv, (unsigned)a.B);
-    hipLaunchKernelGGL(gqa_partial_kernel<D>, grid1, dim3(kThreads), 0, stream, a);
+    if (a.fused) {
+        hipLaunchKernelGGL((gqa_partial_kernel<D, true>), grid1, dim3(kThreads), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        for (int i = 1; i < 3 && events; i++)
+            if ((e = hipEventRecord(events[i], stream)) != hipSuccess) return e;
+        return hipSuccess;
+    }
+    hipLaunchKernelGGL((gqa_partial_kernel<D, false>), grid1, dim3(kThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return e;
     const long items = (long)a.B * a.Hq * (D / 8);
@@ -307,6 +428,30 @@ hipError_t launch_gqa_d(const GqaArgs& a, hipStream_t stream, hipEvent_t* events
 }  // namespace
 
 int gqa_rows_per_split(int D) { return kWaves * (D <= 128 ? 64 : 32); }
+
+namespace {
+
+template <int D>
+int fused_capacity() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&gqa_partial_kernel<D, true>), kThreads, 0) != hipSuccess)
+        return 0;
+    return cus * per_cu;
+}
+
+}  // namespace
+
+int gqa_fused_capacity(int D) {
+    switch (D) {
+        case 64: return fused_capacity<64>();
+        case 128: return fused_capacity<128>();
+        case 256: return fused_capacity<256>();
+        default: return 0;
+    }
+}
 
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream, hipEvent_t* events) {
     switch (a.D) {

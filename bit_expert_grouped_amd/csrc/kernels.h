@@ -259,6 +259,10 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 // partials, then their merge).  q [B][Hq][D], k/v [B][Hkv][S_max][D] bf16,
 // seq_len [B]; part: B * Hkv * n_split partials of G * D + 32 floats (o [G][D],
 // then m and l, 16 slots each); out [B][Hq][D] float32.  c = scale * log2(e).
+// With fused set (every workgroup of the grid resident at once), one kernel
+// also merges: cnt holds 1024 control words per (sequence, KV head) (arrival
+// counter, epoch, flag copies; zero before the first call); err is set if a
+// wait timed out.
 struct GqaArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -266,12 +270,17 @@ struct GqaArgs {
     const int32_t* seq_len;
     float* part;
     float* out;
+    unsigned* cnt;
+    unsigned* err;
     int B, Hq, Hkv, G, D, S_max, n_split;
+    int fused;
     float c;
 };
 
 // rows of the cache one pass-1 workgroup covers (the run length of a partial)
 int gqa_rows_per_split(int D);
+// workgroups of the fused kernel the current device holds at once (0 on error)
+int gqa_fused_capacity(int D);
 // events (nullable): 3 events recorded before pass 1, between the passes and after pass 2
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream, hipEvent_t* events);
 

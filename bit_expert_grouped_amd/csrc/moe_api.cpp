@@ -689,10 +689,29 @@ int gqa_splits(const moe_gqa_dims* d) {
     return (d->max_seq + r - 1) / r;
 }
 
-size_t gqa_ws_bytes(const moe_gqa_dims* d) {
+// workspace: the partials, then 4 KiB of control words per (sequence, KV
+// head) (arrival counter, epoch and flag copies of the fused merge), then the
+// timeout word
+size_t gqa_part_bytes(const moe_gqa_dims* d) {
     const size_t G = (size_t)(d->n_q_heads / d->n_kv_heads);
     const size_t bytes = (size_t)d->B * d->n_kv_heads * (size_t)gqa_splits(d) * (G * d->head_dim + 32) * 4;
     return (bytes + 255) & ~(size_t)255;
+}
+
+size_t gqa_ws_bytes(const moe_gqa_dims* d) {
+    return gqa_part_bytes(d) + (size_t)d->B * d->n_kv_heads * 4096 + 256;
+}
+
+// workgroups of the fused attention kernel the current device holds at once
+int gqa_capacity(int D) {
+    static std::mutex mu;
+    static int cap[64][3];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    const int i = D == 64 ? 0 : D == 128 ? 1 : 2;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cap[dev][i] == 0) cap[dev][i] = gqa_fused_capacity(D);
+    return cap[dev][i];
 }
 
 }  // namespace
@@ -727,6 +746,8 @@ moe_status gqa_impl(const moe_gqa_dims* d, const uint16_t* q, const uint16_t* k_
     a.v = v_cache;
     a.seq_len = seq_len;
     a.part = static_cast<float*>(ws);
+    a.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + gqa_part_bytes(d));
+    a.err = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + gqa_part_bytes(d) + (size_t)d->B * d->n_kv_heads * 4096);
     a.out = out;
     a.B = d->B;
     a.Hq = d->n_q_heads;
@@ -735,6 +756,7 @@ moe_status gqa_impl(const moe_gqa_dims* d, const uint16_t* q, const uint16_t* k_
     a.D = d->head_dim;
     a.S_max = d->max_seq;
     a.n_split = gqa_splits(d);
+    a.fused = moe_gqa_decode_kernels(d) == 1 ? 1 : 0;
     a.c = c;
     HIP_TRY(launch_gqa_decode(a, stream, events));
     return MOE_OK;
@@ -748,6 +770,11 @@ moe_status moe_gqa_decode(const moe_gqa_dims* d, const uint16_t* q, const uint16
                           const uint16_t* v_cache, const int32_t* seq_len, float scale, float* out, void* ws,
                           size_t ws_bytes, hipStream_t stream) {
     return gqa_impl(d, q, k_cache, v_cache, seq_len, scale, out, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t moe_gqa_decode_kernels(const moe_gqa_dims* d) {
+    if (check_gqa_dims(d) != MOE_OK || d->B == 0) return 0;
+    return (int64_t)gqa_splits(d) * d->n_kv_heads * d->B <= (int64_t)gqa_capacity(d->head_dim) ? 1 : 2;
 }
 
 moe_status moe_gqa_decode_events(const moe_gqa_dims* d, const uint16_t* q, const uint16_t* k_cache,

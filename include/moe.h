@@ -371,24 +371,37 @@ typedef struct {
 
 /* Bytes of device workspace moe_gqa_decode needs (host-only, pure; 0 when the
  * dims are invalid): B * n_kv_heads * ceil(max_seq / R) partials of
- * (G * head_dim + 32) floats, R = 256 rows (128 at head_dim 256).  It needs no
- * clearing.  Not shared with moe_workspace_size's workspace contract: any
- * buffer of this size will do, reused freely between calls that do not
- * overlap in time. */
+ * (G * head_dim + 32) floats (R = 256 rows, 128 at head_dim 256), rounded up
+ * to 256 bytes, then 4 KiB of control words per (sequence, KV head), then 256
+ * bytes whose first word is set to nonzero, and stays so, if a device-side
+ * wait of a call timed out (that call's output is then invalid).  Zero-fill it
+ * once after allocating it; every call leaves it ready for the next, for any
+ * dims that fit.  Its own contract, separate from moe_workspace_size's; calls
+ * that share one must not overlap in time. */
 size_t moe_gqa_workspace_size(const moe_gqa_dims *dims /* host */);
 
 /* q [B][Hq][D] bf16; k_cache, v_cache [B][Hkv][max_seq][D] bf16 (16-byte
  * aligned, each head's rows contiguous); seq_len [B] int32 (4-byte aligned);
  * out [B][Hq][D] float32; scale finite (1/sqrt(D) is the usual one; NaN or
  * infinite: MOE_ERR_SHAPE); ws of moe_gqa_workspace_size bytes, 256-byte
- * aligned (MOE_ERR_WORKSPACE when smaller).  Two kernels on `stream`. */
+ * aligned (MOE_ERR_WORKSPACE when smaller).  One kernel on `stream` when the
+ * device holds all B * n_kv_heads * ceil(max_seq / R) of its workgroups at
+ * once (they then wait on each other to merge their partials: launch nothing
+ * else on the device concurrently), two kernels otherwise. */
 moe_status moe_gqa_decode(const moe_gqa_dims *dims /* host */, const uint16_t *q, const uint16_t *k_cache,
                           const uint16_t *v_cache, const int32_t *seq_len, float scale, float *out, void *ws,
                           size_t ws_bytes, hipStream_t stream);
 
+/* Number of kernels a moe_gqa_decode call with these dims launches on the
+ * current device: 1 when all its workgroups fit on the device at once (the
+ * merge of the partials then runs in the same launch), else 2; 0 when the dims
+ * are invalid or B == 0 (host-only). */
+int32_t moe_gqa_decode_kernels(const moe_gqa_dims *dims /* host */);
+
 /* moe_gqa_decode plus HIP events, for instrumentation: events[0] is recorded
- * on `stream` before the first of its two kernels (the per-run partials),
- * events[1] between them and events[2] after the second (their merge).
+ * on `stream` before its first kernel (the per-run partials), events[1] after
+ * it and events[2] after the merge (with the merge in the same kernel,
+ * events[1] and events[2] both follow that kernel).
  * events NULL: MOE_ERR_NULL; n_events < 3: MOE_ERR_SHAPE.  B == 0 records
  * nothing. */
 moe_status moe_gqa_decode_events(const moe_gqa_dims *dims /* host */, const uint16_t *q, const uint16_t *k_cache,

@@ -26,7 +26,8 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^[a-z_ ]*?\**\s*\b(moe_[a-z_]+)\s*\(", text, re.M)))
+    # declarations start in column 0 with their return type
+    return sorted(set(re.findall(r"^(?:const\s+)?[a-z_][a-z_0-9]*\s*\**\s*(moe_[a-z_]+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -246,10 +247,13 @@ def test_gqa_workspace_and_checks(lib):
     """moe_gqa_workspace_size and moe_gqa_decode's host-side checks."""
     d = bem.gqa_dims(1, 16, 2, 128, 32768)
     n = lib.moe_gqa_workspace_size(C.byref(d))
-    # 128 runs of 256 rows per KV head, each partial 8 heads x 128 columns + 32 floats
-    assert n == 2 * 128 * (8 * 128 + 32) * 4
-    assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(1, 16, 2, 256, 32768))) == 2 * 256 * (8 * 256 + 32) * 4
-    assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(3, 16, 2, 128, 100))) == 3 * 2 * 1 * (8 * 128 + 32) * 4
+    # 128 runs of 256 rows per KV head, each partial 8 heads x 128 columns + 32 floats;
+    # 4 KiB of control words per (sequence, KV head); 256 bytes for the timeout word
+    assert n == 2 * 128 * (8 * 128 + 32) * 4 + 2 * 4096 + 256
+    assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(1, 16, 2, 256, 32768))) == \
+        2 * 256 * (8 * 256 + 32) * 4 + 2 * 4096 + 256
+    assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(3, 16, 2, 128, 100))) == \
+        3 * 2 * 1 * (8 * 128 + 32) * 4 + 6 * 4096 + 256
     assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(1, 16, 3, 128, 10))) == 0
 
     def call(dims, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, scale=0.088, out=FAKE, ws=FAKE, ws_bytes=n):
@@ -272,6 +276,8 @@ def test_gqa_workspace_and_checks(lib):
     assert call(d, ws=None) == -1
     assert call(d, ws=FAKE + 16) == -4
     assert call(d, ws_bytes=n - 1) == -5
+    assert lib.moe_gqa_decode_kernels(C.byref(bem.gqa_dims(0, 16, 2, 128, 64))) == 0
+    assert lib.moe_gqa_decode_kernels(C.byref(bem.gqa_dims(1, 16, 3, 128, 64))) == 0
     ev = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
     assert lib.moe_gqa_decode_events(C.byref(d), FAKE, FAKE, FAKE, FAKE, 0.088, FAKE, FAKE, n, None, None, 3) == -1
     assert lib.moe_gqa_decode_events(C.byref(d), FAKE, FAKE, FAKE, FAKE, 0.088, FAKE, FAKE, n, None, ev, 2) == -2

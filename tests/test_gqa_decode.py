@@ -64,8 +64,11 @@ def run(shape, lens, seed, q_std=1.0, scale=None):
     lens = np.asarray(lens, dtype=np.int32)
     ref = oracle.gqa_decode(q, k, v, lens, scale)
     m = bem()
-    out = m.gqa_decode(_dev(q), _dev(k), _dev(v), torch.from_numpy(lens).cuda(), scale)
+    d = m.gqa_dims(shape.B, shape.Hq, shape.Hkv, shape.D, shape.S)
+    ws = m.gqa_workspace(d)
+    out = m.gqa_decode(_dev(q), _dev(k), _dev(v), torch.from_numpy(lens).cuda(), scale, ws=ws)
     torch.cuda.synchronize()
+    assert not m.gqa_timed_out(ws, d)
     return out.cpu().numpy(), ref, v, lens
 
 
@@ -85,6 +88,17 @@ def test_gqa_small_shapes(B, Hq, Hkv, D, S, lens, q_std):
     print("case B=%d Hq=%d Hkv=%d D=%d S=%d lens=%s q_std=%g" % (B, Hq, Hkv, D, S, lens, q_std), flush=True)
     out, ref, v, lens = run(shape, lens, 61, q_std)
     check(out, ref, v, lens, Hq // Hkv, "gqa %s" % (shape,))
+
+
+def test_gqa_grid_larger_than_the_device():
+    """24 sequences of 4096 rows: 768 workgroups, more than the device holds at
+    once, so the partials are merged by a second kernel."""
+    shape = moe_synth.AttnShape(B=24, Hq=16, Hkv=2, D=128, S=4096)
+    assert bem().gqa_decode_kernels(bem().gqa_dims(24, 16, 2, 128, 4096)) == 2
+    assert bem().gqa_decode_kernels(bem().gqa_dims(1, 16, 2, 128, 32768)) == 1
+    lens = [4096 - 97 * i for i in range(24)]
+    out, ref, v, lens = run(shape, lens, 66)
+    check(out, ref, v, lens, 8, "two-kernel merge")
 
 
 def test_gqa_scale_argument():
