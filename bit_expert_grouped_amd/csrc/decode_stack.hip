@@ -33,19 +33,18 @@
 //   - gate/up: workgroup w takes 16 rows of the intermediate dim of one routed
 //     slot (2 rows per wave, gate and up) and publishes h as float16 pairs; the
 //     shared expert's gate/up (2 rows per workgroup) runs on weights read ahead;
-//   - down: workgroup w takes 64 output rows of one routed slot (8 rows per
-//     wave, one 64-column group per lane) and 8 rows of the shared expert, and
-//     adds w_j * (W_down h) into the layer's output accumulator;
-//   - output: each down workgroup stores its contributions, w_j * (W_down h)
-//     for its rows, as {epoch, float32} words in one array per slot (no
-//     atomics; every word has one reader).  Workgroup w owns columns
-//     [8 w, 8 w + 8): it polls their k + 1 contributions, sums them in slot
-//     order (so the output is the same bit for bit on every call), forms the
-//     next layer's stream x(l+1) = bf16(x(l) + sum) and publishes it packed
-//     ({16-bit tag, 3 bf16} words) in kStackXCopies copies; every workgroup
-//     then reads the whole stream from its copy.  Broadcasting a few KB to 256
-//     workgroups costs what its most-read cache line costs, so every value
-//     all workgroups read is replicated until each copy has ~8 readers.
+//   - down and output: workgroup w owns output columns [8 w, 8 w + 8) and
+//     computes them for every slot: wave j the 8 rows of routed slot j (one
+//     64-column group per lane), waves 4-7 the 8 rows of the shared expert.
+//     Every workgroup therefore reads every slot's h (each gate/up unit
+//     publishes its h in kStackRoutedHCopies copies).  The k + 1
+//     contributions of a column are summed in LDS in slot order (so the output
+//     is the same bit for bit on every call) and the workgroup forms the next
+//     layer's stream x(l+1) = bf16(x(l) + sum) for its columns and publishes
+//     it packed ({16-bit tag, 3 bf16} words) in kStackXCopies copies; every
+//     workgroup then reads the whole stream from its copy.  Broadcasting a few
+//     KB to 256 workgroups costs what its most-read cache line costs, so every
+//     value all workgroups read is replicated until each copy has ~8 readers.
 //   - every exchange region is kept twice, by the parity of the layer's epoch:
 //     a workgroup can run at most one layer ahead of the slowest (each layer's
 //     logits come from all of them), so a word is never rewritten while a
@@ -70,7 +69,6 @@ using namespace dec;
 constexpr int kWorkers = 8;
 constexpr int kThreads = kWorkers * kWave;
 constexpr int kGURows = 16;  // intermediate rows of a routed gate/up unit: 2 per wave
-constexpr int kDRows = 64;   // output rows of a routed down unit: 8 per wave
 constexpr long kSpinLimit = 1l << 20;
 constexpr int kHWords = kStackMaxI / 2;  // h words per slot (float16 pairs)
 constexpr int kPollThreads = kStackMaxH / 8;  // threads that poll the output, one 8-column block each
@@ -91,8 +89,9 @@ struct StackShared {
     float ssq[4];                // sums of squares of the stream, one per polling wave
     uint4 hsp[kStackMaxI / 8];   // shared expert's h, pairs per 8 columns
     float2 hss[kStackMaxI / 8];
-    uint4 hrp[kStackMaxI / 8];   // routed h of this workgroup's down slot
-    float2 hrs[kStackMaxI / 8];
+    uint4 hrp[8][kStackMaxI / 8];  // routed h of every slot, pairs per 8 columns
+    float2 hrs[8][kStackMaxI / 8];
+    float ycon[8 + 1][8];        // contributions to the owned columns: routed slots, then the shared expert
     uint32_t keys[kMaxE];        // order keys of the logits
     uint32_t tkey[kMaxTopK];     // the selected keys, in expert order
     int tidx[kMaxTopK];
@@ -105,7 +104,6 @@ struct StackShared {
     int ncand;                   // candidates of the top k (keys >= min of m2)
     uint32_t ckey[kWave];
     int cidx[kWave];
-    int xflag;                   // layer whose output wave 0 has seen complete
     int last;
 };
 
@@ -248,65 +246,70 @@ __device__ __forceinline__ void read_ahead(const StackArgs& a, int l, int hw, co
     }
 }
 
-// The owner step of workgroup w (wave 0; lanes 0..7 own columns 8 w + lane):
-// poll the contributions of epoch epp to the owned columns, sum them in slot
-// order (the k routed slots, then the shared expert), add the stream xb
-// entering that layer, and publish the result, the stream of epoch ep_next,
-// in every copy.  Lane c < 8 returns its column's sum (out) and new stream
-// value (xn).  Returns false on timeout (then sets the error word).
-__device__ bool owner_step(const StackArgs& a, int w, int lane, unsigned epp, unsigned ep_next, int n_slots,
-                           bool publish_next, const uint16_t* xb, bool failed, float& out, uint16_t& xn) {
-    const bool mine = lane < 8 && 8 * w < a.H;
-    const unsigned long long* pp = a.part + (size_t)(epp & 1) * kStackSlots * kStackMaxH + 8 * w + lane;
+// Publish the owned block of the stream of epoch ep_next (wave 0; lane c < 8
+// holds column 8 w + c in xn): the block's 8 values in every lane, packed 3 to
+// a word under the tag, in every copy.
+__device__ void publish_x(const StackArgs& a, int w, int lane, unsigned ep_next, uint16_t xn) {
+    uint32_t b[8];
+#pragma unroll
+    for (int c = 0; c < 8; c++) b[c] = (uint32_t)__shfl((int)xn, c);
+    const unsigned long long tag = (unsigned long long)xtag(ep_next) << 48;
+    const unsigned long long words[3] = {
+        tag | ((unsigned long long)b[2] << 32) | ((unsigned long long)b[1] << 16) | b[0],
+        tag | ((unsigned long long)b[5] << 32) | ((unsigned long long)b[4] << 16) | b[3],
+        tag | ((unsigned long long)b[7] << 16) | b[6]};
+    unsigned long long* dst = a.xpub + (size_t)(ep_next & 1) * kStackXCopies * kStackXWords + 3 * w;
+    for (int i = lane; i < 3 * kStackXCopies; i += kWave) {
+        const int q = i % 3, copy = i / 3;
+        const unsigned long long word = q == 0 ? words[0] : q == 1 ? words[1] : words[2];
+        if (8 * w < a.H)
+            __hip_atomic_store(dst + (size_t)copy * kStackXWords + q, word, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Poll the n_words {epoch, float16 pair} words of one slot's h (the whole wave:
+// 4 words per lane, all in flight at once) into LDS as pairs in nibble order,
+// then form the low/high sums of every block (lane b: block b).  Returns false
+// on timeout (then sets the error word).
+__device__ bool poll_slot_h(const unsigned long long* src, int n_words, unsigned epoch, uint4* pairs, float2* sums,
+                            int lane, bool failed, unsigned* ctl) {
+    constexpr int kPer = kHWords / kWave;  // words per lane
     bool ok = true;
-    float o = 0.0f;
+    unsigned long long val[kPer] = {};
     if (!failed) {
         for (long spins = 0;; spins++) {
             bool have = true;
-            if (mine) {
-                // all slots' words in flight at once (a loop of dependent
-                // loads would wait out each one's latency in turn)
-                unsigned long long v[kStackSlots];
 #pragma unroll
-                for (int j = 0; j < kStackSlots; j++) v[j] = peek(pp + (size_t)min(j, n_slots - 1) * kStackMaxH);
-                o = 0.0f;
+            for (int t = 0; t < kPer; t++) val[t] = peek(src + min(kWave * t + lane, n_words - 1));
 #pragma unroll
-                for (int j = 0; j < kStackSlots; j++) {
-                    if (j < n_slots) {
-                        have = have && (unsigned)(v[j] >> 32) == epp;
-                        o += __uint_as_float((uint32_t)v[j]);
-                    }
-                }
-            }
+            for (int t = 0; t < kPer; t++) have = have && (unsigned)(val[t] >> 32) == epoch;
             if (__ballot(!have) == 0) break;
             if (spins > kSpinLimit) {
-                if (lane == 0) flag_error(a.ctl);
+                if (lane == 0) flag_error(ctl);
                 ok = false;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
     }
-    const float xo = mine ? bf16_to_f32(xb[8 * w + lane]) : 0.0f;
-    xn = bf16_rne(xo + o);
-    out = o;
-    if (publish_next) {
-        // the block's 8 values in every lane, packed 3 to a word under the tag
-        uint32_t b[9];
+    _Float16* hh = reinterpret_cast<_Float16*>(pairs);
 #pragma unroll
-        for (int c = 0; c < 8; c++) b[c] = (uint32_t)__shfl((int)xn, c);
-        b[8] = 0;
-        const unsigned long long tag = (unsigned long long)xtag(ep_next) << 48;
-        unsigned long long* dst =
-            a.xpub + (size_t)(ep_next & 1) * kStackXCopies * kStackXWords + 3 * w;
-        for (int i = lane; i < 3 * kStackXCopies; i += kWave) {
-            const int q = i % 3, copy = i / 3;
-            const unsigned long long word =
-                tag | ((unsigned long long)b[3 * q + 2] << 32) | ((unsigned long long)b[3 * q + 1] << 16) | b[3 * q];
-            if (8 * w < a.H)
-                __hip_atomic_store(dst + (size_t)copy * kStackXWords + q, word, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = 0; t < kPer; t++) {
+        const int wd = kWave * t + lane;
+        if (wd < n_words) {
+            const half2_t pr = as_half2((uint32_t)val[t]);
+            const int c0 = 2 * wd, c1 = 2 * wd + 1;
+            hh[(c0 >> 3) * 8 + slot_of_column(c0 & 7)] = pr.x;
+            hh[(c1 >> 3) * 8 + slot_of_column(c1 & 7)] = pr.y;
         }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's values are in LDS
+    if (lane * 4 < n_words) {
+        const uint4 p = pairs[lane];
+        const half2_t a = as_half2(p.x), b = as_half2(p.y), c = as_half2(p.z), d = as_half2(p.w);
+        sums[lane] = make_float2(((float)a.x + (float)a.y) + ((float)c.x + (float)c.y),
+                                 ((float)b.x + (float)b.y) + ((float)d.x + (float)d.y));
     }
     return ok;
 }
@@ -331,9 +334,8 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
     const int gu_per_slot = I / kGURows;
     const bool has_gu = w < k * gu_per_slot;
     const int gu_slot = min(w / gu_per_slot, k - 1), gu_i0 = (w % gu_per_slot) * kGURows;
-    const int dn_per_slot = H / kDRows;
-    const bool has_dn = w < k * dn_per_slot;
-    const int dn_slot = min(w / dn_per_slot, k - 1), dn_n0 = (w % dn_per_slot) * kDRows;
+    const bool owns = 8 * w < H;  // output columns [8 w, 8 w + 8)
+    const int own0 = min(8 * w, H - 8);
     const bool has_sgu = shared && w < a.I_shared / 2;
     const int nblk = H / 8;
     const int chunks = H / 32;
@@ -359,18 +361,14 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
     const uint32_t off_gq = (uint32_t)(gchunk * 16), off_gsb = (uint32_t)((gchunk / 2) * kSB);
     const int ia = min(gu_i0 + 2 * wave, I - 2);  // this wave's two intermediate rows
     const int dgrp = lane % 8, dgrp_c = min(dgrp, I / kGroup - 1);
-    const int drow = dn_n0 + 8 * wave + lane / 8;  // this lane's output row (H % 64 == 0: always < H)
     const uint32_t off_dq = (uint32_t)((lane / 8) * (I / 2) + dgrp_c * 32);
     const uint32_t off_dsb = (uint32_t)(((lane / 8) * (I / kGroup) + dgrp_c) * kSB);
-    const bool dmine = has_dn && dgrp < I / kGroup;
+    const bool dmine = owns && wave < k && dgrp < I / kGroup;  // routed slot `wave`, row own0 + lane / 8
 
     Ahead<SB> ah{};
     if (holder) read_ahead<SB>(a, 0, hw, ao, ah);
     uint32_t mykey = 0;  // waves 0-3: the order key of expert tid's logit
-    if (tid == 0) {
-        sh.ncand = 0;
-        sh.xflag = -1;
-    }
+    if (tid == 0) sh.ncand = 0;
 
     // the normalisation weight of each block of 8 columns, read ahead a layer
     // at a time by waves 0-3 (thread t: block t)
@@ -397,22 +395,10 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
         unsigned long long* logits_p = a.logits + par * (kStackLogitCopies * kMaxE);
         unsigned long long* sh_h_p = a.sh_h + par * (kStackSharedHCopies * kHWords);
         unsigned long long* rt_h_p = a.rt_h + par * (8 * kStackRoutedHCopies * kHWords);
-        unsigned long long* part_p = a.part + par * (kStackSlots * kStackMaxH);
 
-        // ---- x of this layer: the owner step for the previous layer's output
-        // (wave 0), then every block of the stream from this workgroup's copy
-        // (waves 0-3, thread t: block t)
+        // ---- x of this layer: every block of the stream from this workgroup's
+        // copy (waves 0-3, thread t: block t)
         if (l > 0) {
-            if (wave == 0) {
-                float o;
-                uint16_t xn;
-                const bool ok = owner_step(a, w, lane, ep - 1, ep, n_slots, true, sh.xb, failed, o, xn);
-                failed = failed || !ok;
-                if (lane < 8 && 8 * w < H) {
-                    if (a.layer_out) a.layer_out[(size_t)(l - 1) * H + 8 * w + lane] = o;
-                    if (a.layer_x) a.layer_x[(size_t)l * H + 8 * w + lane] = xn;
-                }
-            }
             if (tid < kPollThreads) {
                 const unsigned long long* src =
                     a.xpub + (par * kStackXCopies + (size_t)(w % kStackXCopies)) * kStackXWords + 3 * tid;
@@ -650,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
         __syncthreads();  // B4: the routing in LDS
 
         // ---- routed loads, gate/up rows first, then down rows
-        const int ex_gu = uniform(sh.sel_e[gu_slot]), ex_dn = uniform(sh.sel_e[dn_slot]);
+        const int ex_gu = uniform(sh.sel_e[gu_slot]), ex_dn = uniform(sh.sel_e[min(wave, k - 1)]);
         uint4 gq[4];
         SB gs[4], gb[4];
 #pragma unroll
@@ -666,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
         uint4 dq0, dq1;
         SB ds, db;
         {
-            const size_t row0 = (size_t)ex_dn * H + dn_n0 + 8 * wave;  // this wave's first row
+            const size_t row0 = (size_t)ex_dn * H + own0;  // this wave's slot, the owned rows
             const QMatStride& st = a.experts_stride.down;
             ds = ld<SB>(lay(a.experts.down.s, st.s, l) + row0 * (I / kGroup) * kSB, off_dsb);
             db = ld<SB>(lay(a.experts.down.b, st.b, l) + row0 * (I / kGroup) * kSB, off_dsb);
@@ -730,49 +716,55 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                 y = affine(sb_to_f32<SB>(ah.sdn_s), sb_to_f32<SB>(ah.sdn_b), alo, ahi, s0.x + s1.x, s0.y + s1.y);
             }
             y = group_sum(y, 32);
-            if (lane % 32 == 0 && row < H) publish(part_p + (size_t)k * kStackMaxH + row, ep, __float_as_uint(y));
+            if (lane % 32 == 0) sh.ycon[k][2 * hw + lane / 32] = y;
         }
 
-        // ---- routed down: h of the slot, then 8 rows x one group per lane
-        if (has_dn) {
-            const bool ok = poll_h<32>(rt_h_p + ((size_t)dn_slot * kStackRoutedHCopies + w % kStackRoutedHCopies) *
-                                                    kHWords,
-                                       I / 2, ep, sh.hrp, sh.hrs, wave, lane, failed, a.ctl);
+        // ---- routed down: wave j polls slot j's h, then 8 rows x one group per lane
+        if (owns && wave < k) {
+            const bool ok = poll_slot_h(rt_h_p + ((size_t)wave * kStackRoutedHCopies + w % kStackRoutedHCopies) *
+                                                     kHWords,
+                                        I / 2, ep, sh.hrp[wave], sh.hrs[wave], lane, failed, a.ctl);
             failed = failed || !ok;
         }
-        __syncthreads();  // routed h in LDS
         float y = 0.0f;
         if (dmine) {
             const uint32_t wv[8] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w};
             float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
 #pragma unroll
             for (int m = 0; m < 8; m++) {
-                dot_word(wv[m], pairs_of(sh.hrp[8 * dgrp + m]), alo, ahi);
-                const float2 sm = sh.hrs[8 * dgrp + m];
+                dot_word(wv[m], pairs_of(sh.hrp[wave][8 * dgrp + m]), alo, ahi);
+                const float2 sm = sh.hrs[wave][8 * dgrp + m];
                 lo += sm.x;
                 hi += sm.y;
             }
             y = affine(sb_to_f32<SB>(ds), sb_to_f32<SB>(db), alo, ahi, lo, hi);
         }
         y = group_sum(y, 8);  // the row's groups: 8 lanes
-        if (dgrp == 0 && has_dn)
-            publish(part_p + (size_t)dn_slot * kStackMaxH + drow, ep, __float_as_uint(sh.sel_w[dn_slot] * y));
+        if (dgrp == 0 && wave < k) sh.ycon[wave][lane / 8] = sh.sel_w[wave] * y;
         // every poll and product of this layer is done: waves 4-7 read the next
         // layer's data-independent weights ahead; they land while this layer's
         // output completes
         __builtin_amdgcn_sched_barrier(0);
         if (holder) read_ahead<SB>(a, min(l + 1, L - 1), hw, ao, ah);
         if (tid < kPollThreads && a.norm_w) gam = ld<uint4>(lay(a.norm_w, a.norm_stride, min(l + 1, L - 1)), off_norm);
-    }
+        __syncthreads();  // every contribution to the owned columns in LDS
 
-    // ---- the output of the last layer: the owner step, into x_out
-    if (wave == 0) {
-        float o;
-        uint16_t xn;
-        owner_step(a, w, lane, e0 + (unsigned)L, 0u, n_slots, false, sh.xb, failed, o, xn);
-        if (lane < 8 && 8 * w < H) {
-            a.x_out[8 * w + lane] = xn;
-            if (a.layer_out) a.layer_out[(size_t)(L - 1) * H + 8 * w + lane] = o;
+        // ---- the owned columns of the layer's output and of the next stream
+        // (wave 0, lane c < 8: column 8 w + c), summed in slot order
+        if (wave == 0) {
+            float o = 0.0f;
+            uint16_t xn = 0;
+            if (lane < 8 && owns) {
+                for (int j = 0; j < n_slots; j++) o += sh.ycon[j][lane];
+                xn = bf16_rne(bf16_to_f32(sh.xb[8 * w + lane]) + o);
+                if (a.layer_out) a.layer_out[(size_t)l * H + 8 * w + lane] = o;
+                if (l + 1 < L) {
+                    if (a.layer_x) a.layer_x[(size_t)(l + 1) * H + 8 * w + lane] = xn;
+                } else {
+                    a.x_out[8 * w + lane] = xn;
+                }
+            }
+            if (l + 1 < L) publish_x(a, w, lane, ep + 1, xn);
         }
     }
 

@@ -171,8 +171,8 @@ struct DecodeArgs {
 // launch, each layer reading the RMS-normalised residual stream): a grid of kStackGrid workgroups, all resident at once, that hand
 // values over through words of the stack region below (fixed offsets after the
 // one-layer decode region, zero before the first call).  Limits: T = 1,
-// H <= kStackMaxH, I <= kStackMaxI, top_k * I / 16 <= kStackGrid and
-// top_k * H / 64 <= kStackGrid.
+// H <= kStackMaxH (8 output columns per workgroup), I <= kStackMaxI,
+// top_k * I / 16 <= kStackGrid.
 constexpr int kStackGrid = 256;
 constexpr int kStackMaxH = 2048;
 constexpr int kStackMaxI = 512;
@@ -180,18 +180,16 @@ constexpr int kStackMaxI = 512;
 // each copy has few readers: polled words are what floods the memory system.
 constexpr int kStackLogitCopies = 32;    // of the logits: 8 readers each
 constexpr int kStackSharedHCopies = 32;  // of the shared expert's h: 8 readers each
-constexpr int kStackRoutedHCopies = 4;   // of each routed slot's h: 8 readers each
+constexpr int kStackRoutedHCopies = 32;  // of each routed slot's h (every workgroup reads every slot): 8 readers each
 constexpr int kStackXCopies = 32;        // of the stream entering a layer: 8 readers each
 constexpr int kStackXWords = kStackMaxH / 8 * 3;  // per copy: 3 words {16-bit tag, 3 bf16} per 8 columns
-constexpr int kStackSlots = 8 + 1;       // contribution arrays: k routed slots, then the shared expert
 // every region twice: layer l uses the half of its epoch's parity
 constexpr size_t kStackLogitWords = (size_t)2 * kStackLogitCopies * 256;
 constexpr size_t kStackSharedHWords = (size_t)2 * kStackSharedHCopies * (kStackMaxI / 2);
 constexpr size_t kStackRoutedHWords = (size_t)2 * 8 * kStackRoutedHCopies * (kStackMaxI / 2);
-constexpr size_t kStackPartWords = (size_t)2 * kStackSlots * kStackMaxH;
 constexpr size_t kStackXPubWords = (size_t)2 * kStackXCopies * kStackXWords;
 constexpr size_t kStackRegionBytes =
-    8 * (kStackLogitWords + kStackSharedHWords + kStackRoutedHWords + kStackPartWords + kStackXPubWords);
+    8 * (kStackLogitWords + kStackSharedHWords + kStackRoutedHWords + kStackXPubWords);
 // every region at fixed offsets at the start of the workspace
 constexpr size_t kFixedRegionBytes = kDecodeRegionBytes + kStackRegionBytes;
 
@@ -224,7 +222,6 @@ struct StackArgs {
     unsigned long long* logits;  // [kStackLogitCopies][256] {epoch, logit}
     unsigned long long* sh_h;    // [kStackSharedHCopies][kStackMaxI / 2] {epoch, float16 pair}
     unsigned long long* rt_h;    // [8 slots][kStackRoutedHCopies][kStackMaxI / 2] {epoch, float16 pair}
-    unsigned long long* part;    // [kStackSlots][kStackMaxH] {epoch, float32 contribution}
     unsigned long long* xpub;    // [kStackXCopies][kStackXWords] {16-bit tag, 3 bf16}
 };
 

@@ -579,8 +579,7 @@ moe_status moe_decode_stack(const moe_dims* d, const moe_weights* wts, const uin
     a.logits = sw;
     a.sh_h = sw + kStackLogitWords;
     a.rt_h = a.sh_h + kStackSharedHWords;
-    a.part = a.rt_h + kStackRoutedHWords;
-    a.xpub = a.part + kStackPartWords;
+    a.xpub = a.rt_h + kStackRoutedHWords;
     HIP_TRY(launch_decode_stack(a, d->sb_dtype == MOE_BF16, stream));
     return MOE_OK;
 }

@@ -51,7 +51,9 @@ def test_workspace_size(lib):
     n = bem.moe_workspace_size(d)
     # float16 activations, h rows and expert output rows (routed + shared) dominate
     big = 4096 * 2048 * 2 + (4096 * 8 + 4096) * 512 * 2 + (4096 * 8 + 4096) * 2048 * 2
-    assert big <= n < big + (8 << 20)
+    # plus the small regions: routing, tile maps, logit partials and the fixed
+    # decode and stack exchange regions (about 2 MB)
+    assert big <= n < big + (12 << 20)
     assert bem.moe_workspace_size(qwen_dims(1)) > 0
     assert bem.moe_workspace_size(qwen_dims(0)) > 0
     assert bem.moe_workspace_size(qwen_dims(4096)) > bem.moe_workspace_size(qwen_dims(512))
