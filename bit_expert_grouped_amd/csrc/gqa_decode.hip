@@ -35,13 +35,21 @@
 //     the partials of all runs, o_total = sum_s 2^(m_s - M) o_s over l_total
 //     likewise, spread over ~B * Hq * D / 8 waves so that the merge is not bound
 //     by one compute unit's bandwidth.  When the whole grid fits on the device
-//     at once, the merge runs in the same launch: each workgroup counts itself
-//     in on its (sequence, KV head)'s arrival counter after storing its
-//     partial; the last to arrive resets the counter and raises the call's
-//     epoch in 16 copies of a flag (so that no cache line has more than ~8
-//     readers); the others wait (bounded) for their copy, and every workgroup
-//     then merges its share of the head's outputs.  Otherwise a second kernel
-//     (gqa_merge_kernel) merges.
+//     at once, the merge runs in the same launch.  Each workgroup stores its
+//     partial with agent-scope stores, which write through the per-XCD L2, in
+//     the order the merge reads it (per output item: 8 values, then the head's
+//     m and l, 48 bytes), waits for the stores to be acknowledged and raises
+//     the run's ready flag (its own cache line) to this call's epoch.  It then
+//     merges its share of the head's outputs: it polls (bounded) only the
+//     flags of every run, then reads each run's 48 bytes with three plain
+//     16-byte loads.  No cache holds a line of a partial before its flag is up
+//     (the kernel boundary drops what the previous call left), so plain loads
+//     after the flag see the data.  Polling one word per run instead of every
+//     value cut the merge from ~4 us to ~1 us.  The epoch is one more than a
+//     per-(sequence, KV head) word that every workgroup reads when it starts;
+//     the first run's workgroup raises it after its merge, when every run's
+//     flag (so every workgroup's read of it) is in.  Otherwise a second kernel
+//     (gqa_merge_kernel) merges plain partials.
 //
 // Rows past a sequence's length are never read: their loads are clamped to the
 // last valid row (whose values are finite) and their scores set to -inf.
@@ -58,10 +66,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr long kSpinLimit = 1l << 20;  // bound of the fused merge's wait (s_sleep rounds)
-constexpr int kFlagCopies = 16;         // copies of the merge's completion flag
-constexpr int kCtlWords = 64 + 32 * kFlagCopies;  // control words per (sequence, KV head)
-static_assert(kCtlWords * 4 <= 4096, "control block of a (sequence, KV head)");
+constexpr long kSpinLimit = 1l << 20;  // bound of the fused merge's polls (s_sleep rounds)
+constexpr int kCtlWords = 64;           // control words per (sequence, KV head): the epoch, its own line
 
 // rows per wave: D <= 128 keeps 64 rows (16 KB of K and 16 KB of V per wave in
 // flight); D = 256 keeps 32
@@ -77,69 +83,78 @@ __device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m); }
 
-// Partials that another workgroup of the same launch merges go through
-// agent-scope stores and loads, which pass the per-XCD L2 (written through on
-// store, missed on load), so no L2 write-back or invalidation is needed; with
-// the merge in a second kernel, plain accesses do.
-template <bool kCoherent>
-__device__ __forceinline__ void put_f(float* p, float v) {
-    if (kCoherent)
-        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-        *p = v;
+__device__ __forceinline__ unsigned long long peek(const unsigned long long* p) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool kCoherent>
-__device__ __forceinline__ float get_f(const float* p) {
-    if (kCoherent) return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return *p;
-}
+// Bytes of one run's partial in the fused layout: a 128-byte line for the
+// ready flag, then per output item (query head hh, 8 columns) 8 values, m and
+// l of head hh and 2 words of padding (48 bytes).
+__host__ __device__ constexpr size_t fused_part_bytes(int G, int D) { return 128 + (size_t)G * (D / 8) * 48; }
 
-// two consecutive floats (8-byte aligned)
-template <bool kCoherent>
-__device__ __forceinline__ void put_f2(float* p, float x, float y) {
-    const unsigned long long w = ((unsigned long long)__float_as_uint(y) << 32) | __float_as_uint(x);
-    if (kCoherent)
-        __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-        *reinterpret_cast<unsigned long long*>(p) = w;
-}
-
-template <bool kCoherent>
-__device__ __forceinline__ float2 get_f2(const float* p) {
-    unsigned long long w;
-    if (kCoherent)
-        w = __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-    else
-        w = *reinterpret_cast<const unsigned long long*>(p);
-    return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
+// two float32 values with one agent-scope (L2 write-through) store
+__device__ __forceinline__ void put2_wt(char* p, float x, float y) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                       ((unsigned long long)__float_as_uint(y) << 32) | __float_as_uint(x), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One wave merges output columns [8 chunk, 8 chunk + 8) of query head h of
 // sequence b over its ns partials.  Each lane takes two runs per round and
 // issues both runs' loads before any arithmetic (clamped indices, unused runs
 // weighted 0), keeping a running (max, sum, output) rescaled as it goes; the
-// lanes are combined at the end.
-template <int D, bool kCoherent>
-__device__ void merge_item(const GqaArgs& a, int b, int h, int chunk, int ns, int lane) {
+// lanes are combined at the end.  Tagged partials are polled until every word
+// the wave needs carries `tag` (bounded: on timeout the error word is set).
+template <int D, bool kTagged>
+__device__ void merge_item(const GqaArgs& a, int b, int h, int chunk, int ns, int lane, unsigned tag) {
     const int G = a.G, g = h / G, hh = h % G;
-    const size_t stride = (size_t)(G * D + 32);
-    const float* base = a.part + ((size_t)b * a.Hkv + g) * a.n_split * stride;
+    const size_t stride = (size_t)(G * D + 32);  // values per partial
+    const size_t base_i = ((size_t)b * a.Hkv + g) * a.n_split * stride;
     float M = -INFINITY, L = 0.0f;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int s0 = 0; s0 < ns; s0 += 2 * kWave) {
         float mr[2], lr[2], ov[2][8];
+        if (kTagged) {
+            // the flags of this round's runs, then their items' 48 bytes
+            const char* blk0 = reinterpret_cast<const char*>(a.part) +
+                               ((size_t)b * a.Hkv + g) * a.n_split * fused_part_bytes(G, D);
+            for (long spins = 0;; spins++) {
+                bool have = true;
 #pragma unroll
-        for (int r = 0; r < 2; r++) {
-            const float* p = base + (size_t)min(s0 + r * kWave + lane, ns - 1) * stride;
-            mr[r] = get_f<kCoherent>(p + G * D + hh);
-            lr[r] = get_f<kCoherent>(p + G * D + 16 + hh);
+                for (int r = 0; r < 2; r++) {
+                    const unsigned* f = reinterpret_cast<const unsigned*>(
+                        blk0 + (size_t)min(s0 + r * kWave + lane, ns - 1) * fused_part_bytes(G, D));
+                    have = have && __hip_atomic_load(const_cast<unsigned*>(f), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) == tag;
+                }
+                if (__ballot(!have) == 0) break;
+                if (spins > kSpinLimit) {
+                    if (lane == 0) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            const int item = hh * (D / 8) + chunk;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float2 v = get_f2<kCoherent>(p + hh * D + 8 * chunk + 2 * i);
-                ov[r][2 * i] = v.x;
-                ov[r][2 * i + 1] = v.y;
+            for (int r = 0; r < 2; r++) {
+                const float4* q = reinterpret_cast<const float4*>(
+                    blk0 + (size_t)min(s0 + r * kWave + lane, ns - 1) * fused_part_bytes(G, D) + 128 + item * 48);
+                const float4 o0 = q[0], o1 = q[1], ml = q[2];
+                ov[r][0] = o0.x, ov[r][1] = o0.y, ov[r][2] = o0.z, ov[r][3] = o0.w;
+                ov[r][4] = o1.x, ov[r][5] = o1.y, ov[r][6] = o1.z, ov[r][7] = o1.w;
+                mr[r] = ml.x;
+                lr[r] = ml.y;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 2; r++) {
+                const float* p = a.part + base_i + (size_t)min(s0 + r * kWave + lane, ns - 1) * stride;
+                mr[r] = p[G * D + hh];
+                lr[r] = p[G * D + 16 + hh];
+                const float4 o0 = *reinterpret_cast<const float4*>(p + hh * D + 8 * chunk);
+                const float4 o1 = *reinterpret_cast<const float4*>(p + hh * D + 8 * chunk + 4);
+                ov[r][0] = o0.x, ov[r][1] = o0.y, ov[r][2] = o0.z, ov[r][3] = o0.w;
+                ov[r][4] = o1.x, ov[r][5] = o1.y, ov[r][6] = o1.z, ov[r][7] = o1.w;
             }
         }
 #pragma unroll
@@ -191,6 +206,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
     static_assert(kVtElems * 2 >= kWaves * 16 * D * 4, "the merge buffer must fit in the V region");
     __shared__ __align__(16) uint16_t vt[kVtElems];
     __shared__ float red_m[kWaves][16], red_l[kWaves][16];
+    __shared__ unsigned epoch_sh;
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -206,10 +222,9 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
         return;
     }
     const int wrow0 = row0 + wave * RW;
-    // the merge's control words: arrival counter, epoch, 16 flag copies, one line each
+    // the merge's epoch word of this (sequence, KV head)
     unsigned* ctl = a.cnt + ((size_t)b * a.Hkv + g) * kCtlWords;
-    unsigned epoch = 0;
-    if (kFused && threadIdx.x == 0) epoch = __hip_atomic_load(ctl + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (kFused && threadIdx.x == 0) epoch_sh = __hip_atomic_load(ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const size_t head_base = ((size_t)b * a.Hkv + g) * (size_t)a.S_max * D;
     const uint16_t* kb = a.k + head_base;
     const uint16_t* vb = a.v + head_base;
@@ -282,8 +297,17 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
     l += shfl_xor_f(l, 16);
     l += shfl_xor_f(l, 32);
 
-    // ---- V transposed into this wave's LDS region: vt[d][j], 4 rows per 8 bytes
+    // ---- V transposed into this wave's LDS region (vt[d][j], 4 rows per 8
+    // bytes) and O = P V (16 heads x 16 columns per block, 16 rows per step),
+    // a group of columns at a time: item t covers columns [32 t, 32 t + 32) of
+    // every row, so the products of those columns run as soon as it is written
+    // and V's later loads land meanwhile.  The region is this wave's alone and
+    // a wave's LDS accesses complete in order, so no barrier is needed.
+    static_assert((8 * kWave / NQ) % 16 == 0 && NI * (8 * kWave / NQ) == D, "items cover whole column blocks");
     uint16_t* myvt = vt + (size_t)wave * D * VTS;
+    floatx4 oacc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; db++) oacc[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < NI; t++) {
         const int it = lane + kWave * t, rq = it % NQ, c = it / NQ;
@@ -298,21 +322,18 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
             *reinterpret_cast<uint2*>(myvt + (8 * c + 2 * w) * VTS + 4 * rq) = lo;
             *reinterpret_cast<uint2*>(myvt + (8 * c + 2 * w + 1) * VTS + 4 * rq) = hi;
         }
+        asm volatile("" ::: "memory");  // the reads below after this wave's writes
+        // item t wrote columns [8 (kWave t / NQ), 8 (kWave (t + 1) / NQ))
+        constexpr int kColsPerItem = 8 * kWave / NQ;
+#pragma unroll
+        for (int db = t * kColsPerItem / 16; db < (t + 1) * kColsPerItem / 16; db++)
+#pragma unroll
+            for (int rb = 0; rb < NB; rb++) {
+                const uint2 v4 = *reinterpret_cast<const uint2*>(myvt + (16 * db + li) * VTS + 16 * rb + 4 * lg);
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop[rb], __builtin_bit_cast(short4_t, v4),
+                                                                     oacc[db], 0, 0, 0);
+            }
     }
-    __syncthreads();
-
-    // ---- O = P V: 16 heads x 16 columns per block, 16 rows per step
-    floatx4 oacc[ND];
-#pragma unroll
-    for (int db = 0; db < ND; db++) oacc[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int rb = 0; rb < NB; rb++)
-#pragma unroll
-        for (int db = 0; db < ND; db++) {
-            const uint2 v4 = *reinterpret_cast<const uint2*>(myvt + (16 * db + li) * VTS + 16 * rb + 4 * lg);
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop[rb], __builtin_bit_cast(short4_t, v4),
-                                                                 oacc[db], 0, 0, 0);
-        }
     // lane (li, lg) holds heads 4 lg + i at column 16 db + li
 
     // ---- merge the 4 waves in LDS and store the workgroup's partial
@@ -327,7 +348,9 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; i++) ob[((size_t)wave * 16 + 4 * lg + i) * D + 16 * db + li] = oacc[db][i];
     __syncthreads();
-    float* part = a.part + (((size_t)b * a.Hkv + g) * a.n_split + split) * (size_t)(G * D + 32);
+    const size_t part_i = (((size_t)b * a.Hkv + g) * a.n_split + split) * (size_t)(G * D + 32);
+    char* fblk = reinterpret_cast<char*>(a.part) + (((size_t)b * a.Hkv + g) * a.n_split + split) * fused_part_bytes(G, D);
+    const unsigned tag = kFused ? epoch_sh + 1u : 0u;  // read after the barriers above
     for (int e = 2 * threadIdx.x; e < G * D; e += 2 * kThreads) {
         const int hh = e / D, d = e % D;
         float M = -INFINITY;
@@ -340,7 +363,20 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
             o0 += sc * ob[((size_t)w * 16 + hh) * D + d];
             o1 += sc * ob[((size_t)w * 16 + hh) * D + d + 1];
         }
-        put_f2<kFused>(part + e, o0, o1);
+        if (kFused) {
+            char* it = fblk + 128 + (size_t)(hh * (D / 8) + d / 8) * 48;
+            put2_wt(it + (d % 8) * 4, o0, o1);
+            if (d % 8 == 0) {  // the head's m and l beside each of its items
+                float L = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; w++)
+                    L += (red_m[w][hh] == -INFINITY ? 0.0f : exp2f(red_m[w][hh] - M)) * red_l[w][hh];
+                put2_wt(it + 32, M, L);
+            }
+        } else {
+            a.part[part_i + e] = o0;
+            a.part[part_i + e + 1] = o1;
+        }
     }
     if (threadIdx.x < G) {
         const int hh = threadIdx.x;
@@ -351,39 +387,28 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(GqaArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; w++)
             L += (red_m[w][hh] == -INFINITY ? 0.0f : exp2f(red_m[w][hh] - M)) * red_l[w][hh];
-        put_f<kFused>(part + G * D + hh, M);
-        put_f<kFused>(part + G * D + 16 + hh, L);
-    }
-    if (!kFused) return;
-
-    // ---- the merge in this launch: wait for every run of this (sequence, KV head)
-    const int ns = (n + kWaves * RW - 1) / (kWaves * RW);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores acknowledged (written through)
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned next = epoch + 1u;
-        if (atomicAdd(ctl, 1u) == (unsigned)ns - 1) {
-            // the last run of this head: reset the counter, raise the epoch
-            __hip_atomic_store(ctl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ctl + 32, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int c = 0; c < kFlagCopies; c++)
-                __hip_atomic_store(ctl + 64 + 32 * c, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            unsigned* flag = ctl + 64 + 32 * (split % kFlagCopies);
-            for (long spins = 0; __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != next;
-                 spins++) {
-                if (spins > kSpinLimit) {
-                    __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
+        if (!kFused) {
+            a.part[part_i + G * D + hh] = M;
+            a.part[part_i + G * D + 16 + hh] = L;
         }
     }
+    if (!kFused) return;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores acknowledged (written through)
     __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(reinterpret_cast<unsigned*>(fblk), tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // ---- the merge in this launch: poll the flags of every run of this
+    // (sequence, KV head), read their items; the first run's workgroup then
+    // raises the epoch
+    const int ns = (n + kWaves * RW - 1) / (kWaves * RW);
     const int items = G * (D / 8);
     for (int it = split + ns * wave; it < items; it += ns * kWaves)
-        merge_item<D, true>(a, b, g * G + it / (D / 8), it % (D / 8), ns, lane);
+        merge_item<D, true>(a, b, g * G + it / (D / 8), it % (D / 8), ns, lane, tag);
+    if (split == 0) {
+        __syncthreads();  // every item of this workgroup merged: every run's partial was in
+        if (threadIdx.x == 0) __hip_atomic_store(ctl, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // One wave per (sequence, query head, 8 output columns): merge the partials of
@@ -399,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(GqaArgs a) {
     const int h = (int)((item / (D / 8)) % a.Hq);
     const int b = (int)(item / ((long)(D / 8) * a.Hq));
     const int n = min(max(a.seq_len[b], 0), a.S_max);
-    merge_item<D, false>(a, b, h, chunk, (n + RWG - 1) / RWG, lane);
+    merge_item<D, false>(a, b, h, chunk, (n + RWG - 1) / RWG, lane, 0u);
 }
 
 template <int D>

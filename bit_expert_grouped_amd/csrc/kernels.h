@@ -257,9 +257,9 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 // seq_len [B]; part: B * Hkv * n_split partials of G * D + 32 floats (o [G][D],
 // then m and l, 16 slots each); out [B][Hq][D] float32.  c = scale * log2(e).
 // With fused set (every workgroup of the grid resident at once), one kernel
-// also merges: cnt holds 1024 control words per (sequence, KV head) (arrival
-// counter, epoch, flag copies; zero before the first call); err is set if a
-// wait timed out.
+// also merges: part then holds {epoch, float32} words, cnt 64 control words
+// per (sequence, KV head) (word 0: the epoch; zero before the first call);
+// err is set if a poll timed out.
 struct GqaArgs {
     const uint16_t* q;
     const uint16_t* k;

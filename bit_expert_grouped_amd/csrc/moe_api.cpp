@@ -688,17 +688,19 @@ int gqa_splits(const moe_gqa_dims* d) {
     return (d->max_seq + r - 1) / r;
 }
 
-// workspace: the partials, then 4 KiB of control words per (sequence, KV
-// head) (arrival counter, epoch and flag copies of the fused merge), then the
+// workspace: the partials (the fused merge's layout, 128 + 6 G D bytes per
+// run: a flag line, then 48 bytes per 8-column item; the second kernel's plain
+// float32 layout, 4 G D + 128 bytes per run, fits in it), then 256 bytes of
+// control words per (sequence, KV head) (the fused merge's epoch), then the
 // timeout word
 size_t gqa_part_bytes(const moe_gqa_dims* d) {
     const size_t G = (size_t)(d->n_q_heads / d->n_kv_heads);
-    const size_t bytes = (size_t)d->B * d->n_kv_heads * (size_t)gqa_splits(d) * (G * d->head_dim + 32) * 4;
+    const size_t bytes = (size_t)d->B * d->n_kv_heads * (size_t)gqa_splits(d) * (128 + 6 * G * d->head_dim);
     return (bytes + 255) & ~(size_t)255;
 }
 
 size_t gqa_ws_bytes(const moe_gqa_dims* d) {
-    return gqa_part_bytes(d) + (size_t)d->B * d->n_kv_heads * 4096 + 256;
+    return gqa_part_bytes(d) + (size_t)d->B * d->n_kv_heads * 256 + 256;
 }
 
 // workgroups of the fused attention kernel the current device holds at once
@@ -746,7 +748,7 @@ moe_status gqa_impl(const moe_gqa_dims* d, const uint16_t* q, const uint16_t* k_
     a.seq_len = seq_len;
     a.part = static_cast<float*>(ws);
     a.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + gqa_part_bytes(d));
-    a.err = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + gqa_part_bytes(d) + (size_t)d->B * d->n_kv_heads * 4096);
+    a.err = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + gqa_part_bytes(d) + (size_t)d->B * d->n_kv_heads * 256);
     a.out = out;
     a.B = d->B;
     a.Hq = d->n_q_heads;

@@ -371,8 +371,9 @@ typedef struct {
 
 /* Bytes of device workspace moe_gqa_decode needs (host-only, pure; 0 when the
  * dims are invalid): B * n_kv_heads * ceil(max_seq / R) partials of
- * (G * head_dim + 32) floats (R = 256 rows, 128 at head_dim 256), rounded up
- * to 256 bytes, then 4 KiB of control words per (sequence, KV head), then 256
+ * 128 + 6 * G * head_dim bytes (R = 256 rows, 128 at head_dim 256), rounded
+ * up to 256 bytes, then 256 bytes of control words per (sequence, KV head),
+ * then 256
  * bytes whose first word is set to nonzero, and stays so, if a device-side
  * wait of a call timed out (that call's output is then invalid).  Zero-fill it
  * once after allocating it; every call leaves it ready for the next, for any

@@ -249,13 +249,13 @@ def test_gqa_workspace_and_checks(lib):
     """moe_gqa_workspace_size and moe_gqa_decode's host-side checks."""
     d = bem.gqa_dims(1, 16, 2, 128, 32768)
     n = lib.moe_gqa_workspace_size(C.byref(d))
-    # 128 runs of 256 rows per KV head, each partial 8 heads x 128 columns + 32 floats;
-    # 4 KiB of control words per (sequence, KV head); 256 bytes for the timeout word
-    assert n == 2 * 128 * (8 * 128 + 32) * 4 + 2 * 4096 + 256
+    # 128 runs of 256 rows per KV head, each partial a 128-byte flag line and 6 bytes per
+    # (head, column); 256 bytes of control words per (sequence, KV head); 256 for the timeout word
+    assert n == 2 * 128 * (128 + 6 * 8 * 128) + 2 * 256 + 256
     assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(1, 16, 2, 256, 32768))) == \
-        2 * 256 * (8 * 256 + 32) * 4 + 2 * 4096 + 256
+        2 * 256 * (128 + 6 * 8 * 256) + 2 * 256 + 256
     assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(3, 16, 2, 128, 100))) == \
-        3 * 2 * 1 * (8 * 128 + 32) * 4 + 6 * 4096 + 256
+        (3 * 2 * 1 * (128 + 6 * 8 * 128) + 255) // 256 * 256 + 6 * 256 + 256
     assert lib.moe_gqa_workspace_size(C.byref(bem.gqa_dims(1, 16, 3, 128, 10))) == 0
 
     def call(dims, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, scale=0.088, out=FAKE, ws=FAKE, ws_bytes=n):

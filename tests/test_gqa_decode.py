@@ -165,3 +165,45 @@ def test_gqa_events_variant_matches():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert ev[0].elapsed_time(ev[1]) > 0 and ev[1].elapsed_time(ev[2]) > 0
+
+
+def test_gqa_back_to_back_calls_share_a_workspace():
+    """Four calls on different caches, one workspace, launched back to back with
+    no host sync between them (then replayed as a graph): each output matches
+    its own oracle, so nothing a call leaves in the workspace or in a cache is
+    read by the next."""
+    shape = moe_synth.AttnShape(B=1, Hq=16, Hkv=2, D=128, S=8192)
+    m = bem()
+    d = m.gqa_dims(1, 16, 2, 128, 8192)
+    ws = m.gqa_workspace(d)
+    lens = np.array([8192 - 300 * i for i in range(4)], dtype=np.int32)
+    cases = []
+    for i in range(4):
+        q, k, v = moe_synth.attn_inputs(shape, 70 + i)
+        ref = oracle.gqa_decode(q, k, v, lens[i:i + 1])
+        cases.append((_dev(q), _dev(k), _dev(v), torch.from_numpy(lens[i:i + 1]).cuda(), ref, v))
+    outs = [torch.empty(1, 16, 128, dtype=torch.float32, device="cuda") for _ in range(4)]
+    for (tq, tk, tv, tl, _, _), o in zip(cases, outs):
+        m.gqa_decode(tq, tk, tv, tl, out=o, ws=ws)
+    torch.cuda.synchronize()
+    assert not m.gqa_timed_out(ws, d)
+    for (_, _, _, _, ref, v), o, i in zip(cases, outs, range(4)):
+        check(o.cpu().numpy(), ref, v, lens[i:i + 1], 8, "back to back call %d" % i)
+    eager = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for (tq, tk, tv, tl, _, _), o in zip(cases, outs):
+                m.gqa_decode(tq, tk, tv, tl, out=o, ws=ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e)
+    assert not m.gqa_timed_out(ws, d)
