@@ -11,51 +11,56 @@
 // the same job"); routing stays on the GPU (same section; dzen.guru page,
 // section "Where does the speed-up come from?").
 //
-// What one layer needs at T = 1 is a chain: x -> its normalisation -> router logits -> top-k ->
-// the k experts' gate/up -> their down -> x of the next layer.  Only the k
-// routed experts' weights (14 MB at the Qwen shapes) depend on the data; the
-// router (1 MiB) and the shared expert (1.8 MB) do not, so they are read ahead
-// of the layer that uses them.  The kernel keeps every hand-over inside one
-// launch and takes as few of them as the chain allows:
+// What one layer needs at T = 1 is a chain: x -> its normalisation -> router
+// logits -> top-k -> the k experts' gate/up -> their down -> x of the next
+// layer.  Only the k routed experts' weights (14 MB at the Qwen shapes) depend
+// on the data; the router (1 MiB) and the shared expert (1.8 MB) do not, so
+// they are read ahead of the layer that uses them.  Each link of the chain is a
+// hand-over between workgroups, and its cost is a round trip to wherever the
+// two workgroups share memory: the L2 of their XCD (~0.4 us for an all-gather
+// among an XCD's 32 workgroups), or, across XCDs, the memory side of the
+// fabric (~1-2 us).  So the layer is laid out along the device's XCDs:
 //
 //   - the grid is kStackGrid workgroups of 8 waves, one per compute unit, all
 //     resident at once (the host checks the device can hold them), and every
-//     wait is bounded;
-//   - router: workgroup w scores expert w and publishes its logit ({epoch,
-//     logit} words, kStackLogitCopies copies); every workgroup then reads all
-//     E logits and selects the top k itself, so the routing costs one
-//     hand-over, not two.  Each of four waves holds 64 order keys; their two
-//     largest give at least 8 keys at or above the smallest of the four
-//     second-largest, so the top k (k <= 8) are among the keys at or above it.
-//     Those few candidates are ranked by counting (ties to the lower expert
-//     index); a radix search over all keys serves the rare case of more than
-//     64 candidates or of under two experts per wave;
-//   - gate/up: workgroup w takes 16 rows of the intermediate dim of one routed
-//     slot (2 rows per wave, gate and up) and publishes h as float16 pairs; the
-//     shared expert's gate/up (2 rows per workgroup) runs on weights read ahead;
-//   - down and output: workgroup w owns output columns [8 w, 8 w + 8) and
-//     computes them for every slot: wave j the 8 rows of routed slot j (one
-//     64-column group per lane), waves 4-7 the 8 rows of the shared expert.
-//     Every workgroup therefore reads every slot's h (each gate/up unit
-//     publishes its h in kStackRoutedHCopies copies).  The k + 1
-//     contributions of a column are summed in LDS in slot order (so the output
-//     is the same bit for bit on every call) and the workgroup forms the next
-//     layer's stream x(l+1) = bf16(x(l) + sum) for its columns and publishes
-//     it packed ({16-bit tag, 3 bf16} words) in kStackXCopies copies; every
-//     workgroup then reads the whole stream from its copy.  Broadcasting a few
-//     KB to 256 workgroups costs what its most-read cache line costs, so every
-//     value all workgroups read is replicated until each copy has ~8 readers.
+//     wait is bounded.  Each workgroup reads the id of the XCD it runs on from
+//     the hardware and takes an index j among that XCD's 32 workgroups;
+//   - every XCD carries the layer up to the routed experts on its own: its 32
+//     workgroups score all E experts (workgroup j experts 8 j .. 8 j + 7, from
+//     router rows read ahead), read all E logits from their XCD's L2, and each
+//     selects the top k itself.  The XCDs compute the same logits with the same
+//     arithmetic, so they select the same experts;
+//   - XCD x computes routed slot x (k <= 8 slots for 8 XCDs): workgroup j the
+//     16 intermediate rows [16 j, 16 j + 16) of the slot's gate/up, published
+//     in the XCD's L2; then every workgroup reads the slot's whole h and
+//     computes its 64 owned output columns [64 j, 64 j + 64) of the slot's
+//     down.  The shared expert is cut along its intermediate dimension: XCD x
+//     takes rows [x I_s / 8, (x + 1) I_s / 8), gate/up and the matching slice of
+//     down, so every XCD adds one eighth of it;
+//   - the one hand-over across XCDs: workgroup j of XCD x publishes its partial
+//     sum p_x = w_x y_x + y_shared,x for its 64 columns, and reads the 8 XCDs'
+//     partials of the same columns.  Every XCD adds them in XCD order, so the
+//     next stream x(l+1) = bf16(x(l) + sum_x p_x) is the same bits in every XCD,
+//     and each XCD gathers it from its own L2;
+//   - values handed within an XCD are stored with workgroup-scope stores, which
+//     pass through the compute unit's write-through L1 into the XCD's L2, and
+//     read with agent-scope loads, which miss the L1 and are served by the L2
+//     line the store wrote (lines no other XCD touches).  Values crossing XCDs
+//     are stored and read with agent-scope accesses, which write through to and
+//     read from the memory side.  Each value carries its epoch, so a reader
+//     waits for the value itself, with no flags or counters;
 //   - every exchange region is kept twice, by the parity of the layer's epoch:
-//     a workgroup can run at most one layer ahead of the slowest (each layer's
-//     logits come from all of them), so a word is never rewritten while a
+//     a workgroup can run at most one layer ahead of any other (each layer's
+//     logits come from all 32 workgroups of its XCD, and its output from the
+//     same workgroup index in all 8 XCDs), so a word is never rewritten while a
 //     reader may still wait for its previous value.
 //
 // Loads of one wave complete in order (the vmcnt counter), so a poll waits
-// behind every load its wave issued before.  Each wave therefore issues the
-// next layer's read-ahead (router row, shared expert slices, logit bias, into
-// registers) only after the last poll of the layer, and polls follow the loads
-// whose data they must wait for anyway.
-//
+// behind every load its wave issued before.  Waves 0-3 do every poll but one
+// (the shared expert's h, polled by wave 6 long after its read-ahead landed);
+// waves 4-7 hold the read-ahead (router rows, the shared expert's slices, the
+// logit bias and the normalisation weight, in registers) and issue the next
+// layer's as soon as their gate/up products are done.
 #include "common.h"
 #include "decode_common.h"
 #include "kernels.h"
@@ -68,15 +73,21 @@ using namespace dec;
 
 constexpr int kWorkers = 8;
 constexpr int kThreads = kWorkers * kWave;
-constexpr int kGURows = 16;  // intermediate rows of a routed gate/up unit: 2 per wave
+constexpr int kXcds = kStackXcds;
+constexpr int kPerXcd = kStackGrid / kStackXcds;  // workgroups per XCD
+constexpr int kGURows = 16;                       // routed gate/up rows of a workgroup: 2 per wave
+constexpr int kOwn = 64;                          // output columns a workgroup owns: 8 per wave
+constexpr int kLogitsPerWg = 8;                   // experts a workgroup scores: 2 per holding wave
 constexpr long kSpinLimit = 1l << 20;
-constexpr int kHWords = kStackMaxI / 2;  // h words per slot (float16 pairs)
-constexpr int kPollThreads = kStackMaxH / 8;  // threads that poll the output, one 8-column block each
+constexpr int kPollThreads = kStackMaxH / 8;  // threads that poll the stream, one 8-column block each
+constexpr int kCopies = kStackLocalCopies;
+constexpr int kRankCands = 32;  // candidates ranked in parallel (8 threads each); more take a radix search
 
 // control words (uint32 indices) of the stack kernel inside the decode control block
-constexpr int kCtlStEpoch = 2048;         // epoch of the last layer of the last call
-constexpr int kCtlStDone = 2048 + 64;     // groups of workgroups finished in this call
+constexpr int kCtlStEpoch = 2048;            // epoch of the last layer of the last call
+constexpr int kCtlStDone = 2048 + 64;        // groups of workgroups finished in this call
 constexpr int kCtlStGroupDone = 2048 + 128;  // + 32 g: workgroups of group g finished
+constexpr int kCtlStClaim = 2048 + 512;      // + 32 x: workgroups that ever started on XCD x
 constexpr int kDoneGroups = 8;
 
 constexpr float kNormEps = 1e-6f;  // epsilon of the stream's normalisation
@@ -87,35 +98,27 @@ struct StackShared {
     uint16_t xb[kStackMaxH];     // the residual stream entering the layer, bf16
     uint16_t xn[kStackMaxH];     // its normalisation, the layer's input, bf16
     float ssq[4];                // sums of squares of the stream, one per polling wave
-    uint4 hsp[kStackMaxI / 8];   // shared expert's h, pairs per 8 columns
-    float2 hss[kStackMaxI / 8];
-    uint4 hrp[8][kStackMaxI / 8];  // routed h of every slot, pairs per 8 columns
-    float2 hrs[8][kStackMaxI / 8];
-    float ycon[8 + 1][8];        // contributions to the owned columns: routed slots, then the shared expert
+    uint4 hsp[kStackMaxI / 64];  // the XCD's share of the shared expert's h, pairs per 8 values
+    float2 hss[kStackMaxI / 64];
+    uint4 hrp[kStackMaxI / 8];   // the XCD's routed slot's h, pairs per 8 values
+    float2 hrs[kStackMaxI / 8];
+    float yr[kOwn];              // the routed slot's rows of the owned columns
+    float ysh[kOwn];             // the shared expert's share of the same rows
+    float pp[kXcds][kOwn];       // every XCD's partial sums of the owned columns
     uint32_t keys[kMaxE];        // order keys of the logits
     uint32_t tkey[kMaxTopK];     // the selected keys, in expert order
     int tidx[kMaxTopK];
-    float red[kWorkers];         // router partial sums, one per wave
-    float sred[kWorkers];        // shared gate/up partial sums, two waves per row
+    float sred[4];               // shared gate/up rows of this workgroup (gate 2j, 2j+1, up 2j, 2j+1)
     int sel_e[kMaxTopK];         // the top k in rank order
     uint32_t sel_key[kMaxTopK];
     float sel_w[kMaxTopK];
     uint32_t m2[4];              // second largest key of each wave's 64
-    int ncand;                   // candidates of the top k (keys >= min of m2)
-    uint32_t ckey[kWave];
-    int cidx[kWave];
-    int last;
+    uint32_t ckey[4][kWave];     // candidates of the top k (keys >= min of m2), per polling wave
+    int cidx[4][kWave];
+    int ccnt[4];
+    uint4 gam[kStackMaxH / 8];   // the layer's normalisation weight, per 8 columns
+    unsigned xcd, idx;           // this workgroup's XCD and its index there
 };
-
-template <typename T>
-__device__ __forceinline__ const T* layer_ptr(const T* p, int64_t stride, int l) {
-    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + stride * (int64_t)l);
-}
-
-template <typename SB>
-__device__ __forceinline__ const SB* sb_ptr(const void* p, int64_t stride, int l) {
-    return reinterpret_cast<const SB*>(reinterpret_cast<const char*>(p) + stride * (int64_t)l);
-}
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -124,6 +127,26 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 // tag of the stream words of epoch ep: 16 bits, never 0 (a zero-filled workspace's)
 __device__ __forceinline__ unsigned xtag(unsigned ep) { return ep % 65535u + 1u; }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// c + a.lo b.lo + a.hi b.hi over bf16 pairs (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// the XCD this wave runs on (hardware register)
+__device__ __forceinline__ unsigned xcc_id() {
+    unsigned v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return v & 0xFu;
+}
+
+// an {epoch, value} word (or a tagged stream word) for the workgroups of this
+// XCD: a workgroup-scope store, through the write-through L1 into the XCD's L2
+__device__ __forceinline__ void put_local(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 // 8 values of one 8-column block -> float16 pairs in nibble order and their
 // low/high nibble sums (taken over the float16 values the products use)
@@ -185,20 +208,35 @@ __device__ bool poll_h(const unsigned long long* src, int n_words, unsigned epoc
     return ok;
 }
 
+// Sum over the wave, as a wave-uniform value: DPP butterflies inside each row of
+// 16 lanes, then the four row totals through readlane (no LDS round trip, as
+// the last two steps of group_sum take).
+__device__ __forceinline__ float wave_total(float v) {
+    v += dpp<0xB1>(v);   // quad_perm 1,0,3,2
+    v += dpp<0x4E>(v);   // quad_perm 2,3,0,1
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 // s * (sum of code * a over a word or words) + b * (sum of a), from the
 // exponent-trick partial sums of dot_word
 __device__ __forceinline__ float affine(float s, float b, float alo, float ahi, float lo, float hi) {
     return s * ((alo - 1024.0f * lo) + (ahi - 64.0f * hi)) + b * (lo + hi);
 }
 
-// Addressing.  Every load, poll and atomic of the loop takes a base address
-// that is uniform over the wave (kernel arguments, the layer, the expert: kept
-// in scalar registers) plus a per-lane byte offset computed once before the
-// loop.  The loop then writes no vector register that a memory operation in
-// flight still reads as its address, which would make the compiler wait for
-// that operation to complete.  Every load is issued whatever the shape
-// (indices clamped into the tensors), so that each wave's count of loads in
-// flight is the same on every path and the compiler's waits stay exact.
+// Addressing.  Every load of the loop takes a base address that is uniform over
+// the wave (kernel arguments, the layer, the expert: kept in scalar registers)
+// plus a per-lane byte offset computed once before the loop.  The loop then
+// writes no vector register that a memory operation in flight still reads as
+// its address, which would make the compiler wait for that operation to
+// complete.  Every load is issued whatever the shape (indices clamped into the
+// tensors), so that each wave's count of loads in flight is the same on every
+// path and the compiler's waits stay exact.
 __device__ __forceinline__ const char* lay(const void* p, int64_t stride, int l) {
     return reinterpret_cast<const char*>(p) + stride * (int64_t)l;
 }
@@ -209,109 +247,58 @@ __device__ __forceinline__ T ld(const char* base, uint32_t off) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Read-ahead of one layer's data-independent weights, held in the registers of
-// waves 4-7 until the layer runs.  Thread u = tid - 256 of those waves holds:
-//   router  columns [8 u, 8 u + 8) of expert w's router row, and its logit bias;
-//   sgu     columns [32 lane, 32 lane + 32) of shared gate row 2w (wave 4), 2w+1
-//           (wave 5), shared up row 2w (wave 6), 2w+1 (wave 7), with the
-//           group's scale and bias;
-//   sdn     words 2 (lane % 32), +1 of shared down row 8w + 2 (wave - 4) + lane / 32.
+// waves 4-7 until the layer runs.  Thread u = tid - 256 of those waves (lane,
+// hw = wave - 4) holds:
+//   rt      8-column blocks [4 lane, 4 lane + 4) of the router rows of experts
+//           8 j + 2 hw and 8 j + 2 hw + 1;
+//   bias    the logit bias of expert 8 j + 2 hw + lane % 2;
+//   sgu     columns [32 lane, 32 lane + 32) of the XCD's shared gate row 2 j
+//           (hw 0), 2 j + 1 (hw 1), shared up row 2 j (hw 2), 2 j + 1 (hw 3),
+//           with the group's scale and bias;
+//   sdn     words 2 (u % 4), +1 of owned column 64 j + u / 4 of the shared down
+//           rows over the XCD's intermediate slice, with its scale and bias;
+//   gam     the normalisation weight of 8-column block u.
 template <typename SB>
 struct Ahead {
-    uint4 router;
+    uint4 rt[2][4];
     float bias;
     uint4 sgu;
     SB sgu_s, sgu_b;
-    uint2 sdn;
+    uint32_t sdn0, sdn1;
     SB sdn_s, sdn_b;
+    uint4 gam;
 };
 
 struct AheadOffsets {
-    uint32_t router, bias, sgu_q, sgu_sb, sdn_q, sdn_sb;
+    uint32_t rt0, rt1, bias, sgu_q, sgu_sb, sdn_q0, sdn_q1, sdn_sb, gam;
 };
 
 template <typename SB>
 __device__ __forceinline__ void read_ahead(const StackArgs& a, int l, int hw, const AheadOffsets& o, Ahead<SB>& r) {
-    r.router = ld<uint4>(lay(a.router, a.router_stride, l), o.router);
-    if (a.logit_bias) r.bias = ld<float>(lay(a.logit_bias, a.bias_stride, l), o.bias);
-    if (a.I_shared > 0) {
-        const QMatPtr& m = hw < 2 ? a.shared.gate : a.shared.up;
-        const QMatStride& st = hw < 2 ? a.shared_stride.gate : a.shared_stride.up;
-        r.sgu = ld<uint4>(lay(m.q, st.q, l), o.sgu_q);
-        r.sgu_s = ld<SB>(lay(m.s, st.s, l), o.sgu_sb);
-        r.sgu_b = ld<SB>(lay(m.b, st.b, l), o.sgu_sb);
-        const QMatStride& sd = a.shared_stride.down;
-        r.sdn = ld<uint2>(lay(a.shared.down.q, sd.q, l), o.sdn_q);
-        r.sdn_s = ld<SB>(lay(a.shared.down.s, sd.s, l), o.sdn_sb);
-        r.sdn_b = ld<SB>(lay(a.shared.down.b, sd.b, l), o.sdn_sb);
-    }
-}
-
-// Publish the owned block of the stream of epoch ep_next (wave 0; lane c < 8
-// holds column 8 w + c in xn): the block's 8 values in every lane, packed 3 to
-// a word under the tag, in every copy.
-__device__ void publish_x(const StackArgs& a, int w, int lane, unsigned ep_next, uint16_t xn) {
-    uint32_t b[8];
+    // every load is issued on every path (an absent tensor is replaced by one
+    // that exists, its value unused), so that the waves' counts of loads in
+    // flight, and the compiler's waits on them, do not depend on the shape
+    const bool shared = a.I_shared > 0;
+    const char* rb = lay(a.router, a.router_stride, l);
 #pragma unroll
-    for (int c = 0; c < 8; c++) b[c] = (uint32_t)__shfl((int)xn, c);
-    const unsigned long long tag = (unsigned long long)xtag(ep_next) << 48;
-    const unsigned long long words[3] = {
-        tag | ((unsigned long long)b[2] << 32) | ((unsigned long long)b[1] << 16) | b[0],
-        tag | ((unsigned long long)b[5] << 32) | ((unsigned long long)b[4] << 16) | b[3],
-        tag | ((unsigned long long)b[7] << 16) | b[6]};
-    unsigned long long* dst = a.xpub + (size_t)(ep_next & 1) * kStackXCopies * kStackXWords + 3 * w;
-    for (int i = lane; i < 3 * kStackXCopies; i += kWave) {
-        const int q = i % 3, copy = i / 3;
-        const unsigned long long word = q == 0 ? words[0] : q == 1 ? words[1] : words[2];
-        if (8 * w < a.H)
-            __hip_atomic_store(dst + (size_t)copy * kStackXWords + q, word, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 4; i++) {
+        r.rt[0][i] = ld<uint4>(rb, o.rt0 + 16 * i);
+        r.rt[1][i] = ld<uint4>(rb, o.rt1 + 16 * i);
     }
-}
-
-// Poll the n_words {epoch, float16 pair} words of one slot's h (the whole wave:
-// 4 words per lane, all in flight at once) into LDS as pairs in nibble order,
-// then form the low/high sums of every block (lane b: block b).  Returns false
-// on timeout (then sets the error word).
-__device__ bool poll_slot_h(const unsigned long long* src, int n_words, unsigned epoch, uint4* pairs, float2* sums,
-                            int lane, bool failed, unsigned* ctl) {
-    constexpr int kPer = kHWords / kWave;  // words per lane
-    bool ok = true;
-    unsigned long long val[kPer] = {};
-    if (!failed) {
-        for (long spins = 0;; spins++) {
-            bool have = true;
-#pragma unroll
-            for (int t = 0; t < kPer; t++) val[t] = peek(src + min(kWave * t + lane, n_words - 1));
-#pragma unroll
-            for (int t = 0; t < kPer; t++) have = have && (unsigned)(val[t] >> 32) == epoch;
-            if (__ballot(!have) == 0) break;
-            if (spins > kSpinLimit) {
-                if (lane == 0) flag_error(ctl);
-                ok = false;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-    _Float16* hh = reinterpret_cast<_Float16*>(pairs);
-#pragma unroll
-    for (int t = 0; t < kPer; t++) {
-        const int wd = kWave * t + lane;
-        if (wd < n_words) {
-            const half2_t pr = as_half2((uint32_t)val[t]);
-            const int c0 = 2 * wd, c1 = 2 * wd + 1;
-            hh[(c0 >> 3) * 8 + slot_of_column(c0 & 7)] = pr.x;
-            hh[(c1 >> 3) * 8 + slot_of_column(c1 & 7)] = pr.y;
-        }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's values are in LDS
-    if (lane * 4 < n_words) {
-        const uint4 p = pairs[lane];
-        const half2_t a = as_half2(p.x), b = as_half2(p.y), c = as_half2(p.z), d = as_half2(p.w);
-        sums[lane] = make_float2(((float)a.x + (float)a.y) + ((float)c.x + (float)c.y),
-                                 ((float)b.x + (float)b.y) + ((float)d.x + (float)d.y));
-    }
-    return ok;
+    r.bias = a.logit_bias ? ld<float>(lay(a.logit_bias, a.bias_stride, l), o.bias) : ld<float>(rb, o.bias);
+    r.gam = a.norm_w ? ld<uint4>(lay(a.norm_w, a.norm_stride, l), o.gam) : ld<uint4>(rb, o.gam);
+    const QMatPtr& m = shared ? (hw < 2 ? a.shared.gate : a.shared.up) : a.experts.gate;
+    const QMatStride& st = shared ? (hw < 2 ? a.shared_stride.gate : a.shared_stride.up) : a.experts_stride.gate;
+    r.sgu = ld<uint4>(lay(m.q, st.q, l), o.sgu_q);
+    r.sgu_s = ld<SB>(lay(m.s, st.s, l), o.sgu_sb);
+    r.sgu_b = ld<SB>(lay(m.b, st.b, l), o.sgu_sb);
+    const QMatPtr& d = shared ? a.shared.down : a.experts.down;
+    const QMatStride& sd = shared ? a.shared_stride.down : a.experts_stride.down;
+    const char* dq = lay(d.q, sd.q, l);
+    r.sdn0 = ld<uint32_t>(dq, o.sdn_q0);
+    r.sdn1 = ld<uint32_t>(dq, o.sdn_q1);
+    r.sdn_s = ld<SB>(lay(d.s, sd.s, l), o.sdn_sb);
+    r.sdn_b = ld<SB>(lay(d.b, sd.b, l), o.sdn_sb);
 }
 
 template <typename SB>
@@ -319,10 +306,8 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
     __shared__ StackShared sh;
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = uniform(tid / kWave);
-    const int w = blockIdx.x;
     const int H = a.H, I = a.I, E = a.E, k = a.top_k, L = a.L;
     const bool shared = a.I_shared > 0;
-    const int n_slots = k + (shared ? 1 : 0);  // contributions per output column
     constexpr uint32_t kSB = sizeof(SB);
     // a plain load: stored by the previous call, which has ended
     const unsigned e0 = a.ctl[kCtlStEpoch];
@@ -330,123 +315,146 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
     const int hw = wave - 4;        // their index 0..3
     const int u = tid - 4 * kWave;  // their thread index 0..255
 
+    // this workgroup's XCD x and its index j among the XCD's workgroups (each
+    // call starts kPerXcd workgroups on every XCD, which count themselves)
+    if (tid == 0) {
+        const unsigned xc = xcc_id();
+        unsigned idx = 0;
+        if (xc < (unsigned)kXcds)
+            idx = __hip_atomic_fetch_add(a.ctl + kCtlStClaim + 32 * xc, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) % (unsigned)kPerXcd;
+        else
+            flag_error(a.ctl);
+        sh.xcd = xc;
+        sh.idx = idx;
+    }
+    __syncthreads();
+    bool failed = sh.xcd >= (unsigned)kXcds;
+    const int x = uniform((int)min(sh.xcd, (unsigned)kXcds - 1)), j = uniform((int)sh.idx);
+
     // this workgroup's units
-    const int gu_per_slot = I / kGURows;
-    const bool has_gu = w < k * gu_per_slot;
-    const int gu_slot = min(w / gu_per_slot, k - 1), gu_i0 = (w % gu_per_slot) * kGURows;
-    const bool owns = 8 * w < H;  // output columns [8 w, 8 w + 8)
-    const int own0 = min(8 * w, H - 8);
-    const bool has_sgu = shared && w < a.I_shared / 2;
-    const int nblk = H / 8;
-    const int chunks = H / 32;
-    bool failed = false;
+    const int nblk = H / 8, chunks = H / 32;
+    const int Ix = a.I_shared / kXcds;          // the XCD's share of the shared expert's rows
+    const bool has_slot = x < k;                // XCD x computes routed slot x
+    const bool has_gu = has_slot && kGURows * j < I;
+    const int ia = min(kGURows * j + 2 * wave, I - 2);  // this wave's two intermediate rows
+    const bool owns = kOwn * j < H;             // output columns [64 j, 64 j + 64)
+    const int own0 = min(kOwn * j, H - kOwn);
+    const bool has_sgu = shared && 2 * j < Ix;  // shared rows x Ix + 2 j, + 1
+    const int sgrow = x * Ix + min(2 * j, max(Ix - 2, 0));
+    const bool zero_rank = x == 0 && j == 0;    // writes the routing outputs
+    const bool recorder = x == 0;               // XCD 0 writes the per-layer outputs
 
     // per-lane byte offsets, fixed for the whole call
     AheadOffsets ao{};
     {
-        const int e = min(w, E - 1), c = min(u, nblk - 1);
-        ao.router = (uint32_t)((e * H + 8 * c) * 2);
-        ao.bias = (uint32_t)(e * 4);
+        const int e0r = min(kLogitsPerWg * j + 2 * hw, E - 1), e1r = min(kLogitsPerWg * j + 2 * hw + 1, E - 1);
+        const int rb = min(4 * lane, nblk - 4);
+        ao.rt0 = (uint32_t)((e0r * H + 8 * rb) * 2);
+        ao.rt1 = (uint32_t)((e1r * H + 8 * rb) * 2);
+        ao.bias = (uint32_t)(min(kLogitsPerWg * j + 2 * hw + (lane & 1), E - 1) * 4);
+        ao.gam = (uint32_t)(min(u, nblk - 1) * 16);
         if (shared) {
             const int Is = a.I_shared;
-            const int row = min(2 * w + (hw & 1), Is - 1), cc = min(lane, chunks - 1);
+            const int row = min(sgrow + (hw & 1), Is - 1), cc = min(lane, chunks - 1);
             ao.sgu_q = (uint32_t)(row * (H / 2) + cc * 16);
             ao.sgu_sb = (uint32_t)((row * (H / kGroup) + cc / 2) * kSB);
-            const int drow = min(kWorkers * w + 2 * hw + lane / 32, H - 1), wd = min(2 * (lane % 32), I / 8 - 2);
-            ao.sdn_q = (uint32_t)(drow * (I / 2) + wd * 4);
-            ao.sdn_sb = (uint32_t)((drow * (I / kGroup) + wd / 8) * kSB);
+            // shared down: row (output column) own0 + u / 4, words 2 (u % 4), +1
+            // of the slice [x Ix, x Ix + Ix) of its Is values (Ix / 8 words)
+            const int drow = own0 + u / 4, wpr = Ix / 8;
+            const int w0 = min(2 * (u % 4), wpr - 1), w1 = min(2 * (u % 4) + 1, wpr - 1);
+            ao.sdn_q0 = (uint32_t)(drow * (Is / 2) + (x * Ix) / 2 + 4 * w0);
+            ao.sdn_q1 = (uint32_t)(drow * (Is / 2) + (x * Ix) / 2 + 4 * w1);
+            ao.sdn_sb = (uint32_t)((drow * (Is / kGroup) + (x * Ix) / kGroup) * kSB);
         }
     }
+    const bool rt_mine = 4 * lane < nblk;  // the router blocks this lane holds are real
     const int gchunk = min(lane, chunks - 1);
     const uint32_t off_gq = (uint32_t)(gchunk * 16), off_gsb = (uint32_t)((gchunk / 2) * kSB);
-    const int ia = min(gu_i0 + 2 * wave, I - 2);  // this wave's two intermediate rows
     const int dgrp = lane % 8, dgrp_c = min(dgrp, I / kGroup - 1);
     const uint32_t off_dq = (uint32_t)((lane / 8) * (I / 2) + dgrp_c * 32);
     const uint32_t off_dsb = (uint32_t)(((lane / 8) * (I / kGroup) + dgrp_c) * kSB);
-    const bool dmine = owns && wave < k && dgrp < I / kGroup;  // routed slot `wave`, row own0 + lane / 8
+    const bool dmine = owns && has_slot && dgrp < I / kGroup;  // row own0 + 8 wave + lane / 8, group dgrp
+    const bool sdmine = shared && owns && 2 * (u % 4) < Ix / 8;  // (waves 4-7) the first of the two words
+    const bool sdmine1 = shared && owns && 2 * (u % 4) + 1 < Ix / 8;
 
     Ahead<SB> ah{};
     if (holder) read_ahead<SB>(a, 0, hw, ao, ah);
-    uint32_t mykey = 0;  // waves 0-3: the order key of expert tid's logit
-    if (tid == 0) sh.ncand = 0;
 
-    // the normalisation weight of each block of 8 columns, read ahead a layer
-    // at a time by waves 0-3 (thread t: block t)
-    const uint32_t off_norm = (uint32_t)(min(tid, nblk - 1) * 16);
-    uint4 gam = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 ones
-    if (tid < kPollThreads && a.norm_w) gam = ld<uint4>(lay(a.norm_w, a.norm_stride, 0), off_norm);
     // this thread's block of the stream entering the layer (waves 0-3)
     float xv[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-
-    // the first layer's input
     if (tid < nblk) {
         const uint4 raw = reinterpret_cast<const uint4*>(a.x_in)[tid];
         const uint16_t* b = reinterpret_cast<const uint16_t*>(&raw);
 #pragma unroll
         for (int i = 0; i < 8; i++) xv[i] = bf16_to_f32(b[i]);
         reinterpret_cast<uint4*>(sh.xb)[tid] = raw;
-        if (a.layer_x && tid == w) reinterpret_cast<uint4*>(a.layer_x)[tid] = raw;
+        if (a.layer_x && recorder && tid / 8 == j) reinterpret_cast<uint4*>(a.layer_x)[tid] = raw;
     }
+    uint32_t mykey = 0;  // waves 0-3: the order key of expert tid's logit
 
     for (int l = 0; l < L; l++) {
         const unsigned ep = e0 + 1 + (unsigned)l;
-        // this layer's halves of the exchange regions
         const size_t par = ep & 1;
-        unsigned long long* logits_p = a.logits + par * (kStackLogitCopies * kMaxE);
-        unsigned long long* sh_h_p = a.sh_h + par * (kStackSharedHCopies * kHWords);
-        unsigned long long* rt_h_p = a.rt_h + par * (8 * kStackRoutedHCopies * kHWords);
+        // this layer's halves of the exchange regions
+        unsigned long long* loc_x = a.local + ((size_t)x * 2 + par) * kStackLocWords;
+        unsigned long long* loc_logits = loc_x + (size_t)kCopies * kStackXWords;
+        unsigned long long* loc_h = loc_logits + (size_t)kCopies * kMaxE;
+        unsigned long long* loc_sh = loc_h + (size_t)kCopies * (kStackMaxI / 2);
+        unsigned long long* part = a.part + par * ((size_t)kStackGrid * kOwn);
 
-        // ---- x of this layer: every block of the stream from this workgroup's
-        // copy (waves 0-3, thread t: block t)
-        if (l > 0) {
-            if (tid < kPollThreads) {
-                const unsigned long long* src =
-                    a.xpub + (par * kStackXCopies + (size_t)(w % kStackXCopies)) * kStackXWords + 3 * tid;
-                const unsigned tag = xtag(ep);
-                const bool mine = tid < nblk;
-                unsigned long long q0 = 0, q1 = 0, q2 = 0;
-                for (long spins = 0;; spins++) {
-                    bool have = true;
-                    if (mine && !failed) {
-                        q0 = peek(src);
-                        q1 = peek(src + 1);
-                        q2 = peek(src + 2);
-                        have = (unsigned)(q0 >> 48) == tag && (unsigned)(q1 >> 48) == tag &&
-                               (unsigned)(q2 >> 48) == tag;
-                    }
-                    if (__ballot(!have) == 0) break;
-                    if (spins > kSpinLimit) {
-                        if (lane == 0) flag_error(a.ctl);
-                        failed = true;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
+        // ---- x of this layer: every block of the stream from this XCD's copy
+        // (waves 0-3, thread t: block t)
+        if (l > 0 && tid < kPollThreads) {
+            const unsigned long long* src = loc_x + (size_t)(j % kCopies) * kStackXWords + 3 * tid;
+            const unsigned tag = xtag(ep);
+            const bool mine = tid < nblk;
+            unsigned long long q0 = 0, q1 = 0, q2 = 0;
+            for (long spins = 0;; spins++) {
+                bool have = true;
+                if (mine && !failed) {
+                    q0 = peek(src);
+                    q1 = peek(src + 1);
+                    q2 = peek(src + 2);
+                    have = (unsigned)(q0 >> 48) == tag && (unsigned)(q1 >> 48) == tag &&
+                           (unsigned)(q2 >> 48) == tag;
                 }
-                if (mine) {
-                    const uint32_t nb[8] = {(uint32_t)(q0 & 0xFFFF), (uint32_t)((q0 >> 16) & 0xFFFF),
-                                            (uint32_t)((q0 >> 32) & 0xFFFF), (uint32_t)(q1 & 0xFFFF),
-                                            (uint32_t)((q1 >> 16) & 0xFFFF), (uint32_t)((q1 >> 32) & 0xFFFF),
-                                            (uint32_t)(q2 & 0xFFFF), (uint32_t)((q2 >> 16) & 0xFFFF)};
+                if (__ballot(!have) == 0) break;
+                if (spins > kSpinLimit) {
+                    if (lane == 0) flag_error(a.ctl);
+                    failed = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (mine) {
+                const uint32_t nb[8] = {(uint32_t)(q0 & 0xFFFF), (uint32_t)((q0 >> 16) & 0xFFFF),
+                                        (uint32_t)((q0 >> 32) & 0xFFFF), (uint32_t)(q1 & 0xFFFF),
+                                        (uint32_t)((q1 >> 16) & 0xFFFF), (uint32_t)((q1 >> 32) & 0xFFFF),
+                                        (uint32_t)(q2 & 0xFFFF), (uint32_t)((q2 >> 16) & 0xFFFF)};
 #pragma unroll
-                    for (int i = 0; i < 8; i++) xv[i] = __uint_as_float(nb[i] << 16);
-                    reinterpret_cast<uint4*>(sh.xb)[tid] =
-                        make_uint4(nb[0] | (nb[1] << 16), nb[2] | (nb[3] << 16), nb[4] | (nb[5] << 16),
-                                   nb[6] | (nb[7] << 16));
-                }
+                for (int i = 0; i < 8; i++) xv[i] = __uint_as_float(nb[i] << 16);
+                reinterpret_cast<uint4*>(sh.xb)[tid] = make_uint4(nb[0] | (nb[1] << 16), nb[2] | (nb[3] << 16),
+                                                                  nb[4] | (nb[5] << 16), nb[6] | (nb[7] << 16));
             }
         }
-        // ---- the layer's input: the stream's RMS normalisation (waves 0-3)
+        // ---- the layer's normalisation weight, read ahead (waves 4-7)
+        if (holder && u < nblk) sh.gam[u] = a.norm_w ? ah.gam : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+        // ---- the stream's sum of squares (waves 0-3)
         if (tid < kPollThreads) {
             float ss = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; i++) ss += xv[i] * xv[i];
-            ss = group_sum(ss, kWave);
+            ss = wave_total(ss);
             if (lane == 0) sh.ssq[wave] = ss;
         }
         __syncthreads();  // B1: the stream and its sums of squares in LDS
+
+        // ---- the layer's input: the stream's RMS normalisation (waves 0-3, thread t: block t)
         if (tid < nblk) {
             const float r = 1.0f / sqrtf(((sh.ssq[0] + sh.ssq[1]) + (sh.ssq[2] + sh.ssq[3])) / (float)H + kNormEps);
-            const uint32_t gw[4] = {gam.x, gam.y, gam.z, gam.w};
+            const uint4 gm = sh.gam[tid];
+            const uint32_t gw[4] = {gm.x, gm.y, gm.z, gm.w};
             float v[8];
             uint16_t nb[8];
 #pragma unroll
@@ -459,26 +467,44 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                                          nb[4] | ((uint32_t)nb[5] << 16), nb[6] | ((uint32_t)nb[7] << 16));
             reinterpret_cast<uint4*>(sh.xn)[tid] = raw;
             block_pairs(v, sh.xp[tid], sh.xs[tid]);
-            if (a.layer_in && tid == w) reinterpret_cast<uint4*>(a.layer_in + (size_t)l * H)[tid] = raw;
+            if (a.layer_in && recorder && tid / 8 == j) reinterpret_cast<uint4*>(a.layer_in + (size_t)l * H)[tid] = raw;
         }
         __syncthreads();  // the layer's input in LDS
 
-        // ---- router logit of expert w and the shared expert's gate/up (waves 4-7)
+        // ---- router logits of experts 8 j + 2 hw, + 1 and the shared gate/up (waves 4-7)
         if (holder) {
-            float p = 0.0f;
-            if (w < E && u < nblk) {
-                // bf16 pairs as words: the low half widens by a shift, the high
-                // half by masking (exact, as bf16 -> float32 is)
-                const uint4 xr = reinterpret_cast<const uint4*>(sh.xn)[u];
-                const uint4 rr = ah.router;
-                const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w}, rw[4] = {rr.x, rr.y, rr.z, rr.w};
+            // two partial sums per row (blocks 4 lane, +2 and 4 lane + 1, +3), bf16
+            // pairs against bf16 pairs
+            float p0a = 0.0f, p0b = 0.0f, p1a = 0.0f, p1b = 0.0f;
+            if (rt_mine) {
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    p += __uint_as_float(xw[i] << 16) * __uint_as_float(rw[i] << 16);
-                    p += __uint_as_float(xw[i] & 0xFFFF0000u) * __uint_as_float(rw[i] & 0xFFFF0000u);
+                    const uint4 xr = reinterpret_cast<const uint4*>(sh.xn)[4 * lane + i];
+                    const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
+                    const uint32_t r0[4] = {ah.rt[0][i].x, ah.rt[0][i].y, ah.rt[0][i].z, ah.rt[0][i].w};
+                    const uint32_t r1[4] = {ah.rt[1][i].x, ah.rt[1][i].y, ah.rt[1][i].z, ah.rt[1][i].w};
+#pragma unroll
+                    for (int m = 0; m < 4; m++) {
+                        if (i & 1) {
+                            p0b = dot2_bf16(xw[m], r0[m], p0b);
+                            p1b = dot2_bf16(xw[m], r1[m], p1b);
+                        } else {
+                            p0a = dot2_bf16(xw[m], r0[m], p0a);
+                            p1a = dot2_bf16(xw[m], r1[m], p1a);
+                        }
+                    }
                 }
             }
-            p = group_sum(p, kWave);
+            const float p0 = wave_total(p0a + p0b), p1 = wave_total(p1a + p1b);
+            // lane: expert 8 j + 2 hw + lane % 2, copy lane / 2
+            {
+                const int e = kLogitsPerWg * j + 2 * hw + (lane & 1);
+                if (lane < 2 * kCopies && e < E) {
+                    const float lg = ((lane & 1) ? p1 : p0) + (a.logit_bias ? ah.bias : 0.0f);
+                    put_local(loc_logits + (size_t)(lane / 2) * kMaxE + e,
+                              ((unsigned long long)ep << 32) | __float_as_uint(lg));
+                }
+            }
             float q = 0.0f;
             if (has_sgu && lane < chunks) {
                 float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
@@ -492,24 +518,20 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                 }
                 q = affine(sb_to_f32<SB>(ah.sgu_s), sb_to_f32<SB>(ah.sgu_b), alo, ahi, lo, hi);
             }
-            q = group_sum(q, kWave);
-            if (lane == 0) {
-                sh.red[hw] = p;
-                sh.sred[hw] = q;
-            }
+            q = wave_total(q);
+            if (lane == 0) sh.sred[hw] = q;
         }
-        __syncthreads();  // B2: partial sums in LDS
-        if (wave == 4 && w < E) {  // lanes 0..7 publish one copy each of the logit
-            const float lg = ((sh.red[0] + sh.red[1]) + (sh.red[2] + sh.red[3])) + (a.logit_bias ? ah.bias : 0.0f);
-            if (lane < kStackLogitCopies) publish(logits_p + (size_t)lane * kMaxE + w, ep, __float_as_uint(lg));
-        } else if (wave == 5 && has_sgu) {  // rows 2w, 2w+1 of the shared expert's h
+        __syncthreads();  // B2: this workgroup's shared gate/up rows in LDS
+        if (wave == 5 && has_sgu) {  // shared rows x Ix + 2 j, + 1 of h
             const half2_t hp = {(_Float16)(silu(sh.sred[0]) * sh.sred[2]), (_Float16)(silu(sh.sred[1]) * sh.sred[3])};
-            if (lane < kStackSharedHCopies) publish(sh_h_p + (size_t)lane * kHWords + w, ep, as_u32(hp));
+            if (lane < kCopies)
+                put_local(loc_sh + (size_t)lane * kStackShWords + j, ((unsigned long long)ep << 32) | as_u32(hp));
         }
 
-        // ---- every logit of the layer (waves 0-3 poll one word each)
+        // ---- every logit of the layer (waves 0-3 poll one word each) and the
+        // XCD's share of the shared expert's h (wave 6)
         if (tid < kMaxE) {
-            const unsigned long long* src = logits_p + (size_t)(w % kStackLogitCopies) * kMaxE;
+            const unsigned long long* src = loc_logits + (size_t)(j % kCopies) * kMaxE;
             const bool mine = tid < E;
             unsigned long long v = 0;
             for (long spins = 0;; spins++) {
@@ -533,46 +555,70 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
             const int first = (int)__builtin_ctzll(__ballot(mykey == m1));
             const uint32_t m2 = wave_max_u32(lane == first ? 0u : mykey);
             if (lane == 0) sh.m2[wave] = m2;
+        } else if (wave == 6 && shared) {
+            const bool ok = poll_h<kStackShWords>(loc_sh + (size_t)(j % kCopies) * kStackShWords, Ix / 2, ep, sh.hsp,
+                                                  sh.hss, 0, lane, failed, a.ctl);
+            failed = failed || !ok;
         }
-        __syncthreads();  // B3: keys in LDS
+        __syncthreads();  // B3: keys and the shared share's h in LDS
         // candidates of the top k: keys >= the least of the four waves' second
         // largest keys.  At least two keys of every wave reach it, so the k <= 8
         // largest are among the candidates, and no key below it ranks in the
         // top k.  (Fewer than 194 experts leave a wave with under two keys: then
-        // every expert is a candidate.)
+        // every expert is a candidate.)  Each polling wave lists its own.
         if (tid < kMaxE) {
             const uint32_t lim = E >= 194 ? min(min(sh.m2[0], sh.m2[1]), min(sh.m2[2], sh.m2[3])) : 1u;
-            if (mykey != 0u && mykey >= lim) {
-                const int pos = atomicAdd(&sh.ncand, 1);
-                if (pos < kWave) {
-                    sh.ckey[pos] = mykey;
-                    sh.cidx[pos] = tid;
-                }
+            const bool c = mykey != 0u && mykey >= lim;
+            const uint64_t bal = __ballot(c);
+            if (c) {
+                const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+                sh.ckey[wave][pos] = mykey;
+                sh.cidx[wave][pos] = tid;
             }
+            if (lane == 0) sh.ccnt[wave] = __popcll(bal);
         }
         __syncthreads();  // candidates in LDS
 
         // ---- top k: every workgroup selects for itself, from the same words
-        if (wave == 0) {
-            const int n = sh.ncand;
-            if (n <= kWave) {
-                // rank of each candidate: the candidates above it, and the equal
-                // ones of lower expert index; every other key is below them all
-                const uint32_t ck = lane < n ? sh.ckey[lane] : 0u;
-                const int ce = lane < n ? sh.cidx[lane] : 0;
-                int rank = 0;
-                for (int j = 0; j < n; j++) {
-                    const uint32_t kj = __builtin_amdgcn_readlane(ck, j);
-                    const int ej = __builtin_amdgcn_readlane(ce, j);
-                    rank += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
+        {
+            const int n0 = sh.ccnt[0], n1 = sh.ccnt[1], n2 = sh.ccnt[2], n3 = sh.ccnt[3];
+            const int n = n0 + n1 + n2 + n3;
+            if (n <= kRankCands) {
+                // rank of candidate i (8 threads each, candidates j = t % 8 + 8 m):
+                // the candidates above it, and the equal ones of lower expert
+                // index; every other key is below them all
+                if (tid < 8 * kRankCands) {
+                    auto cand = [&](int p, uint32_t& key, int& e) {
+                        const int w = p < n0 ? 0 : p < n0 + n1 ? 1 : p < n0 + n1 + n2 ? 2 : 3;
+                        const int q = p - (w > 0 ? n0 : 0) - (w > 1 ? n1 : 0) - (w > 2 ? n2 : 0);
+                        key = sh.ckey[w][q];
+                        e = sh.cidx[w][q];
+                    };
+                    const int i = tid / 8;
+                    uint32_t ck = 0;
+                    int ce = 0;
+                    if (i < n) cand(i, ck, ce);
+                    int rank = 0;
+#pragma unroll
+                    for (int m = 0; m < kRankCands / 8; m++) {
+                        const int jj = tid % 8 + 8 * m;
+                        if (jj < n) {
+                            uint32_t kj;
+                            int ej;
+                            cand(jj, kj, ej);
+                            rank += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
+                        }
+                    }
+                    rank = (int)group_sum((float)rank, 8);
+                    if (tid % 8 == 0 && i < n && rank < k) {
+                        sh.sel_e[rank] = ce;
+                        sh.sel_key[rank] = ck;
+                    }
                 }
-                if (lane < n && rank < k) {
-                    sh.sel_e[rank] = ce;
-                    sh.sel_key[rank] = ck;
-                }
-            } else {
-                // many equal keys: the k-th largest key by a radix search, then
-                // every key above it and the equal ones by ascending index
+            } else if (wave == 0) {
+                // many candidates (many equal keys, or few experts): the k-th
+                // largest key by a radix search, then every key above it and the
+                // equal ones by ascending index
                 uint32_t key[kMaxE / kWave];
 #pragma unroll
                 for (int i = 0; i < kMaxE / kWave; i++) key[i] = sh.keys[lane + kWave * i];
@@ -624,26 +670,18 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                     sh.sel_key[rank] = mk;
                 }
             }
-            // weights: softmax of the kept logits, summed in rank order
-            const uint32_t rk = lane < k ? sh.sel_key[lane] : 0u;
-            const float top = key_float(__builtin_amdgcn_readlane(rk, 0));
-            const float pr = expf(key_float(rk) - top);
-            float z = 0.0f;
-            for (int m = 0; m < k; m++) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr), m));
-            if (lane < k) sh.sel_w[lane] = pr / z;
-            if (lane == 0) sh.ncand = 0;  // for the next layer (past several barriers)
         }
         __syncthreads();  // B4: the routing in LDS
 
-        // ---- routed loads, gate/up rows first, then down rows
-        const int ex_gu = uniform(sh.sel_e[gu_slot]), ex_dn = uniform(sh.sel_e[min(wave, k - 1)]);
+        // ---- routed loads of the XCD's slot: gate/up rows first, then down rows
+        const int ex = uniform(sh.sel_e[min(x, k - 1)]);
         uint4 gq[4];
         SB gs[4], gb[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const QMatPtr& m = r < 2 ? a.experts.gate : a.experts.up;
             const QMatStride& st = r < 2 ? a.experts_stride.gate : a.experts_stride.up;
-            const size_t row = (size_t)ex_gu * I + ia + (r & 1);
+            const size_t row = (size_t)ex * I + ia + (r & 1);
             gs[r] = ld<SB>(lay(m.s, st.s, l) + row * (H / kGroup) * kSB, off_gsb);
             gb[r] = ld<SB>(lay(m.b, st.b, l) + row * (H / kGroup) * kSB, off_gsb);
             gq[r] = ld<uint4>(lay(m.q, st.q, l) + row * (H / 2), off_gq);
@@ -652,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
         uint4 dq0, dq1;
         SB ds, db;
         {
-            const size_t row0 = (size_t)ex_dn * H + own0;  // this wave's slot, the owned rows
+            const size_t row0 = (size_t)ex * H + own0 + 8 * wave;  // this wave's 8 owned rows
             const QMatStride& st = a.experts_stride.down;
             ds = ld<SB>(lay(a.experts.down.s, st.s, l) + row0 * (I / kGroup) * kSB, off_dsb);
             db = ld<SB>(lay(a.experts.down.b, st.b, l) + row0 * (I / kGroup) * kSB, off_dsb);
@@ -661,12 +699,30 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
             dq1 = ld<uint4>(qb, off_dq + 16);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (w == 0 && tid < k) {
-            if (a.idx_out) a.idx_out[(size_t)l * k + tid] = sh.sel_e[tid];
-            if (a.w_out) a.w_out[(size_t)l * k + tid] = sh.sel_w[tid];
+        // ---- the shared expert's share of the owned columns (waves 4-7, while
+        // their routed loads are in flight; its weights were read ahead during
+        // the previous layer and are replaced by the next layer's after the gate/up)
+        if (holder && shared && owns) {
+            float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
+            const int w0 = 2 * (u % 4);
+            if (sdmine) {
+                dot_word(ah.sdn0, pairs_of(sh.hsp[w0]), alo, ahi);
+                const float2 s0 = sh.hss[w0];
+                lo += s0.x;
+                hi += s0.y;
+            }
+            if (sdmine1) {
+                dot_word(ah.sdn1, pairs_of(sh.hsp[w0 + 1]), alo, ahi);
+                const float2 s1 = sh.hss[w0 + 1];
+                lo += s1.x;
+                hi += s1.y;
+            }
+            float y = sdmine ? affine(sb_to_f32<SB>(ah.sdn_s), sb_to_f32<SB>(ah.sdn_b), alo, ahi, lo, hi) : 0.0f;
+            y = group_sum(y, 4);  // the row's 4 threads
+            if (u % 4 == 0) sh.ysh[u / 4] = y;
         }
 
-        // ---- routed gate/up: rows ia, ia + 1 of h per wave
+        // ---- routed gate/up: rows ia, ia + 1 of the slot's h per wave
         if (has_gu) {
             float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (lane < chunks) {
@@ -690,81 +746,130 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc4[r] = group_sum(acc4[r], kWave);
-            if (lane < kStackRoutedHCopies) {  // one copy per lane
+            for (int r = 0; r < 4; r++) acc4[r] = wave_total(acc4[r]);
+            if (lane < kCopies) {  // one copy per lane
                 const half2_t hp = {(_Float16)(silu(acc4[0]) * acc4[2]), (_Float16)(silu(acc4[1]) * acc4[3])};
-                publish(rt_h_p + ((size_t)gu_slot * kStackRoutedHCopies + lane) * kHWords + gu_i0 / 2 + wave, ep,
-                        as_u32(hp));
+                put_local(loc_h + (size_t)lane * (kStackMaxI / 2) + ia / 2, ((unsigned long long)ep << 32) | as_u32(hp));
             }
         }
-
-        // ---- shared expert's down (waves 4-7: 2 rows each, 2 words per lane)
-        if (shared && holder) {
-            const bool ok = poll_h<2 * 32>(sh_h_p + (size_t)(w % kStackSharedHCopies) * kHWords, a.I_shared / 2, ep,
-                                           sh.hsp, sh.hss, hw, lane, failed, a.ctl);
-            failed = failed || !ok;
-        }
-        __syncthreads();  // shared h in LDS
-        if (shared && holder) {
-            const int row = kWorkers * w + 2 * hw + lane / 32, wd = 2 * (lane % 32);
-            float y = 0.0f;
-            if (row < H && wd < I / 8) {
-                float alo = 0.0f, ahi = 0.0f;
-                dot_word(ah.sdn.x, pairs_of(sh.hsp[wd]), alo, ahi);
-                dot_word(ah.sdn.y, pairs_of(sh.hsp[wd + 1]), alo, ahi);
-                const float2 s0 = sh.hss[wd], s1 = sh.hss[wd + 1];
-                y = affine(sb_to_f32<SB>(ah.sdn_s), sb_to_f32<SB>(ah.sdn_b), alo, ahi, s0.x + s1.x, s0.y + s1.y);
+        // ---- the routing weights: softmax of the kept logits, summed in rank
+        // order (wave 0; used from the down on)
+        if (wave == 0) {
+            const uint32_t rk = lane < k ? sh.sel_key[lane] : 0u;
+            const float top = key_float(__builtin_amdgcn_readlane(rk, 0));
+            const float pr = expf(key_float(rk) - top);
+            float z = 0.0f;
+            for (int m = 0; m < k; m++) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr), m));
+            const float wr = pr / z;
+            if (lane < k) sh.sel_w[lane] = wr;
+            if (zero_rank && lane < k) {
+                if (a.idx_out) a.idx_out[(size_t)l * k + lane] = sh.sel_e[lane];
+                if (a.w_out) a.w_out[(size_t)l * k + lane] = wr;
             }
-            y = group_sum(y, 32);
-            if (lane % 32 == 0) sh.ycon[k][2 * hw + lane / 32] = y;
         }
-
-        // ---- routed down: wave j polls slot j's h, then 8 rows x one group per lane
-        if (owns && wave < k) {
-            const bool ok = poll_slot_h(rt_h_p + ((size_t)wave * kStackRoutedHCopies + w % kStackRoutedHCopies) *
-                                                     kHWords,
-                                        I / 2, ep, sh.hrp[wave], sh.hrs[wave], lane, failed, a.ctl);
-            failed = failed || !ok;
-        }
-        float y = 0.0f;
-        if (dmine) {
-            const uint32_t wv[8] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w};
-            float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
-#pragma unroll
-            for (int m = 0; m < 8; m++) {
-                dot_word(wv[m], pairs_of(sh.hrp[wave][8 * dgrp + m]), alo, ahi);
-                const float2 sm = sh.hrs[wave][8 * dgrp + m];
-                lo += sm.x;
-                hi += sm.y;
-            }
-            y = affine(sb_to_f32<SB>(ds), sb_to_f32<SB>(db), alo, ahi, lo, hi);
-        }
-        y = group_sum(y, 8);  // the row's groups: 8 lanes
-        if (dgrp == 0 && wave < k) sh.ycon[wave][lane / 8] = sh.sel_w[wave] * y;
-        // every poll and product of this layer is done: waves 4-7 read the next
-        // layer's data-independent weights ahead; they land while this layer's
-        // output completes
+        // every poll of this layer by waves 4-7 is done: they read the next
+        // layer's data-independent weights ahead; the loads land while this
+        // layer's down and output hand-over complete
         __builtin_amdgcn_sched_barrier(0);
         if (holder) read_ahead<SB>(a, min(l + 1, L - 1), hw, ao, ah);
-        if (tid < kPollThreads && a.norm_w) gam = ld<uint4>(lay(a.norm_w, a.norm_stride, min(l + 1, L - 1)), off_norm);
-        __syncthreads();  // every contribution to the owned columns in LDS
+        __builtin_amdgcn_sched_barrier(0);
 
-        // ---- the owned columns of the layer's output and of the next stream
-        // (wave 0, lane c < 8: column 8 w + c), summed in slot order
-        if (wave == 0) {
-            float o = 0.0f;
-            uint16_t xn = 0;
-            if (lane < 8 && owns) {
-                for (int j = 0; j < n_slots; j++) o += sh.ycon[j][lane];
-                xn = bf16_rne(bf16_to_f32(sh.xb[8 * w + lane]) + o);
-                if (a.layer_out) a.layer_out[(size_t)l * H + 8 * w + lane] = o;
-                if (l + 1 < L) {
-                    if (a.layer_x) a.layer_x[(size_t)(l + 1) * H + 8 * w + lane] = xn;
-                } else {
-                    a.x_out[8 * w + lane] = xn;
+        // ---- the slot's whole h (waves 0-3: 64 words each)
+        if (has_slot && owns && wave < 4) {
+            const bool ok = poll_h<kWave>(loc_h + (size_t)(j % kCopies) * (kStackMaxI / 2), I / 2, ep, sh.hrp, sh.hrs,
+                                          wave, lane, failed, a.ctl);
+            failed = failed || !ok;
+        }
+        __syncthreads();  // the slot's h in LDS
+
+        // ---- the routed slot's down for the owned columns: 8 rows per wave, one
+        // 64-value group per lane
+        if (has_slot && owns) {
+            float y = 0.0f;
+            if (dmine) {
+                const uint32_t wv[8] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w};
+                float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    dot_word(wv[m], pairs_of(sh.hrp[8 * dgrp + m]), alo, ahi);
+                    const float2 sm = sh.hrs[8 * dgrp + m];
+                    lo += sm.x;
+                    hi += sm.y;
+                }
+                y = affine(sb_to_f32<SB>(ds), sb_to_f32<SB>(db), alo, ahi, lo, hi);
+            }
+            y = group_sum(y, 8);  // the row's groups: 8 lanes
+            if (dgrp == 0) sh.yr[8 * wave + lane / 8] = y;
+        }
+        __syncthreads();  // the owned rows of both products in LDS
+
+        // ---- this XCD's partial sums of the owned columns, to the 8 workgroups
+        // that own them (wave 0, lane c: column own0 + c)
+        if (wave == 0 && owns) {
+            const float pr = (has_slot ? sh.sel_w[x] * sh.yr[lane] : 0.0f) + (shared ? sh.ysh[lane] : 0.0f);
+            publish(part + ((size_t)x * kPerXcd + j) * kOwn + lane, ep, __float_as_uint(pr));
+        }
+        // every XCD's partials of the owned columns (waves 0-3: XCDs 2 wave, + 1)
+        if (owns && wave < 4) {
+            const unsigned long long* s0 = part + ((size_t)(2 * wave) * kPerXcd + j) * kOwn + lane;
+            const unsigned long long* s1 = s0 + (size_t)kPerXcd * kOwn;
+            unsigned long long v0 = 0, v1 = 0;
+            if (!failed) {
+                for (long spins = 0;; spins++) {
+                    v0 = peek(s0);
+                    v1 = peek(s1);
+                    const bool have = (unsigned)(v0 >> 32) == ep && (unsigned)(v1 >> 32) == ep;
+                    if (__ballot(!have) == 0) break;
+                    if (spins > kSpinLimit) {
+                        if (lane == 0) flag_error(a.ctl);
+                        failed = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
                 }
             }
-            if (l + 1 < L) publish_x(a, w, lane, ep + 1, xn);
+            sh.pp[2 * wave][lane] = __uint_as_float((uint32_t)v0);
+            sh.pp[2 * wave + 1][lane] = __uint_as_float((uint32_t)v1);
+        }
+        __syncthreads();  // every partial of the owned columns in LDS
+
+        // ---- the owned columns of the layer's output and of the next stream
+        // (wave 0, lane c: column own0 + c), summed in XCD order
+        if (wave == 0 && owns) {
+            float o = 0.0f;
+#pragma unroll
+            for (int xx = 0; xx < kXcds; xx++) o += sh.pp[xx][lane];
+            const int col = own0 + lane;
+            const uint16_t xn = bf16_rne(bf16_to_f32(sh.xb[col]) + o);
+            if (recorder) {
+                if (a.layer_out) a.layer_out[(size_t)l * H + col] = o;
+                if (l + 1 < L) {
+                    if (a.layer_x) a.layer_x[(size_t)(l + 1) * H + col] = xn;
+                } else {
+                    a.x_out[col] = xn;
+                }
+            }
+            if (l + 1 < L) {
+                // block lane / 8 of the owned columns: 3 tagged words, written by
+                // lanes 8 b .. 8 b + 2 into every copy of the next layer's stream
+                const int b = lane / 8, q = lane % 8;
+                uint32_t v[8];
+#pragma unroll
+                for (int c = 0; c < 8; c++) v[c] = (uint32_t)__shfl((int)xn, 8 * b + c);
+                const unsigned long long tag = (unsigned long long)xtag(ep + 1) << 48;
+                const unsigned long long w0 =
+                    tag | ((unsigned long long)v[2] << 32) | ((unsigned long long)v[1] << 16) | v[0];
+                const unsigned long long w1 =
+                    tag | ((unsigned long long)v[5] << 32) | ((unsigned long long)v[4] << 16) | v[3];
+                const unsigned long long w2 = tag | ((unsigned long long)v[7] << 16) | v[6];
+                const unsigned long long word = q == 0 ? w0 : q == 1 ? w1 : w2;
+                if (q < 3) {
+                    unsigned long long* nx = a.local + ((size_t)x * 2 + ((ep + 1) & 1)) * kStackLocWords;
+                    const size_t wd = (size_t)3 * (own0 / 8 + b) + q;
+#pragma unroll
+                    for (int c = 0; c < kCopies; c++) put_local(nx + (size_t)c * kStackXWords + wd, word);
+                }
+            }
         }
     }
 

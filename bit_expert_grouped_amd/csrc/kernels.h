@@ -168,28 +168,32 @@ struct DecodeArgs {
 };
 
 // Persistent multi-layer decode (one token through L stacked layers in one
-// launch, each layer reading the RMS-normalised residual stream): a grid of kStackGrid workgroups, all resident at once, that hand
-// values over through words of the stack region below (fixed offsets after the
-// one-layer decode region, zero before the first call).  Limits: T = 1,
-// H <= kStackMaxH (8 output columns per workgroup), I <= kStackMaxI,
-// top_k * I / 16 <= kStackGrid.
+// launch, each layer reading the RMS-normalised residual stream): a grid of
+// kStackGrid workgroups, all resident at once, spread by the hardware over the
+// device's kStackXcds XCDs (kStackGrid / kStackXcds on each).  Each XCD carries
+// one routed slot of the layer; its workgroups hand values to each other
+// through words in that XCD's L2 (the local region below), and the XCDs meet
+// once per layer, in the cross region.  Both regions sit at fixed offsets after
+// the one-layer decode region and are zero before the first call.  Limits:
+// T = 1, H <= kStackMaxH, I a power of two in [64, kStackMaxI], top_k <= 8.
 constexpr int kStackGrid = 256;
+constexpr int kStackXcds = 8;
 constexpr int kStackMaxH = 2048;
 constexpr int kStackMaxI = 512;
-// Copies of the values every workgroup (or a slot's workgroups) read, so that
-// each copy has few readers: polled words are what floods the memory system.
-constexpr int kStackLogitCopies = 32;    // of the logits: 8 readers each
-constexpr int kStackSharedHCopies = 32;  // of the shared expert's h: 8 readers each
-constexpr int kStackRoutedHCopies = 32;  // of each routed slot's h (every workgroup reads every slot): 8 readers each
-constexpr int kStackXCopies = 32;        // of the stream entering a layer: 8 readers each
-constexpr int kStackXWords = kStackMaxH / 8 * 3;  // per copy: 3 words {16-bit tag, 3 bf16} per 8 columns
-// every region twice: layer l uses the half of its epoch's parity
-constexpr size_t kStackLogitWords = (size_t)2 * kStackLogitCopies * 256;
-constexpr size_t kStackSharedHWords = (size_t)2 * kStackSharedHCopies * (kStackMaxI / 2);
-constexpr size_t kStackRoutedHWords = (size_t)2 * 8 * kStackRoutedHCopies * (kStackMaxI / 2);
-constexpr size_t kStackXPubWords = (size_t)2 * kStackXCopies * kStackXWords;
-constexpr size_t kStackRegionBytes =
-    8 * (kStackLogitWords + kStackSharedHWords + kStackRoutedHWords + kStackXPubWords);
+// Copies of each XCD-local vector, so that each copy has 8 of the XCD's 32
+// workgroups polling it.
+constexpr int kStackLocalCopies = 4;
+constexpr int kStackXWords = kStackMaxH / 8 * 3;   // the stream: 3 words {16-bit tag, 3 bf16} per 8 columns
+constexpr int kStackShWords = kStackMaxI / 16;     // an XCD's share of the shared expert's h, float16 pairs
+// one XCD's local words of one parity: [copies][stream] [copies][logits]
+// [copies][routed h] [copies][shared h share], each vector a whole number of
+// 128-byte lines
+constexpr size_t kStackLocWords =
+    (size_t)kStackLocalCopies * (kStackXWords + 256 + kStackMaxI / 2 + kStackShWords);
+constexpr size_t kStackLocalWords = (size_t)kStackXcds * 2 * kStackLocWords;
+// cross region: [2 parities][XCD][workgroup of the XCD][64 owned columns] {epoch, float32}
+constexpr size_t kStackPartWords = (size_t)2 * kStackGrid * 64;
+constexpr size_t kStackRegionBytes = 8 * (kStackLocalWords + kStackPartWords);
 // every region at fixed offsets at the start of the workspace
 constexpr size_t kFixedRegionBytes = kDecodeRegionBytes + kStackRegionBytes;
 
@@ -218,11 +222,8 @@ struct StackArgs {
     FfnPtr experts, shared;   // shared.gate.q == nullptr: no shared expert
     FfnStride experts_stride, shared_stride;
     unsigned* ctl;               // the workspace's control words
-    // exchange words, each region [2 parities][...]
-    unsigned long long* logits;  // [kStackLogitCopies][256] {epoch, logit}
-    unsigned long long* sh_h;    // [kStackSharedHCopies][kStackMaxI / 2] {epoch, float16 pair}
-    unsigned long long* rt_h;    // [8 slots][kStackRoutedHCopies][kStackMaxI / 2] {epoch, float16 pair}
-    unsigned long long* xpub;    // [kStackXCopies][kStackXWords] {16-bit tag, 3 bf16}
+    unsigned long long* local;   // [kStackXcds][2 parities][kStackLocWords] XCD-local words
+    unsigned long long* part;    // [2 parities][kStackXcds][kStackGrid / kStackXcds][64] partial sums
 };
 
 // Workgroups the stack kernel can keep resident on the current device (0 on error).

@@ -525,9 +525,10 @@ moe_status moe_decode_stack(const moe_dims* d, const moe_weights* wts, const uin
     if (d->T == 0) return MOE_OK;
     if (n_layers < 1) return MOE_ERR_SHAPE;
     if (d->T != 1 || d->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-    if (d->H > kStackMaxH || d->I > kStackMaxI) return MOE_ERR_UNSUPPORTED;
-    if ((int64_t)d->top_k * (d->I / 16) > kStackGrid || (int64_t)d->top_k * ((d->H + 63) / 64) > kStackGrid)
-        return MOE_ERR_UNSUPPORTED;
+    // one routed slot per XCD; the intermediate dim a power of two, so that an
+    // XCD's eighth of the shared expert sits inside one scale group
+    if (d->H > kStackMaxH || d->I > kStackMaxI || d->top_k > kStackXcds) return MOE_ERR_UNSUPPORTED;
+    if (d->I < kGroup || (d->I & (d->I - 1)) != 0) return MOE_ERR_UNSUPPORTED;
     if (!wts) return MOE_ERR_NULL;
     if (wts->router_q8 || wts->shared_expert_gate) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(check_ptrs({x_in, x_out, wts->router}));
@@ -576,10 +577,8 @@ moe_status moe_decode_stack(const moe_dims* d, const moe_weights* wts, const uin
     a.shared_stride = to_stride(st.shared);
     a.ctl = at<unsigned>(ws, L.ctl);
     unsigned long long* sw = at<unsigned long long>(ws, L.stack);
-    a.logits = sw;
-    a.sh_h = sw + kStackLogitWords;
-    a.rt_h = a.sh_h + kStackSharedHWords;
-    a.xpub = a.rt_h + kStackRoutedHWords;
+    a.local = sw;
+    a.part = sw + kStackLocalWords;
     HIP_TRY(launch_decode_stack(a, d->sb_dtype == MOE_BF16, stream));
     return MOE_OK;
 }

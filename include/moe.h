@@ -293,13 +293,17 @@ typedef struct {
  *     entering each layer; layer_in [H] bf16, its normalisation; layer_out [H]
  *     float32, each layer's output; topk_idx_out, topk_w_out [top_k], the
  *     routing in rank order.
- * Each element of a layer's output is the float32 sum, in a fixed order
- * (the routed experts in rank order, then the shared expert), of its expert
- * contributions, so outputs are the same bit for bit on every call.  Limits (MOE_ERR_UNSUPPORTED): T == 1 (T == 0: nothing to do);
- * H <= 2048; I <= 512; top_k * I / 16 <= 256; top_k * ceil(H / 64) <= 256;
- * dims->out_dtype == MOE_BF16; n_layers >= 1 (else MOE_ERR_SHAPE); the device
- * must hold 256 workgroups of 512 threads at once (all of them run together
- * and wait on each other; launch nothing else on the device concurrently). */
+ * The layer is spread over the device's 8 XCDs: XCD x computes routed slot x
+ * (rank order) and the shared expert's intermediate rows [x I / 8,
+ * (x + 1) I / 8).  Each element of a layer's output is the float32 sum, in XCD
+ * order, of the XCDs' partials w_x y_x + (the shared expert's part), so
+ * outputs are the same bit for bit on every call.  Limits
+ * (MOE_ERR_UNSUPPORTED): T == 1 (T == 0: nothing to do); H <= 2048; I a power
+ * of two in [64, 512]; top_k <= 8; dims->out_dtype == MOE_BF16; n_layers >= 1
+ * (else MOE_ERR_SHAPE); the device must hold 256 workgroups of 512 threads at
+ * once (all of them run together and wait on each other; launch nothing else
+ * on the device concurrently), spread evenly over 8 XCDs (a workgroup on an
+ * XCD numbered 8 or more sets word 255). */
 moe_status moe_decode_stack(const moe_dims *dims, const moe_weights *weights /* host */,
                             const uint16_t *norm_weight, const moe_layer_strides *strides /* host, nullable */,
                             int32_t n_layers, const uint16_t *x_in, uint16_t *x_out, uint16_t *layer_x,
