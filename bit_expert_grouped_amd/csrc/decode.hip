@@ -18,18 +18,16 @@
 //
 // Workgroup roles, in grid order (the grid is dispatched in order and every
 // role waits only on roles before it, so waits always terminate):
-//   router  [0, R)     R = E/4: one expert per wave, its logit for every token;
-//                      also clears the output rows.  Once every logit is out,
-//                      each router workgroup ranks its own experts against all
-//                      of them (one ballot per 64 logits) and publishes, for
-//                      each expert that made the top k, its logit and index
-//                      at its rank.
+//   router  [0, R)     R = E: one expert per workgroup (its 256 threads split
+//                      the row), its logit for every token; also clears the
+//                      output rows, then publishes the logits.
 //   gate/up [R, R+G)   one per (slot, 16-row block of the intermediate dim);
 //                      the shared expert is one more slot per token.  Reads
-//                      the k words of its token's top k, then computes 16
-//                      values of h = silu(gate x) * (up x).
-//   down    [R+G, ...) one per (slot, 64 output rows).  Reads the top k like
-//                      gate/up, has its 16 KB of whole down rows land in LDS
+//                      all E logits of its token and selects the top k itself
+//                      (so routing is one hand-over), then computes 16 values
+//                      of h = silu(gate x) * (up x).
+//   down    [R+G, ...) one per (slot, 64 output rows).  Selects like gate/up,
+//                      has its 16 KB of whole down rows land in LDS
 //                      (direct loads, issued before it waits for h), waits for
 //                      the slot's h, then adds w * (W_down h) for its rows to
 //                      the float32 output with atomics (the fused combine: k+1
@@ -42,9 +40,8 @@
 //     (agent-scope) stores; a reader waits for the words themselves.  The
 //     epoch is one more than the control word the previous call left; the last
 //     workgroup to finish stores it.
-//   - the router workgroups read one of kXchReplicas copies of the logits, the
-//     expert workgroups one of kSelReplicas copies of the top k (lanes 0..k-1
-//     of one wave poll them).
+//   - the expert workgroups read one of kXchReplicas copies of the logits
+//     (thread e of the workgroup polls expert e's word).
 //   - h goes out as float16 pairs, one pair per {epoch, pair} word; a gate/up
 //     workgroup's 16 values are 8 words stored by 8 lanes of one wave.  Each
 //     wave of a down workgroup polls the words of its own 64-column groups of
@@ -70,11 +67,8 @@ using namespace dec;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kRouterExperts = kWaves;  // one expert per wave
 constexpr int kXchReplicas = kDecodeXchReplicas;
-constexpr int kSelReplicas = kDecodeSelReplicas;
 constexpr size_t kXchWords = (size_t)kDecodeMaxT * kMaxE;     // one copy of the logits: [T][E]
-constexpr size_t kSelWords = (size_t)kDecodeMaxT * kMaxTopK;  // one copy of the top k: [T][k]
 constexpr int kGURows = 16;  // gate and up rows per gate/up workgroup
 constexpr int kDRows = 64;   // output rows per down workgroup
 constexpr long kSpinLimit = 1l << 20;
@@ -109,8 +103,10 @@ struct RoleShared {
             float part[kWaves][kDRows];    // each wave's part of every row's dot product
             int wave_ok[kWaves];           // each wave saw its part of h in time
         } down;
-        unsigned long long keys[kDecodeMaxT * kMaxE];  // router role: ranking keys [t][e]
+        TopkShared tk;  // gate/up and down roles: the token's top k (before the roles' own LDS use)
     };
+    float rsum[kDecodeMaxT][kWaves];  // router role: each wave's part of the logits
+    int route_ok[kWaves];             // each wave saw its token's logits in time
     float hrow[kGURows];  // gate/up role: this workgroup's h
     int ex;
     float wgt;
@@ -145,71 +141,67 @@ __device__ bool await_published(const unsigned long long* src, int n, unsigned e
     }
 }
 
-// Ranking key of logit v of expert e: a larger key ranks first, i.e. the larger
-// logit, and on equal logits the lower expert index.  The float maps to an
-// order-preserving unsigned integer (flip all bits of negatives, the sign bit of
-// the rest; -0 is taken as +0, which it equals); the low word holds ~e.
-__device__ __forceinline__ unsigned long long rank_key(float v, int e) {
-    const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)o << 32) | (uint32_t)~e;
-}
-
-__device__ __forceinline__ float lane_f(float v, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Read token t's top k from copy `rep` of the published entries: on return lane
-// j < k of the calling wave holds the logit and expert of rank j.  Polls until
-// all k entries carry `epoch`; returns false on timeout.
-__device__ bool read_topk(const DecodeArgs& p, int t, int rep, unsigned epoch, float& l, int& ex) {
-    const int lane = threadIdx.x % kWave, k = p.top_k;
-    const unsigned long long* wl = p.sel64 + rep * kSelWords + t * kMaxTopK + lane;
-    const unsigned long long* we = wl + kSelReplicas * kSelWords;
-    l = 0.0f;
-    ex = 0;
+// The expert and weight of `slot`: the workgroup polls its token's E logits
+// (copy blockIdx % kXchReplicas, thread e: expert e), selects the top k and
+// keeps rank slot % top_k.  The shared expert's down slots wait for the logits
+// too (so that they never add into rows not yet cleared) and take expert 0 of
+// the shared stack with weight 1.
+__device__ void route_slot(const DecodeArgs& p, int slot, int t, bool routed, unsigned epoch, RoleShared& sh) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const unsigned long long* src = p.xch64 + (blockIdx.x % kXchReplicas) * kXchWords + (size_t)t * p.E;
+    const bool mine = tid < p.E;
+    unsigned long long v = 0;
+    bool ok = true;
+    // wait on one word first (the last expert's), so that hundreds of
+    // workgroups do not poll every word while the router works: that traffic
+    // slows the router's own loads (13.5 against 15.0 us per call)
+    if (tid == 0) {
+        for (long spins = 0; spins <= kSpinLimit; spins++) {
+            if ((unsigned)(peek(src + p.E - 1) >> 32) == epoch) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
     for (long spins = 0;; spins++) {
         bool have = true;
-        if (lane < k) {
-            const unsigned long long a = peek(wl), c = peek(we);
-            have = (unsigned)(a >> 32) == epoch && (unsigned)(c >> 32) == epoch;
-            l = __uint_as_float((uint32_t)a);
-            ex = (int)(uint32_t)c;
+        if (mine) {
+            v = peek(src + tid);
+            have = (unsigned)(v >> 32) == epoch;
         }
-        if (__ballot(!have) == 0) return true;
+        if (__ballot(!have) == 0) break;
         if (spins > kSpinLimit) {
             if (lane == 0) flag_error(p.ctl);
-            return false;
+            ok = false;
+            break;
         }
         __builtin_amdgcn_s_sleep(1);
     }
-}
-
-// Routing weight of rank j: softmax over the k kept logits (lane r holds the
-// logit of rank r), summed in rank order.  Wave-uniform result.
-__device__ __forceinline__ float topk_weight(float l, int k, int j) {
-    const float pr = expf(l - lane_f(l, 0));
-    float z = 0.0f;
-    for (int r = 0; r < k; r++) z += lane_f(pr, r);
-    return lane_f(pr, j) / z;
-}
-
-// The expert and weight of `slot`: wave 0 reads its token's top k (copy
-// blockIdx % kSelReplicas) and keeps rank slot % top_k.  The shared expert's
-// slots read it too (so that they never add into rows not yet cleared) and take
-// expert 0 of the shared stack with weight 1.
-__device__ void route_slot(const DecodeArgs& p, int slot, int t, bool routed, unsigned epoch, RoleShared& sh) {
-    if (threadIdx.x < kWave) {
-        float l;
-        int ex;
-        const bool ok = read_topk(p, t, blockIdx.x % kSelReplicas, epoch, l, ex);
+    if (lane == 0) sh.route_ok[wave] = ok;
+    if (!routed) {
+        __syncthreads();
+        if (tid == 0) {
+            sh.ex = 0;
+            sh.wgt = 1.0f;
+            sh.ok = sh.route_ok[0] && sh.route_ok[1] && sh.route_ok[2] && sh.route_ok[3];
+        }
+        __syncthreads();
+        return;
+    }
+    const uint32_t mykey = mine ? order_key(__uint_as_float((uint32_t)v)) : 0u;
+    topk_keys(sh.tk, mykey, tid, lane, wave);
+    __syncthreads();
+    topk_candidates(sh.tk, mykey, p.E, tid, lane, wave);
+    __syncthreads();
+    topk_rank(sh.tk, p.top_k, tid, lane, wave);
+    __syncthreads();
+    if (wave == 0) {
         const int j = slot % p.top_k;
-        const float w = topk_weight(l, p.top_k, j);
-        const int e = __builtin_amdgcn_readlane(ex, j);
-        if (threadIdx.x == 0) {
-            sh.ex = routed ? min(max(e, 0), p.E - 1) : 0;  // in range whatever was read
-            sh.wgt = routed ? w : 1.0f;
-            sh.ok = ok;
+        const float w = topk_weight_of_lane(sh.tk, p.top_k, lane);
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+        if (lane == 0) {
+            sh.ex = min(max(sh.tk.sel_e[j], 0), p.E - 1);  // in range whatever was read
+            sh.wgt = wj;
+            sh.ok = sh.route_ok[0] && sh.route_ok[1] && sh.route_ok[2] && sh.route_ok[3];
         }
     }
     __syncthreads();
@@ -221,11 +213,10 @@ template <typename SB, bool kQ8>
 __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShared& sh) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int H = p.H, T = p.T, E = p.E;
-    const int e = b * kRouterExperts + wave;
+    const int e = b;  // one expert per workgroup
     const int nblk = H / 8;  // 16-byte chunks of a row
     // clear the output rows (write-through); they are complete before any logit
-    // goes out, hence before any top-k entry, which every down workgroup reads
-    // before it adds into them
+    // goes out, which every down workgroup reads before it adds into them
     for (int i = b * kThreads + tid; i < T * H; i += p.router_wgs * kThreads) put(p.out + i, 0.0f);
 
     float acc[kDecodeMaxT];
@@ -238,74 +229,46 @@ __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShar
     const uint2* wq = reinterpret_cast<const uint2*>(p.router_q8 + (size_t)er * (H / 4));
     const SB* rs = static_cast<const SB*>(p.router_s) + (size_t)er * (H / 64);
     const SB* rb = static_cast<const SB*>(p.router_b) + (size_t)er * (H / 64);
-    for (int c0 = 0; c0 < nblk; c0 += 4 * kWave) {
-        uint4 a[4], xv[kDecodeMaxT][4];
-        uint2 aq[4];
-        SB sq[4], bq[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int c = min(c0 + lane + kWave * j, nblk - 1);
-            if (kQ8) {
-                aq[j] = wq[c];
-                sq[j] = rs[c / 8];
-                bq[j] = rb[c / 8];
-            } else {
-                a[j] = wr[c];
-            }
-#pragma unroll
-            for (int t = 0; t < kDecodeMaxT; t++)
-                xv[t][j] = reinterpret_cast<const uint4*>(p.x + (size_t)min(t, T - 1) * H)[c];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int c0 = 0; c0 < nblk; c0 += kThreads) {
+        const int c = min(c0 + tid, nblk - 1);
+        uint4 a, xv[kDecodeMaxT];
+        uint2 aq;
+        SB sq, bq;
         if (kQ8) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) a[j] = restore_q8x8(aq[j], sb_to_f32<SB>(sq[j]), sb_to_f32<SB>(bq[j]));
+            aq = wq[c];
+            sq = rs[c / 8];
+            bq = rb[c / 8];
+        } else {
+            a = wr[c];
         }
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            if (c0 + lane + kWave * j >= nblk) continue;
-            const uint16_t* ab = reinterpret_cast<const uint16_t*>(&a[j]);
+        for (int t = 0; t < kDecodeMaxT; t++) xv[t] = reinterpret_cast<const uint4*>(p.x + (size_t)min(t, T - 1) * H)[c];
+        __builtin_amdgcn_sched_barrier(0);
+        if (kQ8) a = restore_q8x8(aq, sb_to_f32<SB>(sq), sb_to_f32<SB>(bq));
+        if (c0 + tid < nblk) {
+            const uint16_t* ab = reinterpret_cast<const uint16_t*>(&a);
 #pragma unroll
             for (int t = 0; t < kDecodeMaxT; t++) {
-                const uint16_t* xb = reinterpret_cast<const uint16_t*>(&xv[t][j]);
+                const uint16_t* xb = reinterpret_cast<const uint16_t*>(&xv[t]);
 #pragma unroll
                 for (int i = 0; i < 8; i++) acc[t] += bf16_to_f32(xb[i]) * bf16_to_f32(ab[i]);
             }
         }
     }
-    const float bias = (p.logit_bias && e < E) ? p.logit_bias[e] : 0.0f;
-#pragma unroll
-    for (int t = 0; t < kDecodeMaxT; t++) acc[t] = group_sum(acc[t], kWave) + bias;  // every lane: the logit
-    for (int i = tid; i < kDecodeMaxT * kMaxE; i += kThreads) sh.keys[i] = 0;  // below every real key
-    __builtin_amdgcn_s_waitcnt(0);  // the clearing stores are out
-    __syncthreads();
-    if (lane < kXchReplicas && e < E) {  // lane r writes copy r
-#pragma unroll
-        for (int t = 0; t < kDecodeMaxT; t++)
-            if (t < T) publish(p.xch64 + lane * kXchWords + (size_t)t * E + e, epoch, __float_as_uint(acc[t]));
-    }
-
-    // rank this workgroup's experts against every logit: the rank of a key is
-    // the number of larger keys (keys are distinct), one ballot per 64 of them
-    const bool ok = await_published(p.xch64 + (b % kXchReplicas) * kXchWords, T * E, epoch,
-                                    [&](int i, uint32_t bits) { sh.keys[i] = rank_key(__uint_as_float(bits), i % E); },
-                                    p.ctl);
-    if (e >= E || !ok) return;
 #pragma unroll
     for (int t = 0; t < kDecodeMaxT; t++) {
-        if (t >= T) break;
-        const unsigned long long* kt = sh.keys + t * E;
-        const unsigned long long mine = kt[e];
-        int r = 0;
+        const float w = wave_total(acc[t]);
+        if (lane == 0) sh.rsum[t][wave] = w;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the clearing stores are out
+    __syncthreads();
+    const float bias = (p.logit_bias && e < E) ? p.logit_bias[e] : 0.0f;
+    if (tid < kXchReplicas && e < E) {  // thread r writes copy r
 #pragma unroll
-        for (int i = 0; i < kMaxE / kWave; i++) {
-            const int j = lane + kWave * i;
-            r += __popcll(__ballot(j < E && kt[min(j, E - 1)] > mine));
-        }
-        if (r < p.top_k && lane < kSelReplicas) {  // lane r writes copy r
-            unsigned long long* w = p.sel64 + lane * kSelWords + t * kMaxTopK + r;
-            publish(w, epoch, __float_as_uint(acc[t]));
-            publish(w + kSelReplicas * kSelWords, epoch, (uint32_t)e);
+        for (int t = 0; t < kDecodeMaxT; t++) {
+            if (t >= T) break;
+            const float lg = ((sh.rsum[t][0] + sh.rsum[t][1]) + (sh.rsum[t][2] + sh.rsum[t][3])) + bias;
+            publish(p.xch64 + tid * kXchWords + (size_t)t * E + e, epoch, __float_as_uint(lg));
         }
     }
 }
@@ -635,31 +598,39 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
     }
 }
 
-// Routing outputs requested by the caller, from the top-k entries the layer
-// kernel used (copy 0), with the same weight arithmetic: a tiny second kernel,
-// only when asked.
+// Routing outputs requested by the caller: the top k of the logits the layer
+// kernel published (copy 0), selected by one wave with the same ranking and
+// weight arithmetic as the expert workgroups (a tiny second kernel, only when
+// asked).
 __global__ __launch_bounds__(kWave) void decode_routing_out_kernel(DecodeArgs p) {
     __shared__ int counts[kMaxE];
     const int lane = threadIdx.x;
     const unsigned epoch = __hip_atomic_load(p.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int k = p.top_k;
+    const int k = p.top_k, E = p.E;
     for (int e = lane; e < kMaxE; e += kWave) counts[e] = 0;
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kDecodeMaxT; t++) {
         if (t >= p.T) break;
-        float l;
+        float held[kMaxE / kWave];
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) {
+            const int e = lane + kWave * i;
+            const unsigned long long wd = e < E ? peek(p.xch64 + (size_t)t * E + e) : 0ull;
+            ok = ok && (e >= E || (unsigned)(wd >> 32) == epoch);
+            held[i] = e < E ? __uint_as_float((uint32_t)wd) : -INFINITY;
+        }
         int ex;
-        read_topk(p, t, 0, epoch, l, ex);
-        float w = 0.0f;
-        for (int j = 0; j < k; j++) {
-            const float wj = topk_weight(l, k, j);
-            if (lane == j) w = wj;
+        float w;
+        wave_topk_held(held, E, k, lane, &ex, &w);
+        if (__ballot(!ok) != 0) {
+            if (lane == 0) flag_error(p.ctl);
         }
         if (lane < k) {
             if (p.idx_out) p.idx_out[t * k + lane] = ex;
             if (p.w_out) p.w_out[t * k + lane] = w;
-            if (ex >= 0 && ex < p.E) atomicAdd(&counts[ex], 1);
+            if (ex >= 0 && ex < E) atomicAdd(&counts[ex], 1);
         }
     }
     __syncthreads();
@@ -669,7 +640,7 @@ __global__ __launch_bounds__(kWave) void decode_routing_out_kernel(DecodeArgs p)
 
 }  // namespace
 
-int decode_router_wgs(int E) { return (E + kRouterExperts - 1) / kRouterExperts; }
+int decode_router_wgs(int E) { return E; }
 int decode_gateup_wgs(int T, int k, bool shared, int I) { return (T * k + (shared ? T : 0)) * (I / kGURows); }
 int decode_down_wgs(int T, int k, bool shared, int H) {
     return (T * k + (shared ? T : 0)) * ((H + kDRows - 1) / kDRows);

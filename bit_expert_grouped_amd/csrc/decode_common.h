@@ -79,6 +79,168 @@ __device__ __forceinline__ float group_sum(float v, int n) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// Sum over the wave, as a wave-uniform value: DPP butterflies inside each row of
+// 16 lanes, then the four row totals through readlane (no LDS round trip, as
+// the last two steps of group_sum take).
+__device__ __forceinline__ float wave_total(float v) {
+    v += dpp<0xB1>(v);   // quad_perm 1,0,3,2
+    v += dpp<0x4E>(v);   // quad_perm 2,3,0,1
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// ---- top k of a token's E <= 256 logits, selected by one workgroup whose
+// threads 0..255 (4 waves) hold one order key each (thread t: expert t; key 0
+// for t >= E).  Rank order: larger logit first, equal logits by lower expert
+// index.  Three steps with a workgroup barrier between them:
+//   topk_keys        every thread 0..255: its key into LDS, each wave's two
+//                    largest keys;
+//   topk_candidates  keys at or above the least of the four waves' second
+//                    largest: at least two keys of every wave reach it, so the
+//                    k <= 8 largest are among them and no key below it ranks in
+//                    the top k (fewer than 194 experts can leave a wave with
+//                    under two keys: then every expert is a candidate).  Each
+//                    wave lists its own candidates;
+//   topk_rank        up to kRankCands candidates are ranked in parallel, 8
+//                    threads each (the candidates above one, and the equal ones
+//                    of lower index); more take a radix search for the k-th
+//                    key in one wave.  Writes sel_e / sel_key for ranks < k.
+constexpr int kRankCands = 32;
+
+struct TopkShared {
+    uint32_t keys[kMaxE];
+    uint32_t m2[4];
+    uint32_t ckey[4][kWave];
+    int cidx[4][kWave];
+    int ccnt[4];
+    uint32_t tkey[kMaxTopK];
+    int tidx[kMaxTopK];
+    int sel_e[kMaxTopK];
+    uint32_t sel_key[kMaxTopK];
+};
+
+__device__ __forceinline__ void topk_keys(TopkShared& s, uint32_t mykey, int tid, int lane, int wave) {
+    s.keys[tid] = mykey;
+    const uint32_t m1 = wave_max_u32(mykey);
+    const int first = (int)__builtin_ctzll(__ballot(mykey == m1));
+    const uint32_t m2 = wave_max_u32(lane == first ? 0u : mykey);
+    if (lane == 0) s.m2[wave] = m2;
+}
+
+__device__ __forceinline__ void topk_candidates(TopkShared& s, uint32_t mykey, int E, int tid, int lane, int wave) {
+    const uint32_t lim = E >= 194 ? min(min(s.m2[0], s.m2[1]), min(s.m2[2], s.m2[3])) : 1u;
+    const bool c = mykey != 0u && mykey >= lim;
+    const uint64_t bal = __ballot(c);
+    if (c) {
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        s.ckey[wave][pos] = mykey;
+        s.cidx[wave][pos] = tid;
+    }
+    if (lane == 0) s.ccnt[wave] = __popcll(bal);
+}
+
+__device__ __forceinline__ void topk_rank(TopkShared& s, int k, int tid, int lane, int wave) {
+    const int n0 = s.ccnt[0], n1 = s.ccnt[1], n2 = s.ccnt[2], n3 = s.ccnt[3];
+    const int n = n0 + n1 + n2 + n3;
+    if (n <= kRankCands) {
+        if (tid < 8 * kRankCands) {
+            auto cand = [&](int q, uint32_t& key, int& e) {
+                const int w = q < n0 ? 0 : q < n0 + n1 ? 1 : q < n0 + n1 + n2 ? 2 : 3;
+                const int r = q - (w > 0 ? n0 : 0) - (w > 1 ? n1 : 0) - (w > 2 ? n2 : 0);
+                key = s.ckey[w][r];
+                e = s.cidx[w][r];
+            };
+            const int i = tid / 8;
+            uint32_t ck = 0;
+            int ce = 0;
+            if (i < n) cand(i, ck, ce);
+            int rank = 0;
+#pragma unroll
+            for (int m = 0; m < kRankCands / 8; m++) {
+                const int jj = tid % 8 + 8 * m;
+                if (jj < n) {
+                    uint32_t kj;
+                    int ej;
+                    cand(jj, kj, ej);
+                    rank += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
+                }
+            }
+            rank = (int)group_sum((float)rank, 8);
+            if (tid % 8 == 0 && i < n && rank < k) {
+                s.sel_e[rank] = ce;
+                s.sel_key[rank] = ck;
+            }
+        }
+    } else if (wave == 0) {
+        uint32_t key[kMaxE / kWave];
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) key[i] = s.keys[lane + kWave * i];
+        uint32_t theta = 0;
+        for (int b = 31; b >= 0; b--) {
+            const uint32_t cand = theta | (1u << b);
+            int c = 0;
+#pragma unroll
+            for (int i = 0; i < kMaxE / kWave; i++) c += __popcll(__ballot(key[i] >= cand));
+            if (c >= k) theta = cand;
+        }
+        uint64_t sel[kMaxE / kWave];
+        int need = k;
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) {
+            sel[i] = __ballot(key[i] > theta);
+            need -= __popcll(sel[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) {
+            uint64_t eq = __ballot(key[i] == theta);
+            while (need > 0 && eq) {
+                const uint64_t bit = eq & (~eq + 1);
+                sel[i] |= bit;
+                eq ^= bit;
+                need--;
+            }
+        }
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) {
+            if ((sel[i] >> lane) & 1ull) {
+                const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(sel[i] >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)sel[i], 0));
+                s.tkey[pos] = key[i];
+                s.tidx[pos] = lane + kWave * i;
+            }
+            base += __popcll(sel[i]);
+        }
+        if (lane < k) {
+            const uint32_t mk = s.tkey[lane];
+            const int me = s.tidx[lane];
+            int rank = 0;
+            for (int m = 0; m < k; m++) {
+                const uint32_t om = s.tkey[m];
+                rank += (om > mk || (om == mk && s.tidx[m] < me)) ? 1 : 0;
+            }
+            s.sel_e[rank] = me;
+            s.sel_key[rank] = mk;
+        }
+    }
+}
+
+// Routing weight of every rank (lane j < k: rank j), softmax of the kept
+// logits summed in rank order; one wave, after topk_rank and a barrier.
+__device__ __forceinline__ float topk_weight_of_lane(const TopkShared& s, int k, int lane) {
+    const uint32_t rk = lane < k ? s.sel_key[lane] : 0u;
+    const float top = key_float(__builtin_amdgcn_readlane(rk, 0));
+    const float pr = expf(key_float(rk) - top);
+    float z = 0.0f;
+    for (int m = 0; m < k; m++) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr), m));
+    return pr / z;
+}
+
 // {epoch, value} words and plain values crossing workgroups: agent-scope
 // accesses bypass the per-XCD L2, so no write-back or invalidate is needed
 __device__ __forceinline__ void publish(unsigned long long* p, unsigned epoch, uint32_t bits) {

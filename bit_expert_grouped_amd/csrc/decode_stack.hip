@@ -81,7 +81,6 @@ constexpr int kLogitsPerWg = 8;                   // experts a workgroup scores:
 constexpr long kSpinLimit = 1l << 20;
 constexpr int kPollThreads = kStackMaxH / 8;  // threads that poll the stream, one 8-column block each
 constexpr int kCopies = kStackLocalCopies;
-constexpr int kRankCands = 32;  // candidates ranked in parallel (8 threads each); more take a radix search
 
 // control words (uint32 indices) of the stack kernel inside the decode control block
 constexpr int kCtlStEpoch = 2048;            // epoch of the last layer of the last call
@@ -105,17 +104,9 @@ struct StackShared {
     float yr[kOwn];              // the routed slot's rows of the owned columns
     float ysh[kOwn];             // the shared expert's share of the same rows
     float pp[kXcds][kOwn];       // every XCD's partial sums of the owned columns
-    uint32_t keys[kMaxE];        // order keys of the logits
-    uint32_t tkey[kMaxTopK];     // the selected keys, in expert order
-    int tidx[kMaxTopK];
+    TopkShared tk;               // the top-k selection
     float sred[4];               // shared gate/up rows of this workgroup (gate 2j, 2j+1, up 2j, 2j+1)
-    int sel_e[kMaxTopK];         // the top k in rank order
-    uint32_t sel_key[kMaxTopK];
-    float sel_w[kMaxTopK];
-    uint32_t m2[4];              // second largest key of each wave's 64
-    uint32_t ckey[4][kWave];     // candidates of the top k (keys >= min of m2), per polling wave
-    int cidx[4][kWave];
-    int ccnt[4];
+    float sel_w[kMaxTopK];       // routing weights in rank order
     uint4 gam[kStackMaxH / 8];   // the layer's normalisation weight, per 8 columns
     unsigned xcd, idx;           // this workgroup's XCD and its index there
 };
@@ -206,21 +197,6 @@ __device__ bool poll_h(const unsigned long long* src, int n_words, unsigned epoc
                                 ((float)b.x + (float)b.y) + ((float)d.x + (float)d.y));
     }
     return ok;
-}
-
-// Sum over the wave, as a wave-uniform value: DPP butterflies inside each row of
-// 16 lanes, then the four row totals through readlane (no LDS round trip, as
-// the last two steps of group_sum take).
-__device__ __forceinline__ float wave_total(float v) {
-    v += dpp<0xB1>(v);   // quad_perm 1,0,3,2
-    v += dpp<0x4E>(v);   // quad_perm 2,3,0,1
-    v += dpp<0x141>(v);  // row_half_mirror
-    v += dpp<0x140>(v);  // row_mirror
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
 }
 
 // s * (sum of code * a over a word or words) + b * (sum of a), from the
@@ -549,132 +525,21 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                 __builtin_amdgcn_s_sleep(1);
             }
             mykey = mine ? order_key(__uint_as_float((uint32_t)v)) : 0u;
-            sh.keys[tid] = mykey;
-            // the two largest keys of this wave's 64 (equal keys count apart)
-            const uint32_t m1 = wave_max_u32(mykey);
-            const int first = (int)__builtin_ctzll(__ballot(mykey == m1));
-            const uint32_t m2 = wave_max_u32(lane == first ? 0u : mykey);
-            if (lane == 0) sh.m2[wave] = m2;
+            topk_keys(sh.tk, mykey, tid, lane, wave);
         } else if (wave == 6 && shared) {
             const bool ok = poll_h<kStackShWords>(loc_sh + (size_t)(j % kCopies) * kStackShWords, Ix / 2, ep, sh.hsp,
                                                   sh.hss, 0, lane, failed, a.ctl);
             failed = failed || !ok;
         }
         __syncthreads();  // B3: keys and the shared share's h in LDS
-        // candidates of the top k: keys >= the least of the four waves' second
-        // largest keys.  At least two keys of every wave reach it, so the k <= 8
-        // largest are among the candidates, and no key below it ranks in the
-        // top k.  (Fewer than 194 experts leave a wave with under two keys: then
-        // every expert is a candidate.)  Each polling wave lists its own.
-        if (tid < kMaxE) {
-            const uint32_t lim = E >= 194 ? min(min(sh.m2[0], sh.m2[1]), min(sh.m2[2], sh.m2[3])) : 1u;
-            const bool c = mykey != 0u && mykey >= lim;
-            const uint64_t bal = __ballot(c);
-            if (c) {
-                const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-                sh.ckey[wave][pos] = mykey;
-                sh.cidx[wave][pos] = tid;
-            }
-            if (lane == 0) sh.ccnt[wave] = __popcll(bal);
-        }
-        __syncthreads();  // candidates in LDS
-
         // ---- top k: every workgroup selects for itself, from the same words
-        {
-            const int n0 = sh.ccnt[0], n1 = sh.ccnt[1], n2 = sh.ccnt[2], n3 = sh.ccnt[3];
-            const int n = n0 + n1 + n2 + n3;
-            if (n <= kRankCands) {
-                // rank of candidate i (8 threads each, candidates j = t % 8 + 8 m):
-                // the candidates above it, and the equal ones of lower expert
-                // index; every other key is below them all
-                if (tid < 8 * kRankCands) {
-                    auto cand = [&](int p, uint32_t& key, int& e) {
-                        const int w = p < n0 ? 0 : p < n0 + n1 ? 1 : p < n0 + n1 + n2 ? 2 : 3;
-                        const int q = p - (w > 0 ? n0 : 0) - (w > 1 ? n1 : 0) - (w > 2 ? n2 : 0);
-                        key = sh.ckey[w][q];
-                        e = sh.cidx[w][q];
-                    };
-                    const int i = tid / 8;
-                    uint32_t ck = 0;
-                    int ce = 0;
-                    if (i < n) cand(i, ck, ce);
-                    int rank = 0;
-#pragma unroll
-                    for (int m = 0; m < kRankCands / 8; m++) {
-                        const int jj = tid % 8 + 8 * m;
-                        if (jj < n) {
-                            uint32_t kj;
-                            int ej;
-                            cand(jj, kj, ej);
-                            rank += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
-                        }
-                    }
-                    rank = (int)group_sum((float)rank, 8);
-                    if (tid % 8 == 0 && i < n && rank < k) {
-                        sh.sel_e[rank] = ce;
-                        sh.sel_key[rank] = ck;
-                    }
-                }
-            } else if (wave == 0) {
-                // many candidates (many equal keys, or few experts): the k-th
-                // largest key by a radix search, then every key above it and the
-                // equal ones by ascending index
-                uint32_t key[kMaxE / kWave];
-#pragma unroll
-                for (int i = 0; i < kMaxE / kWave; i++) key[i] = sh.keys[lane + kWave * i];
-                uint32_t theta = 0;
-                for (int b = 31; b >= 0; b--) {
-                    const uint32_t cand = theta | (1u << b);
-                    int c = 0;
-#pragma unroll
-                    for (int i = 0; i < kMaxE / kWave; i++) c += __popcll(__ballot(key[i] >= cand));
-                    if (c >= k) theta = cand;
-                }
-                uint64_t sel[kMaxE / kWave];
-                int need = k;
-#pragma unroll
-                for (int i = 0; i < kMaxE / kWave; i++) {
-                    sel[i] = __ballot(key[i] > theta);
-                    need -= __popcll(sel[i]);
-                }
-#pragma unroll
-                for (int i = 0; i < kMaxE / kWave; i++) {
-                    uint64_t eq = __ballot(key[i] == theta);
-                    while (need > 0 && eq) {
-                        const uint64_t bit = eq & (~eq + 1);
-                        sel[i] |= bit;
-                        eq ^= bit;
-                        need--;
-                    }
-                }
-                int base = 0;
-#pragma unroll
-                for (int i = 0; i < kMaxE / kWave; i++) {
-                    if ((sel[i] >> lane) & 1ull) {
-                        const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(sel[i] >> 32),
-                                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)sel[i], 0));
-                        sh.tkey[pos] = key[i];
-                        sh.tidx[pos] = lane + kWave * i;
-                    }
-                    base += __popcll(sel[i]);
-                }
-                if (lane < k) {
-                    const uint32_t mk = sh.tkey[lane];
-                    const int me = sh.tidx[lane];
-                    int rank = 0;
-                    for (int m = 0; m < k; m++) {
-                        const uint32_t om = sh.tkey[m];
-                        rank += (om > mk || (om == mk && sh.tidx[m] < me)) ? 1 : 0;
-                    }
-                    sh.sel_e[rank] = me;
-                    sh.sel_key[rank] = mk;
-                }
-            }
-        }
+        if (tid < kMaxE) topk_candidates(sh.tk, mykey, E, tid, lane, wave);
+        __syncthreads();  // candidates in LDS
+        topk_rank(sh.tk, k, tid, lane, wave);
         __syncthreads();  // B4: the routing in LDS
 
         // ---- routed loads of the XCD's slot: gate/up rows first, then down rows
-        const int ex = uniform(sh.sel_e[min(x, k - 1)]);
+        const int ex = uniform(sh.tk.sel_e[min(x, k - 1)]);
         uint4 gq[4];
         SB gs[4], gb[4];
 #pragma unroll
@@ -755,15 +620,10 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
         // ---- the routing weights: softmax of the kept logits, summed in rank
         // order (wave 0; used from the down on)
         if (wave == 0) {
-            const uint32_t rk = lane < k ? sh.sel_key[lane] : 0u;
-            const float top = key_float(__builtin_amdgcn_readlane(rk, 0));
-            const float pr = expf(key_float(rk) - top);
-            float z = 0.0f;
-            for (int m = 0; m < k; m++) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr), m));
-            const float wr = pr / z;
+            const float wr = topk_weight_of_lane(sh.tk, k, lane);
             if (lane < k) sh.sel_w[lane] = wr;
             if (zero_rank && lane < k) {
-                if (a.idx_out) a.idx_out[(size_t)l * k + lane] = sh.sel_e[lane];
+                if (a.idx_out) a.idx_out[(size_t)l * k + lane] = sh.tk.sel_e[lane];
                 if (a.w_out) a.w_out[(size_t)l * k + lane] = wr;
             }
         }

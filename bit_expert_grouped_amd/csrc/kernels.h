@@ -131,20 +131,19 @@ hipError_t launch_down(const GemmProblem& p, const _Float16* h, _Float16* y16, f
                        hipStream_t stream);
 
 // Decode path (T <= kDecodeMaxT, I <= kMaxDecodeI): one kernel per call whose
-// router workgroups publish the logits and rank them, whose gate/up workgroups
+// router workgroups publish the logits (each expert workgroup selects its
+// token's top k from them), whose gate/up workgroups
 // publish h, and whose down workgroups combine into `out` with float32
 // atomics.  It uses the decode region at the start of the workspace
 // (kDecodeRegionBytes, the same offsets for every dims, zero before the first
 // call): control words, then the values handed between workgroups.
 constexpr int kDecodeMaxT = 4;
 constexpr int kMaxDecodeI = 4096;
-constexpr int kDecodeXchReplicas = 4;   // copies of the logits, each read by a share of the router workgroups
-constexpr int kDecodeSelReplicas = 16;  // copies of the top k, each read by a share of the expert workgroups
+constexpr int kDecodeXchReplicas = 32;  // copies of the logits, each read by a share of the expert workgroups
 constexpr int kDecodeControlBytes = 16384;
 constexpr size_t kDecodeXchBytes = (size_t)kDecodeXchReplicas * kDecodeMaxT * 256 * 8;
-constexpr size_t kDecodeSelBytes = (size_t)2 * kDecodeSelReplicas * kDecodeMaxT * 8 * 8;
 constexpr size_t kDecodeHBytes = (size_t)kDecodeMaxT * (8 + 1) * kMaxDecodeI * 8;
-constexpr size_t kDecodeRegionBytes = kDecodeControlBytes + kDecodeXchBytes + kDecodeSelBytes + kDecodeHBytes;
+constexpr size_t kDecodeRegionBytes = kDecodeControlBytes + kDecodeXchBytes + kDecodeHBytes;
 
 struct DecodeArgs {
     int T, H, E, top_k, I;
@@ -157,7 +156,6 @@ struct DecodeArgs {
     const float* logit_bias;
     unsigned* ctl;               // control words and counters
     unsigned long long* xch64;   // kDecodeXchReplicas copies of [kDecodeMaxT][256] {epoch, logit}
-    unsigned long long* sel64;   // logits, then experts: each kDecodeSelReplicas copies of [kDecodeMaxT][8] {epoch, value}
     unsigned long long* h64;     // [slots][I] {epoch, h}; slots = T*k routed, then T shared
     int32_t* idx_out;            // optional copies of the routing
     float* w_out;

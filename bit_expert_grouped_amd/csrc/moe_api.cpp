@@ -39,7 +39,7 @@ moe_status check_dims(const moe_dims* d) {
 
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
-    size_t ctl, xch, sel, hbuf, stack;                   // decode regions (fixed offsets)
+    size_t ctl, xch, hbuf, stack;                        // decode regions (fixed offsets)
     size_t x16, h, y16, logits, hist, cursor;            // prefill buffers
     size_t idx, w, counts, offsets, sorted, tiles, n_tiles, tiles64, n_tiles64, shared_w, yacc, router16, total;
 };
@@ -57,8 +57,6 @@ Layout layout_of(const moe_dims* d) {
     o += kDecodeControlBytes;
     L.xch = o;
     o += kDecodeXchBytes;
-    L.sel = o;
-    o += kDecodeSelBytes;
     L.hbuf = o;
     o = up256(o + kDecodeHBytes);
     L.stack = o;  // exchange words of the persistent multi-layer decode kernel
@@ -361,7 +359,6 @@ moe_status layer_impl(const moe_dims* d, const moe_weights* wts, const uint16_t*
         a.logit_bias = wts->logit_bias;
         a.ctl = at<unsigned>(ws, L.ctl);
         a.xch64 = at<unsigned long long>(ws, L.xch);
-        a.sel64 = at<unsigned long long>(ws, L.sel);
         a.h64 = at<unsigned long long>(ws, L.hbuf);
         a.idx_out = topk_idx_out;
         a.w_out = topk_w_out;
