@@ -286,13 +286,9 @@ __device__ void gateup_role(const DecodeArgs& p, int slot, int blk, unsigned epo
     const int t = routed ? slot / p.top_k : slot - TK;
     const int i0 = blk * kGURows;
 
-    // the shared expert does not depend on the routing and starts at once
-    if (routed) {
-        route_slot(p, slot, t, true, epoch, sh);
-    } else if (tid == 0) {
-        sh.ex = 0;
-        sh.ok = 1;
-    }
+    // the shared expert waits for the logits too, so that its loads do not
+    // compete with the router's (13.38 against 13.46 us per call)
+    route_slot(p, slot, t, routed, epoch, sh);
     __syncthreads();
     const size_t ex = (size_t)sh.ex;
 
