@@ -116,6 +116,14 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// LDS positions of 16-byte blocks, transposed so that the lanes of one read
+// instruction touch consecutive blocks (no bank conflicts): the layer's input
+// (block 4 l + i, read by lane l as its i-th block, at i * 64 + l) and the
+// routed h (block 8 g + m, read by the lanes of group g as their m-th block,
+// at m * 8 + g)
+__device__ __forceinline__ int xpos(int b) { return (b & 3) * (kStackMaxH / 32) + (b >> 2); }
+__device__ __forceinline__ int hpos(int b) { return (b & 7) * (kStackMaxI / 64) + (b >> 3); }
+
 // tag of the stream words of epoch ep: 16 bits, never 0 (a zero-filled workspace's)
 __device__ __forceinline__ unsigned xtag(unsigned ep) { return ep % 65535u + 1u; }
 
@@ -158,9 +166,10 @@ __device__ __forceinline__ void block_pairs(const float (&v)[8], uint4& pairs, f
 // place the values in LDS as pairs in nibble order; then lanes 0..n/4-1 form
 // the low/high sums of the wave's blocks.  Returns false on timeout (then sets
 // the error word).
-template <int kPer>
+template <int kPer, bool kT>
 __device__ bool poll_h(const unsigned long long* src, int n_words, unsigned epoch, uint4* pairs, float2* sums,
                        int v, int lane, bool failed, unsigned* ctl) {
+    auto pos = [](int b) { return kT ? hpos(b) : b; };
     const int wd = kPer * v + lane;
     const bool mine = lane < kPer && wd < n_words;
     bool ok = true;
@@ -185,15 +194,15 @@ __device__ bool poll_h(const unsigned long long* src, int n_words, unsigned epoc
     if (mine) {
         const half2_t pr = as_half2((uint32_t)val);
         const int c0 = 2 * wd, c1 = 2 * wd + 1;
-        hh[(c0 >> 3) * 8 + slot_of_column(c0 & 7)] = pr.x;
-        hh[(c1 >> 3) * 8 + slot_of_column(c1 & 7)] = pr.y;
+        hh[pos(c0 >> 3) * 8 + slot_of_column(c0 & 7)] = pr.x;
+        hh[pos(c1 >> 3) * 8 + slot_of_column(c1 & 7)] = pr.y;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's values are in LDS
     const int blk = (kPer / 4) * v + lane;
     if (lane < kPer / 4 && blk * 4 < n_words) {
-        const uint4 p = pairs[blk];
+        const uint4 p = pairs[pos(blk)];
         const half2_t a = as_half2(p.x), b = as_half2(p.y), c = as_half2(p.z), d = as_half2(p.w);
-        sums[blk] = make_float2(((float)a.x + (float)a.y) + ((float)c.x + (float)c.y),
+        sums[pos(blk)] = make_float2(((float)a.x + (float)a.y) + ((float)c.x + (float)c.y),
                                 ((float)b.x + (float)b.y) + ((float)d.x + (float)d.y));
     }
     return ok;
@@ -441,8 +450,8 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
             }
             const uint4 raw = make_uint4(nb[0] | ((uint32_t)nb[1] << 16), nb[2] | ((uint32_t)nb[3] << 16),
                                          nb[4] | ((uint32_t)nb[5] << 16), nb[6] | ((uint32_t)nb[7] << 16));
-            reinterpret_cast<uint4*>(sh.xn)[tid] = raw;
-            block_pairs(v, sh.xp[tid], sh.xs[tid]);
+            reinterpret_cast<uint4*>(sh.xn)[xpos(tid)] = raw;
+            block_pairs(v, sh.xp[xpos(tid)], sh.xs[xpos(tid)]);
             if (a.layer_in && recorder && tid / 8 == j) reinterpret_cast<uint4*>(a.layer_in + (size_t)l * H)[tid] = raw;
         }
         __syncthreads();  // the layer's input in LDS
@@ -455,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
             if (rt_mine) {
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const uint4 xr = reinterpret_cast<const uint4*>(sh.xn)[4 * lane + i];
+                    const uint4 xr = reinterpret_cast<const uint4*>(sh.xn)[xpos(4 * lane + i)];
                     const uint32_t xw[4] = {xr.x, xr.y, xr.z, xr.w};
                     const uint32_t r0[4] = {ah.rt[0][i].x, ah.rt[0][i].y, ah.rt[0][i].z, ah.rt[0][i].w};
                     const uint32_t r1[4] = {ah.rt[1][i].x, ah.rt[1][i].y, ah.rt[1][i].z, ah.rt[1][i].w};
@@ -487,8 +496,8 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                 const uint32_t qw[4] = {ah.sgu.x, ah.sgu.y, ah.sgu.z, ah.sgu.w};
 #pragma unroll
                 for (int m = 0; m < 4; m++) {
-                    dot_word(qw[m], pairs_of(sh.xp[4 * lane + m]), alo, ahi);
-                    const float2 sm = sh.xs[4 * lane + m];
+                    dot_word(qw[m], pairs_of(sh.xp[xpos(4 * lane + m)]), alo, ahi);
+                    const float2 sm = sh.xs[xpos(4 * lane + m)];
                     lo += sm.x;
                     hi += sm.y;
                 }
@@ -527,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
             mykey = mine ? order_key(__uint_as_float((uint32_t)v)) : 0u;
             topk_keys(sh.tk, mykey, tid, lane, wave);
         } else if (wave == 6 && shared) {
-            const bool ok = poll_h<kStackShWords>(loc_sh + (size_t)(j % kCopies) * kStackShWords, Ix / 2, ep, sh.hsp,
+            const bool ok = poll_h<kStackShWords, false>(loc_sh + (size_t)(j % kCopies) * kStackShWords, Ix / 2, ep, sh.hsp,
                                                   sh.hss, 0, lane, failed, a.ctl);
             failed = failed || !ok;
         }
@@ -595,8 +604,8 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                 Pairs8 px[4];
 #pragma unroll
                 for (int m = 0; m < 4; m++) {
-                    px[m] = pairs_of(sh.xp[4 * lane + m]);
-                    const float2 sm = sh.xs[4 * lane + m];
+                    px[m] = pairs_of(sh.xp[xpos(4 * lane + m)]);
+                    const float2 sm = sh.xs[xpos(4 * lane + m)];
                     lo += sm.x;
                     hi += sm.y;
                 }
@@ -636,7 +645,7 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
 
         // ---- the slot's whole h (waves 0-3: 64 words each)
         if (has_slot && owns && wave < 4) {
-            const bool ok = poll_h<kWave>(loc_h + (size_t)(j % kCopies) * (kStackMaxI / 2), I / 2, ep, sh.hrp, sh.hrs,
+            const bool ok = poll_h<kWave, true>(loc_h + (size_t)(j % kCopies) * (kStackMaxI / 2), I / 2, ep, sh.hrp, sh.hrs,
                                           wave, lane, failed, a.ctl);
             failed = failed || !ok;
         }
@@ -651,8 +660,8 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
                 float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
 #pragma unroll
                 for (int m = 0; m < 8; m++) {
-                    dot_word(wv[m], pairs_of(sh.hrp[8 * dgrp + m]), alo, ahi);
-                    const float2 sm = sh.hrs[8 * dgrp + m];
+                    dot_word(wv[m], pairs_of(sh.hrp[hpos(8 * dgrp + m)]), alo, ahi);
+                    const float2 sm = sh.hrs[hpos(8 * dgrp + m)];
                     lo += sm.x;
                     hi += sm.y;
                 }
