@@ -561,6 +561,10 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
             gq[r] = ld<uint4>(lay(m.q, st.q, l) + row * (H / 2), off_gq);
         }
         __builtin_amdgcn_sched_barrier(0);  // the gate/up products wait for their loads only
+        // every wave's gate/up loads go out before any down load: the older
+        // waves 0-3 would otherwise issue their down rows ahead of the gate/up
+        // rows of waves 4-7, whose h then comes last (10.48 against 10.64 us)
+        __syncthreads();
         uint4 dq0, dq1;
         SB ds, db;
         {
