@@ -447,12 +447,12 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
 
 
     // h of the slot, by 64-column groups: wave w takes groups w, w + 4, ...
-    // (32 words {epoch, float16 pair} each), polls their words itself and, as
-    // soon as they carry this call's epoch, adds their part of every row's dot
-    // product, so the arithmetic overlaps the wait for the other groups.  h is
-    // kept as float16 in nibble order; 8-column block m of group g sits at
-    // block g * 8 + (m + g) % 8, so the 8 groups the lanes read at once hit
-    // different banks.
+    // (32 words {epoch, float16 pair} each), polls their words itself and, once
+    // they all carry this call's epoch, moves on to the products.  Lane i of
+    // the poll holds word i of the wave's words and returns the sum of its pair
+    // (0 for a lane past the groups).  h is kept in LDS as float16 in nibble
+    // order; 8-column block m of group g sits at block g * 8 + (m + g) % 8, so
+    // the 8 groups the lanes read at once hit different banks.
     const unsigned long long* hsrc = p.h64 + (size_t)slot * I / 2;
     _Float16* hh = sh.down.hh;
     auto h_pos = [](int i) {
@@ -461,68 +461,146 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     };
     const int gpw = (gd + kWaves - 1) / kWaves;  // groups per wave
     const int nw = 32 * gpw;                      // words this wave polls
-    int ok_h = 1;
-    for (long spins = 0;; spins++) {
-        bool have = true;
-        for (int idx = lane; idx < nw; idx += kWave) {
-            const int g = wave + kWaves * (idx / 32);
-            if (g >= gd) continue;
-            const int wd = 32 * g + idx % 32;
-            const unsigned long long v = peek(hsrc + wd);
-            if ((unsigned)(v >> 32) == epoch) {
-                const half2_t pr = as_half2((uint32_t)v);
-                hh[h_pos(2 * wd)] = pr.x;
-                hh[h_pos(2 * wd + 1)] = pr.y;
-            } else {
-                have = false;
+    auto poll_h = [&](float& pair_sum) -> int {
+        for (long spins = 0;; spins++) {
+            bool have = true;
+            for (int idx = lane; idx < nw; idx += kWave) {
+                const int g = wave + kWaves * (idx / 32);
+                if (g >= gd) continue;
+                const int wd = 32 * g + idx % 32;
+                const unsigned long long v = peek(hsrc + wd);
+                if ((unsigned)(v >> 32) == epoch) {
+                    const half2_t pr = as_half2((uint32_t)v);
+                    hh[h_pos(2 * wd)] = pr.x;
+                    hh[h_pos(2 * wd + 1)] = pr.y;
+                    pair_sum = (float)pr.x + (float)pr.y;
+                } else {
+                    have = false;
+                }
             }
+            if (__ballot(!have) == 0) return 1;
+            if (spins > kSpinLimit) {
+                if (lane == 0) flag_error(p.ctl);
+                return 0;
+            }
+            __builtin_amdgcn_s_sleep(4);
         }
-        if (__ballot(!have) == 0) break;
-        if (spins > kSpinLimit) {
-            if (lane == 0) flag_error(p.ctl);
-            ok_h = 0;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(4);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's h is in LDS
-    for (int idx = lane; idx < 8 * gpw; idx += kWave) {
-        const int g = wave + kWaves * (idx / 8), m = idx % 8;
-        if (g >= gd) continue;
-        const _Float16* hv = hh + ((g << 3) + ((m + g) & 7)) * 8;  // 0,4,1,5,2,6,3,7
-        sh.down.hsum[g * 8 + m] = make_float2((float)hv[0] + (float)hv[1] + (float)hv[4] + (float)hv[5],
-                                              (float)hv[2] + (float)hv[3] + (float)hv[6] + (float)hv[7]);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-    // lane r: this wave's groups of row r
-    const int r = lane;
+    };
+    const int r = lane;  // lane r: this wave's groups of row r
     float y = 0.0f;
-    if (r < n_rows) {
-        for (int j = 0; j < gpw; j++) {
+    int ok_h;
+    if (rows_in_lds) {
+        // I <= 512, so at most two groups per wave.  While h is on its way each
+        // lane turns its row's codes of those groups into exact float16 values
+        // (the exponent trick, then one packed subtract of 1024 or 64) and
+        // takes their scales and biases, so that once h is in only the dot
+        // products remain: y += s * sum(q * h) + b * sum(h) per group.
+        half2_t qv[2][32];
+        float sv[2] = {0.0f, 0.0f}, bv[2] = {0.0f, 0.0f};
+        const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+        const half2_t k64 = {(_Float16)64.0f, (_Float16)64.0f};
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
             const int g = wave + kWaves * j;
-            if (g >= gd) break;
-            uint4 v0, v1;
-            if (rows_in_lds) {
-                v0 = sh.down.drows[r * u_per_row + ((2 * g) ^ (r & swz_mask))];
-                v1 = sh.down.drows[r * u_per_row + ((2 * g + 1) ^ (r & swz_mask))];
-            } else {
-                v0 = dq[(size_t)r * u_per_row + 2 * g];
-                v1 = dq[(size_t)r * u_per_row + 2 * g + 1];
-            }
-            const uint4* hp4 = reinterpret_cast<const uint4*>(hh) + g * 8;  // blocks rotated by g
-            float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
+            const int gc = min(g, gd - 1), rr = min(r, n_rows - 1);  // in bounds for every lane
+            const uint4 v0 = sh.down.drows[rr * u_per_row + ((2 * gc) ^ (rr & swz_mask))];
+            const uint4 v1 = sh.down.drows[rr * u_per_row + ((2 * gc + 1) ^ (rr & swz_mask))];
             const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
             for (int m = 0; m < 8; m++) {
-                dot_word(wv[m], pairs_of(hp4[(m + g) & 7]), alo, ahi);
-                const float2 sm = sh.down.hsum[g * 8 + m];
-                lo += sm.x;
-                hi += sm.y;
+                const uint32_t w8 = wv[m] >> 8;
+                qv[j][4 * m + 0] = as_half2(and_or(wv[m], 0x000F000Fu, 0x64006400u)) - k1024;
+                qv[j][4 * m + 1] = as_half2(and_or(wv[m], 0x00F000F0u, 0x54005400u)) - k64;
+                qv[j][4 * m + 2] = as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)) - k1024;
+                qv[j][4 * m + 3] = as_half2(and_or(w8, 0x00F000F0u, 0x54005400u)) - k64;
             }
-            const SB sv = sb_in_lds ? lds_s[r * gd + g] : ds[(size_t)r * gd + g];
-            const SB bv = sb_in_lds ? lds_b[r * gd + g] : db[(size_t)r * gd + g];
-            y += sb_to_f32<SB>(sv) * ((alo - 1024.0f * lo) + (ahi - 64.0f * hi)) + sb_to_f32<SB>(bv) * (lo + hi);
+            if (g < gd) {
+                sv[j] = sb_to_f32<SB>(lds_s[rr * gd + g]);
+                bv[j] = sb_to_f32<SB>(lds_b[rr * gd + g]);
+            }
+        }
+        // keep the compiler from sinking this work past the wait for h
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                uint32_t u = as_u32(qv[j][i]);
+                asm volatile("" : "+v"(u));
+                qv[j][i] = as_half2(u);
+            }
+            asm volatile("" : "+v"(sv[j]), "+v"(bv[j]));
+        }
+        float pair_sum = 0.0f;
+        ok_h = poll_h(pair_sum);
+        // sum of h over each of the wave's groups: lanes 0..31 polled group
+        // wave, lanes 32..63 group wave + 4
+        float t = pair_sum;
+        t += dpp<0xB1>(t);   // quad_perm 1,0,3,2
+        t += dpp<0x4E>(t);   // quad_perm 2,3,0,1
+        t += dpp<0x141>(t);  // row_half_mirror
+        t += dpp<0x140>(t);  // row_mirror
+        const float hs[2] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 0)) +
+                                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 16)),
+                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 32)) +
+                                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 48))};
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's h is in LDS
+        // all 16 blocks of h the wave needs (broadcast reads), then one wait
+        const uint4* hp4 = reinterpret_cast<const uint4*>(hh);
+        uint4 hv[2][8];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int g = min(wave + kWaves * j, gd - 1);
+#pragma unroll
+            for (int m = 0; m < 8; m++) hv[j][m] = hp4[g * 8 + ((m + g) & 7)];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            if (wave + kWaves * j >= gd) break;
+            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                a0 = __builtin_amdgcn_fdot2(qv[j][4 * m + 0], as_half2(hv[j][m].x), a0, false);
+                a1 = __builtin_amdgcn_fdot2(qv[j][4 * m + 1], as_half2(hv[j][m].y), a1, false);
+                a2 = __builtin_amdgcn_fdot2(qv[j][4 * m + 2], as_half2(hv[j][m].z), a2, false);
+                a3 = __builtin_amdgcn_fdot2(qv[j][4 * m + 3], as_half2(hv[j][m].w), a3, false);
+            }
+            y += sv[j] * ((a0 + a1) + (a2 + a3)) + bv[j] * hs[j];
+        }
+        if (r >= n_rows) y = 0.0f;
+    } else {
+        // rows of more than 512 columns stay in global memory
+        float unused = 0.0f;
+        ok_h = poll_h(unused);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's h is in LDS
+        for (int idx = lane; idx < 8 * gpw; idx += kWave) {
+            const int g = wave + kWaves * (idx / 8), m = idx % 8;
+            if (g >= gd) continue;
+            const _Float16* hv = hh + ((g << 3) + ((m + g) & 7)) * 8;  // 0,4,1,5,2,6,3,7
+            sh.down.hsum[g * 8 + m] = make_float2((float)hv[0] + (float)hv[1] + (float)hv[4] + (float)hv[5],
+                                                  (float)hv[2] + (float)hv[3] + (float)hv[6] + (float)hv[7]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (r < n_rows) {
+            for (int j = 0; j < gpw; j++) {
+                const int g = wave + kWaves * j;
+                if (g >= gd) break;
+                const uint4 v0 = dq[(size_t)r * u_per_row + 2 * g];
+                const uint4 v1 = dq[(size_t)r * u_per_row + 2 * g + 1];
+                const uint4* hp4 = reinterpret_cast<const uint4*>(hh) + g * 8;  // blocks rotated by g
+                float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
+                const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    dot_word(wv[m], pairs_of(hp4[(m + g) & 7]), alo, ahi);
+                    const float2 sm = sh.down.hsum[g * 8 + m];
+                    lo += sm.x;
+                    hi += sm.y;
+                }
+                const SB sv = sb_in_lds ? lds_s[r * gd + g] : ds[(size_t)r * gd + g];
+                const SB bv = sb_in_lds ? lds_b[r * gd + g] : db[(size_t)r * gd + g];
+                y += sb_to_f32<SB>(sv) * ((alo - 1024.0f * lo) + (ahi - 64.0f * hi)) + sb_to_f32<SB>(bv) * (lo + hi);
+            }
         }
     }
     sh.down.part[wave][lane] = y;
