@@ -106,10 +106,8 @@ struct RoleShared {
         TopkShared tk;  // gate/up and down roles: the token's top k (before the roles' own LDS use)
     };
     float rsum[kDecodeMaxT][kWaves];  // router role: each wave's part of the logits
-    int route_ok[kWaves];             // each wave saw its token's logits in time
     float hrow[kGURows];  // gate/up role: this workgroup's h
     int ex;
-    float wgt;
     float gatew;  // down role of the shared expert: its weight under an optional gate
     int ok;       // routing read in time
     int wait_ok;  // result of the last wait on published values
@@ -141,70 +139,62 @@ __device__ bool await_published(const unsigned long long* src, int n, unsigned e
     }
 }
 
-// The expert and weight of `slot`: the workgroup polls its token's E logits
-// (copy blockIdx % kXchReplicas, thread e: expert e), selects the top k and
-// keeps rank slot % top_k.  The shared expert's down slots wait for the logits
-// too (so that they never add into rows not yet cleared) and take expert 0 of
-// the shared stack with weight 1.
-__device__ void route_slot(const DecodeArgs& p, int slot, int t, bool routed, unsigned epoch, RoleShared& sh) {
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const unsigned long long* src = p.xch64 + (blockIdx.x % kXchReplicas) * kXchWords + (size_t)t * p.E;
-    const bool mine = tid < p.E;
-    unsigned long long v = 0;
-    bool ok = true;
-    // wait on one word first (the last expert's), so that hundreds of
-    // workgroups do not poll every word while the router works: that traffic
-    // slows the router's own loads (13.5 against 15.0 us per call)
-    if (tid == 0) {
-        for (long spins = 0; spins <= kSpinLimit; spins++) {
-            if ((unsigned)(peek(src + p.E - 1) >> 32) == epoch) break;
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    __syncthreads();
-    for (long spins = 0;; spins++) {
-        bool have = true;
-        if (mine) {
-            v = peek(src + tid);
-            have = (unsigned)(v >> 32) == epoch;
-        }
-        if (__ballot(!have) == 0) break;
-        if (spins > kSpinLimit) {
-            if (lane == 0) flag_error(p.ctl);
-            ok = false;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    if (lane == 0) sh.route_ok[wave] = ok;
-    if (!routed) {
-        __syncthreads();
-        if (tid == 0) {
-            sh.ex = 0;
-            sh.wgt = 1.0f;
-            sh.ok = sh.route_ok[0] && sh.route_ok[1] && sh.route_ok[2] && sh.route_ok[3];
-        }
-        __syncthreads();
-        return;
-    }
-    const uint32_t mykey = mine ? order_key(__uint_as_float((uint32_t)v)) : 0u;
-    topk_keys(sh.tk, mykey, tid, lane, wave);
-    __syncthreads();
-    topk_candidates(sh.tk, mykey, p.E, tid, lane, wave);
-    __syncthreads();
-    topk_rank(sh.tk, p.top_k, tid, lane, wave);
-    __syncthreads();
+// The expert of `slot`: wave 0 of the workgroup polls its token's E logits
+// (copy blockIdx % kXchReplicas; lane l: experts l, l + 64, l + 128, l + 192),
+// selects the top k in registers and keeps rank slot % top_k; the other waves
+// only meet it at the closing barrier.  Returns, in wave 0's lane j < top_k,
+// the order key of rank j (the routing weight is formed from these later, off
+// the path to the expert's loads).  The shared expert's slots wait for the
+// logits too (so that its down workgroups never add into rows not yet cleared)
+// and take expert 0 of the shared stack.
+__device__ uint32_t route_slot(const DecodeArgs& p, int slot, int t, bool routed, unsigned epoch, RoleShared& sh) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    constexpr int kPer = kMaxE / kWave;
+    uint32_t rk = 0;
     if (wave == 0) {
-        const int j = slot % p.top_k;
-        const float w = topk_weight_of_lane(sh.tk, p.top_k, lane);
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+        const unsigned long long* src = p.xch64 + (blockIdx.x % kXchReplicas) * kXchWords + (size_t)t * p.E;
+        // wait on one word first (the last expert's), so that hundreds of
+        // workgroups do not poll every word while the router works: that traffic
+        // slows the router's own loads (13.5 against 15.0 us per call)
         if (lane == 0) {
-            sh.ex = min(max(sh.tk.sel_e[j], 0), p.E - 1);  // in range whatever was read
-            sh.wgt = wj;
-            sh.ok = sh.route_ok[0] && sh.route_ok[1] && sh.route_ok[2] && sh.route_ok[3];
+            for (long spins = 0; spins <= kSpinLimit; spins++) {
+                if ((unsigned)(peek(src + p.E - 1) >> 32) == epoch) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        // the four loads go out together (a lane past E reads expert E-1 again)
+        unsigned long long v[kPer];
+        bool ok = true;
+        for (long spins = 0;; spins++) {
+#pragma unroll
+            for (int i = 0; i < kPer; i++) v[i] = peek(src + min(lane + kWave * i, p.E - 1));
+            bool have = true;
+#pragma unroll
+            for (int i = 0; i < kPer; i++) have &= (unsigned)(v[i] >> 32) == epoch;
+            if (__ballot(!have) == 0) break;
+            if (spins > kSpinLimit) {
+                if (lane == 0) flag_error(p.ctl);
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        int ex = 0;
+        if (routed) {
+            uint32_t key[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; i++)
+                key[i] = lane + kWave * i < p.E ? order_key(__uint_as_float((uint32_t)v[i])) : 0u;
+            rk = topk_wave_select(sh.tk, key, p.top_k, lane);
+            ex = min(max(sh.tk.sel_e[slot % p.top_k], 0), p.E - 1);  // in range whatever was read
+        }
+        if (lane == 0) {
+            sh.ex = ex;
+            sh.ok = ok;
         }
     }
     __syncthreads();
+    return rk;
 }
 
 // ------------------------------------------------------------------ router role
@@ -289,7 +279,6 @@ __device__ void gateup_role(const DecodeArgs& p, int slot, int blk, unsigned epo
     // the shared expert waits for the logits too, so that its loads do not
     // compete with the router's (13.38 against 13.46 us per call)
     route_slot(p, slot, t, routed, epoch, sh);
-    __syncthreads();
     const size_t ex = (size_t)sh.ex;
 
     const FfnPtr& f = kRouted ? p.experts : p.shared;
@@ -402,9 +391,8 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     }
     // every down workgroup waits for its token's logits, shared ones too: the
     // router clears the output rows before it publishes them
-    route_slot(p, slot, t, routed, epoch, sh);
+    const uint32_t rk = route_slot(p, slot, t, routed, epoch, sh);
     const size_t ex = (size_t)sh.ex;
-    const float wgt = sh.wgt;
     const FfnPtr& f = kRouted ? p.experts : p.shared;
     const uint32_t* d_q = f.down.q;
     const void* d_s = f.down.s;
@@ -440,6 +428,14 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
     }
     const SB* lds_s = reinterpret_cast<const SB*>(sh.down.dsb[0]);
     const SB* lds_b = reinterpret_cast<const SB*>(sh.down.dsb[1]);
+
+    // the slot's routing weight, by wave 0 (which adds the rows at the end)
+    // while the loads are in flight
+    float wgt = 1.0f;
+    if (kRouted && wave == 0) {
+        const float w = topk_weight_of_keys(rk, p.top_k);
+        wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), slot % p.top_k));
+    }
 
     // every wave's direct loads of rows and scales have landed
     __builtin_amdgcn_s_waitcnt(0);

@@ -144,6 +144,130 @@ __device__ __forceinline__ void topk_candidates(TopkShared& s, uint32_t mykey, i
     if (lane == 0) s.ccnt[wave] = __popcll(bal);
 }
 
+// Top k of the E <= 256 order keys one wave holds (key[i] of lane l: expert
+// l + 64 i, 0 for a missing expert) by a radix search for the k-th largest
+// key: the keys above it, then the equal ones of lowest index, ranked among
+// themselves.  Wave-local (uses tkey / tidx); writes sel_e / sel_key.
+__device__ __forceinline__ void topk_radix_wave(TopkShared& s, const uint32_t (&key)[kMaxE / kWave], int k, int lane) {
+    uint32_t theta = 0;
+    for (int b = 31; b >= 0; b--) {
+        const uint32_t cand = theta | (1u << b);
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) c += __popcll(__ballot(key[i] >= cand));
+        if (c >= k) theta = cand;
+    }
+    uint64_t sel[kMaxE / kWave];
+    int need = k;
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; i++) {
+        sel[i] = __ballot(key[i] > theta);
+        need -= __popcll(sel[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; i++) {
+        uint64_t eq = __ballot(key[i] == theta);
+        while (need > 0 && eq) {
+            const uint64_t bit = eq & (~eq + 1);
+            sel[i] |= bit;
+            eq ^= bit;
+            need--;
+        }
+    }
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; i++) {
+        if ((sel[i] >> lane) & 1ull) {
+            const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(sel[i] >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)sel[i], 0));
+            s.tkey[pos] = key[i];
+            s.tidx[pos] = lane + kWave * i;
+        }
+        base += __popcll(sel[i]);
+    }
+    if (lane < k) {
+        const uint32_t mk = s.tkey[lane];
+        const int me = s.tidx[lane];
+        int rank = 0;
+        for (int m = 0; m < k; m++) {
+            const uint32_t om = s.tkey[m];
+            rank += (om > mk || (om == mk && s.tidx[m] < me)) ? 1 : 0;
+        }
+        s.sel_e[rank] = me;
+        s.sel_key[rank] = mk;
+    }
+}
+
+// Top k (k <= 8) of the E <= 256 order keys one wave holds (as above), with no
+// workgroup barrier.  The keys of each of the 8 groups of 32 (slot i, lanes
+// 0..31 or 32..63) have a maximum; every key at or above the least of those 8
+// maxima is a candidate.  Each group holds one, so at least 8 >= k keys are
+// candidates and no key below the bound ranks in the top k.  The candidates
+// (~21 of 256 typically) move to lanes 0..n-1 through LDS, and lane c counts
+// the candidates that rank above its own (larger key, or equal key and lower
+// expert index).  More than 64 candidates (many equal logits, or E small enough
+// that a group is empty) take the radix search.  Writes sel_e / sel_key for
+// ranks < k and returns, in lane j < k, the key of rank j (0 in other lanes).
+__device__ __forceinline__ uint32_t topk_wave_select(TopkShared& s, const uint32_t (&key)[kMaxE / kWave], int k, int lane) {
+    uint32_t lim = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; i++) {
+        uint32_t m = key[i];
+        m = max_dpp<0xB1>(m);   // quad_perm 1,0,3,2
+        m = max_dpp<0x4E>(m);   // quad_perm 2,3,0,1
+        m = max_dpp<0x141>(m);  // row_half_mirror
+        m = max_dpp<0x140>(m);  // row_mirror
+        const uint32_t a = __builtin_amdgcn_readlane(m, 0), b = __builtin_amdgcn_readlane(m, 16);
+        const uint32_t c = __builtin_amdgcn_readlane(m, 32), d = __builtin_amdgcn_readlane(m, 48);
+        lim = min(lim, min(max(a, b), max(c, d)));  // unsigned compares
+    }
+    uint64_t bal[kMaxE / kWave];
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; i++) {
+        bal[i] = __ballot(key[i] != 0u && key[i] >= lim);
+        n += __popcll(bal[i]);
+    }
+    if (n > kWave) {
+        topk_radix_wave(s, key, k, lane);
+    } else {
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxE / kWave; i++) {
+            if ((bal[i] >> lane) & 1ull) {
+                const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[i] >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal[i], 0));
+                s.ckey[0][pos] = key[i];
+                s.cidx[0][pos] = lane + kWave * i;
+            }
+            base += __popcll(bal[i]);
+        }
+        // candidate c (lane c < n) as one 64-bit value that orders as the rank
+        // order: the key above 255 - expert index.  Lanes past n hold 0, below
+        // every candidate.  The broadcasts take constant lane indices.
+        const uint32_t ck = lane < n ? s.ckey[0][lane] : 0u;
+        const int ce = lane < n ? s.cidx[0][lane] : 0;
+        const uint64_t mine = lane < n ? ((uint64_t)ck << 8) | (uint32_t)(255 - ce) : 0ull;
+        const uint32_t mlo = (uint32_t)mine, mhi = (uint32_t)(mine >> 32);
+        int rank = 0;
+#pragma unroll
+        for (int c0 = 0; c0 < kWave; c0 += 8) {
+            if (c0 >= n) break;
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                const uint64_t km = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(mhi, c0 + m) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane(mlo, c0 + m);
+                rank += km > mine ? 1 : 0;
+            }
+        }
+        if (lane < n && rank < k) {
+            s.sel_e[rank] = ce;
+            s.sel_key[rank] = ck;
+        }
+    }
+    return lane < k ? s.sel_key[lane] : 0u;
+}
+
 __device__ __forceinline__ void topk_rank(TopkShared& s, int k, int tid, int lane, int wave) {
     const int n0 = s.ccnt[0], n1 = s.ccnt[1], n2 = s.ccnt[2], n3 = s.ccnt[3];
     const int n = n0 + n1 + n2 + n3;
@@ -180,65 +304,23 @@ __device__ __forceinline__ void topk_rank(TopkShared& s, int k, int tid, int lan
         uint32_t key[kMaxE / kWave];
 #pragma unroll
         for (int i = 0; i < kMaxE / kWave; i++) key[i] = s.keys[lane + kWave * i];
-        uint32_t theta = 0;
-        for (int b = 31; b >= 0; b--) {
-            const uint32_t cand = theta | (1u << b);
-            int c = 0;
-#pragma unroll
-            for (int i = 0; i < kMaxE / kWave; i++) c += __popcll(__ballot(key[i] >= cand));
-            if (c >= k) theta = cand;
-        }
-        uint64_t sel[kMaxE / kWave];
-        int need = k;
-#pragma unroll
-        for (int i = 0; i < kMaxE / kWave; i++) {
-            sel[i] = __ballot(key[i] > theta);
-            need -= __popcll(sel[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < kMaxE / kWave; i++) {
-            uint64_t eq = __ballot(key[i] == theta);
-            while (need > 0 && eq) {
-                const uint64_t bit = eq & (~eq + 1);
-                sel[i] |= bit;
-                eq ^= bit;
-                need--;
-            }
-        }
-        int base = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxE / kWave; i++) {
-            if ((sel[i] >> lane) & 1ull) {
-                const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(sel[i] >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)sel[i], 0));
-                s.tkey[pos] = key[i];
-                s.tidx[pos] = lane + kWave * i;
-            }
-            base += __popcll(sel[i]);
-        }
-        if (lane < k) {
-            const uint32_t mk = s.tkey[lane];
-            const int me = s.tidx[lane];
-            int rank = 0;
-            for (int m = 0; m < k; m++) {
-                const uint32_t om = s.tkey[m];
-                rank += (om > mk || (om == mk && s.tidx[m] < me)) ? 1 : 0;
-            }
-            s.sel_e[rank] = me;
-            s.sel_key[rank] = mk;
-        }
+        topk_radix_wave(s, key, k, lane);
     }
 }
 
 // Routing weight of every rank (lane j < k: rank j), softmax of the kept
-// logits summed in rank order; one wave, after topk_rank and a barrier.
-__device__ __forceinline__ float topk_weight_of_lane(const TopkShared& s, int k, int lane) {
-    const uint32_t rk = lane < k ? s.sel_key[lane] : 0u;
+// logits summed in rank order, from the ranks' keys (rk of lane j < k: rank j's
+// key); one wave.
+__device__ __forceinline__ float topk_weight_of_keys(uint32_t rk, int k) {
     const float top = key_float(__builtin_amdgcn_readlane(rk, 0));
     const float pr = expf(key_float(rk) - top);
     float z = 0.0f;
     for (int m = 0; m < k; m++) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr), m));
     return pr / z;
+}
+// the same from sel_key, after topk_rank and a barrier
+__device__ __forceinline__ float topk_weight_of_lane(const TopkShared& s, int k, int lane) {
+    return topk_weight_of_keys(lane < k ? s.sel_key[lane] : 0u, k);
 }
 
 // {epoch, value} words and plain values crossing workgroups: agent-scope

@@ -318,7 +318,10 @@ def _tied(T, H, E, k, I, seed=91, tau=1e-4):
     return w, x[np.array(keep[:T])]
 
 
-@pytest.mark.parametrize("T,H,E", [(3, 256, 48), (64, 256, 48), (1, 2048, 256), (600, 2048, 256)])
+# (3, 256, 96) and the E = 128 decode shape below leave whole groups of the
+# decode selection's 8 groups of 32 experts empty, so more than 64 candidates
+# reach its bound and it falls back to the radix search
+@pytest.mark.parametrize("T,H,E", [(3, 256, 48), (3, 256, 96), (64, 256, 48), (1, 2048, 256), (600, 2048, 256)])
 def test_exact_logit_ties_go_to_the_lower_index(T, H, E):
     k = 8
     w, x = _tied(T, H, E, k, 64)
@@ -597,6 +600,7 @@ def test_decode_path_real_shapes(T):
     (2, 512, 40, 3, 128, True, True),
     (1, 128, 8, 8, 64, True, False),
     (4, 2560, 64, 4, 192, True, True),
+    (2, 256, 128, 8, 64, True, True),
     # down rows too long for LDS (I > 512): the down workgroups read them from memory
     (2, 1024, 16, 2, 1024, False, True),
     # ... and float32 scales and biases of I = 2048 that do not fit beside them either
