@@ -100,7 +100,7 @@ struct StackShared {
     uint4 hsp[kStackMaxI / 64];  // the XCD's share of the shared expert's h, pairs per 8 values
     float2 hss[kStackMaxI / 64];
     uint4 hrp[kStackMaxI / 8];   // the XCD's routed slot's h, pairs per 8 values
-    float2 hrs[kStackMaxI / 8];
+    float2 hrs[kStackMaxI / 64];  // its even- and odd-column sums per 64-column group
     float yr[kOwn];              // the routed slot's rows of the owned columns
     float ysh[kOwn];             // the shared expert's share of the same rows
     float pp[kXcds][kOwn];       // every XCD's partial sums of the owned columns
@@ -163,9 +163,13 @@ __device__ __forceinline__ void block_pairs(const float (&v)[8], uint4& pairs, f
 
 // Poll the {epoch, float16 pair} words [n v, n v + n) of an h vector of
 // n_words words (lanes 0..n-1 of wave v, one word each; n = kPer <= 64) and
-// place the values in LDS as pairs in nibble order; then lanes 0..n/4-1 form
-// the low/high sums of the wave's blocks.  Returns false on timeout (then sets
-// the error word).
+// place the values in LDS as pairs in nibble order.  Then the low/high sums
+// that dot_word's exponent-trick codes need: the sums of the even and of the
+// odd columns (the two values of a word).  With kT (the routed h, n = 64) they
+// are formed per 64-column group by DPP sums over the words the wave holds
+// (group 2v in lanes 0..31, group 2v + 1 in lanes 32..63) and sums[g] is group
+// g's; otherwise lanes 0..n/4-1 form them per block of 8 columns.  Returns false
+// on timeout (then sets the error word).
 template <int kPer, bool kT>
 __device__ bool poll_h(const unsigned long long* src, int n_words, unsigned epoch, uint4* pairs, float2* sums,
                        int v, int lane, bool failed, unsigned* ctl) {
@@ -191,11 +195,35 @@ __device__ bool poll_h(const unsigned long long* src, int n_words, unsigned epoc
         }
     }
     _Float16* hh = reinterpret_cast<_Float16*>(pairs);
+    float ev = 0.0f, od = 0.0f;
     if (mine) {
         const half2_t pr = as_half2((uint32_t)val);
         const int c0 = 2 * wd, c1 = 2 * wd + 1;
         hh[pos(c0 >> 3) * 8 + slot_of_column(c0 & 7)] = pr.x;
         hh[pos(c1 >> 3) * 8 + slot_of_column(c1 & 7)] = pr.y;
+        ev = (float)pr.x;
+        od = (float)pr.y;
+    }
+    if constexpr (kT) {
+        static_assert(kPer == kWave, "one word per lane of the whole wave");
+        ev += dpp<0xB1>(ev);  // quad_perm 1,0,3,2
+        od += dpp<0xB1>(od);
+        ev += dpp<0x4E>(ev);  // quad_perm 2,3,0,1
+        od += dpp<0x4E>(od);
+        ev += dpp<0x141>(ev);  // row_half_mirror
+        od += dpp<0x141>(od);
+        ev += dpp<0x140>(ev);  // row_mirror
+        od += dpp<0x140>(od);
+        // the row totals are read by the whole wave: under a one-lane branch the
+        // compiler may finish the sums in that lane only
+        auto at = [](float f, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), l)); };
+        const float2 g0 = make_float2(at(ev, 0) + at(ev, 16), at(od, 0) + at(od, 16));
+        const float2 g1 = make_float2(at(ev, 32) + at(ev, 48), at(od, 32) + at(od, 48));
+        if (lane == 0) {
+            sums[2 * v] = g0;
+            sums[2 * v + 1] = g1;
+        }
+        return ok;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's values are in LDS
     const int blk = (kPer / 4) * v + lane;
@@ -661,15 +689,19 @@ __global__ __launch_bounds__(kThreads) void decode_stack_kernel(StackArgs a) {
             float y = 0.0f;
             if (dmine) {
                 const uint32_t wv[8] = {dq0.x, dq0.y, dq0.z, dq0.w, dq1.x, dq1.y, dq1.z, dq1.w};
-                float alo = 0.0f, ahi = 0.0f, lo = 0.0f, hi = 0.0f;
+                // the group's 8 blocks of h and its sums, read together
+                uint4 hv[8];
 #pragma unroll
-                for (int m = 0; m < 8; m++) {
-                    dot_word(wv[m], pairs_of(sh.hrp[hpos(8 * dgrp + m)]), alo, ahi);
-                    const float2 sm = sh.hrs[hpos(8 * dgrp + m)];
-                    lo += sm.x;
-                    hi += sm.y;
+                for (int m = 0; m < 8; m++) hv[m] = sh.hrp[hpos(8 * dgrp + m)];
+                const float2 gs = sh.hrs[dgrp];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                float alo0 = 0.0f, ahi0 = 0.0f, alo1 = 0.0f, ahi1 = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 8; m += 2) {
+                    dot_word(wv[m], pairs_of(hv[m]), alo0, ahi0);
+                    dot_word(wv[m + 1], pairs_of(hv[m + 1]), alo1, ahi1);
                 }
-                y = affine(sb_to_f32<SB>(ds), sb_to_f32<SB>(db), alo, ahi, lo, hi);
+                y = affine(sb_to_f32<SB>(ds), sb_to_f32<SB>(db), alo0 + alo1, ahi0 + ahi1, gs.x, gs.y);
             }
             y = group_sum(y, 8);  // the row's groups: 8 lanes
             if (dgrp == 0) sh.yr[8 * wave + lane / 8] = y;
