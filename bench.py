@@ -235,12 +235,19 @@ def _cpu_model():
 
 def check_decode_words(ws, decode_calls_expected=None):
     """The decode path's control words after a run: the timeout flag (word 255)
-    must be clear; the call counter (word 0) must have advanced by the number
-    of decode calls made, when that is known.  Raises on a violation."""
+    must be clear; the call counter (the high halves of the 32 64-bit words the
+    decode workgroups count themselves in on, uint32 words 513 + 32 g) must
+    agree and have advanced by the number of decode calls made, when that is
+    known, and no call may be left half counted (words 512 + 32 g).  Raises on
+    a violation."""
     import torch
 
-    words = ws[:1024].view(torch.int32).cpu()
-    calls, flag = int(words[0]), int(words[255])
+    words = ws[:8192].view(torch.int32).cpu()
+    counts = {int(words[513 + 32 * g]) for g in range(32)}
+    flag = int(words[255])
+    if len(counts) != 1 or any(int(words[512 + 32 * g]) != 0 for g in range(32)):
+        raise RuntimeError("decode arrival words disagree after the run: %s" % sorted(counts))
+    calls = counts.pop()
     if flag != 0:
         raise RuntimeError("a device-side wait of the decode kernel timed out (workspace word 255 = %d): "
                            "the timed outputs are invalid" % flag)

@@ -38,10 +38,10 @@
 // streaming through.  So every poll is a few lanes on a few words:
 //   - values go out as 64-bit words {epoch, value} written with L2-bypassing
 //     (agent-scope) stores; a reader waits for the words themselves.  The
-//     epoch is one more than the control word the previous call left; the last
-//     workgroup to finish stores it.
+//     epoch comes from a control word every workgroup counts itself in on when
+//     it starts (arrive()), so nothing is left to do when the work is done.
 //   - the expert workgroups read one of kXchReplicas copies of the logits
-//     (thread e of the workgroup polls expert e's word).
+//     (wave 0 polls them all, four experts per lane).
 //   - h goes out as float16 pairs, one pair per {epoch, pair} word; a gate/up
 //     workgroup's 16 values are 8 words stored by 8 lanes of one wave.  Each
 //     wave of a down workgroup polls the words of its own 64-column groups of
@@ -73,12 +73,48 @@ constexpr int kGURows = 16;  // gate and up rows per gate/up workgroup
 constexpr int kDRows = 64;   // output rows per down workgroup
 constexpr long kSpinLimit = 1l << 20;
 
+
 // control words (uint32 indices into the workspace control block); words that
-// many workgroups touch sit on lines of their own
-constexpr int kCtlEpoch = 0;      // epoch of the last completed call
-constexpr int kCtlDone = 64;      // groups of workgroups finished in this call
-constexpr int kCtlGroupDone = 512;  // + 32 g: workgroups of group g (blockIdx % 8 == g) finished
-constexpr int kDoneGroups = 8;
+// many workgroups touch sit on lines of their own.  Workgroup b counts itself
+// in on the 64-bit word of group b % kArriveGroups, at kCtlArrive + 32 g: the
+// group's workgroups of the running call that have started (low half) and the
+// calls started before it (high half, one copy per group).  One word for every
+// workgroup would serialize hundreds of atomics at the start of each call: one
+// word 19.5 us per call, 8 words 11.6, 16 words 11.1, 32 words 11.0.
+constexpr int kCtlArrive = 512;
+constexpr int kArriveGroups = 32;  // the grid has at least this many workgroups
+
+// A call's epoch: the count of calls before it with the top bit set, so that
+// it is never 0 (the epoch of the words of a zero-filled workspace) and two
+// consecutive calls never share one, across the count's wrap too.
+__device__ __forceinline__ unsigned epoch_of_calls(unsigned calls) { return calls | 0x80000000u; }
+
+// Counting a workgroup in: count_in() adds it to its group's word and returns
+// the word as it was; counted_in() then returns the call's epoch, and in the
+// last workgroup of the group to start moves the word on to the next call
+// (calls + 1, started 0) with an add whose result it does not wait for.  The
+// next call's workgroups start only after this kernel has ended, and every
+// call has workgroups in every group, so the groups' counts of calls stay
+// equal and every workgroup of a call reads the same one, whatever the grid
+// size of either call.  Two steps, so that a workgroup can put work between
+// the atomic and the use of its result.
+__device__ __forceinline__ unsigned long long* arrive_word(unsigned* ctl) {
+    return reinterpret_cast<unsigned long long*>(ctl + kCtlArrive + 32 * (blockIdx.x % kArriveGroups));
+}
+__device__ __forceinline__ unsigned long long count_in(unsigned* ctl) {
+    // an offset the compiler cannot prove uniform: it would otherwise merge the
+    // lanes' atomics into one and read the result back at once
+    unsigned zero = 0;
+    asm volatile("" : "+v"(zero));
+    return __hip_atomic_fetch_add(arrive_word(ctl) + zero, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned counted_in(unsigned* ctl, unsigned long long old) {
+    const unsigned g = blockIdx.x % kArriveGroups;
+    const unsigned members = (gridDim.x - g + kArriveGroups - 1) / kArriveGroups;
+    if ((unsigned)old == members - 1)
+        __hip_atomic_fetch_add(arrive_word(ctl), (1ull << 32) - members, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return epoch_of_calls((unsigned)(old >> 32));
+}
 
 // Sum each of 8 per-lane values over the 64 lanes of a wave through an LDS
 // transpose (red: 64*9 floats of this wave).  Lane 8v receives the total of value v.
@@ -111,7 +147,7 @@ struct RoleShared {
     float gatew;  // down role of the shared expert: its weight under an optional gate
     int ok;       // routing read in time
     int wait_ok;  // result of the last wait on published values
-    int last;     // this workgroup finished last
+    unsigned epoch;  // this call's epoch
 };
 
 // Poll n published words until every one carries `epoch`; each thread handles
@@ -200,7 +236,7 @@ __device__ uint32_t route_slot(const DecodeArgs& p, int slot, int t, bool routed
 // ------------------------------------------------------------------ router role
 
 template <typename SB, bool kQ8>
-__device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShared& sh) {
+__device__ void router_role(const DecodeArgs& p, int b, RoleShared& sh) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int H = p.H, T = p.T, E = p.E;
     const int e = b;  // one expert per workgroup
@@ -212,6 +248,7 @@ __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShar
     float acc[kDecodeMaxT];
 #pragma unroll
     for (int t = 0; t < kDecodeMaxT; t++) acc[t] = 0.0f;
+    unsigned long long arrived = 0;
     const int er = min(e, E - 1);
     const uint4* wr = reinterpret_cast<const uint4*>(p.router + (size_t)er * H);
     // 8-bit router: the row's codes (8 per 8-byte pair of words) and the scale
@@ -233,6 +270,9 @@ __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShar
         }
 #pragma unroll
         for (int t = 0; t < kDecodeMaxT; t++) xv[t] = reinterpret_cast<const uint4*>(p.x + (size_t)min(t, T - 1) * H)[c];
+        // count the workgroup in after this wave's loads, so that the atomic's
+        // return (in order with them) does not delay the products
+        if (c0 == 0 && tid == 0) arrived = count_in(p.ctl);
         __builtin_amdgcn_sched_barrier(0);
         if (kQ8) a = restore_q8x8(aq, sb_to_f32<SB>(sq), sb_to_f32<SB>(bq));
         if (c0 + tid < nblk) {
@@ -250,8 +290,10 @@ __device__ void router_role(const DecodeArgs& p, int b, unsigned epoch, RoleShar
         const float w = wave_total(acc[t]);
         if (lane == 0) sh.rsum[t][wave] = w;
     }
+    if (tid == 0) sh.epoch = counted_in(p.ctl, arrived);
     __builtin_amdgcn_s_waitcnt(0);  // the clearing stores are out
     __syncthreads();
+    const unsigned epoch = sh.epoch;
     const float bias = (p.logit_bias && e < E) ? p.logit_bias[e] : 0.0f;
     if (tid < kXchReplicas && e < E) {  // thread r writes copy r
 #pragma unroll
@@ -613,16 +655,18 @@ __device__ void down_role(const DecodeArgs& p, int slot, int blk, unsigned epoch
 template <typename SB, bool kQ8>
 __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
     __shared__ RoleShared sh;
-    // a plain load: the word was stored by the previous call (visible once that
-    // kernel has ended) and changes only after every workgroup of this call has
-    // read it, so each XCD's L2 can serve it instead of every workgroup going to
-    // memory for the same word
-    unsigned epoch = p.ctl[kCtlEpoch] + 1;
-    if (epoch == 0) epoch = 1;  // words of a zero-filled workspace carry epoch 0
     const int b = blockIdx.x;
     if (b < p.router_wgs) {
-        router_role<SB, kQ8>(p, b, epoch, sh);
-    } else if (b < p.router_wgs + p.gateup_wgs) {
+        router_role<SB, kQ8>(p, b, sh);
+        return;
+    }
+    // the expert workgroups need the epoch first for the logits, which take
+    // longer to come than the count
+    if (threadIdx.x == 0) sh.epoch = counted_in(p.ctl, count_in(p.ctl));
+    if (b >= p.router_wgs + p.gateup_wgs + p.down_wgs) return;  // padding up to kArriveGroups
+    __syncthreads();
+    const unsigned epoch = sh.epoch;
+    if (b < p.router_wgs + p.gateup_wgs) {
         const int unit = b - p.router_wgs, nblk = p.I / kGURows;
         const int slot = unit / nblk, blk = unit % nblk;
         if (slot < p.T * p.top_k)
@@ -637,35 +681,6 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
         else
             down_role<SB, false>(p, slot, blk, epoch, sh);
     }
-    // the last workgroup to finish resets the done counters and advances the
-    // epoch for the next call.  Its own stores and atomics need not have
-    // landed: the next call starts after this kernel has ended, and every
-    // workgroup read the epoch when it started, before it counted itself done.
-    // The count has two levels: workgroup b counts itself in group b % 8 (a
-    // counter on a line of its own), and the last of a group counts the group.
-    // The hundreds of down workgroups finish within a microsecond or two, and
-    // one counter for all of them serializes their atomics at the end of the
-    // kernel.
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned g = blockIdx.x % kDoneGroups;
-        const unsigned members = (gridDim.x - g + kDoneGroups - 1) / kDoneGroups;
-        const unsigned groups = min(gridDim.x, (unsigned)kDoneGroups);
-        bool last = false;
-        const unsigned old = __hip_atomic_fetch_add(p.ctl + kCtlGroupDone + 32 * g, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (old == members - 1)
-            last = __hip_atomic_fetch_add(p.ctl + kCtlDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   groups - 1;
-        sh.last = last;
-    }
-    __syncthreads();
-    if (sh.last && threadIdx.x == 0) {
-        for (int g = 0; g < kDoneGroups; g++)
-            __hip_atomic_store(p.ctl + kCtlGroupDone + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.ctl + kCtlDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.ctl + kCtlEpoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 }
 
 // Routing outputs requested by the caller: the top k of the logits the layer
@@ -675,7 +690,9 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs p) {
 __global__ __launch_bounds__(kWave) void decode_routing_out_kernel(DecodeArgs p) {
     __shared__ int counts[kMaxE];
     const int lane = threadIdx.x;
-    const unsigned epoch = __hip_atomic_load(p.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the layer kernel's epoch: it counted its call in when it started
+    const unsigned calls = __hip_atomic_load(p.ctl + kCtlArrive + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // group 0's
+    const unsigned epoch = epoch_of_calls(calls - 1u);
     const int k = p.top_k, E = p.E;
     for (int e = lane; e < kMaxE; e += kWave) counts[e] = 0;
     __syncthreads();
@@ -717,7 +734,7 @@ int decode_down_wgs(int T, int k, bool shared, int H) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool sb_bf16, hipStream_t stream) {
-    const dim3 grid(a.router_wgs + a.gateup_wgs + a.down_wgs);
+    const dim3 grid(max(a.router_wgs + a.gateup_wgs + a.down_wgs, kArriveGroups));
     const bool q8 = a.router_q8 != nullptr;
     if (sb_bf16 && !q8)
         hipLaunchKernelGGL((decode_layer_kernel<uint16_t, false>), grid, dim3(kThreads), 0, stream, a);

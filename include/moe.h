@@ -139,8 +139,11 @@ typedef struct {
  * compute", applied before anything is sized).  One workspace serves every entry point.
  * Zero-fill the whole workspace once after allocating it; after that, every
  * call leaves it ready for the next one, whatever the dims of either.  The
- * first 16384 bytes are control words of the decode path: word 0 counts its
- * calls, and word 255 (bytes 1020..1023) is set to nonzero, and stays so, if a
+ * first 16384 bytes are control words of the decode path: the 32 64-bit words
+ * at bytes 2048 + 128 g count the workgroups of a running decode call (low
+ * halves, 0 between calls) and the calls made (high halves, uint32 words
+ * 513 + 32 g, all equal), and word 255 (bytes 1020..1023) is set to nonzero,
+ * and stays so, if a
  * device-side wait of a decode call timed out (that call's output is then
  * invalid).  Calls that share a workspace must not overlap in time (use one
  * workspace per stream). */

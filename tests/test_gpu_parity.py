@@ -601,6 +601,8 @@ def test_decode_path_real_shapes(T):
     (1, 128, 8, 8, 64, True, False),
     (4, 2560, 64, 4, 192, True, True),
     (2, 256, 128, 8, 64, True, True),
+    # a grid of 7 workgroups, padded up to the 32 the decode kernel's arrival count needs
+    (1, 64, 2, 1, 64, True, False),
     # down rows too long for LDS (I > 512): the down workgroups read them from memory
     (2, 1024, 16, 2, 1024, False, True),
     # ... and float32 scales and biases of I = 2048 that do not fit beside them either
@@ -619,16 +621,21 @@ def test_decode_path_other_shapes(T, H, E, k, I, bf16, shared):
 
 
 def control_words(ws):
-    """(decode call counter, timeout flag) of a workspace."""
-    words = ws[:1024].view(torch.int32).cpu().numpy()
-    return int(words[0]), int(words[255])
+    """(decode call counter, timeout flag) of a workspace.  The decode
+    workgroups count themselves in on 32 64-bit words (uint32 words 512 + 32 g
+    and 513 + 32 g: started workgroups of the running call, calls made), whose
+    call counts must agree; word 255 is the timeout flag."""
+    words = ws[:8192].view(torch.int32).cpu().numpy()
+    calls = {int(words[513 + 32 * g]) for g in range(32)}
+    assert len(calls) == 1, calls
+    return calls.pop(), int(words[255])
 
 
-def done_counters(ws):
-    """The decode kernel's completion counters (uint32 word 64: finished groups; word
-    512 + 32 g: finished workgroups of group g), all back to zero after a call."""
-    words = ws[:4096].view(torch.int32).cpu().numpy()
-    return [int(words[64])] + [int(words[512 + 32 * g]) for g in range(8)]
+def arrivals(ws):
+    """Workgroups of a running decode call that have started, per group: all
+    back to zero once a call has run, whatever its grid."""
+    words = ws[:8192].view(torch.int32).cpu().numpy()
+    return [int(words[512 + 32 * g]) for g in range(32)]
 
 
 def test_decode_repeated_calls_and_control_words():
@@ -645,7 +652,7 @@ def test_decode_repeated_calls_and_control_words():
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ref["out"], "decode call %d" % t)
         assert control_words(ws) == (t + 1, 0)
-        assert done_counters(ws) == [0] * 9
+        assert arrivals(ws) == [0] * 32
 
 
 def test_workspace_shared_by_prefill_and_decode():
@@ -664,6 +671,7 @@ def test_workspace_shared_by_prefill_and_decode():
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ref["out"], "call %d T%d" % (n, T))
     assert control_words(ws) == (sum(1 for T in calls if T <= 4), 0)
+    assert arrivals(ws) == [0] * 32
 
 
 # ------------------------------------------------------------------ HIP graph capture
@@ -738,6 +746,6 @@ def test_back_to_back_decode_calls_in_one_graph():
         g.replay()
         torch.cuda.synchronize()
         assert control_words(ws) == ((rep + 1) * n, 0)
-        assert done_counters(ws) == [0] * 9
+        assert arrivals(ws) == [0] * 32
         for i in range(n):
             assert_close(outs[i].cpu().numpy(), refs[i], "graph replay %d call %d" % (rep, i))
