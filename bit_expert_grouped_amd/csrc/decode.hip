@@ -28,25 +28,27 @@
 //                      of h = silu(gate x) * (up x).
 //   down    [R+G, ...) one per (slot, 64 output rows).  Selects like gate/up,
 //                      has its 16 KB of whole down rows land in LDS
-//                      (direct loads, issued before it waits for h), waits for
-//                      the slot's h, then adds w * (W_down h) for its rows to
-//                      the float32 output with atomics (the fused combine: k+1
-//                      adds per output element).
+//                      (direct loads), turns its rows' codes into float16
+//                      values in registers and forms the routing weight while
+//                      it waits for the slot's h, then adds w * (W_down h) for
+//                      its rows to the float32 output with atomics (the fused
+//                      combine: k+1 adds per output element).
 // Hand-over between workgroups.  Polling is what costs here: a poll waits
 // behind every load its compute unit has in flight, and hundreds of
 // workgroups polling many words flood the memory system that the weights are
 // streaming through.  So every poll is a few lanes on a few words:
 //   - values go out as 64-bit words {epoch, value} written with L2-bypassing
 //     (agent-scope) stores; a reader waits for the words themselves.  The
-//     epoch comes from a control word every workgroup counts itself in on when
-//     it starts (arrive()), so nothing is left to do when the work is done.
+//     epoch comes from control words every workgroup counts itself in on when
+//     it starts (count_in / counted_in), so nothing is left to do when the
+//     work is done.
 //   - the expert workgroups read one of kXchReplicas copies of the logits
 //     (wave 0 polls them all, four experts per lane).
 //   - h goes out as float16 pairs, one pair per {epoch, pair} word; a gate/up
 //     workgroup's 16 values are 8 words stored by 8 lanes of one wave.  Each
 //     wave of a down workgroup polls the words of its own 64-column groups of
-//     the slot's h (the poll is the read), sleeping between rounds, and adds
-//     their part of the rows' dot products as soon as they are in.
+//     the slot's h (the poll is the read), sleeping between rounds; once all
+//     are in, the products need only broadcast reads of h.
 // Waits are bounded: after kSpinLimit polls a workgroup sets the error control
 // word and carries on (that call's output is then invalid).
 //
@@ -54,7 +56,9 @@
 // nibbles become 1024+q and its high nibbles 64+q as float16, so
 //   sum_k q_k a_k = (sum over low of (1024+q) a) - 1024 * (sum over low of a)
 //                 + (sum over high of (64+q) a) -   64 * (sum over high of a)
-// and a group contributes scale * sum q a + bias * sum a: 9 VALU ops per word.
+// and a group contributes scale * sum q a + bias * sum a: 9 VALU ops per word
+// (the router and gate/up products).  The down products take codes turned into
+// exact float16 q before h arrives (one packed subtract of 1024 or 64 per pair).
 #include "common.h"
 #include "decode_common.h"
 #include "kernels.h"
