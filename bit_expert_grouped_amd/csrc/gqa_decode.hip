@@ -83,6 +83,29 @@ __device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m); }
 
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+// the wave's largest value / total, wave-uniform: DPP within each row of 16
+// lanes (quad_perm 1,0,3,2; quad_perm 2,3,0,1; row_half_mirror; row_mirror),
+// then the four row results through readlane
+__device__ __forceinline__ float wave_max_f(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
 __device__ __forceinline__ unsigned long long peek(const unsigned long long* p) {
     return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -169,19 +192,11 @@ __device__ void merge_item(const GqaArgs& a, int b, int h, int chunk, int ns, in
             for (int i = 0; i < 8; i++) acc[i] = acc[i] * keep + w * ov[r][i];
         }
     }
-    float Mw = M;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, o));
+    const float Mw = wave_max_f(M);
     const float sc = M == -INFINITY ? 0.0f : exp2f(M - Mw);
-    L *= sc;
+    L = wave_sum_f(L * sc);
 #pragma unroll
-    for (int i = 0; i < 8; i++) acc[i] *= sc;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        L += __shfl_xor(L, o);
-#pragma unroll
-        for (int i = 0; i < 8; i++) acc[i] += __shfl_xor(acc[i], o);
-    }
+    for (int i = 0; i < 8; i++) acc[i] = wave_sum_f(acc[i] * sc);
     if (lane == 0) {
         float* out = a.out + ((size_t)b * a.Hq + h) * D + 8 * chunk;
         const float inv = ns > 0 ? 1.0f / L : 0.0f;
