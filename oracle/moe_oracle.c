@@ -69,28 +69,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-typedef struct {
-    const uint32_t *q; /* [N][K/8] packed 4-bit codes */
-    const void *s;     /* [N][K/group] scales: float32, or bfloat16 bits */
-    const void *b;     /* [N][K/group] biases, same type as s */
-    int32_t sb_bf16;   /* 1: s and b hold bfloat16 bit patterns */
-    int32_t N, K, group;
-} oracle_qmat;
-
-typedef struct {
-    int32_t T, H, E, top_k, I, I_shared, group, sb_bf16;
-    const uint16_t *x;          /* [T][H] bfloat16 bits */
-    const uint16_t *router;     /* [E][H] bfloat16 bits */
-    const float *logit_bias;    /* [E] or NULL */
-    /* routed experts, stacked: gate/up q [E][I][H/8], s/b [E][I][H/group];
-       down q [E][H][I/8], s/b [E][H][I/group] */
-    const uint32_t *gate_q, *up_q, *down_q;
-    const void *gate_s, *gate_b, *up_s, *up_b, *down_s, *down_b;
-    /* shared expert (single); gate_q == NULL means no shared expert */
-    const uint32_t *sh_gate_q, *sh_up_q, *sh_down_q;
-    const void *sh_gate_s, *sh_gate_b, *sh_up_s, *sh_up_b, *sh_down_s, *sh_down_b;
-    const uint16_t *sh_expert_gate; /* [H] bfloat16 bits, or NULL: shared weight 1 (R14) */
-} oracle_layer;
+#include "moe_oracle.h"
 
 static double bf16_bits_value(uint16_t bits)
 {
@@ -372,7 +351,8 @@ static oracle_qmat expert_mat(const uint32_t *q, const void *s, const void *b, i
  * listed slots in stable slot order.
  * Outputs: out [n_tok][H]; logits [T][E] (nullable); idx [T][k]; w [T][k];
  * counts [E]; offsets [E+1]; sorted_slot [T*k] (nullable).
- * Returns 0, or -1 if a working buffer could not be allocated.
+ * Returns 0, or -1 if a working buffer could not be allocated (every buffer
+ * this call allocated is freed either way).
  */
 int oracle_moe_layer(const oracle_layer *L, int32_t n_tok, const int32_t *tok, double *out,
                      double *logits, int32_t *idx, double *w, int32_t *counts, int32_t *offsets,
@@ -391,9 +371,10 @@ int oracle_moe_layer(const oracle_layer *L, int32_t n_tok, const int32_t *tok, d
     int32_t *rdst = (int32_t *)malloc(sizeof(int32_t) * ((size_t)nt * k + 1));
     double *ybuf = (double *)malloc(sizeof(double) * ((size_t)nt * k + 1) * H);
     double *s_sh = L->sh_expert_gate ? (double *)malloc(sizeof(double) * ((size_t)nt + 1)) : NULL;
+    int status = -1;
     if (!lg || !ss || !pos || !y_slot || (L->sh_gate_q && !y_sh) || !w_sub || !rows || !rdst || !ybuf ||
         (L->sh_expert_gate && !s_sh))
-        return -1;
+        goto done;
 
     oracle_router_logits(T, H, E, L->x, L->router, L->logit_bias, lg);
     oracle_select(T, E, k, lg, idx, w);
@@ -441,9 +422,10 @@ int oracle_moe_layer(const oracle_layer *L, int32_t n_tok, const int32_t *tok, d
         for (int32_t i = 0; i < nt; i++)
             oracle_shared_gate(1, H, L->x + (size_t)(tok ? tok[i] : i) * H, L->sh_expert_gate, s_sh + i);
     oracle_combine(nt, k, H, y_slot, w_sub, y_sh, s_sh, out);
+    status = 0;
 
+done:
     free(s_sh);
-
     free(ybuf);
     free(rdst);
     free(rows);
@@ -455,7 +437,7 @@ int oracle_moe_layer(const oracle_layer *L, int32_t n_tok, const int32_t *tok, d
         free(ss);
     if (!logits)
         free(lg);
-    return 0;
+    return status;
 }
 
 /* Decode attention with grouped-query KV sharing (R19).  q [B][Hq][D],

@@ -78,7 +78,8 @@ def test_mutation_is_caught(name):
         so = os.path.join(d, "libm.so")
         with open(cpath, "w") as f:
             f.write(src.replace(old, new))
-        subprocess.check_call(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-o", so, cpath, "-lm"])
+        subprocess.check_call(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-I" + os.path.dirname(SRC),
+                               "-o", so, cpath, "-lm"])
         saved_path, saved_lib = oracle._LIB_PATH, oracle._lib
         oracle._LIB_PATH, oracle._lib = so, None
         failed = []
