@@ -516,6 +516,15 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     // scale block goes out before the ring, so waiting for stage 0 also waits
     // for it (loads of a wave complete in order); later blocks go out during
     // the last stage of the block before, so the ring never drains.
+    // gate/up synchronises the workgroup once per pair of stages (an even
+    // stage and the odd one after it): compute(kg) refills the slot of stage
+    // kg - 2, which belongs to the pair before, so one barrier per pair covers
+    // every refill, and the wave that finishes a stage first goes on to the
+    // next instead of waiting at a barrier for its SIMD's other wave.  down,
+    // with 8 stages per item at I = 512, waits per stage: waiting for a whole
+    // pair at its start costs it more than the barriers saved.
+    constexpr bool kPairs = kMode == kGateUp;
+    static_assert(!kPairs || kBlk % 2 == 0, "a scale block starts on the first stage of a pair");
     load_scales(0);
 #pragma unroll
     for (int j = 0; j < D - 2; j++)
@@ -524,23 +533,28 @@ __device__ void gemm_tile(const GemmArgs& p, const Tile& tl, int slab, unsigned 
     int slot = 0, fill = D - 2;  // slot of stage kg; slot that stage kg + D - 2 goes to
 #pragma unroll 1
     for (int kg = 0; kg < n_groups; kg++) {
-        int younger = 0;
-        if (kg == g0 + kBlk) {
-            // first stage of the next scale block: the block went out in the
-            // previous iteration, after the loads of stages up to kg + D - 4
-            // and before those of stage kg + D - 3, so all but stage
-            // kg + D - 3's loads must have landed
-            g0 = kg;
-            if (kg + D - 3 < n_groups) younger = R::loads(kg + D - 3);
-        } else {
-            // stage kg has landed once only the loads of the stages issued
-            // after it (kg + 1 .. kg + D - 3, those that exist) may be outstanding
+        if (!kPairs || (kg & 1) == 0) {
+            // this wait covers stages kg .. last: the loads of the stages
+            // issued after `last` (up to kg + D - 3, those that exist) may be
+            // outstanding
+            const int last = kPairs ? kg + 1 : kg;
+            int younger = 0;
+            if (kg == g0 + kBlk) {
+                // first stage of the next scale block: the block went out in
+                // the previous iteration, after the loads of stages up to
+                // kg + D - 4 and before those of stage kg + D - 3, so all but
+                // stage kg + D - 3's loads must have landed (and all of them
+                // when that stage is one the wait covers)
+                g0 = kg;
+                if (kg + D - 3 > last && kg + D - 3 < n_groups) younger = R::loads(kg + D - 3);
+            } else {
 #pragma unroll
-            for (int j = 1; j <= D - 3; j++)
-                if (kg + j < n_groups) younger += R::loads(kg + j);
+                for (int j = 1; j <= D - 3; j++)
+                    if (kg + j > last && kg + j < n_groups) younger += R::loads(kg + j);
+            }
+            wait_vm(younger);
+            barrier();  // every wave's stages kg .. last have landed; every wave is done with the stages before kg
         }
-        wait_vm(younger);
-        barrier();  // every wave's stage kg has landed; every wave is done with stage kg - 1
         const int g_next = kg + 1 == g0 + kBlk && kg + 1 < n_groups ? kg + 1 : -1;
         compute(slot, kg, g0, kg + D - 2 < n_groups ? kg + D - 2 : -1, fill, g_next);
         slot = slot == D - 1 ? 0 : slot + 1;
