@@ -278,6 +278,9 @@ def _custom(T, H, E, k, I, Is, bf16=True, seed=77, bias=None):
     (600, 384, 16, 2, 192, True),      # ragged H and I: partial column slabs in both products
     (520, 256, 12, 3, 320, False),     # E not a multiple of 32, fp32 scales, I = 256 + 64
     (1200, 256, 8, 2, 128, True),      # ~300 rows per expert: several 128-row tiles each
+    # gate/up synchronises once per pair of K stages; a scale block starts on the first stage of a pair
+    (1100, 320, 8, 2, 128, False),     # fp32 scales (4 groups per block): 5 stages, a block start at stage 4, which is alone
+    (1100, 576, 8, 2, 64, True),       # bf16 scales (8 groups per block): 9 stages, the block start at 8 alone in its pair
     # large-batch router (T >= 2048): LDS-staged 64 x 64 logit tiles with K split S ways
     (2100, 1024, 256, 8, 64, True),    # ragged last token tile, S = 2 (8 chunks of 64 columns)
     (2100, 256, 40, 3, 64, False),     # one 64-expert tile with 24 clamped rows, S = 4 (one chunk)
